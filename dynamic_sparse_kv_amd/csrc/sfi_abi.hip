@@ -1,0 +1,360 @@
+// C ABI of libsfi: argument validation, workspace carving, launch planning.
+// The contract of every entry point is documented in include/sfi.h.
+#include "sfi.h"
+
+#include <string.h>
+
+#include "sfi_internal.hpp"
+
+namespace {
+
+using namespace sfi;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool supported_group(int G) { return G == 1 || G == 2 || G == 4 || G == 5 || G == 8; }
+
+// Validates the cache description; on success fills the device view.
+sfi_status check_kv(const sfi_kv *kv, KVView *view, bool *paged) {
+  if (!kv) return SFI_ERR_NULL;
+  if (!kv->k || !kv->v || !kv->seq_len) return SFI_ERR_NULL;
+  if (kv->B < 1 || kv->Hq < 1 || kv->Hkv < 1 || kv->Hq % kv->Hkv != 0) return SFI_ERR_SHAPE;
+  if (kv->d != 64 && kv->d != 128) return SFI_ERR_UNSUPPORTED;
+  if (!supported_group(kv->Hq / kv->Hkv)) return SFI_ERR_UNSUPPORTED;
+  if (kv->max_seq_len < 1) return SFI_ERR_RANGE;
+  view->k = kv->k;
+  view->v = kv->v;
+  view->Hkv = kv->Hkv;
+  view->page_table = kv->page_table;
+  if (kv->page_table) {
+    const int ps = kv->page_size;
+    if (ps < 16 || ps > 1024 || (ps & (ps - 1)) != 0) return SFI_ERR_RANGE;
+    if (kv->max_pages < 1 || kv->num_pages < 1) return SFI_ERR_SHAPE;
+    if ((long long)kv->max_seq_len > (long long)kv->max_pages * ps) return SFI_ERR_RANGE;
+    int sh = 0;
+    while ((1 << sh) < ps) ++sh;
+    view->page_shift = sh;
+    view->max_pages = kv->max_pages;
+    view->num_pages = kv->num_pages;
+    view->cap = 0;
+    *paged = true;
+  } else {
+    if (kv->cap < 1) return SFI_ERR_SHAPE;
+    if (kv->max_seq_len > kv->cap) return SFI_ERR_RANGE;
+    view->page_shift = 0;
+    view->max_pages = 0;
+    view->num_pages = 0;
+    view->cap = kv->cap;
+    *paged = false;
+  }
+  return SFI_OK;
+}
+
+sfi_status check_batch(const sfi_kv *kv, int32_t batch_n) {
+  if (batch_n < 0 || batch_n > kv->B) return SFI_ERR_RANGE;
+  return SFI_OK;
+}
+
+struct SlowWs {
+  size_t o, ml, logits, total;
+  int stride;
+};
+
+SlowWs slow_ws(const sfi_kv *kv) {
+  SlowWs w{};
+  w.stride = (kv->max_seq_len + kMinSlowChunk - 1) / kMinSlowChunk;
+  const size_t rows = (size_t)kv->B * kv->Hq * w.stride;
+  w.o = 0;
+  w.ml = align_up(w.o + rows * kv->d * sizeof(float));
+  w.logits = align_up(w.ml + rows * 2 * sizeof(float));
+  w.total = align_up(w.logits + (size_t)kv->B * kv->Hq * kv->max_seq_len * sizeof(float));
+  return w;
+}
+
+struct FastWs {
+  size_t o, ml, total;
+  int stride;
+};
+
+FastWs fast_ws(const sfi_kv *kv, int sel_k, int n_sink, int window) {
+  FastWs w{};
+  const long long L = (long long)n_sink + window + sel_k;
+  const long long Lb = L < kv->max_seq_len + (long long)sel_k ? L : kv->max_seq_len + (long long)sel_k;
+  w.stride = (int)((Lb + kFastChunk - 1) / kFastChunk);
+  if (w.stride < 1) w.stride = 1;
+  const size_t rows = (size_t)kv->B * kv->Hq * w.stride;
+  w.o = 0;
+  w.ml = align_up(rows * kv->d * sizeof(float));
+  w.total = align_up(w.ml + rows * 2 * sizeof(float));
+  return w;
+}
+
+struct SelWs {
+  size_t stats, wsum, sbuf, total;
+  int nch;
+};
+
+SelWs select_ws(int B, int H, int max_seq_len) {
+  SelWs w{};
+  w.nch = (max_seq_len + kStatChunk - 1) / kStatChunk;
+  const size_t rows = (size_t)B * H;
+  w.stats = 0;
+  w.wsum = align_up(rows * w.nch * 2 * sizeof(double));
+  w.sbuf = align_up(w.wsum + rows * w.nch * sizeof(double));
+  w.total = align_up(w.sbuf + rows * (size_t)max_seq_len * sizeof(float));
+  return w;
+}
+
+struct VerWs {
+  size_t o, ml, agg, total;
+  int stride, chunk;
+};
+
+VerWs verify_ws(const sfi_kv *kv, int T) {
+  VerWs w{};
+  w.chunk = verify_chunk_for(kv->B, kv->Hkv, kv->max_seq_len);
+  w.stride = (kv->max_seq_len + w.chunk - 1) / w.chunk;
+  const size_t rows = (size_t)kv->B * T * kv->Hq * w.stride;
+  w.o = 0;
+  w.ml = align_up(rows * kv->d * sizeof(float));
+  w.agg = align_up(w.ml + rows * 2 * sizeof(float));
+  w.total = align_up(w.agg + (size_t)kv->B * kv->Hkv * kv->max_seq_len * sizeof(float));
+  return w;
+}
+
+template <typename T>
+T *carve(void *ws, size_t off) {
+  return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sfi_slow_workspace_bytes(const sfi_kv *kv) {
+  KVView v;
+  bool pg;
+  if (check_kv(kv, &v, &pg) != SFI_OK) return 0;
+  return slow_ws(kv).total;
+}
+
+size_t sfi_select_workspace_bytes(int32_t B, int32_t H, int32_t max_seq_len) {
+  if (B < 1 || H < 1 || max_seq_len < 1) return 0;
+  return select_ws(B, H, max_seq_len).total;
+}
+
+size_t sfi_fast_workspace_bytes(const sfi_kv *kv, int32_t sel_k, int32_t n_sink, int32_t window) {
+  KVView v;
+  bool pg;
+  if (check_kv(kv, &v, &pg) != SFI_OK || sel_k < 0 || n_sink < 0 || window < 0) return 0;
+  return fast_ws(kv, sel_k, n_sink, window).total;
+}
+
+sfi_status sfi_slow_step(const sfi_kv *kv, const int32_t *batch_ids, int32_t batch_n,
+                         const uint16_t *q, float *out, float *evidence, float *key_norm,
+                         int32_t ld, void *ws, size_t ws_bytes, void *stream) {
+  KVView view;
+  bool paged = false;
+  sfi_status s = check_kv(kv, &view, &paged);
+  if (s != SFI_OK) return s;
+  if ((s = check_batch(kv, batch_n)) != SFI_OK) return s;
+  if (!q || !out) return SFI_ERR_NULL;
+  if ((evidence || key_norm) && ld < kv->max_seq_len) return SFI_ERR_RANGE;
+  const SlowWs w = slow_ws(kv);
+  if (!ws) return SFI_ERR_NULL;
+  if (ws_bytes < w.total) return SFI_ERR_WORKSPACE;
+  if (batch_n == 0) return SFI_OK;
+
+  AttnLaunch a{};
+  a.kv = view;
+  a.seq_len = kv->seq_len;
+  a.batch_ids = batch_ids;
+  a.batch_n = batch_n;
+  a.B = kv->B; a.Hq = kv->Hq; a.Hkv = kv->Hkv; a.d = kv->d; a.G = kv->Hq / kv->Hkv;
+  a.max_len = kv->max_seq_len;
+  a.paged = paged;
+  a.q = q;
+  a.out = out;
+  a.part_o = carve<float>(ws, w.o);
+  a.part_ml = carve<float>(ws, w.ml);
+  a.plan.chunk = slow_chunk_for(batch_n, kv->Hkv, kv->max_seq_len);
+  a.plan.splits = (kv->max_seq_len + a.plan.chunk - 1) / a.plan.chunk;
+  a.plan.stride = w.stride;
+  a.logits = carve<float>(ws, w.logits);
+  a.lld = kv->max_seq_len;
+  a.evidence = evidence;
+  a.key_norm = key_norm;
+  a.ld = ld;
+  return launch_slow(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SFI_OK : SFI_ERR_HIP;
+}
+
+sfi_status sfi_select(const sfi_select_params *p, const int32_t *batch_ids, int32_t batch_n,
+                      const int32_t *seq_len, int32_t B, int32_t H, int32_t max_seq_len,
+                      const float *score, const float *key_norm, int32_t ld, int32_t *sel_idx,
+                      int32_t *sel_count, float *fused_out, void *ws, size_t ws_bytes,
+                      void *stream) {
+  if (!p || !seq_len || !score || !sel_idx || !sel_count) return SFI_ERR_NULL;
+  if (p->mode != SFI_SCORE_FUSED && p->mode != SFI_SCORE_RAW) return SFI_ERR_RANGE;
+  if (B < 1 || H < 1 || max_seq_len < 1) return SFI_ERR_SHAPE;
+  if (batch_n < 0 || batch_n > B) return SFI_ERR_RANGE;
+  if (ld < max_seq_len) return SFI_ERR_RANGE;
+  if (p->k < 1 || p->n_sink < 0 || p->window < 0) return SFI_ERR_RANGE;
+  const bool fused = p->mode == SFI_SCORE_FUSED;
+  if (fused) {
+    if (!key_norm) return SFI_ERR_NULL;
+    if (!(p->lambda >= 0.f && p->lambda <= 1.f)) return SFI_ERR_RANGE;
+    if (!(p->pos_tau > 0.f) || !(p->norm_coef == p->norm_coef)) return SFI_ERR_RANGE;
+  }
+  const SelWs w = select_ws(B, H, max_seq_len);
+  if (!ws) return SFI_ERR_NULL;
+  if (ws_bytes < w.total) return SFI_ERR_WORKSPACE;
+  if (batch_n == 0) return SFI_OK;
+
+  SelectLaunch a{};
+  a.mode = p->mode;
+  a.lambda = p->lambda; a.norm_coef = p->norm_coef; a.pos_tau = p->pos_tau;
+  a.n_sink = p->n_sink; a.window = p->window; a.k = p->k;
+  a.batch_ids = batch_ids; a.batch_n = batch_n; a.seq_len = seq_len;
+  a.B = B; a.H = H; a.max_seq_len = max_seq_len;
+  a.score = score; a.key_norm = key_norm; a.ld = ld;
+  a.sel_idx = sel_idx; a.sel_count = sel_count;
+  if (fused && fused_out) {
+    a.sbuf = fused_out;
+    a.sld = ld;
+  } else {
+    a.sbuf = carve<float>(ws, w.sbuf);
+    a.sld = max_seq_len;
+  }
+  a.stats = carve<double>(ws, w.stats);
+  a.wsum = carve<double>(ws, w.wsum);
+  a.nch = w.nch;
+  return launch_select(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SFI_OK : SFI_ERR_HIP;
+}
+
+sfi_status sfi_fast_step(const sfi_kv *kv, const int32_t *batch_ids, int32_t batch_n,
+                         const uint16_t *q, const int32_t *sel_idx, const int32_t *sel_count,
+                         int32_t sel_heads, int32_t sel_k, int32_t n_sink, int32_t window,
+                         float *out, void *ws, size_t ws_bytes, void *stream) {
+  KVView view;
+  bool paged = false;
+  sfi_status s = check_kv(kv, &view, &paged);
+  if (s != SFI_OK) return s;
+  if ((s = check_batch(kv, batch_n)) != SFI_OK) return s;
+  if (!q || !out || !sel_count) return SFI_ERR_NULL;
+  if (sel_k < 0 || n_sink < 0 || window < 0) return SFI_ERR_RANGE;
+  if (sel_k > 0 && !sel_idx) return SFI_ERR_NULL;
+  if (sel_heads != 1 && sel_heads != kv->Hkv) return SFI_ERR_SHAPE;
+  const FastWs w = fast_ws(kv, sel_k, n_sink, window);
+  if (!ws) return SFI_ERR_NULL;
+  if (ws_bytes < w.total) return SFI_ERR_WORKSPACE;
+  if (batch_n == 0) return SFI_OK;
+
+  AttnLaunch a{};
+  a.kv = view;
+  a.seq_len = kv->seq_len;
+  a.batch_ids = batch_ids;
+  a.batch_n = batch_n;
+  a.B = kv->B; a.Hq = kv->Hq; a.Hkv = kv->Hkv; a.d = kv->d; a.G = kv->Hq / kv->Hkv;
+  a.max_len = kv->max_seq_len;
+  a.paged = paged;
+  a.q = q;
+  a.out = out;
+  a.part_o = carve<float>(ws, w.o);
+  a.part_ml = carve<float>(ws, w.ml);
+  a.plan.chunk = kFastChunk;
+  a.plan.splits = w.stride;
+  a.plan.stride = w.stride;
+  a.sel_idx = sel_idx;
+  a.sel_count = sel_count;
+  a.sel_heads = sel_heads;
+  a.sel_k = sel_k;
+  a.n_sink = n_sink;
+  a.window = window;
+  return launch_fast(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SFI_OK : SFI_ERR_HIP;
+}
+
+size_t sfi_verify_workspace_bytes(const sfi_kv *kv, int32_t T) {
+  KVView v;
+  bool pg;
+  if (check_kv(kv, &v, &pg) != SFI_OK || T < 1 || T > 32) return 0;
+  return verify_ws(kv, T).total;
+}
+
+sfi_status sfi_verify_aggregate(const sfi_kv *kv, const int32_t *batch_ids, int32_t batch_n,
+                                const uint16_t *q, int32_t T, uint32_t row_mask, float *out,
+                                float *agg, int32_t ld, void *ws, size_t ws_bytes, void *stream) {
+  KVView view;
+  bool paged = false;
+  sfi_status s = check_kv(kv, &view, &paged);
+  if (s != SFI_OK) return s;
+  if ((s = check_batch(kv, batch_n)) != SFI_OK) return s;
+  if (!q || !out || !agg) return SFI_ERR_NULL;
+  const int G = kv->Hq / kv->Hkv;
+  if (T < 1 || G * T > 32) return SFI_ERR_UNSUPPORTED;
+  if (G == 5) return SFI_ERR_UNSUPPORTED;
+  const uint32_t all = (T >= 32) ? 0xffffffffu : ((1u << T) - 1u);
+  if (row_mask == 0u || (row_mask & ~all) != 0u) return SFI_ERR_RANGE;
+  if (kv->max_seq_len < T) return SFI_ERR_RANGE;
+  if (ld < kv->max_seq_len - T) return SFI_ERR_RANGE;
+  const VerWs w = verify_ws(kv, T);
+  if (!ws) return SFI_ERR_NULL;
+  if (ws_bytes < w.total) return SFI_ERR_WORKSPACE;
+  if (batch_n == 0) return SFI_OK;
+
+  VerifyLaunch a{};
+  a.kv = view;
+  a.seq_len = kv->seq_len;
+  a.batch_ids = batch_ids;
+  a.batch_n = batch_n;
+  a.B = kv->B; a.Hq = kv->Hq; a.Hkv = kv->Hkv; a.d = kv->d; a.G = G; a.T = T;
+  a.max_seq_len = kv->max_seq_len;
+  a.paged = paged;
+  a.row_mask = row_mask;
+  a.q = q;
+  a.out = out;
+  a.agg = agg;
+  a.ld = ld;
+  a.part_o = carve<float>(ws, w.o);
+  a.part_ml = carve<float>(ws, w.ml);
+  a.part_agg = carve<float>(ws, w.agg);
+  a.lld = kv->max_seq_len;
+  a.plan.chunk = w.chunk;
+  a.plan.splits = w.stride;
+  a.plan.stride = w.stride;
+  return launch_verify(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SFI_OK : SFI_ERR_HIP;
+}
+
+sfi_status sfi_schedule(const uint8_t *events, int32_t steps, int32_t B, int32_t budget,
+                        uint8_t *slow) {
+  if (!events || !slow) return SFI_ERR_NULL;
+  if (steps < 0 || B < 1) return SFI_ERR_SHAPE;
+  for (int32_t b = 0; b < B; ++b) {
+    int32_t run = 0;
+    for (int32_t s = 0; s < steps; ++s) {
+      const size_t i = (size_t)s * B + b;
+      const bool is_slow = s == 0 || events[i] != 0 || (budget >= 0 && run >= budget);
+      slow[i] = is_slow ? 1 : 0;
+      run = is_slow ? 0 : run + 1;
+    }
+  }
+  return SFI_OK;
+}
+
+const char *sfi_status_string(sfi_status s) {
+  switch (s) {
+    case SFI_OK: return "ok";
+    case SFI_ERR_NULL: return "required pointer is NULL";
+    case SFI_ERR_SHAPE: return "inconsistent or unsupported sizes";
+    case SFI_ERR_RANGE: return "parameter out of range";
+    case SFI_ERR_WORKSPACE: return "workspace too small";
+    case SFI_ERR_UNSUPPORTED: return "no kernel for this configuration";
+    case SFI_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+const char *sfi_version(void) { return "libsfi 0.1 gfx950"; }
+
+}  // extern "C"

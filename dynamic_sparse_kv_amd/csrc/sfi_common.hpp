@@ -1,0 +1,87 @@
+// Device helpers shared by the libsfi kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sfi {
+
+constexpr float kLog2e = 1.4426950408889634f;
+// Finite "minus infinity" for running maxima: exp2(kNegBig - x) == 0 for any
+// finite logit x, and kNegBig - kNegBig == 0 keeps empty states NaN-free.
+constexpr float kNegBig = -1.0e30f;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf_lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+
+// a.lo*b.lo + a.hi*b.hi + c: the bf16 products are exact in fp32.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over aligned groups of LPR (8 or 16) lanes; every lane of the group
+// receives the group's sum.  DPP row permutes only, so no LDS traffic.
+template <int LPR>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(LPR == 8 || LPR == 16, "group of 8 or 16 lanes");
+  x += dpp_f32<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_f32<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_f32<0x141>(x);  // row_half_mirror: the other quad of each 8
+  if constexpr (LPR == 16) x += dpp_f32<0x140>(x);  // row_mirror: other 8 of 16
+  return x;
+}
+
+// Location of one cached K/V row.
+struct KVView {
+  const uint16_t *k;
+  const uint16_t *v;
+  const int32_t *page_table;  // nullptr: contiguous [B][Hkv][cap][D]
+  int32_t page_shift;         // log2(page_size)
+  int32_t max_pages;
+  int32_t num_pages;
+  int32_t Hkv;
+  int32_t cap;
+};
+
+template <int D, bool PAGED>
+__device__ __forceinline__ size_t kv_row(const KVView &kv, int b, int g, int j) {
+  if constexpr (!PAGED) {
+    return ((size_t)(b * kv.Hkv + g) * (size_t)kv.cap + (size_t)j) * D;
+  } else {
+    int pg = kv.page_table[(size_t)b * kv.max_pages + (j >> kv.page_shift)];
+    pg = min(max(pg, 0), kv.num_pages - 1);
+    const int off = j & ((1 << kv.page_shift) - 1);
+    return ((((size_t)pg * kv.Hkv + g) << kv.page_shift) + (size_t)off) * D;
+  }
+}
+
+// Sequence id of batch entry i (nullptr list: identity); -1 when out of range.
+__device__ __forceinline__ int batch_seq(const int32_t *ids, int i, int B) {
+  const int b = ids ? ids[i] : i;
+  return (b >= 0 && b < B) ? b : -1;
+}
+
+// Cached length of sequence b clamped to [0, max_len].
+__device__ __forceinline__ int clamp_len(const int32_t *seq_len, int b, int max_len) {
+  return min(max(seq_len[b], 0), max_len);
+}
+
+// Order-preserving map float -> uint32 (larger float -> larger key).
+__device__ __forceinline__ uint32_t float_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint4 ldg16(const uint16_t *p) {
+  return *reinterpret_cast<const uint4 *>(p);
+}
+
+}  // namespace sfi

@@ -1,0 +1,103 @@
+// Host-side interface between the C ABI (sfi_abi.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "sfi_common.hpp"
+
+namespace sfi {
+
+// Rows per workgroup of the split-K kernels.
+constexpr int kMinSlowChunk = 256;
+constexpr int kMaxSlowChunk = 8192;
+constexpr int kFastChunk = 128;
+// Keys per workgroup of the evidence / prior passes.
+constexpr int kEvidChunk = 2048;
+constexpr int kStatChunk = 4096;
+
+// Plan of a split-K decode launch.
+struct SplitPlan {
+  int chunk;   // rows per workgroup
+  int splits;  // workgroups per (sequence, kv head) for the host bound
+  int stride;  // split stride of the partial buffers (>= splits)
+};
+
+int slow_chunk_for(int batch_n, int Hkv, int max_seq_len);
+
+struct AttnLaunch {
+  KVView kv;
+  const int32_t *seq_len;
+  const int32_t *batch_ids;
+  int batch_n;
+  int B, Hq, Hkv, d, G;
+  int max_len;
+  bool paged;
+  const uint16_t *q;
+  float *out;
+  // partials, indexed by sequence slot b: o [B][Hq][stride][d], ml [B][Hq][stride][2]
+  float *part_o;
+  float *part_ml;
+  SplitPlan plan;
+  // slow-step side outputs
+  float *logits;      // [B][Hkv][lld][G] (log2-scaled), workspace
+  int lld;
+  float *evidence;    // [B][Hkv][ld] or nullptr
+  float *key_norm;    // [B][Hkv][ld] or nullptr
+  int ld;
+  // fast step
+  const int32_t *sel_idx;
+  const int32_t *sel_count;
+  int sel_heads, sel_k, n_sink, window;
+};
+
+hipError_t launch_slow(const AttnLaunch &a, hipStream_t st);
+hipError_t launch_fast(const AttnLaunch &a, hipStream_t st);
+
+struct SelectLaunch {
+  int mode;
+  float lambda, norm_coef, pos_tau;
+  int n_sink, window, k;
+  const int32_t *batch_ids;
+  int batch_n;
+  const int32_t *seq_len;
+  int B, H, max_seq_len;
+  const float *score;
+  const float *key_norm;
+  int ld;
+  int32_t *sel_idx;
+  int32_t *sel_count;
+  float *sbuf;        // [B][H][ld]: fused_out or workspace
+  int sld;
+  double *stats;      // [B][H][nch][2]
+  double *wsum;       // [B][H][nch]
+  int nch;
+};
+
+hipError_t launch_select(const SelectLaunch &a, hipStream_t st);
+
+struct VerifyLaunch {
+  KVView kv;
+  const int32_t *seq_len;
+  const int32_t *batch_ids;
+  int batch_n;
+  int B, Hq, Hkv, d, G, T;
+  int max_seq_len;
+  bool paged;
+  uint32_t row_mask;
+  const uint16_t *q;
+  float *out;
+  float *agg;
+  int ld;
+  float *part_o;      // [B][T*Hq][stride][d]
+  float *part_ml;     // [B][T*Hq][stride][2]
+  float *part_agg;    // [B][Hkv][lld]
+  int lld;
+  SplitPlan plan;
+};
+
+hipError_t launch_verify(const VerifyLaunch &a, hipStream_t st);
+int verify_chunk_for(int batch_n, int Hkv, int max_seq_len);
+
+}  // namespace sfi

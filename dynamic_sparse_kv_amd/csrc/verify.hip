@@ -1,0 +1,353 @@
+// Multi-query verification attention with aggregated logits on gfx950 MFMA.
+//
+// Vegas (gist.science/it/paper/2602.07223), section 2: the verification pass
+// runs full attention for the gamma+1 verified tokens and its logits pick the
+// keys the next draft phase attends; section 2.A: the selection score of a
+// prefix key is its pre-softmax logit summed over the verified queries and
+// all query heads; section 2.B: Collect-2-Query sums only the first draft
+// query and the bonus query.  Logits are q.k/sqrt(d) (section 3: taken before
+// the softmax).
+//
+// One kv head serves R = (Hq/Hkv) * T query rows (32 for GQA 4:1 and T = 8),
+// so a 32-key tile is a dense 32 x 32 x d contraction: it runs on
+// v_mfma_f32_32x32x16_bf16 with keys on the M axis (S^T = K Q^T).  In that
+// orientation
+//   * the K tile is the A operand and is loaded straight from HBM into
+//     registers (lane: one key, 8 consecutive dims per k-step);
+//   * the accumulator gives every lane one query column and 16 keys, so the
+//     per-row softmax max/sum needs a single cross-half exchange;
+//   * the same accumulator, re-typed to bf16, is already the B operand of
+//     O^T = V^T P^T (P is split into a bf16 high part and a bf16 residual, so
+//     P V keeps ~16 mantissa bits);
+//   * V^T's A operand is gathered as 32-bit (even, odd dim) pairs, one dword
+//     per key per lane, and repacked into the even-dim and odd-dim m-tiles;
+//   * the aggregate is a masked sum of accumulator columns, done as a
+//     16-shuffle reduce-scatter inside each 32-lane half.
+// Each wave owns a contiguous key range and writes its own (m, Z, O) partial;
+// a finalize kernel merges them in a fixed order and sums the per-kv-head
+// aggregates over kv heads.
+#include "sfi_internal.hpp"
+
+namespace sfi {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kVThreads = 256;
+constexpr int kVWaves = kVThreads / 64;
+
+struct VArgs {
+  KVView kv;
+  int B, max_len;
+  const int32_t *seq_len;
+  const int32_t *batch_ids;
+  const uint16_t *q;  // [B][T][Hq][D]
+  int Hq, T;
+  uint32_t row_mask;
+  int wchunk;         // keys per wave
+  int stride;         // wave partials per row
+  float *part_o;      // [B][T*Hq][stride][D]
+  float *part_ml;     // [B][T*Hq][stride][2]
+  float *part_agg;    // [B][Hkv][lld]
+  int lld;
+  float qscale;       // log2(e)/sqrt(d)
+  float lscale;       // 1/sqrt(d)
+};
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) {
+  u32x4_t v = {u.x, u.y, u.z, u.w};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// Key (within a 32-key tile) held by accumulator element r of a lane in half hs.
+__device__ __forceinline__ int acc_key(int r, int hs) { return 8 * (r >> 2) + 4 * hs + (r & 3); }
+
+template <int D, int G, bool PAGED>
+__global__ __launch_bounds__(kVThreads) void verify_partial_kernel(VArgs a) {
+  constexpr int KK = D / 16;  // k-steps of Q K^T
+  constexpr int MT = D / 32;  // m-tiles of O^T
+  constexpr int NP = MT / 2;  // (even, odd) m-tile pairs
+
+  const int b = batch_seq(a.batch_ids, blockIdx.z, a.B);
+  if (b < 0) return;
+  const int g = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 31, hs = lane >> 5;
+  const int n = clamp_len(a.seq_len, b, a.max_len);
+  const int T = a.T;
+  const int R = G * T;
+  const int widx = blockIdx.x * kVWaves + wave;
+  const int k0 = widx * a.wchunk;
+  if (k0 >= n) return;
+  const int k1 = min(n, k0 + a.wchunk);
+
+  // Query column of this lane: verify row jt, head jh of the group.
+  const bool colv = col < R;
+  const int jt = colv ? col / G : 0;
+  const int jh = colv ? col % G : 0;
+  const int lim = n - T + jt;  // last visible key of row jt
+  const float amask = (colv && ((a.row_mask >> jt) & 1u)) ? 1.f : 0.f;
+  const int prefix = n - T;    // aggregate covers keys < prefix
+
+  bf16x8_t qb[KK];
+  {
+    const uint16_t *qp = a.q + (((size_t)b * T + jt) * a.Hq + g * G + jh) * D + 8 * hs;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const uint4 t = colv ? ldg16(qp + 16 * kk) : make_uint4(0, 0, 0, 0);
+      qb[kk] = as_bf16x8(t);
+    }
+  }
+
+  f32x16_t o[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[mt][r] = 0.f;
+  float m = kNegBig, z = 0.f;
+  const size_t aggrow = ((size_t)b * a.kv.Hkv + g) * a.lld;
+
+  for (int kb = k0; kb < k1; kb += 32) {
+    // A operand of Q K^T: key kb+col, dims 16kk + 8hs .. +8.
+    bf16x8_t ka[KK];
+    {
+      const int key = kb + col;
+      if (key < k1) {
+        const uint16_t *kp = a.kv.k + kv_row<D, PAGED>(a.kv, b, g, key) + 8 * hs;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) ka[kk] = as_bf16x8(ldg16(kp + 16 * kk));
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) ka[kk] = as_bf16x8(make_uint4(0, 0, 0, 0));
+      }
+    }
+    // V (even, odd)-dim dword of each key this lane needs for O^T's A operand.
+    uint32_t vw[2][NP][8];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int key = kb + 16 * ks + acc_key(e, hs);
+        if (key < k1) {
+          const uint16_t *vp = a.kv.v + kv_row<D, PAGED>(a.kv, b, g, key) + 2 * col;
+#pragma unroll
+          for (int p = 0; p < NP; ++p) vw[ks][p][e] = *reinterpret_cast<const uint32_t *>(vp + 64 * p);
+        } else {
+#pragma unroll
+          for (int p = 0; p < NP; ++p) vw[ks][p][e] = 0u;
+        }
+      }
+    }
+
+    f32x16_t s;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], qb[kk], s, 0, 0, 0);
+
+    // Aggregate: masked column sum, reduce-scattered over the 32 lanes of the half.
+    {
+      float v[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) v[r] = s[r] * amask;
+      const bool b4 = (col & 16) != 0, b3 = (col & 8) != 0, b2 = (col & 4) != 0, b1 = (col & 2) != 0;
+      float w8[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float keep = b4 ? v[8 + i] : v[i];
+        const float send = b4 ? v[i] : v[8 + i];
+        w8[i] = keep + __shfl_xor(send, 16);
+      }
+      float w4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float keep = b3 ? w8[4 + i] : w8[i];
+        const float send = b3 ? w8[i] : w8[4 + i];
+        w4[i] = keep + __shfl_xor(send, 8);
+      }
+      float w2[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const float keep = b2 ? w4[2 + i] : w4[i];
+        const float send = b2 ? w4[i] : w4[2 + i];
+        w2[i] = keep + __shfl_xor(send, 4);
+      }
+      float w1 = (b1 ? w2[1] : w2[0]) + __shfl_xor(b1 ? w2[0] : w2[1], 2);
+      w1 += __shfl_xor(w1, 1);
+      const int r = 8 * (int)b4 + 4 * (int)b3 + 2 * (int)b2 + (int)b1;
+      const int key = kb + acc_key(r, hs);
+      if ((col & 1) == 0 && key < k1 && key < prefix) a.part_agg[aggrow + key] = w1 * a.lscale;
+    }
+
+    // Online softmax of column col over this tile (16 keys here, 16 in lane^32).
+    float sv[16];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = kb + acc_key(r, hs);
+      const bool ok = key < k1 && key <= lim;
+      sv[r] = ok ? s[r] * a.qscale : -INFINITY;
+      mx = fmaxf(mx, sv[r]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mn = fmaxf(m, mx);
+    const float sc = exp2f(m - mn);
+    m = mn;
+    z *= sc;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[mt][r] *= sc;
+
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8_t phi, plo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = exp2f(sv[8 * ks + e] - mn);
+        z += p;
+        const float ph = __uint_as_float(__float_as_uint(p) & 0xffff0000u);
+        phi[e] = (__bf16)ph;
+        plo[e] = (__bf16)(p - ph);
+      }
+#pragma unroll
+      for (int pp = 0; pp < NP; ++pp) {
+        u32x4_t ev, od;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t w0 = vw[ks][pp][2 * i], w1 = vw[ks][pp][2 * i + 1];
+          ev[i] = (w0 & 0xffffu) | (w1 << 16);
+          od[i] = (w0 >> 16) | (w1 & 0xffff0000u);
+        }
+        const bf16x8_t ae = __builtin_bit_cast(bf16x8_t, ev);
+        const bf16x8_t ao = __builtin_bit_cast(bf16x8_t, od);
+        o[2 * pp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ae, phi, o[2 * pp], 0, 0, 0);
+        o[2 * pp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ae, plo, o[2 * pp], 0, 0, 0);
+        o[2 * pp + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, phi, o[2 * pp + 1], 0, 0, 0);
+        o[2 * pp + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, plo, o[2 * pp + 1], 0, 0, 0);
+      }
+    }
+  }
+
+  const float zt = z + __shfl_xor(z, 32);
+  if (colv) {
+    const size_t slot = ((size_t)b * T * a.Hq + (size_t)jt * a.Hq + g * G + jh) * a.stride + widx;
+    float *op = a.part_o + slot * D;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) op[64 * (mt >> 1) + 2 * acc_key(r, hs) + (mt & 1)] = o[mt][r];
+    if (hs == 0) {
+      a.part_ml[slot * 2 + 0] = m;
+      a.part_ml[slot * 2 + 1] = zt;
+    }
+  }
+}
+
+struct VFinal {
+  int B, max_len;
+  const int32_t *seq_len;
+  const int32_t *batch_ids;
+  int Hq, Hkv, T, wchunk, stride;
+  const float *part_o;
+  const float *part_ml;
+  float *out;
+  const float *part_agg;
+  int lld;
+  float *agg;
+  int ld;
+};
+
+// grid.x = T*Hq rows, one block of D threads each: fixed-order merge.
+template <int D>
+__global__ __launch_bounds__(D) void verify_combine_kernel(VFinal a) {
+  const int b = batch_seq(a.batch_ids, blockIdx.y, a.B);
+  if (b < 0) return;
+  const int row = blockIdx.x;  // t*Hq + h
+  const int n = clamp_len(a.seq_len, b, a.max_len);
+  const int S = (n + a.wchunk - 1) / a.wchunk;
+  const size_t base = ((size_t)b * a.T * a.Hq + row) * a.stride;
+  float M = kNegBig;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, a.part_ml[(base + s) * 2]);
+  float Z = 0.f, o = 0.f;
+  const int e = threadIdx.x;
+  for (int s = 0; s < S; ++s) {
+    const float w = exp2f(a.part_ml[(base + s) * 2] - M);
+    Z = fmaf(a.part_ml[(base + s) * 2 + 1], w, Z);
+    o = fmaf(a.part_o[(base + s) * D + e], w, o);
+  }
+  a.out[((size_t)b * a.T * a.Hq + row) * D + e] = (Z > 0.f) ? o / Z : 0.f;
+}
+
+// agg[b][i] = sum over kv heads (fixed order) of the per-head partials, i < n - T.
+__global__ __launch_bounds__(256) void verify_agg_kernel(VFinal a) {
+  const int b = batch_seq(a.batch_ids, blockIdx.y, a.B);
+  if (b < 0) return;
+  const int n = clamp_len(a.seq_len, b, a.max_len);
+  const int P = n - a.T;
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < P; i += gridDim.x * 256) {
+    float s = 0.f;
+    for (int g = 0; g < a.Hkv; ++g) s += a.part_agg[((size_t)b * a.Hkv + g) * a.lld + i];
+    a.agg[(size_t)b * a.ld + i] = s;
+  }
+}
+
+template <int D, int G, bool PAGED>
+hipError_t verify_t(const VerifyLaunch &L, hipStream_t st) {
+  VArgs a{};
+  a.B = L.B; a.max_len = L.max_seq_len;
+  a.kv = L.kv; a.seq_len = L.seq_len; a.batch_ids = L.batch_ids; a.q = L.q;
+  a.Hq = L.Hq; a.T = L.T; a.row_mask = L.row_mask;
+  a.wchunk = L.plan.chunk; a.stride = L.plan.stride;
+  a.part_o = L.part_o; a.part_ml = L.part_ml; a.part_agg = L.part_agg; a.lld = L.lld;
+  a.qscale = kLog2e / sqrtf((float)D);
+  a.lscale = 1.0f / sqrtf((float)D);
+  const int wgs = (L.plan.splits + kVWaves - 1) / kVWaves;
+  hipLaunchKernelGGL((verify_partial_kernel<D, G, PAGED>), dim3(wgs, L.Hkv, L.batch_n),
+                     dim3(kVThreads), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  VFinal f{};
+  f.B = L.B; f.max_len = L.max_seq_len;
+  f.seq_len = L.seq_len; f.batch_ids = L.batch_ids; f.Hq = L.Hq; f.Hkv = L.Hkv; f.T = L.T;
+  f.wchunk = L.plan.chunk; f.stride = L.plan.stride; f.part_o = L.part_o; f.part_ml = L.part_ml;
+  f.out = L.out; f.part_agg = L.part_agg; f.lld = L.lld; f.agg = L.agg; f.ld = L.ld;
+  hipLaunchKernelGGL((verify_combine_kernel<D>), dim3(L.T * L.Hq, L.batch_n), dim3(D), 0, st, f);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int aggb = min(1024, (L.max_seq_len + 255) / 256);
+  hipLaunchKernelGGL(verify_agg_kernel, dim3(aggb > 0 ? aggb : 1, L.batch_n), dim3(256), 0, st, f);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int verify_chunk_for(int batch_n, int Hkv, int max_seq_len) {
+  // Keys per wave: long enough that a wave's (m, Z, O) partial (R x (d+2)
+  // floats) stays a few percent of the K/V bytes it streams.
+  (void)batch_n;
+  (void)Hkv;
+  if (max_seq_len >= 32768) return 2048;
+  if (max_seq_len >= 8192) return 1024;
+  return 256;
+}
+
+hipError_t launch_verify(const VerifyLaunch &L, hipStream_t st) {
+  const bool pg = L.paged;
+  switch (L.d * 16 + L.G) {
+    case 64 * 16 + 1: return pg ? verify_t<64, 1, true>(L, st) : verify_t<64, 1, false>(L, st);
+    case 64 * 16 + 2: return pg ? verify_t<64, 2, true>(L, st) : verify_t<64, 2, false>(L, st);
+    case 64 * 16 + 4: return pg ? verify_t<64, 4, true>(L, st) : verify_t<64, 4, false>(L, st);
+    case 64 * 16 + 8: return pg ? verify_t<64, 8, true>(L, st) : verify_t<64, 8, false>(L, st);
+    case 128 * 16 + 1: return pg ? verify_t<128, 1, true>(L, st) : verify_t<128, 1, false>(L, st);
+    case 128 * 16 + 2: return pg ? verify_t<128, 2, true>(L, st) : verify_t<128, 2, false>(L, st);
+    case 128 * 16 + 4: return pg ? verify_t<128, 4, true>(L, st) : verify_t<128, 4, false>(L, st);
+    case 128 * 16 + 8: return pg ? verify_t<128, 8, true>(L, st) : verify_t<128, 8, false>(L, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace sfi

@@ -1,0 +1,183 @@
+"""Host driver of the decode loop: buffers, schedule, per-step launches.
+
+This is the orchestration layer above the C ABI (the schedule of the
+Slow-Fast Inference pages, technical summary section 3.A: fast steps by
+default, a slow step at a semantic boundary or once the reuse budget is
+spent).  It owns device buffers (torch tensors used as plain memory), stages
+every per-step argument on the device up front, and issues libsfi calls on a
+stream, so a whole run can also be captured into one HIP graph.  It computes
+nothing itself.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import sfi
+
+
+def _dev_i32(x, device):
+    return torch.as_tensor(np.ascontiguousarray(x, dtype=np.int32), device=device)
+
+
+class DecodePlan:
+    """Per-step device arguments of one run.
+
+    slow[s, b] (host bool) says whether sequence b takes a slow step at step
+    s.  seq_len[s, b] = ctx_b + s + 1 keys are visible at step s.
+    """
+
+    def __init__(self, slow: np.ndarray, ctx: np.ndarray, device):
+        steps, B = slow.shape
+        self.steps, self.B = steps, B
+        self.slow = slow.astype(bool)
+        lens = ctx[None, :].astype(np.int64) + np.arange(steps)[:, None] + 1
+        self.seq_len_host = lens.astype(np.int32)
+        self.seq_len = _dev_i32(lens, device)               # [steps][B]
+        slow_ids = np.zeros((steps, B), dtype=np.int32)
+        fast_ids = np.zeros((steps, B), dtype=np.int32)
+        self.n_slow = np.zeros(steps, dtype=np.int64)
+        self.n_fast = np.zeros(steps, dtype=np.int64)
+        for s in range(steps):
+            si = np.nonzero(self.slow[s])[0]
+            fi = np.nonzero(~self.slow[s])[0]
+            slow_ids[s, : len(si)] = si
+            fast_ids[s, : len(fi)] = fi
+            self.n_slow[s] = len(si)
+            self.n_fast[s] = len(fi)
+        self.slow_ids = _dev_i32(slow_ids, device)
+        self.fast_ids = _dev_i32(fast_ids, device)
+
+
+class SFIDecoder:
+    """Slow/fast decode of one attention layer over a resident KV cache."""
+
+    def __init__(self, K, V, Hq: int, max_len: int, *, n_sink: int, window: int, k: int,
+                 lam: float, norm_coef: float = 0.5, pos_tau: float = 1024.0,
+                 page_table=None, page_size: int = 0, keep_fused: bool = False):
+        dev = K.device
+        self.dev = dev
+        self.K, self.V = K, V
+        self.Hq = Hq
+        self.page_table = page_table
+        if page_table is None:
+            B, Hkv, cap, d = K.shape
+        else:
+            Hkv, d = K.shape[1], K.shape[3]
+            B = page_table.shape[0]
+        self.B, self.Hkv, self.d = B, Hkv, d
+        self.max_len = int(max_len)
+        self.n_sink, self.window, self.k = n_sink, window, k
+        self._dummy_len = torch.full((B,), self.max_len, dtype=torch.int32, device=dev)
+        self.kv = sfi.make_kv(K, V, self._dummy_len, Hq, self.max_len, page_table, page_size)
+        self.params = sfi.select_params(sfi.SFI_SCORE_FUSED, lam, k, n_sink, window, norm_coef, pos_tau)
+        self.ld = self.max_len
+        f32 = dict(dtype=torch.float32, device=dev)
+        self.out = torch.zeros((B, Hq, d), **f32)
+        self.evidence = torch.zeros((B, Hkv, self.ld), **f32)
+        self.key_norm = torch.zeros((B, Hkv, self.ld), **f32)
+        self.fused = torch.zeros((B, Hkv, self.ld), **f32) if keep_fused else None
+        self.sel_idx = torch.full((B, Hkv, k), -1, dtype=torch.int32, device=dev)
+        self.sel_count = torch.zeros((B, Hkv), dtype=torch.int32, device=dev)
+        u8 = dict(dtype=torch.uint8, device=dev)
+        self.ws_slow_bytes = sfi.sfi_slow_workspace_bytes(self.kv)
+        self.ws_sel_bytes = sfi.sfi_select_workspace_bytes(B, Hkv, self.max_len)
+        self.ws_fast_bytes = sfi.sfi_fast_workspace_bytes(self.kv, k, n_sink, window)
+        self.ws_slow = torch.empty(self.ws_slow_bytes, **u8)
+        self.ws_sel = torch.empty(self.ws_sel_bytes, **u8)
+        self.ws_fast = torch.empty(self.ws_fast_bytes, **u8)
+
+    # -- single calls -------------------------------------------------------
+    def slow(self, q, seq_len, batch_ids, batch_n: int, stream=None, select: bool = True):
+        """Dense step + evidence for the listed sequences, then the selector."""
+        self.kv.seq_len = seq_len.data_ptr() if torch.is_tensor(seq_len) else seq_len
+        sfi.sfi_slow_step(self.kv, batch_ids, batch_n, q, self.out, self.evidence, self.key_norm,
+                          self.ld, self.ws_slow, self.ws_slow_bytes, stream)
+        if select:
+            self.slow_select_only(self.kv.seq_len, batch_ids, batch_n, stream)
+
+    def slow_select_only(self, seq_len, batch_ids, batch_n: int, stream=None):
+        """The selector over the evidence and norms of the last slow step."""
+        ptr = seq_len.data_ptr() if torch.is_tensor(seq_len) else seq_len
+        sfi.sfi_select(self.params, batch_ids, batch_n, ptr, self.B, self.Hkv, self.max_len,
+                       self.evidence, self.key_norm, self.ld, self.sel_idx, self.sel_count,
+                       self.fused, self.ws_sel, self.ws_sel_bytes, stream)
+
+    def dense(self, q, seq_len, batch_ids, batch_n: int, stream=None):
+        """Plain dense attention (no evidence): the full-KV comparator."""
+        self.kv.seq_len = seq_len.data_ptr() if torch.is_tensor(seq_len) else seq_len
+        sfi.sfi_slow_step(self.kv, batch_ids, batch_n, q, self.out, None, None, self.ld,
+                          self.ws_slow, self.ws_slow_bytes, stream)
+
+    def fast(self, q, seq_len, batch_ids, batch_n: int, stream=None):
+        self.kv.seq_len = seq_len.data_ptr() if torch.is_tensor(seq_len) else seq_len
+        sfi.sfi_fast_step(self.kv, batch_ids, batch_n, q, self.sel_idx, self.sel_count, self.Hkv,
+                          self.k, self.n_sink, self.window, self.out, self.ws_fast,
+                          self.ws_fast_bytes, stream)
+
+    # -- one decode step of a planned run ------------------------------------
+    def step(self, plan: DecodePlan, s: int, q_steps, stream=None):
+        """Decode step s: q_steps is the device tensor [steps][B][Hq][d]."""
+        q = q_steps[s]
+        sl = plan.seq_len[s]
+        ns, nf = int(plan.n_slow[s]), int(plan.n_fast[s])
+        if ns:
+            self.slow(q, sl, plan.slow_ids[s], ns, stream)
+        if nf:
+            self.fast(q, sl, plan.fast_ids[s], nf, stream)
+
+
+class VegasDecoder:
+    """Verify -> select -> draft iterations over a resident KV cache."""
+
+    def __init__(self, K, V, Hq: int, max_len: int, T: int, *, n_sink: int, window: int, k: int,
+                 page_table=None, page_size: int = 0):
+        dev = K.device
+        self.dev = dev
+        self.Hq, self.T = Hq, T
+        if page_table is None:
+            B, Hkv, cap, d = K.shape
+        else:
+            Hkv, d = K.shape[1], K.shape[3]
+            B = page_table.shape[0]
+        self.B, self.Hkv, self.d = B, Hkv, d
+        self.max_len = int(max_len)
+        self.n_sink, self.window, self.k = n_sink, window, k
+        self._dummy_len = torch.full((B,), self.max_len, dtype=torch.int32, device=dev)
+        self.kv = sfi.make_kv(K, V, self._dummy_len, Hq, self.max_len, page_table, page_size)
+        self.params = sfi.select_params(sfi.SFI_SCORE_RAW, 0.0, k, n_sink, window)
+        self.ld = self.max_len
+        f32 = dict(dtype=torch.float32, device=dev)
+        self.vout = torch.zeros((B, T, Hq, d), **f32)
+        self.out = torch.zeros((B, Hq, d), **f32)
+        self.agg = torch.zeros((B, self.ld), **f32)
+        self.sel_idx = torch.full((B, 1, k), -1, dtype=torch.int32, device=dev)
+        self.sel_count = torch.zeros((B, 1), dtype=torch.int32, device=dev)
+        u8 = dict(dtype=torch.uint8, device=dev)
+        self.ws_ver_bytes = sfi.sfi_verify_workspace_bytes(self.kv, T)
+        self.ws_sel_bytes = sfi.sfi_select_workspace_bytes(B, 1, self.max_len)
+        self.ws_fast_bytes = sfi.sfi_fast_workspace_bytes(self.kv, k, n_sink, window)
+        self.ws_ver = torch.empty(self.ws_ver_bytes, **u8)
+        self.ws_sel = torch.empty(self.ws_sel_bytes, **u8)
+        self.ws_fast = torch.empty(self.ws_fast_bytes, **u8)
+
+    def verify(self, q_rows, seq_len, row_mask: int, batch_ids=None, batch_n=None, stream=None):
+        """q_rows [B][T][Hq][d] bf16; seq_len counts the T verified rows."""
+        self.kv.seq_len = seq_len.data_ptr() if torch.is_tensor(seq_len) else seq_len
+        bn = self.B if batch_n is None else batch_n
+        sfi.sfi_verify_aggregate(self.kv, batch_ids, bn, q_rows, self.T, row_mask, self.vout,
+                                 self.agg, self.ld, self.ws_ver, self.ws_ver_bytes, stream)
+
+    def select(self, seq_len, batch_ids=None, batch_n=None, stream=None):
+        ptr = seq_len.data_ptr() if torch.is_tensor(seq_len) else seq_len
+        bn = self.B if batch_n is None else batch_n
+        sfi.sfi_select(self.params, batch_ids, bn, ptr, self.B, 1, self.max_len, self.agg, None,
+                       self.ld, self.sel_idx, self.sel_count, None, self.ws_sel, self.ws_sel_bytes,
+                       stream)
+
+    def draft(self, q, seq_len, batch_ids=None, batch_n=None, stream=None):
+        self.kv.seq_len = seq_len.data_ptr() if torch.is_tensor(seq_len) else seq_len
+        bn = self.B if batch_n is None else batch_n
+        sfi.sfi_fast_step(self.kv, batch_ids, bn, q, self.sel_idx, self.sel_count, 1, self.k,
+                          self.n_sink, self.window, self.out, self.ws_fast, self.ws_fast_bytes,
+                          stream)

@@ -1,0 +1,195 @@
+/*
+ * sfi.h -- C ABI of libsfi: slow-fast decode attention (SFI) and
+ * verification-guided sparse selection (Vegas) on AMD Instinct MI355X (gfx950).
+ *
+ * Sources:
+ *   [SFI]   "Slow-Fast Inference: Training-Free Inference Acceleration via
+ *           Within-Sentence Support Stability" (gist.science/it|pt|ko/paper/
+ *           2603.12038): technical summary, section 1 (every decode step
+ *           attends the whole cached history), section 3.A / 2.A (fast steps
+ *           over sinks + recent window + selected memory; slow steps with
+ *           dense attention at boundaries or when the reuse budget is spent),
+ *           section 3.B / 2.B (selector: evidence from the slow step's
+ *           attention, prior from key norms and positions, closed-form
+ *           reverse-KL fusion s = (1-lam) f + lam r, Top-K).
+ *   [Vegas] "Vegas: Decodifica Auto-Speculativa con Attenzione Sparsa Guidata
+ *           dalla Verifica" (gist.science/it/paper/2602.07223): section 2
+ *           (verify with full attention, select from its logits, draft with
+ *           sparse attention), section 2.A (argmax over |T| = k of the
+ *           logits summed over the verified queries and all query heads),
+ *           section 2.B (Collect-2-Query), section 3 (pre-softmax logits).
+ *
+ * Conventions shared by every call:
+ *   - Pointers are DEVICE pointers unless marked [host].  The caller owns all
+ *     memory, including the workspace `ws` (size from the matching
+ *     *_workspace_bytes call).  No call allocates, frees or synchronises.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
+ *     null stream) and the call returns.  Argument errors are reported
+ *     synchronously, before anything is enqueued.  SFI_ERR_HIP means a launch
+ *     was rejected; faults inside kernels surface at the caller's next
+ *     synchronisation.
+ *   - K/V/Q are bf16 bit patterns (uint16_t).  Outputs are fp32.  Logits are
+ *     q.k / sqrt(d); query head h reads kv head h / (Hq / Hkv).
+ *   - A batch is a list of sequence ids (`batch_ids`, int32, device, length
+ *     `batch_n`; NULL means 0..batch_n-1).  Results are written at each
+ *     sequence's own slot b, so full-batch buffers can be shared by calls
+ *     that touch disjoint subsets.  Ids must be distinct and < B.
+ *   - Calls on one stream run in order; calls that share a workspace must be
+ *     ordered by the caller.  Results are bitwise repeatable (no floating-
+ *     point atomics; reductions run in a fixed order).
+ */
+#ifndef SFI_H
+#define SFI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SFI_OK = 0,
+  SFI_ERR_NULL = -1,        /* a required pointer is NULL */
+  SFI_ERR_SHAPE = -2,       /* inconsistent or unsupported sizes */
+  SFI_ERR_RANGE = -3,       /* a parameter outside its documented range */
+  SFI_ERR_WORKSPACE = -4,   /* ws_bytes smaller than required */
+  SFI_ERR_UNSUPPORTED = -5, /* valid request this build has no kernel for */
+  SFI_ERR_HIP = -6          /* the HIP runtime rejected a launch */
+} sfi_status;
+
+/* The KV cache of one attention layer.
+ *   Contiguous (page_table == NULL): k, v are [B][Hkv][cap][d].
+ *   Paged: k, v are a pool [num_pages][Hkv][page_size][d]; logical row j of
+ *   sequence b lives in page page_table[b * max_pages + j / page_size] at
+ *   offset j % page_size.
+ * seq_len[b] (device) is the number of cached keys of sequence b, including
+ * the token(s) being decoded.  max_seq_len [host] bounds seq_len over every
+ * sequence a call touches; it sizes grids and workspaces.  Device values are
+ * trusted only within bounds: seq_len is clamped to [0, max_seq_len], page ids
+ * to [0, num_pages), and listed sequence ids outside [0, B) are skipped, so a
+ * corrupt argument yields wrong numbers, never an out-of-bounds access. */
+typedef struct sfi_kv {
+  const uint16_t *k;
+  const uint16_t *v;
+  const int32_t *page_table;  /* NULL => contiguous */
+  int32_t page_size;          /* paged only: power of two, 16..1024 */
+  int32_t max_pages;          /* paged only: row stride of page_table */
+  int32_t num_pages;          /* paged only: pages in the pool */
+  const int32_t *seq_len;     /* [B] */
+  int32_t B, Hq, Hkv, d;      /* d in {64, 128}; Hq % Hkv == 0; Hq/Hkv in {1,2,4,5,8} */
+  int32_t cap;                /* contiguous only: rows per (b, kv head) */
+  int32_t max_seq_len;        /* [host] */
+} sfi_kv;
+
+enum { SFI_SCORE_FUSED = 0, SFI_SCORE_RAW = 1 };
+
+/* Selector parameters.  FUSED: score = evidence f, prior r from key norms
+ * and positions, s = (1-lambda) f + lambda r  [SFI 3.B; fusion closed form in
+ * the Korean summary, section 2.B].  RAW: the scores are ranked as given
+ * (Vegas aggregated logits). */
+typedef struct sfi_select_params {
+  int32_t mode;       /* SFI_SCORE_FUSED or SFI_SCORE_RAW */
+  float lambda;       /* [0, 1] */
+  float norm_coef;    /* prior: weight of the standardised key norm (0.5) */
+  float pos_tau;      /* prior: recency time constant in tokens (1024), > 0 */
+  int32_t n_sink;     /* >= 0 */
+  int32_t window;     /* >= 0 */
+  int32_t k;          /* > 0: capacity of each index list */
+} sfi_select_params;
+
+/* ---------------------------------------------------------------- sizes */
+
+/* Workspace for sfi_slow_step on this cache (valid for any batch_n <= B). */
+size_t sfi_slow_workspace_bytes(const sfi_kv *kv);
+/* Workspace for sfi_select over B x H score rows of max length max_seq_len. */
+size_t sfi_select_workspace_bytes(int32_t B, int32_t H, int32_t max_seq_len);
+/* Workspace for sfi_fast_step with index lists of capacity sel_k. */
+size_t sfi_fast_workspace_bytes(const sfi_kv *kv, int32_t sel_k, int32_t n_sink, int32_t window);
+/* Workspace for sfi_verify_aggregate with T query rows per sequence. */
+size_t sfi_verify_workspace_bytes(const sfi_kv *kv, int32_t T);
+
+/* ---------------------------------------------------------------- calls */
+
+/* Slow step [SFI 3.A slow steps, 3.B evidence]: dense attention of one decode
+ * query per sequence over all seq_len[b] keys.
+ *   q         [B][Hq][d] bf16; row b is used for each listed sequence b.
+ *   out       [B][Hq][d] fp32: softmax(q K^T / sqrt(d)) V per head.
+ *   evidence  [B][Hkv][ld] fp32 or NULL: f[b][g][j], j < seq_len[b], the
+ *             softmax probability of key j averaged over the Hq/Hkv query
+ *             heads of kv head g (sums to 1).  NULL => plain dense attention.
+ *   key_norm  [B][Hkv][ld] fp32 or NULL: Euclidean norm of key j.
+ *   ld        >= max_seq_len when evidence or key_norm is given.
+ * Errors: NULL/SHAPE/RANGE/WORKSPACE before launch, HIP on launch failure. */
+sfi_status sfi_slow_step(const sfi_kv *kv, const int32_t *batch_ids, int32_t batch_n,
+                         const uint16_t *q, float *out, float *evidence, float *key_norm,
+                         int32_t ld, void *ws, size_t ws_bytes, void *stream);
+
+/* Selector [SFI 3.B; Vegas 2.A]: per listed sequence b and head row h < H,
+ * pick the min(k, |C|) best keys of C = [n_sink, seq_len[b] - window) by
+ * (score desc, index asc) and write them ascending to
+ * sel_idx[b][h][0..count), padding to k with -1; sel_count[b][h] = count.
+ *   FUSED: score = evidence f [B][H][ld], key_norm [B][H][ld] (both over
+ *          j < seq_len[b]).  Prior r_j = w_j / sum w, w_j = exp(-norm_coef
+ *          z_j) (1 + exp(-(t - j) / pos_tau)), z_j = key norm standardised by
+ *          its population mean and std over j < seq_len[b] (z = 0 if the std
+ *          is 0), t = seq_len[b] - 1.  s = (1 - lambda) f + lambda r is ranked
+ *          and, if fused_out != NULL, written to fused_out[b][h][j] for
+ *          j < seq_len[b].
+ *   RAW:   score [B][H][ld] is ranked as is (finite values; key_norm,
+ *          lambda, norm_coef, pos_tau and fused_out are ignored).  Scores
+ *          must be defined on all of C.
+ * H is Hkv for per-head memories (SFI) or 1 for one head-shared list (Vegas).
+ * NaN scores give an unspecified (but in-range) selection. */
+sfi_status sfi_select(const sfi_select_params *p, const int32_t *batch_ids, int32_t batch_n,
+                      const int32_t *seq_len, int32_t B, int32_t H, int32_t max_seq_len,
+                      const float *score, const float *key_norm, int32_t ld,
+                      int32_t *sel_idx, int32_t *sel_count, float *fused_out,
+                      void *ws, size_t ws_bytes, void *stream);
+
+/* Fast step [SFI 3.A fast steps; Vegas 2 drafting]: attention of one decode
+ * query per sequence over the fast set of its kv head g, with n = seq_len[b]:
+ *   [0, min(n_sink, n))  U  [max(n_sink, n - window), n)  U
+ *   { sel_idx[b][hs][i] : i < sel_count[b][hs], n_sink <= j < n - window }
+ * where hs = g if sel_heads == Hkv, hs = 0 if sel_heads == 1 (head-shared).
+ * Entries outside that range (including -1 padding and keys now inside the
+ * window) are skipped.  The listed entries of one list must be distinct.
+ *   sel_idx [B][sel_heads][sel_k] int32, sel_count [B][sel_heads] int32.
+ *   out     [B][Hq][d] fp32. */
+sfi_status sfi_fast_step(const sfi_kv *kv, const int32_t *batch_ids, int32_t batch_n,
+                         const uint16_t *q, const int32_t *sel_idx, const int32_t *sel_count,
+                         int32_t sel_heads, int32_t sel_k, int32_t n_sink, int32_t window,
+                         float *out, void *ws, size_t ws_bytes, void *stream);
+
+/* Verification with aggregated logits [Vegas 2, 2.A, 2.B, 3]: T query rows
+ * per sequence; row t sits at position n - T + t (n = seq_len[b], which
+ * already counts the T rows) and attends keys [0, n - T + t].
+ *   q        [B][T][Hq][d] bf16.
+ *   out      [B][T][Hq][d] fp32.
+ *   agg      [B][ld] fp32: agg[b][i] = sum over rows t in row_mask and all
+ *            Hq heads of the logit of key i, for i < n - T (the prefix).
+ *   row_mask bit t selects row t: (1 << T) - 1 for all rows,
+ *            1 | 1 << (T - 1) for Collect-2-Query.  Nonzero, < (1 << T).
+ *   1 <= T and T * Hq / Hkv <= 32; ld >= max_seq_len - T. */
+sfi_status sfi_verify_aggregate(const sfi_kv *kv, const int32_t *batch_ids, int32_t batch_n,
+                                const uint16_t *q, int32_t T, uint32_t row_mask, float *out,
+                                float *agg, int32_t ld, void *ws, size_t ws_bytes, void *stream);
+
+/* Slow/fast schedule [SFI 3.A: slow at a semantic boundary or when the reuse
+ * budget is spent] -- host only.  events [steps][B] [host] marks boundaries
+ * (or any other slow trigger); slow [steps][B] [host] receives 1 where the
+ * step is slow: step 0, every event, and every step that follows `budget`
+ * consecutive fast steps (budget < 0: no budget). */
+sfi_status sfi_schedule(const uint8_t *events, int32_t steps, int32_t B, int32_t budget,
+                        uint8_t *slow);
+
+/* Human-readable name of a status [host]. */
+const char *sfi_status_string(sfi_status s);
+
+/* Library version string [host]. */
+const char *sfi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SFI_H */

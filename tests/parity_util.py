@@ -1,0 +1,54 @@
+"""Helpers shared by the GPU parity tests: error measures and selection checks.
+
+Tolerances:
+  * attention outputs: per output row (sequence, head[, verify row]),
+    max|x - y| / max|y| <= 2e-3 (bf16 inputs, fp32 accumulation);
+  * evidence f and fused score s: per row max|x - y| / max|y| <= 1e-4 (fp32
+    logits carry ~1e-6 relative error; exp and the normaliser add a few ulp);
+  * key norms: relative 1e-5;
+  * selections: identical index sets except for keys whose oracle score lies
+    within 1e-5 relative of the oracle's k-th score (the near-tie band); the
+    number of such keys is returned so tests can report it.
+"""
+import numpy as np
+
+from oracle import sfi_oracle as O
+
+OUT_TOL = 2e-3
+EVID_TOL = 1e-4
+NORM_TOL = 1e-5
+TIE_BAND = 1e-5
+
+
+def row_rel_err(x, y):
+    """max over rows of max|x - y| / max|y| (last axis = row)."""
+    x = np.asarray(x, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64)
+    num = np.abs(x - y).max(axis=-1)
+    den = np.maximum(np.abs(y).max(axis=-1), 1e-30)
+    return float((num / den).max())
+
+
+def check_selection(gpu_idx, gpu_cnt, score, lo, hi, k):
+    """Compare one GPU index list with the oracle's Top-K of ``score``.
+
+    Returns the number of near-tie keys that differ.  Asserts that the GPU
+    list is ascending, unique, inside [lo, hi), padded with -1, of the right
+    length, and that every difference lies in the near-tie band.
+    """
+    gpu_idx = np.asarray(gpu_idx)
+    want = O.topk_indices(score, lo, hi, k)
+    assert int(gpu_cnt) == len(want), (int(gpu_cnt), len(want))
+    got = gpu_idx[: int(gpu_cnt)]
+    assert np.all(gpu_idx[int(gpu_cnt):] == -1)
+    if len(got):
+        assert np.all(np.diff(got) > 0), "not ascending / not unique"
+        assert got.min() >= lo and got.max() < hi
+    diff = np.setxor1d(got, want)
+    if diff.size == 0:
+        return 0
+    kth = O.kth_score(score, lo, hi, k)
+    assert kth is not None
+    band = np.abs(np.asarray(score)[diff] - kth) <= TIE_BAND * abs(kth)
+    assert band.all(), f"selection differs outside the near-tie band: {diff[~band][:10]}"
+    return int(diff.size)

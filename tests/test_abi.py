@@ -1,0 +1,159 @@
+"""The C ABI without a GPU: exports, host-only calls, argument validation.
+
+Every compute call made here fails validation before anything is enqueued
+(or has batch_n == 0), so no kernel is ever launched from these tests.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from dynamic_sparse_kv_amd import sfi
+from oracle import sfi_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000  # never dereferenced: each call below is rejected first
+
+
+def _header_functions():
+    txt = open(os.path.join(ROOT, "include", "sfi.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(sfi_[a-z_]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_function():
+    names = _header_functions()
+    assert len(names) >= 10
+    L = ctypes.CDLL(sfi.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings_and_version():
+    assert sfi.sfi_status_string(sfi.SFI_OK) == "ok"
+    for s in range(-6, 0):
+        assert sfi.sfi_status_string(s) not in ("", "unknown status")
+    assert "gfx950" in sfi.sfi_version()
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_schedule_matches_oracle(seed):
+    rng = np.random.default_rng(seed)
+    steps, B = int(rng.integers(1, 60)), int(rng.integers(1, 5))
+    ev = rng.random((steps, B)) < rng.uniform(0.0, 0.3)
+    budget = int(rng.integers(-1, 20))
+    got = sfi.sfi_schedule(ev, budget).astype(bool)
+    want = O.schedule(ev, None if budget < 0 else budget)
+    np.testing.assert_array_equal(got, want)
+
+
+def _kv(**over):
+    kv = sfi.sfi_kv()
+    kv.k = kv.v = kv.seq_len = FAKE
+    kv.page_table = None
+    kv.page_size = kv.max_pages = kv.num_pages = 0
+    kv.B, kv.Hq, kv.Hkv, kv.d, kv.cap, kv.max_seq_len = 2, 8, 2, 128, 1000, 900
+    for k, v in over.items():
+        setattr(kv, k, v)
+    return kv
+
+
+def _slow(kv, ws_bytes=1 << 40, ld=1000, **kw):
+    L = sfi.lib()
+    args = dict(batch_ids=None, batch_n=1, q=FAKE, out=FAKE, evidence=None, key_norm=None)
+    args.update(kw)
+    return L.sfi_slow_step(ctypes.byref(kv), args["batch_ids"], args["batch_n"], args["q"],
+                           args["out"], args["evidence"], args["key_norm"], ld, FAKE, ws_bytes, None)
+
+
+def test_workspace_sizes():
+    kv = _kv()
+    assert sfi.sfi_slow_workspace_bytes(kv) > 0
+    assert sfi.sfi_fast_workspace_bytes(kv, 64, 4, 256) > 0
+    assert sfi.sfi_verify_workspace_bytes(kv, 8) > 0
+    assert sfi.sfi_select_workspace_bytes(2, 2, 900) >= 2 * 2 * 900 * 4
+    assert sfi.sfi_slow_workspace_bytes(_kv(d=96)) == 0
+    assert sfi.sfi_select_workspace_bytes(0, 2, 900) == 0
+    assert sfi.sfi_verify_workspace_bytes(kv, 0) == 0
+
+
+def test_slow_step_validation():
+    assert sfi.lib().sfi_slow_step(None, None, 1, FAKE, FAKE, None, None, 0, FAKE, 1, None) == sfi.SFI_ERR_NULL
+    assert _slow(_kv(k=None)) == sfi.SFI_ERR_NULL
+    assert _slow(_kv(Hq=6, Hkv=4)) == sfi.SFI_ERR_SHAPE
+    assert _slow(_kv(d=96)) == sfi.SFI_ERR_UNSUPPORTED
+    assert _slow(_kv(Hq=6, Hkv=2)) == sfi.SFI_ERR_UNSUPPORTED       # G = 3
+    assert _slow(_kv(max_seq_len=1001)) == sfi.SFI_ERR_RANGE
+    assert _slow(_kv(max_seq_len=0)) == sfi.SFI_ERR_RANGE
+    assert _slow(_kv(), batch_n=3) == sfi.SFI_ERR_RANGE
+    assert _slow(_kv(), q=None) == sfi.SFI_ERR_NULL
+    assert _slow(_kv(), evidence=FAKE, ld=899) == sfi.SFI_ERR_RANGE
+    assert _slow(_kv(), ws_bytes=16) == sfi.SFI_ERR_WORKSPACE
+    assert _slow(_kv(), batch_n=0) == sfi.SFI_OK                      # nothing to do
+    # paged descriptions
+    assert _slow(_kv(page_table=FAKE, page_size=24, max_pages=100, num_pages=200)) == sfi.SFI_ERR_RANGE
+    assert _slow(_kv(page_table=FAKE, page_size=16, max_pages=10, num_pages=200)) == sfi.SFI_ERR_RANGE
+    assert _slow(_kv(page_table=FAKE, page_size=16, max_pages=100, num_pages=0)) == sfi.SFI_ERR_SHAPE
+
+
+def _select(p, B=2, H=2, max_len=900, ld=900, ws_bytes=1 << 40, **kw):
+    args = dict(seq_len=FAKE, score=FAKE, key_norm=FAKE, sel_idx=FAKE, sel_count=FAKE, batch_n=1)
+    args.update(kw)
+    return sfi.lib().sfi_select(ctypes.byref(p), None, args["batch_n"], args["seq_len"], B, H, max_len,
+                                args["score"], args["key_norm"], ld, args["sel_idx"], args["sel_count"],
+                                None, FAKE, ws_bytes, None)
+
+
+def test_select_validation():
+    P = sfi.select_params
+    ok = P(sfi.SFI_SCORE_FUSED, 0.3, 64, 4, 256)
+    assert _select(P(sfi.SFI_SCORE_FUSED, 1.5, 64, 4, 256)) == sfi.SFI_ERR_RANGE
+    assert _select(P(sfi.SFI_SCORE_FUSED, -0.1, 64, 4, 256)) == sfi.SFI_ERR_RANGE
+    assert _select(P(sfi.SFI_SCORE_FUSED, 0.3, 0, 4, 256)) == sfi.SFI_ERR_RANGE
+    assert _select(P(sfi.SFI_SCORE_FUSED, 0.3, 64, -1, 256)) == sfi.SFI_ERR_RANGE
+    assert _select(P(sfi.SFI_SCORE_FUSED, 0.3, 64, 4, 256, pos_tau=0.0)) == sfi.SFI_ERR_RANGE
+    assert _select(P(7, 0.3, 64, 4, 256)) == sfi.SFI_ERR_RANGE
+    assert _select(ok, key_norm=None) == sfi.SFI_ERR_NULL
+    assert _select(ok, ld=899) == sfi.SFI_ERR_RANGE
+    assert _select(ok, ws_bytes=8) == sfi.SFI_ERR_WORKSPACE
+    assert _select(ok, batch_n=3) == sfi.SFI_ERR_RANGE
+    assert _select(ok, batch_n=0) == sfi.SFI_OK
+    raw = P(sfi.SFI_SCORE_RAW, 0.0, 64, 4, 256)
+    assert _select(raw, key_norm=None, batch_n=0) == sfi.SFI_OK          # RAW needs no norms
+
+
+def test_fast_step_validation():
+    L = sfi.lib()
+
+    def call(kv, sel_heads=2, sel_k=64, ws_bytes=1 << 40, sel_idx=FAKE, n_sink=4, window=256, batch_n=1):
+        return L.sfi_fast_step(ctypes.byref(kv), None, batch_n, FAKE, sel_idx, FAKE, sel_heads, sel_k,
+                               n_sink, window, FAKE, FAKE, ws_bytes, None)
+
+    assert call(_kv(), sel_heads=3) == sfi.SFI_ERR_SHAPE
+    assert call(_kv(), sel_k=-1) == sfi.SFI_ERR_RANGE
+    assert call(_kv(), window=-1) == sfi.SFI_ERR_RANGE
+    assert call(_kv(), sel_idx=None) == sfi.SFI_ERR_NULL
+    assert call(_kv(), ws_bytes=8) == sfi.SFI_ERR_WORKSPACE
+    assert call(_kv(d=256)) == sfi.SFI_ERR_UNSUPPORTED
+    assert call(_kv(), batch_n=0) == sfi.SFI_OK
+
+
+def test_verify_validation():
+    L = sfi.lib()
+
+    def call(kv, T=8, mask=0xFF, ld=1000, ws_bytes=1 << 40, agg=FAKE, batch_n=1):
+        return L.sfi_verify_aggregate(ctypes.byref(kv), None, batch_n, FAKE, T, mask, FAKE, agg, ld,
+                                      FAKE, ws_bytes, None)
+
+    kv = _kv(Hq=32, Hkv=8)
+    assert call(kv, T=9, mask=0x1FF) == sfi.SFI_ERR_UNSUPPORTED          # 4 * 9 > 32 rows
+    assert call(kv, T=0, mask=0) == sfi.SFI_ERR_UNSUPPORTED
+    assert call(kv, mask=0) == sfi.SFI_ERR_RANGE
+    assert call(kv, mask=0x100) == sfi.SFI_ERR_RANGE
+    assert call(kv, ld=10) == sfi.SFI_ERR_RANGE
+    assert call(kv, agg=None) == sfi.SFI_ERR_NULL
+    assert call(kv, ws_bytes=8) == sfi.SFI_ERR_WORKSPACE
+    assert call(_kv(Hq=40, Hkv=8), T=4, mask=0xF) == sfi.SFI_ERR_UNSUPPORTED  # G = 5 has no MFMA tile
+    assert call(kv, batch_n=0) == sfi.SFI_OK

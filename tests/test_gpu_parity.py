@@ -1,0 +1,451 @@
+"""GPU parity: every libsfi entry point against the CPU oracle.
+
+Inputs come from the seeded generator (drawn on the GPU, copied to the host
+for the oracle); expected values come only from oracle/.  Tolerances are in
+tests/parity_util.py.  Cases span several tiles/splits and ragged tails, GQA
+groups 1/4/5/8, d = 64 and 128, batch subsets, paged caches, the degenerate
+selections (empty candidate set, fewer candidates than k, exact ties) and a
+sampled check at the full 32K-context, 8-sequence shape.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from dynamic_sparse_kv_amd import sfi
+from dynamic_sparse_kv_amd import workload as W
+from dynamic_sparse_kv_amd.runner import DecodePlan, SFIDecoder, VegasDecoder
+from oracle import sfi_oracle as O
+
+from parity_util import EVID_TOL, NORM_TOL, OUT_TOL, check_selection, row_rel_err
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _bits(t):
+    return W.bf16_bits(t)
+
+
+def _rand_kv(B, Hkv, cap, d, seed, hh=0):
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    K = torch.randn((B, Hkv, cap, d), generator=g, device=DEV)
+    if hh:
+        idx = torch.randint(0, cap, (hh,), generator=g, device=DEV)
+        K[:, :, idx] *= 3.0
+    V = torch.randn((B, Hkv, cap, d), generator=g, device=DEV)
+    return K.to(torch.bfloat16).contiguous(), V.to(torch.bfloat16).contiguous()
+
+
+def _rand_q(shape, seed):
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    return torch.randn(shape, generator=g, device=DEV).to(torch.bfloat16).contiguous()
+
+
+# ----------------------------------------------------------------- slow step
+
+SLOW_CASES = [
+    # B, Hq, Hkv, d, lens
+    (1, 8, 2, 64, [4097]),
+    (3, 32, 8, 128, [3000, 517, 9000]),
+    (2, 8, 8, 128, [1300, 257]),          # G = 1
+    (2, 40, 8, 128, [5000, 2049]),        # G = 5
+    (1, 16, 2, 64, [700]),                # G = 8
+    (2, 8, 2, 128, [1, 33]),              # tiny contexts
+]
+
+
+@pytest.mark.parametrize("case", SLOW_CASES, ids=lambda c: f"B{c[0]}-Hq{c[1]}-Hkv{c[2]}-d{c[3]}")
+def test_slow_step_matches_oracle(case):
+    B, Hq, Hkv, d, lens = case
+    _say(f"slow step case {case}")
+    cap = max(lens) + 5
+    K, V = _rand_kv(B, Hkv, cap, d, seed=B * 1000 + Hq + d, hh=7)
+    q = _rand_q((B, Hq, d), seed=11 + Hq)
+    seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    dec = SFIDecoder(K, V, Hq, max(lens), n_sink=4, window=256, k=64, lam=0.3)
+    dec.slow(q, seq, None, B, select=False)
+    torch.cuda.synchronize()
+    out = dec.out.cpu().numpy()
+    ev = dec.evidence.cpu().numpy()
+    nrm = dec.key_norm.cpu().numpy()
+    Kb, Vb, qb = _bits(K), _bits(V), _bits(q)
+    for b in range(B):
+        n = lens[b]
+        o_ref, p = O.dense_step(qb[b], Kb[b], Vb[b], n)
+        f_ref = O.evidence(p, Hkv)
+        assert row_rel_err(out[b], o_ref) <= OUT_TOL
+        assert row_rel_err(ev[b, :, :n], f_ref) <= EVID_TOL
+        np.testing.assert_allclose(ev[b, :, :n].sum(axis=1), 1.0, rtol=1e-4)
+        np.testing.assert_allclose(nrm[b, :, :n], O.key_norms(Kb[b], n), rtol=NORM_TOL)
+
+
+def test_slow_batch_subset_and_plain_dense():
+    B, Hq, Hkv, d = 4, 32, 8, 128
+    lens = [2000, 3000, 1000, 2500]
+    K, V = _rand_kv(B, Hkv, 3100, d, seed=5)
+    q = _rand_q((B, Hq, d), seed=6)
+    seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    dec = SFIDecoder(K, V, Hq, 3000, n_sink=4, window=256, k=64, lam=0.3)
+    dec.out.fill_(7.0)
+    ids = torch.tensor([2, 0], dtype=torch.int32, device=DEV)
+    dec.dense(q, seq, ids, 2)
+    torch.cuda.synchronize()
+    out = dec.out.cpu().numpy()
+    Kb, Vb, qb = _bits(K), _bits(V), _bits(q)
+    for b in (0, 2):
+        o_ref, _ = O.dense_step(qb[b], Kb[b], Vb[b], lens[b])
+        assert row_rel_err(out[b], o_ref) <= OUT_TOL
+    assert np.all(out[1] == 7.0) and np.all(out[3] == 7.0)     # untouched slots
+
+
+# ------------------------------------------------------------------- select
+
+def _select_gpu(mode, score, key_norm, lens, k, n_sink, window, lam=0.3, H=None, fused=False):
+    B = score.shape[0]
+    H = score.shape[1] if H is None else H
+    ld = score.shape[2]
+    max_len = max(lens)
+    seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    p = sfi.select_params(mode, lam, k, n_sink, window)
+    sel = torch.full((B, H, k), -7, dtype=torch.int32, device=DEV)
+    cnt = torch.full((B, H), -7, dtype=torch.int32, device=DEV)
+    fo = torch.zeros((B, H, ld), dtype=torch.float32, device=DEV) if fused else None
+    wsb = sfi.sfi_select_workspace_bytes(B, H, max_len)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    sfi.sfi_select(p, None, B, seq, B, H, max_len, score, key_norm, ld, sel, cnt, fo, ws, wsb)
+    torch.cuda.synchronize()
+    return sel.cpu().numpy(), cnt.cpu().numpy(), (fo.cpu().numpy() if fused else None)
+
+
+def test_select_raw_exact_ties_and_degenerate():
+    _say("select raw ties")
+    rng = np.random.default_rng(3)
+    B, H, ld = 4, 3, 6000
+    lens = [6000, 5000, 300, 200]     # 300: |C| = 40 < k; 200: C empty
+    sc = rng.integers(-50, 50, size=(B, H, ld)).astype(np.float32)   # many exact ties
+    sc[0, 1] = 1.0                                                  # all equal
+    sc[1, 2] = rng.standard_normal(ld).astype(np.float32) * 1e-30   # tiny / denormal-ish values
+    k, ns, win = 257, 4, 256
+    sel, cnt, _ = _select_gpu(sfi.SFI_SCORE_RAW, torch.from_numpy(sc).to(DEV), None, lens, k, ns, win)
+    for b in range(B):
+        lo, hi = O.candidate_range(lens[b], ns, win)
+        for h in range(H):
+            want = O.topk_indices(sc[b, h].astype(np.float64), lo, hi, k)
+            assert cnt[b, h] == len(want)
+            np.testing.assert_array_equal(sel[b, h, : len(want)], want)
+            assert np.all(sel[b, h, len(want):] == -1)
+
+
+def test_select_raw_large_k_and_multi_tile():
+    rng = np.random.default_rng(4)
+    B, H, ld = 2, 1, 70000
+    lens = [70000, 65536]
+    sc = rng.standard_normal((B, H, ld)).astype(np.float32)
+    k = 4096
+    sel, cnt, _ = _select_gpu(sfi.SFI_SCORE_RAW, torch.from_numpy(sc).to(DEV), None, lens, k, 4, 256)
+    for b in range(B):
+        lo, hi = O.candidate_range(lens[b], 4, 256)
+        want = O.topk_indices(sc[b, 0].astype(np.float64), lo, hi, k)
+        np.testing.assert_array_equal(sel[b, 0, :k], want)
+
+
+def test_select_fused_from_oracle_evidence():
+    """Selector alone: oracle f and norms in, oracle s and Top-K out."""
+    _say("select fused")
+    B, Hq, Hkv, d = 2, 8, 2, 64
+    lens = [4100, 3000]
+    cap = 4200
+    K, V = _rand_kv(B, Hkv, cap, d, seed=21, hh=20)
+    q = _rand_q((B, Hq, d), seed=22)
+    Kb, Vb, qb = _bits(K), _bits(V), _bits(q)
+    f = np.zeros((B, Hkv, cap), dtype=np.float32)
+    nu = np.zeros((B, Hkv, cap), dtype=np.float32)
+    s_ref = []
+    for b in range(B):
+        n = lens[b]
+        _, p = O.dense_step(qb[b], Kb[b], Vb[b], n)
+        fb = O.evidence(p, Hkv)
+        f[b, :, :n] = fb
+        nu[b, :, :n] = O.key_norms(Kb[b], n)
+        s_ref.append(O.fuse(fb, O.prior(Kb[b], n), 0.3))
+    k = 256
+    sel, cnt, fo = _select_gpu(sfi.SFI_SCORE_FUSED, torch.from_numpy(f).to(DEV), torch.from_numpy(nu).to(DEV),
+                               lens, k, 4, 256, lam=0.3, fused=True)
+    ties = 0
+    for b in range(B):
+        n = lens[b]
+        lo, hi = O.candidate_range(n, 4, 256)
+        assert row_rel_err(fo[b, :, :n], s_ref[b]) <= EVID_TOL
+        for g in range(Hkv):
+            ties += check_selection(sel[b, g], cnt[b, g], s_ref[b][g], lo, hi, k)
+    _say(f"  near-tie differences: {ties}")
+
+
+# ----------------------------------------------------------------- fast step
+
+def _fast_gpu(K, V, Hq, q, lens, sel_np, cnt_np, n_sink, window, sel_heads):
+    B = K.shape[0]
+    seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    kv = sfi.make_kv(K, V, seq, Hq, max(lens))
+    sel = torch.from_numpy(np.ascontiguousarray(sel_np, dtype=np.int32)).to(DEV)
+    cnt = torch.from_numpy(np.ascontiguousarray(cnt_np, dtype=np.int32)).to(DEV)
+    sel_k = sel.shape[2]
+    out = torch.full((B, Hq, K.shape[3]), 9.0, device=DEV)
+    wsb = sfi.sfi_fast_workspace_bytes(kv, sel_k, n_sink, window)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    sfi.sfi_fast_step(kv, None, B, q, sel, cnt, sel_heads, sel_k, n_sink, window, out, ws, wsb)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("Hq,Hkv,d", [(8, 2, 64), (32, 8, 128), (40, 8, 128)])
+def test_fast_step_matches_oracle(Hq, Hkv, d):
+    _say(f"fast step Hq={Hq} Hkv={Hkv} d={d}")
+    B = 3
+    lens = [5000, 2000, 700]
+    K, V = _rand_kv(B, Hkv, 5100, d, seed=Hq + d)
+    q = _rand_q((B, Hq, d), seed=Hq * 3)
+    rng = np.random.default_rng(Hq)
+    k = 300
+    sel = np.full((B, Hkv, k), -1, dtype=np.int32)
+    cnt = np.zeros((B, Hkv), dtype=np.int32)
+    for b in range(B):
+        for g in range(Hkv):
+            # a slow-step selection from an earlier, shorter cache: some entries
+            # now fall inside the window and must be skipped; sinks too
+            pool = np.arange(0, lens[b])
+            c = min(k - 3, len(pool))
+            pick = np.sort(rng.choice(pool, c, replace=False))
+            sel[b, g, :c] = pick
+            cnt[b, g] = c
+    out = _fast_gpu(K, V, Hq, q, lens, sel, cnt, 4, 256, Hkv)
+    Kb, Vb, qb = _bits(K), _bits(V), _bits(q)
+    for b in range(B):
+        lists = [sel[b, g, : cnt[b, g]] for g in range(Hkv)]
+        o_ref = O.fast_step(qb[b], Kb[b], Vb[b], lens[b], lists, 4, 256)
+        assert row_rel_err(out[b], o_ref) <= OUT_TOL
+
+
+def test_fast_full_selection_equals_dense_and_shared_list():
+    B, Hq, Hkv, d = 2, 32, 8, 128
+    lens = [3000, 1500]
+    K, V = _rand_kv(B, Hkv, 3000, d, seed=77)
+    q = _rand_q((B, Hq, d), seed=78)
+    ns, win = 4, 256
+    k = 3000
+    sel = np.full((B, 1, k), -1, dtype=np.int32)
+    cnt = np.zeros((B, 1), dtype=np.int32)
+    for b in range(B):
+        c = np.arange(ns, lens[b] - win)
+        sel[b, 0, : len(c)] = c
+        cnt[b, 0] = len(c)
+    out = _fast_gpu(K, V, Hq, q, lens, sel, cnt, ns, win, 1)
+    Kb, Vb, qb = _bits(K), _bits(V), _bits(q)
+    for b in range(B):
+        o_ref, _ = O.dense_step(qb[b], Kb[b], Vb[b], lens[b])
+        assert row_rel_err(out[b], o_ref) <= OUT_TOL
+
+
+# ------------------------------------------------------------ whole decode run
+
+def test_decode_run_tiny_config_every_step():
+    """Config: tiny 4K single layer, all 64 steps, slow/fast schedule."""
+    cfg = W.CONFIGS["c1"]
+    _say("decode run c1")
+    K, V = W.make_kv(cfg, device=DEV)
+    starts = W.sentence_starts(cfg)
+    slow = sfi.sfi_schedule(starts, cfg.budget).astype(bool)
+    np.testing.assert_array_equal(slow, O.schedule(starts, cfg.budget))
+    qh = W.make_queries(cfg, starts)
+    q = qh.to(DEV)
+    ctx = W.context_lengths(cfg)
+    plan = DecodePlan(slow, ctx, DEV)
+    dec = SFIDecoder(K, V, cfg.Hq, int(ctx.max()) + cfg.steps, n_sink=cfg.n_sink, window=cfg.window,
+                     k=cfg.k, lam=cfg.lam, keep_fused=True)
+    Kb, Vb, qb = _bits(K), _bits(V), _bits(qh)
+    ref = O.decode_run(qb[:, 0], Kb[0], Vb[0], int(ctx[0]), slow[:, 0], lam=cfg.lam, k=cfg.k,
+                       n_sink=cfg.n_sink, window=cfg.window)
+    ties = 0
+    for s in range(cfg.steps):
+        dec.step(plan, s, q)
+        torch.cuda.synchronize()
+        r = ref[s]
+        assert row_rel_err(dec.out[0].cpu().numpy(), r["o"]) <= OUT_TOL, s
+        if r["kind"] == "slow":
+            sel = dec.sel_idx[0].cpu().numpy()
+            cnt = dec.sel_count[0].cpu().numpy()
+            for g in range(cfg.Hkv):
+                ties += check_selection(sel[g], cnt[g], r["s"][g], r["lo"], r["hi"], cfg.k)
+            assert row_rel_err(dec.fused[0, :, : r["n"]].cpu().numpy(), r["s"]) <= EVID_TOL
+    _say(f"  near-tie differences over the run: {ties}")
+    assert ties == 0   # fast outputs above were compared against the oracle's own selection
+
+
+def test_bitwise_repeatable():
+    cfg = W.CONFIGS["c1"].replace(B=2, steps=24)
+    K, V = W.make_kv(cfg, device=DEV)
+    starts = W.sentence_starts(cfg)
+    slow = O.schedule(starts, cfg.budget)
+    q = W.make_queries(cfg, starts).to(DEV)
+    plan = DecodePlan(slow, W.context_lengths(cfg), DEV)
+    outs = []
+    for rep in range(2):
+        dec = SFIDecoder(K, V, cfg.Hq, cfg.ctx + cfg.steps, n_sink=4, window=256, k=cfg.k, lam=cfg.lam)
+        hist = []
+        for s in range(cfg.steps):
+            dec.step(plan, s, q)
+            hist.append(dec.out.clone())
+        torch.cuda.synchronize()
+        outs.append((torch.stack(hist), dec.sel_idx.clone(), dec.evidence.clone()))
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a,
+                           b.view(torch.int32) if b.dtype == torch.float32 else b)
+
+
+# ------------------------------------------------------------------- verify
+
+@pytest.mark.parametrize("Hq,Hkv,d,T", [(32, 8, 128, 8), (8, 2, 64, 8), (16, 8, 128, 4), (8, 8, 128, 1)])
+def test_verify_matches_oracle(Hq, Hkv, d, T):
+    _say(f"verify Hq={Hq} Hkv={Hkv} d={d} T={T}")
+    B = 2
+    lens = [3000, 1111]
+    K, V = _rand_kv(B, Hkv, 3000, d, seed=Hq * 7 + T)
+    q = _rand_q((B, T, Hq, d), seed=T + 100)
+    seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    vd = VegasDecoder(K, V, Hq, max(lens), T, n_sink=4, window=256, k=256)
+    Kb, Vb, qb = _bits(K), _bits(V), _bits(q)
+    for mode in ("all", "c2q"):
+        rows = O.collect_rows(T, mode)
+        mask = sum(1 << t for t in rows)
+        vd.agg.fill_(123.0)
+        vd.verify(q, seq, mask)
+        vd.select(seq)
+        torch.cuda.synchronize()
+        out = vd.vout.cpu().numpy()
+        agg = vd.agg.cpu().numpy()
+        sel = vd.sel_idx.cpu().numpy()
+        cnt = vd.sel_count.cpu().numpy()
+        for b in range(B):
+            n = lens[b]
+            o_ref, a_ref = O.verify(qb[b], Kb[b], Vb[b], n, rows)
+            for t in range(T):
+                assert row_rel_err(out[b, t], o_ref[t]) <= OUT_TOL, (mode, b, t)
+            P = n - T
+            err = np.abs(agg[b, :P] - a_ref).max() / np.abs(a_ref).max()
+            assert err <= 1e-5, (mode, b, err)
+            assert np.all(agg[b, P:n] == 123.0)          # no writes past the prefix
+            lo, hi = O.candidate_range(n, 4, 256)
+            check_selection(sel[b, 0], cnt[b, 0], a_ref, lo, hi, 256)
+
+
+def test_vegas_draft_steps_with_shared_selection():
+    B, Hq, Hkv, d, T = 2, 32, 8, 128, 8
+    n0 = 2600
+    K, V = _rand_kv(B, Hkv, n0 + 8, d, seed=31)
+    q = _rand_q((B, T, Hq, d), seed=32)
+    seq = torch.full((B,), n0, dtype=torch.int32, device=DEV)
+    vd = VegasDecoder(K, V, Hq, n0 + 7, T, n_sink=4, window=256, k=512)
+    vd.verify(q, seq, 0xFF)
+    vd.select(seq)
+    torch.cuda.synchronize()
+    sel = vd.sel_idx.cpu().numpy()
+    cnt = vd.sel_count.cpu().numpy()
+    Kb, Vb, qb = _bits(K), _bits(V), _bits(q)
+    for j in range(1, 8):
+        seqj = torch.full((B,), n0 + j - 1 + 1, dtype=torch.int32, device=DEV)
+        qd = _rand_q((B, Hq, d), seed=40 + j)
+        vd.draft(qd, seqj)
+        torch.cuda.synchronize()
+        out = vd.out.cpu().numpy()
+        qdb = _bits(qd)
+        for b in range(B):
+            lst = [sel[b, 0, : cnt[b, 0]]] * Hkv
+            o_ref = O.fast_step(qdb[b], Kb[b], Vb[b], n0 + j, lst, 4, 256)
+            assert row_rel_err(out[b], o_ref) <= OUT_TOL
+
+
+# -------------------------------------------------------------------- paged
+
+def test_paged_cache_matches_contiguous_and_oracle():
+    _say("paged")
+    cfg = W.CONFIGS["c5"].replace(B=4, Hq=40, Hkv=8, d=128, ctx=6000, ragged_min=1000, steps=2)
+    ctx = W.context_lengths(cfg)
+    K, V = W.make_kv(cfg, device=DEV)
+    cap = K.shape[2]
+    table, npages = W.page_table(cfg, np.full(cfg.B, cap))
+    Kp = W.to_paged(K, table, npages, 16)
+    Vp = W.to_paged(V, table, npages, 16)
+    tab = torch.from_numpy(table).to(DEV)
+    lens = [int(c) + 1 for c in ctx]
+    seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    q = _rand_q((cfg.B, cfg.Hq, cfg.d), seed=55)
+    ml = max(lens)
+    dc = SFIDecoder(K, V, cfg.Hq, ml, n_sink=4, window=256, k=128, lam=0.3)
+    dp = SFIDecoder(Kp, Vp, cfg.Hq, ml, n_sink=4, window=256, k=128, lam=0.3, page_table=tab, page_size=16)
+    for d_ in (dc, dp):
+        d_.slow(q, seq, None, cfg.B)
+        d_.fast(q, seq, None, cfg.B)
+    torch.cuda.synchronize()
+    assert torch.equal(dc.sel_idx, dp.sel_idx)
+    assert torch.equal(dc.out.view(torch.int32), dp.out.view(torch.int32))
+    Kb, Vb, qb = _bits(K), _bits(V), _bits(q)
+    sel = dp.sel_idx.cpu().numpy()
+    cnt = dp.sel_count.cpu().numpy()
+    out = dp.out.cpu().numpy()
+    for b in range(cfg.B):
+        lists = [sel[b, g, : cnt[b, g]] for g in range(cfg.Hkv)]
+        o_ref = O.fast_step(qb[b], Kb[b], Vb[b], lens[b], lists, 4, 256)
+        assert row_rel_err(out[b], o_ref) <= OUT_TOL
+
+
+# ------------------------------------------------- full size, sampled outputs
+
+def test_full_size_llama_layer_32k_sampled():
+    """8 sequences x 32K context, Hq=32/Hkv=8, d=128, k=2048: the benchmark's
+    launch shapes; the oracle checks two sampled sequences."""
+    cfg = W.CONFIGS["c2"]
+    _say("full size 32K")
+    K, V = W.make_kv(cfg, device=DEV)
+    ctx = W.context_lengths(cfg)
+    ml = int(ctx.max()) + cfg.steps
+    q = _rand_q((cfg.B, cfg.Hq, cfg.d), seed=99)
+    lens = [int(ctx[b]) + 1 + 13 * b for b in range(cfg.B)]
+    seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    dec = SFIDecoder(K, V, cfg.Hq, ml, n_sink=cfg.n_sink, window=cfg.window, k=cfg.k, lam=cfg.lam,
+                     keep_fused=True)
+    dec.slow(q, seq, None, cfg.B)
+    torch.cuda.synchronize()
+    out = dec.out.cpu().numpy()
+    sel = dec.sel_idx.cpu().numpy()
+    cnt = dec.sel_count.cpu().numpy()
+    ties = 0
+    for b in (0, 5):
+        n = lens[b]
+        Kb = _bits(K[b, :, :n])
+        Vb = _bits(V[b, :, :n])
+        qb = _bits(q[b])
+        r = O.slow_select(qb, Kb, Vb, n, lam=cfg.lam, k=cfg.k, n_sink=cfg.n_sink, window=cfg.window)
+        assert row_rel_err(out[b], r["o"]) <= OUT_TOL
+        for g in range(cfg.Hkv):
+            ties += check_selection(sel[b, g], cnt[b, g], r["s"][g], r["lo"], r["hi"], cfg.k)
+        # fast step 10 tokens later with the oracle's own selection as input
+        sel_in = np.full((cfg.B, cfg.Hkv, cfg.k), -1, dtype=np.int32)
+        cnt_in = np.zeros((cfg.B, cfg.Hkv), dtype=np.int32)
+        for g in range(cfg.Hkv):
+            sel_in[:, g, : len(r["sel"][g])] = r["sel"][g]
+            cnt_in[:, g] = len(r["sel"][g])
+        lens_f = [min(x + 10, ml) for x in lens]
+        of = _fast_gpu(K, V, cfg.Hq, q, lens_f, sel_in, cnt_in, cfg.n_sink, cfg.window, cfg.Hkv)
+        Kf = _bits(K[b, :, : lens_f[b]])
+        Vf = _bits(V[b, :, : lens_f[b]])
+        o_ref = O.fast_step(qb, Kf, Vf, lens_f[b], r["sel"], cfg.n_sink, cfg.window)
+        assert row_rel_err(of[b], o_ref) <= OUT_TOL
+    _say(f"  near-tie differences: {ties}")
