@@ -13,9 +13,9 @@ on the device before the clock starts.
 
 Printed: one JSON line with the throughput, a roofline record for the
 dominant call (algorithmic bytes / duration from HIP events on the launch
-stream in a second, eager pass over the same steps, each step preceded by an
-L2 + Infinity Cache flush), and the CPU oracle's throughput on a bounded
-sample of the same workload.
+stream in a second, eager pass over the same steps, each call preceded by a
+1 GiB read that evicts L2 and the Infinity Cache), and the CPU oracle's
+throughput on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -153,15 +153,17 @@ def main():
     torch.cuda.synchronize()
 
     # ---- headline: K steps replayed from one HIP graph -------------------
+    # Slow steps + selector on one stream, fast steps on a second one, joined
+    # per step (each chain waits for the other's previous step).
     use_graph = not args.no_graph
+    side = torch.cuda.Stream()
+    side_b = torch.cuda.Stream()
     if use_graph:
         g = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
         side.wait_stream(stream)
         with torch.cuda.stream(side):
             with torch.cuda.graph(g, stream=side):
-                for s in range(K_steps):
-                    dec.step(plan, s, q, side)
+                dec.run_two_streams(plan, q, 0, K_steps, side, side_b)
         torch.cuda.synchronize()
         g.replay()                      # untimed replay (first launch of the graph)
         torch.cuda.synchronize()
@@ -173,23 +175,25 @@ def main():
     else:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        run_steps(K_steps)
+        dec.run_two_streams(plan, q, 0, K_steps, stream, side_b)
         torch.cuda.synchronize()
         t_total = time.perf_counter() - t0
     tokens = cfg.B * K_steps
     value = tokens / t_total
 
-    # ---- eager pass with a cache flush and HIP events around every call ----
+    # ---- eager pass: HIP events around every call, each call preceded by a
+    # 1 GiB read that evicts L2 and the Infinity Cache and keeps the stream
+    # busy while the host enqueues the call and its events ----------------
     _log("[bench] per-call timing pass")
-    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     calls = {"slow": [], "select": [], "fast": []}
     bytes_by = {"slow": [], "select": [], "fast": []}
     ev = []
     for s in range(K_steps):
-        flush.fill_(float(s))
         ns, nf = int(plan.n_slow[s]), int(plan.n_fast[s])
         lens = plan.seq_len_host[s]
         if ns:
+            flush.sum()
             ids = np.nonzero(plan.slow[s])[0]
             e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
             e0.record(stream)
@@ -200,7 +204,7 @@ def main():
             ev.append(("slow", e0, e1, sum(algorithmic_bytes("slow", int(lens[b]), cfg) for b in ids)))
             ev.append(("select", e1, e2, sum(algorithmic_bytes("select", int(lens[b]), cfg) for b in ids)))
         if nf:
-            flush.fill_(float(s) + 0.5)
+            flush.sum()
             ids = np.nonzero(~plan.slow[s])[0]
             e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
             e0.record(stream)
@@ -208,6 +212,7 @@ def main():
             e1.record(stream)
             ev.append(("fast", e0, e1, sum(algorithmic_bytes("fast", int(lens[b]), cfg) for b in ids)))
     torch.cuda.synchronize()
+    del flush
     for kind, a, b_, nbytes in ev:
         calls[kind].append(a.elapsed_time(b_) * 1e-3)
         bytes_by[kind].append(nbytes)
@@ -225,18 +230,25 @@ def main():
     achieved = dc["alg_GBps"]
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": {"slow": "sfi_slow_step (split-K partial + finalize)",
-                           "select": "sfi_select (stats + prior + radix top-k)",
-                           "fast": "sfi_fast_step (gather partial + finalize)"}[dom]}
+                "kernel": {"slow": "sfi_slow_step: split-K partial + finalize kernels",
+                           "select": "sfi_select: fused selector kernel",
+                           "fast": "sfi_fast_step: gather partial + finalize kernels"}[dom]}
 
     # ---- all-dense comparator: every sequence dense every step -----------
     _log("[bench] dense comparator")
     all_ids = torch.arange(cfg.B, dtype=torch.int32, device=dev)
     n_dense = min(K_steps, 64)
+    gd = torch.cuda.CUDAGraph()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(gd, stream=side):
+            for s in range(n_dense):
+                dec.dense(q[s], plan.seq_len[s], all_ids, cfg.B, side)
+    torch.cuda.synchronize()
+    gd.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(n_dense):
-        dec.dense(q[s], plan.seq_len[s], all_ids, cfg.B, stream)
+    gd.replay()
     torch.cuda.synchronize()
     t_dense = (time.perf_counter() - t0) / n_dense
     dense_tps = cfg.B / t_dense
@@ -259,7 +271,8 @@ def main():
                                f"lambda {cfg.lam}, {K_steps} decode steps",
                    "global_batch": cfg.B, "seq_len": cfg.ctx, "parallelism": "none (1 GPU)",
                    "slow_fraction": round(float(plan.slow[:K_steps].mean()), 4),
-                   "timing": "hip graph replay" if use_graph else "eager"},
+                   "timing": ("hip graph replay, slow+selector and fast steps on two streams"
+                              if use_graph else "eager, two streams")},
         "roofline": roofline,
         "per_call": per_call,
         "dense_tokens_per_s": round(dense_tps, 1),

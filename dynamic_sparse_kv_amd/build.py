@@ -3,7 +3,8 @@
     python -m dynamic_sparse_kv_amd.build [-v]
 
 Every .hip file under csrc/ is compiled to an object (in parallel) and
-linked into dynamic_sparse_kv_amd/libsfi.so.
+linked into dynamic_sparse_kv_amd/libsfi.so.  SFI_EXTRA_CFLAGS adds hipcc
+flags, e.g. -DSFI_DECODE_U=2 to override a launch-shape default.
 """
 from __future__ import annotations
 
@@ -43,7 +44,8 @@ def sources():
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    extra = os.environ.get("SFI_EXTRA_CFLAGS", "").split()
+    cmd = [HIPCC, *CFLAGS, *extra, "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

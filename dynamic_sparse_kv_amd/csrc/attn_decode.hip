@@ -21,14 +21,22 @@
 //   * a finalize kernel merges the partials in a fixed order and, for slow
 //     steps, turns the per-key logits written on the way into the evidence
 //     f_j = (1/G) sum_h p_hj.
+#include <algorithm>
+
 #include "sfi_internal.hpp"
 
 namespace sfi {
 namespace {
 
+#ifndef SFI_DECODE_U
+#define SFI_DECODE_U 2
+#endif
+#ifndef SFI_WAVES_OF_WG
+#define SFI_WAVES_OF_WG 1
+#endif
+
 enum { MODE_SLOW = 0, MODE_FAST = 1 };
 constexpr int kThreads = 256;
-constexpr int kMaxFastChunk = 1024;
 
 struct PartialArgs {
   KVView kv;
@@ -74,10 +82,17 @@ __device__ __forceinline__ FastList fast_list(const int32_t *sel_idx, const int3
 
 template <int D, int G, bool PAGED, int MODE, bool EVID>
 __global__ __launch_bounds__(kThreads) void partial_kernel(PartialArgs a) {
-  constexpr int LPR = D / 8;          // lanes per row
-  constexpr int RPB = kThreads / LPR; // rows per workgroup instruction
-  constexpr int U = 4;                // rows in flight per lane group
+  // 8 lanes per row halves the cross-lane reduction and softmax work per row
+  // compared with 16; wide groups (G*D > 640) use 16 to bound accumulators.
+  constexpr int LPR = (G * D > 640) ? 16 : 8;  // lanes per row
+  constexpr int DPL = D / LPR;         // dims per lane (8 or 16)
+  constexpr int NV = DPL / 8;          // 16-byte slices per row per lane
+  constexpr int RPB = kThreads / LPR;  // rows per workgroup instruction
+  constexpr int U = SFI_DECODE_U;      // rows per lane group per pipeline stage
   constexpr int NW = kThreads / 64;
+  // Lazy rescaling: the running reference m only moves when a logit exceeds
+  // it by more than kSlack (log2 units), so p = 2^(l - m) stays <= 2^kSlack.
+  constexpr float kSlack = 8.0f;
 
   __shared__ int s_idx[MODE == MODE_FAST ? kMaxFastChunk : 1];
   __shared__ float s_m[NW][G], s_z[NW][G];
@@ -119,66 +134,86 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialArgs a) {
   const int sub = tid % LPR;
   const int rg = tid / LPR;
 
-  uint32_t qv[G][4];
+  uint32_t qv[G][4 * NV];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const uint4 t = ldg16(a.q + ((size_t)b * a.Hq + g * G + h) * D + sub * 8);
-    qv[h][0] = t.x; qv[h][1] = t.y; qv[h][2] = t.z; qv[h][3] = t.w;
+#pragma unroll
+    for (int c = 0; c < NV; ++c) {
+      const uint4 t = ldg16(a.q + ((size_t)b * a.Hq + g * G + h) * D + sub * DPL + 8 * c);
+      qv[h][4 * c + 0] = t.x; qv[h][4 * c + 1] = t.y; qv[h][4 * c + 2] = t.z; qv[h][4 * c + 3] = t.w;
+    }
   }
 
-  float m[G], Z[G], acc[G][8];
+  float m[G], Z[G], acc[G][DPL];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     m[h] = kNegBig;
     Z[h] = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+    for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
   }
 
   const size_t lrow = (size_t)(b * a.kv.Hkv + g);
 
-  for (int base = p0 + rg; base < p1; base += RPB * U) {
-    uint4 kr[U], vr[U];
-    int jr[U];
+  // One pipeline stage: U rows per lane group, K and V slices of DPL dims.
+  struct Stage {
+    uint4 k[U][NV], v[U][NV];
+    int j[U];
+  };
+  auto load_stage = [&](Stage &st, int base) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int p = base + u * RPB;
       int j = -1;
       if (p < p1) j = (MODE == MODE_FAST) ? s_idx[p - p0] : p;
-      jr[u] = j;
+      st.j[u] = j;
       if (j >= 0) {
-        const size_t off = kv_row<D, PAGED>(a.kv, b, g, j) + sub * 8;
-        kr[u] = ldg16(a.kv.k + off);
-        vr[u] = ldg16(a.kv.v + off);
+        const size_t off = kv_row<D, PAGED>(a.kv, b, g, j) + sub * DPL;
+#pragma unroll
+        for (int c = 0; c < NV; ++c) {
+          st.k[u][c] = ldg16(a.kv.k + off + 8 * c);
+          st.v[u][c] = ldg16(a.kv.v + off + 8 * c);
+        }
       } else {
-        kr[u] = make_uint4(0, 0, 0, 0);
-        vr[u] = kr[u];
+#pragma unroll
+        for (int c = 0; c < NV; ++c) {
+          st.k[u][c] = make_uint4(0, 0, 0, 0);
+          st.v[u][c] = st.k[u][c];
+        }
       }
     }
-
+  };
+  auto consume = [&](const Stage &st) {
     float l[U][G];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        float s = dot2_bf16(qv[h][0], kr[u].x, 0.f);
-        s = dot2_bf16(qv[h][1], kr[u].y, s);
-        s = dot2_bf16(qv[h][2], kr[u].z, s);
-        s = dot2_bf16(qv[h][3], kr[u].w, s);
-        s = group_sum<LPR>(s);
-        l[u][h] = (jr[u] >= 0) ? s * a.qscale : -INFINITY;
+        float sdot = 0.f;
+#pragma unroll
+        for (int c = 0; c < NV; ++c) {
+          sdot = dot2_bf16(qv[h][4 * c + 0], st.k[u][c].x, sdot);
+          sdot = dot2_bf16(qv[h][4 * c + 1], st.k[u][c].y, sdot);
+          sdot = dot2_bf16(qv[h][4 * c + 2], st.k[u][c].z, sdot);
+          sdot = dot2_bf16(qv[h][4 * c + 3], st.k[u][c].w, sdot);
+        }
+        sdot = group_sum<LPR>(sdot);
+        l[u][h] = (st.j[u] >= 0) ? sdot * a.qscale : -INFINITY;
       }
     }
-
     if constexpr (EVID) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        float nn = dot2_bf16(kr[u].x, kr[u].x, 0.f);
-        nn = dot2_bf16(kr[u].y, kr[u].y, nn);
-        nn = dot2_bf16(kr[u].z, kr[u].z, nn);
-        nn = dot2_bf16(kr[u].w, kr[u].w, nn);
+        float nn = 0.f;
+#pragma unroll
+        for (int c = 0; c < NV; ++c) {
+          nn = dot2_bf16(st.k[u][c].x, st.k[u][c].x, nn);
+          nn = dot2_bf16(st.k[u][c].y, st.k[u][c].y, nn);
+          nn = dot2_bf16(st.k[u][c].z, st.k[u][c].z, nn);
+          nn = dot2_bf16(st.k[u][c].w, st.k[u][c].w, nn);
+        }
         nn = group_sum<LPR>(nn);
-        const int j = jr[u];
+        const int j = st.j[u];
         if (j >= 0) {
           if (sub < G) {
             float v = l[u][0];
@@ -186,39 +221,58 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialArgs a) {
             for (int h = 1; h < G; ++h) v = (sub == h) ? l[u][h] : v;
             a.logits[(lrow * a.lld + j) * G + sub] = v;
           }
-          if (sub == 0 && a.key_norm) a.key_norm[lrow * a.ld + j] = sqrtf(nn);
+          if (sub == G % LPR && a.key_norm) a.key_norm[lrow * a.ld + j] = sqrtf(nn);
         }
       }
     }
-
-    float vf[U][8];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      vf[u][0] = bf_lo(vr[u].x); vf[u][1] = bf_hi(vr[u].x);
-      vf[u][2] = bf_lo(vr[u].y); vf[u][3] = bf_hi(vr[u].y);
-      vf[u][4] = bf_lo(vr[u].z); vf[u][5] = bf_hi(vr[u].z);
-      vf[u][6] = bf_lo(vr[u].w); vf[u][7] = bf_hi(vr[u].w);
-    }
-
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float mx = l[0][h];
 #pragma unroll
       for (int u = 1; u < U; ++u) mx = fmaxf(mx, l[u][h]);
-      const float mn = fmaxf(m[h], mx);
-      const float sc = exp2f(m[h] - mn);
-      m[h] = mn;
-      Z[h] *= sc;
+      const bool need = mx > m[h] + kSlack;
+      if (__any(need)) {
+        const float mn = need ? mx : m[h];
+        const float sc = exp2f(m[h] - mn);
+        m[h] = mn;
+        Z[h] *= sc;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] *= sc;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float pu = exp2f(l[u][h] - mn);
-        Z[h] += pu;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pu, vf[u][e], acc[h][e]);
+        for (int e = 0; e < DPL; ++e) acc[h][e] *= sc;
       }
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float pu[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        pu[h] = exp2f(l[u][h] - m[h]);
+        Z[h] += pu[h];
+      }
+#pragma unroll
+      for (int c = 0; c < NV; ++c) {
+        const uint32_t w4[4] = {st.v[u][c].x, st.v[u][c].y, st.v[u][c].z, st.v[u][c].w};
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) {
+          const float v0 = bf_lo(w4[q2]), v1 = bf_hi(w4[q2]);
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            acc[h][8 * c + 2 * q2] = fmaf(pu[h], v0, acc[h][8 * c + 2 * q2]);
+            acc[h][8 * c + 2 * q2 + 1] = fmaf(pu[h], v1, acc[h][8 * c + 2 * q2 + 1]);
+          }
+        }
+      }
+    }
+  };
+
+  // Two stages in flight: the loads of one stage overlap the math of the other.
+  constexpr int STEP = RPB * U;
+  Stage sa, sb;
+  load_stage(sa, p0 + rg);
+  for (int base = p0 + rg; base < p1; base += 2 * STEP) {
+    load_stage(sb, base + STEP);
+    consume(sa);
+    load_stage(sa, base + 2 * STEP);
+    consume(sb);
   }
 
   // Merge the lane groups of each wave (they hold the same dimensions).
@@ -232,7 +286,7 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialArgs a) {
       const float s1 = exp2f(m[h] - mn), s2 = exp2f(mo - mn);
       Z[h] = Z[h] * s1 + zo * s2;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] = acc[h][e] * s1 + __shfl_xor(acc[h][e], off) * s2;
+      for (int e = 0; e < DPL; ++e) acc[h][e] = acc[h][e] * s1 + __shfl_xor(acc[h][e], off) * s2;
       m[h] = mn;
     }
   }
@@ -242,7 +296,7 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialArgs a) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s_acc[wv][h][lane * 8 + e] = acc[h][e];
+      for (int e = 0; e < DPL; ++e) s_acc[wv][h][lane * DPL + e] = acc[h][e];
       if (lane == 0) {
         s_m[wv][h] = m[h];
         s_z[wv][h] = Z[h];
@@ -306,9 +360,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 template <int D, int G, int MODE, bool EVID>
 __global__ __launch_bounds__(kThreads) void finalize_kernel(FinalArgs a) {
   constexpr int NW = kThreads / 64;
-  constexpr int PARTS = kThreads / D;
   __shared__ float red[NW][G];
-  __shared__ float s_part[PARTS][D];
 
   const int b = batch_seq(a.batch_ids, blockIdx.z, a.B);
   if (b < 0) return;
@@ -382,19 +434,54 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(FinalArgs a) {
       Mh = (x == h) ? M[h] : Mh;
       Zh = (x == h) ? Zs[h] : Zh;
     }
+    // PARTS4 groups of D/4 threads; each thread merges 4 dims of every
+    // PARTS4-th partial, four partials in flight at a time.
+    constexpr int TPP = D / 4;
+    constexpr int PARTS4 = kThreads / TPP;
     const size_t row = hbase + x;
-    const int e = tid % D, part = tid / D;
-    float o = 0.f;
-    for (int s = part; s < S; s += PARTS) {
-      const float w = exp2f(a.part_ml[(row * a.stride + s) * 2] - Mh);
-      o = fmaf(w, a.part_o[(row * a.stride + s) * D + e], o);
+    const int e4 = tid % TPP, part = tid / TPP;
+    const float *pm = a.part_ml + row * a.stride * 2;
+    const float4 *po = reinterpret_cast<const float4 *>(a.part_o + row * a.stride * D) + e4;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    int s = part;
+    for (; s + 3 * PARTS4 < S; s += 4 * PARTS4) {
+      float4 v[4];
+      float w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[i] = po[(size_t)(s + i * PARTS4) * TPP];
+        w[i] = pm[(s + i * PARTS4) * 2];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float wi = exp2f(w[i] - Mh);
+        o.x = fmaf(wi, v[i].x, o.x);
+        o.y = fmaf(wi, v[i].y, o.y);
+        o.z = fmaf(wi, v[i].z, o.z);
+        o.w = fmaf(wi, v[i].w, o.w);
+      }
     }
-    s_part[part][e] = o;
+    for (; s < S; s += PARTS4) {
+      const float4 v = po[(size_t)s * TPP];
+      const float wi = exp2f(pm[s * 2] - Mh);
+      o.x = fmaf(wi, v.x, o.x);
+      o.y = fmaf(wi, v.y, o.y);
+      o.z = fmaf(wi, v.z, o.z);
+      o.w = fmaf(wi, v.w, o.w);
+    }
+    __shared__ float4 s_o4[PARTS4][TPP];
+    s_o4[part][e4] = o;
     __syncthreads();
     if (part == 0) {
 #pragma unroll
-      for (int p = 1; p < PARTS; ++p) o += s_part[p][e];
-      a.out[row * D + e] = (Zh > 0.f) ? o / Zh : 0.f;
+      for (int p = 1; p < PARTS4; ++p) {
+        const float4 t = s_o4[p][e4];
+        o.x += t.x; o.y += t.y; o.z += t.z; o.w += t.w;
+      }
+      const float rz = (Zh > 0.f) ? 1.0f / Zh : 0.f;
+      float4 r = make_float4(o.x * rz, o.y * rz, o.z * rz, o.w * rz);
+      if (Zh <= 0.f) r = make_float4(0.f, 0.f, 0.f, 0.f);
+      reinterpret_cast<float4 *>(a.out + row * D)[e4] = r;
     }
     return;
   }
@@ -406,25 +493,55 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(FinalArgs a) {
     const size_t lrow = (size_t)b * a.Hkv + g;
     const int j0 = (x - G) * kEvidChunk;
     const int j1 = min(n, j0 + kEvidChunk);
-    for (int j = j0 + tid; j < j1; j += kThreads) {
-      const float *lp = a.logits + (lrow * a.lld + j) * G;
+    constexpr int PER = kEvidChunk / kThreads;
+    float lg[PER][G];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int j = j0 + tid + i * kThreads;
+      const float *lp = a.logits + (lrow * a.lld + (size_t)min(j, j1 - 1)) * G;
+#pragma unroll
+      for (int h = 0; h < G; ++h) lg[i][h] = lp[h];
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int j = j0 + tid + i * kThreads;
       float f = 0.f;
 #pragma unroll
-      for (int h = 0; h < G; ++h) f = fmaf(exp2f(lp[h] - M[h]), rz[h], f);
-      a.evidence[lrow * a.ld + j] = f;
+      for (int h = 0; h < G; ++h) f = fmaf(exp2f(lg[i][h] - M[h]), rz[h], f);
+      if (j < j1) a.evidence[lrow * a.ld + j] = f;
     }
   }
 }
 
+// Resident workgroups of one kernel instance across the device (cached).
+template <typename Kern>
+int resident_slots(Kern kern) {
+  static int slots[16] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
+  if (slots[dev] == 0) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, kThreads, 0) != hipSuccess || nb < 1) nb = 1;
+    slots[dev] = nb * device_cu_count() * SFI_WAVES_OF_WG;
+  }
+  return slots[dev];
+}
+
 template <int D, int G, bool PAGED>
-hipError_t slow_t(const AttnLaunch &a, hipStream_t st) {
+hipError_t slow_t(const AttnLaunch &a_in, hipStream_t st) {
+  AttnLaunch a = a_in;
+  const bool side = a.evidence != nullptr || a.key_norm != nullptr;
+  {
+    const int slots = side ? resident_slots(partial_kernel<D, G, PAGED, MODE_SLOW, true>)
+                           : resident_slots(partial_kernel<D, G, PAGED, MODE_SLOW, false>);
+    a.plan = plan_splits(a.max_len, a.batch_n * a.Hkv, slots, a.plan.stride, 1 << 30);
+  }
   PartialArgs p{};
   p.B = a.B; p.max_len = a.max_len;
   p.kv = a.kv; p.seq_len = a.seq_len; p.batch_ids = a.batch_ids; p.q = a.q; p.Hq = a.Hq;
   p.chunk = a.plan.chunk; p.stride = a.plan.stride; p.part_o = a.part_o; p.part_ml = a.part_ml;
   p.logits = a.logits; p.lld = a.lld; p.key_norm = a.key_norm; p.ld = a.ld;
   p.qscale = kLog2e / sqrtf((float)D);
-  const bool side = a.evidence != nullptr || a.key_norm != nullptr;
   dim3 grid(a.plan.splits, a.Hkv, a.batch_n);
   if (side)
     hipLaunchKernelGGL((partial_kernel<D, G, PAGED, MODE_SLOW, true>), grid, dim3(kThreads), 0, st, p);
@@ -449,7 +566,13 @@ hipError_t slow_t(const AttnLaunch &a, hipStream_t st) {
 }
 
 template <int D, int G, bool PAGED>
-hipError_t fast_t(const AttnLaunch &a, hipStream_t st) {
+hipError_t fast_t(const AttnLaunch &a_in, hipStream_t st) {
+  AttnLaunch a = a_in;
+  {
+    const long long L = (long long)std::min(a.n_sink, a.max_len) + std::min(a.window, a.max_len) + a.sel_k;
+    const int slots = resident_slots(partial_kernel<D, G, PAGED, MODE_FAST, false>);
+    a.plan = plan_splits(L, a.batch_n * a.Hkv, slots, a.plan.stride, kMaxFastChunk);
+  }
   PartialArgs p{};
   p.B = a.B; p.max_len = a.max_len;
   p.kv = a.kv; p.seq_len = a.seq_len; p.batch_ids = a.batch_ids; p.q = a.q; p.Hq = a.Hq;
@@ -492,17 +615,43 @@ hipError_t fast_t(const AttnLaunch &a, hipStream_t st) {
 
 }  // namespace
 
-int slow_chunk_for(int batch_n, int Hkv, int max_seq_len) {
-  // Aim at >= 2048 workgroups (8 per CU) with chunks of 256..8192 rows.
-  const long long rows = (long long)batch_n * Hkv * max_seq_len;
-  int chunk = kMinSlowChunk;
-  while (chunk < kMaxSlowChunk && rows / (2LL * chunk) >= 2048) chunk *= 2;
-  return chunk;
+int device_cu_count() {
+  static int cus[16] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
+  if (cus[dev] == 0) {
+    int c = 0;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c < 1) c = 256;
+    cus[dev] = c;
+  }
+  return cus[dev];
+}
+
+SplitPlan plan_splits(long long L, int pairs, int slots, int stride, int max_chunk) {
+  SplitPlan pl{};
+  if (L < 1) L = 1;
+  if (pairs < 1) pairs = 1;
+  long long want = slots / pairs;  // splits per pair: fill the resident slots at most once
+  const long long by_rows = (L + kSplitGranule - 1) / kSplitGranule;
+  if (want > by_rows) want = by_rows;
+  if (want > stride) want = stride;
+  if (want < 1) want = 1;
+  long long chunk = (L + want - 1) / want;
+  chunk = (chunk + kSplitGranule - 1) / kSplitGranule * kSplitGranule;
+  if (chunk > max_chunk) chunk = max_chunk;
+  long long splits = (L + chunk - 1) / chunk;
+  if (splits > stride) {  // cannot happen for strides from split_stride(), kept as a guard
+    splits = stride;
+    chunk = (L + splits - 1) / splits;
+  }
+  pl.chunk = (int)chunk;
+  pl.splits = (int)splits;
+  pl.stride = stride;
+  return pl;
 }
 
 hipError_t launch_slow(const AttnLaunch &a, hipStream_t st) { SFI_DISPATCH(slow_t, a, st); }
 hipError_t launch_fast(const AttnLaunch &a, hipStream_t st) {
-  if (a.plan.chunk > kMaxFastChunk) return hipErrorInvalidValue;
   SFI_DISPATCH(fast_t, a, st);
 }
 

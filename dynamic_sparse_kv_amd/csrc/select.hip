@@ -7,16 +7,23 @@
 // the selectable keys becomes the next selected memory.  Vegas (section 2.A)
 // ranks aggregated verify logits the same way, with one list per sequence.
 //
-// Kernels, per (sequence, head row):
-//   stats_kernel  - chunked fp64 sums of key norms and squared norms;
-//   prior_kernel  - mean/std from those sums (fixed-order merge), unnormalised
-//                   prior weights w_j and chunked fp64 sums of w;
-//   topk_kernel   - one 1024-thread workgroup: s_j = (1-lambda) f_j +
-//                   lambda w_j / sum(w) fused into the first radix pass, a
-//                   12/12/8-bit radix select of the k-th largest key in LDS
-//                   histograms, then an ordered compaction (ballot-free block
-//                   scans) that emits the winners in ascending index order
-//                   with ties at the threshold going to the lowest indices.
+// One 1024-thread workgroup per (sequence, head row) does the whole job in a
+// single launch.  A block of 40960 keys is 10 slabs of 4096; thread t owns
+// keys 4t..4t+3 of every slab (one coalesced 16-byte access per slab).  When
+// the row fits one block (contexts up to 40K) the values never leave
+// registers between phases:
+//   1. fp64 sums of key norms and squared norms -> population mean and std;
+//   2. prior weights w_j = exp(-c z_j)(1 + exp(-(t-j)/tau)) and their fp64 sum;
+//   3. s_j = (1-lambda) f_j + lambda w_j / sum(w) on an order-preserving
+//      32-bit key, with the min and max key of the candidates;
+//   4. radix select of the k-th largest key: 12-bit LDS histograms starting
+//      at the highest bit where min and max differ (the bits above are
+//      common to every candidate, so the first digit already spreads the
+//      keys), stopping as soon as the threshold bin is taken whole;
+//   5. ordered compaction, one block scan per slab over packed (above,
+//      equal) counts: keys above the threshold plus the lowest-index keys
+//      equal to it, written in ascending index order.
+// Longer rows stream their blocks from L2 in every phase instead.
 #include "sfi_internal.hpp"
 
 namespace sfi {
@@ -24,7 +31,12 @@ namespace {
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kPerThread = 8;
+constexpr int kSlabs = 10;                        // slabs per block
+constexpr int kSlab = kSelThreads * 4;            // 4096 keys per slab
+constexpr int kVPT = kSlabs * 4;                  // values per thread per block
+constexpr int kBlock = kSelThreads * kVPT;        // 40960 keys
+constexpr int kDigit = 12;                        // radix digit width
+constexpr int kBins = 1 << kDigit;
 
 __device__ __forceinline__ double wave_sum_d(double x) {
 #pragma unroll
@@ -32,82 +44,45 @@ __device__ __forceinline__ double wave_sum_d(double x) {
   return x;
 }
 
-__global__ __launch_bounds__(256) void stats_kernel(SelectLaunch a) {
-  __shared__ double red[4][2];
-  const int b = batch_seq(a.batch_ids, blockIdx.z, a.B);
-  if (b < 0) return;
-  const int h = blockIdx.y;
-  const int n = clamp_len(a.seq_len, b, a.max_seq_len);
-  const int j0 = blockIdx.x * kStatChunk;
-  if (j0 >= n) return;
-  const int j1 = min(n, j0 + kStatChunk);
-  const size_t row = (size_t)b * a.H + h;
-  const float *nu = a.key_norm + row * a.ld;
-  double s1 = 0.0, s2 = 0.0;
-  for (int j = j0 + threadIdx.x; j < j1; j += 256) {
-    const double v = nu[j];
-    s1 += v;
-    s2 += v * v;
-  }
-  s1 = wave_sum_d(s1);
-  s2 = wave_sum_d(s2);
+// Sum over the workgroup in a fixed order (deterministic).
+__device__ __forceinline__ double block_sum_d(double x, double *s_red) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  x = wave_sum_d(x);
+  if (lane == 0) s_red[wv] = x;
+  __syncthreads();
+  double t = 0.0;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) t += s_red[w];
+  __syncthreads();
+  return t;
+}
+
+// Workgroup min and max of a key.
+__device__ __forceinline__ void block_minmax(uint32_t mn, uint32_t mx, uint32_t *s_u,
+                                             uint32_t *out_mn, uint32_t *out_mx) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, off));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, off));
+  }
   if (lane == 0) {
-    red[wv][0] = s1;
-    red[wv][1] = s2;
+    s_u[wv] = mn;
+    s_u[kSelWaves + wv] = mx;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    double t1 = 0.0, t2 = 0.0;
-    for (int w = 0; w < 4; ++w) {
-      t1 += red[w][0];
-      t2 += red[w][1];
-    }
-    a.stats[(row * a.nch + blockIdx.x) * 2 + 0] = t1;
-    a.stats[(row * a.nch + blockIdx.x) * 2 + 1] = t2;
+  uint32_t a = 0xFFFFFFFFu, b = 0u;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) {
+    a = min(a, s_u[w]);
+    b = max(b, s_u[kSelWaves + w]);
   }
-}
-
-__global__ __launch_bounds__(256) void prior_kernel(SelectLaunch a) {
-  __shared__ double red[4];
-  const int b = batch_seq(a.batch_ids, blockIdx.z, a.B);
-  if (b < 0) return;
-  const int h = blockIdx.y;
-  const int n = clamp_len(a.seq_len, b, a.max_seq_len);
-  const int j0 = blockIdx.x * kStatChunk;
-  if (j0 >= n) return;
-  const int j1 = min(n, j0 + kStatChunk);
-  const size_t row = (size_t)b * a.H + h;
-  const int nc = (n + kStatChunk - 1) / kStatChunk;
-  double t1 = 0.0, t2 = 0.0;
-  for (int c = 0; c < nc; ++c) {
-    t1 += a.stats[(row * a.nch + c) * 2 + 0];
-    t2 += a.stats[(row * a.nch + c) * 2 + 1];
-  }
-  const double mu = t1 / n;
-  const double var = fmax(t2 / n - mu * mu, 0.0);
-  const double sd = sqrt(var);
-  const float muf = (float)mu;
-  const float inv_sd = sd > 0.0 ? (float)(1.0 / sd) : 0.0f;
-  const float t = (float)(n - 1);
-  const float inv_tau = 1.0f / a.pos_tau;
-  const float *nu = a.key_norm + row * a.ld;
-  float *w = a.sbuf + row * a.sld;
-  double sw = 0.0;
-  for (int j = j0 + threadIdx.x; j < j1; j += 256) {
-    const float z = (nu[j] - muf) * inv_sd;
-    const float wj = expf(-a.norm_coef * z) * (1.0f + expf(-(t - (float)j) * inv_tau));
-    w[j] = wj;
-    sw += (double)wj;
-  }
-  sw = wave_sum_d(sw);
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  if (lane == 0) red[wv] = sw;
   __syncthreads();
-  if (threadIdx.x == 0) a.wsum[row * a.nch + blockIdx.x] = red[0] + red[1] + red[2] + red[3];
+  *out_mn = a;
+  *out_mx = b;
 }
 
-// Exclusive prefix sum over the 1024 threads in thread order; *total gets the sum.
+// Exclusive prefix sum over the workgroup in thread order; *total gets the sum.
 __device__ __forceinline__ int block_exscan(int v, int *s_wave, int *total) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   int x = v;
@@ -130,17 +105,17 @@ __device__ __forceinline__ int block_exscan(int v, int *s_wave, int *total) {
   return base + x - v;
 }
 
-// Given a histogram of NB bins, find the bin holding the want-th largest
-// element (want >= 1).  Returns the bin in *bin and the rank left inside it.
-template <int NB>
-__device__ __forceinline__ void find_bin(const unsigned *hist, int want, int *s_wave,
+// Bin of a histogram (nb <= kBins bins; highest bin = largest keys) that
+// holds the want-th largest element: s_res = {bin, rank inside, bin count}.
+__device__ __forceinline__ void find_bin(const unsigned *hist, int nb, int want, int *s_wave,
                                          int *s_res) {
   const int t = threadIdx.x;
   if (t == 0) {
     s_res[0] = 0;
     s_res[1] = 1;
+    s_res[2] = 0;
   }
-  const int hi = NB - 1 - 4 * t;
+  const int hi = nb - 1 - 4 * t;
   int cnt = 0;
   if (hi >= 0) {
 #pragma unroll
@@ -150,11 +125,12 @@ __device__ __forceinline__ void find_bin(const unsigned *hist, int want, int *s_
   const int above = block_exscan(cnt, s_wave, &total);
   if (hi >= 0 && above < want && want <= above + cnt) {
     int acc = above;
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4 && hi - i >= 0; ++i) {
       const int c = (int)hist[hi - i];
       if (acc + c >= want) {
         s_res[0] = hi - i;
         s_res[1] = want - acc;
+        s_res[2] = c;
         break;
       }
       acc += c;
@@ -164,10 +140,12 @@ __device__ __forceinline__ void find_bin(const unsigned *hist, int want, int *s_
 }
 
 template <bool FUSED>
-__global__ __launch_bounds__(kSelThreads) void topk_kernel(SelectLaunch a) {
-  __shared__ unsigned hist[4096];
+__global__ __launch_bounds__(kSelThreads) void select_kernel(SelectLaunch a) {
+  __shared__ unsigned hist[kBins];
   __shared__ int s_wave[kSelWaves];
-  __shared__ int s_res[2];
+  __shared__ uint32_t s_u[2 * kSelWaves];
+  __shared__ double s_red[kSelWaves];
+  __shared__ int s_res[3];
 
   const int b = batch_seq(a.batch_ids, blockIdx.y, a.B);
   if (b < 0) return;
@@ -179,112 +157,227 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(SelectLaunch a) {
   const int hi = max(a.n_sink, n - a.window);
   const int ncand = max(0, hi - lo);
   const int K = a.k;
+  const bool take_all = ncand <= K;
   int32_t *out = a.sel_idx + row * K;
 
-  // Scores of this row: FUSED writes s into sbuf during the first pass.
-  const float *src = FUSED ? (const float *)(a.sbuf + row * a.sld) : a.score + row * a.ld;
+  const int span = FUSED ? n : hi;  // keys [0, span) are visited
+  const int NB = (span + kBlock - 1) / kBlock;
+  const bool resident = NB <= 1;
+  const float *score = a.score + row * a.ld;
+  float *sb = FUSED ? a.sbuf + row * a.sld : nullptr;
+  const float *src = FUSED ? (const float *)sb : score;  // ranked values when streaming
 
-  for (int i = tid; i < 4096; i += kSelThreads) hist[i] = 0u;
-  __syncthreads();
-
-  if constexpr (FUSED) {
-    const int nc = (n + kStatChunk - 1) / kStatChunk;
-    double W = 0.0;
-    for (int c = 0; c < nc; ++c) W += a.wsum[row * a.nch + c];
-    const float cf = 1.0f - a.lambda;
-    const float cr = (float)((double)a.lambda / W);
-    const float *f = a.score + row * a.ld;
-    float *s = a.sbuf + row * a.sld;
-    for (int j = tid; j < n; j += kSelThreads) {
-      const float v = fmaf(cf, f[j], cr * s[j]);
-      s[j] = v;
-      if (j >= lo && j < hi && ncand > K) atomicAdd(&hist[float_key(v) >> 20], 1u);
-    }
-  } else {
-    if (ncand > K) {
-      for (int j = lo + tid; j < hi; j += kSelThreads) atomicAdd(&hist[float_key(src[j]) >> 20], 1u);
-    }
-  }
-  __syncthreads();
-
-  uint32_t thr = 0u;   // full 32-bit threshold key
-  int take_eq = 0;     // how many keys equal to thr are taken (lowest index first)
-  const bool take_all = ncand <= K;
-  if (!take_all) {
-    // pass 1: bits 31..20
-    find_bin<4096>(hist, K, s_wave, s_res);
-    const uint32_t b1 = (uint32_t)s_res[0];
-    int want = s_res[1];
-    __syncthreads();
-    for (int i = tid; i < 4096; i += kSelThreads) hist[i] = 0u;
-    __syncthreads();
-    // pass 2: bits 19..8 among keys whose top 12 bits equal b1
-    for (int j = lo + tid; j < hi; j += kSelThreads) {
-      const uint32_t key = float_key(src[j]);
-      if ((key >> 20) == b1) atomicAdd(&hist[(key >> 8) & 0xFFFu], 1u);
-    }
-    __syncthreads();
-    find_bin<4096>(hist, want, s_wave, s_res);
-    const uint32_t b2 = (uint32_t)s_res[0];
-    want = s_res[1];
-    __syncthreads();
-    for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0u;
-    __syncthreads();
-    const uint32_t pre = (b1 << 12) | b2;
-    // pass 3: bits 7..0
-    for (int j = lo + tid; j < hi; j += kSelThreads) {
-      const uint32_t key = float_key(src[j]);
-      if ((key >> 8) == pre) atomicAdd(&hist[key & 0xFFu], 1u);
-    }
-    __syncthreads();
-    find_bin<256>(hist, want, s_wave, s_res);
-    thr = (pre << 8) | (uint32_t)s_res[0];
-    take_eq = s_res[1];
-    __syncthreads();
-  }
-
-  // Ordered compaction: thread t owns kPerThread consecutive candidates of
-  // each tile, so winners come out in ascending index order.
-  int carry_eq = 0, carry_sel = 0;
-  constexpr int TILE = kSelThreads * kPerThread;
-  for (int base = lo; base < hi; base += TILE) {
-    const int j0 = base + tid * kPerThread;
-    uint32_t keys[kPerThread];
-    int gt = 0, eq = 0;
+  // Value i of this thread in block blk is key blk*kBlock + (i/4)*kSlab + 4*tid + i%4.
+  auto key_of = [&](int blk, int i) { return blk * kBlock + (i >> 2) * kSlab + 4 * tid + (i & 3); };
+  float v[kVPT];
+  auto load = [&](const float *p, int blk, bool vec) {
 #pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int j = j0 + i;
-      keys[i] = (j < hi) ? float_key(src[j]) : 0u;
-      if (j < hi) {
-        if (take_all || keys[i] > thr) ++gt;
-        else if (keys[i] == thr) ++eq;
+    for (int sl = 0; sl < kSlabs; ++sl) {
+      const int j = blk * kBlock + sl * kSlab + 4 * tid;
+      if (vec && j + 4 <= span) {
+        const float4 t = *reinterpret_cast<const float4 *>(p + j);
+        v[4 * sl + 0] = t.x; v[4 * sl + 1] = t.y; v[4 * sl + 2] = t.z; v[4 * sl + 3] = t.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[4 * sl + e] = (j + e < span) ? p[j + e] : 0.f;
       }
     }
-    int eq_tot;
-    const int eq_base = carry_eq + block_exscan(eq, s_wave, &eq_tot);
-    const int take_here = min(max(take_eq - eq_base, 0), eq);
-    int sel_tot;
-    const int sel_base = carry_sel + block_exscan(gt + take_here, s_wave, &sel_tot);
-    int pos = sel_base, er = eq_base;
+  };
+  auto store = [&](float *p, int blk, bool vec) {
 #pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int j = j0 + i;
-      if (j < hi) {
-        if (take_all || keys[i] > thr) {
-          if (pos < K) out[pos] = j;
-          ++pos;
-        } else if (keys[i] == thr) {
-          if (er < take_eq) {
+    for (int sl = 0; sl < kSlabs; ++sl) {
+      const int j = blk * kBlock + sl * kSlab + 4 * tid;
+      if (vec && j + 4 <= span) {
+        *reinterpret_cast<float4 *>(p + j) =
+            make_float4(v[4 * sl + 0], v[4 * sl + 1], v[4 * sl + 2], v[4 * sl + 3]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (j + e < span) p[j + e] = v[4 * sl + e];
+      }
+    }
+  };
+  // 16-byte accesses need 16-byte aligned rows.
+  const float *nu = FUSED ? a.key_norm + row * a.ld : nullptr;
+  const bool vsc = ((reinterpret_cast<uintptr_t>(score) | reinterpret_cast<uintptr_t>(nu)) & 15u) == 0;
+  const bool vsb = FUSED ? ((reinterpret_cast<uintptr_t>(sb) & 15u) == 0) : vsc;
+  const bool vsrc = FUSED ? vsb : vsc;
+
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;  // candidate key range of this thread
+  auto range_add = [&](int blk) {
+#pragma unroll
+    for (int i = 0; i < kVPT; ++i) {
+      const int j = key_of(blk, i);
+      if (j >= lo && j < hi) {
+        const uint32_t key = float_key(v[i]);
+        kmin = min(kmin, key);
+        kmax = max(kmax, key);
+      }
+    }
+  };
+
+  if constexpr (FUSED) {
+    // Mean and population variance in two passes (per-thread fp32 partials,
+    // fp64 across the workgroup), so no large-number cancellation.
+    float s1f = 0.f;
+    for (int blk = 0; blk < NB; ++blk) {
+      if (!resident || blk == 0) load(nu, blk, vsc);
+#pragma unroll
+      for (int i = 0; i < kVPT; ++i) s1f += v[i];
+    }
+    const double mu = n > 0 ? block_sum_d((double)s1f, s_red) / n : 0.0;
+    const float muf = (float)mu;
+    float s2f = 0.f;
+    for (int blk = 0; blk < NB; ++blk) {
+      if (!resident) load(nu, blk, vsc);
+#pragma unroll
+      for (int i = 0; i < kVPT; ++i) {
+        const float dv = (key_of(blk, i) < n) ? v[i] - muf : 0.f;
+        s2f = fmaf(dv, dv, s2f);
+      }
+    }
+    const double var = n > 0 ? block_sum_d((double)s2f, s_red) / n : 0.0;
+    const double sd = sqrt(var);
+    const float isd = sd > 0.0 ? (float)(1.0 / sd) : 0.0f;
+    const float tq = (float)(n - 1);
+    // w_j = exp(-c z_j) (1 + exp(-(t - j)/tau)) evaluated as powers of two.
+    const float cz = -a.norm_coef * isd * kLog2e;
+    const float ct = kLog2e / a.pos_tau;
+    double sw = 0.0;
+    for (int blk = 0; blk < NB; ++blk) {
+      if (!resident) load(nu, blk, vsc);
+      float swf = 0.f;
+#pragma unroll
+      for (int i = 0; i < kVPT; ++i) {
+        const int j = key_of(blk, i);
+        const float w = (j < n) ? exp2f(cz * (v[i] - muf)) * (1.0f + exp2f(((float)j - tq) * ct)) : 0.f;
+        v[i] = w;
+        swf += w;
+      }
+      sw += (double)swf;
+      if (!resident) store(sb, blk, vsb);
+    }
+    const double W = block_sum_d(sw, s_red);
+    const float cf = 1.0f - a.lambda;
+    const float cr = W > 0.0 ? (float)((double)a.lambda / W) : 0.f;
+    for (int blk = 0; blk < NB; ++blk) {
+      if (!resident) load(sb, blk, vsb);
+#pragma unroll
+      for (int sl = 0; sl < kSlabs; ++sl) {
+        const int j = blk * kBlock + sl * kSlab + 4 * tid;
+        float f4[4];
+        if (vsc && j + 4 <= span) {
+          const float4 t = *reinterpret_cast<const float4 *>(score + j);
+          f4[0] = t.x; f4[1] = t.y; f4[2] = t.z; f4[3] = t.w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) f4[e] = (j + e < span) ? score[j + e] : 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[4 * sl + e] = fmaf(cf, f4[e], cr * v[4 * sl + e]);
+      }
+      if (!resident || a.store_s) store(sb, blk, vsb);
+      range_add(blk);
+    }
+  } else {
+    for (int blk = 0; blk < NB; ++blk) {
+      load(score, blk, vsc);
+      range_add(blk);
+    }
+  }
+  block_minmax(kmin, kmax, s_u, &kmin, &kmax);
+
+  // Radix select.  Selected = keys whose bits at and above `lvl` exceed `thr`,
+  // plus the first take_eq (by index) of those equal to it.
+  uint32_t thr = 0u;
+  int lvl = 0;
+  int take_eq = 0;
+  if (!take_all) {
+    const uint32_t diff = kmin ^ kmax;
+    if (diff == 0u) {  // every candidate has the same key
+      thr = kmax;
+      take_eq = K;
+    } else {
+      int top = 31 - __builtin_clz(diff);                       // highest differing bit
+      uint32_t prefix = (top >= 31) ? 0u : (kmax >> (top + 1));  // common bits above it
+      int want = K;
+      for (;;) {
+        const int lo_bit = max(top - kDigit + 1, 0);
+        const int width = top - lo_bit + 1;
+        const uint32_t dmask = (1u << width) - 1u;
+        for (int i = tid; i < (1 << width); i += kSelThreads) hist[i] = 0u;
+        __syncthreads();
+        for (int blk = 0; blk < NB; ++blk) {
+          if (!resident) load(src, blk, vsrc);
+#pragma unroll
+          for (int i = 0; i < kVPT; ++i) {
+            const int j = key_of(blk, i);
+            if (j >= lo && j < hi) {
+              const uint32_t key = float_key(v[i]);
+              const uint32_t up = (top >= 31) ? 0u : (key >> (top + 1));
+              if (up == prefix) atomicAdd(&hist[(key >> lo_bit) & dmask], 1u);
+            }
+          }
+        }
+        __syncthreads();
+        find_bin(hist, 1 << width, want, s_wave, s_res);
+        const uint32_t bin = (uint32_t)s_res[0];
+        want = s_res[1];
+        const int cnt = s_res[2];
+        __syncthreads();
+        prefix = (width >= 32) ? bin : ((prefix << width) | bin);
+        if (lo_bit == 0 || want == cnt) {  // exact key reached, or the whole bin is taken
+          thr = prefix;
+          lvl = lo_bit;
+          take_eq = want;
+          break;
+        }
+        top = lo_bit - 1;
+      }
+    }
+  }
+
+  // Ordered compaction, slab by slab: one scan of packed (above, equal)
+  // counts gives each thread the number of winners before its 4 keys.
+  int carry_gt = 0, carry_eq = 0;
+  for (int blk = 0; blk < NB; ++blk) {
+    if (!resident) load(src, blk, vsrc);
+#pragma unroll
+    for (int sl = 0; sl < kSlabs; ++sl) {
+      int gt = 0, eq = 0;
+      uint32_t keys[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = key_of(blk, 4 * sl + e);
+        keys[e] = float_key(v[4 * sl + e]) >> lvl;
+        const bool in = j >= lo && j < hi;
+        gt += (in && (take_all || keys[e] > thr)) ? 1 : 0;
+        eq += (in && !take_all && keys[e] == thr) ? 1 : 0;
+      }
+      int tot;
+      const int pre = block_exscan((gt << 16) | eq, s_wave, &tot);
+      int eqb = carry_eq + (pre & 0xFFFF);
+      int pos = carry_gt + (pre >> 16) + min(eqb, take_eq);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = key_of(blk, 4 * sl + e);
+        if (j >= lo && j < hi) {
+          bool take = take_all || keys[e] > thr;
+          if (!take && keys[e] == thr) {
+            take = eqb < take_eq;
+            ++eqb;
+          }
+          if (take) {
             if (pos < K) out[pos] = j;
             ++pos;
           }
-          ++er;
         }
       }
+      carry_gt += tot >> 16;
+      carry_eq += tot & 0xFFFF;
     }
-    carry_eq += eq_tot;
-    carry_sel += sel_tot;
   }
+  const int carry_sel = carry_gt + min(carry_eq, take_eq);
   for (int i = carry_sel + tid; i < K; i += kSelThreads) out[i] = -1;
   if (tid == 0) a.sel_count[row] = min(carry_sel, K);
 }
@@ -292,18 +385,10 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(SelectLaunch a) {
 }  // namespace
 
 hipError_t launch_select(const SelectLaunch &a, hipStream_t st) {
-  if (a.mode == 0) {
-    dim3 g1(a.nch, a.H, a.batch_n);
-    hipLaunchKernelGGL(stats_kernel, g1, dim3(256), 0, st, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(prior_kernel, g1, dim3(256), 0, st, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(topk_kernel<true>, dim3(a.H, a.batch_n), dim3(kSelThreads), 0, st, a);
-  } else {
-    hipLaunchKernelGGL(topk_kernel<false>, dim3(a.H, a.batch_n), dim3(kSelThreads), 0, st, a);
-  }
+  if (a.mode == 0)
+    hipLaunchKernelGGL(select_kernel<true>, dim3(a.H, a.batch_n), dim3(kSelThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(select_kernel<false>, dim3(a.H, a.batch_n), dim3(kSelThreads), 0, st, a);
   return hipGetLastError();
 }
 

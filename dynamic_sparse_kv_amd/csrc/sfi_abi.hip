@@ -4,6 +4,8 @@
 
 #include <string.h>
 
+#include <algorithm>
+
 #include "sfi_internal.hpp"
 
 namespace {
@@ -64,7 +66,7 @@ struct SlowWs {
 
 SlowWs slow_ws(const sfi_kv *kv) {
   SlowWs w{};
-  w.stride = (kv->max_seq_len + kMinSlowChunk - 1) / kMinSlowChunk;
+  w.stride = split_stride(kv->max_seq_len);
   const size_t rows = (size_t)kv->B * kv->Hq * w.stride;
   w.o = 0;
   w.ml = align_up(w.o + rows * kv->d * sizeof(float));
@@ -80,10 +82,9 @@ struct FastWs {
 
 FastWs fast_ws(const sfi_kv *kv, int sel_k, int n_sink, int window) {
   FastWs w{};
-  const long long L = (long long)n_sink + window + sel_k;
-  const long long Lb = L < kv->max_seq_len + (long long)sel_k ? L : kv->max_seq_len + (long long)sel_k;
-  w.stride = (int)((Lb + kFastChunk - 1) / kFastChunk);
-  if (w.stride < 1) w.stride = 1;
+  const long long L = (long long)std::min(n_sink, kv->max_seq_len) +
+                      std::min(window, kv->max_seq_len) + sel_k;
+  w.stride = split_stride(L);
   const size_t rows = (size_t)kv->B * kv->Hq * w.stride;
   w.o = 0;
   w.ml = align_up(rows * kv->d * sizeof(float));
@@ -92,18 +93,14 @@ FastWs fast_ws(const sfi_kv *kv, int sel_k, int n_sink, int window) {
 }
 
 struct SelWs {
-  size_t stats, wsum, sbuf, total;
-  int nch;
+  size_t sbuf, total;
 };
 
 SelWs select_ws(int B, int H, int max_seq_len) {
   SelWs w{};
-  w.nch = (max_seq_len + kStatChunk - 1) / kStatChunk;
   const size_t rows = (size_t)B * H;
-  w.stats = 0;
-  w.wsum = align_up(rows * w.nch * 2 * sizeof(double));
-  w.sbuf = align_up(w.wsum + rows * w.nch * sizeof(double));
-  w.total = align_up(w.sbuf + rows * (size_t)max_seq_len * sizeof(float));
+  w.sbuf = 0;
+  w.total = align_up(rows * (size_t)max_seq_len * sizeof(float));
   return w;
 }
 
@@ -179,9 +176,7 @@ sfi_status sfi_slow_step(const sfi_kv *kv, const int32_t *batch_ids, int32_t bat
   a.out = out;
   a.part_o = carve<float>(ws, w.o);
   a.part_ml = carve<float>(ws, w.ml);
-  a.plan.chunk = slow_chunk_for(batch_n, kv->Hkv, kv->max_seq_len);
-  a.plan.splits = (kv->max_seq_len + a.plan.chunk - 1) / a.plan.chunk;
-  a.plan.stride = w.stride;
+  a.plan.stride = w.stride;  // chunking is planned by the launcher
   a.logits = carve<float>(ws, w.logits);
   a.lld = kv->max_seq_len;
   a.evidence = evidence;
@@ -223,13 +218,12 @@ sfi_status sfi_select(const sfi_select_params *p, const int32_t *batch_ids, int3
   if (fused && fused_out) {
     a.sbuf = fused_out;
     a.sld = ld;
+    a.store_s = true;
   } else {
     a.sbuf = carve<float>(ws, w.sbuf);
     a.sld = max_seq_len;
+    a.store_s = false;
   }
-  a.stats = carve<double>(ws, w.stats);
-  a.wsum = carve<double>(ws, w.wsum);
-  a.nch = w.nch;
   return launch_select(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SFI_OK : SFI_ERR_HIP;
 }
 
@@ -263,9 +257,7 @@ sfi_status sfi_fast_step(const sfi_kv *kv, const int32_t *batch_ids, int32_t bat
   a.out = out;
   a.part_o = carve<float>(ws, w.o);
   a.part_ml = carve<float>(ws, w.ml);
-  a.plan.chunk = kFastChunk;
-  a.plan.splits = w.stride;
-  a.plan.stride = w.stride;
+  a.plan.stride = w.stride;  // chunking is planned by the launcher
   a.sel_idx = sel_idx;
   a.sel_count = sel_count;
   a.sel_heads = sel_heads;

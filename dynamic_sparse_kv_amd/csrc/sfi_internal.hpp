@@ -9,13 +9,13 @@
 
 namespace sfi {
 
-// Rows per workgroup of the split-K kernels.
-constexpr int kMinSlowChunk = 256;
-constexpr int kMaxSlowChunk = 8192;
-constexpr int kFastChunk = 128;
-// Keys per workgroup of the evidence / prior passes.
+// Split-K planning: a (sequence, kv head) row range is cut into chunks of a
+// multiple of kSplitGranule rows, at most kMaxSplits per pair.
+constexpr int kSplitGranule = 32;
+constexpr int kMaxSplits = 512;
+constexpr int kMaxFastChunk = 1024;  // fast-step chunks stage their row ids in LDS
+// Keys per workgroup of the evidence pass.
 constexpr int kEvidChunk = 2048;
-constexpr int kStatChunk = 4096;
 
 // Plan of a split-K decode launch.
 struct SplitPlan {
@@ -24,7 +24,19 @@ struct SplitPlan {
   int stride;  // split stride of the partial buffers (>= splits)
 };
 
-int slow_chunk_for(int batch_n, int Hkv, int max_seq_len);
+// Partial-buffer stride (splits per pair) that covers L rows.
+inline int split_stride(long long L) {
+  long long s = (L + kSplitGranule - 1) / kSplitGranule;
+  if (s < 1) s = 1;
+  return s > kMaxSplits ? kMaxSplits : (int)s;
+}
+
+// Chunking of L rows per pair over `pairs` pairs so that one launch fills
+// `slots` resident workgroups once, within the stride and a chunk cap.
+SplitPlan plan_splits(long long L, int pairs, int slots, int stride, int max_chunk);
+
+// Compute units of the current device (cached per device).
+int device_cu_count();
 
 struct AttnLaunch {
   KVView kv;
@@ -68,11 +80,9 @@ struct SelectLaunch {
   int ld;
   int32_t *sel_idx;
   int32_t *sel_count;
-  float *sbuf;        // [B][H][ld]: fused_out or workspace
+  float *sbuf;        // [B][H][sld]: fused_out or workspace
   int sld;
-  double *stats;      // [B][H][nch][2]
-  double *wsum;       // [B][H][nch]
-  int nch;
+  bool store_s;       // write s to sbuf even when the row stays in registers
 };
 
 hipError_t launch_select(const SelectLaunch &a, hipStream_t st);

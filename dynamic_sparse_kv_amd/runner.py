@@ -88,11 +88,12 @@ class SFIDecoder:
         self.ws_fast = torch.empty(self.ws_fast_bytes, **u8)
 
     # -- single calls -------------------------------------------------------
-    def slow(self, q, seq_len, batch_ids, batch_n: int, stream=None, select: bool = True):
+    def slow(self, q, seq_len, batch_ids, batch_n: int, stream=None, select: bool = True, out=None):
         """Dense step + evidence for the listed sequences, then the selector."""
         self.kv.seq_len = seq_len.data_ptr() if torch.is_tensor(seq_len) else seq_len
-        sfi.sfi_slow_step(self.kv, batch_ids, batch_n, q, self.out, self.evidence, self.key_norm,
-                          self.ld, self.ws_slow, self.ws_slow_bytes, stream)
+        sfi.sfi_slow_step(self.kv, batch_ids, batch_n, q, self.out if out is None else out,
+                          self.evidence, self.key_norm, self.ld, self.ws_slow, self.ws_slow_bytes,
+                          stream)
         if select:
             self.slow_select_only(self.kv.seq_len, batch_ids, batch_n, stream)
 
@@ -109,22 +110,62 @@ class SFIDecoder:
         sfi.sfi_slow_step(self.kv, batch_ids, batch_n, q, self.out, None, None, self.ld,
                           self.ws_slow, self.ws_slow_bytes, stream)
 
-    def fast(self, q, seq_len, batch_ids, batch_n: int, stream=None):
+    def fast(self, q, seq_len, batch_ids, batch_n: int, stream=None, out=None):
         self.kv.seq_len = seq_len.data_ptr() if torch.is_tensor(seq_len) else seq_len
         sfi.sfi_fast_step(self.kv, batch_ids, batch_n, q, self.sel_idx, self.sel_count, self.Hkv,
-                          self.k, self.n_sink, self.window, self.out, self.ws_fast,
-                          self.ws_fast_bytes, stream)
+                          self.k, self.n_sink, self.window, self.out if out is None else out,
+                          self.ws_fast, self.ws_fast_bytes, stream)
 
     # -- one decode step of a planned run ------------------------------------
-    def step(self, plan: DecodePlan, s: int, q_steps, stream=None):
+    def step(self, plan: DecodePlan, s: int, q_steps, stream=None, out=None):
         """Decode step s: q_steps is the device tensor [steps][B][Hq][d]."""
         q = q_steps[s]
         sl = plan.seq_len[s]
         ns, nf = int(plan.n_slow[s]), int(plan.n_fast[s])
         if ns:
-            self.slow(q, sl, plan.slow_ids[s], ns, stream)
+            self.slow(q, sl, plan.slow_ids[s], ns, stream, out=out)
         if nf:
-            self.fast(q, sl, plan.fast_ids[s], nf, stream)
+            self.fast(q, sl, plan.fast_ids[s], nf, stream, out=out)
+
+    def run_two_streams(self, plan: DecodePlan, q_steps, s_begin: int, s_end: int, stream_a,
+                        stream_b, out_steps=None):
+        """Steps [s_begin, s_end) as two overlapping chains.
+
+        Stream A carries each step's slow steps and selector, stream B its fast
+        steps, so the selector of step s runs while the fast steps of step s
+        stream their rows (the asynchronous pipeline of the Slow-Fast Inference
+        pages, technical summary section 3.C).  Ordering: B(s) waits for A(s-1)
+        (a sequence refreshed at s-1 reads its new index list at s), and A(s)
+        waits for B(s-1) (the selector may only overwrite a list once the fast
+        steps that read it are done).  Both chains join back into stream_a.
+        out_steps, if given, is [steps][B][Hq][d] and receives each step's
+        output; otherwise the shared output buffer is used (still race-free:
+        the two chains never write the same slot concurrently).
+        """
+        start = torch.cuda.Event()
+        start.record(stream_a)
+        stream_b.wait_event(start)
+        prev_a = prev_b = None
+        for s in range(s_begin, s_end):
+            q = q_steps[s]
+            sl = plan.seq_len[s]
+            out = None if out_steps is None else out_steps[s]
+            ns, nf = int(plan.n_slow[s]), int(plan.n_fast[s])
+            if prev_b is not None:
+                stream_a.wait_event(prev_b)
+            if ns:
+                self.slow(q, sl, plan.slow_ids[s], ns, stream_a, out=out)
+            ev_a = torch.cuda.Event()
+            ev_a.record(stream_a)
+            if prev_a is not None:
+                stream_b.wait_event(prev_a)
+            if nf:
+                self.fast(q, sl, plan.fast_ids[s], nf, stream_b, out=out)
+            ev_b = torch.cuda.Event()
+            ev_b.record(stream_b)
+            prev_a, prev_b = ev_a, ev_b
+        if prev_b is not None:
+            stream_a.wait_event(prev_b)
 
 
 class VegasDecoder:

@@ -189,6 +189,27 @@ def test_select_fused_from_oracle_evidence():
     _say(f"  near-tie differences: {ties}")
 
 
+def test_select_fused_long_row_streams_blocks():
+    """Rows longer than one register block (40960 keys) take the streaming path."""
+    _say("select fused long row")
+    B, Hq, Hkv, d = 1, 4, 2, 64
+    n = 50001
+    K, V = _rand_kv(B, Hkv, n, d, seed=23, hh=40)
+    q = _rand_q((B, Hq, d), seed=24)
+    Kb, Vb, qb = _bits(K), _bits(V), _bits(q)
+    _, p = O.dense_step(qb[0], Kb[0], Vb[0], n)
+    fb = O.evidence(p, Hkv)
+    s_ref = O.fuse(fb, O.prior(Kb[0], n), 0.2)
+    f = torch.from_numpy(fb.astype(np.float32)[None]).to(DEV).contiguous()
+    nu = torch.from_numpy(O.key_norms(Kb[0], n).astype(np.float32)[None]).to(DEV).contiguous()
+    k = 3000
+    sel, cnt, fo = _select_gpu(sfi.SFI_SCORE_FUSED, f, nu, [n], k, 4, 256, lam=0.2, fused=True)
+    lo, hi = O.candidate_range(n, 4, 256)
+    assert row_rel_err(fo[0], s_ref) <= EVID_TOL
+    ties = sum(check_selection(sel[0, g], cnt[0, g], s_ref[g], lo, hi, k) for g in range(Hkv))
+    _say(f"  near-tie differences: {ties}")
+
+
 # ----------------------------------------------------------------- fast step
 
 def _fast_gpu(K, V, Hq, q, lens, sel_np, cnt_np, n_sink, window, sel_heads):
@@ -308,6 +329,49 @@ def test_bitwise_repeatable():
     for a, b in zip(outs[0], outs[1]):
         assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a,
                            b.view(torch.int32) if b.dtype == torch.float32 else b)
+
+
+def test_two_stream_pipeline_matches_single_stream():
+    """Slow chain and fast steps on two streams give the same bits per step."""
+    cfg = W.CONFIGS["c1"].replace(B=3, steps=40, k=128)
+    K, V = W.make_kv(cfg, device=DEV)
+    starts = W.sentence_starts(cfg)
+    slow = O.schedule(starts, cfg.budget)
+    q = W.make_queries(cfg, starts).to(DEV)
+    plan = DecodePlan(slow, W.context_lengths(cfg), DEV)
+    res = []
+    for mode in ("one", "two", "graph"):
+        dec = SFIDecoder(K, V, cfg.Hq, cfg.ctx + cfg.steps, n_sink=4, window=256, k=cfg.k, lam=cfg.lam)
+        outs = torch.zeros((cfg.steps, cfg.B, cfg.Hq, cfg.d), device=DEV)
+        if mode == "one":
+            for s in range(cfg.steps):
+                dec.step(plan, s, q, out=outs[s])
+        elif mode == "two":
+            sa = torch.cuda.current_stream()
+            sb = torch.cuda.Stream()
+            dec.run_two_streams(plan, q, 0, cfg.steps, sa, sb, out_steps=outs)
+        else:
+            g = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            sb = torch.cuda.Stream()
+            with torch.cuda.stream(side):
+                with torch.cuda.graph(g, stream=side):
+                    dec.run_two_streams(plan, q, 0, cfg.steps, side, sb, out_steps=outs)
+            torch.cuda.synchronize()
+            reps = []
+            for _ in range(3):       # replays separated by host work and syncs
+                outs.zero_()
+                torch.cuda.synchronize()
+                g.replay()
+                torch.cuda.synchronize()
+                reps.append(outs.clone())
+            for r in reps[1:]:
+                assert torch.equal(r.view(torch.int32), reps[0].view(torch.int32))
+        torch.cuda.synchronize()
+        res.append(outs.clone())
+    assert torch.equal(res[0].view(torch.int32), res[1].view(torch.int32))
+    assert torch.equal(res[0].view(torch.int32), res[2].view(torch.int32))
 
 
 # ------------------------------------------------------------------- verify
