@@ -153,17 +153,15 @@ def main():
     torch.cuda.synchronize()
 
     # ---- headline: K steps replayed from one HIP graph -------------------
-    # Slow steps + selector on one stream, fast steps on a second one, joined
-    # per step (each chain waits for the other's previous step).
     use_graph = not args.no_graph
     side = torch.cuda.Stream()
-    side_b = torch.cuda.Stream()
     if use_graph:
         g = torch.cuda.CUDAGraph()
         side.wait_stream(stream)
         with torch.cuda.stream(side):
             with torch.cuda.graph(g, stream=side):
-                dec.run_two_streams(plan, q, 0, K_steps, side, side_b)
+                for s in range(K_steps):
+                    dec.step(plan, s, q, side)
         torch.cuda.synchronize()
         g.replay()                      # untimed replay (first launch of the graph)
         torch.cuda.synchronize()
@@ -175,7 +173,7 @@ def main():
     else:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        dec.run_two_streams(plan, q, 0, K_steps, stream, side_b)
+        run_steps(K_steps)
         torch.cuda.synchronize()
         t_total = time.perf_counter() - t0
     tokens = cfg.B * K_steps
@@ -271,8 +269,7 @@ def main():
                                f"lambda {cfg.lam}, {K_steps} decode steps",
                    "global_batch": cfg.B, "seq_len": cfg.ctx, "parallelism": "none (1 GPU)",
                    "slow_fraction": round(float(plan.slow[:K_steps].mean()), 4),
-                   "timing": ("hip graph replay, slow+selector and fast steps on two streams"
-                              if use_graph else "eager, two streams")},
+                   "timing": "hip graph replay, one stream" if use_graph else "eager, one stream"},
         "roofline": roofline,
         "per_call": per_call,
         "dense_tokens_per_s": round(dense_tps, 1),

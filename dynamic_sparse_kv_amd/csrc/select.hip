@@ -12,17 +12,19 @@
 // keys 4t..4t+3 of every slab (one coalesced 16-byte access per slab).  When
 // the row fits one block (contexts up to 40K) the values never leave
 // registers between phases:
-//   1. fp64 sums of key norms and squared norms -> population mean and std;
-//   2. prior weights w_j = exp(-c z_j)(1 + exp(-(t-j)/tau)) and their fp64 sum;
-//   3. s_j = (1-lambda) f_j + lambda w_j / sum(w) on an order-preserving
-//      32-bit key, with the min and max key of the candidates;
+//   1. mean, then population variance of the key norms (two passes, fp32
+//      per thread, fp64 across the workgroup);
+//   2. prior weights w_j = exp(-c z_j)(1 + exp(-(t-j)/tau)) and their sum;
+//   3. s_j = (1-lambda) f_j + lambda w_j / sum(w), turned into an
+//      order-preserving 32-bit key, with the min and max key of the
+//      candidates;
 //   4. radix select of the k-th largest key: 12-bit LDS histograms starting
 //      at the highest bit where min and max differ (the bits above are
 //      common to every candidate, so the first digit already spreads the
 //      keys), stopping as soon as the threshold bin is taken whole;
-//   5. ordered compaction, one block scan per slab over packed (above,
-//      equal) counts: keys above the threshold plus the lowest-index keys
-//      equal to it, written in ascending index order.
+//   5. ordered compaction through LDS bitmaps: winners (and, when the
+//      threshold key is tied, the lowest-index ties) are marked, one scan of
+//      per-word popcounts places every word, indices come out ascending.
 // Longer rows stream their blocks from L2 in every phase instead.
 #include "sfi_internal.hpp"
 
@@ -37,6 +39,7 @@ constexpr int kVPT = kSlabs * 4;                  // values per thread per block
 constexpr int kBlock = kSelThreads * kVPT;        // 40960 keys
 constexpr int kDigit = 12;                        // radix digit width
 constexpr int kBins = 1 << kDigit;
+constexpr int kWords = kBlock / 32;               // bitmap words per block
 
 __device__ __forceinline__ double wave_sum_d(double x) {
 #pragma unroll
@@ -81,6 +84,10 @@ __device__ __forceinline__ void block_minmax(uint32_t mn, uint32_t mx, uint32_t 
   *out_mn = a;
   *out_mx = b;
 }
+
+// Population count as a signed int (HIP's __popc returns unsigned, which would
+// turn differences of counts into wrapped unsigned values).
+__device__ __forceinline__ int popc32(uint32_t x) { return (int)__popc(x); }
 
 // Exclusive prefix sum over the workgroup in thread order; *total gets the sum.
 __device__ __forceinline__ int block_exscan(int v, int *s_wave, int *total) {
@@ -142,6 +149,8 @@ __device__ __forceinline__ void find_bin(const unsigned *hist, int nb, int want,
 template <bool FUSED>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectLaunch a) {
   __shared__ unsigned hist[kBins];
+  __shared__ uint32_t bm_sel[kWords];  // per-block bitmap of winners
+  __shared__ uint32_t bm_eq[kWords];   // per-block bitmap of threshold ties
   __shared__ int s_wave[kSelWaves];
   __shared__ uint32_t s_u[2 * kSelWaves];
   __shared__ double s_red[kSelWaves];
@@ -169,17 +178,20 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectLaunch a) {
 
   // Value i of this thread in block blk is key blk*kBlock + (i/4)*kSlab + 4*tid + i%4.
   auto key_of = [&](int blk, int i) { return blk * kBlock + (i >> 2) * kSlab + 4 * tid + (i & 3); };
-  float v[kVPT];
+  // u[] holds the raw float bits of the current block until make_keys turns
+  // them into order-preserving keys in place.
+  uint32_t u[kVPT];
   auto load = [&](const float *p, int blk, bool vec) {
 #pragma unroll
     for (int sl = 0; sl < kSlabs; ++sl) {
       const int j = blk * kBlock + sl * kSlab + 4 * tid;
       if (vec && j + 4 <= span) {
         const float4 t = *reinterpret_cast<const float4 *>(p + j);
-        v[4 * sl + 0] = t.x; v[4 * sl + 1] = t.y; v[4 * sl + 2] = t.z; v[4 * sl + 3] = t.w;
+        u[4 * sl + 0] = __float_as_uint(t.x); u[4 * sl + 1] = __float_as_uint(t.y);
+        u[4 * sl + 2] = __float_as_uint(t.z); u[4 * sl + 3] = __float_as_uint(t.w);
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[4 * sl + e] = (j + e < span) ? p[j + e] : 0.f;
+        for (int e = 0; e < 4; ++e) u[4 * sl + e] = __float_as_uint((j + e < span) ? p[j + e] : 0.f);
       }
     }
   };
@@ -189,11 +201,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectLaunch a) {
       const int j = blk * kBlock + sl * kSlab + 4 * tid;
       if (vec && j + 4 <= span) {
         *reinterpret_cast<float4 *>(p + j) =
-            make_float4(v[4 * sl + 0], v[4 * sl + 1], v[4 * sl + 2], v[4 * sl + 3]);
+            make_float4(__uint_as_float(u[4 * sl + 0]), __uint_as_float(u[4 * sl + 1]),
+                        __uint_as_float(u[4 * sl + 2]), __uint_as_float(u[4 * sl + 3]));
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (j + e < span) p[j + e] = v[4 * sl + e];
+          if (j + e < span) p[j + e] = __uint_as_float(u[4 * sl + e]);
       }
     }
   };
@@ -203,16 +216,35 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectLaunch a) {
   const bool vsb = FUSED ? ((reinterpret_cast<uintptr_t>(sb) & 15u) == 0) : vsc;
   const bool vsrc = FUSED ? vsb : vsc;
 
+  // Keys of non-candidates (j outside [lo, hi)) are set to 0.  Every finite
+  // or infinite score maps to a key >= 0x007FFFFF, and the radix digits never
+  // put such a key in the bin of 0, so 0 marks "not a candidate" exactly.
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;  // candidate key range of this thread
-  auto range_add = [&](int blk) {
+  auto make_keys = [&](int blk) {
+#pragma unroll
+    for (int sl = 0; sl < kSlabs; ++sl) {
+      const int j0 = blk * kBlock + sl * kSlab + 4 * tid;
+      const bool all_in = j0 >= lo && j0 + 3 < hi;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * sl + e;
+        const bool in = all_in || (j0 + e >= lo && j0 + e < hi);
+        u[i] = in ? float_key(__uint_as_float(u[i])) : 0u;
+      }
+    }
+  };
+  auto range_add = [&]() {
 #pragma unroll
     for (int i = 0; i < kVPT; ++i) {
-      const int j = key_of(blk, i);
-      if (j >= lo && j < hi) {
-        const uint32_t key = float_key(v[i]);
-        kmin = min(kmin, key);
-        kmax = max(kmax, key);
-      }
+      kmin = min(kmin, u[i] ? u[i] : 0xFFFFFFFFu);
+      kmax = max(kmax, u[i]);
+    }
+  };
+  // Keys of block blk: already in registers for a resident row, else reloaded.
+  auto block_keys = [&](int blk) {
+    if (!resident) {
+      load(src, blk, vsrc);
+      make_keys(blk);
     }
   };
 
@@ -223,7 +255,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectLaunch a) {
     for (int blk = 0; blk < NB; ++blk) {
       if (!resident || blk == 0) load(nu, blk, vsc);
 #pragma unroll
-      for (int i = 0; i < kVPT; ++i) s1f += v[i];
+      for (int i = 0; i < kVPT; ++i) s1f += __uint_as_float(u[i]);
     }
     const double mu = n > 0 ? block_sum_d((double)s1f, s_red) / n : 0.0;
     const float muf = (float)mu;
@@ -232,7 +264,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectLaunch a) {
       if (!resident) load(nu, blk, vsc);
 #pragma unroll
       for (int i = 0; i < kVPT; ++i) {
-        const float dv = (key_of(blk, i) < n) ? v[i] - muf : 0.f;
+        const float dv = (key_of(blk, i) < n) ? __uint_as_float(u[i]) - muf : 0.f;
         s2f = fmaf(dv, dv, s2f);
       }
     }
@@ -250,8 +282,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectLaunch a) {
 #pragma unroll
       for (int i = 0; i < kVPT; ++i) {
         const int j = key_of(blk, i);
-        const float w = (j < n) ? exp2f(cz * (v[i] - muf)) * (1.0f + exp2f(((float)j - tq) * ct)) : 0.f;
-        v[i] = w;
+        const float w = (j < n) ? exp2f(cz * (__uint_as_float(u[i]) - muf)) * (1.0f + exp2f(((float)j - tq) * ct)) : 0.f;
+        u[i] = __float_as_uint(w);
         swf += w;
       }
       sw += (double)swf;
@@ -274,15 +306,18 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectLaunch a) {
           for (int e = 0; e < 4; ++e) f4[e] = (j + e < span) ? score[j + e] : 0.f;
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[4 * sl + e] = fmaf(cf, f4[e], cr * v[4 * sl + e]);
+        for (int e = 0; e < 4; ++e)
+          u[4 * sl + e] = __float_as_uint(fmaf(cf, f4[e], cr * __uint_as_float(u[4 * sl + e])));
       }
       if (!resident || a.store_s) store(sb, blk, vsb);
-      range_add(blk);
+      make_keys(blk);
+      range_add();
     }
   } else {
     for (int blk = 0; blk < NB; ++blk) {
       load(score, blk, vsc);
-      range_add(blk);
+      make_keys(blk);
+      range_add();
     }
   }
   block_minmax(kmin, kmax, s_u, &kmin, &kmax);
@@ -292,11 +327,13 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectLaunch a) {
   uint32_t thr = 0u;
   int lvl = 0;
   int take_eq = 0;
+  int eq_total = 0;  // candidates whose (key >> lvl) equals thr
   if (!take_all) {
     const uint32_t diff = kmin ^ kmax;
     if (diff == 0u) {  // every candidate has the same key
       thr = kmax;
       take_eq = K;
+      eq_total = ncand;
     } else {
       int top = 31 - __builtin_clz(diff);                       // highest differing bit
       uint32_t prefix = (top >= 31) ? 0u : (kmax >> (top + 1));  // common bits above it
@@ -307,16 +344,13 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectLaunch a) {
         const uint32_t dmask = (1u << width) - 1u;
         for (int i = tid; i < (1 << width); i += kSelThreads) hist[i] = 0u;
         __syncthreads();
+        const int sh_up = top + 1;
         for (int blk = 0; blk < NB; ++blk) {
-          if (!resident) load(src, blk, vsrc);
+          block_keys(blk);
 #pragma unroll
           for (int i = 0; i < kVPT; ++i) {
-            const int j = key_of(blk, i);
-            if (j >= lo && j < hi) {
-              const uint32_t key = float_key(v[i]);
-              const uint32_t up = (top >= 31) ? 0u : (key >> (top + 1));
-              if (up == prefix) atomicAdd(&hist[(key >> lo_bit) & dmask], 1u);
-            }
+            const uint32_t up = (sh_up >= 32) ? 0u : (u[i] >> sh_up);
+            if (u[i] && up == prefix) atomicAdd(&hist[(u[i] >> lo_bit) & dmask], 1u);
           }
         }
         __syncthreads();
@@ -330,6 +364,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectLaunch a) {
           thr = prefix;
           lvl = lo_bit;
           take_eq = want;
+          eq_total = cnt;
           break;
         }
         top = lo_bit - 1;
@@ -337,47 +372,85 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectLaunch a) {
     }
   }
 
-  // Ordered compaction, slab by slab: one scan of packed (above, equal)
-  // counts gives each thread the number of winners before its 4 keys.
-  int carry_gt = 0, carry_eq = 0;
+  // Ordered compaction through per-block bitmaps: winners are marked in
+  // bm_sel (ties at the threshold in bm_eq, of which the first take_eq by
+  // index are kept), then one scan of per-word popcounts gives every word
+  // its output offset, so indices come out ascending.
+  const bool ge_mode = take_all || take_eq == eq_total;  // the whole tie bin is taken
+  const bool inc = (tid * 2) < kWords;
+  int carry_eq = 0, carry_sel = 0;
   for (int blk = 0; blk < NB; ++blk) {
-    if (!resident) load(src, blk, vsrc);
+    for (int w = tid; w < kWords; w += kSelThreads) {
+      bm_sel[w] = 0u;
+      bm_eq[w] = 0u;
+    }
+    __syncthreads();
+    block_keys(blk);
 #pragma unroll
     for (int sl = 0; sl < kSlabs; ++sl) {
-      int gt = 0, eq = 0;
-      uint32_t keys[4];
+      uint32_t ngt = 0u, neq = 0u;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int j = key_of(blk, 4 * sl + e);
-        keys[e] = float_key(v[4 * sl + e]) >> lvl;
-        const bool in = j >= lo && j < hi;
-        gt += (in && (take_all || keys[e] > thr)) ? 1 : 0;
-        eq += (in && !take_all && keys[e] == thr) ? 1 : 0;
+        const int i = 4 * sl + e;
+        const bool in = u[i] != 0u;
+        const uint32_t kk = u[i] >> lvl;
+        const bool gt = in && (take_all || (ge_mode ? kk >= thr : kk > thr));
+        const bool eq = in && !ge_mode && kk == thr;
+        ngt |= (gt ? 1u : 0u) << e;
+        neq |= (eq ? 1u : 0u) << e;
       }
-      int tot;
-      const int pre = block_exscan((gt << 16) | eq, s_wave, &tot);
-      int eqb = carry_eq + (pre & 0xFFFF);
-      int pos = carry_gt + (pre >> 16) + min(eqb, take_eq);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = key_of(blk, 4 * sl + e);
-        if (j >= lo && j < hi) {
-          bool take = take_all || keys[e] > thr;
-          if (!take && keys[e] == thr) {
-            take = eqb < take_eq;
-            ++eqb;
-          }
-          if (take) {
-            if (pos < K) out[pos] = j;
-            ++pos;
-          }
-        }
-      }
-      carry_gt += tot >> 16;
-      carry_eq += tot & 0xFFFF;
+      const int word = sl * (kSlab / 32) + (tid >> 3);
+      const int sh = (tid & 7) * 4;
+      if (ngt) atomicOr(&bm_sel[word], ngt << sh);
+      if (neq) atomicOr(&bm_eq[word], neq << sh);
     }
+    __syncthreads();
+    if (!ge_mode) {
+      const uint32_t e0 = inc ? bm_eq[2 * tid] : 0u, e1 = inc ? bm_eq[2 * tid + 1] : 0u;
+      int tot;
+      const int before = carry_eq + block_exscan(popc32(e0) + popc32(e1), s_wave, &tot);
+      if (inc) {
+        // keep the lowest `m` set bits of each tie word
+        int m0 = min(max(take_eq - before, 0), popc32(e0));
+        uint32_t keep0 = 0u, w0 = e0;
+        for (; m0 > 0; --m0) { const uint32_t lb = w0 & (0u - w0); keep0 |= lb; w0 ^= lb; }
+        int m1 = min(max(take_eq - before - popc32(e0), 0), popc32(e1));
+        uint32_t keep1 = 0u, w1 = e1;
+        for (; m1 > 0; --m1) { const uint32_t lb = w1 & (0u - w1); keep1 |= lb; w1 ^= lb; }
+        bm_sel[2 * tid] |= keep0;
+        bm_sel[2 * tid + 1] |= keep1;
+      }
+      carry_eq += tot;
+      __syncthreads();
+    }
+    const uint32_t s0 = inc ? bm_sel[2 * tid] : 0u, s1 = inc ? bm_sel[2 * tid + 1] : 0u;
+    int tot;
+    int pos = carry_sel + block_exscan(popc32(s0) + popc32(s1), s_wave, &tot);
+    if (inc) {
+      const int base = blk * kBlock;
+      uint32_t w = s0;
+      while (w) {
+        const int bit = __ffs(w) - 1;
+        w &= w - 1u;
+        // word 2t holds keys of slab (2t / 128), lanes 4*(t' ...): decode its key index
+        const int wd = 2 * tid;
+        const int j = base + (wd / (kSlab / 32)) * kSlab + (wd % (kSlab / 32)) * 32 + bit;
+        if (pos < K) out[pos] = j;
+        ++pos;
+      }
+      w = s1;
+      while (w) {
+        const int bit = __ffs(w) - 1;
+        w &= w - 1u;
+        const int wd = 2 * tid + 1;
+        const int j = base + (wd / (kSlab / 32)) * kSlab + (wd % (kSlab / 32)) * 32 + bit;
+        if (pos < K) out[pos] = j;
+        ++pos;
+      }
+    }
+    carry_sel += tot;
+    __syncthreads();
   }
-  const int carry_sel = carry_gt + min(carry_eq, take_eq);
   for (int i = carry_sel + tid; i < K; i += kSelThreads) out[i] = -1;
   if (tid == 0) a.sel_count[row] = min(carry_sel, K);
 }

@@ -47,6 +47,21 @@ class DecodePlan:
             self.n_fast[s] = len(fi)
         self.slow_ids = _dev_i32(slow_ids, device)
         self.fast_ids = _dev_i32(fast_ids, device)
+        # fast sequences split by whether they were refreshed on the step before
+        old_ids = np.zeros((steps, B), dtype=np.int32)
+        new_ids = np.zeros((steps, B), dtype=np.int32)
+        self.n_fast_old = np.zeros(steps, dtype=np.int64)
+        self.n_fast_new = np.zeros(steps, dtype=np.int64)
+        for s in range(steps):
+            fresh = self.slow[s - 1] if s > 0 else np.zeros(B, dtype=bool)
+            oi = np.nonzero(~self.slow[s] & ~fresh)[0]
+            ni = np.nonzero(~self.slow[s] & fresh)[0]
+            old_ids[s, : len(oi)] = oi
+            new_ids[s, : len(ni)] = ni
+            self.n_fast_old[s] = len(oi)
+            self.n_fast_new[s] = len(ni)
+        self.fast_old_ids = _dev_i32(old_ids, device)
+        self.fast_new_ids = _dev_i32(new_ids, device)
 
 
 class SFIDecoder:
@@ -79,6 +94,15 @@ class SFIDecoder:
         self.fused = torch.zeros((B, Hkv, self.ld), **f32) if keep_fused else None
         self.sel_idx = torch.full((B, Hkv, k), -1, dtype=torch.int32, device=dev)
         self.sel_count = torch.zeros((B, Hkv), dtype=torch.int32, device=dev)
+        # second evidence / key-norm copy for the pipelined schedule (allocated
+        # here, never inside a graph capture)
+        self.evidence_alt = torch.zeros((B, Hkv, self.ld), **f32)
+        self.key_norm_alt = torch.zeros((B, Hkv, self.ld), **f32)
+        # Events of the multi-stream schedules.  They stay referenced for the
+        # decoder's lifetime: an event destroyed while a graph capture that
+        # recorded or waited on it is still open leaves the capture holding a
+        # dangling handle.
+        self._events = []
         u8 = dict(dtype=torch.uint8, device=dev)
         self.ws_slow_bytes = sfi.sfi_slow_workspace_bytes(self.kv)
         self.ws_sel_bytes = sfi.sfi_select_workspace_bytes(B, Hkv, self.max_len)
@@ -116,6 +140,11 @@ class SFIDecoder:
                           self.k, self.n_sink, self.window, self.out if out is None else out,
                           self.ws_fast, self.ws_fast_bytes, stream)
 
+    def _new_event(self):
+        e = torch.cuda.Event()
+        self._events.append(e)
+        return e
+
     # -- one decode step of a planned run ------------------------------------
     def step(self, plan: DecodePlan, s: int, q_steps, stream=None, out=None):
         """Decode step s: q_steps is the device tensor [steps][B][Hq][d]."""
@@ -126,6 +155,76 @@ class SFIDecoder:
             self.slow(q, sl, plan.slow_ids[s], ns, stream, out=out)
         if nf:
             self.fast(q, sl, plan.fast_ids[s], nf, stream, out=out)
+
+    def run_pipelined(self, plan: DecodePlan, q_steps, s_begin: int, s_end: int, stream_a,
+                      stream_b, stream_c, out_steps):
+        """Steps [s_begin, s_end) as three overlapping chains.
+
+        A: slow steps (dense attention + evidence), C: the selector, B: fast
+        steps -- the asynchronous pipeline of the Slow-Fast Inference pages
+        (technical summary section 3.C), which hides the selector behind other
+        attention work.  The evidence and key-norm buffers alternate between
+        two copies by step parity, so the slow step of s+1 may run while the
+        selector of s still reads the copy of s.  Dependencies, per step s:
+          A(s) after the last selector that read copy s % 2;
+          C(s) after A(s) and after B(s-1) (fast steps still reading the
+               index lists C(s) rewrites);
+          B(s) fast steps of sequences refreshed at s-1 after C(s-1); the
+               other fast steps need nothing new (B is one ordered chain).
+        out_steps ([steps][B][Hq][d]) receives each step's output: the chains
+        may run different steps at the same time.  All chains join back into
+        stream_a.
+        """
+        copies = [(self.evidence, self.key_norm), (self.evidence_alt, self.key_norm_alt)]
+        ev = self._new_event
+        start = ev()
+        start.record(stream_a)
+        stream_b.wait_event(start)
+        stream_c.wait_event(start)
+        last_c_parity = [None, None]
+        prev_b = None
+        prev_c = None
+        for s in range(s_begin, s_end):
+            q = q_steps[s]
+            sl = plan.seq_len[s]
+            out = out_steps[s]
+            ns = int(plan.n_slow[s])
+            c_ev = None
+            if ns:
+                ev_buf, kn_buf = copies[s % 2]
+                if last_c_parity[s % 2] is not None:
+                    stream_a.wait_event(last_c_parity[s % 2])
+                self.kv.seq_len = sl.data_ptr()
+                sfi.sfi_slow_step(self.kv, plan.slow_ids[s], ns, q, out, ev_buf, kn_buf, self.ld,
+                                  self.ws_slow, self.ws_slow_bytes, stream_a)
+                a_ev = ev()
+                a_ev.record(stream_a)
+                stream_c.wait_event(a_ev)
+                if prev_b is not None:
+                    stream_c.wait_event(prev_b)
+                sfi.sfi_select(self.params, plan.slow_ids[s], ns, sl.data_ptr(), self.B, self.Hkv,
+                               self.max_len, ev_buf, kn_buf, self.ld, self.sel_idx, self.sel_count,
+                               None, self.ws_sel, self.ws_sel_bytes, stream_c)
+                c_ev = ev()
+                c_ev.record(stream_c)
+                last_c_parity[s % 2] = c_ev
+            no, nn = int(plan.n_fast_old[s]), int(plan.n_fast_new[s])
+            if no:
+                self.fast(q, sl, plan.fast_old_ids[s], no, stream_b, out=out)
+            if nn:
+                if prev_c is not None:
+                    stream_b.wait_event(prev_c)
+                self.fast(q, sl, plan.fast_new_ids[s], nn, stream_b, out=out)
+            b_ev = ev()
+            b_ev.record(stream_b)
+            prev_b = b_ev
+            prev_c = c_ev
+        end_b = ev()
+        end_b.record(stream_b)
+        end_c = ev()
+        end_c.record(stream_c)
+        stream_a.wait_event(end_b)
+        stream_a.wait_event(end_c)
 
     def run_two_streams(self, plan: DecodePlan, q_steps, s_begin: int, s_end: int, stream_a,
                         stream_b, out_steps=None):
@@ -142,7 +241,8 @@ class SFIDecoder:
         output; otherwise the shared output buffer is used (still race-free:
         the two chains never write the same slot concurrently).
         """
-        start = torch.cuda.Event()
+        ev = self._new_event
+        start = ev()
         start.record(stream_a)
         stream_b.wait_event(start)
         prev_a = prev_b = None
@@ -155,13 +255,13 @@ class SFIDecoder:
                 stream_a.wait_event(prev_b)
             if ns:
                 self.slow(q, sl, plan.slow_ids[s], ns, stream_a, out=out)
-            ev_a = torch.cuda.Event()
+            ev_a = ev()
             ev_a.record(stream_a)
             if prev_a is not None:
                 stream_b.wait_event(prev_a)
             if nf:
                 self.fast(q, sl, plan.fast_ids[s], nf, stream_b, out=out)
-            ev_b = torch.cuda.Event()
+            ev_b = ev()
             ev_b.record(stream_b)
             prev_a, prev_b = ev_a, ev_b
         if prev_b is not None:
