@@ -22,6 +22,7 @@
 //     steps, turns the per-key logits written on the way into the evidence
 //     f_j = (1/G) sum_h p_hj.
 #include <algorithm>
+#include <type_traits>
 
 #include "sfi_internal.hpp"
 
@@ -33,6 +34,9 @@ namespace {
 #endif
 #ifndef SFI_WAVES_OF_WG
 #define SFI_WAVES_OF_WG 1
+#endif
+#ifndef SFI_FUSE_FAST_COMBINE
+#define SFI_FUSE_FAST_COMBINE 0
 #endif
 
 enum { MODE_SLOW = 0, MODE_FAST = 1 };
@@ -57,6 +61,8 @@ struct PartialArgs {
   const int32_t *sel_count;
   int sel_heads, sel_k, n_sink, window;
   float qscale;  // log2(e) / sqrt(d)
+  unsigned *counters;  // fast step, fused combine: [B][Hkv] arrival counters
+  float *out;          // fast step, fused combine: [B][Hq][D]
 };
 
 // Fast-step row list of (b, g): [sinks | window | selected].
@@ -112,8 +118,29 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialArgs a) {
     L = fl.length();
   }
   const int p0 = split * a.chunk;
-  if (p0 >= L) return;
+  if (p0 >= L) {
+    if constexpr (MODE == MODE_FAST && SFI_FUSE_FAST_COMBINE) {
+      // an empty row list has no partials to merge: its output is zero
+      if (L == 0 && split == 0)
+        for (int idx = tid; idx < G * D; idx += kThreads)
+          a.out[((size_t)b * a.Hq + g * G) * D + idx] = 0.f;
+    }
+    return;
+  }
   const int p1 = min(L, p0 + a.chunk);
+
+  const int sub = tid % LPR;
+  const int rg = tid / LPR;
+
+  uint32_t qv[G][4 * NV];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+#pragma unroll
+    for (int c = 0; c < NV; ++c) {
+      const uint4 t = ldg16(a.q + ((size_t)b * a.Hq + g * G + h) * D + sub * DPL + 8 * c);
+      qv[h][4 * c + 0] = t.x; qv[h][4 * c + 1] = t.y; qv[h][4 * c + 2] = t.z; qv[h][4 * c + 3] = t.w;
+    }
+  }
 
   if constexpr (MODE == MODE_FAST) {
     for (int p = p0 + tid; p < p1; p += kThreads) {
@@ -131,18 +158,6 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialArgs a) {
     __syncthreads();
   }
 
-  const int sub = tid % LPR;
-  const int rg = tid / LPR;
-
-  uint32_t qv[G][4 * NV];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-#pragma unroll
-    for (int c = 0; c < NV; ++c) {
-      const uint4 t = ldg16(a.q + ((size_t)b * a.Hq + g * G + h) * D + sub * DPL + 8 * c);
-      qv[h][4 * c + 0] = t.x; qv[h][4 * c + 1] = t.y; qv[h][4 * c + 2] = t.z; qv[h][4 * c + 3] = t.w;
-    }
-  }
 
   float m[G], Z[G], acc[G][DPL];
 #pragma unroll
@@ -275,32 +290,54 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialArgs a) {
     consume(sb);
   }
 
-  // Merge the lane groups of each wave (they hold the same dimensions).
-#pragma unroll
-  for (int off = LPR; off < 64; off <<= 1) {
+  // Merge the lane groups of each wave as a reduce-scatter: in the round
+  // with partner lane ^ off, each lane keeps half of its dimensions (the half
+  // chosen by bit `off` of its lane id), receives the partner's values for
+  // that half and combines them; the other half goes to the partner.  The
+  // xor-8 round stays inside a 16-lane row and uses a DPP rotate.
+  const int lane = tid & 63, wv = tid >> 6;
+  int dim_off = 0;
+  auto merge_round = [&](auto off_c, auto half_c) {
+    constexpr int OFF = decltype(off_c)::value;
+    constexpr int HALF = decltype(half_c)::value;
+    const bool bit = (lane & OFF) != 0;
+    auto xch = [&](float x) -> float {
+      if constexpr (OFF == 8) return dpp_f32<0x128>(x);  // row_ror:8 == lane ^ 8 within a row
+      else return __shfl_xor(x, OFF);
+    };
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float mo = __shfl_xor(m[h], off);
-      const float zo = __shfl_xor(Z[h], off);
+      const float mo = xch(m[h]);
+      const float zo = xch(Z[h]);
       const float mn = fmaxf(m[h], mo);
       const float s1 = exp2f(m[h] - mn), s2 = exp2f(mo - mn);
       Z[h] = Z[h] * s1 + zo * s2;
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[h][e] = acc[h][e] * s1 + __shfl_xor(acc[h][e], off) * s2;
       m[h] = mn;
-    }
-  }
-
-  const int lane = tid & 63, wv = tid >> 6;
-  if (lane < LPR) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) s_acc[wv][h][lane * DPL + e] = acc[h][e];
-      if (lane == 0) {
-        s_m[wv][h] = m[h];
-        s_z[wv][h] = Z[h];
+      for (int i = 0; i < HALF; ++i) {
+        const float keep = bit ? acc[h][HALF + i] : acc[h][i];
+        const float send = bit ? acc[h][i] : acc[h][HALF + i];
+        acc[h][i] = keep * s1 + xch(send) * s2;
       }
+    }
+    dim_off += bit ? HALF : 0;
+  };
+  if constexpr (LPR == 8) {
+    merge_round(std::integral_constant<int, 8>{}, std::integral_constant<int, DPL / 2>{});
+    merge_round(std::integral_constant<int, 16>{}, std::integral_constant<int, DPL / 4>{});
+    merge_round(std::integral_constant<int, 32>{}, std::integral_constant<int, DPL / 8>{});
+  } else {
+    merge_round(std::integral_constant<int, 16>{}, std::integral_constant<int, DPL / 2>{});
+    merge_round(std::integral_constant<int, 32>{}, std::integral_constant<int, DPL / 4>{});
+  }
+  constexpr int KEPT = (LPR == 8) ? DPL / 8 : DPL / 4;  // dims per lane after the rounds
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+#pragma unroll
+    for (int i = 0; i < KEPT; ++i) s_acc[wv][h][sub * DPL + dim_off + i] = acc[h][i];
+    if (lane == 0) {
+      s_m[wv][h] = m[h];
+      s_z[wv][h] = Z[h];
     }
   }
   __syncthreads();
@@ -322,6 +359,39 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialArgs a) {
     if (e == 0) {
       a.part_ml[slot * 2 + 0] = M;
       a.part_ml[slot * 2 + 1] = z;
+    }
+  }
+
+  if constexpr (MODE == MODE_FAST && SFI_FUSE_FAST_COMBINE) {
+    // The last workgroup of this (sequence, kv head) to arrive merges all
+    // partials in split order (release/acquire at agent scope around the
+    // arrival counter; the counter is reset for the next call).
+    __shared__ int s_last;
+    __threadfence();
+    __syncthreads();
+    const int S = (L + a.chunk - 1) / a.chunk;
+    if (tid == 0) {
+      unsigned *cnt = a.counters + (size_t)b * a.kv.Hkv + g;
+      const unsigned old = atomicAdd(cnt, 1u);
+      const int last = old == (unsigned)(S - 1);
+      if (last) atomicExch(cnt, 0u);
+      s_last = last;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    for (int idx = tid; idx < G * D; idx += kThreads) {
+      const int h = idx / D, e = idx % D;
+      const size_t row = ((size_t)b * a.Hq + g * G + h) * a.stride;
+      float M = kNegBig;
+      for (int s2 = 0; s2 < S; ++s2) M = fmaxf(M, a.part_ml[(row + s2) * 2]);
+      float o = 0.f, z = 0.f;
+      for (int s2 = 0; s2 < S; ++s2) {
+        const float w = exp2f(a.part_ml[(row + s2) * 2] - M);
+        z = fmaf(a.part_ml[(row + s2) * 2 + 1], w, z);
+        o = fmaf(a.part_o[(row + s2) * D + e], w, o);
+      }
+      a.out[((size_t)b * a.Hq + g * G + h) * D + e] = (z > 0.f) ? o / z : 0.f;
     }
   }
 }
@@ -580,10 +650,13 @@ hipError_t fast_t(const AttnLaunch &a_in, hipStream_t st) {
   p.sel_idx = a.sel_idx; p.sel_count = a.sel_count; p.sel_heads = a.sel_heads; p.sel_k = a.sel_k;
   p.n_sink = a.n_sink; p.window = a.window;
   p.qscale = kLog2e / sqrtf((float)D);
+  p.counters = a.counters;
+  p.out = a.out;
   dim3 grid(a.plan.splits, a.Hkv, a.batch_n);
   hipLaunchKernelGGL((partial_kernel<D, G, PAGED, MODE_FAST, false>), grid, dim3(kThreads), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (SFI_FUSE_FAST_COMBINE) return hipSuccess;
   FinalArgs f{};
   f.B = a.B; f.max_len = a.max_len;
   f.seq_len = a.seq_len; f.batch_ids = a.batch_ids; f.Hq = a.Hq; f.Hkv = a.Hkv;
