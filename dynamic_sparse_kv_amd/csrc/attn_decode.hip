@@ -35,9 +35,6 @@ namespace {
 #ifndef SFI_WAVES_OF_WG
 #define SFI_WAVES_OF_WG 1
 #endif
-#ifndef SFI_FUSE_FAST_COMBINE
-#define SFI_FUSE_FAST_COMBINE 0
-#endif
 
 enum { MODE_SLOW = 0, MODE_FAST = 1 };
 constexpr int kThreads = 256;
@@ -61,8 +58,6 @@ struct PartialArgs {
   const int32_t *sel_count;
   int sel_heads, sel_k, n_sink, window;
   float qscale;  // log2(e) / sqrt(d)
-  unsigned *counters;  // fast step, fused combine: [B][Hkv] arrival counters
-  float *out;          // fast step, fused combine: [B][Hq][D]
 };
 
 // Fast-step row list of (b, g): [sinks | window | selected].
@@ -118,15 +113,7 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialArgs a) {
     L = fl.length();
   }
   const int p0 = split * a.chunk;
-  if (p0 >= L) {
-    if constexpr (MODE == MODE_FAST && SFI_FUSE_FAST_COMBINE) {
-      // an empty row list has no partials to merge: its output is zero
-      if (L == 0 && split == 0)
-        for (int idx = tid; idx < G * D; idx += kThreads)
-          a.out[((size_t)b * a.Hq + g * G) * D + idx] = 0.f;
-    }
-    return;
-  }
+  if (p0 >= L) return;
   const int p1 = min(L, p0 + a.chunk);
 
   const int sub = tid % LPR;
@@ -359,39 +346,6 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialArgs a) {
     if (e == 0) {
       a.part_ml[slot * 2 + 0] = M;
       a.part_ml[slot * 2 + 1] = z;
-    }
-  }
-
-  if constexpr (MODE == MODE_FAST && SFI_FUSE_FAST_COMBINE) {
-    // The last workgroup of this (sequence, kv head) to arrive merges all
-    // partials in split order (release/acquire at agent scope around the
-    // arrival counter; the counter is reset for the next call).
-    __shared__ int s_last;
-    __threadfence();
-    __syncthreads();
-    const int S = (L + a.chunk - 1) / a.chunk;
-    if (tid == 0) {
-      unsigned *cnt = a.counters + (size_t)b * a.kv.Hkv + g;
-      const unsigned old = atomicAdd(cnt, 1u);
-      const int last = old == (unsigned)(S - 1);
-      if (last) atomicExch(cnt, 0u);
-      s_last = last;
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    for (int idx = tid; idx < G * D; idx += kThreads) {
-      const int h = idx / D, e = idx % D;
-      const size_t row = ((size_t)b * a.Hq + g * G + h) * a.stride;
-      float M = kNegBig;
-      for (int s2 = 0; s2 < S; ++s2) M = fmaxf(M, a.part_ml[(row + s2) * 2]);
-      float o = 0.f, z = 0.f;
-      for (int s2 = 0; s2 < S; ++s2) {
-        const float w = exp2f(a.part_ml[(row + s2) * 2] - M);
-        z = fmaf(a.part_ml[(row + s2) * 2 + 1], w, z);
-        o = fmaf(a.part_o[(row + s2) * D + e], w, o);
-      }
-      a.out[((size_t)b * a.Hq + g * G + h) * D + e] = (z > 0.f) ? o / z : 0.f;
     }
   }
 }
@@ -650,13 +604,10 @@ hipError_t fast_t(const AttnLaunch &a_in, hipStream_t st) {
   p.sel_idx = a.sel_idx; p.sel_count = a.sel_count; p.sel_heads = a.sel_heads; p.sel_k = a.sel_k;
   p.n_sink = a.n_sink; p.window = a.window;
   p.qscale = kLog2e / sqrtf((float)D);
-  p.counters = a.counters;
-  p.out = a.out;
   dim3 grid(a.plan.splits, a.Hkv, a.batch_n);
   hipLaunchKernelGGL((partial_kernel<D, G, PAGED, MODE_FAST, false>), grid, dim3(kThreads), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (SFI_FUSE_FAST_COMBINE) return hipSuccess;
   FinalArgs f{};
   f.B = a.B; f.max_len = a.max_len;
   f.seq_len = a.seq_len; f.batch_ids = a.batch_ids; f.Hq = a.Hq; f.Hkv = a.Hkv;

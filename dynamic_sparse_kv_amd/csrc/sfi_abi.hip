@@ -76,7 +76,7 @@ SlowWs slow_ws(const sfi_kv *kv) {
 }
 
 struct FastWs {
-  size_t o, ml, cnt, total;
+  size_t o, ml, total;
   int stride;
 };
 
@@ -88,8 +88,7 @@ FastWs fast_ws(const sfi_kv *kv, int sel_k, int n_sink, int window) {
   const size_t rows = (size_t)kv->B * kv->Hq * w.stride;
   w.o = 0;
   w.ml = align_up(rows * kv->d * sizeof(float));
-  w.cnt = align_up(w.ml + rows * 2 * sizeof(float));
-  w.total = align_up(w.cnt + (size_t)kv->B * kv->Hkv * sizeof(unsigned));
+  w.total = align_up(w.ml + rows * 2 * sizeof(float));
   return w;
 }
 
@@ -258,7 +257,6 @@ sfi_status sfi_fast_step(const sfi_kv *kv, const int32_t *batch_ids, int32_t bat
   a.out = out;
   a.part_o = carve<float>(ws, w.o);
   a.part_ml = carve<float>(ws, w.ml);
-  a.counters = carve<unsigned>(ws, w.cnt);
   a.plan.stride = w.stride;  // chunking is planned by the launcher
   a.sel_idx = sel_idx;
   a.sel_count = sel_count;

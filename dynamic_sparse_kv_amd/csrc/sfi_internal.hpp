@@ -62,7 +62,6 @@ struct AttnLaunch {
   const int32_t *sel_idx;
   const int32_t *sel_count;
   int sel_heads, sel_k, n_sink, window;
-  unsigned *counters;  // fast step: per (sequence, kv head) arrival counters
 };
 
 hipError_t launch_slow(const AttnLaunch &a, hipStream_t st);

@@ -107,9 +107,9 @@ class SFIDecoder:
         self.ws_slow_bytes = sfi.sfi_slow_workspace_bytes(self.kv)
         self.ws_sel_bytes = sfi.sfi_select_workspace_bytes(B, Hkv, self.max_len)
         self.ws_fast_bytes = sfi.sfi_fast_workspace_bytes(self.kv, k, n_sink, window)
-        self.ws_slow = torch.zeros(self.ws_slow_bytes, **u8)
-        self.ws_sel = torch.zeros(self.ws_sel_bytes, **u8)
-        self.ws_fast = torch.zeros(self.ws_fast_bytes, **u8)
+        self.ws_slow = torch.empty(self.ws_slow_bytes, **u8)
+        self.ws_sel = torch.empty(self.ws_sel_bytes, **u8)
+        self.ws_fast = torch.empty(self.ws_fast_bytes, **u8)
 
     # -- single calls -------------------------------------------------------
     def slow(self, q, seq_len, batch_ids, batch_n: int, stream=None, select: bool = True, out=None):
@@ -298,9 +298,9 @@ class VegasDecoder:
         self.ws_ver_bytes = sfi.sfi_verify_workspace_bytes(self.kv, T)
         self.ws_sel_bytes = sfi.sfi_select_workspace_bytes(B, 1, self.max_len)
         self.ws_fast_bytes = sfi.sfi_fast_workspace_bytes(self.kv, k, n_sink, window)
-        self.ws_ver = torch.zeros(self.ws_ver_bytes, **u8)
-        self.ws_sel = torch.zeros(self.ws_sel_bytes, **u8)
-        self.ws_fast = torch.zeros(self.ws_fast_bytes, **u8)
+        self.ws_ver = torch.empty(self.ws_ver_bytes, **u8)
+        self.ws_sel = torch.empty(self.ws_sel_bytes, **u8)
+        self.ws_fast = torch.empty(self.ws_fast_bytes, **u8)
 
     def verify(self, q_rows, seq_len, row_mask: int, batch_ids=None, batch_n=None, stream=None):
         """q_rows [B][T][Hq][d] bf16; seq_len counts the T verified rows."""

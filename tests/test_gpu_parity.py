@@ -223,7 +223,7 @@ def _fast_gpu(K, V, Hq, q, lens, sel_np, cnt_np, n_sink, window, sel_heads):
     sel_k = sel.shape[2]
     out = torch.full((B, Hq, K.shape[3]), 9.0, device=DEV)
     wsb = sfi.sfi_fast_workspace_bytes(kv, sel_k, n_sink, window)
-    ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
     sfi.sfi_fast_step(kv, None, B, q, sel, cnt, sel_heads, sel_k, n_sink, window, out, ws, wsb)
     torch.cuda.synchronize()
     return out.cpu().numpy()
