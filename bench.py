@@ -31,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_llama3_8b_layer_32k.json")
 METRIC = "decode attn tokens/s (slow+fast mix) at 32K/128K ctx; % HBM roofline/kernel"
 
 
@@ -51,6 +52,34 @@ def algorithmic_bytes(kind, n, cfg):
         rows = min(cfg.n_sink, n) + min(cfg.window, n) + k
         return rows * Hkv * 4 * d + k * Hkv * 4 + Hq * d * 6
     raise ValueError(kind)
+
+
+def kernel_source_hash():
+    """sha256 over every HIP source of the library: counter-derived traffic
+    is reported only while the kernels are the ones it was measured on."""
+    import hashlib
+    csrc = os.path.join(ROOT, "dynamic_sparse_kv_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp", ".h")):
+            h.update(f.encode())
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kind, alg_bytes_per_launch):
+    """HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE
+    measurement (measured/algorithmic ratio of this call kind on this
+    workload, scaled to this run's launches), or None if the kernels changed."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_hash() or kind not in t.get("ratio", {}):
+        return None
+    return int(round(t["ratio"][kind] * alg_bytes_per_launch))
 
 
 def cpu_baseline(cfg, K, V, q_host, slow, ctx, budget_s=20.0):
@@ -109,6 +138,9 @@ def main():
     ap.add_argument("--config", default="c2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="first run one plain 256 MiB device-to-device copy (a known-size kernel "
+                         "for scaling hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); the path has no multi-GPU mode",
@@ -125,6 +157,13 @@ def main():
         sys.exit(2)
     sfi.lib()
     dev = "cuda"
+    if args.calib_copy:
+        src = torch.ones(1 << 26, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     cfg = W.CONFIGS[args.config]
     K_steps, W_steps = args.steps, args.warmup
     plan_steps = max(K_steps, W_steps, 1)
@@ -227,7 +266,8 @@ def main():
     dc = per_call[dom]
     achieved = dc["alg_GBps"]
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(dom, dc["alg_bytes_per_launch"]),
                 "kernel": {"slow": "sfi_slow_step: split-K partial + finalize kernels",
                            "select": "sfi_select: fused selector kernel",
                            "fast": "sfi_fast_step: gather partial + finalize kernels"}[dom]}
@@ -236,18 +276,24 @@ def main():
     _log("[bench] dense comparator")
     all_ids = torch.arange(cfg.B, dtype=torch.int32, device=dev)
     n_dense = min(K_steps, 64)
-    gd = torch.cuda.CUDAGraph()
-    side.wait_stream(stream)
-    with torch.cuda.stream(side):
-        with torch.cuda.graph(gd, stream=side):
-            for s in range(n_dense):
-                dec.dense(q[s], plan.seq_len[s], all_ids, cfg.B, side)
-    torch.cuda.synchronize()
-    gd.replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    gd.replay()
-    torch.cuda.synchronize()
+    if use_graph:
+        gd = torch.cuda.CUDAGraph()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(gd, stream=side):
+                for s in range(n_dense):
+                    dec.dense(q[s], plan.seq_len[s], all_ids, cfg.B, side)
+        torch.cuda.synchronize()
+        gd.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        gd.replay()
+        torch.cuda.synchronize()
+    else:
+        t0 = time.perf_counter()
+        for s in range(n_dense):
+            dec.dense(q[s], plan.seq_len[s], all_ids, cfg.B, stream)
+        torch.cuda.synchronize()
     t_dense = (time.perf_counter() - t0) / n_dense
     dense_tps = cfg.B / t_dense
 
