@@ -32,6 +32,17 @@ namespace {
 #ifndef SFI_DECODE_U
 #define SFI_DECODE_U 2
 #endif
+// Fast-step launch shape (rows per stage, lanes per row; 0 = the automatic
+// choice) and lanes per row for dense/slow steps.
+#ifndef SFI_FAST_U
+#define SFI_FAST_U SFI_DECODE_U
+#endif
+#ifndef SFI_FAST_LPR
+#define SFI_FAST_LPR 0
+#endif
+#ifndef SFI_DENSE_LPR
+#define SFI_DENSE_LPR 0
+#endif
 #ifndef SFI_WAVES_OF_WG
 #define SFI_WAVES_OF_WG 1
 #endif
@@ -85,11 +96,13 @@ template <int D, int G, bool PAGED, int MODE, bool EVID>
 __global__ __launch_bounds__(kThreads) void partial_kernel(PartialArgs a) {
   // 8 lanes per row halves the cross-lane reduction and softmax work per row
   // compared with 16; wide groups (G*D > 640) use 16 to bound accumulators.
-  constexpr int LPR = (G * D > 640) ? 16 : 8;  // lanes per row
+  constexpr int LPR_AUTO = (G * D > 640) ? 16 : 8;
+  constexpr int LPR_SET = (MODE == MODE_FAST) ? SFI_FAST_LPR : SFI_DENSE_LPR;
+  constexpr int LPR = (LPR_SET == 8 || (LPR_SET == 16 && D == 128)) ? LPR_SET : LPR_AUTO;  // lanes per row
   constexpr int DPL = D / LPR;         // dims per lane (8 or 16)
   constexpr int NV = DPL / 8;          // 16-byte slices per row per lane
   constexpr int RPB = kThreads / LPR;  // rows per workgroup instruction
-  constexpr int U = SFI_DECODE_U;      // rows per lane group per pipeline stage
+  constexpr int U = (MODE == MODE_FAST) ? SFI_FAST_U : SFI_DECODE_U;  // rows per lane group per stage
   constexpr int NW = kThreads / 64;
   // Lazy rescaling: the running reference m only moves when a logit exceeds
   // it by more than kSlack (log2 units), so p = 2^(l - m) stays <= 2^kSlack.
@@ -162,26 +175,29 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialArgs a) {
     uint4 k[U][NV], v[U][NV];
     int j[U];
   };
+  // Every lane issues its loads unconditionally: a row past the chunk or a
+  // skipped list entry reads row 0 of the same (sequence, kv head), which
+  // exists whenever the list is non-empty, and is masked out in consume().
+  // Loads that sit behind a per-lane branch would leave the number of loads
+  // in flight unknown at compile time, and every later wait would have to
+  // drain all of them, collapsing the two-stage pipeline.
   auto load_stage = [&](Stage &st, int base) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int p = base + u * RPB;
-      int j = -1;
-      if (p < p1) j = (MODE == MODE_FAST) ? s_idx[p - p0] : p;
-      st.j[u] = j;
-      if (j >= 0) {
-        const size_t off = kv_row<D, PAGED>(a.kv, b, g, j) + sub * DPL;
-#pragma unroll
-        for (int c = 0; c < NV; ++c) {
-          st.k[u][c] = ldg16(a.kv.k + off + 8 * c);
-          st.v[u][c] = ldg16(a.kv.v + off + 8 * c);
-        }
+      int j;
+      if constexpr (MODE == MODE_FAST) {
+        j = s_idx[min(p - p0, a.chunk - 1)];
+        j = (p < p1) ? j : -1;
       } else {
+        j = (p < p1) ? p : -1;
+      }
+      st.j[u] = j;
+      const size_t off = kv_row<D, PAGED>(a.kv, b, g, max(j, 0)) + sub * DPL;
 #pragma unroll
-        for (int c = 0; c < NV; ++c) {
-          st.k[u][c] = make_uint4(0, 0, 0, 0);
-          st.v[u][c] = st.k[u][c];
-        }
+      for (int c = 0; c < NV; ++c) {
+        st.k[u][c] = ldg16(a.kv.k + off + 8 * c);
+        st.v[u][c] = ldg16(a.kv.v + off + 8 * c);
       }
     }
   };
@@ -250,9 +266,13 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialArgs a) {
         pu[h] = exp2f(l[u][h] - m[h]);
         Z[h] += pu[h];
       }
+      // a masked row contributes p = 0; zeroing its V bits keeps a non-finite
+      // value in the stand-in row from turning 0 * v into NaN
+      const uint32_t vm = (st.j[u] >= 0) ? 0xFFFFFFFFu : 0u;
 #pragma unroll
       for (int c = 0; c < NV; ++c) {
-        const uint32_t w4[4] = {st.v[u][c].x, st.v[u][c].y, st.v[u][c].z, st.v[u][c].w};
+        const uint32_t w4[4] = {st.v[u][c].x & vm, st.v[u][c].y & vm, st.v[u][c].z & vm,
+                                st.v[u][c].w & vm};
 #pragma unroll
         for (int q2 = 0; q2 < 4; ++q2) {
           const float v0 = bf_lo(w4[q2]), v1 = bf_hi(w4[q2]);
@@ -368,23 +388,21 @@ struct FinalArgs {
   int sel_heads, sel_k, n_sink, window;
 };
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-  return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
-  return x;
+// Merge (m2, z2) into the running softmax pair (m, z): both are a log2-domain
+// reference and the sum of 2^(l - reference) over their keys.
+__device__ __forceinline__ void mz_merge(float &m, float &z, float m2, float z2) {
+  const float mn = fmaxf(m, m2);
+  z = z * exp2f(m - mn) + z2 * exp2f(m2 - mn);
+  m = mn;
 }
 
 // grid.x = G combine blocks (one per query head of the group) followed, for
-// slow steps with evidence, by one block per kEvidChunk keys.
+// slow steps with evidence, by one block per kEvidChunk keys.  Every block
+// issues all of its global loads before it needs the merged maxima, so a
+// block costs one memory round trip.
 template <int D, int G, int MODE, bool EVID>
 __global__ __launch_bounds__(kThreads) void finalize_kernel(FinalArgs a) {
   constexpr int NW = kThreads / 64;
-  __shared__ float red[NW][G];
 
   const int b = batch_seq(a.batch_ids, blockIdx.z, a.B);
   if (b < 0) return;
@@ -402,122 +420,79 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(FinalArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const size_t hbase = (size_t)b * a.Hq + (size_t)g * G;
 
-  // Global running max and normaliser of every head of the group.
-  float M[G], Zs[G];
-  {
-    float ml[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) ml[h] = kNegBig;
-    for (int s = tid; s < S; s += kThreads) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) ml[h] = fmaxf(ml[h], a.part_ml[((hbase + h) * a.stride + s) * 2]);
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      ml[h] = wave_max(ml[h]);
-      if (lane == 0) red[wv][h] = ml[h];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float v = red[0][h];
-#pragma unroll
-      for (int w = 1; w < NW; ++w) v = fmaxf(v, red[w][h]);
-      M[h] = v;
-    }
-    __syncthreads();
-    float zl[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) zl[h] = 0.f;
-    for (int s = tid; s < S; s += kThreads) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float *ml2 = a.part_ml + ((hbase + h) * a.stride + s) * 2;
-        zl[h] = fmaf(ml2[1], exp2f(ml2[0] - M[h]), zl[h]);
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      zl[h] = wave_sum(zl[h]);
-      if (lane == 0) red[wv][h] = zl[h];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float v = 0.f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) v += red[w][h];
-      Zs[h] = v;
-    }
-  }
-
   if (comb) {
-    float Mh = M[0], Zh = Zs[0];
-#pragma unroll
-    for (int h = 1; h < G; ++h) {
-      Mh = (x == h) ? M[h] : Mh;
-      Zh = (x == h) ? Zs[h] : Zh;
-    }
-    // PARTS4 groups of D/4 threads; each thread merges 4 dims of every
-    // PARTS4-th partial, four partials in flight at a time.
+    // PARTS groups of D/4 threads; group `part` merges partials part,
+    // part + PARTS, ... (four at a time, their loads in flight together)
+    // into a running (m, z, o); the groups are then merged through LDS.
     constexpr int TPP = D / 4;
-    constexpr int PARTS4 = kThreads / TPP;
+    constexpr int PARTS = kThreads / TPP;
     const size_t row = hbase + x;
     const int e4 = tid % TPP, part = tid / TPP;
     const float *pm = a.part_ml + row * a.stride * 2;
     const float4 *po = reinterpret_cast<const float4 *>(a.part_o + row * a.stride * D) + e4;
+    float m = kNegBig, z = 0.f;
     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-    int s = part;
-    for (; s + 3 * PARTS4 < S; s += 4 * PARTS4) {
+    for (int s0 = part; s0 < S; s0 += 4 * PARTS) {
       float4 v[4];
-      float w[4];
+      float ms[4], zs[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        v[i] = po[(size_t)(s + i * PARTS4) * TPP];
-        w[i] = pm[(s + i * PARTS4) * 2];
+        const int s = min(s0 + i * PARTS, S - 1);
+        v[i] = po[(size_t)s * TPP];
+        ms[i] = pm[s * 2];
+        zs[i] = pm[s * 2 + 1];
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float wi = exp2f(w[i] - Mh);
-        o.x = fmaf(wi, v[i].x, o.x);
-        o.y = fmaf(wi, v[i].y, o.y);
-        o.z = fmaf(wi, v[i].z, o.z);
-        o.w = fmaf(wi, v[i].w, o.w);
+        if (s0 + i * PARTS < S) {
+          const float mn = fmaxf(m, ms[i]);
+          const float c = exp2f(m - mn), w = exp2f(ms[i] - mn);
+          z = z * c + zs[i] * w;
+          o.x = o.x * c + v[i].x * w;
+          o.y = o.y * c + v[i].y * w;
+          o.z = o.z * c + v[i].z * w;
+          o.w = o.w * c + v[i].w * w;
+          m = mn;
+        }
       }
     }
-    for (; s < S; s += PARTS4) {
-      const float4 v = po[(size_t)s * TPP];
-      const float wi = exp2f(pm[s * 2] - Mh);
-      o.x = fmaf(wi, v.x, o.x);
-      o.y = fmaf(wi, v.y, o.y);
-      o.z = fmaf(wi, v.z, o.z);
-      o.w = fmaf(wi, v.w, o.w);
+    __shared__ float s_pm[PARTS], s_pz[PARTS];
+    __shared__ float4 s_po[PARTS][TPP];
+    if (e4 == 0) {
+      s_pm[part] = m;
+      s_pz[part] = z;
     }
-    __shared__ float4 s_o4[PARTS4][TPP];
-    s_o4[part][e4] = o;
+    s_po[part][e4] = o;
     __syncthreads();
     if (part == 0) {
+      float M = s_pm[0];
 #pragma unroll
-      for (int p = 1; p < PARTS4; ++p) {
-        const float4 t = s_o4[p][e4];
-        o.x += t.x; o.y += t.y; o.z += t.z; o.w += t.w;
+      for (int p = 1; p < PARTS; ++p) M = fmaxf(M, s_pm[p]);
+      float Z = 0.f;
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int p = 0; p < PARTS; ++p) {
+        const float w = exp2f(s_pm[p] - M);
+        const float4 t = s_po[p][e4];
+        Z = fmaf(s_pz[p], w, Z);
+        acc.x = fmaf(t.x, w, acc.x);
+        acc.y = fmaf(t.y, w, acc.y);
+        acc.z = fmaf(t.z, w, acc.z);
+        acc.w = fmaf(t.w, w, acc.w);
       }
-      const float rz = (Zh > 0.f) ? 1.0f / Zh : 0.f;
-      float4 r = make_float4(o.x * rz, o.y * rz, o.z * rz, o.w * rz);
-      if (Zh <= 0.f) r = make_float4(0.f, 0.f, 0.f, 0.f);
-      reinterpret_cast<float4 *>(a.out + row * D)[e4] = r;
+      const float rz = (Z > 0.f) ? 1.0f / Z : 0.f;
+      reinterpret_cast<float4 *>(a.out + row * D)[e4] =
+          make_float4(acc.x * rz, acc.y * rz, acc.z * rz, acc.w * rz);
     }
     return;
   }
 
   if constexpr (EVID) {
-    float rz[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) rz[h] = 1.0f / ((float)G * Zs[h]);
     const size_t lrow = (size_t)b * a.Hkv + g;
     const int j0 = (x - G) * kEvidChunk;
     const int j1 = min(n, j0 + kEvidChunk);
     constexpr int PER = kEvidChunk / kThreads;
+    // the chunk's logits do not depend on the merged maxima: load them first
     float lg[PER][G];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -525,6 +500,43 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(FinalArgs a) {
       const float *lp = a.logits + (lrow * a.lld + (size_t)min(j, j1 - 1)) * G;
 #pragma unroll
       for (int h = 0; h < G; ++h) lg[i][h] = lp[h];
+    }
+    // merged (max, sum) of every head of the group over the S partials
+    float m[G], z[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      m[h] = kNegBig;
+      z[h] = 0.f;
+    }
+    for (int s = tid; s < S; s += kThreads) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float *ml2 = a.part_ml + ((hbase + h) * a.stride + s) * 2;
+        mz_merge(m[h], z[h], ml2[0], ml2[1]);
+      }
+    }
+    __shared__ float s_m[NW][G], s_z[NW][G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const float m2 = __shfl_xor(m[h], off), z2 = __shfl_xor(z[h], off);
+        mz_merge(m[h], z[h], m2, z2);
+      }
+      if (lane == 0) {
+        s_m[wv][h] = m[h];
+        s_z[wv][h] = z[h];
+      }
+    }
+    __syncthreads();
+    float M[G], rz[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float mm = s_m[0][h], zz = s_z[0][h];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) mz_merge(mm, zz, s_m[w][h], s_z[w][h]);
+      M[h] = mm;
+      rz[h] = 1.0f / ((float)G * zz);
     }
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -537,15 +549,17 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(FinalArgs a) {
   }
 }
 
-// Resident workgroups of one kernel instance across the device (cached).
-template <typename Kern>
-int resident_slots(Kern kern) {
+// Resident workgroups of one kernel across the device, cached per kernel and
+// device (the kernel is a template argument so every instantiation keeps its
+// own cache: all partial kernels share one function-pointer type).
+template <auto KERN>
+int resident_slots() {
   static int slots[16] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
   if (slots[dev] == 0) {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, kThreads, 0) != hipSuccess || nb < 1) nb = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, KERN, kThreads, 0) != hipSuccess || nb < 1) nb = 1;
     slots[dev] = nb * device_cu_count() * SFI_WAVES_OF_WG;
   }
   return slots[dev];
@@ -556,8 +570,8 @@ hipError_t slow_t(const AttnLaunch &a_in, hipStream_t st) {
   AttnLaunch a = a_in;
   const bool side = a.evidence != nullptr || a.key_norm != nullptr;
   {
-    const int slots = side ? resident_slots(partial_kernel<D, G, PAGED, MODE_SLOW, true>)
-                           : resident_slots(partial_kernel<D, G, PAGED, MODE_SLOW, false>);
+    const int slots = side ? resident_slots<partial_kernel<D, G, PAGED, MODE_SLOW, true>>()
+                           : resident_slots<partial_kernel<D, G, PAGED, MODE_SLOW, false>>();
     a.plan = plan_splits(a.max_len, a.batch_n * a.Hkv, slots, a.plan.stride, 1 << 30);
   }
   PartialArgs p{};
@@ -594,7 +608,7 @@ hipError_t fast_t(const AttnLaunch &a_in, hipStream_t st) {
   AttnLaunch a = a_in;
   {
     const long long L = (long long)std::min(a.n_sink, a.max_len) + std::min(a.window, a.max_len) + a.sel_k;
-    const int slots = resident_slots(partial_kernel<D, G, PAGED, MODE_FAST, false>);
+    const int slots = resident_slots<partial_kernel<D, G, PAGED, MODE_FAST, false>>();
     a.plan = plan_splits(L, a.batch_n * a.Hkv, slots, a.plan.stride, kMaxFastChunk);
   }
   PartialArgs p{};

@@ -169,7 +169,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectLaunch a) {
   const bool take_all = ncand <= K;
   int32_t *out = a.sel_idx + row * K;
 
-  const int span = FUSED ? n : hi;  // keys [0, span) are visited
+  // keys [0, span) are visited (uniform: it steers the slab-level branches)
+  const int span = __builtin_amdgcn_readfirstlane(FUSED ? n : hi);
   const int NB = (span + kBlock - 1) / kBlock;
   const bool resident = NB <= 1;
   const float *score = a.score + row * a.ld;
@@ -181,18 +182,33 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectLaunch a) {
   // u[] holds the raw float bits of the current block until make_keys turns
   // them into order-preserving keys in place.
   uint32_t u[kVPT];
+  // Slab-level cases are uniform across the workgroup: a whole slab in range
+  // takes one 16-byte load per thread, a slab past the end takes none, and
+  // only the slab that holds the end of the row uses clamped scalar loads.
+  // No load sits behind a per-lane branch, so all slabs' loads are in flight
+  // together (a per-lane branch makes the compiler drain them one by one).
+  auto load4 = [&](const float *p, int slab0, bool vec, float (&x)[4]) {
+    const int j = slab0 + 4 * tid;
+    if (vec && slab0 + kSlab <= span) {
+      const float4 t = *reinterpret_cast<const float4 *>(p + j);
+      x[0] = t.x; x[1] = t.y; x[2] = t.z; x[3] = t.w;
+    } else if (slab0 >= span) {
+      x[0] = x[1] = x[2] = x[3] = 0.f;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float t = p[min(j + e, span - 1)];
+        x[e] = (j + e < span) ? t : 0.f;
+      }
+    }
+  };
   auto load = [&](const float *p, int blk, bool vec) {
 #pragma unroll
     for (int sl = 0; sl < kSlabs; ++sl) {
-      const int j = blk * kBlock + sl * kSlab + 4 * tid;
-      if (vec && j + 4 <= span) {
-        const float4 t = *reinterpret_cast<const float4 *>(p + j);
-        u[4 * sl + 0] = __float_as_uint(t.x); u[4 * sl + 1] = __float_as_uint(t.y);
-        u[4 * sl + 2] = __float_as_uint(t.z); u[4 * sl + 3] = __float_as_uint(t.w);
-      } else {
+      float x[4];
+      load4(p, blk * kBlock + sl * kSlab, vec, x);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) u[4 * sl + e] = __float_as_uint((j + e < span) ? p[j + e] : 0.f);
-      }
+      for (int e = 0; e < 4; ++e) u[4 * sl + e] = __float_as_uint(x[e]);
     }
   };
   auto store = [&](float *p, int blk, bool vec) {
@@ -296,15 +312,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectLaunch a) {
       if (!resident) load(sb, blk, vsb);
 #pragma unroll
       for (int sl = 0; sl < kSlabs; ++sl) {
-        const int j = blk * kBlock + sl * kSlab + 4 * tid;
         float f4[4];
-        if (vsc && j + 4 <= span) {
-          const float4 t = *reinterpret_cast<const float4 *>(score + j);
-          f4[0] = t.x; f4[1] = t.y; f4[2] = t.z; f4[3] = t.w;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) f4[e] = (j + e < span) ? score[j + e] : 0.f;
-        }
+        load4(score, blk * kBlock + sl * kSlab, vsc, f4);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           u[4 * sl + e] = __float_as_uint(fmaf(cf, f4[e], cr * __uint_as_float(u[4 * sl + e])));
