@@ -93,14 +93,24 @@ FastWs fast_ws(const sfi_kv *kv, int sel_k, int n_sink, int window) {
 }
 
 struct SelWs {
-  size_t sbuf, total;
+  int P, ldk;
+  size_t keys, cand, hist, nsum, wsum, gt1, offs, meta, total;
 };
 
 SelWs select_ws(int B, int H, int max_seq_len) {
   SelWs w{};
   const size_t rows = (size_t)B * H;
-  w.sbuf = 0;
-  w.total = align_up(rows * (size_t)max_seq_len * sizeof(float));
+  w.P = (max_seq_len + kSelChunk - 1) / kSelChunk;
+  w.ldk = w.P * kSelChunk;
+  w.keys = 0;
+  w.cand = align_up(w.keys + rows * w.ldk * sizeof(uint32_t));
+  w.hist = align_up(w.cand + rows * w.ldk * sizeof(unsigned long long));
+  w.nsum = align_up(w.hist + rows * 4096 * sizeof(uint32_t));
+  w.wsum = align_up(w.nsum + rows * w.P * 2 * sizeof(double));
+  w.gt1 = align_up(w.wsum + rows * w.P * sizeof(double));
+  w.offs = align_up(w.gt1 + rows * w.P * sizeof(int));
+  w.meta = align_up(w.offs + rows * w.P * sizeof(int));
+  w.total = align_up(w.meta + rows * sizeof(SelRowMeta));
   return w;
 }
 
@@ -138,7 +148,7 @@ size_t sfi_slow_workspace_bytes(const sfi_kv *kv) {
 }
 
 size_t sfi_select_workspace_bytes(int32_t B, int32_t H, int32_t max_seq_len) {
-  if (B < 1 || H < 1 || max_seq_len < 1) return 0;
+  if (B < 1 || H < 1 || max_seq_len < 1 || max_seq_len > kSelMaxChunks * kSelChunk) return 0;
   return select_ws(B, H, max_seq_len).total;
 }
 
@@ -193,6 +203,7 @@ sfi_status sfi_select(const sfi_select_params *p, const int32_t *batch_ids, int3
   if (!p || !seq_len || !score || !sel_idx || !sel_count) return SFI_ERR_NULL;
   if (p->mode != SFI_SCORE_FUSED && p->mode != SFI_SCORE_RAW) return SFI_ERR_RANGE;
   if (B < 1 || H < 1 || max_seq_len < 1) return SFI_ERR_SHAPE;
+  if (max_seq_len > kSelMaxChunks * kSelChunk) return SFI_ERR_UNSUPPORTED;
   if (batch_n < 0 || batch_n > B) return SFI_ERR_RANGE;
   if (ld < max_seq_len) return SFI_ERR_RANGE;
   if (p->k < 1 || p->n_sink < 0 || p->window < 0) return SFI_ERR_RANGE;
@@ -215,15 +226,18 @@ sfi_status sfi_select(const sfi_select_params *p, const int32_t *batch_ids, int3
   a.B = B; a.H = H; a.max_seq_len = max_seq_len;
   a.score = score; a.key_norm = key_norm; a.ld = ld;
   a.sel_idx = sel_idx; a.sel_count = sel_count;
-  if (fused && fused_out) {
-    a.sbuf = fused_out;
-    a.sld = ld;
-    a.store_s = true;
-  } else {
-    a.sbuf = carve<float>(ws, w.sbuf);
-    a.sld = max_seq_len;
-    a.store_s = false;
-  }
+  a.fused_out = fused ? fused_out : nullptr;
+  a.fo_ld = ld;
+  a.ws.P = w.P;
+  a.ws.ldk = w.ldk;
+  a.ws.keys = carve<uint32_t>(ws, w.keys);
+  a.ws.cand = carve<unsigned long long>(ws, w.cand);
+  a.ws.hist = carve<uint32_t>(ws, w.hist);
+  a.ws.nsum = carve<double>(ws, w.nsum);
+  a.ws.wsum = carve<double>(ws, w.wsum);
+  a.ws.gt1 = carve<int>(ws, w.gt1);
+  a.ws.offs = carve<int>(ws, w.offs);
+  a.ws.meta = carve<SelRowMeta>(ws, w.meta);
   return launch_select(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SFI_OK : SFI_ERR_HIP;
 }
 

@@ -67,6 +67,33 @@ struct AttnLaunch {
 hipError_t launch_slow(const AttnLaunch &a, hipStream_t st);
 hipError_t launch_fast(const AttnLaunch &a, hipStream_t st);
 
+constexpr int kSelChunk = 2048;       // keys per selector chunk workgroup
+constexpr int kSelMaxChunks = 4096;   // chunks per row: rows up to 8,388,608 keys
+
+// Per-row state shared by the selector's kernels.
+struct SelRowMeta {
+  int b1;                  // first-digit bin of the k-th largest key (0: take all)
+  int want1;               // keys to take from that bin
+  int m;                   // tie-bin candidates appended
+  int pad;
+  float muf, cz;           // prior: mean key norm, -norm_coef log2(e) / std
+  unsigned long long T;    // tie-bin winners: composite >= T
+};
+
+// Selector workspace, carved from the caller's buffer.
+struct SelWork {
+  int P;                      // chunks per row
+  int ldk;                    // P * kSelChunk
+  uint32_t *keys;             // [rows][ldk] order-preserving keys
+  unsigned long long *cand;   // [rows][ldk] tie-bin candidates
+  uint32_t *hist;             // [rows][4096] first-digit histogram
+  double *nsum;               // [rows][P][2] key-norm sums per chunk
+  double *wsum;               // [rows][P] prior-weight sums per chunk
+  int *gt1;                   // [rows][P] keys above the tie bin per chunk
+  int *offs;                  // [rows][P] output offset per chunk
+  SelRowMeta *meta;           // [rows]
+};
+
 struct SelectLaunch {
   int mode;
   float lambda, norm_coef, pos_tau;
@@ -80,9 +107,9 @@ struct SelectLaunch {
   int ld;
   int32_t *sel_idx;
   int32_t *sel_count;
-  float *sbuf;        // [B][H][sld]: fused_out or workspace
-  int sld;
-  bool store_s;       // write s to sbuf even when the row stays in registers
+  float *fused_out;   // [B][H][fo_ld] or null
+  int fo_ld;
+  SelWork ws;
 };
 
 hipError_t launch_select(const SelectLaunch &a, hipStream_t st);
