@@ -92,8 +92,11 @@ __device__ __forceinline__ FastList fast_list(const int32_t *sel_idx, const int3
   return f;
 }
 
+// One workgroup's share of a decode step: rows [split*chunk, ...) of the row
+// list of (sequence batch_ids[zb], kv head g).  A device function so that the
+// co-launch kernel below can run slow and fast shares in one grid.
 template <int D, int G, bool PAGED, int MODE, bool EVID>
-__global__ __launch_bounds__(kThreads) void partial_kernel(PartialArgs a) {
+__device__ __forceinline__ void partial_body(const PartialArgs &a, int split, int g, int zb) {
   // 8 lanes per row halves the cross-lane reduction and softmax work per row
   // compared with 16; wide groups (G*D > 640) use 16 to bound accumulators.
   constexpr int LPR_AUTO = (G * D > 640) ? 16 : 8;
@@ -112,10 +115,8 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialArgs a) {
   __shared__ float s_m[NW][G], s_z[NW][G];
   __shared__ float s_acc[NW][G][D];
 
-  const int b = batch_seq(a.batch_ids, blockIdx.z, a.B);
+  const int b = batch_seq(a.batch_ids, zb, a.B);
   if (b < 0) return;
-  const int g = blockIdx.y;
-  const int split = blockIdx.x;
   const int n = clamp_len(a.seq_len, b, a.max_len);
   const int tid = threadIdx.x;
 
@@ -370,6 +371,29 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialArgs a) {
   }
 }
 
+template <int D, int G, bool PAGED, int MODE, bool EVID>
+__global__ __launch_bounds__(kThreads) void partial_kernel(PartialArgs a) {
+  partial_body<D, G, PAGED, MODE, EVID>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+// Slow (dense with evidence) and fast shares of one decode step in a single
+// grid: linear blocks [0, ns) are the slow grid (s_splits x Hkv x slow
+// sequences), the rest the fast grid.  The two sets of sequences are
+// disjoint, so nothing orders one share after the other.
+template <int D, int G, bool PAGED>
+__global__ __launch_bounds__(kThreads) void copartial_kernel(PartialArgs s, PartialArgs f, int s_splits,
+                                                             int f_splits, int Hkv, int ns) {
+  int id = blockIdx.x;
+  if (id < ns) {
+    partial_body<D, G, PAGED, MODE_SLOW, true>(s, id % s_splits, (id / s_splits) % Hkv,
+                                               id / (s_splits * Hkv));
+  } else {
+    id -= ns;
+    partial_body<D, G, PAGED, MODE_FAST, false>(f, id % f_splits, (id / f_splits) % Hkv,
+                                                id / (f_splits * Hkv));
+  }
+}
+
 struct FinalArgs {
   int B, max_len;
   const int32_t *seq_len;
@@ -401,13 +425,11 @@ __device__ __forceinline__ void mz_merge(float &m, float &z, float m2, float z2)
 // issues all of its global loads before it needs the merged maxima, so a
 // block costs one memory round trip.
 template <int D, int G, int MODE, bool EVID>
-__global__ __launch_bounds__(kThreads) void finalize_kernel(FinalArgs a) {
+__device__ __forceinline__ void finalize_body(const FinalArgs &a, int x, int g, int zb) {
   constexpr int NW = kThreads / 64;
 
-  const int b = batch_seq(a.batch_ids, blockIdx.z, a.B);
+  const int b = batch_seq(a.batch_ids, zb, a.B);
   if (b < 0) return;
-  const int g = blockIdx.y;
-  const int x = blockIdx.x;
   const int n = clamp_len(a.seq_len, b, a.max_len);
   int L = n;
   if constexpr (MODE == MODE_FAST) {
@@ -549,6 +571,25 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(FinalArgs a) {
   }
 }
 
+template <int D, int G, int MODE, bool EVID>
+__global__ __launch_bounds__(kThreads) void finalize_kernel(FinalArgs a) {
+  finalize_body<D, G, MODE, EVID>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+// Slow and fast finalize blocks of one decode step in a single grid (layout
+// as in copartial_kernel: s_gx x Hkv x slow sequences, then the fast grid).
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) void cofinal_kernel(FinalArgs s, FinalArgs f, int s_gx, int f_gx,
+                                                           int Hkv, int ns) {
+  int id = blockIdx.x;
+  if (id < ns) {
+    finalize_body<D, G, MODE_SLOW, true>(s, id % s_gx, (id / s_gx) % Hkv, id / (s_gx * Hkv));
+  } else {
+    id -= ns;
+    finalize_body<D, G, MODE_FAST, false>(f, id % f_gx, (id / f_gx) % Hkv, id / (f_gx * Hkv));
+  }
+}
+
 // Resident workgroups of one kernel across the device, cached per kernel and
 // device (the kernel is a template argument so every instantiation keeps its
 // own cache: all partial kernels share one function-pointer type).
@@ -565,6 +606,42 @@ int resident_slots() {
   return slots[dev];
 }
 
+template <int D>
+PartialArgs partial_args(const AttnLaunch &a) {
+  PartialArgs p{};
+  p.B = a.B; p.max_len = a.max_len;
+  p.kv = a.kv; p.seq_len = a.seq_len; p.batch_ids = a.batch_ids; p.q = a.q; p.Hq = a.Hq;
+  p.chunk = a.plan.chunk; p.stride = a.plan.stride; p.part_o = a.part_o; p.part_ml = a.part_ml;
+  p.logits = a.logits; p.lld = a.lld; p.key_norm = a.key_norm; p.ld = a.ld;
+  p.sel_idx = a.sel_idx; p.sel_count = a.sel_count; p.sel_heads = a.sel_heads; p.sel_k = a.sel_k;
+  p.n_sink = a.n_sink; p.window = a.window;
+  p.qscale = kLog2e / sqrtf((float)D);
+  return p;
+}
+
+FinalArgs final_args(const AttnLaunch &a) {
+  FinalArgs f{};
+  f.B = a.B; f.max_len = a.max_len;
+  f.seq_len = a.seq_len; f.batch_ids = a.batch_ids; f.Hq = a.Hq; f.Hkv = a.Hkv;
+  f.chunk = a.plan.chunk; f.stride = a.plan.stride; f.part_o = a.part_o; f.part_ml = a.part_ml;
+  f.out = a.out; f.logits = a.logits; f.lld = a.lld; f.evidence = a.evidence; f.ld = a.ld;
+  f.sel_idx = a.sel_idx; f.sel_count = a.sel_count; f.sel_heads = a.sel_heads;
+  f.sel_k = a.sel_k; f.n_sink = a.n_sink; f.window = a.window;
+  return f;
+}
+
+// Longest row list of a fast step.
+long long fast_rows(const AttnLaunch &a) {
+  return (long long)std::min(a.n_sink, a.max_len) + std::min(a.window, a.max_len) + a.sel_k;
+}
+
+// Finalize blocks per (sequence, kv head) of a slow step: G combine blocks,
+// then one evidence block per kEvidChunk keys.
+int slow_final_blocks(const AttnLaunch &a, int G) {
+  const int kv_max = a.plan.splits * a.plan.chunk;
+  return G + (a.evidence ? (kv_max + kEvidChunk - 1) / kEvidChunk : 0);
+}
+
 template <int D, int G, bool PAGED>
 hipError_t slow_t(const AttnLaunch &a_in, hipStream_t st) {
   AttnLaunch a = a_in;
@@ -574,12 +651,7 @@ hipError_t slow_t(const AttnLaunch &a_in, hipStream_t st) {
                            : resident_slots<partial_kernel<D, G, PAGED, MODE_SLOW, false>>();
     a.plan = plan_splits(a.max_len, a.batch_n * a.Hkv, slots, a.plan.stride, 1 << 30);
   }
-  PartialArgs p{};
-  p.B = a.B; p.max_len = a.max_len;
-  p.kv = a.kv; p.seq_len = a.seq_len; p.batch_ids = a.batch_ids; p.q = a.q; p.Hq = a.Hq;
-  p.chunk = a.plan.chunk; p.stride = a.plan.stride; p.part_o = a.part_o; p.part_ml = a.part_ml;
-  p.logits = a.logits; p.lld = a.lld; p.key_norm = a.key_norm; p.ld = a.ld;
-  p.qscale = kLog2e / sqrtf((float)D);
+  const PartialArgs p = partial_args<D>(a);
   dim3 grid(a.plan.splits, a.Hkv, a.batch_n);
   if (side)
     hipLaunchKernelGGL((partial_kernel<D, G, PAGED, MODE_SLOW, true>), grid, dim3(kThreads), 0, st, p);
@@ -588,14 +660,8 @@ hipError_t slow_t(const AttnLaunch &a_in, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  FinalArgs f{};
-  f.B = a.B; f.max_len = a.max_len;
-  f.seq_len = a.seq_len; f.batch_ids = a.batch_ids; f.Hq = a.Hq; f.Hkv = a.Hkv;
-  f.chunk = a.plan.chunk; f.stride = a.plan.stride; f.part_o = a.part_o; f.part_ml = a.part_ml;
-  f.out = a.out; f.logits = a.logits; f.lld = a.lld; f.evidence = a.evidence; f.ld = a.ld;
-  const int kv_max = a.plan.splits * a.plan.chunk;
-  const int nev = a.evidence ? (kv_max + kEvidChunk - 1) / kEvidChunk : 0;
-  dim3 g2(G + nev, a.Hkv, a.batch_n);
+  const FinalArgs f = final_args(a);
+  dim3 g2(slow_final_blocks(a, G), a.Hkv, a.batch_n);
   if (a.evidence)
     hipLaunchKernelGGL((finalize_kernel<D, G, MODE_SLOW, true>), g2, dim3(kThreads), 0, st, f);
   else
@@ -607,29 +673,47 @@ template <int D, int G, bool PAGED>
 hipError_t fast_t(const AttnLaunch &a_in, hipStream_t st) {
   AttnLaunch a = a_in;
   {
-    const long long L = (long long)std::min(a.n_sink, a.max_len) + std::min(a.window, a.max_len) + a.sel_k;
     const int slots = resident_slots<partial_kernel<D, G, PAGED, MODE_FAST, false>>();
-    a.plan = plan_splits(L, a.batch_n * a.Hkv, slots, a.plan.stride, kMaxFastChunk);
+    a.plan = plan_splits(fast_rows(a), a.batch_n * a.Hkv, slots, a.plan.stride, kMaxFastChunk);
   }
-  PartialArgs p{};
-  p.B = a.B; p.max_len = a.max_len;
-  p.kv = a.kv; p.seq_len = a.seq_len; p.batch_ids = a.batch_ids; p.q = a.q; p.Hq = a.Hq;
-  p.chunk = a.plan.chunk; p.stride = a.plan.stride; p.part_o = a.part_o; p.part_ml = a.part_ml;
-  p.sel_idx = a.sel_idx; p.sel_count = a.sel_count; p.sel_heads = a.sel_heads; p.sel_k = a.sel_k;
-  p.n_sink = a.n_sink; p.window = a.window;
-  p.qscale = kLog2e / sqrtf((float)D);
+  const PartialArgs p = partial_args<D>(a);
   dim3 grid(a.plan.splits, a.Hkv, a.batch_n);
   hipLaunchKernelGGL((partial_kernel<D, G, PAGED, MODE_FAST, false>), grid, dim3(kThreads), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  FinalArgs f{};
-  f.B = a.B; f.max_len = a.max_len;
-  f.seq_len = a.seq_len; f.batch_ids = a.batch_ids; f.Hq = a.Hq; f.Hkv = a.Hkv;
-  f.chunk = a.plan.chunk; f.stride = a.plan.stride; f.part_o = a.part_o; f.part_ml = a.part_ml;
-  f.out = a.out; f.sel_idx = a.sel_idx; f.sel_count = a.sel_count; f.sel_heads = a.sel_heads;
-  f.sel_k = a.sel_k; f.n_sink = a.n_sink; f.window = a.window;
+  const FinalArgs f = final_args(a);
   dim3 g2(G, a.Hkv, a.batch_n);
   hipLaunchKernelGGL((finalize_kernel<D, G, MODE_FAST, false>), g2, dim3(kThreads), 0, st, f);
+  return hipGetLastError();
+}
+
+// A slow step (with evidence) for one set of sequences and a fast step for
+// another, co-launched: one partial grid and one finalize grid.  Both shares
+// are planned with the same number of rows per workgroup, so the workgroups
+// of the combined grid carry about equal bytes and the grid fills the
+// resident slots about once.
+template <int D, int G, bool PAGED>
+hipError_t step_t(const AttnLaunch &sa_in, const AttnLaunch &fa_in, hipStream_t st) {
+  AttnLaunch sa = sa_in, fa = fa_in;
+  {
+    const int slots = resident_slots<copartial_kernel<D, G, PAGED>>();
+    const long long Ls = sa.max_len, Lf = fast_rows(fa);
+    const long long rows = Ls * sa.batch_n * sa.Hkv + Lf * fa.batch_n * fa.Hkv;
+    const long long R = (rows + slots - 1) / slots;
+    sa.plan = plan_rows(Ls, sa.plan.stride, R, 1 << 30);
+    fa.plan = plan_rows(Lf, fa.plan.stride, R, kMaxFastChunk);
+  }
+  const int ns = sa.plan.splits * sa.Hkv * sa.batch_n;
+  const int nf = fa.plan.splits * fa.Hkv * fa.batch_n;
+  hipLaunchKernelGGL((copartial_kernel<D, G, PAGED>), dim3(ns + nf), dim3(kThreads), 0, st,
+                     partial_args<D>(sa), partial_args<D>(fa), sa.plan.splits, fa.plan.splits, sa.Hkv, ns);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int sgx = slow_final_blocks(sa, G);
+  const int ms = sgx * sa.Hkv * sa.batch_n;
+  const int mf = G * fa.Hkv * fa.batch_n;
+  hipLaunchKernelGGL((cofinal_kernel<D, G>), dim3(ms + mf), dim3(kThreads), 0, st, final_args(sa),
+                     final_args(fa), sgx, G, sa.Hkv, ms);
   return hipGetLastError();
 }
 
@@ -688,7 +772,42 @@ SplitPlan plan_splits(long long L, int pairs, int slots, int stride, int max_chu
   return pl;
 }
 
+SplitPlan plan_rows(long long L, int stride, long long R, int max_chunk) {
+  SplitPlan pl{};
+  if (L < 1) L = 1;
+  if (stride < 1) stride = 1;
+  long long chunk = std::max(R, (L + stride - 1) / stride);
+  chunk = (chunk + kSplitGranule - 1) / kSplitGranule * kSplitGranule;
+  if (chunk > max_chunk) chunk = max_chunk;
+  long long splits = (L + chunk - 1) / chunk;
+  if (splits > stride) {  // only when max_chunk binds; kept as a guard
+    splits = stride;
+    chunk = (L + splits - 1) / splits;
+  }
+  pl.chunk = (int)chunk;
+  pl.splits = (int)splits;
+  pl.stride = stride;
+  return pl;
+}
+
 hipError_t launch_slow(const AttnLaunch &a, hipStream_t st) { SFI_DISPATCH(slow_t, a, st); }
+hipError_t launch_step(const AttnLaunch &sa, const AttnLaunch &fa, hipStream_t st) {
+  const bool pg = sa.paged;
+  switch (sa.d * 16 + sa.G) {
+    case 64 * 16 + 1: return pg ? step_t<64, 1, true>(sa, fa, st) : step_t<64, 1, false>(sa, fa, st);
+    case 64 * 16 + 2: return pg ? step_t<64, 2, true>(sa, fa, st) : step_t<64, 2, false>(sa, fa, st);
+    case 64 * 16 + 4: return pg ? step_t<64, 4, true>(sa, fa, st) : step_t<64, 4, false>(sa, fa, st);
+    case 64 * 16 + 5: return pg ? step_t<64, 5, true>(sa, fa, st) : step_t<64, 5, false>(sa, fa, st);
+    case 64 * 16 + 8: return pg ? step_t<64, 8, true>(sa, fa, st) : step_t<64, 8, false>(sa, fa, st);
+    case 128 * 16 + 1: return pg ? step_t<128, 1, true>(sa, fa, st) : step_t<128, 1, false>(sa, fa, st);
+    case 128 * 16 + 2: return pg ? step_t<128, 2, true>(sa, fa, st) : step_t<128, 2, false>(sa, fa, st);
+    case 128 * 16 + 4: return pg ? step_t<128, 4, true>(sa, fa, st) : step_t<128, 4, false>(sa, fa, st);
+    case 128 * 16 + 5: return pg ? step_t<128, 5, true>(sa, fa, st) : step_t<128, 5, false>(sa, fa, st);
+    case 128 * 16 + 8: return pg ? step_t<128, 8, true>(sa, fa, st) : step_t<128, 8, false>(sa, fa, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_fast(const AttnLaunch &a, hipStream_t st) {
   SFI_DISPATCH(fast_t, a, st);
 }

@@ -136,6 +136,65 @@ T *carve(void *ws, size_t off) {
   return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
 }
 
+AttnLaunch slow_launch(const sfi_kv *kv, const KVView &view, bool paged, const SlowWs &w, void *ws,
+                       const int32_t *batch_ids, int32_t batch_n, const uint16_t *q, float *out,
+                       float *evidence, float *key_norm, int32_t ld) {
+  AttnLaunch a{};
+  a.kv = view;
+  a.seq_len = kv->seq_len;
+  a.batch_ids = batch_ids;
+  a.batch_n = batch_n;
+  a.B = kv->B; a.Hq = kv->Hq; a.Hkv = kv->Hkv; a.d = kv->d; a.G = kv->Hq / kv->Hkv;
+  a.max_len = kv->max_seq_len;
+  a.paged = paged;
+  a.q = q;
+  a.out = out;
+  a.part_o = carve<float>(ws, w.o);
+  a.part_ml = carve<float>(ws, w.ml);
+  a.plan.stride = w.stride;  // chunking is planned by the launcher
+  a.logits = carve<float>(ws, w.logits);
+  a.lld = kv->max_seq_len;
+  a.evidence = evidence;
+  a.key_norm = key_norm;
+  a.ld = ld;
+  return a;
+}
+
+AttnLaunch fast_launch(const sfi_kv *kv, const KVView &view, bool paged, const FastWs &w, void *ws,
+                       const int32_t *batch_ids, int32_t batch_n, const uint16_t *q, float *out,
+                       const int32_t *sel_idx, const int32_t *sel_count, int32_t sel_heads,
+                       int32_t sel_k, int32_t n_sink, int32_t window) {
+  AttnLaunch a{};
+  a.kv = view;
+  a.seq_len = kv->seq_len;
+  a.batch_ids = batch_ids;
+  a.batch_n = batch_n;
+  a.B = kv->B; a.Hq = kv->Hq; a.Hkv = kv->Hkv; a.d = kv->d; a.G = kv->Hq / kv->Hkv;
+  a.max_len = kv->max_seq_len;
+  a.paged = paged;
+  a.q = q;
+  a.out = out;
+  a.part_o = carve<float>(ws, w.o);
+  a.part_ml = carve<float>(ws, w.ml);
+  a.plan.stride = w.stride;  // chunking is planned by the launcher
+  a.sel_idx = sel_idx;
+  a.sel_count = sel_count;
+  a.sel_heads = sel_heads;
+  a.sel_k = sel_k;
+  a.n_sink = n_sink;
+  a.window = window;
+  return a;
+}
+
+sfi_status check_fast(const sfi_kv *kv, const int32_t *sel_idx, const int32_t *sel_count,
+                      int32_t sel_heads, int32_t sel_k, int32_t n_sink, int32_t window) {
+  if (!sel_count) return SFI_ERR_NULL;
+  if (sel_k < 0 || n_sink < 0 || window < 0) return SFI_ERR_RANGE;
+  if (sel_k > 0 && !sel_idx) return SFI_ERR_NULL;
+  if (sel_heads != 1 && sel_heads != kv->Hkv) return SFI_ERR_SHAPE;
+  return SFI_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -173,26 +232,54 @@ sfi_status sfi_slow_step(const sfi_kv *kv, const int32_t *batch_ids, int32_t bat
   if (!ws) return SFI_ERR_NULL;
   if (ws_bytes < w.total) return SFI_ERR_WORKSPACE;
   if (batch_n == 0) return SFI_OK;
-
-  AttnLaunch a{};
-  a.kv = view;
-  a.seq_len = kv->seq_len;
-  a.batch_ids = batch_ids;
-  a.batch_n = batch_n;
-  a.B = kv->B; a.Hq = kv->Hq; a.Hkv = kv->Hkv; a.d = kv->d; a.G = kv->Hq / kv->Hkv;
-  a.max_len = kv->max_seq_len;
-  a.paged = paged;
-  a.q = q;
-  a.out = out;
-  a.part_o = carve<float>(ws, w.o);
-  a.part_ml = carve<float>(ws, w.ml);
-  a.plan.stride = w.stride;  // chunking is planned by the launcher
-  a.logits = carve<float>(ws, w.logits);
-  a.lld = kv->max_seq_len;
-  a.evidence = evidence;
-  a.key_norm = key_norm;
-  a.ld = ld;
+  const AttnLaunch a = slow_launch(kv, view, paged, w, ws, batch_ids, batch_n, q, out, evidence,
+                                   key_norm, ld);
   return launch_slow(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SFI_OK : SFI_ERR_HIP;
+}
+
+size_t sfi_decode_step_workspace_bytes(const sfi_kv *kv, int32_t sel_k, int32_t n_sink,
+                                       int32_t window) {
+  KVView view;
+  bool paged = false;
+  if (check_kv(kv, &view, &paged) != SFI_OK || sel_k < 0 || n_sink < 0 || window < 0) return 0;
+  return slow_ws(kv).total + fast_ws(kv, sel_k, n_sink, window).total;
+}
+
+sfi_status sfi_decode_step(const sfi_kv *kv, const int32_t *slow_ids, int32_t n_slow,
+                           const int32_t *fast_ids, int32_t n_fast, const uint16_t *q, float *out,
+                           float *evidence, float *key_norm, int32_t ld, const int32_t *sel_idx,
+                           const int32_t *sel_count, int32_t sel_heads, int32_t sel_k,
+                           int32_t n_sink, int32_t window, void *ws, size_t ws_bytes,
+                           void *stream) {
+  KVView view;
+  bool paged = false;
+  sfi_status s = check_kv(kv, &view, &paged);
+  if (s != SFI_OK) return s;
+  if ((s = check_batch(kv, n_slow)) != SFI_OK) return s;
+  if ((s = check_batch(kv, n_fast)) != SFI_OK) return s;
+  if (n_slow + n_fast > kv->B) return SFI_ERR_RANGE;
+  if (!q || !out) return SFI_ERR_NULL;
+  if (n_slow > 0 && !evidence) return SFI_ERR_NULL;
+  if (n_slow > 0 && ld < kv->max_seq_len) return SFI_ERR_RANGE;
+  if (n_fast > 0 && (s = check_fast(kv, sel_idx, sel_count, sel_heads, sel_k, n_sink, window)) != SFI_OK)
+    return s;
+  if (sel_k < 0 || n_sink < 0 || window < 0) return SFI_ERR_RANGE;
+  const SlowWs sw = slow_ws(kv);
+  const FastWs fw = fast_ws(kv, sel_k, n_sink, window);
+  if (!ws) return SFI_ERR_NULL;
+  if (ws_bytes < sw.total + fw.total) return SFI_ERR_WORKSPACE;
+  if (n_slow == 0 && n_fast == 0) return SFI_OK;
+  void *ws_fast = static_cast<char *>(ws) + sw.total;
+  const AttnLaunch sa = slow_launch(kv, view, paged, sw, ws, slow_ids, n_slow, q, out, evidence,
+                                    key_norm, ld);
+  const AttnLaunch fa = fast_launch(kv, view, paged, fw, ws_fast, fast_ids, n_fast, q, out, sel_idx,
+                                    sel_count, sel_heads, sel_k, n_sink, window);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (n_fast == 0) e = launch_slow(sa, st);
+  else if (n_slow == 0) e = launch_fast(fa, st);
+  else e = launch_step(sa, fa, st);
+  return e == hipSuccess ? SFI_OK : SFI_ERR_HIP;
 }
 
 sfi_status sfi_select(const sfi_select_params *p, const int32_t *batch_ids, int32_t batch_n,
@@ -250,34 +337,14 @@ sfi_status sfi_fast_step(const sfi_kv *kv, const int32_t *batch_ids, int32_t bat
   sfi_status s = check_kv(kv, &view, &paged);
   if (s != SFI_OK) return s;
   if ((s = check_batch(kv, batch_n)) != SFI_OK) return s;
-  if (!q || !out || !sel_count) return SFI_ERR_NULL;
-  if (sel_k < 0 || n_sink < 0 || window < 0) return SFI_ERR_RANGE;
-  if (sel_k > 0 && !sel_idx) return SFI_ERR_NULL;
-  if (sel_heads != 1 && sel_heads != kv->Hkv) return SFI_ERR_SHAPE;
+  if (!q || !out) return SFI_ERR_NULL;
+  if ((s = check_fast(kv, sel_idx, sel_count, sel_heads, sel_k, n_sink, window)) != SFI_OK) return s;
   const FastWs w = fast_ws(kv, sel_k, n_sink, window);
   if (!ws) return SFI_ERR_NULL;
   if (ws_bytes < w.total) return SFI_ERR_WORKSPACE;
   if (batch_n == 0) return SFI_OK;
-
-  AttnLaunch a{};
-  a.kv = view;
-  a.seq_len = kv->seq_len;
-  a.batch_ids = batch_ids;
-  a.batch_n = batch_n;
-  a.B = kv->B; a.Hq = kv->Hq; a.Hkv = kv->Hkv; a.d = kv->d; a.G = kv->Hq / kv->Hkv;
-  a.max_len = kv->max_seq_len;
-  a.paged = paged;
-  a.q = q;
-  a.out = out;
-  a.part_o = carve<float>(ws, w.o);
-  a.part_ml = carve<float>(ws, w.ml);
-  a.plan.stride = w.stride;  // chunking is planned by the launcher
-  a.sel_idx = sel_idx;
-  a.sel_count = sel_count;
-  a.sel_heads = sel_heads;
-  a.sel_k = sel_k;
-  a.n_sink = n_sink;
-  a.window = window;
+  const AttnLaunch a = fast_launch(kv, view, paged, w, ws, batch_ids, batch_n, q, out, sel_idx,
+                                   sel_count, sel_heads, sel_k, n_sink, window);
   return launch_fast(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SFI_OK : SFI_ERR_HIP;
 }
 

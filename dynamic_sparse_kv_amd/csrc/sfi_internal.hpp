@@ -34,6 +34,8 @@ inline int split_stride(long long L) {
 // Chunking of L rows per pair over `pairs` pairs so that one launch fills
 // `slots` resident workgroups once, within the stride and a chunk cap.
 SplitPlan plan_splits(long long L, int pairs, int slots, int stride, int max_chunk);
+// Chunking of L rows with about R rows per workgroup (multiple of the granule).
+SplitPlan plan_rows(long long L, int stride, long long R, int max_chunk);
 
 // Compute units of the current device (cached per device).
 int device_cu_count();
@@ -66,6 +68,8 @@ struct AttnLaunch {
 
 hipError_t launch_slow(const AttnLaunch &a, hipStream_t st);
 hipError_t launch_fast(const AttnLaunch &a, hipStream_t st);
+// Slow step with evidence (sa) and fast step (fa) on disjoint sequences, co-launched.
+hipError_t launch_step(const AttnLaunch &sa, const AttnLaunch &fa, hipStream_t st);
 
 constexpr int kSelChunk = 2048;       // keys per selector chunk workgroup
 constexpr int kSelMaxChunks = 4096;   // chunks per row: rows up to 8,388,608 keys

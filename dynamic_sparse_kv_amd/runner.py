@@ -107,9 +107,11 @@ class SFIDecoder:
         self.ws_slow_bytes = sfi.sfi_slow_workspace_bytes(self.kv)
         self.ws_sel_bytes = sfi.sfi_select_workspace_bytes(B, Hkv, self.max_len)
         self.ws_fast_bytes = sfi.sfi_fast_workspace_bytes(self.kv, k, n_sink, window)
+        self.ws_step_bytes = sfi.sfi_decode_step_workspace_bytes(self.kv, k, n_sink, window)
         self.ws_slow = torch.empty(self.ws_slow_bytes, **u8)
         self.ws_sel = torch.empty(self.ws_sel_bytes, **u8)
         self.ws_fast = torch.empty(self.ws_fast_bytes, **u8)
+        self.ws_step = torch.empty(self.ws_step_bytes, **u8)
 
     # -- single calls -------------------------------------------------------
     def slow(self, q, seq_len, batch_ids, batch_n: int, stream=None, select: bool = True, out=None):
@@ -140,17 +142,37 @@ class SFIDecoder:
                           self.k, self.n_sink, self.window, self.out if out is None else out,
                           self.ws_fast, self.ws_fast_bytes, stream)
 
+    def co_step(self, q, seq_len, slow_ids, n_slow: int, fast_ids, n_fast: int, stream=None,
+                out=None, select: bool = True):
+        """Slow steps of slow_ids and fast steps of fast_ids in one co-launched
+        pass, then the selector of the slow sequences."""
+        self.kv.seq_len = seq_len.data_ptr() if torch.is_tensor(seq_len) else seq_len
+        sfi.sfi_decode_step(self.kv, slow_ids, n_slow, fast_ids, n_fast, q,
+                            self.out if out is None else out, self.evidence, self.key_norm, self.ld,
+                            self.sel_idx, self.sel_count, self.Hkv, self.k, self.n_sink, self.window,
+                            self.ws_step, self.ws_step_bytes, stream)
+        if select and n_slow:
+            self.slow_select_only(self.kv.seq_len, slow_ids, n_slow, stream)
+
     def _new_event(self):
         e = torch.cuda.Event()
         self._events.append(e)
         return e
 
     # -- one decode step of a planned run ------------------------------------
-    def step(self, plan: DecodePlan, s: int, q_steps, stream=None, out=None):
-        """Decode step s: q_steps is the device tensor [steps][B][Hq][d]."""
+    def step(self, plan: DecodePlan, s: int, q_steps, stream=None, out=None, co: bool = True):
+        """Decode step s: q_steps is the device tensor [steps][B][Hq][d].
+
+        With co=True a step that has both slow and fast sequences runs them
+        in one co-launched pass (sfi_decode_step) before the selector;
+        otherwise the slow step, the selector and the fast step are separate
+        calls."""
         q = q_steps[s]
         sl = plan.seq_len[s]
         ns, nf = int(plan.n_slow[s]), int(plan.n_fast[s])
+        if co and ns and nf:
+            self.co_step(q, sl, plan.slow_ids[s], ns, plan.fast_ids[s], nf, stream, out=out)
+            return
         if ns:
             self.slow(q, sl, plan.slow_ids[s], ns, stream, out=out)
         if nf:

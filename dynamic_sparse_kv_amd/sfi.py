@@ -79,6 +79,11 @@ def lib():
         L.sfi_fast_step.argtypes = [P(sfi_kv), _vp, _c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int,
                                     _c_int, _vp, _vp, _sz, _vp]
         L.sfi_fast_step.restype = _c_int
+        L.sfi_decode_step_workspace_bytes.argtypes = [P(sfi_kv), _c_int, _c_int, _c_int]
+        L.sfi_decode_step_workspace_bytes.restype = _sz
+        L.sfi_decode_step.argtypes = [P(sfi_kv), _vp, _c_int, _vp, _c_int, _vp, _vp, _vp, _vp, _c_int,
+                                      _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _sz, _vp]
+        L.sfi_decode_step.restype = _c_int
         L.sfi_verify_aggregate.argtypes = [P(sfi_kv), _vp, _c_int, _vp, _c_int, ctypes.c_uint32, _vp,
                                            _vp, _c_int, _vp, _sz, _vp]
         L.sfi_verify_aggregate.restype = _c_int
@@ -193,6 +198,19 @@ def sfi_fast_step(kv: sfi_kv, batch_ids, batch_n: int, q, sel_idx, sel_count, se
     _check(lib().sfi_fast_step(ctypes.byref(kv), _ptr(batch_ids), batch_n, _ptr(q), _ptr(sel_idx),
                                _ptr(sel_count), sel_heads, sel_k, n_sink, window, _ptr(out),
                                _ptr(ws), ws_bytes, _stream(stream)), "sfi_fast_step")
+
+
+def sfi_decode_step_workspace_bytes(kv: sfi_kv, sel_k: int, n_sink: int, window: int) -> int:
+    return int(lib().sfi_decode_step_workspace_bytes(ctypes.byref(kv), sel_k, n_sink, window))
+
+
+def sfi_decode_step(kv: sfi_kv, slow_ids, n_slow: int, fast_ids, n_fast: int, q, out, evidence,
+                    key_norm, ld: int, sel_idx, sel_count, sel_heads: int, sel_k: int, n_sink: int,
+                    window: int, ws, ws_bytes: int, stream=None):
+    _check(lib().sfi_decode_step(ctypes.byref(kv), _ptr(slow_ids), n_slow, _ptr(fast_ids), n_fast,
+                                 _ptr(q), _ptr(out), _ptr(evidence), _ptr(key_norm), ld, _ptr(sel_idx),
+                                 _ptr(sel_count), sel_heads, sel_k, n_sink, window, _ptr(ws), ws_bytes,
+                                 _stream(stream)), "sfi_decode_step")
 
 
 def sfi_verify_aggregate(kv: sfi_kv, batch_ids, batch_n: int, q, T: int, row_mask: int, out, agg,

@@ -161,6 +161,28 @@ sfi_status sfi_fast_step(const sfi_kv *kv, const int32_t *batch_ids, int32_t bat
                          int32_t sel_heads, int32_t sel_k, int32_t n_sink, int32_t window,
                          float *out, void *ws, size_t ws_bytes, void *stream);
 
+/* One decode step of a batch whose sequences take different paths [SFI 3.A
+ * slow and fast steps; 3.C, which overlaps the slow path with fast steps]:
+ * the slow step (dense attention with evidence) of slow_ids[0..n_slow) and the
+ * fast step of fast_ids[0..n_fast), computed by one partial grid and one
+ * finalize grid in which both sets of sequences share the chip.  The outputs
+ * equal those of sfi_slow_step on slow_ids and sfi_fast_step on fast_ids, up to
+ * floating-point rounding (the two calls split the rows differently).
+ *   slow_ids, fast_ids  device int32 lists; together at most B ids, all
+ *                       distinct (a sequence takes one path per step).
+ *   evidence            required when n_slow > 0; key_norm optional.
+ *   ws                  sfi_decode_step_workspace_bytes(kv, sel_k, n_sink, window).
+ * Other arguments as in sfi_slow_step and sfi_fast_step.
+ * Errors: as those two calls, and SFI_ERR_RANGE if n_slow + n_fast > B. */
+size_t sfi_decode_step_workspace_bytes(const sfi_kv *kv, int32_t sel_k, int32_t n_sink,
+                                       int32_t window);
+sfi_status sfi_decode_step(const sfi_kv *kv, const int32_t *slow_ids, int32_t n_slow,
+                           const int32_t *fast_ids, int32_t n_fast, const uint16_t *q, float *out,
+                           float *evidence, float *key_norm, int32_t ld, const int32_t *sel_idx,
+                           const int32_t *sel_count, int32_t sel_heads, int32_t sel_k,
+                           int32_t n_sink, int32_t window, void *ws, size_t ws_bytes,
+                           void *stream);
+
 /* Verification with aggregated logits [Vegas 2, 2.A, 2.B, 3]: T query rows
  * per sequence; row t sits at position n - T + t (n = seq_len[b], which
  * already counts the T rows) and attends keys [0, n - T + t].

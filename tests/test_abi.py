@@ -140,6 +140,31 @@ def test_fast_step_validation():
     assert call(_kv(), batch_n=0) == sfi.SFI_OK
 
 
+def test_decode_step_validation():
+    L = sfi.lib()
+
+    def call(kv, n_slow=1, n_fast=1, evidence=FAKE, ld=1000, sel_count=FAKE, sel_heads=2,
+             sel_k=64, ws_bytes=1 << 40):
+        return L.sfi_decode_step(ctypes.byref(kv), FAKE, n_slow, FAKE, n_fast, FAKE, FAKE, evidence,
+                                 None, ld, FAKE, sel_count, sel_heads, sel_k, 4, 256, FAKE, ws_bytes,
+                                 None)
+
+    kv = _kv()
+    B = kv.B
+    assert call(kv, n_slow=B, n_fast=1) == sfi.SFI_ERR_RANGE            # more ids than sequences
+    assert call(kv, n_slow=-1) == sfi.SFI_ERR_RANGE
+    assert call(kv, evidence=None) == sfi.SFI_ERR_NULL                  # slow part needs evidence
+    assert call(kv, ld=10) == sfi.SFI_ERR_RANGE
+    assert call(kv, sel_count=None) == sfi.SFI_ERR_NULL
+    assert call(kv, sel_heads=3) == sfi.SFI_ERR_SHAPE
+    assert call(kv, ws_bytes=8) == sfi.SFI_ERR_WORKSPACE
+    assert call(_kv(d=256)) == sfi.SFI_ERR_UNSUPPORTED
+    assert call(kv, n_slow=0, n_fast=0) == sfi.SFI_OK
+    need = sfi.sfi_decode_step_workspace_bytes(kv, 64, 4, 256)
+    assert need == sfi.sfi_slow_workspace_bytes(kv) + sfi.sfi_fast_workspace_bytes(kv, 64, 4, 256)
+    assert call(kv, n_slow=0, n_fast=0, ws_bytes=need) == sfi.SFI_OK
+
+
 def test_verify_validation():
     L = sfi.lib()
 

@@ -385,6 +385,100 @@ def test_stream_pipelines_match_single_stream():
         assert torch.equal(res[0].view(torch.int32), r.view(torch.int32))
 
 
+# ------------------------------------------------- co-launched decode step
+
+@pytest.mark.parametrize("Hq,Hkv,d,paged", [(8, 2, 64, False), (40, 8, 128, True)])
+def test_decode_step_co_launch_matches_oracle(Hq, Hkv, d, paged):
+    """sfi_decode_step: slow steps (with evidence) of some sequences and fast
+    steps of the others in one pass, against the oracle."""
+    _say(f"co-launched step Hq={Hq} Hkv={Hkv} d={d} paged={paged}")
+    B = 5
+    lens = [4100, 2500, 5000, 700, 3300]
+    cap = 5100
+    K, V = _rand_kv(B, Hkv, cap, d, seed=300 + Hq, hh=9)
+    q = _rand_q((B, Hq, d), seed=301 + Hq)
+    seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    k = 200
+    rng = np.random.default_rng(Hq + d)
+    sel = np.full((B, Hkv, k), -1, dtype=np.int32)
+    cnt = np.zeros((B, Hkv), dtype=np.int32)
+    for b in range(B):
+        for g in range(Hkv):
+            c = min(k - 5, lens[b])
+            sel[b, g, :c] = np.sort(rng.choice(lens[b], c, replace=False))
+            cnt[b, g] = c
+    if paged:
+        cfg = W.CONFIGS["c5"].replace(B=B, Hq=Hq, Hkv=Hkv, d=d)
+        table, npages = W.page_table(cfg, np.full(B, cap))
+        Kd, Vd = W.to_paged(K, table, npages, 16), W.to_paged(V, table, npages, 16)
+        tab = torch.from_numpy(table).to(DEV)
+        dec = SFIDecoder(Kd, Vd, Hq, max(lens), n_sink=4, window=256, k=k, lam=0.3,
+                         page_table=tab, page_size=16)
+    else:
+        dec = SFIDecoder(K, V, Hq, max(lens), n_sink=4, window=256, k=k, lam=0.3)
+    dec.sel_idx.copy_(torch.from_numpy(sel))
+    dec.sel_count.copy_(torch.from_numpy(cnt))
+    dec.out.fill_(5.0)
+    slow_b, fast_b = [3, 0], [4, 1, 2]
+    sids = torch.tensor(slow_b, dtype=torch.int32, device=DEV)
+    fids = torch.tensor(fast_b, dtype=torch.int32, device=DEV)
+    dec.co_step(q, seq, sids, len(slow_b), fids, len(fast_b), select=False)
+    torch.cuda.synchronize()
+    out = dec.out.cpu().numpy()
+    ev = dec.evidence.cpu().numpy()
+    nrm = dec.key_norm.cpu().numpy()
+    Kb, Vb, qb = _bits(K), _bits(V), _bits(q)
+    for b in slow_b:
+        n = lens[b]
+        o_ref, p = O.dense_step(qb[b], Kb[b], Vb[b], n)
+        assert row_rel_err(out[b], o_ref) <= OUT_TOL
+        assert row_rel_err(ev[b, :, :n], O.evidence(p, Hkv)) <= EVID_TOL
+        np.testing.assert_allclose(nrm[b, :, :n], O.key_norms(Kb[b], n), rtol=NORM_TOL)
+    for b in fast_b:
+        lists = [sel[b, g, : cnt[b, g]] for g in range(Hkv)]
+        o_ref = O.fast_step(qb[b], Kb[b], Vb[b], lens[b], lists, 4, 256)
+        assert row_rel_err(out[b], o_ref) <= OUT_TOL
+
+
+def test_decode_run_mixed_batch_co_launch():
+    """Three sequences with their own schedules, 40 steps: every step that
+    mixes slow and fast sequences is co-launched; each sequence's outputs and
+    selections follow the oracle's decode run, and the separate-call path
+    agrees within tolerance."""
+    cfg = W.CONFIGS["c1"].replace(B=3, steps=40)
+    _say("mixed-batch decode run")
+    K, V = W.make_kv(cfg, device=DEV)
+    starts = W.sentence_starts(cfg)
+    slow = sfi.sfi_schedule(starts, cfg.budget).astype(bool)
+    assert any(slow[s].any() and (~slow[s]).any() for s in range(cfg.steps))
+    qh = W.make_queries(cfg, starts)
+    q = qh.to(DEV)
+    ctx = W.context_lengths(cfg)
+    plan = DecodePlan(slow, ctx, DEV)
+    Kb, Vb, qb = _bits(K), _bits(V), _bits(qh)
+    refs = [O.decode_run(qb[:, b], Kb[b], Vb[b], int(ctx[b]), slow[:, b], lam=cfg.lam, k=cfg.k,
+                         n_sink=cfg.n_sink, window=cfg.window) for b in range(cfg.B)]
+    decs = [SFIDecoder(K, V, cfg.Hq, int(ctx.max()) + cfg.steps, n_sink=cfg.n_sink,
+                       window=cfg.window, k=cfg.k, lam=cfg.lam, keep_fused=True) for _ in range(2)]
+    ties = 0
+    for s in range(cfg.steps):
+        for co, dec in zip((True, False), decs):
+            dec.step(plan, s, q, co=co)
+        torch.cuda.synchronize()
+        o_co, o_sep = decs[0].out.cpu().numpy(), decs[1].out.cpu().numpy()
+        for b in range(cfg.B):
+            r = refs[b][s]
+            assert row_rel_err(o_co[b], r["o"]) <= OUT_TOL, (s, b)
+            assert row_rel_err(o_sep[b], o_co[b]) <= OUT_TOL, (s, b)
+            if r["kind"] == "slow":
+                sel = decs[0].sel_idx[b].cpu().numpy()
+                cnt = decs[0].sel_count[b].cpu().numpy()
+                for g in range(cfg.Hkv):
+                    ties += check_selection(sel[g], cnt[g], r["s"][g], r["lo"], r["hi"], cfg.k)
+    _say(f"  near-tie differences over the run: {ties}")
+    assert ties == 0
+
+
 # ------------------------------------------------------------------- verify
 
 @pytest.mark.parametrize("Hq,Hkv,d,T", [(32, 8, 128, 8), (8, 2, 64, 8), (16, 8, 128, 4), (8, 8, 128, 1)])
