@@ -223,31 +223,35 @@ def main():
     # busy while the host enqueues the call and its events ----------------
     _log("[bench] per-call timing pass")
     flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-    calls = {"slow": [], "select": [], "fast": []}
-    bytes_by = {"slow": [], "select": [], "fast": []}
+    calls = {"step": [], "slow": [], "select": [], "fast": []}
+    bytes_by = {"step": [], "slow": [], "select": [], "fast": []}
     ev = []
+
+    def timed(kind, fn, nbytes):
+        flush.sum()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        ev.append((kind, e0, e1, nbytes))
+
     for s in range(K_steps):
         ns, nf = int(plan.n_slow[s]), int(plan.n_fast[s])
         lens = plan.seq_len_host[s]
+        sb = sum(algorithmic_bytes("slow", int(lens[b]), cfg) for b in np.nonzero(plan.slow[s])[0])
+        fb = sum(algorithmic_bytes("fast", int(lens[b]), cfg) for b in np.nonzero(~plan.slow[s])[0])
+        selb = sum(algorithmic_bytes("select", int(lens[b]), cfg) for b in np.nonzero(plan.slow[s])[0])
+        if ns and nf:   # the co-launched slow + fast pass the step runs, then the selector
+            timed("step", lambda: dec.co_step(q[s], plan.seq_len[s], plan.slow_ids[s], ns,
+                                              plan.fast_ids[s], nf, stream, select=False), sb + fb)
+        elif ns:
+            timed("slow", lambda: dec.slow(q[s], plan.seq_len[s], plan.slow_ids[s], ns, stream,
+                                           select=False), sb)
+        elif nf:
+            timed("fast", lambda: dec.fast(q[s], plan.seq_len[s], plan.fast_ids[s], nf, stream), fb)
         if ns:
-            flush.sum()
-            ids = np.nonzero(plan.slow[s])[0]
-            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-            e0.record(stream)
-            dec.slow(q[s], plan.seq_len[s], plan.slow_ids[s], ns, stream, select=False)
-            e1.record(stream)
-            dec.slow_select_only(plan.seq_len[s], plan.slow_ids[s], ns, stream)
-            e2.record(stream)
-            ev.append(("slow", e0, e1, sum(algorithmic_bytes("slow", int(lens[b]), cfg) for b in ids)))
-            ev.append(("select", e1, e2, sum(algorithmic_bytes("select", int(lens[b]), cfg) for b in ids)))
-        if nf:
-            flush.sum()
-            ids = np.nonzero(~plan.slow[s])[0]
-            e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
-            e0.record(stream)
-            dec.fast(q[s], plan.seq_len[s], plan.fast_ids[s], nf, stream)
-            e1.record(stream)
-            ev.append(("fast", e0, e1, sum(algorithmic_bytes("fast", int(lens[b]), cfg) for b in ids)))
+            timed("select", lambda: dec.slow_select_only(plan.seq_len[s], plan.slow_ids[s], ns, stream),
+                  selb)
     torch.cuda.synchronize()
     del flush
     for kind, a, b_, nbytes in ev:
@@ -268,8 +272,9 @@ def main():
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(dom, dc["alg_bytes_per_launch"]),
-                "kernel": {"slow": "sfi_slow_step: split-K partial + finalize kernels",
-                           "select": "sfi_select: fused selector kernel",
+                "kernel": {"step": "sfi_decode_step: co-launched slow + fast partial and finalize kernels",
+                           "slow": "sfi_slow_step: split-K partial + finalize kernels",
+                           "select": "sfi_select: six chunk-parallel selector kernels",
                            "fast": "sfi_fast_step: gather partial + finalize kernels"}[dom]}
 
     # ---- all-dense comparator: every sequence dense every step -----------

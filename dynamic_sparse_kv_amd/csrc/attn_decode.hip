@@ -43,6 +43,13 @@ namespace {
 #ifndef SFI_DENSE_LPR
 #define SFI_DENSE_LPR 0
 #endif
+// Dims of a key row held by lane `sub` of its lane group: line-major (1) puts
+// the lane's c-th 16-byte slice in the c-th 128-byte line of the row, so one
+// load instruction of the group reads whole lines; 0 gives each lane one
+// contiguous run of D/LPR dims.
+#ifndef SFI_LINE_MAJOR
+#define SFI_LINE_MAJOR 1
+#endif
 #ifndef SFI_WAVES_OF_WG
 #define SFI_WAVES_OF_WG 1
 #endif
@@ -98,8 +105,9 @@ __device__ __forceinline__ FastList fast_list(const int32_t *sel_idx, const int3
 template <int D, int G, bool PAGED, int MODE, bool EVID>
 __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, int g, int zb) {
   // 8 lanes per row halves the cross-lane reduction and softmax work per row
-  // compared with 16; wide groups (G*D > 640) use 16 to bound accumulators.
-  constexpr int LPR_AUTO = (G * D > 640) ? 16 : 8;
+  // compared with 16; wide groups (G*D >= 640) use 16 to bound accumulators
+  // (at G = 5, d = 128 eight lanes would need all 256 VGPRs).
+  constexpr int LPR_AUTO = (G * D >= 640) ? 16 : 8;
   constexpr int LPR_SET = (MODE == MODE_FAST) ? SFI_FAST_LPR : SFI_DENSE_LPR;
   constexpr int LPR = (LPR_SET == 8 || (LPR_SET == 16 && D == 128)) ? LPR_SET : LPR_AUTO;  // lanes per row
   constexpr int DPL = D / LPR;         // dims per lane (8 or 16)
@@ -132,13 +140,15 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
 
   const int sub = tid % LPR;
   const int rg = tid / LPR;
+  // element offset in the row of this lane's c-th 16-byte slice
+  auto slice = [&](int c) { return SFI_LINE_MAJOR ? c * LPR * 8 + sub * 8 : sub * DPL + 8 * c; };
 
   uint32_t qv[G][4 * NV];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
 #pragma unroll
     for (int c = 0; c < NV; ++c) {
-      const uint4 t = ldg16(a.q + ((size_t)b * a.Hq + g * G + h) * D + sub * DPL + 8 * c);
+      const uint4 t = ldg16(a.q + ((size_t)b * a.Hq + g * G + h) * D + slice(c));
       qv[h][4 * c + 0] = t.x; qv[h][4 * c + 1] = t.y; qv[h][4 * c + 2] = t.z; qv[h][4 * c + 3] = t.w;
     }
   }
@@ -194,11 +204,11 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
         j = (p < p1) ? p : -1;
       }
       st.j[u] = j;
-      const size_t off = kv_row<D, PAGED>(a.kv, b, g, max(j, 0)) + sub * DPL;
+      const size_t off = kv_row<D, PAGED>(a.kv, b, g, max(j, 0));
 #pragma unroll
       for (int c = 0; c < NV; ++c) {
-        st.k[u][c] = ldg16(a.kv.k + off + 8 * c);
-        st.v[u][c] = ldg16(a.kv.v + off + 8 * c);
+        st.k[u][c] = ldg16(a.kv.k + off + slice(c));
+        st.v[u][c] = ldg16(a.kv.v + off + slice(c));
       }
     }
   };
@@ -342,7 +352,10 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
 #pragma unroll
   for (int h = 0; h < G; ++h) {
 #pragma unroll
-    for (int i = 0; i < KEPT; ++i) s_acc[wv][h][sub * DPL + dim_off + i] = acc[h][i];
+    for (int i = 0; i < KEPT; ++i) {
+      const int li = dim_off + i;  // index in the lane's slices
+      s_acc[wv][h][slice(li / 8) + li % 8] = acc[h][i];
+    }
     if (lane == 0) {
       s_m[wv][h] = m[h];
       s_z[wv][h] = Z[h];
@@ -647,8 +660,10 @@ hipError_t slow_t(const AttnLaunch &a_in, hipStream_t st) {
   AttnLaunch a = a_in;
   const bool side = a.evidence != nullptr || a.key_norm != nullptr;
   {
-    const int slots = side ? resident_slots<partial_kernel<D, G, PAGED, MODE_SLOW, true>>()
-                           : resident_slots<partial_kernel<D, G, PAGED, MODE_SLOW, false>>();
+    // planned with the contiguous-cache kernel's occupancy, so a paged cache
+    // gets the same split plan and therefore the same bits
+    const int slots = side ? resident_slots<partial_kernel<D, G, false, MODE_SLOW, true>>()
+                           : resident_slots<partial_kernel<D, G, false, MODE_SLOW, false>>();
     a.plan = plan_splits(a.max_len, a.batch_n * a.Hkv, slots, a.plan.stride, 1 << 30);
   }
   const PartialArgs p = partial_args<D>(a);
@@ -673,7 +688,7 @@ template <int D, int G, bool PAGED>
 hipError_t fast_t(const AttnLaunch &a_in, hipStream_t st) {
   AttnLaunch a = a_in;
   {
-    const int slots = resident_slots<partial_kernel<D, G, PAGED, MODE_FAST, false>>();
+    const int slots = resident_slots<partial_kernel<D, G, false, MODE_FAST, false>>();
     a.plan = plan_splits(fast_rows(a), a.batch_n * a.Hkv, slots, a.plan.stride, kMaxFastChunk);
   }
   const PartialArgs p = partial_args<D>(a);
@@ -696,12 +711,20 @@ template <int D, int G, bool PAGED>
 hipError_t step_t(const AttnLaunch &sa_in, const AttnLaunch &fa_in, hipStream_t st) {
   AttnLaunch sa = sa_in, fa = fa_in;
   {
-    const int slots = resident_slots<copartial_kernel<D, G, PAGED>>();
+    const int slots = resident_slots<copartial_kernel<D, G, false>>();
     const long long Ls = sa.max_len, Lf = fast_rows(fa);
-    const long long rows = Ls * sa.batch_n * sa.Hkv + Lf * fa.batch_n * fa.Hkv;
-    const long long R = (rows + slots - 1) / slots;
-    sa.plan = plan_rows(Ls, sa.plan.stride, R, 1 << 30);
-    fa.plan = plan_rows(Lf, fa.plan.stride, R, kMaxFastChunk);
+    const long long ps = (long long)sa.batch_n * sa.Hkv, pf = (long long)fa.batch_n * fa.Hkv;
+    // smallest multiple of the granule whose rounded-up splits still fit the
+    // resident slots in one wave (a second wave would double the runtime)
+    long long R = (Ls * ps + Lf * pf + slots - 1) / slots;
+    R = (R + kSplitGranule - 1) / kSplitGranule * kSplitGranule;
+    for (;;) {
+      sa.plan = plan_rows(Ls, sa.plan.stride, R, 1 << 30);
+      fa.plan = plan_rows(Lf, fa.plan.stride, R, kMaxFastChunk);
+      const long long wgs = ps * sa.plan.splits + pf * fa.plan.splits;
+      if (wgs <= slots || (sa.plan.splits == 1 && fa.plan.splits == 1)) break;
+      R += kSplitGranule;
+    }
   }
   const int ns = sa.plan.splits * sa.Hkv * sa.batch_n;
   const int nf = fa.plan.splits * fa.Hkv * fa.batch_n;
