@@ -274,7 +274,7 @@ def main():
                 "traffic": measured_traffic(dom, dc["alg_bytes_per_launch"]),
                 "kernel": {"step": "sfi_decode_step: co-launched slow + fast partial and finalize kernels",
                            "slow": "sfi_slow_step: split-K partial + finalize kernels",
-                           "select": "sfi_select: six chunk-parallel selector kernels",
+                           "select": "sfi_select: four chunk-parallel selector kernels (norm sums, prior, keys + bucket sort, pick)",
                            "fast": "sfi_fast_step: gather partial + finalize kernels"}[dom]}
 
     # ---- all-dense comparator: every sequence dense every step -----------

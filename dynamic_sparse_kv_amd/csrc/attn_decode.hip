@@ -102,7 +102,7 @@ __device__ __forceinline__ FastList fast_list(const int32_t *sel_idx, const int3
 // One workgroup's share of a decode step: rows [split*chunk, ...) of the row
 // list of (sequence batch_ids[zb], kv head g).  A device function so that the
 // co-launch kernel below can run slow and fast shares in one grid.
-template <int D, int G, bool PAGED, int MODE, bool EVID>
+template <int D, int G, bool PAGED, int MODE, bool EVID, bool STREAM = false>
 __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, int g, int zb) {
   // 8 lanes per row halves the cross-lane reduction and softmax work per row
   // compared with 16; wide groups (G*D >= 640) use 16 to bound accumulators
@@ -207,8 +207,17 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
       const size_t off = kv_row<D, PAGED>(a.kv, b, g, max(j, 0));
 #pragma unroll
       for (int c = 0; c < NV; ++c) {
-        st.k[u][c] = ldg16(a.kv.k + off + slice(c));
-        st.v[u][c] = ldg16(a.kv.v + off + slice(c));
+        // the slow share of a co-launched step streams its rows once with a
+        // non-temporal hint, so it does not evict the rows that the fast
+        // share (and the next fast steps) read again; alone, a dense stream
+        // measured faster with ordinary loads
+        if constexpr (STREAM) {
+          st.k[u][c] = ldg16_stream(a.kv.k + off + slice(c));
+          st.v[u][c] = ldg16_stream(a.kv.v + off + slice(c));
+        } else {
+          st.k[u][c] = ldg16(a.kv.k + off + slice(c));
+          st.v[u][c] = ldg16(a.kv.v + off + slice(c));
+        }
       }
     }
   };
@@ -398,8 +407,8 @@ __global__ __launch_bounds__(kThreads) void copartial_kernel(PartialArgs s, Part
                                                              int f_splits, int Hkv, int ns) {
   int id = blockIdx.x;
   if (id < ns) {
-    partial_body<D, G, PAGED, MODE_SLOW, true>(s, id % s_splits, (id / s_splits) % Hkv,
-                                               id / (s_splits * Hkv));
+    partial_body<D, G, PAGED, MODE_SLOW, true, true>(s, id % s_splits, (id / s_splits) % Hkv,
+                                                     id / (s_splits * Hkv));
   } else {
     id -= ns;
     partial_body<D, G, PAGED, MODE_FAST, false>(f, id % f_splits, (id / f_splits) % Hkv,

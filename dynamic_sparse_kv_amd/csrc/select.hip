@@ -8,33 +8,37 @@
 // ranks aggregated verify logits the same way, with one list per sequence.
 //
 // A selector row (sequence, head row) is cut into chunks of 2048 keys, one
-// 256-thread workgroup per chunk, so a row's loads and arithmetic run on ~16
-// compute units instead of one.  Each step that needs a row-wide result is a
-// kernel boundary (no workgroup ever waits for another):
-//   1. norm sums     (fused)  per-chunk sum and sum of squares of the key
-//                             norms (fp64);
-//   2. prior         (fused)  mean and population std from the chunk sums
-//                             (fixed order), prior weights w_j and their
-//                             per-chunk sums; also clears the row's histogram;
-//   3. keys                   s_j = (1 - lambda) f_j + lambda w_j / sum(w)
-//                             as an order-preserving 32-bit key (0 for keys
-//                             outside the candidate range), stored; a
-//                             histogram of the top 12 key bits, merged into
-//                             the row's histogram with integer atomics;
-//   4. tie bin                every chunk finds the bin holding the k-th
-//                             largest key from the row histogram; counts its
-//                             keys above that bin and appends the keys inside
-//                             it, as 64-bit (key, inverted index) composites,
-//                             to the row's candidate list;
-//   5. threshold (one workgroup per row) radix-selects the composite
-//                             threshold T among the candidates (the index part
-//                             makes lower indices win ties), then turns
-//                             per-chunk winner counts into output offsets;
-//   6. compaction             each chunk writes its winners, ascending, at
-//                             its offset.
-// Integer atomics only build histograms and reserve list slots, and every
+// 256-thread workgroup per chunk, so every pass over a row's keys runs on
+// ~16 compute units per row instead of one.  Each step that needs a row-wide
+// result is a kernel boundary (no workgroup ever waits for another):
+//   1. norm sums (fused)  per-chunk sum and sum of squares of the key norms
+//                         (fp64);
+//   2. prior     (fused)  mean and population std from the chunk sums (fixed
+//                         order), prior weights w_j and their per-chunk sums;
+//                         also clears the row's histogram;
+//   3. keys               s_j = (1 - lambda) f_j + lambda w_j / sum(w) as an
+//                         order-preserving 32-bit key; the chunk's candidate
+//                         keys are bucket-sorted by their top 12 bits in LDS
+//                         and written (one coalesced pass) as 64-bit (key,
+//                         inverted index) composites in descending bucket
+//                         order, with the
+//                         chunk's cumulative bucket counts; the bucket counts
+//                         are merged into the row histogram with integer
+//                         atomics;
+//   4. pick (per chunk)   every chunk workgroup reads the row histogram and
+//                         finds the bucket b1 holding the k-th largest key;
+//                         the bucket's keys (a contiguous run in each chunk)
+//                         are gathered and radix-selected to the composite
+//                         threshold T (the index part makes lower indices win
+//                         ties).  Keys in buckets above b1 and bucket keys
+//                         >= T win.  Per-chunk winner counts give each chunk
+//                         its output offset, and the chunk writes its winners
+//                         in ascending index order through an LDS bitmap.
+//   The threshold search is repeated by every chunk of the row, which costs
+//   O(candidates in b1) per workgroup and saves a launch.
+// Integer atomics only build histograms and reserve bucket slots, and every
 // floating-point sum runs in a fixed order, so results are bitwise
-// repeatable.
+// repeatable (the order of keys inside a bucket does not affect any result).
 #include "sfi_internal.hpp"
 
 namespace sfi {
@@ -43,15 +47,18 @@ namespace {
 constexpr int kT = 256;                 // threads of a chunk workgroup
 constexpr int kTW = kT / 64;
 constexpr int kCH = kSelChunk;          // keys per chunk
-constexpr int kHalf = kCH / 2;          // keys per half chunk (4 per thread)
+constexpr int kQuarter = kCH / 2;       // keys per half chunk (4 per thread)
 constexpr int kPT = kCH / kT;           // keys per thread
-constexpr int kD1 = 12;                 // first digit: key bits 31..20
+constexpr int kD1 = 12;                 // bucket: key bits 31..20
 constexpr int kBins1 = 1 << kD1;
-constexpr int kRT = 1024;               // threads of the threshold workgroup
-constexpr int kRW = kRT / 64;
-constexpr int kD2 = 11;                 // digit width inside the tie bin
+constexpr int kBPT = kBins1 / kT;       // buckets per thread
+constexpr int kD2 = 11;                 // digit width inside the bucket
 constexpr int kBins2 = 1 << kD2;
-static_assert(kHalf == 4 * kT, "a half chunk is four keys per thread");
+constexpr int kCandLds = 4096;          // bucket candidates gathered into LDS
+constexpr int kCPT = kSelMaxChunks / kT;  // chunks per thread in the pick scans
+static_assert(kQuarter == 4 * kT, "a half chunk is four keys per thread");
+static_assert(kBPT == 16, "sixteen buckets per thread");
+static_assert(kCH <= 65535, "cumulative bucket counts are 16-bit");
 
 template <int NW>
 __device__ __forceinline__ double block_sum_d(double x, double *s_red) {
@@ -92,8 +99,9 @@ __device__ __forceinline__ int block_exscan(int v, int *s_wave, int *total) {
 }
 
 // Row of the selector handled by this workgroup, and its geometry.
+// Candidates are [lo, hi); nch chunks hold them (0 when the range is empty).
 struct RowGeo {
-  int b, h, n, lo, hi, span;
+  int b, h, n, lo, hi, span, nch;
   size_t row;
 };
 
@@ -105,25 +113,27 @@ __device__ __forceinline__ bool row_geo(const SelectLaunch &a, RowGeo &r) {
   r.lo = a.n_sink;
   r.hi = max(a.n_sink, r.n - a.window);
   r.span = (a.mode == 0) ? r.n : r.hi;  // keys [0, span) are visited
+  r.nch = (r.hi > r.lo) ? (r.hi + kCH - 1) / kCH : 0;
   r.row = (size_t)r.b * a.H + r.h;
   return true;
 }
 
-// Key i of thread t in a chunk sits at j0 + (i / 4) * kHalf + 4 t + i % 4.
+// Key i of thread t in a chunk sits at j0 + (i / 4) * kQuarter + 4 t + i % 4.
 __device__ __forceinline__ int key_pos(int j0, int i) {
-  return j0 + (i >> 2) * kHalf + 4 * (int)threadIdx.x + (i & 3);
+  return j0 + (i >> 2) * kQuarter + 4 * (int)threadIdx.x + (i & 3);
 }
 
 // Values [j0, j0 + kCH) of a row restricted to [0, span) (0 outside).  The
 // half-chunk cases are uniform across the workgroup, so no load sits behind a
 // per-lane branch: a whole half in range takes one 16-byte load per thread.
+// Requires j0 < span.
 __device__ __forceinline__ void load_chunk(const float *p, int j0, int span, bool vec,
                                            float (&x)[kPT]) {
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf) {
-    const int base = j0 + hf * kHalf;
+    const int base = j0 + hf * kQuarter;
     const int j = base + 4 * (int)threadIdx.x;
-    if (vec && base + kHalf <= span) {
+    if (vec && base + kQuarter <= span) {
       const float4 t = *reinterpret_cast<const float4 *>(p + j);
       x[4 * hf + 0] = t.x; x[4 * hf + 1] = t.y; x[4 * hf + 2] = t.z; x[4 * hf + 3] = t.w;
     } else if (base >= span) {
@@ -136,14 +146,6 @@ __device__ __forceinline__ void load_chunk(const float *p, int j0, int span, boo
         x[4 * hf + e] = (j + e < span) ? t : 0.f;
       }
     }
-  }
-}
-
-__device__ __forceinline__ void load_keys(const uint32_t *p, int j0, uint32_t (&k)[kPT]) {
-#pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
-    const uint4 t = *reinterpret_cast<const uint4 *>(p + j0 + hf * kHalf + 4 * threadIdx.x);
-    k[4 * hf + 0] = t.x; k[4 * hf + 1] = t.y; k[4 * hf + 2] = t.z; k[4 * hf + 3] = t.w;
   }
 }
 
@@ -162,6 +164,10 @@ __device__ __forceinline__ float prior_w(float nu, int j, float muf, float cz, f
 // Composite rank value: larger key first, then lower index.
 __device__ __forceinline__ unsigned long long composite(uint32_t key, int j) {
   return ((unsigned long long)key << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)j);
+}
+
+__device__ __forceinline__ int composite_index(unsigned long long c) {
+  return (int)(0xFFFFFFFFu - (uint32_t)(c & 0xFFFFFFFFull));
 }
 
 // ---------------------------------------------------------------- 1. sums
@@ -196,13 +202,14 @@ __global__ __launch_bounds__(kT) void prior_kernel(SelectLaunch a) {
   if (!row_geo(a, r)) return;
   const int p = blockIdx.x, j0 = p * kCH;
   const int tid = threadIdx.x;
-  // clear the row's histogram (striped over all chunk workgroups) and its
-  // candidate counter, for steps 3 and 4
-  uint32_t *h1 = a.ws.hist + r.row * kBins1;
+  // clear the row histogram (striped over all chunk workgroups) for step 3
+  uint32_t *h1 = a.ws.ghist + r.row * kBins1;
   for (int i = p * kT + tid; i < kBins1; i += a.ws.P * kT) h1[i] = 0u;
-  if (p == 0 && tid == 0) a.ws.meta[r.row].m = 0;
   if constexpr (FUSED) {
     if (j0 >= r.n) return;
+    const float *nu = a.key_norm + r.row * a.ld;
+    float x[kPT];
+    load_chunk(nu, j0, r.n, aligned16(nu) && (a.ld & 3) == 0, x);
     const int Pn = (r.n + kCH - 1) / kCH;
     double s1 = 0.0, s2 = 0.0;
     for (int q = tid; q < Pn; q += kT) {
@@ -219,9 +226,6 @@ __global__ __launch_bounds__(kT) void prior_kernel(SelectLaunch a) {
     const float cz = -a.norm_coef * isd * kLog2e;
     const float ct = kLog2e / a.pos_tau;
     const float tq = (float)(r.n - 1);
-    const float *nu = a.key_norm + r.row * a.ld;
-    float x[kPT];
-    load_chunk(nu, j0, r.n, aligned16(nu) && (a.ld & 3) == 0, x);
     float sw = 0.f;
 #pragma unroll
     for (int i = 0; i < kPT; ++i) {
@@ -243,31 +247,33 @@ __global__ __launch_bounds__(kT) void prior_kernel(SelectLaunch a) {
 template <bool FUSED>
 __global__ __launch_bounds__(kT) void keys_kernel(SelectLaunch a) {
   __shared__ unsigned hist[kBins1];
+  __shared__ unsigned long long s_sorted[kCH];
   __shared__ double s_red[kTW];
+  __shared__ int s_wave[kTW];
   RowGeo r;
   if (!row_geo(a, r)) return;
   const int p = blockIdx.x, j0 = p * kCH;
   if (j0 >= r.span) return;
   const int tid = threadIdx.x;
-  for (int i = tid; i < kBins1; i += kT) hist[i] = 0u;
 
   float s[kPT];
   if constexpr (FUSED) {
-    const int Pn = (r.n + kCH - 1) / kCH;
-    double W = 0.0;
-    for (int q = tid; q < Pn; q += kT) W += a.ws.wsum[r.row * a.ws.P + q];
-    W = block_sum_d<kTW>(W, s_red);
-    const float cf = 1.0f - a.lambda;
-    const float cr = W > 0.0 ? (float)((double)a.lambda / W) : 0.f;
-    const float muf = a.ws.meta[r.row].muf, cz = a.ws.meta[r.row].cz;
-    const float ct = kLog2e / a.pos_tau;
-    const float tq = (float)(r.n - 1);
     const float *f = a.score + r.row * a.ld;
     const float *nu = a.key_norm + r.row * a.ld;
     const bool vec = aligned16(f) && aligned16(nu) && (a.ld & 3) == 0;
     float fv[kPT], nv[kPT];
     load_chunk(f, j0, r.n, vec, fv);
     load_chunk(nu, j0, r.n, vec, nv);
+    const int Pn = (r.n + kCH - 1) / kCH;
+    double W = 0.0;
+    for (int q = tid; q < Pn; q += kT) W += a.ws.wsum[r.row * a.ws.P + q];
+    for (int i = tid; i < kBins1; i += kT) hist[i] = 0u;
+    W = block_sum_d<kTW>(W, s_red);
+    const float cf = 1.0f - a.lambda;
+    const float cr = W > 0.0 ? (float)((double)a.lambda / W) : 0.f;
+    const float muf = a.ws.meta[r.row].muf, cz = a.ws.meta[r.row].cz;
+    const float ct = kLog2e / a.pos_tau;
+    const float tq = (float)(r.n - 1);
 #pragma unroll
     for (int i = 0; i < kPT; ++i) {
       const int j = key_pos(j0, i);
@@ -285,123 +291,76 @@ __global__ __launch_bounds__(kT) void keys_kernel(SelectLaunch a) {
   } else {
     const float *sc = a.score + r.row * a.ld;
     load_chunk(sc, j0, r.span, aligned16(sc) && (a.ld & 3) == 0, s);
+    for (int i = tid; i < kBins1; i += kT) hist[i] = 0u;
+    __syncthreads();
   }
+  if (p >= r.nch) return;  // no candidates in this chunk
+
   uint32_t key[kPT];
 #pragma unroll
   for (int i = 0; i < kPT; ++i) {
     const int j = key_pos(j0, i);
     key[i] = (j >= r.lo && j < r.hi) ? float_key(s[i]) : 0u;
-  }
-  uint32_t *kp = a.ws.keys + r.row * a.ws.ldk + j0;
-#pragma unroll
-  for (int hf = 0; hf < 2; ++hf)
-    *reinterpret_cast<uint4 *>(kp + hf * kHalf + 4 * tid) =
-        make_uint4(key[4 * hf], key[4 * hf + 1], key[4 * hf + 2], key[4 * hf + 3]);
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < kPT; ++i)
     if (key[i]) atomicAdd(&hist[key[i] >> (32 - kD1)], 1u);
+  }
   __syncthreads();
-  uint32_t *h1 = a.ws.hist + r.row * kBins1;
-  for (int i = tid; i < kBins1; i += kT) {
-    const unsigned c = hist[i];
-    if (c) atomicAdd(&h1[i], c);
-  }
-}
-
-// ----------------------------------------------------------- 4. tie bin
-__global__ __launch_bounds__(kT) void tie_kernel(SelectLaunch a) {
-  __shared__ int s_wave[kTW];
-  __shared__ int s_res[3];
-  __shared__ int s_base;
-  RowGeo r;
-  if (!row_geo(a, r)) return;
-  const int p = blockIdx.x, j0 = p * kCH;
-  if (j0 >= r.span) return;
-  const int tid = threadIdx.x;
-  const int K = a.k;
-
-  // The row histogram: thread t holds bins BPT t .. BPT t + BPT - 1.
-  constexpr int BPT = kBins1 / kT;
-  const uint32_t *h1 = a.ws.hist + r.row * kBins1 + BPT * tid;
-  uint32_t hb[BPT];
+  // Cumulative counts in descending bucket order: cum[b] = keys in buckets
+  // >= b.  Thread t owns buckets 16 t .. 16 t + 15.
+  uint32_t c[kBPT];
+  int tot = 0;
 #pragma unroll
-  for (int i = 0; i < BPT; i += 4) {
-    const uint4 t = *reinterpret_cast<const uint4 *>(h1 + i);
-    hb[i] = t.x; hb[i + 1] = t.y; hb[i + 2] = t.z; hb[i + 3] = t.w;
+  for (int i = 0; i < kBPT; ++i) {
+    c[i] = hist[kBPT * tid + i];
+    tot += (int)c[i];
   }
-  int cnt = 0;
-#pragma unroll
-  for (int i = 0; i < BPT; ++i) cnt += (int)hb[i];
   int total;
-  const int below = block_exscan<kTW>(cnt, s_wave, &total);  // keys in lower bins
-  if (tid == 0) {
-    s_res[0] = 0;  // b1 = 0 takes every candidate (their top digit is > 0)
-    s_res[1] = 0;
-    s_res[2] = 0;
+  const int below = block_exscan<kTW>(tot, s_wave, &total);  // keys in lower buckets
+  int run = total - below - tot;                              // keys in higher buckets
+  uint32_t cum[kBPT];
+#pragma unroll
+  for (int i = kBPT - 1; i >= 0; --i) {
+    run += (int)c[i];
+    cum[i] = (uint32_t)run;
   }
+  // bucket b's first slot in the descending layout is cum[b] - count[b]
+#pragma unroll
+  for (int i = 0; i < kBPT; ++i) hist[kBPT * tid + i] = cum[i] - c[i];
+  uint4 *cd = reinterpret_cast<uint4 *>(a.ws.cum + (r.row * a.ws.P + p) * kBins1 + kBPT * tid);
+  cd[0] = make_uint4(cum[0] | cum[1] << 16, cum[2] | cum[3] << 16, cum[4] | cum[5] << 16,
+                     cum[6] | cum[7] << 16);
+  cd[1] = make_uint4(cum[8] | cum[9] << 16, cum[10] | cum[11] << 16, cum[12] | cum[13] << 16,
+                     cum[14] | cum[15] << 16);
+  uint32_t *h1 = a.ws.ghist + r.row * kBins1 + kBPT * tid;
+#pragma unroll
+  for (int i = 0; i < kBPT; ++i)
+    if (c[i]) atomicAdd(&h1[i], c[i]);
   __syncthreads();
-  const int above = total - below - cnt;
-  if (total > K && above < K && K <= above + cnt) {
-    int acc = above;
-    for (int i = BPT - 1; i >= 0; --i) {
-      const int c = (int)hb[i];
-      if (acc + c >= K) {
-        s_res[0] = BPT * tid + i;
-        s_res[1] = K - acc;
-        s_res[2] = c;
-        break;
-      }
-      acc += c;
-    }
-  }
-  __syncthreads();
-  const uint32_t b1 = (uint32_t)s_res[0];
-  if (p == 0 && tid == 0) {
-    a.ws.meta[r.row].b1 = (int)b1;
-    a.ws.meta[r.row].want1 = s_res[1];
-  }
-
-  uint32_t key[kPT];
-  load_keys(a.ws.keys + r.row * a.ws.ldk, j0, key);
-  int gt = 0, ne = 0;
+  // bucket sort in LDS, then one coalesced write of the chunk's sorted run
 #pragma unroll
   for (int i = 0; i < kPT; ++i) {
-    const uint32_t d = key[i] >> (32 - kD1);
-    gt += (key[i] != 0u && d > b1) ? 1 : 0;
-    ne += (key[i] != 0u && b1 != 0u && d == b1) ? 1 : 0;
-  }
-  int gtot;
-  block_exscan<kTW>(gt, s_wave, &gtot);
-  int etot;
-  const int eoff = block_exscan<kTW>(ne, s_wave, &etot);
-  if (tid == 0) {
-    a.ws.gt1[r.row * a.ws.P + p] = gtot;
-    s_base = etot ? atomicAdd(&a.ws.meta[r.row].m, etot) : 0;
-  }
-  __syncthreads();
-  if (ne) {
-    unsigned long long *cl = a.ws.cand + r.row * a.ws.ldk + s_base + eoff;
-    int o = 0;
-#pragma unroll
-    for (int i = 0; i < kPT; ++i) {
-      if (key[i] != 0u && (key[i] >> (32 - kD1)) == b1) cl[o++] = composite(key[i], key_pos(j0, i));
+    if (key[i]) {
+      const unsigned slot = atomicAdd(&hist[key[i] >> (32 - kD1)], 1u);
+      s_sorted[slot] = composite(key[i], key_pos(j0, i));
     }
   }
+  __syncthreads();
+  unsigned long long *so = a.ws.sorted + (r.row * a.ws.P + p) * kCH;
+  for (int i = tid; i < total; i += kT) so[i] = s_sorted[i];
 }
 
 // Bin of an nb-bin histogram (nb <= kBins2, highest bin = largest values)
 // holding the want-th largest element: s_res = {bin, rank inside it, count}.
-__device__ __forceinline__ void find_bin_row(const unsigned *hist, int nb, int want, int *s_wave,
-                                             int *s_res) {
+// s_res must hold a default before the call; the call ends with a barrier.
+__device__ __forceinline__ void find_bin_desc(const unsigned *hist, int nb, int want, int *s_wave,
+                                              int *s_res) {
   const int t = threadIdx.x;
-  constexpr int BPT = kBins2 / kRT;
+  constexpr int BPT = kBins2 / kT;
   const int top = nb - 1 - BPT * t;
   int cnt = 0;
 #pragma unroll
   for (int i = 0; i < BPT; ++i) cnt += (top - i >= 0) ? (int)hist[top - i] : 0;
   int total;
-  const int above = block_exscan<kRW>(cnt, s_wave, &total);
+  const int above = block_exscan<kTW>(cnt, s_wave, &total);
   if (top >= 0 && above < want && want <= above + cnt) {
     int acc = above;
     for (int i = 0; i < BPT && top - i >= 0; ++i) {
@@ -418,45 +377,152 @@ __device__ __forceinline__ void find_bin_row(const unsigned *hist, int nb, int w
   __syncthreads();
 }
 
-// ---------------------------------------------------------- 5. threshold
-__global__ __launch_bounds__(kRT) void threshold_kernel(SelectLaunch a) {
-  __shared__ unsigned hist[kBins2];
-  __shared__ int cnt[kSelMaxChunks];
-  __shared__ int s_wave[kRW];
+// Cumulative bucket count cum[b] (keys in buckets >= b) of chunk q; 0 for b
+// past the last bucket.
+__device__ __forceinline__ int cum_at(const SelectLaunch &a, size_t row, int q, int b) {
+  return b < kBins1 ? (int)a.ws.cum[(row * a.ws.P + q) * kBins1 + b] : 0;
+}
+
+// ----------------------------------------------------------- 4. pick
+__global__ __launch_bounds__(kT) void pick_kernel(SelectLaunch a) {
+  __shared__ unsigned h2[kBins2];
+  __shared__ unsigned long long s_cand[kCandLds];
+  __shared__ int s_above[kSelMaxChunks];   // winners above the bucket, per chunk
+  __shared__ int s_toff[kSelMaxChunks + 1];  // bucket candidates before each chunk
+  __shared__ int s_tw[kSelMaxChunks];      // bucket winners per chunk
+  __shared__ unsigned s_bits[kCH / 32];
+  __shared__ int s_wave[kTW];
   __shared__ int s_res[3];
   RowGeo r;
   if (!row_geo(a, r)) return;
-  const int tid = threadIdx.x;
+  const int p = blockIdx.x, tid = threadIdx.x;
+  if (p >= max(r.nch, 1)) return;
   const int K = a.k;
-  const int Pn = (r.span + kCH - 1) / kCH;
-  const int b1 = a.ws.meta[r.row].b1;
-  const int want1 = a.ws.meta[r.row].want1;
-  const int m = (b1 != 0) ? a.ws.meta[r.row].m : 0;
-  const unsigned long long *cl = a.ws.cand + r.row * a.ws.ldk;
+  int32_t *out = a.sel_idx + r.row * K;
+  const unsigned long long *srow = a.ws.sorted + r.row * a.ws.P * kCH;
 
-  // Radix select of the want1-th largest composite among the m candidates.
-  // Their top 12 bits all equal b1; digits of 11 bits cover bits 51..0.
+  // this chunk's bucket-sorted composites (slots past its candidates unused)
+  unsigned long long own[kPT];
+#pragma unroll
+  for (int i = 0; i < kPT; ++i) own[i] = (p < r.nch) ? srow[p * kCH + tid + kT * i] : 0ull;
+
+  // 1. Bucket b1 holding the K-th largest key; thread t holds buckets
+  //    16 t .. 16 t + 15 of the row histogram.
+  uint32_t hb[kBPT];
+  {
+    const uint4 *hp = reinterpret_cast<const uint4 *>(a.ws.ghist + r.row * kBins1 + kBPT * tid);
+#pragma unroll
+    for (int i = 0; i < kBPT / 4; ++i) {
+      const uint4 v = hp[i];
+      hb[4 * i] = v.x; hb[4 * i + 1] = v.y; hb[4 * i + 2] = v.z; hb[4 * i + 3] = v.w;
+    }
+  }
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < kBPT; ++i) cnt += (int)hb[i];
+  int total;
+  const int below = block_exscan<kTW>(cnt, s_wave, &total);
+  if (tid == 0) {
+    s_res[0] = 0;  // b1 = 0: every candidate wins (candidate keys never sit in bucket 0)
+    s_res[1] = 0;
+    s_res[2] = 0;
+  }
+  __syncthreads();
+  const int above = total - below - cnt;
+  if (total > K && above < K && K <= above + cnt) {
+    int acc = above;
+    for (int i = kBPT - 1; i >= 0; --i) {
+      const int c = (int)hb[i];
+      if (acc + c >= K) {
+        s_res[0] = kBPT * tid + i;
+        s_res[1] = K - acc;
+        s_res[2] = c;
+        break;
+      }
+      acc += c;
+    }
+  }
+  __syncthreads();
+  const int b1 = s_res[0];
+  const int want1 = s_res[1];
+  const int m = s_res[2];
+  const bool split = b1 != 0 && want1 < m;  // only part of bucket b1 wins
+
+  // 2. Per chunk: winners above the bucket (a prefix of its sorted run) and
+  //    its run of bucket-b1 keys.  Thread t handles chunks kCPT t ...
+  int na[kCPT], nt[kCPT];
+  int tsum = 0;
+#pragma unroll
+  for (int i = 0; i < kCPT; ++i) {
+    const int q = kCPT * tid + i;
+    na[i] = nt[i] = 0;
+    if (q < r.nch) {
+      if (b1 == 0) {
+        na[i] = cum_at(a, r.row, q, 0);
+      } else if (split) {
+        na[i] = cum_at(a, r.row, q, b1 + 1);
+        nt[i] = cum_at(a, r.row, q, b1) - na[i];
+      } else {
+        na[i] = cum_at(a, r.row, q, b1);
+      }
+      s_above[q] = na[i];
+    }
+    tsum += nt[i];
+  }
+  int mtot;
+  int toff = block_exscan<kTW>(tsum, s_wave, &mtot);
+#pragma unroll
+  for (int i = 0; i < kCPT; ++i) {
+    const int q = kCPT * tid + i;
+    if (q < r.nch) {
+      s_toff[q] = toff;
+      s_tw[q] = 0;
+    }
+    toff += nt[i];
+  }
+  if (tid == 0) s_toff[r.nch] = mtot;
+  __syncthreads();
+
+  // 3. Radix select of the want1-th largest composite among the m bucket-b1
+  //    keys; their top 12 bits all equal b1 and 11-bit digits cover bits
+  //    51..0.  Bucket keys win iff their composite >= T.
   unsigned long long T = 0ull;
-  if (m > 0) {
-    unsigned long long prefix = (unsigned long long)b1;  // bits above the digit
+  if (split) {
+    const bool in_lds = mtot <= kCandLds;
+    // i-th bucket key of the row, in chunk order
+    auto cand_at = [&](int i) -> unsigned long long {
+      int lo = 0, hi = r.nch - 1;
+      while (lo < hi) {  // last chunk q with s_toff[q] <= i
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_toff[mid] <= i) lo = mid;
+        else hi = mid - 1;
+      }
+      return srow[lo * kCH + s_above[lo] + (i - s_toff[lo])];
+    };
+    if (in_lds) {
+      for (int i = tid; i < mtot; i += kT) s_cand[i] = cand_at(i);
+      __syncthreads();
+    }
+    auto cand = [&](int i) { return in_lds ? s_cand[i] : cand_at(i); };
+    unsigned long long prefix = (unsigned long long)b1;
     int top = 51, want = want1;
     for (;;) {
       const int lo_bit = max(top - kD2 + 1, 0);
       const int width = top - lo_bit + 1;
       const unsigned long long dmask = (1ull << width) - 1ull;
-      for (int i = tid; i < (1 << width); i += kRT) hist[i] = 0u;
+      for (int i = tid; i < (1 << width); i += kT) h2[i] = 0u;
       if (tid == 0) {
         s_res[0] = 0;
         s_res[1] = 1;
         s_res[2] = 0;
       }
       __syncthreads();
-      for (int i = tid; i < m; i += kRT) {
-        const unsigned long long c = cl[i];
-        if ((c >> (top + 1)) == prefix) atomicAdd(&hist[(c >> lo_bit) & dmask], 1u);
+      for (int i = tid; i < mtot; i += kT) {
+        const unsigned long long c = cand(i);
+        if ((c >> (top + 1)) == prefix) atomicAdd(&h2[(c >> lo_bit) & dmask], 1u);
       }
       __syncthreads();
-      find_bin_row(hist, 1 << width, want, s_wave, s_res);
+      find_bin_desc(h2, 1 << width, want, s_wave, s_res);
       const int bin = s_res[0];
       want = s_res[1];
       const int c = s_res[2];
@@ -468,82 +534,62 @@ __global__ __launch_bounds__(kRT) void threshold_kernel(SelectLaunch a) {
       }
       top = lo_bit - 1;
     }
+    // bucket winners per chunk (the chunk is the key index / chunk size)
+    for (int i = tid; i < mtot; i += kT) {
+      const unsigned long long c = cand(i);
+      if (c >= T) atomicAdd(&s_tw[min(composite_index(c) / kCH, r.nch - 1)], 1);
+    }
+    __syncthreads();
   }
 
-  // Winners per chunk: keys above the tie bin plus candidates >= T.
-  for (int q = tid; q < Pn; q += kRT) cnt[q] = a.ws.gt1[r.row * a.ws.P + q];
-  __syncthreads();
-  for (int i = tid; i < m; i += kRT) {
-    const unsigned long long c = cl[i];
-    if (c >= T) {
-      const int j = (int)(0xFFFFFFFFu - (uint32_t)(c & 0xFFFFFFFFull));
-      atomicAdd(&cnt[j / kCH], 1);
+  // 4. Output offset of this chunk (winners of the chunks before it) and
+  //    the row's winner count.
+  int wb = 0, wt = 0;
+#pragma unroll
+  for (int i = 0; i < kCPT; ++i) {
+    const int q = kCPT * tid + i;
+    if (q < r.nch) {
+      const int w = s_above[q] + s_tw[q];
+      wt += w;
+      wb += (q < p) ? w : 0;
     }
   }
-  __syncthreads();
-  // Output offset of every chunk (thread t scans chunks [t*CPT, t*CPT+CPT)).
-  constexpr int CPT = kSelMaxChunks / kRT;
-  int loc[CPT];
-  int sum = 0;
-#pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    const int q = tid * CPT + i;
-    loc[i] = (q < Pn) ? cnt[q] : 0;
-    sum += loc[i];
-  }
-  int total;
-  int off = block_exscan<kRW>(sum, s_wave, &total);
-#pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    const int q = tid * CPT + i;
-    if (q < Pn) a.ws.offs[r.row * a.ws.P + q] = off;
-    off += loc[i];
-  }
-  if (tid == 0) {
-    a.ws.meta[r.row].T = T;
-    a.sel_count[r.row] = min(total, K);
-  }
-  int32_t *out = a.sel_idx + r.row * K;
-  for (int i = total + tid; i < K; i += kRT) out[i] = -1;
-}
+  int before, total_w;
+  block_exscan<kTW>(wb, s_wave, &before);
+  block_exscan<kTW>(wt, s_wave, &total_w);
+  const int count = min(total_w, K);
 
-// --------------------------------------------------------- 6. compaction
-__global__ __launch_bounds__(kT) void compact_kernel(SelectLaunch a) {
-  __shared__ int s_wave[kTW];
-  RowGeo r;
-  if (!row_geo(a, r)) return;
-  const int p = blockIdx.x, j0 = p * kCH;
-  if (j0 >= r.span) return;
-  const int tid = threadIdx.x;
-  const int K = a.k;
-  const uint32_t b1 = (uint32_t)a.ws.meta[r.row].b1;
-  const unsigned long long T = a.ws.meta[r.row].T;
-  const int base = a.ws.offs[r.row * a.ws.P + p];
-  uint32_t key[kPT];
-  load_keys(a.ws.keys + r.row * a.ws.ldk, j0, key);
-  bool win[kPT];
-  int c0 = 0, c1 = 0;
+  // 5. This chunk's winners, ascending, through a 2048-bit bitmap.
+  if (p < r.nch) {
+    if (tid < kCH / 32) s_bits[tid] = 0u;
+    __syncthreads();
+    const int na_p = s_above[p];
+    const int ne_p = split ? s_toff[p + 1] - s_toff[p] : 0;
 #pragma unroll
-  for (int i = 0; i < kPT; ++i) {
-    const uint32_t d = key[i] >> (32 - kD1);
-    win[i] = key[i] != 0u &&
-             (d > b1 || (b1 != 0u && d == b1 && composite(key[i], key_pos(j0, i)) >= T));
-    if (i < 4) c0 += win[i] ? 1 : 0;
-    else c1 += win[i] ? 1 : 0;
-  }
-  // ascending order: the first half chunk (four keys per thread, in thread
-  // order), then the second
-  int t0, t1;
-  int o0 = block_exscan<kTW>(c0, s_wave, &t0);
-  int o1 = t0 + block_exscan<kTW>(c1, s_wave, &t1);
-  int32_t *out = a.sel_idx + r.row * K + base;
-#pragma unroll
-  for (int i = 0; i < kPT; ++i) {
-    if (win[i]) {
-      int &o = (i < 4) ? o0 : o1;
-      if (base + o < K) out[o] = key_pos(j0, i);
-      ++o;
+    for (int i = 0; i < kPT; ++i) {
+      const int slot = tid + kT * i;
+      const bool w = slot < na_p || (slot < na_p + ne_p && own[i] >= T);
+      if (w) {
+        const int jl = composite_index(own[i]) - p * kCH;
+        if (jl >= 0 && jl < kCH) atomicOr(&s_bits[jl >> 5], 1u << (jl & 31));
+      }
     }
+    __syncthreads();
+    // thread t owns bits 8 t .. 8 t + 7
+    const uint32_t byte = (s_bits[tid >> 2] >> (8 * (tid & 3))) & 0xFFu;
+    int tot8;
+    int o = before + block_exscan<kTW>(__popc(byte), s_wave, &tot8);
+    for (int e = 0; e < 8; ++e) {
+      if (byte & (1u << e)) {
+        if (o < K) out[o] = p * kCH + 8 * tid + e;
+        ++o;
+      }
+    }
+  }
+  // 6. The last chunk's workgroup pads the list and writes its length.
+  if (p == max(r.nch, 1) - 1) {
+    if (tid == 0) a.sel_count[r.row] = count;
+    for (int i = count + tid; i < K; i += kT) out[i] = -1;
   }
 }
 
@@ -551,7 +597,6 @@ __global__ __launch_bounds__(kT) void compact_kernel(SelectLaunch a) {
 
 hipError_t launch_select(const SelectLaunch &a, hipStream_t st) {
   const dim3 grid(a.ws.P, a.H, a.batch_n);
-  const dim3 rgrid(1, a.H, a.batch_n);
   const bool fused = a.mode == 0;
   hipError_t e;
   if (fused) {
@@ -566,11 +611,7 @@ hipError_t launch_select(const SelectLaunch &a, hipStream_t st) {
     hipLaunchKernelGGL(keys_kernel<false>, grid, dim3(kT), 0, st, a);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(tie_kernel, grid, dim3(kT), 0, st, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(threshold_kernel, rgrid, dim3(kRT), 0, st, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(compact_kernel, grid, dim3(kT), 0, st, a);
+  hipLaunchKernelGGL(pick_kernel, grid, dim3(kT), 0, st, a);
   return hipGetLastError();
 }
 

@@ -93,23 +93,20 @@ FastWs fast_ws(const sfi_kv *kv, int sel_k, int n_sink, int window) {
 }
 
 struct SelWs {
-  int P, ldk;
-  size_t keys, cand, hist, nsum, wsum, gt1, offs, meta, total;
+  int P;
+  size_t ghist, cum, sorted, nsum, wsum, meta, total;
 };
 
 SelWs select_ws(int B, int H, int max_seq_len) {
   SelWs w{};
   const size_t rows = (size_t)B * H;
   w.P = (max_seq_len + kSelChunk - 1) / kSelChunk;
-  w.ldk = w.P * kSelChunk;
-  w.keys = 0;
-  w.cand = align_up(w.keys + rows * w.ldk * sizeof(uint32_t));
-  w.hist = align_up(w.cand + rows * w.ldk * sizeof(unsigned long long));
-  w.nsum = align_up(w.hist + rows * 4096 * sizeof(uint32_t));
+  w.ghist = 0;
+  w.cum = align_up(w.ghist + rows * 4096 * sizeof(uint32_t));
+  w.sorted = align_up(w.cum + rows * w.P * 4096 * sizeof(uint16_t));
+  w.nsum = align_up(w.sorted + rows * w.P * kSelChunk * sizeof(unsigned long long));
   w.wsum = align_up(w.nsum + rows * w.P * 2 * sizeof(double));
-  w.gt1 = align_up(w.wsum + rows * w.P * sizeof(double));
-  w.offs = align_up(w.gt1 + rows * w.P * sizeof(int));
-  w.meta = align_up(w.offs + rows * w.P * sizeof(int));
+  w.meta = align_up(w.wsum + rows * w.P * sizeof(double));
   w.total = align_up(w.meta + rows * sizeof(SelRowMeta));
   return w;
 }
@@ -207,7 +204,7 @@ size_t sfi_slow_workspace_bytes(const sfi_kv *kv) {
 }
 
 size_t sfi_select_workspace_bytes(int32_t B, int32_t H, int32_t max_seq_len) {
-  if (B < 1 || H < 1 || max_seq_len < 1 || max_seq_len > kSelMaxChunks * kSelChunk) return 0;
+  if (B < 1 || H < 1 || max_seq_len < 1 || max_seq_len > kSelMaxLen) return 0;
   return select_ws(B, H, max_seq_len).total;
 }
 
@@ -290,7 +287,7 @@ sfi_status sfi_select(const sfi_select_params *p, const int32_t *batch_ids, int3
   if (!p || !seq_len || !score || !sel_idx || !sel_count) return SFI_ERR_NULL;
   if (p->mode != SFI_SCORE_FUSED && p->mode != SFI_SCORE_RAW) return SFI_ERR_RANGE;
   if (B < 1 || H < 1 || max_seq_len < 1) return SFI_ERR_SHAPE;
-  if (max_seq_len > kSelMaxChunks * kSelChunk) return SFI_ERR_UNSUPPORTED;
+  if (max_seq_len > kSelMaxLen) return SFI_ERR_UNSUPPORTED;
   if (batch_n < 0 || batch_n > B) return SFI_ERR_RANGE;
   if (ld < max_seq_len) return SFI_ERR_RANGE;
   if (p->k < 1 || p->n_sink < 0 || p->window < 0) return SFI_ERR_RANGE;
@@ -316,14 +313,11 @@ sfi_status sfi_select(const sfi_select_params *p, const int32_t *batch_ids, int3
   a.fused_out = fused ? fused_out : nullptr;
   a.fo_ld = ld;
   a.ws.P = w.P;
-  a.ws.ldk = w.ldk;
-  a.ws.keys = carve<uint32_t>(ws, w.keys);
-  a.ws.cand = carve<unsigned long long>(ws, w.cand);
-  a.ws.hist = carve<uint32_t>(ws, w.hist);
+  a.ws.ghist = carve<uint32_t>(ws, w.ghist);
+  a.ws.cum = carve<uint16_t>(ws, w.cum);
+  a.ws.sorted = carve<unsigned long long>(ws, w.sorted);
   a.ws.nsum = carve<double>(ws, w.nsum);
   a.ws.wsum = carve<double>(ws, w.wsum);
-  a.ws.gt1 = carve<int>(ws, w.gt1);
-  a.ws.offs = carve<int>(ws, w.offs);
   a.ws.meta = carve<SelRowMeta>(ws, w.meta);
   return launch_select(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SFI_OK : SFI_ERR_HIP;
 }

@@ -84,4 +84,12 @@ __device__ __forceinline__ uint4 ldg16(const uint16_t *p) {
   return *reinterpret_cast<const uint4 *>(p);
 }
 
+// 16-byte load marked non-temporal: for rows streamed once per call (dense
+// and slow steps), so they do not displace reused data in the caches.
+__device__ __forceinline__ uint4 ldg16_stream(const uint16_t *p) {
+  typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
+  const u32x4_nt t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt *>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
 }  // namespace sfi

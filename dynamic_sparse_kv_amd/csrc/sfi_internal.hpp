@@ -72,29 +72,22 @@ hipError_t launch_fast(const AttnLaunch &a, hipStream_t st);
 hipError_t launch_step(const AttnLaunch &sa, const AttnLaunch &fa, hipStream_t st);
 
 constexpr int kSelChunk = 2048;       // keys per selector chunk workgroup
-constexpr int kSelMaxChunks = 4096;   // chunks per row: rows up to 8,388,608 keys
+constexpr int kSelMaxChunks = 1024;   // chunks per row
+constexpr int kSelMaxLen = kSelChunk * kSelMaxChunks;  // longest row: 2,097,152 keys
 
-// Per-row state shared by the selector's kernels.
+// Per-row prior constants shared by the selector's kernels.
 struct SelRowMeta {
-  int b1;                  // first-digit bin of the k-th largest key (0: take all)
-  int want1;               // keys to take from that bin
-  int m;                   // tie-bin candidates appended
-  int pad;
-  float muf, cz;           // prior: mean key norm, -norm_coef log2(e) / std
-  unsigned long long T;    // tie-bin winners: composite >= T
+  float muf, cz;           // mean key norm, -norm_coef log2(e) / std
 };
 
 // Selector workspace, carved from the caller's buffer.
 struct SelWork {
   int P;                      // chunks per row
-  int ldk;                    // P * kSelChunk
-  uint32_t *keys;             // [rows][ldk] order-preserving keys
-  unsigned long long *cand;   // [rows][ldk] tie-bin candidates
-  uint32_t *hist;             // [rows][4096] first-digit histogram
+  uint32_t *ghist;            // [rows][4096] bucket histogram of the row
+  uint16_t *cum;              // [rows][P][4096] per chunk: keys in buckets >= b
+  unsigned long long *sorted; // [rows][P][kSelChunk] bucket-sorted composites
   double *nsum;               // [rows][P][2] key-norm sums per chunk
   double *wsum;               // [rows][P] prior-weight sums per chunk
-  int *gt1;                   // [rows][P] keys above the tie bin per chunk
-  int *offs;                  // [rows][P] output offset per chunk
   SelRowMeta *meta;           // [rows]
 };
 

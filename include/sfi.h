@@ -140,7 +140,8 @@ sfi_status sfi_slow_step(const sfi_kv *kv, const int32_t *batch_ids, int32_t bat
  *          lambda, norm_coef, pos_tau and fused_out are ignored).  Scores
  *          must be defined on all of C.
  * H is Hkv for per-head memories (SFI) or 1 for one head-shared list (Vegas).
- * NaN scores give an unspecified (but in-range) selection. */
+ * max_seq_len <= 2,097,152 (else SFI_ERR_UNSUPPORTED).  NaN scores give an
+ * unspecified (but in-range) selection. */
 sfi_status sfi_select(const sfi_select_params *p, const int32_t *batch_ids, int32_t batch_n,
                       const int32_t *seq_len, int32_t B, int32_t H, int32_t max_seq_len,
                       const float *score, const float *key_norm, int32_t ld,
