@@ -31,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix peak of one MI355X
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_llama3_8b_layer_32k.json")
 METRIC = "decode attn tokens/s (slow+fast mix) at 32K/128K ctx; % HBM roofline/kernel"
 
@@ -130,6 +131,219 @@ def cpu_baseline(cfg, K, V, q_host, slow, ctx, budget_s=20.0):
     }
 
 
+def _graph_time(fn, side, stream):
+    """Capture fn(side) into one HIP graph, replay once untimed, then time one
+    replay (seconds)."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            fn(side)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g.replay()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0, g
+
+
+class _CallTimer:
+    """HIP events around single calls on the launch stream, each call after
+    a 1 GiB read that evicts L2 and the Infinity Cache."""
+
+    def __init__(self, dev, stream):
+        import torch
+        self.torch = torch
+        self.flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        self.stream = stream
+        self.ev = []
+
+    def __call__(self, kind, fn, nbytes, flops=0.0):
+        t = self.torch
+        self.flush.sum()
+        e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        fn()
+        e1.record(self.stream)
+        self.ev.append((kind, e0, e1, nbytes, flops))
+
+    def summary(self):
+        self.torch.cuda.synchronize()
+        agg = {}
+        for kind, a, b, nbytes, flops in self.ev:
+            d = agg.setdefault(kind, [[], [], []])
+            d[0].append(a.elapsed_time(b) * 1e-3)
+            d[1].append(nbytes)
+            d[2].append(flops)
+        out = {}
+        for kind, (ts, bs, fs) in agg.items():
+            t = float(np.mean(ts))
+            by = float(np.mean(bs))
+            rec = {"launches": len(ts), "avg_us": round(t * 1e6, 2),
+                   "alg_bytes_per_launch": int(by), "alg_GBps": round(by / t / 1e9, 1),
+                   "frac_of_hbm_peak": round(by / t / 1e9 / HBM_PEAK_GBS, 4)}
+            if any(fs):
+                fl = float(np.mean(fs))
+                rec["TFLOPs"] = round(fl / t / 1e12, 2)
+                rec["mfma_util_bf16"] = round(fl / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+            out[kind] = rec
+        del self.flush
+        return out
+
+
+def leg_stack128k(timed_steps=24, dense_steps=4):
+    """32 attention layers of the Llama-3-8B shape at 128K context, B=4,
+    4+256+4096, lambda 0.2, sentence schedule shared by the layers; one token
+    passes all 32 layers (independent seeded KV and queries per layer)."""
+    import torch
+    from dynamic_sparse_kv_amd import sfi
+    from dynamic_sparse_kv_amd import workload as W
+    from dynamic_sparse_kv_amd.runner import DecodePlan, SFIDecoder
+    dev = "cuda"
+    steps = timed_steps + 1
+    cfg = W.CONFIGS["c3"].replace(steps=steps)
+    ctx = W.context_lengths(cfg)
+    starts = W.sentence_starts(cfg)
+    slow = sfi.sfi_schedule(starts, cfg.budget).astype(bool)
+    plan = DecodePlan(slow, ctx, dev)
+    max_len = int(ctx.max()) + steps
+    decs, qs = [], []
+    _log(f"[bench] stack32-128k: generating {cfg.layers} layers")
+    for layer in range(cfg.layers):
+        K, V = W.make_kv(cfg, layer=layer, device=dev, cap=max_len)
+        qs.append(W.make_queries(cfg, starts, layer=layer).to(dev))
+        decs.append(SFIDecoder(K, V, cfg.Hq, max_len, n_sink=cfg.n_sink, window=cfg.window,
+                               k=cfg.k, lam=cfg.lam, norm_coef=cfg.norm_coef, pos_tau=cfg.pos_tau))
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    for layer in range(cfg.layers):      # step 0: every sequence slow (first selection)
+        decs[layer].step(plan, 0, qs[layer], stream)
+    torch.cuda.synchronize()
+
+    def run(st):
+        for s in range(1, steps):
+            for layer in range(cfg.layers):
+                decs[layer].step(plan, s, qs[layer], st)
+
+    _log("[bench] stack32-128k: timing graph replay")
+    t_total, g = _graph_time(run, side, stream)
+    del g
+    value = cfg.B * timed_steps / t_total
+
+    timer = _CallTimer(dev, stream)
+    for s in range(1, steps):
+        ns, nf = int(plan.n_slow[s]), int(plan.n_fast[s])
+        lens = plan.seq_len_host[s]
+        sb = sum(algorithmic_bytes("slow", int(lens[b]), cfg) for b in np.nonzero(plan.slow[s])[0])
+        fb = sum(algorithmic_bytes("fast", int(lens[b]), cfg) for b in np.nonzero(~plan.slow[s])[0])
+        selb = sum(algorithmic_bytes("select", int(lens[b]), cfg) for b in np.nonzero(plan.slow[s])[0])
+        for layer in (0, cfg.layers // 2):
+            d, q = decs[layer], qs[layer][s]
+            if ns and nf:
+                timer("step", lambda: d.co_step(q, plan.seq_len[s], plan.slow_ids[s], ns, plan.fast_ids[s],
+                                                nf, stream, select=False), sb + fb)
+            elif ns:
+                timer("slow", lambda: d.slow(q, plan.seq_len[s], plan.slow_ids[s], ns, stream,
+                                             select=False), sb)
+            elif nf:
+                timer("fast", lambda: d.fast(q, plan.seq_len[s], plan.fast_ids[s], nf, stream), fb)
+            if ns:
+                timer("select", lambda: d.slow_select_only(plan.seq_len[s], plan.slow_ids[s], ns, stream),
+                      selb)
+    all_ids = torch.arange(cfg.B, dtype=torch.int32, device=dev)
+    for s in range(1, 1 + dense_steps):
+        lens = plan.seq_len_host[s]
+        db = sum(algorithmic_bytes("dense", int(lens[b]), cfg) for b in range(cfg.B))
+        timer("dense", lambda: decs[0].dense(qs[0][s], plan.seq_len[s], all_ids, cfg.B, stream), db)
+    per_call = timer.summary()
+
+    def run_dense(st):
+        for s in range(1, 1 + dense_steps):
+            for layer in range(cfg.layers):
+                decs[layer].dense(qs[layer][s], plan.seq_len[s], all_ids, cfg.B, st)
+
+    _log("[bench] stack32-128k: dense comparator")
+    t_dense, g = _graph_time(run_dense, side, stream)
+    del g
+    dense_tps = cfg.B * dense_steps / t_dense
+    res = {"workload": f"{cfg.name}: {cfg.layers} layers, B={cfg.B} Hq={cfg.Hq} Hkv={cfg.Hkv} d={cfg.d}, "
+                       f"ctx {cfg.ctx}, fast state {cfg.n_sink}+{cfg.window}+{cfg.k}, lambda {cfg.lam}, "
+                       f"{timed_steps} decode steps after a first all-slow step",
+           "tokens_per_s": round(value, 1), "ms_per_step": round(t_total / timed_steps * 1e3, 4),
+           "slow_fraction": round(float(plan.slow[1:].mean()), 4),
+           "timing": "hip graph replay, one stream; per_call: eager, cold, layers 0 and 16",
+           "per_call": per_call, "dense_tokens_per_s": round(dense_tps, 2),
+           "speedup_vs_dense": round(value / dense_tps, 2)}
+    del decs, qs
+    torch.cuda.empty_cache()
+    return res
+
+
+def leg_vegas64k(iters=12):
+    """Verification-guided selection at 64K context, B=16, T=8 verify rows:
+    per iteration verify (all T rows, logits aggregated in-kernel), top-2048
+    of the aggregate per sequence, 7 sparse draft steps; ALL rows and
+    Collect-2-Query (first and last row) aggregates."""
+    import torch
+    from dynamic_sparse_kv_amd import workload as W
+    from dynamic_sparse_kv_amd.runner import VegasDecoder
+    dev = "cuda"
+    cfg = W.CONFIGS["c4"].replace(steps=iters)
+    T = cfg.vegas_T
+    ctx = int(W.context_lengths(cfg).max())
+    _log("[bench] vegas-64k: generating")
+    K, V = W.make_kv(cfg, device=dev)
+    cap = K.shape[2]
+    qpos = W.make_vegas_queries(cfg).to(dev)           # [positions][B][Hq][d]
+    vd = VegasDecoder(K, V, cfg.Hq, cap, T, n_sink=cfg.n_sink, window=cfg.window, k=cfg.k)
+    q_rows = [qpos[it * T: it * T + T].permute(1, 0, 2, 3).contiguous() for it in range(iters)]
+    seq_v = [torch.full((cfg.B,), ctx + T * (it + 1), dtype=torch.int32, device=dev) for it in range(iters)]
+    seq_d = [[torch.full((cfg.B,), ctx + T * (it + 1) + j, dtype=torch.int32, device=dev)
+              for j in range(1, T)] for it in range(iters)]
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    masks = {"all": (1 << T) - 1, "collect2": 1 | (1 << (T - 1))}
+
+    def iteration(it, mask, st):
+        vd.verify(q_rows[it], seq_v[it], mask, stream=st)
+        vd.select(seq_v[it], stream=st)
+        for j in range(1, T):
+            vd.draft(qpos[it * T + T + j - 1], seq_d[it][j - 1], stream=st)
+
+    res = {"workload": f"{cfg.name}: B={cfg.B} Hq={cfg.Hq} Hkv={cfg.Hkv} d={cfg.d}, ctx {ctx}, "
+                       f"T={T} verify rows, top-{cfg.k} of the aggregated logits + {cfg.n_sink} sinks + "
+                       f"{cfg.window} window, {T - 1} drafts per iteration, {iters} iterations",
+           "tokens_per_iteration": f"{T} per sequence (all drafts accepted)"}
+    for name, mask in masks.items():
+        iteration(0, mask, stream)
+        torch.cuda.synchronize()
+        t_total, g = _graph_time(lambda st: [iteration(it, mask, st) for it in range(iters)], side, stream)
+        del g
+        res[f"tokens_per_s_{name}"] = round(cfg.B * T * iters / t_total, 1)
+        res[f"ms_per_iteration_{name}"] = round(t_total / iters * 1e3, 4)
+    timer = _CallTimer(dev, stream)
+    d, Hq, Hkv = cfg.d, cfg.Hq, cfg.Hkv
+    for it in range(min(iters, 4)):
+        n = ctx + T * (it + 1)
+        vbytes = cfg.B * (n * Hkv * 4 * d + (n - T) * 4 + T * Hq * d * 6)
+        vflops = cfg.B * 4.0 * d * T * Hq * n
+        for name, mask in masks.items():
+            timer(f"verify_{name}", lambda: vd.verify(q_rows[it], seq_v[it], mask, stream=stream),
+                  vbytes, vflops)
+        timer("select", lambda: vd.select(seq_v[it], stream=stream), cfg.B * ((n - T) * 4 + cfg.k * 4))
+        for j in (1, T - 1):
+            nd = n + j
+            rows = cfg.n_sink + cfg.window + cfg.k
+            timer("draft", lambda: vd.draft(qpos[it * T + T + j - 1], seq_d[it][j - 1], stream=stream),
+                  cfg.B * (rows * Hkv * 4 * d + cfg.k * 4 + Hq * d * 6))
+    res["per_call"] = timer.summary()
+    del vd, K, V, qpos, q_rows
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -137,6 +351,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="c2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--legs", default="stack32-128k,vegas-64k",
+                    help="extra workloads measured after the headline (comma list, or 'none')")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy (a known-size kernel "
@@ -329,6 +545,14 @@ def main():
     if not args.no_cpu_baseline:
         _log("[bench] cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(cfg, K, V, q_host, slow[:K_steps], ctx)
+    legs = [x for x in args.legs.split(",") if x and x != "none"]
+    if legs:
+        del dec, K, V, q
+        torch.cuda.empty_cache()
+        result["legs"] = {}
+        for leg in legs:
+            fn = {"stack32-128k": leg_stack128k, "vegas-64k": leg_vegas64k}[leg]
+            result["legs"][leg] = fn()
     print(json.dumps(result), flush=True)
 
 
