@@ -110,43 +110,45 @@ __global__ __launch_bounds__(kVThreads) void verify_partial_kernel(VArgs a) {
   float m = kNegBig, z = 0.f;
   const size_t aggrow = ((size_t)b * a.kv.Hkv + g) * a.lld;
 
-  for (int kb = k0; kb < k1; kb += 32) {
-    // A operand of Q K^T: key kb+col, dims 16kk + 8hs .. +8.
+  // One 32-key tile: the K rows as the A operand of S^T = K Q^T, and the
+  // (even, odd)-dim dwords of the V rows this lane needs for O^T's A operand.
+  struct Tile {
     bf16x8_t ka[KK];
-    {
-      const int key = kb + col;
-      if (key < k1) {
-        const uint16_t *kp = a.kv.k + kv_row<D, PAGED>(a.kv, b, g, key) + 8 * hs;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) ka[kk] = as_bf16x8(ldg16(kp + 16 * kk));
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) ka[kk] = as_bf16x8(make_uint4(0, 0, 0, 0));
-      }
-    }
-    // V (even, odd)-dim dword of each key this lane needs for O^T's A operand.
     uint32_t vw[2][NP][8];
+  };
+  // Every lane issues its loads unconditionally: a key past the wave's range
+  // reads row k1 - 1 instead (k1 > k0, so it exists) and is masked in
+  // consume().  Loads behind per-lane branches would leave the number of
+  // loads in flight unknown at compile time and every later wait would have
+  // to drain them all, which would collapse the two-stage pipeline below.
+  auto load_tile = [&](Tile &t, int kb) {
+    {
+      const int key = min(kb + col, k1 - 1);
+      const uint16_t *kp = a.kv.k + kv_row<D, PAGED>(a.kv, b, g, key) + 8 * hs;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) t.ka[kk] = as_bf16x8(ldg16(kp + 16 * kk));
+    }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int key = kb + 16 * ks + acc_key(e, hs);
-        if (key < k1) {
-          const uint16_t *vp = a.kv.v + kv_row<D, PAGED>(a.kv, b, g, key) + 2 * col;
+        const int key = min(kb + 16 * ks + acc_key(e, hs), k1 - 1);
+        const uint16_t *vp = a.kv.v + kv_row<D, PAGED>(a.kv, b, g, key) + 2 * col;
 #pragma unroll
-          for (int p = 0; p < NP; ++p) vw[ks][p][e] = *reinterpret_cast<const uint32_t *>(vp + 64 * p);
-        } else {
-#pragma unroll
-          for (int p = 0; p < NP; ++p) vw[ks][p][e] = 0u;
-        }
+        for (int p = 0; p < NP; ++p) t.vw[ks][p][e] = *reinterpret_cast<const uint32_t *>(vp + 64 * p);
       }
     }
-
+  };
+  // Lazy rescaling: the running reference m only moves when a logit exceeds
+  // it by more than kSlack (log2 units), so p = 2^(l - m) stays <= 2^kSlack
+  // and the accumulators are rescaled on few tiles.
+  constexpr float kSlack = 8.0f;
+  auto consume = [&](const Tile &t, int kb) {
     f32x16_t s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], qb[kk], s, 0, 0, 0);
+    for (int kk = 0; kk < KK; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t.ka[kk], qb[kk], s, 0, 0, 0);
 
     // Aggregate: masked column sum, reduce-scattered over the 32 lanes of the half.
     {
@@ -193,21 +195,24 @@ __global__ __launch_bounds__(kVThreads) void verify_partial_kernel(VArgs a) {
       mx = fmaxf(mx, sv[r]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mn = fmaxf(m, mx);
-    const float sc = exp2f(m - mn);
-    m = mn;
-    z *= sc;
+    const bool need = mx > m + kSlack;
+    if (__any(need)) {
+      const float mn = need ? mx : m;
+      const float sc = exp2f(m - mn);
+      m = mn;
+      z *= sc;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[mt][r] *= sc;
+        for (int r = 0; r < 16; ++r) o[mt][r] *= sc;
+    }
 
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       bf16x8_t phi, plo;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float p = exp2f(sv[8 * ks + e] - mn);
+        const float p = exp2f(sv[8 * ks + e] - m);
         z += p;
         const float ph = __uint_as_float(__float_as_uint(p) & 0xffff0000u);
         phi[e] = (__bf16)ph;
@@ -218,7 +223,7 @@ __global__ __launch_bounds__(kVThreads) void verify_partial_kernel(VArgs a) {
         u32x4_t ev, od;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const uint32_t w0 = vw[ks][pp][2 * i], w1 = vw[ks][pp][2 * i + 1];
+          const uint32_t w0 = t.vw[ks][pp][2 * i], w1 = t.vw[ks][pp][2 * i + 1];
           ev[i] = (w0 & 0xffffu) | (w1 << 16);
           od[i] = (w0 >> 16) | (w1 & 0xffff0000u);
         }
@@ -230,6 +235,17 @@ __global__ __launch_bounds__(kVThreads) void verify_partial_kernel(VArgs a) {
         o[2 * pp + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, plo, o[2 * pp + 1], 0, 0, 0);
       }
     }
+  };
+
+  // Two tiles in flight: the loads of one overlap the MFMA and softmax work
+  // of the other.  Tiles past k1 are fully masked (p = 0, no aggregate write).
+  Tile ta, tb;
+  load_tile(ta, k0);
+  for (int kb = k0; kb < k1; kb += 64) {
+    load_tile(tb, kb + 32);
+    consume(ta, kb);
+    load_tile(ta, kb + 64);
+    consume(tb, kb + 32);
   }
 
   const float zt = z + __shfl_xor(z, 32);
