@@ -40,9 +40,11 @@ def _log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(kind, n, cfg):
-    """Bytes the method must move for one sequence-step (per layer)."""
-    Hkv, Hq, d, k = cfg.Hkv, cfg.Hq, cfg.d, cfg.k
+def algorithmic_bytes(kind, n, cfg, k=None):
+    """Bytes the method must move for one sequence-step (per layer); k
+    overrides the configured list length (per-sequence k)."""
+    Hkv, Hq, d = cfg.Hkv, cfg.Hq, cfg.d
+    k = cfg.k if k is None else k
     if kind == "dense":
         return n * Hkv * 4 * d + Hq * d * 6
     if kind == "slow":
@@ -344,6 +346,97 @@ def leg_vegas64k(iters=12):
     return res
 
 
+def leg_ragged_paged(timed_steps=32, dense_steps=4):
+    """Ragged long-reasoning batch: B=32 sequences, contexts log-uniform in
+    [8K, 128K], paged bf16 KV in 16-token pages (shuffled pool), Hq=40
+    Hkv=8 d=128, 4+256+min(4096, n/16) keys, lambda 0.3, each sequence
+    slow with probability 1/20 per step (step 0 slow).  Slow and fast shares
+    of a step run in one co-launched grid."""
+    import torch
+    from dynamic_sparse_kv_amd import sfi
+    from dynamic_sparse_kv_amd import workload as W
+    from dynamic_sparse_kv_amd.runner import DecodePlan, SFIDecoder
+    dev = "cuda"
+    steps = timed_steps + 1
+    cfg = W.CONFIGS["c5"].replace(steps=steps)
+    ctx = W.context_lengths(cfg)
+    caps = ctx + cfg.growth()
+    table, npages = W.page_table(cfg, caps)
+    _log(f"[bench] ragged-paged: generating {npages} pages")
+    Kp, Vp = W.make_paged_kv(cfg, table, npages, caps, device=dev)
+    tab = torch.from_numpy(table).to(dev)
+    starts = W.sentence_starts(cfg)
+    slow = sfi.sfi_schedule(starts, -1).astype(bool)
+    plan = DecodePlan(slow, ctx, dev, k_cap=cfg.k, k_div=cfg.k_div)
+    q = W.make_queries(cfg, starts).to(dev)
+    max_len = int(ctx.max()) + steps
+    dec = SFIDecoder(Kp, Vp, cfg.Hq, max_len, n_sink=cfg.n_sink, window=cfg.window, k=cfg.k,
+                     lam=cfg.lam, norm_coef=cfg.norm_coef, pos_tau=cfg.pos_tau, page_table=tab,
+                     page_size=cfg.page_size)
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    dec.step(plan, 0, q, stream)
+    torch.cuda.synchronize()
+
+    def run(st):
+        for s in range(1, steps):
+            dec.step(plan, s, q, st)
+
+    _log("[bench] ragged-paged: timing graph replay")
+    t_total, g = _graph_time(run, side, stream)
+    del g
+    value = cfg.B * timed_steps / t_total
+    kseq = np.minimum(cfg.k, plan.seq_len_host // cfg.k_div)
+    timer = _CallTimer(dev, stream)
+    for s in range(1, steps):
+        ns, nf = int(plan.n_slow[s]), int(plan.n_fast[s])
+        lens = plan.seq_len_host[s]
+        sl_b, fa_b = np.nonzero(plan.slow[s])[0], np.nonzero(~plan.slow[s])[0]
+        sb = sum(algorithmic_bytes("slow", int(lens[b]), cfg) for b in sl_b)
+        fb = sum(algorithmic_bytes("fast", int(lens[b]), cfg, k=int(kseq[s, b])) for b in fa_b)
+        selb = sum(algorithmic_bytes("select", int(lens[b]), cfg, k=int(kseq[s, b])) for b in sl_b)
+        ks = plan.k_seq[s]
+        if ns and nf:
+            timer("step", lambda: dec.co_step(q[s], plan.seq_len[s], plan.slow_ids[s], ns, plan.fast_ids[s],
+                                              nf, stream, select=False), sb + fb)
+        elif ns:
+            timer("slow", lambda: dec.slow(q[s], plan.seq_len[s], plan.slow_ids[s], ns, stream,
+                                           select=False), sb)
+        elif nf:
+            timer("fast", lambda: dec.fast(q[s], plan.seq_len[s], plan.fast_ids[s], nf, stream), fb)
+        if ns:
+            timer("select", lambda: dec.slow_select_only(plan.seq_len[s], plan.slow_ids[s], ns, stream,
+                                                         k_seq=ks), selb)
+    all_ids = torch.arange(cfg.B, dtype=torch.int32, device=dev)
+    for s in range(1, 1 + dense_steps):
+        lens = plan.seq_len_host[s]
+        db = sum(algorithmic_bytes("dense", int(lens[b]), cfg) for b in range(cfg.B))
+        timer("dense", lambda: dec.dense(q[s], plan.seq_len[s], all_ids, cfg.B, stream), db)
+    per_call = timer.summary()
+
+    def run_dense(st):
+        for s in range(1, 1 + dense_steps):
+            dec.dense(q[s], plan.seq_len[s], all_ids, cfg.B, st)
+
+    t_dense, g = _graph_time(run_dense, side, stream)
+    del g
+    dense_tps = cfg.B * dense_steps / t_dense
+    res = {"workload": f"{cfg.name}: B={cfg.B} Hq={cfg.Hq} Hkv={cfg.Hkv} d={cfg.d}, ctx log-uniform in "
+                       f"[{cfg.ragged_min}, {cfg.ctx}] (mean {int(ctx.mean())}), paged {cfg.page_size}-token "
+                       f"pages ({npages} in a shuffled pool), fast state {cfg.n_sink}+{cfg.window}+"
+                       f"min({cfg.k}, n/{cfg.k_div}), lambda {cfg.lam}, slow probability {cfg.slow_prob:.3f}, "
+                       f"{timed_steps} steps after a first all-slow step",
+           "tokens_per_s": round(value, 1), "ms_per_step": round(t_total / timed_steps * 1e3, 4),
+           "slow_fraction": round(float(plan.slow[1:].mean()), 4),
+           "timing": "hip graph replay, one stream (slow and fast shares co-launched in one grid); "
+                     "per_call: eager, cold",
+           "per_call": per_call, "dense_tokens_per_s": round(dense_tps, 1),
+           "speedup_vs_dense": round(value / dense_tps, 2)}
+    del dec, Kp, Vp, q
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -351,7 +444,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="c2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--legs", default="stack32-128k,vegas-64k",
+    ap.add_argument("--legs", default="stack32-128k,vegas-64k,ragged-paged",
                     help="extra workloads measured after the headline (comma list, or 'none')")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
@@ -551,7 +644,8 @@ def main():
         torch.cuda.empty_cache()
         result["legs"] = {}
         for leg in legs:
-            fn = {"stack32-128k": leg_stack128k, "vegas-64k": leg_vegas64k}[leg]
+            fn = {"stack32-128k": leg_stack128k, "vegas-64k": leg_vegas64k,
+                  "ragged-paged": leg_ragged_paged}[leg]
             result["legs"][leg] = fn()
     print(json.dumps(result), flush=True)
 

@@ -723,17 +723,43 @@ hipError_t step_t(const AttnLaunch &sa_in, const AttnLaunch &fa_in, hipStream_t 
     const int slots = resident_slots<copartial_kernel<D, G, false>>();
     const long long Ls = sa.max_len, Lf = fast_rows(fa);
     const long long ps = (long long)sa.batch_n * sa.Hkv, pf = (long long)fa.batch_n * fa.Hkv;
-    // smallest multiple of the granule whose rounded-up splits still fit the
-    // resident slots in one wave (a second wave would double the runtime)
-    long long R = (Ls * ps + Lf * pf + slots - 1) / slots;
-    R = (R + kSplitGranule - 1) / kSplitGranule * kSplitGranule;
-    for (;;) {
-      sa.plan = plan_rows(Ls, sa.plan.stride, R, 1 << 30);
-      fa.plan = plan_rows(Lf, fa.plan.stride, R, kMaxFastChunk);
-      const long long wgs = ps * sa.plan.splits + pf * fa.plan.splits;
-      if (wgs <= slots || (sa.plan.splits == 1 && fa.plan.splits == 1)) break;
-      R += kSplitGranule;
+    const int s_stride = sa.plan.stride, f_stride = fa.plan.stride;
+    // workgroups of the combined grid at R rows per workgroup (non-increasing in R)
+    auto plan_at = [&](long long R) {
+      sa.plan = plan_rows(Ls, s_stride, R, 1 << 30);
+      fa.plan = plan_rows(Lf, f_stride, R, kMaxFastChunk);
+      return ps * sa.plan.splits + pf * fa.plan.splits;
+    };
+    auto rows_per_wg = [&]() {
+      return std::max(std::min<long long>(sa.plan.chunk, Ls), std::min<long long>(fa.plan.chunk, Lf));
+    };
+    // For k waves of resident workgroups take the smallest R (a multiple of
+    // the granule) whose grid fits k waves, and keep the k whose makespan
+    // estimate, k x the largest rows per workgroup, is least.  One wave is
+    // best when it fits without starving one share (a second wave doubles
+    // the runtime); the fast share's chunk is capped (its row ids are staged
+    // in LDS), so a large fast share can need several waves, and a one-wave
+    // plan could then leave each slow workgroup a whole sequence.
+    const long long Rmax = (std::max(Ls, Lf) + kSplitGranule - 1) / kSplitGranule;  // in granules
+    long long best_cost = -1, best_R = Rmax;
+    for (int k = 1; k <= 16; ++k) {
+      const long long cap = (long long)k * slots;
+      if (plan_at(Rmax * kSplitGranule) > cap) continue;
+      long long lo = 1, hi = Rmax;  // hi fits
+      while (lo < hi) {
+        const long long mid = (lo + hi) / 2;
+        if (plan_at(mid * kSplitGranule) <= cap) hi = mid;
+        else lo = mid + 1;
+      }
+      plan_at(hi * kSplitGranule);
+      const long long cost = k * rows_per_wg();
+      if (best_cost < 0 || cost < best_cost) {
+        best_cost = cost;
+        best_R = hi;
+      }
     }
+    // no plan within 16 waves: equal rows per workgroup at the fast cap
+    plan_at(best_cost < 0 ? kMaxFastChunk : best_R * kSplitGranule);
   }
   const int ns = sa.plan.splits * sa.Hkv * sa.batch_n;
   const int nf = fa.plan.splits * fa.Hkv * fa.batch_n;

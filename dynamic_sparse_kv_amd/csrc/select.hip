@@ -397,8 +397,9 @@ __global__ __launch_bounds__(kT) void pick_kernel(SelectLaunch a) {
   if (!row_geo(a, r)) return;
   const int p = blockIdx.x, tid = threadIdx.x;
   if (p >= max(r.nch, 1)) return;
-  const int K = a.k;
-  int32_t *out = a.sel_idx + r.row * K;
+  const int Kcap = a.k;  // row stride of the index lists
+  const int K = a.k_seq ? min(max(a.k_seq[r.b], 0), Kcap) : Kcap;
+  int32_t *out = a.sel_idx + r.row * Kcap;
   const unsigned long long *srow = a.ws.sorted + r.row * a.ws.P * kCH;
 
   // this chunk's bucket-sorted composites (slots past its candidates unused)
@@ -589,7 +590,7 @@ __global__ __launch_bounds__(kT) void pick_kernel(SelectLaunch a) {
   // 6. The last chunk's workgroup pads the list and writes its length.
   if (p == max(r.nch, 1) - 1) {
     if (tid == 0) a.sel_count[r.row] = count;
-    for (int i = count + tid; i < K; i += kT) out[i] = -1;
+    for (int i = count + tid; i < Kcap; i += kT) out[i] = -1;
   }
 }
 

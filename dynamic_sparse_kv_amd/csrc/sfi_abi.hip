@@ -306,6 +306,7 @@ sfi_status sfi_select(const sfi_select_params *p, const int32_t *batch_ids, int3
   a.mode = p->mode;
   a.lambda = p->lambda; a.norm_coef = p->norm_coef; a.pos_tau = p->pos_tau;
   a.n_sink = p->n_sink; a.window = p->window; a.k = p->k;
+  a.k_seq = p->k_per_seq;
   a.batch_ids = batch_ids; a.batch_n = batch_n; a.seq_len = seq_len;
   a.B = B; a.H = H; a.max_seq_len = max_seq_len;
   a.score = score; a.key_norm = key_norm; a.ld = ld;

@@ -95,6 +95,7 @@ struct SelectLaunch {
   int mode;
   float lambda, norm_coef, pos_tau;
   int n_sink, window, k;
+  const int32_t *k_seq;  // [B] per-sequence list length (clamped to k) or null
   const int32_t *batch_ids;
   int batch_n;
   const int32_t *seq_len;

@@ -24,16 +24,21 @@ class DecodePlan:
     """Per-step device arguments of one run.
 
     slow[s, b] (host bool) says whether sequence b takes a slow step at step
-    s.  seq_len[s, b] = ctx_b + s + 1 keys are visible at step s.
+    s.  seq_len[s, b] = ctx_b + s + 1 keys are visible at step s.  With
+    k_div > 0 a slow step of sequence b keeps min(k_cap, seq_len // k_div)
+    keys (k_seq[s, b]); otherwise every list holds up to the decoder's k.
     """
 
-    def __init__(self, slow: np.ndarray, ctx: np.ndarray, device):
+    def __init__(self, slow: np.ndarray, ctx: np.ndarray, device, k_cap: int = 0, k_div: int = 0):
         steps, B = slow.shape
         self.steps, self.B = steps, B
         self.slow = slow.astype(bool)
         lens = ctx[None, :].astype(np.int64) + np.arange(steps)[:, None] + 1
         self.seq_len_host = lens.astype(np.int32)
         self.seq_len = _dev_i32(lens, device)               # [steps][B]
+        self.k_seq = None
+        if k_div > 0:
+            self.k_seq = _dev_i32(np.minimum(k_cap, lens // k_div), device)
         slow_ids = np.zeros((steps, B), dtype=np.int32)
         fast_ids = np.zeros((steps, B), dtype=np.int32)
         self.n_slow = np.zeros(steps, dtype=np.int64)
@@ -114,21 +119,27 @@ class SFIDecoder:
         self.ws_step = torch.empty(self.ws_step_bytes, **u8)
 
     # -- single calls -------------------------------------------------------
-    def slow(self, q, seq_len, batch_ids, batch_n: int, stream=None, select: bool = True, out=None):
+    def slow(self, q, seq_len, batch_ids, batch_n: int, stream=None, select: bool = True, out=None,
+             k_seq=None):
         """Dense step + evidence for the listed sequences, then the selector."""
         self.kv.seq_len = seq_len.data_ptr() if torch.is_tensor(seq_len) else seq_len
         sfi.sfi_slow_step(self.kv, batch_ids, batch_n, q, self.out if out is None else out,
                           self.evidence, self.key_norm, self.ld, self.ws_slow, self.ws_slow_bytes,
                           stream)
         if select:
-            self.slow_select_only(self.kv.seq_len, batch_ids, batch_n, stream)
+            self.slow_select_only(self.kv.seq_len, batch_ids, batch_n, stream, k_seq=k_seq)
 
-    def slow_select_only(self, seq_len, batch_ids, batch_n: int, stream=None):
-        """The selector over the evidence and norms of the last slow step."""
+    def slow_select_only(self, seq_len, batch_ids, batch_n: int, stream=None, k_seq=None):
+        """The selector over the evidence and norms of the last slow step;
+        k_seq (device int32 [B]) optionally caps each sequence's list."""
         ptr = seq_len.data_ptr() if torch.is_tensor(seq_len) else seq_len
-        sfi.sfi_select(self.params, batch_ids, batch_n, ptr, self.B, self.Hkv, self.max_len,
-                       self.evidence, self.key_norm, self.ld, self.sel_idx, self.sel_count,
-                       self.fused, self.ws_sel, self.ws_sel_bytes, stream)
+        self.params.k_per_seq = None if k_seq is None else k_seq.data_ptr()
+        try:
+            sfi.sfi_select(self.params, batch_ids, batch_n, ptr, self.B, self.Hkv, self.max_len,
+                           self.evidence, self.key_norm, self.ld, self.sel_idx, self.sel_count,
+                           self.fused, self.ws_sel, self.ws_sel_bytes, stream)
+        finally:
+            self.params.k_per_seq = None
 
     def dense(self, q, seq_len, batch_ids, batch_n: int, stream=None):
         """Plain dense attention (no evidence): the full-KV comparator."""
@@ -143,7 +154,7 @@ class SFIDecoder:
                           self.ws_fast, self.ws_fast_bytes, stream)
 
     def co_step(self, q, seq_len, slow_ids, n_slow: int, fast_ids, n_fast: int, stream=None,
-                out=None, select: bool = True):
+                out=None, select: bool = True, k_seq=None):
         """Slow steps of slow_ids and fast steps of fast_ids in one co-launched
         pass, then the selector of the slow sequences."""
         self.kv.seq_len = seq_len.data_ptr() if torch.is_tensor(seq_len) else seq_len
@@ -152,7 +163,7 @@ class SFIDecoder:
                             self.sel_idx, self.sel_count, self.Hkv, self.k, self.n_sink, self.window,
                             self.ws_step, self.ws_step_bytes, stream)
         if select and n_slow:
-            self.slow_select_only(self.kv.seq_len, slow_ids, n_slow, stream)
+            self.slow_select_only(self.kv.seq_len, slow_ids, n_slow, stream, k_seq=k_seq)
 
     def _new_event(self):
         e = torch.cuda.Event()
@@ -169,12 +180,13 @@ class SFIDecoder:
         calls."""
         q = q_steps[s]
         sl = plan.seq_len[s]
+        ks = None if plan.k_seq is None else plan.k_seq[s]
         ns, nf = int(plan.n_slow[s]), int(plan.n_fast[s])
         if co and ns and nf:
-            self.co_step(q, sl, plan.slow_ids[s], ns, plan.fast_ids[s], nf, stream, out=out)
+            self.co_step(q, sl, plan.slow_ids[s], ns, plan.fast_ids[s], nf, stream, out=out, k_seq=ks)
             return
         if ns:
-            self.slow(q, sl, plan.slow_ids[s], ns, stream, out=out)
+            self.slow(q, sl, plan.slow_ids[s], ns, stream, out=out, k_seq=ks)
         if nf:
             self.fast(q, sl, plan.fast_ids[s], nf, stream, out=out)
 

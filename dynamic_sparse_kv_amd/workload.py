@@ -241,14 +241,55 @@ def to_paged(K: torch.Tensor, table: np.ndarray, n_pages: int, page_size: int) -
     B, Hkv, cap, d = K.shape
     pool = torch.zeros((n_pages, Hkv, page_size, d), dtype=K.dtype, device=K.device)
     for b in range(B):
-        for p in range(table.shape[1]):
-            pg = int(table[b, p])
-            if pg < 0:
-                break
-            lo = p * page_size
-            hi = min(lo + page_size, cap)
-            pool[pg, :, : hi - lo] = K[b, :, lo:hi]
+        npg = int((table[b] >= 0).sum())
+        rows = min(npg * page_size, cap)
+        src = torch.zeros((Hkv, npg * page_size, d), dtype=K.dtype, device=K.device)
+        src[:, :rows] = K[b, :, :rows]
+        idx = torch.as_tensor(table[b, :npg].astype(np.int64), device=K.device)
+        pool[idx] = src.view(Hkv, npg, page_size, d).permute(1, 0, 2, 3)
     return pool
+
+
+def make_paged_kv(cfg: SFIConfig, table: np.ndarray, n_pages: int, caps: np.ndarray, layer: int = 0,
+                  device="cpu"):
+    """Paged K, V pools [n_pages][Hkv][page][d] drawn sequence by sequence.
+
+    Sequence b owns cache rows [0, caps[b]) in the pages table[b][0 ..]; its
+    rows are N(0,1) with planted heavy-hitter keys scaled by ``hh_scale``,
+    each rounded once to bf16, from the same seeded streams as make_kv (a
+    draw of caps[b] rows per head, so the bytes differ from make_kv's, which
+    draws the batch-wide capacity).  Pool pages nobody owns stay zero.
+    """
+    ps = cfg.page_size
+    ctxs = context_lengths(cfg)
+    Kp = torch.zeros((n_pages, cfg.Hkv, ps, cfg.d), dtype=torch.bfloat16, device=device)
+    Vp = torch.zeros_like(Kp)
+    for b in range(cfg.B):
+        cap = int(caps[b])
+        npg = (cap + ps - 1) // ps
+        idx = torch.as_tensor(table[b, :npg].astype(np.int64), device=device)
+        for which, pool in (("K", Kp), ("V", Vp)):
+            gen = torch.Generator(device=device).manual_seed(seed_for(cfg, layer, b, which))
+            x = torch.zeros((cfg.Hkv, npg * ps, cfg.d), dtype=torch.float32, device=device)
+            x[:, :cap] = torch.randn((cfg.Hkv, cap, cfg.d), generator=gen, device=device,
+                                     dtype=torch.float32)
+            if which == "K":
+                hh = heavy_hitter_positions(cfg, layer, b, int(ctxs[b]))
+                for h in range(cfg.Hkv):
+                    if hh.shape[1]:
+                        x[h, torch.as_tensor(hh[h], device=device)] *= cfg.hh_scale
+            pool[idx] = x.to(torch.bfloat16).view(cfg.Hkv, npg, ps, cfg.d).permute(1, 0, 2, 3)
+            del x
+    return Kp, Vp
+
+
+def gather_paged(pool: torch.Tensor, table: np.ndarray, b: int, n: int) -> torch.Tensor:
+    """Rows [0, n) of sequence b from a paged pool, as [Hkv][n][d] (a copy)."""
+    ps = pool.shape[2]
+    npg = (n + ps - 1) // ps
+    idx = torch.as_tensor(table[b, :npg].astype(np.int64), device=pool.device)
+    rows = pool[idx].permute(1, 0, 2, 3).reshape(pool.shape[1], npg * ps, pool.shape[3])
+    return rows[:, :n].contiguous()
 
 
 def bf16_bits(x: torch.Tensor) -> np.ndarray:

@@ -95,7 +95,10 @@ typedef struct sfi_select_params {
   float pos_tau;      /* prior: recency time constant in tokens (1024), > 0 */
   int32_t n_sink;     /* >= 0 */
   int32_t window;     /* >= 0 */
-  int32_t k;          /* > 0: capacity of each index list */
+  int32_t k;          /* > 0: capacity (and row stride) of each index list */
+  const int32_t *k_per_seq; /* device [B] or NULL: sequence b keeps at most
+                               min(k_per_seq[b], k) keys (negative -> 0);
+                               NULL: k for every sequence */
 } sfi_select_params;
 
 /* ---------------------------------------------------------------- sizes */
@@ -126,9 +129,10 @@ sfi_status sfi_slow_step(const sfi_kv *kv, const int32_t *batch_ids, int32_t bat
                          int32_t ld, void *ws, size_t ws_bytes, void *stream);
 
 /* Selector [SFI 3.B; Vegas 2.A]: per listed sequence b and head row h < H,
- * pick the min(k, |C|) best keys of C = [n_sink, seq_len[b] - window) by
- * (score desc, index asc) and write them ascending to
- * sel_idx[b][h][0..count), padding to k with -1; sel_count[b][h] = count.
+ * pick the min(k_b, |C|) best keys of C = [n_sink, seq_len[b] - window) by
+ * (score desc, index asc), with k_b = k or min(k_per_seq[b], k), and write
+ * them ascending to sel_idx[b][h][0..count) (row stride k), padding to k
+ * with -1; sel_count[b][h] = count.
  *   FUSED: score = evidence f [B][H][ld], key_norm [B][H][ld] (both over
  *          j < seq_len[b]).  Prior r_j = w_j / sum w, w_j = exp(-norm_coef
  *          z_j) (1 + exp(-(t - j) / pos_tau)), z_j = key norm standardised by

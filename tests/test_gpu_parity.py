@@ -159,6 +159,36 @@ def test_select_raw_large_k_and_multi_tile():
         np.testing.assert_array_equal(sel[b, 0, :k], want)
 
 
+def test_select_per_sequence_k():
+    """k_per_seq caps each sequence's list (row stride stays k); values above
+    k clamp to k and negative ones to 0."""
+    _say("select per-sequence k")
+    rng = np.random.default_rng(5)
+    B, H, ld, kcap = 5, 2, 9000, 300
+    lens = [9000, 8000, 7000, 600, 5000]
+    sc = rng.standard_normal((B, H, ld)).astype(np.float32)
+    kseq = np.array([300, 50, 0, 1000, -3], dtype=np.int32)
+    seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    ks = torch.from_numpy(kseq).to(DEV)
+    p = sfi.select_params(sfi.SFI_SCORE_RAW, 0.0, kcap, 4, 256, k_per_seq=ks)
+    sel = torch.full((B, H, kcap), -7, dtype=torch.int32, device=DEV)
+    cnt = torch.full((B, H), -7, dtype=torch.int32, device=DEV)
+    wsb = sfi.sfi_select_workspace_bytes(B, H, max(lens))
+    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    sfi.sfi_select(p, None, B, seq, B, H, max(lens), torch.from_numpy(sc).to(DEV), None, ld, sel, cnt,
+                   None, ws, wsb)
+    torch.cuda.synchronize()
+    sel, cnt = sel.cpu().numpy(), cnt.cpu().numpy()
+    for b in range(B):
+        kb = int(min(max(kseq[b], 0), kcap))
+        lo, hi = O.candidate_range(lens[b], 4, 256)
+        for h in range(H):
+            want = O.topk_indices(sc[b, h].astype(np.float64), lo, hi, kb)
+            assert cnt[b, h] == len(want)
+            np.testing.assert_array_equal(sel[b, h, : len(want)], want)
+            assert np.all(sel[b, h, len(want):] == -1)
+
+
 def test_select_fused_from_oracle_evidence():
     """Selector alone: oracle f and norms in, oracle s and Top-K out."""
     _say("select fused")
