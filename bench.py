@@ -57,6 +57,103 @@ def algorithmic_bytes(kind, n, cfg, k=None):
     raise ValueError(kind)
 
 
+def percall_list(slow, ctx, cfg, steps):
+    """The eager per-call pass of the headline workload, in launch order:
+    (kind, step, algorithmic bytes).  A step with both slow and fast
+    sequences runs them co-launched ("step"), then the selector."""
+    out = []
+    for s in range(steps):
+        lens = ctx + s + 1
+        sl, fa = np.nonzero(slow[s])[0], np.nonzero(~slow[s])[0]
+        sb = sum(algorithmic_bytes("slow", int(lens[b]), cfg) for b in sl)
+        fb = sum(algorithmic_bytes("fast", int(lens[b]), cfg) for b in fa)
+        selb = sum(algorithmic_bytes("select", int(lens[b]), cfg) for b in sl)
+        if len(sl) and len(fa):
+            out.append(("step", s, sb + fb))
+        elif len(sl):
+            out.append(("slow", s, sb))
+        elif len(fa):
+            out.append(("fast", s, fb))
+        if len(sl):
+            out.append(("select", s, selb))
+    return out
+
+
+def traffic_from_counters(d, steps):
+    """HBM bytes per call kind from two rocprofv3 counter runs of
+    bench.py --no-graph --steps S --warmup 1 --no-cpu-baseline --calib-copy --legs none
+    (d/fetch with FETCH_SIZE, d/write with WRITE_SIZE).  The dispatch streams
+    of the two runs are paired in order; FETCH_SIZE and WRITE_SIZE are scaled
+    by what they read for the plain 256 MiB copy the run starts with; after
+    the first 1 GiB flush read every segment between flush reads is one timed
+    call of the eager pass.  Writes the traffic summary json beside the
+    profiles and prints a markdown table."""
+    import csv
+    from dynamic_sparse_kv_amd import sfi
+    from dynamic_sparse_kv_amd import workload as W
+
+    def load(which):
+        rows = list(csv.DictReader(open(os.path.join(d, which, "bench_counter_collection.csv"))))
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        return rows
+    F, Wr = load("fetch"), load("write")
+    assert len(F) == len(Wr), (len(F), len(Wr))
+    for a, b in zip(F, Wr):
+        assert a["Kernel_Name"] == b["Kernel_Name"]
+    # the runtime's buffer fills (torch's reduction output) belong to no call
+    keep = [i for i, r in enumerate(F) if "fillBuffer" not in r["Kernel_Name"]]
+    F, Wr = [F[i] for i in keep], [Wr[i] for i in keep]
+    ci = next(i for i, r in enumerate(F) if "copyBuffer" in r["Kernel_Name"])
+    copy_kib = (1 << 26) * 4 / 1024
+    fs = copy_kib / float(F[ci]["Counter_Value"])
+    ws = copy_kib / float(Wr[ci]["Counter_Value"])
+    flush = [i for i, r in enumerate(F) if "reduce_kernel" in r["Kernel_Name"]]
+    cfg = W.CONFIGS["c2"].replace(steps=steps)
+    slow = sfi.sfi_schedule(W.sentence_starts(cfg), cfg.budget).astype(bool)
+    calls = percall_list(slow, W.context_lengths(cfg), cfg, steps)
+    kinds = {"step": ("copartial_kernel", "cofinal_kernel"),
+             "slow": ("partial_kernel", "finalize_kernel"),
+             "fast": ("partial_kernel", "finalize_kernel"),
+             "select": ("norm_sums_kernel", "prior_kernel", "keys_kernel", "pick_kernel")}
+    nk = {"step": 2, "slow": 2, "fast": 2, "select": 4}   # kernels per call
+    tot = {}
+    for c, (kind, s, alg) in enumerate(calls):
+        lo = flush[c] + 1
+        hi = lo + nk[kind]
+        assert c + 1 >= len(flush) or flush[c + 1] == hi, (c, kind)
+        names = [F[i]["Kernel_Name"] for i in range(lo, hi)]
+        for nm in names:
+            assert any(k in nm for k in kinds[kind]), (c, kind, nm)
+        fb = sum(float(F[i]["Counter_Value"]) for i in range(lo, hi)) * fs * 1024
+        wb = sum(float(Wr[i]["Counter_Value"]) for i in range(lo, hi)) * ws * 1024
+        t = tot.setdefault(kind, [0.0, 0.0, 0, 0])
+        t[0] += fb; t[1] += wb; t[2] += alg; t[3] += 1
+    res = {
+        "workload": f"{cfg.name} (B={cfg.B}, Hq={cfg.Hq}, Hkv={cfg.Hkv}, d={cfg.d}, ctx {cfg.ctx}, "
+                    f"{cfg.n_sink}+{cfg.window}+{cfg.k}, lambda {cfg.lam}), eager pass over decode steps 0..{steps - 1}",
+        "commands": [f"rocprofv3 --pmc {c} --output-format csv -d gpurun_out/traffic/{w} -o bench -- python3 -u "
+                     f"bench.py --no-graph --steps {steps} --warmup 1 --no-cpu-baseline --calib-copy --legs none"
+                     for c, w in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write"))],
+        "calibration": {"copy_bytes": 1 << 28, "fetch_kib_read": float(F[ci]["Counter_Value"]),
+                        "write_kib_read": float(Wr[ci]["Counter_Value"]),
+                        "fetch_scale": round(fs, 4), "write_scale": round(ws, 4)},
+        "ratio": {k: round((v[0] + v[1]) / v[2], 4) for k, v in tot.items()},
+        "totals_bytes": {k: {"calls": v[3], "fetch": int(v[0]), "write": int(v[1]), "algorithmic": int(v[2])}
+                         for k, v in tot.items()},
+        "kernel_source_sha256": kernel_source_hash(),
+    }
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(res, fh, indent=1)
+    print(f"calibration: FETCH_SIZE {F[ci]['Counter_Value']} KiB, WRITE_SIZE {Wr[ci]['Counter_Value']} KiB "
+          f"for a 256 MiB copy -> scales {fs:.4f}, {ws:.4f}; flush reads "
+          f"{sorted(set(round(float(F[i]['Counter_Value']) * fs / 1048576, 3) for i in flush))} GiB")
+    print("| call | calls | fetch MB | write MB | algorithmic MB | measured / algorithmic |")
+    print("|---|---|---|---|---|---|")
+    for k, v in tot.items():
+        print(f"| {k} | {v[3]} | {v[0] / 1e6:.2f} | {v[1] / 1e6:.2f} | {v[2] / 1e6:.2f} | "
+              f"{(v[0] + v[1]) / v[2]:.4f} |")
+
+
 def kernel_source_hash():
     """sha256 over every HIP source of the library: counter-derived traffic
     is reported only while the kernels are the ones it was measured on."""
@@ -447,10 +544,16 @@ def main():
     ap.add_argument("--legs", default="stack32-128k,vegas-64k,ragged-paged",
                     help="extra workloads measured after the headline (comma list, or 'none')")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--traffic", metavar="DIR",
+                    help="no GPU run: derive per-call HBM traffic from the two counter runs under DIR "
+                         "(DIR/fetch, DIR/write; see traffic_from_counters) and rewrite the traffic summary")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy (a known-size kernel "
                          "for scaling hardware byte counters)")
     args = ap.parse_args()
+    if args.traffic:
+        traffic_from_counters(args.traffic, args.steps)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); the path has no multi-GPU mode",
               file=sys.stderr)
@@ -544,23 +647,14 @@ def main():
         e1.record(stream)
         ev.append((kind, e0, e1, nbytes))
 
-    for s in range(K_steps):
+    for kind, s, nbytes in percall_list(plan.slow, ctx, cfg, K_steps):
         ns, nf = int(plan.n_slow[s]), int(plan.n_fast[s])
-        lens = plan.seq_len_host[s]
-        sb = sum(algorithmic_bytes("slow", int(lens[b]), cfg) for b in np.nonzero(plan.slow[s])[0])
-        fb = sum(algorithmic_bytes("fast", int(lens[b]), cfg) for b in np.nonzero(~plan.slow[s])[0])
-        selb = sum(algorithmic_bytes("select", int(lens[b]), cfg) for b in np.nonzero(plan.slow[s])[0])
-        if ns and nf:   # the co-launched slow + fast pass the step runs, then the selector
-            timed("step", lambda: dec.co_step(q[s], plan.seq_len[s], plan.slow_ids[s], ns,
-                                              plan.fast_ids[s], nf, stream, select=False), sb + fb)
-        elif ns:
-            timed("slow", lambda: dec.slow(q[s], plan.seq_len[s], plan.slow_ids[s], ns, stream,
-                                           select=False), sb)
-        elif nf:
-            timed("fast", lambda: dec.fast(q[s], plan.seq_len[s], plan.fast_ids[s], nf, stream), fb)
-        if ns:
-            timed("select", lambda: dec.slow_select_only(plan.seq_len[s], plan.slow_ids[s], ns, stream),
-                  selb)
+        fn = {"step": lambda: dec.co_step(q[s], plan.seq_len[s], plan.slow_ids[s], ns, plan.fast_ids[s], nf,
+                                          stream, select=False),
+              "slow": lambda: dec.slow(q[s], plan.seq_len[s], plan.slow_ids[s], ns, stream, select=False),
+              "fast": lambda: dec.fast(q[s], plan.seq_len[s], plan.fast_ids[s], nf, stream),
+              "select": lambda: dec.slow_select_only(plan.seq_len[s], plan.slow_ids[s], ns, stream)}[kind]
+        timed(kind, fn, nbytes)
     torch.cuda.synchronize()
     del flush
     for kind, a, b_, nbytes in ev:
