@@ -78,6 +78,15 @@ struct PartialArgs {
   float qscale;  // log2(e) / sqrt(d)
 };
 
+// Maximum over the wave of a value that is equal within each aligned group
+// of 8 lanes (xor 8 stays inside a 16-lane row: a DPP rotate).
+__device__ __forceinline__ float wave_max_groups(float x) {
+  x = fmaxf(x, dpp_f32<0x128>(x));  // row_ror:8 == lane ^ 8 within a row
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
 // Fast-step row list of (b, g): [sinks | window | selected].
 struct FastList {
   int ns, w0, nw, cnt;
@@ -117,6 +126,8 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
   constexpr int NW = kThreads / 64;
   // Lazy rescaling: the running reference m only moves when a logit exceeds
   // it by more than kSlack (log2 units), so p = 2^(l - m) stays <= 2^kSlack.
+  // m is the same in every lane of the wave (it moves to the wave's maximum),
+  // so the lane groups' partials merge below by plain addition.
   constexpr float kSlack = 8.0f;
 
   __shared__ int s_idx[MODE == MODE_FAST ? kMaxFastChunk : 1];
@@ -154,17 +165,33 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
   }
 
   if constexpr (MODE == MODE_FAST) {
-    for (int p = p0 + tid; p < p1; p += kThreads) {
-      int j;
-      if (p < fl.ns) {
-        j = p;
-      } else if (p < fl.ns + fl.nw) {
-        j = fl.w0 + (p - fl.ns);
-      } else {
-        j = fl.sel[p - fl.ns - fl.nw];
-        if (j < a.n_sink || j >= fl.w0) j = -1;  // padding, sink or now in window
+    // Every list entry of the chunk is loaded before any is stored, so the
+    // index loads are in flight together (one round trip instead of one per
+    // 256 entries).  A load for a sink or window position reads a valid slot
+    // of the list (it has at least one) and is not used.
+    constexpr int IPT = kMaxFastChunk / kThreads;
+    const int nfix = fl.ns + fl.nw;
+    int jv[IPT];
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+      const int p = p0 + tid + i * kThreads;
+      jv[i] = fl.sel[min(max(p - nfix, 0), max(fl.cnt - 1, 0))];
+    }
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+      const int p = p0 + tid + i * kThreads;
+      if (p < p1) {
+        int j;
+        if (p < fl.ns) {
+          j = p;
+        } else if (p < nfix) {
+          j = fl.w0 + (p - fl.ns);
+        } else {
+          j = jv[i];
+          if (j < a.n_sink || j >= fl.w0) j = -1;  // padding, sink or now in window
+        }
+        s_idx[p - p0] = j;
       }
-      s_idx[p - p0] = j;
     }
     __syncthreads();
   }
@@ -268,9 +295,8 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
       float mx = l[0][h];
 #pragma unroll
       for (int u = 1; u < U; ++u) mx = fmaxf(mx, l[u][h]);
-      const bool need = mx > m[h] + kSlack;
-      if (__any(need)) {
-        const float mn = need ? mx : m[h];
+      if (__any(mx > m[h] + kSlack)) {
+        const float mn = wave_max_groups(fmaxf(mx, m[h]));
         const float sc = exp2f(m[h] - mn);
         m[h] = mn;
         Z[h] *= sc;
@@ -308,12 +334,15 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
 
   // Two stages in flight: the loads of one stage overlap the math of the other.
   constexpr int STEP = RPB * U;
+  // The trip count is the same for every lane of the wave (lane groups past
+  // the chunk's end consume masked rows), so the wave-wide maximum updates
+  // in consume() see every lane and m stays wave-uniform.
   Stage sa, sb;
   load_stage(sa, p0 + rg);
-  for (int base = p0 + rg; base < p1; base += 2 * STEP) {
-    load_stage(sb, base + STEP);
+  for (int base = p0; base < p1; base += 2 * STEP) {
+    load_stage(sb, base + rg + STEP);
     consume(sa);
-    load_stage(sa, base + 2 * STEP);
+    load_stage(sa, base + rg + 2 * STEP);
     consume(sb);
   }
 
@@ -334,17 +363,12 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
     };
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float mo = xch(m[h]);
-      const float zo = xch(Z[h]);
-      const float mn = fmaxf(m[h], mo);
-      const float s1 = exp2f(m[h] - mn), s2 = exp2f(mo - mn);
-      Z[h] = Z[h] * s1 + zo * s2;
-      m[h] = mn;
+      Z[h] += xch(Z[h]);  // the reference m is wave-uniform: partials just add
 #pragma unroll
       for (int i = 0; i < HALF; ++i) {
         const float keep = bit ? acc[h][HALF + i] : acc[h][i];
         const float send = bit ? acc[h][i] : acc[h][HALF + i];
-        acc[h][i] = keep * s1 + xch(send) * s2;
+        acc[h][i] = keep + xch(send);
       }
     }
     dim_off += bit ? HALF : 0;
