@@ -75,6 +75,9 @@ def percall_list(slow, ctx, cfg, steps):
         elif len(fa):
             out.append(("fast", s, fb))
         if len(sl):
+            # the same step as one sfi_decode_step_select call (what the
+            # graph replays), then the selector alone
+            out.append(("step_select", s, sb + fb + selb))
             out.append(("select", s, selb))
     return out
 
@@ -114,8 +117,10 @@ def traffic_from_counters(d, steps):
     kinds = {"step": ("copartial_kernel", "cofinal_kernel"),
              "slow": ("partial_kernel", "finalize_kernel"),
              "fast": ("partial_kernel", "finalize_kernel"),
-             "select": ("norm_sums_kernel", "prior_kernel", "keys_kernel", "pick_kernel")}
-    nk = {"step": 2, "slow": 2, "fast": 2, "select": 4}   # kernels per call
+             "select": ("norm_sums_kernel", "prior_kernel", "keys_kernel", "pick_kernel"),
+             "step_select": ("copartial_kernel", "cofinal_kernel", "partial_kernel", "finalize_kernel",
+                             "keys_kernel", "pick_kernel")}
+    nk = {"step": 2, "slow": 2, "fast": 2, "select": 4, "step_select": 4}   # kernels per call
     tot = {}
     for c, (kind, s, alg) in enumerate(calls):
         lo = flush[c] + 1
@@ -635,8 +640,8 @@ def main():
     # busy while the host enqueues the call and its events ----------------
     _log("[bench] per-call timing pass")
     flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-    calls = {"step": [], "slow": [], "select": [], "fast": []}
-    bytes_by = {"step": [], "slow": [], "select": [], "fast": []}
+    calls = {"step": [], "slow": [], "select": [], "fast": [], "step_select": []}
+    bytes_by = {k_: [] for k_ in calls}
     ev = []
 
     def timed(kind, fn, nbytes):
@@ -653,7 +658,10 @@ def main():
                                           stream, select=False),
               "slow": lambda: dec.slow(q[s], plan.seq_len[s], plan.slow_ids[s], ns, stream, select=False),
               "fast": lambda: dec.fast(q[s], plan.seq_len[s], plan.fast_ids[s], nf, stream),
-              "select": lambda: dec.slow_select_only(plan.seq_len[s], plan.slow_ids[s], ns, stream)}[kind]
+              "select": lambda: dec.slow_select_only(plan.seq_len[s], plan.slow_ids[s], ns, stream),
+              # informational: not a roofline candidate (its selector part is latency-bound)
+              "step_select": lambda: dec.step_select(q[s], plan.seq_len[s], plan.slow_ids[s], ns,
+                                                     plan.fast_ids[s], nf, stream)}[kind]
         timed(kind, fn, nbytes)
     torch.cuda.synchronize()
     del flush
@@ -669,7 +677,7 @@ def main():
                               "total_ms": round(sum(calls[kind]) * 1e3, 3),
                               "alg_bytes_per_launch": int(by),
                               "alg_GBps": round(by / t / 1e9, 1)}
-    dom = max(per_call, key=lambda k_: per_call[k_]["total_ms"])
+    dom = max((k_ for k_ in per_call if k_ != "step_select"), key=lambda k_: per_call[k_]["total_ms"])
     dc = per_call[dom]
     achieved = dc["alg_GBps"]
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -723,7 +731,8 @@ def main():
                                f"lambda {cfg.lam}, {K_steps} decode steps",
                    "global_batch": cfg.B, "seq_len": cfg.ctx, "parallelism": "none (1 GPU)",
                    "slow_fraction": round(float(plan.slow[:K_steps].mean()), 4),
-                   "timing": "hip graph replay, one stream" if use_graph else "eager, one stream"},
+                   "timing": ("hip graph replay, one stream" if use_graph else "eager, one stream") +
+                             "; a step with slow sequences is one sfi_decode_step_select call"},
         "roofline": roofline,
         "per_call": per_call,
         "dense_tokens_per_s": round(dense_tps, 1),

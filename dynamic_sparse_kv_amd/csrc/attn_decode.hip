@@ -76,6 +76,7 @@ struct PartialArgs {
   const int32_t *sel_count;
   int sel_heads, sel_k, n_sink, window;
   float qscale;  // log2(e) / sqrt(d)
+  double *nsum;  // [B][Hkv][stride][2] per-split key-norm sums, or null
 };
 
 // Maximum over the wave of a value that is equal within each aligned group
@@ -198,6 +199,7 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
 
 
   float m[G], Z[G], acc[G][DPL];
+  double ns1 = 0.0, ns2 = 0.0;  // key-norm sums of this lane's rows (evidence mode)
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     m[h] = kNegBig;
@@ -286,7 +288,12 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
             for (int h = 1; h < G; ++h) v = (sub == h) ? l[u][h] : v;
             a.logits[(lrow * a.lld + j) * G + sub] = v;
           }
-          if (sub == G % LPR && a.key_norm) a.key_norm[lrow * a.ld + j] = sqrtf(nn);
+          if (sub == G % LPR) {
+            const float nv = sqrtf(nn);
+            if (a.key_norm) a.key_norm[lrow * a.ld + j] = nv;
+            ns1 += (double)nv;
+            ns2 = fma((double)nv, (double)nv, ns2);
+          }
         }
       }
     }
@@ -394,7 +401,33 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
       s_z[wv][h] = Z[h];
     }
   }
+  __shared__ double s_ns[NW][2];
+  if constexpr (EVID) {
+    if (a.nsum) {
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        ns1 += __shfl_xor(ns1, off);
+        ns2 += __shfl_xor(ns2, off);
+      }
+      if (lane == 0) {
+        s_ns[wv][0] = ns1;
+        s_ns[wv][1] = ns2;
+      }
+    }
+  }
   __syncthreads();
+  if constexpr (EVID) {
+    if (a.nsum && tid == 0) {
+      double t1 = 0.0, t2 = 0.0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        t1 += s_ns[w][0];
+        t2 += s_ns[w][1];
+      }
+      a.nsum[(lrow * a.stride + split) * 2 + 0] = t1;
+      a.nsum[(lrow * a.stride + split) * 2 + 1] = t2;
+    }
+  }
 
   for (int idx = tid; idx < G * D; idx += kThreads) {
     const int h = idx / D, e = idx % D;
@@ -456,6 +489,14 @@ struct FinalArgs {
   const int32_t *sel_idx;
   const int32_t *sel_count;
   int sel_heads, sel_k, n_sink, window;
+  // selector prior (evidence blocks; null nsum: not computed)
+  const double *nsum;
+  const float *key_norm;
+  float norm_coef, pos_tau;
+  double *sel_wsum;
+  SelRowMeta *sel_meta;
+  uint32_t *sel_ghist;
+  int selP;
 };
 
 // Merge (m2, z2) into the running softmax pair (m, z): both are a log2-domain
@@ -560,14 +601,17 @@ __device__ __forceinline__ void finalize_body(const FinalArgs &a, int x, int g, 
     const int j0 = (x - G) * kEvidChunk;
     const int j1 = min(n, j0 + kEvidChunk);
     constexpr int PER = kEvidChunk / kThreads;
-    // the chunk's logits do not depend on the merged maxima: load them first
-    float lg[PER][G];
+    // the chunk's logits (and key norms) do not depend on the merged
+    // maxima: load them first
+    const bool prior = a.nsum != nullptr;
+    float lg[PER][G], nv[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int j = j0 + tid + i * kThreads;
       const float *lp = a.logits + (lrow * a.lld + (size_t)min(j, j1 - 1)) * G;
 #pragma unroll
       for (int h = 0; h < G; ++h) lg[i][h] = lp[h];
+      nv[i] = prior ? a.key_norm[lrow * a.ld + min(j, j1 - 1)] : 0.f;
     }
     // merged (max, sum) of every head of the group over the S partials
     float m[G], z[G];
@@ -614,6 +658,65 @@ __device__ __forceinline__ void finalize_body(const FinalArgs &a, int x, int g, 
       for (int h = 0; h < G; ++h) f = fmaf(exp2f(lg[i][h] - M[h]), rz[h], f);
       if (j < j1) a.evidence[lrow * a.ld + j] = f;
     }
+    if (!prior) return;
+    // The selector's prior for this 2048-key chunk (the selector's chunk p):
+    // mean and population std of the row's key norms from the partial
+    // kernel's per-split sums (fixed order; every chunk block repeats it),
+    // then the chunk's sum of prior weights.  Chunk 0 also stores the row
+    // constants, and the blocks clear the row's bucket histogram between
+    // them, so the selection can start at its key pass.
+    const int pch = x - G;
+    double s1 = 0.0, s2 = 0.0;
+    for (int sp = tid; sp < S; sp += kThreads) {
+      s1 += a.nsum[(lrow * a.stride + sp) * 2 + 0];
+      s2 += a.nsum[(lrow * a.stride + sp) * 2 + 1];
+    }
+    __shared__ double s_d[NW][2];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      s1 += __shfl_xor(s1, off);
+      s2 += __shfl_xor(s2, off);
+    }
+    if (lane == 0) {
+      s_d[wv][0] = s1;
+      s_d[wv][1] = s2;
+    }
+    __syncthreads();
+    s1 = 0.0;
+    s2 = 0.0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      s1 += s_d[w][0];
+      s2 += s_d[w][1];
+    }
+    __syncthreads();
+    float muf, cz;
+    prior_consts(s1, s2, n, a.norm_coef, &muf, &cz);
+    const float ct = kLog2e / a.pos_tau;
+    const float tq = (float)(n - 1);
+    float sw = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int j = j0 + tid + i * kThreads;
+      sw += (j < j1) ? prior_w(nv[i], j, muf, cz, tq, ct) : 0.f;
+    }
+    double W = (double)sw;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) W += __shfl_xor(W, off);
+    if (lane == 0) s_d[wv][0] = W;
+    __syncthreads();
+    if (tid == 0) {
+      double t = 0.0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) t += s_d[w][0];
+      a.sel_wsum[lrow * a.selP + pch] = t;
+      if (pch == 0) {
+        a.sel_meta[lrow].muf = muf;
+        a.sel_meta[lrow].cz = cz;
+      }
+    }
+    const int nch = (n + kEvidChunk - 1) / kEvidChunk;
+    for (int i = pch * kThreads + tid; i < 4096; i += nch * kThreads) a.sel_ghist[lrow * 4096 + i] = 0u;
   }
 }
 
@@ -662,6 +765,7 @@ PartialArgs partial_args(const AttnLaunch &a) {
   p.sel_idx = a.sel_idx; p.sel_count = a.sel_count; p.sel_heads = a.sel_heads; p.sel_k = a.sel_k;
   p.n_sink = a.n_sink; p.window = a.window;
   p.qscale = kLog2e / sqrtf((float)D);
+  p.nsum = a.nsum;
   return p;
 }
 
@@ -673,6 +777,8 @@ FinalArgs final_args(const AttnLaunch &a) {
   f.out = a.out; f.logits = a.logits; f.lld = a.lld; f.evidence = a.evidence; f.ld = a.ld;
   f.sel_idx = a.sel_idx; f.sel_count = a.sel_count; f.sel_heads = a.sel_heads;
   f.sel_k = a.sel_k; f.n_sink = a.n_sink; f.window = a.window;
+  f.nsum = a.nsum; f.key_norm = a.key_norm; f.norm_coef = a.norm_coef; f.pos_tau = a.pos_tau;
+  f.sel_wsum = a.sel_wsum; f.sel_meta = a.sel_meta; f.sel_ghist = a.sel_ghist; f.selP = a.selP;
   return f;
 }
 

@@ -153,14 +153,6 @@ __device__ __forceinline__ bool aligned16(const void *p) {
   return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
 }
 
-// Prior weight of key j: exp(-norm_coef z_j) (1 + exp(-(t - j)/tau)) with
-// z_j = (nu_j - mu)/sd, as powers of two (cz = -norm_coef log2(e)/sd,
-// ct = log2(e)/tau).  Steps 2 and 3 both call it, so the weights and their sum
-// agree bit for bit.
-__device__ __forceinline__ float prior_w(float nu, int j, float muf, float cz, float tq, float ct) {
-  return exp2f(cz * (nu - muf)) * (1.0f + exp2f(((float)j - tq) * ct));
-}
-
 // Composite rank value: larger key first, then lower index.
 __device__ __forceinline__ unsigned long long composite(uint32_t key, int j) {
   return ((unsigned long long)key << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)j);
@@ -218,12 +210,8 @@ __global__ __launch_bounds__(kT) void prior_kernel(SelectLaunch a) {
     }
     s1 = block_sum_d<kTW>(s1, s_red);
     s2 = block_sum_d<kTW>(s2, s_red);
-    const double mu = s1 / r.n;
-    const double var = fmax(s2 / r.n - mu * mu, 0.0);
-    const double sd = sqrt(var);
-    const float muf = (float)mu;
-    const float isd = sd > 0.0 ? (float)(1.0 / sd) : 0.0f;
-    const float cz = -a.norm_coef * isd * kLog2e;
+    float muf, cz;
+    prior_consts(s1, s2, r.n, a.norm_coef, &muf, &cz);
     const float ct = kLog2e / a.pos_tau;
     const float tq = (float)(r.n - 1);
     float sw = 0.f;
@@ -601,10 +589,12 @@ hipError_t launch_select(const SelectLaunch &a, hipStream_t st) {
   const bool fused = a.mode == 0;
   hipError_t e;
   if (fused) {
-    hipLaunchKernelGGL(norm_sums_kernel, grid, dim3(kT), 0, st, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(prior_kernel<true>, grid, dim3(kT), 0, st, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (!a.prior_done) {  // else the slow step's finalize wrote the prior sums
+      hipLaunchKernelGGL(norm_sums_kernel, grid, dim3(kT), 0, st, a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      hipLaunchKernelGGL(prior_kernel<true>, grid, dim3(kT), 0, st, a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(keys_kernel<true>, grid, dim3(kT), 0, st, a);
   } else {
     hipLaunchKernelGGL(prior_kernel<false>, grid, dim3(kT), 0, st, a);

@@ -133,6 +133,51 @@ T *carve(void *ws, size_t off) {
   return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
 }
 
+sfi_status select_impl(const sfi_select_params *p, const int32_t *batch_ids, int32_t batch_n,
+                      const int32_t *seq_len, int32_t B, int32_t H, int32_t max_seq_len,
+                      const float *score, const float *key_norm, int32_t ld, int32_t *sel_idx,
+                      int32_t *sel_count, float *fused_out, void *ws, size_t ws_bytes,
+                      void *stream, bool prior_done) {
+  if (!p || !seq_len || !score || !sel_idx || !sel_count) return SFI_ERR_NULL;
+  if (p->mode != SFI_SCORE_FUSED && p->mode != SFI_SCORE_RAW) return SFI_ERR_RANGE;
+  if (B < 1 || H < 1 || max_seq_len < 1) return SFI_ERR_SHAPE;
+  if (max_seq_len > kSelMaxLen) return SFI_ERR_UNSUPPORTED;
+  if (batch_n < 0 || batch_n > B) return SFI_ERR_RANGE;
+  if (ld < max_seq_len) return SFI_ERR_RANGE;
+  if (p->k < 1 || p->n_sink < 0 || p->window < 0) return SFI_ERR_RANGE;
+  const bool fused = p->mode == SFI_SCORE_FUSED;
+  if (fused) {
+    if (!key_norm) return SFI_ERR_NULL;
+    if (!(p->lambda >= 0.f && p->lambda <= 1.f)) return SFI_ERR_RANGE;
+    if (!(p->pos_tau > 0.f) || !(p->norm_coef == p->norm_coef)) return SFI_ERR_RANGE;
+  }
+  const SelWs w = select_ws(B, H, max_seq_len);
+  if (!ws) return SFI_ERR_NULL;
+  if (ws_bytes < w.total) return SFI_ERR_WORKSPACE;
+  if (batch_n == 0) return SFI_OK;
+
+  SelectLaunch a{};
+  a.mode = p->mode;
+  a.lambda = p->lambda; a.norm_coef = p->norm_coef; a.pos_tau = p->pos_tau;
+  a.n_sink = p->n_sink; a.window = p->window; a.k = p->k;
+  a.k_seq = p->k_per_seq;
+  a.batch_ids = batch_ids; a.batch_n = batch_n; a.seq_len = seq_len;
+  a.B = B; a.H = H; a.max_seq_len = max_seq_len;
+  a.score = score; a.key_norm = key_norm; a.ld = ld;
+  a.sel_idx = sel_idx; a.sel_count = sel_count;
+  a.fused_out = fused ? fused_out : nullptr;
+  a.fo_ld = ld;
+  a.prior_done = prior_done;
+  a.ws.P = w.P;
+  a.ws.ghist = carve<uint32_t>(ws, w.ghist);
+  a.ws.cum = carve<uint16_t>(ws, w.cum);
+  a.ws.sorted = carve<unsigned long long>(ws, w.sorted);
+  a.ws.nsum = carve<double>(ws, w.nsum);
+  a.ws.wsum = carve<double>(ws, w.wsum);
+  a.ws.meta = carve<SelRowMeta>(ws, w.meta);
+  return launch_select(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SFI_OK : SFI_ERR_HIP;
+}
+
 AttnLaunch slow_launch(const sfi_kv *kv, const KVView &view, bool paged, const SlowWs &w, void *ws,
                        const int32_t *batch_ids, int32_t batch_n, const uint16_t *q, float *out,
                        float *evidence, float *key_norm, int32_t ld) {
@@ -279,48 +324,81 @@ sfi_status sfi_decode_step(const sfi_kv *kv, const int32_t *slow_ids, int32_t n_
   return e == hipSuccess ? SFI_OK : SFI_ERR_HIP;
 }
 
+size_t sfi_decode_step_select_workspace_bytes(const sfi_kv *kv, int32_t sel_k, int32_t n_sink,
+                                              int32_t window) {
+  KVView view;
+  bool paged = false;
+  if (check_kv(kv, &view, &paged) != SFI_OK || sel_k < 1 || n_sink < 0 || window < 0) return 0;
+  if (kv->max_seq_len > kSelMaxLen) return 0;
+  const SlowWs sw = slow_ws(kv);
+  return sw.total + fast_ws(kv, sel_k, n_sink, window).total +
+         select_ws(kv->B, kv->Hkv, kv->max_seq_len).total +
+         align_up((size_t)kv->B * kv->Hkv * sw.stride * 2 * sizeof(double));
+}
+
+sfi_status sfi_decode_step_select(const sfi_kv *kv, const sfi_select_params *p,
+                                  const int32_t *slow_ids, int32_t n_slow, const int32_t *fast_ids,
+                                  int32_t n_fast, const uint16_t *q, float *out, float *evidence,
+                                  float *key_norm, int32_t ld, int32_t *sel_idx, int32_t *sel_count,
+                                  float *fused_out, void *ws, size_t ws_bytes, void *stream) {
+  KVView view;
+  bool paged = false;
+  sfi_status s = check_kv(kv, &view, &paged);
+  if (s != SFI_OK) return s;
+  if (!p) return SFI_ERR_NULL;
+  if (p->mode != SFI_SCORE_FUSED) return SFI_ERR_RANGE;
+  if (!(p->lambda >= 0.f && p->lambda <= 1.f)) return SFI_ERR_RANGE;
+  if (!(p->pos_tau > 0.f) || !(p->norm_coef == p->norm_coef)) return SFI_ERR_RANGE;
+  if (p->k < 1 || p->n_sink < 0 || p->window < 0) return SFI_ERR_RANGE;
+  if (kv->max_seq_len > kSelMaxLen) return SFI_ERR_UNSUPPORTED;
+  if ((s = check_batch(kv, n_slow)) != SFI_OK) return s;
+  if ((s = check_batch(kv, n_fast)) != SFI_OK) return s;
+  if (n_slow + n_fast > kv->B) return SFI_ERR_RANGE;
+  if (!q || !out || !sel_idx || !sel_count) return SFI_ERR_NULL;
+  if (n_slow > 0 && (!evidence || !key_norm)) return SFI_ERR_NULL;
+  if (n_slow > 0 && ld < kv->max_seq_len) return SFI_ERR_RANGE;
+  if (n_fast > 0 &&
+      (s = check_fast(kv, sel_idx, sel_count, kv->Hkv, p->k, p->n_sink, p->window)) != SFI_OK)
+    return s;
+  const SlowWs sw = slow_ws(kv);
+  const FastWs fw = fast_ws(kv, p->k, p->n_sink, p->window);
+  const SelWs ew = select_ws(kv->B, kv->Hkv, kv->max_seq_len);
+  const size_t nsum_bytes = align_up((size_t)kv->B * kv->Hkv * sw.stride * 2 * sizeof(double));
+  if (!ws) return SFI_ERR_NULL;
+  if (ws_bytes < sw.total + fw.total + ew.total + nsum_bytes) return SFI_ERR_WORKSPACE;
+  if (n_slow == 0 && n_fast == 0) return SFI_OK;
+  char *base = static_cast<char *>(ws);
+  void *ws_fast = base + sw.total;
+  void *ws_sel = base + sw.total + fw.total;
+  double *nsum = reinterpret_cast<double *>(base + sw.total + fw.total + ew.total);
+  AttnLaunch sa = slow_launch(kv, view, paged, sw, ws, slow_ids, n_slow, q, out, evidence, key_norm, ld);
+  sa.nsum = nsum;
+  sa.norm_coef = p->norm_coef;
+  sa.pos_tau = p->pos_tau;
+  sa.sel_wsum = carve<double>(ws_sel, ew.wsum);
+  sa.sel_meta = carve<SelRowMeta>(ws_sel, ew.meta);
+  sa.sel_ghist = carve<uint32_t>(ws_sel, ew.ghist);
+  sa.selP = ew.P;
+  const AttnLaunch fa = fast_launch(kv, view, paged, fw, ws_fast, fast_ids, n_fast, q, out, sel_idx,
+                                    sel_count, kv->Hkv, p->k, p->n_sink, p->window);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (n_fast == 0) e = launch_slow(sa, st);
+  else if (n_slow == 0) e = launch_fast(fa, st);
+  else e = launch_step(sa, fa, st);
+  if (e != hipSuccess) return SFI_ERR_HIP;
+  if (n_slow == 0) return SFI_OK;
+  return select_impl(p, slow_ids, n_slow, kv->seq_len, kv->B, kv->Hkv, kv->max_seq_len, evidence,
+                     key_norm, ld, sel_idx, sel_count, fused_out, ws_sel, ew.total, stream, true);
+}
+
 sfi_status sfi_select(const sfi_select_params *p, const int32_t *batch_ids, int32_t batch_n,
                       const int32_t *seq_len, int32_t B, int32_t H, int32_t max_seq_len,
                       const float *score, const float *key_norm, int32_t ld, int32_t *sel_idx,
                       int32_t *sel_count, float *fused_out, void *ws, size_t ws_bytes,
                       void *stream) {
-  if (!p || !seq_len || !score || !sel_idx || !sel_count) return SFI_ERR_NULL;
-  if (p->mode != SFI_SCORE_FUSED && p->mode != SFI_SCORE_RAW) return SFI_ERR_RANGE;
-  if (B < 1 || H < 1 || max_seq_len < 1) return SFI_ERR_SHAPE;
-  if (max_seq_len > kSelMaxLen) return SFI_ERR_UNSUPPORTED;
-  if (batch_n < 0 || batch_n > B) return SFI_ERR_RANGE;
-  if (ld < max_seq_len) return SFI_ERR_RANGE;
-  if (p->k < 1 || p->n_sink < 0 || p->window < 0) return SFI_ERR_RANGE;
-  const bool fused = p->mode == SFI_SCORE_FUSED;
-  if (fused) {
-    if (!key_norm) return SFI_ERR_NULL;
-    if (!(p->lambda >= 0.f && p->lambda <= 1.f)) return SFI_ERR_RANGE;
-    if (!(p->pos_tau > 0.f) || !(p->norm_coef == p->norm_coef)) return SFI_ERR_RANGE;
-  }
-  const SelWs w = select_ws(B, H, max_seq_len);
-  if (!ws) return SFI_ERR_NULL;
-  if (ws_bytes < w.total) return SFI_ERR_WORKSPACE;
-  if (batch_n == 0) return SFI_OK;
-
-  SelectLaunch a{};
-  a.mode = p->mode;
-  a.lambda = p->lambda; a.norm_coef = p->norm_coef; a.pos_tau = p->pos_tau;
-  a.n_sink = p->n_sink; a.window = p->window; a.k = p->k;
-  a.k_seq = p->k_per_seq;
-  a.batch_ids = batch_ids; a.batch_n = batch_n; a.seq_len = seq_len;
-  a.B = B; a.H = H; a.max_seq_len = max_seq_len;
-  a.score = score; a.key_norm = key_norm; a.ld = ld;
-  a.sel_idx = sel_idx; a.sel_count = sel_count;
-  a.fused_out = fused ? fused_out : nullptr;
-  a.fo_ld = ld;
-  a.ws.P = w.P;
-  a.ws.ghist = carve<uint32_t>(ws, w.ghist);
-  a.ws.cum = carve<uint16_t>(ws, w.cum);
-  a.ws.sorted = carve<unsigned long long>(ws, w.sorted);
-  a.ws.nsum = carve<double>(ws, w.nsum);
-  a.ws.wsum = carve<double>(ws, w.wsum);
-  a.ws.meta = carve<SelRowMeta>(ws, w.meta);
-  return launch_select(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SFI_OK : SFI_ERR_HIP;
+  return select_impl(p, batch_ids, batch_n, seq_len, B, H, max_seq_len, score, key_norm, ld, sel_idx,
+                     sel_count, fused_out, ws, ws_bytes, stream, false);
 }
 
 sfi_status sfi_fast_step(const sfi_kv *kv, const int32_t *batch_ids, int32_t batch_n,

@@ -80,6 +80,26 @@ __device__ __forceinline__ uint32_t float_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Prior weight of key j: exp(-norm_coef z_j) (1 + exp(-(t - j)/tau)) with
+// z_j = (nu_j - mu)/sd, as powers of two (cz = -norm_coef log2(e)/sd,
+// ct = log2(e)/tau, tq = t).  Every kernel that forms the weights or their
+// sum calls this one function, so sums and keys agree bit for bit.
+__device__ __forceinline__ float prior_w(float nu, int j, float muf, float cz, float tq, float ct) {
+  return exp2f(cz * (nu - muf)) * (1.0f + exp2f(((float)j - tq) * ct));
+}
+
+// Row constants of the prior from fp64 sums of the key norms over n keys:
+// muf = mean, cz = -norm_coef log2(e) / population std (0 when the std is 0).
+__device__ __forceinline__ void prior_consts(double s1, double s2, int n, float norm_coef, float *muf,
+                                             float *cz) {
+  const double mu = s1 / n;
+  const double var = fmax(s2 / n - mu * mu, 0.0);
+  const double sd = sqrt(var);
+  *muf = (float)mu;
+  const float isd = sd > 0.0 ? (float)(1.0 / sd) : 0.0f;
+  *cz = -norm_coef * isd * kLog2e;
+}
+
 __device__ __forceinline__ uint4 ldg16(const uint16_t *p) {
   return *reinterpret_cast<const uint4 *>(p);
 }

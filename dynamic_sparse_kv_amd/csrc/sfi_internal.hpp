@@ -40,6 +40,8 @@ SplitPlan plan_rows(long long L, int stride, long long R, int max_chunk);
 // Compute units of the current device (cached per device).
 int device_cu_count();
 
+struct SelRowMeta;
+
 struct AttnLaunch {
   KVView kv;
   const int32_t *seq_len;
@@ -64,6 +66,16 @@ struct AttnLaunch {
   const int32_t *sel_idx;
   const int32_t *sel_count;
   int sel_heads, sel_k, n_sink, window;
+  // The selector's prior, computed by a slow step for the selection that
+  // follows it (null nsum: not computed): per-split key-norm sums
+  // [B][Hkv][stride][2] (workspace), and the selector workspace's per-chunk
+  // prior-weight sums, row constants and bucket histograms it fills.
+  double *nsum;
+  float norm_coef, pos_tau;
+  double *sel_wsum;      // [B*Hkv][selP]
+  SelRowMeta *sel_meta;  // [B*Hkv]
+  uint32_t *sel_ghist;   // [B*Hkv][4096]
+  int selP;
 };
 
 hipError_t launch_slow(const AttnLaunch &a, hipStream_t st);
@@ -107,6 +119,7 @@ struct SelectLaunch {
   int32_t *sel_count;
   float *fused_out;   // [B][H][fo_ld] or null
   int fo_ld;
+  bool prior_done;    // the slow step already wrote wsum, meta and cleared ghist
   SelWork ws;
 };
 

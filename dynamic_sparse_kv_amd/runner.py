@@ -113,10 +113,12 @@ class SFIDecoder:
         self.ws_sel_bytes = sfi.sfi_select_workspace_bytes(B, Hkv, self.max_len)
         self.ws_fast_bytes = sfi.sfi_fast_workspace_bytes(self.kv, k, n_sink, window)
         self.ws_step_bytes = sfi.sfi_decode_step_workspace_bytes(self.kv, k, n_sink, window)
-        self.ws_slow = torch.empty(self.ws_slow_bytes, **u8)
-        self.ws_sel = torch.empty(self.ws_sel_bytes, **u8)
-        self.ws_fast = torch.empty(self.ws_fast_bytes, **u8)
-        self.ws_step = torch.empty(self.ws_step_bytes, **u8)
+        self.ws_slow = torch.zeros(self.ws_slow_bytes, **u8)
+        self.ws_sel = torch.zeros(self.ws_sel_bytes, **u8)
+        self.ws_fast = torch.zeros(self.ws_fast_bytes, **u8)
+        self.ws_step = torch.zeros(self.ws_step_bytes, **u8)
+        self.ws_stepsel_bytes = sfi.sfi_decode_step_select_workspace_bytes(self.kv, k, n_sink, window)
+        self.ws_stepsel = torch.zeros(self.ws_stepsel_bytes, **u8)
 
     # -- single calls -------------------------------------------------------
     def slow(self, q, seq_len, batch_ids, batch_n: int, stream=None, select: bool = True, out=None,
@@ -165,23 +167,43 @@ class SFIDecoder:
         if select and n_slow:
             self.slow_select_only(self.kv.seq_len, slow_ids, n_slow, stream, k_seq=k_seq)
 
+    def step_select(self, q, seq_len, slow_ids, n_slow: int, fast_ids, n_fast: int, stream=None,
+                    out=None, k_seq=None):
+        """One call for the step and the slow sequences' new selections
+        (sfi_decode_step_select): the slow step forms the selector's prior
+        statistics, so the selection runs only its key and pick passes."""
+        self.kv.seq_len = seq_len.data_ptr() if torch.is_tensor(seq_len) else seq_len
+        self.params.k_per_seq = None if k_seq is None else k_seq.data_ptr()
+        try:
+            sfi.sfi_decode_step_select(self.kv, self.params, slow_ids, n_slow, fast_ids, n_fast, q,
+                                       self.out if out is None else out, self.evidence, self.key_norm,
+                                       self.ld, self.sel_idx, self.sel_count, self.fused, self.ws_stepsel,
+                                       self.ws_stepsel_bytes, stream)
+        finally:
+            self.params.k_per_seq = None
+
     def _new_event(self):
         e = torch.cuda.Event()
         self._events.append(e)
         return e
 
     # -- one decode step of a planned run ------------------------------------
-    def step(self, plan: DecodePlan, s: int, q_steps, stream=None, out=None, co: bool = True):
+    def step(self, plan: DecodePlan, s: int, q_steps, stream=None, out=None, co: bool = True,
+             fused_select: bool = True):
         """Decode step s: q_steps is the device tensor [steps][B][Hq][d].
 
-        With co=True a step that has both slow and fast sequences runs them
-        in one co-launched pass (sfi_decode_step) before the selector;
-        otherwise the slow step, the selector and the fast step are separate
-        calls."""
+        With co=True a step that has slow sequences runs as one call that
+        co-launches its slow and fast shares and refreshes the slow
+        sequences' selections (sfi_decode_step_select; with
+        fused_select=False: sfi_decode_step, then sfi_select); with co=False
+        the slow step, the selector and the fast step are separate calls."""
         q = q_steps[s]
         sl = plan.seq_len[s]
         ks = None if plan.k_seq is None else plan.k_seq[s]
         ns, nf = int(plan.n_slow[s]), int(plan.n_fast[s])
+        if co and ns and fused_select:
+            self.step_select(q, sl, plan.slow_ids[s], ns, plan.fast_ids[s], nf, stream, out=out, k_seq=ks)
+            return
         if co and ns and nf:
             self.co_step(q, sl, plan.slow_ids[s], ns, plan.fast_ids[s], nf, stream, out=out, k_seq=ks)
             return
@@ -332,9 +354,9 @@ class VegasDecoder:
         self.ws_ver_bytes = sfi.sfi_verify_workspace_bytes(self.kv, T)
         self.ws_sel_bytes = sfi.sfi_select_workspace_bytes(B, 1, self.max_len)
         self.ws_fast_bytes = sfi.sfi_fast_workspace_bytes(self.kv, k, n_sink, window)
-        self.ws_ver = torch.empty(self.ws_ver_bytes, **u8)
-        self.ws_sel = torch.empty(self.ws_sel_bytes, **u8)
-        self.ws_fast = torch.empty(self.ws_fast_bytes, **u8)
+        self.ws_ver = torch.zeros(self.ws_ver_bytes, **u8)
+        self.ws_sel = torch.zeros(self.ws_sel_bytes, **u8)
+        self.ws_fast = torch.zeros(self.ws_fast_bytes, **u8)
 
     def verify(self, q_rows, seq_len, row_mask: int, batch_ids=None, batch_n=None, stream=None):
         """q_rows [B][T][Hq][d] bf16; seq_len counts the T verified rows."""

@@ -85,6 +85,11 @@ def lib():
         L.sfi_decode_step.argtypes = [P(sfi_kv), _vp, _c_int, _vp, _c_int, _vp, _vp, _vp, _vp, _c_int,
                                       _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _sz, _vp]
         L.sfi_decode_step.restype = _c_int
+        L.sfi_decode_step_select_workspace_bytes.argtypes = [P(sfi_kv), _c_int, _c_int, _c_int]
+        L.sfi_decode_step_select_workspace_bytes.restype = _sz
+        L.sfi_decode_step_select.argtypes = [P(sfi_kv), P(sfi_select_params), _vp, _c_int, _vp, _c_int,
+                                             _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _vp, _vp, _sz, _vp]
+        L.sfi_decode_step_select.restype = _c_int
         L.sfi_verify_aggregate.argtypes = [P(sfi_kv), _vp, _c_int, _vp, _c_int, ctypes.c_uint32, _vp,
                                            _vp, _c_int, _vp, _sz, _vp]
         L.sfi_verify_aggregate.restype = _c_int
@@ -214,6 +219,20 @@ def sfi_decode_step(kv: sfi_kv, slow_ids, n_slow: int, fast_ids, n_fast: int, q,
                                  _ptr(q), _ptr(out), _ptr(evidence), _ptr(key_norm), ld, _ptr(sel_idx),
                                  _ptr(sel_count), sel_heads, sel_k, n_sink, window, _ptr(ws), ws_bytes,
                                  _stream(stream)), "sfi_decode_step")
+
+
+def sfi_decode_step_select_workspace_bytes(kv: sfi_kv, sel_k: int, n_sink: int, window: int) -> int:
+    return lib().sfi_decode_step_select_workspace_bytes(ctypes.byref(kv), sel_k, n_sink, window)
+
+
+def sfi_decode_step_select(kv: sfi_kv, p: sfi_select_params, slow_ids, n_slow: int, fast_ids,
+                           n_fast: int, q, out, evidence, key_norm, ld: int, sel_idx, sel_count,
+                           fused_out, ws, ws_bytes: int, stream=None):
+    _check(lib().sfi_decode_step_select(ctypes.byref(kv), ctypes.byref(p), _ptr(slow_ids), n_slow,
+                                        _ptr(fast_ids), n_fast, _ptr(q), _ptr(out), _ptr(evidence),
+                                        _ptr(key_norm), ld, _ptr(sel_idx), _ptr(sel_count),
+                                        _ptr(fused_out), _ptr(ws), ws_bytes, _stream(stream)),
+           "sfi_decode_step_select")
 
 
 def sfi_verify_aggregate(kv: sfi_kv, batch_ids, batch_n: int, q, T: int, row_mask: int, out, agg,

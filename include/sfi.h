@@ -188,6 +188,31 @@ sfi_status sfi_decode_step(const sfi_kv *kv, const int32_t *slow_ids, int32_t n_
                            int32_t n_sink, int32_t window, void *ws, size_t ws_bytes,
                            void *stream);
 
+/* A decode step followed by the refresh of the slow sequences' selections
+ * [SFI 3.A: a slow step refreshes the selected memory; 3.B: the selector runs
+ * on the slow step's evidence and the cache statistics]: the outputs of
+ * sfi_decode_step on slow_ids / fast_ids (per-head index lists of capacity
+ * p->k, n_sink = p->n_sink, window = p->window), then the selections of
+ * sfi_select (FUSED) for slow_ids written to sel_idx / sel_count.  The slow
+ * step also forms the selector's prior statistics (key-norm mean and std,
+ * prior-weight sums) while it has the key norms at hand, so the selection
+ * starts at its key pass; results equal those of the separate calls up to
+ * floating-point rounding (near-tie keys may differ).
+ *   p           FUSED parameters (RAW -> SFI_ERR_RANGE); p->k_per_seq allowed.
+ *   evidence, key_norm  required when n_slow > 0 ([B][Hkv][ld]).
+ *   sel_idx, sel_count  read for fast_ids, written for slow_ids (disjoint).
+ *   fused_out   [B][Hkv][ld] or NULL: the fused scores s of slow_ids.
+ *   ws          sfi_decode_step_select_workspace_bytes(kv, p->k, p->n_sink,
+ *               p->window) bytes.
+ * Errors: as sfi_decode_step and sfi_select. */
+size_t sfi_decode_step_select_workspace_bytes(const sfi_kv *kv, int32_t sel_k, int32_t n_sink,
+                                              int32_t window);
+sfi_status sfi_decode_step_select(const sfi_kv *kv, const sfi_select_params *p,
+                                  const int32_t *slow_ids, int32_t n_slow, const int32_t *fast_ids,
+                                  int32_t n_fast, const uint16_t *q, float *out, float *evidence,
+                                  float *key_norm, int32_t ld, int32_t *sel_idx, int32_t *sel_count,
+                                  float *fused_out, void *ws, size_t ws_bytes, void *stream);
+
 /* Verification with aggregated logits [Vegas 2, 2.A, 2.B, 3]: T query rows
  * per sequence; row t sits at position n - T + t (n = seq_len[b], which
  * already counts the T rows) and attends keys [0, n - T + t].

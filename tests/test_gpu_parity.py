@@ -119,7 +119,7 @@ def _select_gpu(mode, score, key_norm, lens, k, n_sink, window, lam=0.3, H=None,
     cnt = torch.full((B, H), -7, dtype=torch.int32, device=DEV)
     fo = torch.zeros((B, H, ld), dtype=torch.float32, device=DEV) if fused else None
     wsb = sfi.sfi_select_workspace_bytes(B, H, max_len)
-    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
     sfi.sfi_select(p, None, B, seq, B, H, max_len, score, key_norm, ld, sel, cnt, fo, ws, wsb)
     torch.cuda.synchronize()
     return sel.cpu().numpy(), cnt.cpu().numpy(), (fo.cpu().numpy() if fused else None)
@@ -174,7 +174,7 @@ def test_select_per_sequence_k():
     sel = torch.full((B, H, kcap), -7, dtype=torch.int32, device=DEV)
     cnt = torch.full((B, H), -7, dtype=torch.int32, device=DEV)
     wsb = sfi.sfi_select_workspace_bytes(B, H, max(lens))
-    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
     sfi.sfi_select(p, None, B, seq, B, H, max(lens), torch.from_numpy(sc).to(DEV), None, ld, sel, cnt,
                    None, ws, wsb)
     torch.cuda.synchronize()
@@ -253,7 +253,7 @@ def _fast_gpu(K, V, Hq, q, lens, sel_np, cnt_np, n_sink, window, sel_heads):
     sel_k = sel.shape[2]
     out = torch.full((B, Hq, K.shape[3]), 9.0, device=DEV)
     wsb = sfi.sfi_fast_workspace_bytes(kv, sel_k, n_sink, window)
-    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
     sfi.sfi_fast_step(kv, None, B, q, sel, cnt, sel_heads, sel_k, n_sink, window, out, ws, wsb)
     torch.cuda.synchronize()
     return out.cpu().numpy()
@@ -507,6 +507,64 @@ def test_decode_run_mixed_batch_co_launch():
                     ties += check_selection(sel[g], cnt[g], r["s"][g], r["lo"], r["hi"], cfg.k)
     _say(f"  near-tie differences over the run: {ties}")
     assert ties == 0
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_decode_step_select_matches_separate_calls(paged):
+    """sfi_decode_step_select (one call: co-launched step + the slow
+    sequences' selections, prior statistics formed by the slow step) against
+    sfi_decode_step + sfi_select and the oracle, with a per-sequence k."""
+    _say(f"decode step + select, paged={paged}")
+    B, Hq, Hkv, d = 4, 32, 8, 128
+    lens = [6100, 4500, 7000, 2600]
+    cap = 7100
+    K, V = _rand_kv(B, Hkv, cap, d, seed=61, hh=30)
+    q = _rand_q((B, Hq, d), seed=62)
+    seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    kseq = torch.tensor([300, 120, 300, 64], dtype=torch.int32, device=DEV)
+    kw = dict(n_sink=4, window=256, k=300, lam=0.3)
+    if paged:
+        cfg = W.CONFIGS["c5"].replace(B=B, Hq=Hq, Hkv=Hkv, d=d)
+        table, npages = W.page_table(cfg, np.full(B, cap))
+        Kp, Vp = W.to_paged(K, table, npages, 16), W.to_paged(V, table, npages, 16)
+        tab = torch.from_numpy(table).to(DEV)
+        mk = lambda: SFIDecoder(Kp, Vp, Hq, cap, page_table=tab, page_size=16, **kw)
+    else:
+        mk = lambda: SFIDecoder(K, V, Hq, cap, **kw)
+    fused, sep = mk(), mk()
+    all_ids = torch.arange(B, dtype=torch.int32, device=DEV)
+    # step A: every sequence slow (slow-only call); step B: 1 and 3 slow, 0 and 2 fast
+    for dec, f in ((fused, True), (sep, False)):
+        if f:
+            dec.step_select(q, seq, all_ids, B, None, 0, k_seq=kseq)
+        else:
+            dec.slow(q, seq, all_ids, B, k_seq=kseq)
+    torch.cuda.synchronize()
+    for t in ("out", "evidence", "key_norm"):
+        assert torch.equal(getattr(fused, t).view(torch.int32), getattr(sep, t).view(torch.int32)), t
+    slow_ids = torch.tensor([1, 3], dtype=torch.int32, device=DEV)
+    fast_ids = torch.tensor([0, 2], dtype=torch.int32, device=DEV)
+    seq2 = seq + 5
+    fused.step_select(q, seq2, slow_ids, 2, fast_ids, 2, k_seq=kseq)
+    sep.co_step(q, seq2, slow_ids, 2, fast_ids, 2, k_seq=kseq)
+    torch.cuda.synchronize()
+    # slow sequences: identical kernels; fast ones read the step-A selections,
+    # which may differ only in near-tie keys
+    for b in (1, 3):
+        assert torch.equal(fused.out[b].view(torch.int32), sep.out[b].view(torch.int32))
+    assert row_rel_err(fused.out.cpu().numpy(), sep.out.cpu().numpy()) <= OUT_TOL
+    Kb, Vb, qb = _bits(K), _bits(V), _bits(q)
+    sel, cnt = fused.sel_idx.cpu().numpy(), fused.sel_count.cpu().numpy()
+    ties = 0
+    for b in range(B):
+        n = lens[b] + 5
+        kb = int(kseq[b])
+        r = O.slow_select(qb[b], Kb[b], Vb[b], n if b in (1, 3) else lens[b], lam=0.3, k=kb,
+                          n_sink=4, window=256)
+        for g in range(Hkv):
+            ties += check_selection(sel[b, g, :kb], cnt[b, g], r["s"][g], r["lo"], r["hi"], kb)
+            assert np.all(sel[b, g, kb:] == -1)
+    _say(f"  near-tie differences: {ties}")
 
 
 # ------------------------------------------------------------------- verify
