@@ -137,24 +137,20 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
 
   const int b = batch_seq(a.batch_ids, zb, a.B);
   if (b < 0) return;
-  const int n = clamp_len(a.seq_len, b, a.max_len);
   const int tid = threadIdx.x;
-
-  int L = n;
-  FastList fl;
-  if constexpr (MODE == MODE_FAST) {
-    fl = fast_list(a.sel_idx, a.sel_count, a.sel_heads, a.sel_k, a.n_sink, a.window, b, g, n);
-    L = fl.length();
-  }
   const int p0 = split * a.chunk;
-  if (p0 >= L) return;
-  const int p1 = min(L, p0 + a.chunk);
-
   const int sub = tid % LPR;
   const int rg = tid / LPR;
   // element offset in the row of this lane's c-th 16-byte slice
   auto slice = [&](int c) { return SFI_LINE_MAJOR ? c * LPR * 8 + sub * 8 : sub * DPL + 8 * c; };
 
+  // Loads that need only the sequence id go out before the sequence length
+  // and the list length are known, so they share one round trip with them:
+  // the query slices and, for the fast step, the chunk's index entries at the
+  // positions they take when the fixed part (sinks + window) is full, which
+  // is every sequence longer than n_sink + window; a shorter sequence loads
+  // them again below.  Entries are clamped to the list's row (sel_k), so every
+  // load stays inside it; entries past the list's length are never used.
   uint32_t qv[G][4 * NV];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -164,19 +160,45 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
       qv[h][4 * c + 0] = t.x; qv[h][4 * c + 1] = t.y; qv[h][4 * c + 2] = t.z; qv[h][4 * c + 3] = t.w;
     }
   }
+  constexpr int IPT = (MODE == MODE_FAST) ? kMaxFastChunk / kThreads : 1;
+  int jv[IPT];
+  const int nfix_full = a.n_sink + a.window;
+  if constexpr (MODE == MODE_FAST) {
+    const int32_t *srow =
+        a.sel_idx + ((size_t)b * a.sel_heads + (a.sel_heads == 1 ? 0 : g)) * a.sel_k;
+#pragma unroll
+    for (int i = 0; i < IPT; ++i)
+      jv[i] = (a.sel_k > 0) ? srow[min(max(p0 + tid + i * kThreads - nfix_full, 0), a.sel_k - 1)] : -1;
+  }
+
+  const int n = clamp_len(a.seq_len, b, a.max_len);
+  int L = n;
+  FastList fl;
+  if constexpr (MODE == MODE_FAST) {
+    fl = fast_list(a.sel_idx, a.sel_count, a.sel_heads, a.sel_k, a.n_sink, a.window, b, g, n);
+    L = fl.length();
+  }
+  if (p0 >= L) {
+    // no rows here: a neutral partial (Z = 0), so the finalize can merge
+    // every planned split without reading the list length
+    if (tid < G) {
+      const size_t slot = ((size_t)b * a.Hq + g * G + tid) * a.stride + split;
+      a.part_ml[slot * 2 + 0] = kNegBig;
+      a.part_ml[slot * 2 + 1] = 0.f;
+    }
+    return;
+  }
+  const int p1 = min(L, p0 + a.chunk);
 
   if constexpr (MODE == MODE_FAST) {
     // Every list entry of the chunk is loaded before any is stored, so the
     // index loads are in flight together (one round trip instead of one per
-    // 256 entries).  A load for a sink or window position reads a valid slot
-    // of the list (it has at least one) and is not used.
-    constexpr int IPT = kMaxFastChunk / kThreads;
+    // 256 entries).
     const int nfix = fl.ns + fl.nw;
-    int jv[IPT];
+    if (nfix != nfix_full) {  // short sequence: the fixed part is shorter
 #pragma unroll
-    for (int i = 0; i < IPT; ++i) {
-      const int p = p0 + tid + i * kThreads;
-      jv[i] = fl.sel[min(max(p - nfix, 0), max(fl.cnt - 1, 0))];
+      for (int i = 0; i < IPT; ++i)
+        jv[i] = (fl.cnt > 0) ? fl.sel[min(max(p0 + tid + i * kThreads - nfix, 0), fl.cnt - 1)] : -1;
     }
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
@@ -479,6 +501,7 @@ struct FinalArgs {
   const int32_t *batch_ids;
   int Hq, Hkv;
   int chunk, stride;
+  int splits;  // planned splits per (sequence, kv head); unused ones hold Z = 0
   const float *part_o;
   const float *part_ml;
   float *out;
@@ -517,19 +540,14 @@ __device__ __forceinline__ void finalize_body(const FinalArgs &a, int x, int g, 
 
   const int b = batch_seq(a.batch_ids, zb, a.B);
   if (b < 0) return;
-  const int n = clamp_len(a.seq_len, b, a.max_len);
-  int L = n;
-  if constexpr (MODE == MODE_FAST) {
-    L = fast_list(a.sel_idx, a.sel_count, a.sel_heads, a.sel_k, a.n_sink, a.window, b, g, n)
-            .length();
-  }
   const bool comb = x < G;
-  if (!comb && (x - G) * kEvidChunk >= n) return;
-  const int S = (L + a.chunk - 1) / a.chunk;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const size_t hbase = (size_t)b * a.Hq + (size_t)g * G;
 
   if (comb) {
+    // every planned split: those past the row list wrote Z = 0 and are
+    // skipped, so no length is read before the partials
+    const int S = a.splits;
     // PARTS groups of D/4 threads; group `part` merges partials part,
     // part + PARTS, ... (four at a time, their loads in flight together)
     // into a running (m, z, o); the groups are then merged through LDS.
@@ -553,7 +571,7 @@ __device__ __forceinline__ void finalize_body(const FinalArgs &a, int x, int g, 
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (s0 + i * PARTS < S) {
+        if (s0 + i * PARTS < S && zs[i] > 0.f) {
           const float mn = fmaxf(m, ms[i]);
           const float c = exp2f(m - mn), w = exp2f(ms[i] - mn);
           z = z * c + zs[i] * w;
@@ -597,6 +615,9 @@ __device__ __forceinline__ void finalize_body(const FinalArgs &a, int x, int g, 
   }
 
   if constexpr (EVID) {
+    const int n = clamp_len(a.seq_len, b, a.max_len);
+    if ((x - G) * kEvidChunk >= n) return;
+    const int S = (n + a.chunk - 1) / a.chunk;
     const size_t lrow = (size_t)b * a.Hkv + g;
     const int j0 = (x - G) * kEvidChunk;
     const int j1 = min(n, j0 + kEvidChunk);
@@ -773,7 +794,8 @@ FinalArgs final_args(const AttnLaunch &a) {
   FinalArgs f{};
   f.B = a.B; f.max_len = a.max_len;
   f.seq_len = a.seq_len; f.batch_ids = a.batch_ids; f.Hq = a.Hq; f.Hkv = a.Hkv;
-  f.chunk = a.plan.chunk; f.stride = a.plan.stride; f.part_o = a.part_o; f.part_ml = a.part_ml;
+  f.chunk = a.plan.chunk; f.stride = a.plan.stride; f.splits = a.plan.splits;
+  f.part_o = a.part_o; f.part_ml = a.part_ml;
   f.out = a.out; f.logits = a.logits; f.lld = a.lld; f.evidence = a.evidence; f.ld = a.ld;
   f.sel_idx = a.sel_idx; f.sel_count = a.sel_count; f.sel_heads = a.sel_heads;
   f.sel_k = a.sel_k; f.n_sink = a.n_sink; f.window = a.window;

@@ -307,6 +307,30 @@ def test_fast_full_selection_equals_dense_and_shared_list():
         assert row_rel_err(out[b], o_ref) <= OUT_TOL
 
 
+def test_fast_without_selection_list():
+    """sel_k = 0 with no index buffer (the boundary allows it): the fast set
+    is sinks + window only, including a sequence shorter than both."""
+    _say("fast step, sel_k = 0")
+    B, Hq, Hkv, d = 3, 32, 8, 128
+    lens = [3000, 700, 150]
+    K, V = _rand_kv(B, Hkv, 3000, d, seed=79)
+    q = _rand_q((B, Hq, d), seed=80)
+    ns, win = 4, 256
+    seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    kv = sfi.make_kv(K, V, seq, Hq, max(lens))
+    cnt = torch.zeros((B, Hkv), dtype=torch.int32, device=DEV)
+    out = torch.full((B, Hq, d), 9.0, device=DEV)
+    wsb = sfi.sfi_fast_workspace_bytes(kv, 0, ns, win)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
+    sfi.sfi_fast_step(kv, None, B, q, None, cnt, Hkv, 0, ns, win, out, ws, wsb)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    Kb, Vb, qb = _bits(K), _bits(V), _bits(q)
+    for b in range(B):
+        o_ref = O.fast_step(qb[b], Kb[b], Vb[b], lens[b], [[]] * Hkv, ns, win)
+        assert row_rel_err(out[b], o_ref) <= OUT_TOL
+
+
 # ------------------------------------------------------------ whole decode run
 
 def test_decode_run_tiny_config_every_step():
