@@ -29,8 +29,12 @@
 namespace sfi {
 namespace {
 
+// Rows per lane group and pipeline stage (0: LPR / 8, i.e. 8 rows per wave
+// per stage whatever the lane-group width; measured faster than 16 at the
+// 32K and 128K G = 4 shapes, whose workgroups then start consuming sooner
+// and finish with a shorter last stage).
 #ifndef SFI_DECODE_U
-#define SFI_DECODE_U 2
+#define SFI_DECODE_U 0
 #endif
 // Fast-step launch shape (rows per stage, lanes per row; 0 = the automatic
 // choice) and lanes per row for dense/slow steps.
@@ -123,7 +127,8 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
   constexpr int DPL = D / LPR;         // dims per lane (8 or 16)
   constexpr int NV = DPL / 8;          // 16-byte slices per row per lane
   constexpr int RPB = kThreads / LPR;  // rows per workgroup instruction
-  constexpr int U = (MODE == MODE_FAST) ? SFI_FAST_U : SFI_DECODE_U;  // rows per lane group per stage
+  constexpr int U_SET = (MODE == MODE_FAST) ? SFI_FAST_U : SFI_DECODE_U;
+  constexpr int U = U_SET > 0 ? U_SET : LPR / 8;  // rows per lane group per stage
   constexpr int NW = kThreads / 64;
   // Lazy rescaling: the running reference m only moves when a logit exceeds
   // it by more than kSlack (log2 units), so p = 2^(l - m) stays <= 2^kSlack.
