@@ -830,7 +830,7 @@ hipError_t slow_t(const AttnLaunch &a_in, hipStream_t st) {
     // gets the same split plan and therefore the same bits
     const int slots = side ? resident_slots<partial_kernel<D, G, false, MODE_SLOW, true>>()
                            : resident_slots<partial_kernel<D, G, false, MODE_SLOW, false>>();
-    a.plan = plan_splits(a.max_len, a.batch_n * a.Hkv, slots, a.plan.stride, 1 << 30);
+    a.plan = plan_splits(a.max_len, a.batch_n * a.Hkv, slots, a.plan.stride, kMaxSlowChunk, true);
   }
   const PartialArgs p = partial_args<D>(a);
   dim3 grid(a.plan.splits, a.Hkv, a.batch_n);
@@ -855,7 +855,7 @@ hipError_t fast_t(const AttnLaunch &a_in, hipStream_t st) {
   AttnLaunch a = a_in;
   {
     const int slots = resident_slots<partial_kernel<D, G, false, MODE_FAST, false>>();
-    a.plan = plan_splits(fast_rows(a), a.batch_n * a.Hkv, slots, a.plan.stride, kMaxFastChunk);
+    a.plan = plan_splits(fast_rows(a), a.batch_n * a.Hkv, slots, a.plan.stride, kMaxFastChunk, false);
   }
   const PartialArgs p = partial_args<D>(a);
   dim3 grid(a.plan.splits, a.Hkv, a.batch_n);
@@ -883,7 +883,7 @@ hipError_t step_t(const AttnLaunch &sa_in, const AttnLaunch &fa_in, hipStream_t 
     const int s_stride = sa.plan.stride, f_stride = fa.plan.stride;
     // workgroups of the combined grid at R rows per workgroup (non-increasing in R)
     auto plan_at = [&](long long R) {
-      sa.plan = plan_rows(Ls, s_stride, R, 1 << 30);
+      sa.plan = plan_rows(Ls, s_stride, R, kMaxSlowChunk);
       fa.plan = plan_rows(Lf, f_stride, R, kMaxFastChunk);
       return ps * sa.plan.splits + pf * fa.plan.splits;
     };
@@ -964,7 +964,7 @@ int device_cu_count() {
   return cus[dev];
 }
 
-SplitPlan plan_splits(long long L, int pairs, int slots, int stride, int max_chunk) {
+SplitPlan plan_splits(long long L, int pairs, int slots, int stride, int max_chunk, bool whole_waves) {
   SplitPlan pl{};
   if (L < 1) L = 1;
   if (pairs < 1) pairs = 1;
@@ -975,6 +975,16 @@ SplitPlan plan_splits(long long L, int pairs, int slots, int stride, int max_chu
   if (want < 1) want = 1;
   long long chunk = (L + want - 1) / want;
   chunk = (chunk + kSplitGranule - 1) / kSplitGranule * kSplitGranule;
+  if (chunk > max_chunk && whole_waves) {
+    // more splits than one wave of workgroups holds: take whole waves (for
+    // dense streams a wave plus a small tail of capped workgroups measured
+    // slower than two full waves), then the chunk that spreads L over them
+    const long long need = (L + max_chunk - 1) / max_chunk;
+    const long long waves = (need + want - 1) / want;
+    long long sp = std::min<long long>(waves * want, stride);
+    chunk = (L + sp - 1) / sp;
+    chunk = (chunk + kSplitGranule - 1) / kSplitGranule * kSplitGranule;
+  }
   if (chunk > max_chunk) chunk = max_chunk;
   long long splits = (L + chunk - 1) / chunk;
   if (splits > stride) {  // cannot happen for strides from split_stride(), kept as a guard

@@ -14,6 +14,15 @@ namespace sfi {
 constexpr int kSplitGranule = 32;
 constexpr int kMaxSplits = 512;
 constexpr int kMaxFastChunk = 1024;  // fast-step chunks stage their row ids in LDS
+// Rows per workgroup of a dense or slow step at most.  Splits are planned
+// from the longest sequence of the batch (its lengths are on the device), so
+// without a cap a long sequence in a ragged batch gets a few huge chunks
+// while the short ones' workgroups exit at once; capped, it takes more
+// workgroups, which the dispatcher runs in further waves.
+#ifndef SFI_MAX_SLOW_CHUNK
+#define SFI_MAX_SLOW_CHUNK 8192
+#endif
+constexpr int kMaxSlowChunk = SFI_MAX_SLOW_CHUNK;
 // Keys per workgroup of the evidence pass.
 constexpr int kEvidChunk = 2048;
 
@@ -32,8 +41,9 @@ inline int split_stride(long long L) {
 }
 
 // Chunking of L rows per pair over `pairs` pairs so that one launch fills
-// `slots` resident workgroups once, within the stride and a chunk cap.
-SplitPlan plan_splits(long long L, int pairs, int slots, int stride, int max_chunk);
+// `slots` resident workgroups once, within the stride and a chunk cap; with
+// whole_waves, a capped plan takes a whole number of such waves.
+SplitPlan plan_splits(long long L, int pairs, int slots, int stride, int max_chunk, bool whole_waves);
 // Chunking of L rows with about R rows per workgroup (multiple of the granule).
 SplitPlan plan_rows(long long L, int stride, long long R, int max_chunk);
 
