@@ -331,10 +331,22 @@ def leg_stack128k(timed_steps=24, dense_steps=4):
             for layer in range(cfg.layers):
                 decs[layer].step(plan, s, qs[layer], st)
 
-    _log("[bench] stack32-128k: timing graph replay")
-    t_total, g = _graph_time(run, side, stream)
+    def run_pipe(st):
+        # each layer's selection runs inside the next layer's grids (the last
+        # layer's inside the next step's first layer), one flush at the end
+        pend = None
+        for s in range(1, steps):
+            for layer in range(cfg.layers):
+                pend = decs[layer].layer_step(plan, s, qs[layer], pending=pend, stream=st)
+        sfi.sfi_run_deferred(pend, st)
+
+    _log("[bench] stack32-128k: timing graph replay (selections pipelined across layers)")
+    t_total, g = _graph_time(run_pipe, side, stream)
     del g
     value = cfg.B * timed_steps / t_total
+    _log("[bench] stack32-128k: timing graph replay (selection after each layer)")
+    t_layer, g = _graph_time(run, side, stream)
+    del g
 
     timer = _CallTimer(dev, stream)
     for s in range(1, steps):
@@ -376,8 +388,12 @@ def leg_stack128k(timed_steps=24, dense_steps=4):
                        f"ctx {cfg.ctx}, fast state {cfg.n_sink}+{cfg.window}+{cfg.k}, lambda {cfg.lam}, "
                        f"{timed_steps} decode steps after a first all-slow step",
            "tokens_per_s": round(value, 1), "ms_per_step": round(t_total / timed_steps * 1e3, 4),
+           "tokens_per_s_selection_per_layer": round(cfg.B * timed_steps / t_layer, 1),
            "slow_fraction": round(float(plan.slow[1:].mean()), 4),
-           "timing": "hip graph replay, one stream; per_call: eager, cold, layers 0 and 16",
+           "timing": "hip graph replay, one stream; tokens_per_s with each layer's selection run inside "
+                     "the next layer's grids (sfi_decode_layer_step), tokens_per_s_selection_per_layer "
+                     "with it after each layer (sfi_decode_step_select); per_call: eager, cold, layers 0 "
+                     "and 16",
            "per_call": per_call, "dense_tokens_per_s": round(dense_tps, 2),
            "speedup_vs_dense": round(value / dense_tps, 2)}
     del decs, qs

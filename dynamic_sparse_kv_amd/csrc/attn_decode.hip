@@ -25,6 +25,7 @@
 #include <type_traits>
 
 #include "sfi_internal.hpp"
+#include "select_body.hpp"
 
 namespace sfi {
 namespace {
@@ -485,11 +486,27 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialArgs a) {
 // Slow (dense with evidence) and fast shares of one decode step in a single
 // grid: linear blocks [0, ns) are the slow grid (s_splits x Hkv x slow
 // sequences), the rest the fast grid.  The two sets of sequences are
-// disjoint, so nothing orders one share after the other.
-template <int D, int G, bool PAGED>
+// disjoint, so nothing orders one share after the other.  With PEND the grid
+// ends with np workgroups of another layer's pending selection (its key
+// pass, chunk-major over (chunk, head row, batch entry)): a selection that
+// reads only that layer's buffers, so it shares the grid with this step.
+// Placed last, its latency-bound workgroups start as the attention
+// workgroups finish and fill the wave's tail (placed first, they took the
+// attention's slots and serialised: workgroups of one kernel all get the
+// attention's register allocation).
+template <int D, int G, bool PAGED, bool PEND>
 __global__ __launch_bounds__(kThreads) void copartial_kernel(PartialArgs s, PartialArgs f, int s_splits,
-                                                             int f_splits, int Hkv, int ns) {
+                                                             int f_splits, int Hkv, int ns,
+                                                             SelectLaunch pend, int np) {
   int id = blockIdx.x;
+  if constexpr (PEND) {
+    const int nt = gridDim.x - np;
+    if (id >= nt) {
+      id -= nt;
+      keys_body<true>(pend, id % pend.ws.P, (id / pend.ws.P) % pend.H, id / (pend.ws.P * pend.H));
+      return;
+    }
+  }
   if (id < ns) {
     partial_body<D, G, PAGED, MODE_SLOW, true, true>(s, id % s_splits, (id / s_splits) % Hkv,
                                                      id / (s_splits * Hkv));
@@ -752,11 +769,20 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(FinalArgs a) {
 }
 
 // Slow and fast finalize blocks of one decode step in a single grid (layout
-// as in copartial_kernel: s_gx x Hkv x slow sequences, then the fast grid).
-template <int D, int G>
+// as in copartial_kernel: s_gx x Hkv x slow sequences, then the fast grid);
+// with PEND it ends with the pending selection's pick pass.
+template <int D, int G, bool PEND>
 __global__ __launch_bounds__(kThreads) void cofinal_kernel(FinalArgs s, FinalArgs f, int s_gx, int f_gx,
-                                                           int Hkv, int ns) {
+                                                           int Hkv, int ns, SelectLaunch pend, int np) {
   int id = blockIdx.x;
+  if constexpr (PEND) {
+    const int nt = gridDim.x - np;
+    if (id >= nt) {
+      id -= nt;
+      pick_body(pend, id % pend.ws.P, (id / pend.ws.P) % pend.H, id / (pend.ws.P * pend.H));
+      return;
+    }
+  }
   if (id < ns) {
     finalize_body<D, G, MODE_SLOW, true>(s, id % s_gx, (id / s_gx) % Hkv, id / (s_gx * Hkv));
   } else {
@@ -874,10 +900,17 @@ hipError_t fast_t(const AttnLaunch &a_in, hipStream_t st) {
 // of the combined grid carry about equal bytes and the grid fills the
 // resident slots about once.
 template <int D, int G, bool PAGED>
-hipError_t step_t(const AttnLaunch &sa_in, const AttnLaunch &fa_in, hipStream_t st) {
+hipError_t step_t(const AttnLaunch &sa_in, const AttnLaunch &fa_in, hipStream_t st,
+                  const SelectLaunch *pend) {
   AttnLaunch sa = sa_in, fa = fa_in;
-  {
-    const int slots = resident_slots<copartial_kernel<D, G, false>>();
+  const int slots = resident_slots<copartial_kernel<D, G, false, false>>();
+  if (sa.batch_n == 0) {  // fast share only (a step that carries a pending selection)
+    fa.plan = plan_splits(fast_rows(fa), fa.batch_n * fa.Hkv, slots, fa.plan.stride, kMaxFastChunk, false);
+    sa.plan = SplitPlan{1, 0, sa.plan.stride};
+  } else if (fa.batch_n == 0) {  // slow share only
+    sa.plan = plan_splits(sa.max_len, sa.batch_n * sa.Hkv, slots, sa.plan.stride, kMaxSlowChunk, true);
+    fa.plan = SplitPlan{1, 0, fa.plan.stride};
+  } else {
     const long long Ls = sa.max_len, Lf = fast_rows(fa);
     const long long ps = (long long)sa.batch_n * sa.Hkv, pf = (long long)fa.batch_n * fa.Hkv;
     const int s_stride = sa.plan.stride, f_stride = fa.plan.stride;
@@ -920,15 +953,28 @@ hipError_t step_t(const AttnLaunch &sa_in, const AttnLaunch &fa_in, hipStream_t 
   }
   const int ns = sa.plan.splits * sa.Hkv * sa.batch_n;
   const int nf = fa.plan.splits * fa.Hkv * fa.batch_n;
-  hipLaunchKernelGGL((copartial_kernel<D, G, PAGED>), dim3(ns + nf), dim3(kThreads), 0, st,
-                     partial_args<D>(sa), partial_args<D>(fa), sa.plan.splits, fa.plan.splits, sa.Hkv, ns);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const int sgx = slow_final_blocks(sa, G);
   const int ms = sgx * sa.Hkv * sa.batch_n;
   const int mf = G * fa.Hkv * fa.batch_n;
-  hipLaunchKernelGGL((cofinal_kernel<D, G>), dim3(ms + mf), dim3(kThreads), 0, st, final_args(sa),
-                     final_args(fa), sgx, G, sa.Hkv, ms);
+  const PartialArgs ps = partial_args<D>(sa), pf = partial_args<D>(fa);
+  const FinalArgs fs = final_args(sa), ff = final_args(fa);
+  hipError_t e;
+  if (pend) {
+    const int np = pend->ws.P * pend->H * pend->batch_n;
+    hipLaunchKernelGGL((copartial_kernel<D, G, PAGED, true>), dim3(np + ns + nf), dim3(kThreads), 0, st, ps,
+                       pf, sa.plan.splits, fa.plan.splits, sa.Hkv, ns, *pend, np);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((cofinal_kernel<D, G, true>), dim3(np + ms + mf), dim3(kThreads), 0, st, fs, ff, sgx,
+                       G, sa.Hkv, ms, *pend, np);
+    return hipGetLastError();
+  }
+  if (ns + nf > 0) {
+    hipLaunchKernelGGL((copartial_kernel<D, G, PAGED, false>), dim3(ns + nf), dim3(kThreads), 0, st, ps, pf,
+                       sa.plan.splits, fa.plan.splits, sa.Hkv, ns, SelectLaunch{}, 0);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((cofinal_kernel<D, G, false>), dim3(ms + mf), dim3(kThreads), 0, st, fs, ff, sgx, G,
+                       sa.Hkv, ms, SelectLaunch{}, 0);
+  }
   return hipGetLastError();
 }
 
@@ -1016,19 +1062,19 @@ SplitPlan plan_rows(long long L, int stride, long long R, int max_chunk) {
 }
 
 hipError_t launch_slow(const AttnLaunch &a, hipStream_t st) { SFI_DISPATCH(slow_t, a, st); }
-hipError_t launch_step(const AttnLaunch &sa, const AttnLaunch &fa, hipStream_t st) {
+hipError_t launch_step(const AttnLaunch &sa, const AttnLaunch &fa, hipStream_t st, const SelectLaunch *pend) {
   const bool pg = sa.paged;
   switch (sa.d * 16 + sa.G) {
-    case 64 * 16 + 1: return pg ? step_t<64, 1, true>(sa, fa, st) : step_t<64, 1, false>(sa, fa, st);
-    case 64 * 16 + 2: return pg ? step_t<64, 2, true>(sa, fa, st) : step_t<64, 2, false>(sa, fa, st);
-    case 64 * 16 + 4: return pg ? step_t<64, 4, true>(sa, fa, st) : step_t<64, 4, false>(sa, fa, st);
-    case 64 * 16 + 5: return pg ? step_t<64, 5, true>(sa, fa, st) : step_t<64, 5, false>(sa, fa, st);
-    case 64 * 16 + 8: return pg ? step_t<64, 8, true>(sa, fa, st) : step_t<64, 8, false>(sa, fa, st);
-    case 128 * 16 + 1: return pg ? step_t<128, 1, true>(sa, fa, st) : step_t<128, 1, false>(sa, fa, st);
-    case 128 * 16 + 2: return pg ? step_t<128, 2, true>(sa, fa, st) : step_t<128, 2, false>(sa, fa, st);
-    case 128 * 16 + 4: return pg ? step_t<128, 4, true>(sa, fa, st) : step_t<128, 4, false>(sa, fa, st);
-    case 128 * 16 + 5: return pg ? step_t<128, 5, true>(sa, fa, st) : step_t<128, 5, false>(sa, fa, st);
-    case 128 * 16 + 8: return pg ? step_t<128, 8, true>(sa, fa, st) : step_t<128, 8, false>(sa, fa, st);
+    case 64 * 16 + 1: return pg ? step_t<64, 1, true>(sa, fa, st, pend) : step_t<64, 1, false>(sa, fa, st, pend);
+    case 64 * 16 + 2: return pg ? step_t<64, 2, true>(sa, fa, st, pend) : step_t<64, 2, false>(sa, fa, st, pend);
+    case 64 * 16 + 4: return pg ? step_t<64, 4, true>(sa, fa, st, pend) : step_t<64, 4, false>(sa, fa, st, pend);
+    case 64 * 16 + 5: return pg ? step_t<64, 5, true>(sa, fa, st, pend) : step_t<64, 5, false>(sa, fa, st, pend);
+    case 64 * 16 + 8: return pg ? step_t<64, 8, true>(sa, fa, st, pend) : step_t<64, 8, false>(sa, fa, st, pend);
+    case 128 * 16 + 1: return pg ? step_t<128, 1, true>(sa, fa, st, pend) : step_t<128, 1, false>(sa, fa, st, pend);
+    case 128 * 16 + 2: return pg ? step_t<128, 2, true>(sa, fa, st, pend) : step_t<128, 2, false>(sa, fa, st, pend);
+    case 128 * 16 + 4: return pg ? step_t<128, 4, true>(sa, fa, st, pend) : step_t<128, 4, false>(sa, fa, st, pend);
+    case 128 * 16 + 5: return pg ? step_t<128, 5, true>(sa, fa, st, pend) : step_t<128, 5, false>(sa, fa, st, pend);
+    case 128 * 16 + 8: return pg ? step_t<128, 8, true>(sa, fa, st, pend) : step_t<128, 8, false>(sa, fa, st, pend);
     default: return hipErrorInvalidValue;
   }
 }

@@ -39,134 +39,16 @@
 // Integer atomics only build histograms and reserve bucket slots, and every
 // floating-point sum runs in a fixed order, so results are bitwise
 // repeatable (the order of keys inside a bucket does not affect any result).
-#include "sfi_internal.hpp"
+#include "select_body.hpp"
 
 namespace sfi {
 namespace {
-
-constexpr int kT = 256;                 // threads of a chunk workgroup
-constexpr int kTW = kT / 64;
-constexpr int kCH = kSelChunk;          // keys per chunk
-constexpr int kQuarter = kCH / 2;       // keys per half chunk (4 per thread)
-constexpr int kPT = kCH / kT;           // keys per thread
-constexpr int kD1 = 12;                 // bucket: key bits 31..20
-constexpr int kBins1 = 1 << kD1;
-constexpr int kBPT = kBins1 / kT;       // buckets per thread
-constexpr int kD2 = 11;                 // digit width inside the bucket
-constexpr int kBins2 = 1 << kD2;
-constexpr int kCandLds = 4096;          // bucket candidates gathered into LDS
-constexpr int kCPT = kSelMaxChunks / kT;  // chunks per thread in the pick scans
-static_assert(kQuarter == 4 * kT, "a half chunk is four keys per thread");
-static_assert(kBPT == 16, "sixteen buckets per thread");
-static_assert(kCH <= 65535, "cumulative bucket counts are 16-bit");
-
-template <int NW>
-__device__ __forceinline__ double block_sum_d(double x, double *s_red) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
-  if (lane == 0) s_red[wv] = x;
-  __syncthreads();
-  double t = 0.0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) t += s_red[w];
-  __syncthreads();
-  return t;
-}
-
-// Exclusive prefix sum over the workgroup in thread order; *total = sum.
-template <int NW>
-__device__ __forceinline__ int block_exscan(int v, int *s_wave, int *total) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
-  if (lane == 63) s_wave[wv] = x;
-  __syncthreads();
-  int base = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const int t = s_wave[w];
-    base += (w < wv) ? t : 0;
-    tot += t;
-  }
-  __syncthreads();
-  *total = tot;
-  return base + x - v;
-}
-
-// Row of the selector handled by this workgroup, and its geometry.
-// Candidates are [lo, hi); nch chunks hold them (0 when the range is empty).
-struct RowGeo {
-  int b, h, n, lo, hi, span, nch;
-  size_t row;
-};
-
-__device__ __forceinline__ bool row_geo(const SelectLaunch &a, RowGeo &r) {
-  r.b = batch_seq(a.batch_ids, blockIdx.z, a.B);
-  if (r.b < 0) return false;
-  r.h = blockIdx.y;
-  r.n = clamp_len(a.seq_len, r.b, a.max_seq_len);
-  r.lo = a.n_sink;
-  r.hi = max(a.n_sink, r.n - a.window);
-  r.span = (a.mode == 0) ? r.n : r.hi;  // keys [0, span) are visited
-  r.nch = (r.hi > r.lo) ? (r.hi + kCH - 1) / kCH : 0;
-  r.row = (size_t)r.b * a.H + r.h;
-  return true;
-}
-
-// Key i of thread t in a chunk sits at j0 + (i / 4) * kQuarter + 4 t + i % 4.
-__device__ __forceinline__ int key_pos(int j0, int i) {
-  return j0 + (i >> 2) * kQuarter + 4 * (int)threadIdx.x + (i & 3);
-}
-
-// Values [j0, j0 + kCH) of a row restricted to [0, span) (0 outside).  The
-// half-chunk cases are uniform across the workgroup, so no load sits behind a
-// per-lane branch: a whole half in range takes one 16-byte load per thread.
-// Requires j0 < span.
-__device__ __forceinline__ void load_chunk(const float *p, int j0, int span, bool vec,
-                                           float (&x)[kPT]) {
-#pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
-    const int base = j0 + hf * kQuarter;
-    const int j = base + 4 * (int)threadIdx.x;
-    if (vec && base + kQuarter <= span) {
-      const float4 t = *reinterpret_cast<const float4 *>(p + j);
-      x[4 * hf + 0] = t.x; x[4 * hf + 1] = t.y; x[4 * hf + 2] = t.z; x[4 * hf + 3] = t.w;
-    } else if (base >= span) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[4 * hf + e] = 0.f;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float t = p[min(j + e, span - 1)];
-        x[4 * hf + e] = (j + e < span) ? t : 0.f;
-      }
-    }
-  }
-}
-
-__device__ __forceinline__ bool aligned16(const void *p) {
-  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
-}
-
-// Composite rank value: larger key first, then lower index.
-__device__ __forceinline__ unsigned long long composite(uint32_t key, int j) {
-  return ((unsigned long long)key << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)j);
-}
-
-__device__ __forceinline__ int composite_index(unsigned long long c) {
-  return (int)(0xFFFFFFFFu - (uint32_t)(c & 0xFFFFFFFFull));
-}
 
 // ---------------------------------------------------------------- 1. sums
 __global__ __launch_bounds__(kT) void norm_sums_kernel(SelectLaunch a) {
   __shared__ double s_red[kTW];
   RowGeo r;
-  if (!row_geo(a, r)) return;
+  if (!row_geo(a, blockIdx.y, blockIdx.z, r)) return;
   const int p = blockIdx.x, j0 = p * kCH;
   if (j0 >= r.n) return;
   const float *nu = a.key_norm + r.row * a.ld;
@@ -191,7 +73,7 @@ template <bool FUSED>
 __global__ __launch_bounds__(kT) void prior_kernel(SelectLaunch a) {
   __shared__ double s_red[kTW];
   RowGeo r;
-  if (!row_geo(a, r)) return;
+  if (!row_geo(a, blockIdx.y, blockIdx.z, r)) return;
   const int p = blockIdx.x, j0 = p * kCH;
   const int tid = threadIdx.x;
   // clear the row histogram (striped over all chunk workgroups) for step 3
@@ -234,352 +116,12 @@ __global__ __launch_bounds__(kT) void prior_kernel(SelectLaunch a) {
 // --------------------------------------------------------------- 3. keys
 template <bool FUSED>
 __global__ __launch_bounds__(kT) void keys_kernel(SelectLaunch a) {
-  __shared__ unsigned hist[kBins1];
-  __shared__ unsigned long long s_sorted[kCH];
-  __shared__ double s_red[kTW];
-  __shared__ int s_wave[kTW];
-  RowGeo r;
-  if (!row_geo(a, r)) return;
-  const int p = blockIdx.x, j0 = p * kCH;
-  if (j0 >= r.span) return;
-  const int tid = threadIdx.x;
-
-  float s[kPT];
-  if constexpr (FUSED) {
-    const float *f = a.score + r.row * a.ld;
-    const float *nu = a.key_norm + r.row * a.ld;
-    const bool vec = aligned16(f) && aligned16(nu) && (a.ld & 3) == 0;
-    float fv[kPT], nv[kPT];
-    load_chunk(f, j0, r.n, vec, fv);
-    load_chunk(nu, j0, r.n, vec, nv);
-    const int Pn = (r.n + kCH - 1) / kCH;
-    double W = 0.0;
-    for (int q = tid; q < Pn; q += kT) W += a.ws.wsum[r.row * a.ws.P + q];
-    for (int i = tid; i < kBins1; i += kT) hist[i] = 0u;
-    W = block_sum_d<kTW>(W, s_red);
-    const float cf = 1.0f - a.lambda;
-    const float cr = W > 0.0 ? (float)((double)a.lambda / W) : 0.f;
-    const float muf = a.ws.meta[r.row].muf, cz = a.ws.meta[r.row].cz;
-    const float ct = kLog2e / a.pos_tau;
-    const float tq = (float)(r.n - 1);
-#pragma unroll
-    for (int i = 0; i < kPT; ++i) {
-      const int j = key_pos(j0, i);
-      const float w = (j < r.n) ? prior_w(nv[i], j, muf, cz, tq, ct) : 0.f;
-      s[i] = fmaf(cf, fv[i], cr * w);
-    }
-    if (a.fused_out) {
-      float *fo = a.fused_out + r.row * a.fo_ld;
-#pragma unroll
-      for (int i = 0; i < kPT; ++i) {
-        const int j = key_pos(j0, i);
-        if (j < r.n) fo[j] = s[i];
-      }
-    }
-  } else {
-    const float *sc = a.score + r.row * a.ld;
-    load_chunk(sc, j0, r.span, aligned16(sc) && (a.ld & 3) == 0, s);
-    for (int i = tid; i < kBins1; i += kT) hist[i] = 0u;
-    __syncthreads();
-  }
-  if (p >= r.nch) return;  // no candidates in this chunk
-
-  uint32_t key[kPT];
-#pragma unroll
-  for (int i = 0; i < kPT; ++i) {
-    const int j = key_pos(j0, i);
-    key[i] = (j >= r.lo && j < r.hi) ? float_key(s[i]) : 0u;
-    if (key[i]) atomicAdd(&hist[key[i] >> (32 - kD1)], 1u);
-  }
-  __syncthreads();
-  // Cumulative counts in descending bucket order: cum[b] = keys in buckets
-  // >= b.  Thread t owns buckets 16 t .. 16 t + 15.
-  uint32_t c[kBPT];
-  int tot = 0;
-#pragma unroll
-  for (int i = 0; i < kBPT; ++i) {
-    c[i] = hist[kBPT * tid + i];
-    tot += (int)c[i];
-  }
-  int total;
-  const int below = block_exscan<kTW>(tot, s_wave, &total);  // keys in lower buckets
-  int run = total - below - tot;                              // keys in higher buckets
-  uint32_t cum[kBPT];
-#pragma unroll
-  for (int i = kBPT - 1; i >= 0; --i) {
-    run += (int)c[i];
-    cum[i] = (uint32_t)run;
-  }
-  // bucket b's first slot in the descending layout is cum[b] - count[b]
-#pragma unroll
-  for (int i = 0; i < kBPT; ++i) hist[kBPT * tid + i] = cum[i] - c[i];
-  uint4 *cd = reinterpret_cast<uint4 *>(a.ws.cum + (r.row * a.ws.P + p) * kBins1 + kBPT * tid);
-  cd[0] = make_uint4(cum[0] | cum[1] << 16, cum[2] | cum[3] << 16, cum[4] | cum[5] << 16,
-                     cum[6] | cum[7] << 16);
-  cd[1] = make_uint4(cum[8] | cum[9] << 16, cum[10] | cum[11] << 16, cum[12] | cum[13] << 16,
-                     cum[14] | cum[15] << 16);
-  uint32_t *h1 = a.ws.ghist + r.row * kBins1 + kBPT * tid;
-#pragma unroll
-  for (int i = 0; i < kBPT; ++i)
-    if (c[i]) atomicAdd(&h1[i], c[i]);
-  __syncthreads();
-  // bucket sort in LDS, then one coalesced write of the chunk's sorted run
-#pragma unroll
-  for (int i = 0; i < kPT; ++i) {
-    if (key[i]) {
-      const unsigned slot = atomicAdd(&hist[key[i] >> (32 - kD1)], 1u);
-      s_sorted[slot] = composite(key[i], key_pos(j0, i));
-    }
-  }
-  __syncthreads();
-  unsigned long long *so = a.ws.sorted + (r.row * a.ws.P + p) * kCH;
-  for (int i = tid; i < total; i += kT) so[i] = s_sorted[i];
-}
-
-// Bin of an nb-bin histogram (nb <= kBins2, highest bin = largest values)
-// holding the want-th largest element: s_res = {bin, rank inside it, count}.
-// s_res must hold a default before the call; the call ends with a barrier.
-__device__ __forceinline__ void find_bin_desc(const unsigned *hist, int nb, int want, int *s_wave,
-                                              int *s_res) {
-  const int t = threadIdx.x;
-  constexpr int BPT = kBins2 / kT;
-  const int top = nb - 1 - BPT * t;
-  int cnt = 0;
-#pragma unroll
-  for (int i = 0; i < BPT; ++i) cnt += (top - i >= 0) ? (int)hist[top - i] : 0;
-  int total;
-  const int above = block_exscan<kTW>(cnt, s_wave, &total);
-  if (top >= 0 && above < want && want <= above + cnt) {
-    int acc = above;
-    for (int i = 0; i < BPT && top - i >= 0; ++i) {
-      const int c = (int)hist[top - i];
-      if (acc + c >= want) {
-        s_res[0] = top - i;
-        s_res[1] = want - acc;
-        s_res[2] = c;
-        break;
-      }
-      acc += c;
-    }
-  }
-  __syncthreads();
-}
-
-// Cumulative bucket count cum[b] (keys in buckets >= b) of chunk q; 0 for b
-// past the last bucket.
-__device__ __forceinline__ int cum_at(const SelectLaunch &a, size_t row, int q, int b) {
-  return b < kBins1 ? (int)a.ws.cum[(row * a.ws.P + q) * kBins1 + b] : 0;
+  keys_body<FUSED>(a, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // ----------------------------------------------------------- 4. pick
 __global__ __launch_bounds__(kT) void pick_kernel(SelectLaunch a) {
-  __shared__ unsigned h2[kBins2];
-  __shared__ unsigned long long s_cand[kCandLds];
-  __shared__ int s_above[kSelMaxChunks];   // winners above the bucket, per chunk
-  __shared__ int s_toff[kSelMaxChunks + 1];  // bucket candidates before each chunk
-  __shared__ int s_tw[kSelMaxChunks];      // bucket winners per chunk
-  __shared__ unsigned s_bits[kCH / 32];
-  __shared__ int s_wave[kTW];
-  __shared__ int s_res[3];
-  RowGeo r;
-  if (!row_geo(a, r)) return;
-  const int p = blockIdx.x, tid = threadIdx.x;
-  if (p >= max(r.nch, 1)) return;
-  const int Kcap = a.k;  // row stride of the index lists
-  const int K = a.k_seq ? min(max(a.k_seq[r.b], 0), Kcap) : Kcap;
-  int32_t *out = a.sel_idx + r.row * Kcap;
-  const unsigned long long *srow = a.ws.sorted + r.row * a.ws.P * kCH;
-
-  // this chunk's bucket-sorted composites (slots past its candidates unused)
-  unsigned long long own[kPT];
-#pragma unroll
-  for (int i = 0; i < kPT; ++i) own[i] = (p < r.nch) ? srow[p * kCH + tid + kT * i] : 0ull;
-
-  // 1. Bucket b1 holding the K-th largest key; thread t holds buckets
-  //    16 t .. 16 t + 15 of the row histogram.
-  uint32_t hb[kBPT];
-  {
-    const uint4 *hp = reinterpret_cast<const uint4 *>(a.ws.ghist + r.row * kBins1 + kBPT * tid);
-#pragma unroll
-    for (int i = 0; i < kBPT / 4; ++i) {
-      const uint4 v = hp[i];
-      hb[4 * i] = v.x; hb[4 * i + 1] = v.y; hb[4 * i + 2] = v.z; hb[4 * i + 3] = v.w;
-    }
-  }
-  int cnt = 0;
-#pragma unroll
-  for (int i = 0; i < kBPT; ++i) cnt += (int)hb[i];
-  int total;
-  const int below = block_exscan<kTW>(cnt, s_wave, &total);
-  if (tid == 0) {
-    s_res[0] = 0;  // b1 = 0: every candidate wins (candidate keys never sit in bucket 0)
-    s_res[1] = 0;
-    s_res[2] = 0;
-  }
-  __syncthreads();
-  const int above = total - below - cnt;
-  if (total > K && above < K && K <= above + cnt) {
-    int acc = above;
-    for (int i = kBPT - 1; i >= 0; --i) {
-      const int c = (int)hb[i];
-      if (acc + c >= K) {
-        s_res[0] = kBPT * tid + i;
-        s_res[1] = K - acc;
-        s_res[2] = c;
-        break;
-      }
-      acc += c;
-    }
-  }
-  __syncthreads();
-  const int b1 = s_res[0];
-  const int want1 = s_res[1];
-  const int m = s_res[2];
-  const bool split = b1 != 0 && want1 < m;  // only part of bucket b1 wins
-
-  // 2. Per chunk: winners above the bucket (a prefix of its sorted run) and
-  //    its run of bucket-b1 keys.  Thread t handles chunks kCPT t ...
-  int na[kCPT], nt[kCPT];
-  int tsum = 0;
-#pragma unroll
-  for (int i = 0; i < kCPT; ++i) {
-    const int q = kCPT * tid + i;
-    na[i] = nt[i] = 0;
-    if (q < r.nch) {
-      if (b1 == 0) {
-        na[i] = cum_at(a, r.row, q, 0);
-      } else if (split) {
-        na[i] = cum_at(a, r.row, q, b1 + 1);
-        nt[i] = cum_at(a, r.row, q, b1) - na[i];
-      } else {
-        na[i] = cum_at(a, r.row, q, b1);
-      }
-      s_above[q] = na[i];
-    }
-    tsum += nt[i];
-  }
-  int mtot;
-  int toff = block_exscan<kTW>(tsum, s_wave, &mtot);
-#pragma unroll
-  for (int i = 0; i < kCPT; ++i) {
-    const int q = kCPT * tid + i;
-    if (q < r.nch) {
-      s_toff[q] = toff;
-      s_tw[q] = 0;
-    }
-    toff += nt[i];
-  }
-  if (tid == 0) s_toff[r.nch] = mtot;
-  __syncthreads();
-
-  // 3. Radix select of the want1-th largest composite among the m bucket-b1
-  //    keys; their top 12 bits all equal b1 and 11-bit digits cover bits
-  //    51..0.  Bucket keys win iff their composite >= T.
-  unsigned long long T = 0ull;
-  if (split) {
-    const bool in_lds = mtot <= kCandLds;
-    // i-th bucket key of the row, in chunk order
-    auto cand_at = [&](int i) -> unsigned long long {
-      int lo = 0, hi = r.nch - 1;
-      while (lo < hi) {  // last chunk q with s_toff[q] <= i
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_toff[mid] <= i) lo = mid;
-        else hi = mid - 1;
-      }
-      return srow[lo * kCH + s_above[lo] + (i - s_toff[lo])];
-    };
-    if (in_lds) {
-      for (int i = tid; i < mtot; i += kT) s_cand[i] = cand_at(i);
-      __syncthreads();
-    }
-    auto cand = [&](int i) { return in_lds ? s_cand[i] : cand_at(i); };
-    unsigned long long prefix = (unsigned long long)b1;
-    int top = 51, want = want1;
-    for (;;) {
-      const int lo_bit = max(top - kD2 + 1, 0);
-      const int width = top - lo_bit + 1;
-      const unsigned long long dmask = (1ull << width) - 1ull;
-      for (int i = tid; i < (1 << width); i += kT) h2[i] = 0u;
-      if (tid == 0) {
-        s_res[0] = 0;
-        s_res[1] = 1;
-        s_res[2] = 0;
-      }
-      __syncthreads();
-      for (int i = tid; i < mtot; i += kT) {
-        const unsigned long long c = cand(i);
-        if ((c >> (top + 1)) == prefix) atomicAdd(&h2[(c >> lo_bit) & dmask], 1u);
-      }
-      __syncthreads();
-      find_bin_desc(h2, 1 << width, want, s_wave, s_res);
-      const int bin = s_res[0];
-      want = s_res[1];
-      const int c = s_res[2];
-      __syncthreads();
-      prefix = (prefix << width) | (unsigned long long)bin;
-      if (lo_bit == 0 || want == c) {  // the whole sub-bin is taken
-        T = prefix << lo_bit;
-        break;
-      }
-      top = lo_bit - 1;
-    }
-    // bucket winners per chunk (the chunk is the key index / chunk size)
-    for (int i = tid; i < mtot; i += kT) {
-      const unsigned long long c = cand(i);
-      if (c >= T) atomicAdd(&s_tw[min(composite_index(c) / kCH, r.nch - 1)], 1);
-    }
-    __syncthreads();
-  }
-
-  // 4. Output offset of this chunk (winners of the chunks before it) and
-  //    the row's winner count.
-  int wb = 0, wt = 0;
-#pragma unroll
-  for (int i = 0; i < kCPT; ++i) {
-    const int q = kCPT * tid + i;
-    if (q < r.nch) {
-      const int w = s_above[q] + s_tw[q];
-      wt += w;
-      wb += (q < p) ? w : 0;
-    }
-  }
-  int before, total_w;
-  block_exscan<kTW>(wb, s_wave, &before);
-  block_exscan<kTW>(wt, s_wave, &total_w);
-  const int count = min(total_w, K);
-
-  // 5. This chunk's winners, ascending, through a 2048-bit bitmap.
-  if (p < r.nch) {
-    if (tid < kCH / 32) s_bits[tid] = 0u;
-    __syncthreads();
-    const int na_p = s_above[p];
-    const int ne_p = split ? s_toff[p + 1] - s_toff[p] : 0;
-#pragma unroll
-    for (int i = 0; i < kPT; ++i) {
-      const int slot = tid + kT * i;
-      const bool w = slot < na_p || (slot < na_p + ne_p && own[i] >= T);
-      if (w) {
-        const int jl = composite_index(own[i]) - p * kCH;
-        if (jl >= 0 && jl < kCH) atomicOr(&s_bits[jl >> 5], 1u << (jl & 31));
-      }
-    }
-    __syncthreads();
-    // thread t owns bits 8 t .. 8 t + 7
-    const uint32_t byte = (s_bits[tid >> 2] >> (8 * (tid & 3))) & 0xFFu;
-    int tot8;
-    int o = before + block_exscan<kTW>(__popc(byte), s_wave, &tot8);
-    for (int e = 0; e < 8; ++e) {
-      if (byte & (1u << e)) {
-        if (o < K) out[o] = p * kCH + 8 * tid + e;
-        ++o;
-      }
-    }
-  }
-  // 6. The last chunk's workgroup pads the list and writes its length.
-  if (p == max(r.nch, 1) - 1) {
-    if (tid == 0) a.sel_count[r.row] = count;
-    for (int i = count + tid; i < Kcap; i += kT) out[i] = -1;
-  }
+  pick_body(a, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 }  // namespace

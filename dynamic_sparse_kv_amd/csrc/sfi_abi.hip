@@ -133,11 +133,12 @@ T *carve(void *ws, size_t off) {
   return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
 }
 
-sfi_status select_impl(const sfi_select_params *p, const int32_t *batch_ids, int32_t batch_n,
-                      const int32_t *seq_len, int32_t B, int32_t H, int32_t max_seq_len,
-                      const float *score, const float *key_norm, int32_t ld, int32_t *sel_idx,
-                      int32_t *sel_count, float *fused_out, void *ws, size_t ws_bytes,
-                      void *stream, bool prior_done) {
+// Validated launch description of a selection (nothing is launched).
+sfi_status select_launch(const sfi_select_params *p, const int32_t *batch_ids, int32_t batch_n,
+                         const int32_t *seq_len, int32_t B, int32_t H, int32_t max_seq_len,
+                         const float *score, const float *key_norm, int32_t ld, int32_t *sel_idx,
+                         int32_t *sel_count, float *fused_out, void *ws, size_t ws_bytes,
+                         bool prior_done, SelectLaunch *out) {
   if (!p || !seq_len || !score || !sel_idx || !sel_count) return SFI_ERR_NULL;
   if (p->mode != SFI_SCORE_FUSED && p->mode != SFI_SCORE_RAW) return SFI_ERR_RANGE;
   if (B < 1 || H < 1 || max_seq_len < 1) return SFI_ERR_SHAPE;
@@ -154,9 +155,9 @@ sfi_status select_impl(const sfi_select_params *p, const int32_t *batch_ids, int
   const SelWs w = select_ws(B, H, max_seq_len);
   if (!ws) return SFI_ERR_NULL;
   if (ws_bytes < w.total) return SFI_ERR_WORKSPACE;
-  if (batch_n == 0) return SFI_OK;
 
-  SelectLaunch a{};
+  SelectLaunch &a = *out;
+  a = SelectLaunch{};
   a.mode = p->mode;
   a.lambda = p->lambda; a.norm_coef = p->norm_coef; a.pos_tau = p->pos_tau;
   a.n_sink = p->n_sink; a.window = p->window; a.k = p->k;
@@ -175,7 +176,26 @@ sfi_status select_impl(const sfi_select_params *p, const int32_t *batch_ids, int
   a.ws.nsum = carve<double>(ws, w.nsum);
   a.ws.wsum = carve<double>(ws, w.wsum);
   a.ws.meta = carve<SelRowMeta>(ws, w.meta);
+  return SFI_OK;
+}
+
+sfi_status select_impl(const sfi_select_params *p, const int32_t *batch_ids, int32_t batch_n,
+                      const int32_t *seq_len, int32_t B, int32_t H, int32_t max_seq_len,
+                      const float *score, const float *key_norm, int32_t ld, int32_t *sel_idx,
+                      int32_t *sel_count, float *fused_out, void *ws, size_t ws_bytes,
+                      void *stream, bool prior_done) {
+  SelectLaunch a;
+  const sfi_status s = select_launch(p, batch_ids, batch_n, seq_len, B, H, max_seq_len, score, key_norm,
+                                     ld, sel_idx, sel_count, fused_out, ws, ws_bytes, prior_done, &a);
+  if (s != SFI_OK || batch_n == 0) return s;
   return launch_select(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SFI_OK : SFI_ERR_HIP;
+}
+
+// Launch description of a deferred selection (its slow step formed the prior).
+sfi_status deferred_launch(const sfi_deferred *d, SelectLaunch *out) {
+  return select_launch(&d->params, d->batch_ids, d->batch_n, d->seq_len, d->B, d->H, d->max_seq_len,
+                       d->evidence, d->key_norm, d->ld, d->sel_idx, d->sel_count, d->fused_out, d->ws,
+                       d->ws_bytes, true, out);
 }
 
 AttnLaunch slow_launch(const sfi_kv *kv, const KVView &view, bool paged, const SlowWs &w, void *ws,
@@ -390,6 +410,115 @@ sfi_status sfi_decode_step_select(const sfi_kv *kv, const sfi_select_params *p,
   if (n_slow == 0) return SFI_OK;
   return select_impl(p, slow_ids, n_slow, kv->seq_len, kv->B, kv->Hkv, kv->max_seq_len, evidence,
                      key_norm, ld, sel_idx, sel_count, fused_out, ws_sel, ew.total, stream, true);
+}
+
+sfi_status sfi_decode_layer_step(const sfi_kv *kv, const sfi_select_params *p, const int32_t *slow_ids,
+                                 int32_t n_slow, const int32_t *fast_ids, int32_t n_fast,
+                                 const uint16_t *q, float *out, float *evidence, float *key_norm,
+                                 int32_t ld, int32_t *sel_idx, int32_t *sel_count, float *fused_out,
+                                 void *ws, size_t ws_bytes, const sfi_deferred *pending,
+                                 sfi_deferred *defer, void *stream) {
+  const bool pend_on = pending && pending->active;
+  if (!pend_on && !defer)  // the plain combined call
+    return sfi_decode_step_select(kv, p, slow_ids, n_slow, fast_ids, n_fast, q, out, evidence, key_norm,
+                                  ld, sel_idx, sel_count, fused_out, ws, ws_bytes, stream);
+  KVView view;
+  bool paged = false;
+  sfi_status s = check_kv(kv, &view, &paged);
+  if (s != SFI_OK) return s;
+  if (!p) return SFI_ERR_NULL;
+  if (p->mode != SFI_SCORE_FUSED) return SFI_ERR_RANGE;
+  if (!(p->lambda >= 0.f && p->lambda <= 1.f)) return SFI_ERR_RANGE;
+  if (!(p->pos_tau > 0.f) || !(p->norm_coef == p->norm_coef)) return SFI_ERR_RANGE;
+  if (p->k < 1 || p->n_sink < 0 || p->window < 0) return SFI_ERR_RANGE;
+  if (kv->max_seq_len > kSelMaxLen) return SFI_ERR_UNSUPPORTED;
+  if ((s = check_batch(kv, n_slow)) != SFI_OK) return s;
+  if ((s = check_batch(kv, n_fast)) != SFI_OK) return s;
+  if (n_slow + n_fast > kv->B) return SFI_ERR_RANGE;
+  if (!q || !out || !sel_idx || !sel_count) return SFI_ERR_NULL;
+  if (n_slow > 0 && (!evidence || !key_norm)) return SFI_ERR_NULL;
+  if (n_slow > 0 && ld < kv->max_seq_len) return SFI_ERR_RANGE;
+  if (n_fast > 0 &&
+      (s = check_fast(kv, sel_idx, sel_count, kv->Hkv, p->k, p->n_sink, p->window)) != SFI_OK)
+    return s;
+  const SlowWs sw = slow_ws(kv);
+  const FastWs fw = fast_ws(kv, p->k, p->n_sink, p->window);
+  const SelWs ew = select_ws(kv->B, kv->Hkv, kv->max_seq_len);
+  const size_t nsum_bytes = align_up((size_t)kv->B * kv->Hkv * sw.stride * 2 * sizeof(double));
+  if (!ws) return SFI_ERR_NULL;
+  if (ws_bytes < sw.total + fw.total + ew.total + nsum_bytes) return SFI_ERR_WORKSPACE;
+  char *base = static_cast<char *>(ws);
+  void *ws_fast = base + sw.total;
+  void *ws_sel = base + sw.total + fw.total;
+  SelectLaunch pend;
+  if (pend_on) {
+    // the pending selection belongs to other buffers (another layer's)
+    if (pending->ws == ws_sel || pending->sel_idx == sel_idx || pending->evidence == evidence)
+      return SFI_ERR_RANGE;
+    if ((s = deferred_launch(pending, &pend)) != SFI_OK) return s;
+    if (pend.mode != SFI_SCORE_FUSED) return SFI_ERR_RANGE;
+  }
+  const bool pend_run = pend_on && pending->batch_n > 0;
+  // this call's own selection (validated before anything is launched)
+  sfi_deferred own{};
+  if (n_slow > 0) {
+    own.active = 1;
+    own.params = *p;
+    own.batch_ids = slow_ids;
+    own.batch_n = n_slow;
+    own.seq_len = kv->seq_len;
+    own.B = kv->B;
+    own.H = kv->Hkv;
+    own.max_seq_len = kv->max_seq_len;
+    own.evidence = evidence;
+    own.key_norm = key_norm;
+    own.ld = ld;
+    own.sel_idx = sel_idx;
+    own.sel_count = sel_count;
+    own.fused_out = fused_out;
+    own.ws = ws_sel;
+    own.ws_bytes = ew.total;
+    SelectLaunch chk;
+    if ((s = deferred_launch(&own, &chk)) != SFI_OK) return s;
+  }
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (n_slow + n_fast > 0 || pend_run) {
+    double *nsum = reinterpret_cast<double *>(base + sw.total + fw.total + ew.total);
+    AttnLaunch sa = slow_launch(kv, view, paged, sw, ws, slow_ids, n_slow, q, out, evidence, key_norm, ld);
+    sa.nsum = nsum;
+    sa.norm_coef = p->norm_coef;
+    sa.pos_tau = p->pos_tau;
+    sa.sel_wsum = carve<double>(ws_sel, ew.wsum);
+    sa.sel_meta = carve<SelRowMeta>(ws_sel, ew.meta);
+    sa.sel_ghist = carve<uint32_t>(ws_sel, ew.ghist);
+    sa.selP = ew.P;
+    const AttnLaunch fa = fast_launch(kv, view, paged, fw, ws_fast, fast_ids, n_fast, q, out, sel_idx,
+                                      sel_count, kv->Hkv, p->k, p->n_sink, p->window);
+    hipError_t e;
+    if (pend_run) e = launch_step(sa, fa, st, &pend);
+    else if (n_fast == 0) e = launch_slow(sa, st);
+    else if (n_slow == 0) e = launch_fast(fa, st);
+    else e = launch_step(sa, fa, st);
+    if (e != hipSuccess) return SFI_ERR_HIP;
+  }
+  if (defer) {
+    *defer = own;
+    return SFI_OK;
+  }
+  if (n_slow == 0) return SFI_OK;
+  SelectLaunch a;
+  if ((s = deferred_launch(&own, &a)) != SFI_OK) return s;
+  return launch_select(a, st) == hipSuccess ? SFI_OK : SFI_ERR_HIP;
+}
+
+sfi_status sfi_run_deferred(const sfi_deferred *d, void *stream) {
+  if (!d) return SFI_ERR_NULL;
+  if (!d->active || d->batch_n == 0) return SFI_OK;
+  SelectLaunch a;
+  const sfi_status s = deferred_launch(d, &a);
+  if (s != SFI_OK) return s;
+  if (a.mode != SFI_SCORE_FUSED) return SFI_ERR_RANGE;
+  return launch_select(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SFI_OK : SFI_ERR_HIP;
 }
 
 sfi_status sfi_select(const sfi_select_params *p, const int32_t *batch_ids, int32_t batch_n,

@@ -90,8 +90,13 @@ struct AttnLaunch {
 
 hipError_t launch_slow(const AttnLaunch &a, hipStream_t st);
 hipError_t launch_fast(const AttnLaunch &a, hipStream_t st);
-// Slow step with evidence (sa) and fast step (fa) on disjoint sequences, co-launched.
-hipError_t launch_step(const AttnLaunch &sa, const AttnLaunch &fa, hipStream_t st);
+struct SelectLaunch;
+// Slow step with evidence (sa) and fast step (fa) on disjoint sequences,
+// co-launched; either share may be empty.  A non-null pend is a selection
+// of other buffers (another layer's, its prior already formed by its slow
+// step) whose key and pick passes run in this step's two grids.
+hipError_t launch_step(const AttnLaunch &sa, const AttnLaunch &fa, hipStream_t st,
+                       const SelectLaunch *pend = nullptr);
 
 constexpr int kSelChunk = 2048;       // keys per selector chunk workgroup
 constexpr int kSelMaxChunks = 1024;   // chunks per row

@@ -182,6 +182,26 @@ class SFIDecoder:
         finally:
             self.params.k_per_seq = None
 
+    def layer_step(self, plan: "DecodePlan", s: int, q_steps, pending=None, stream=None, out=None):
+        """Decode step s of this layer in a stack (sfi_decode_layer_step): the
+        previous layer's deferred selection (pending, an sfi_deferred or None)
+        runs inside this call's grids and this layer's own selection is
+        deferred.  Returns it (active when step s has slow sequences); pass it
+        to the next layer's call, or to sfi_run_deferred after the last."""
+        ks = None if plan.k_seq is None else plan.k_seq[s]
+        ns, nf = int(plan.n_slow[s]), int(plan.n_fast[s])
+        self.kv.seq_len = plan.seq_len[s].data_ptr()
+        self.params.k_per_seq = None if ks is None else ks.data_ptr()
+        own = sfi.sfi_deferred()
+        try:
+            sfi.sfi_decode_layer_step(self.kv, self.params, plan.slow_ids[s], ns, plan.fast_ids[s], nf,
+                                      q_steps[s], self.out if out is None else out, self.evidence,
+                                      self.key_norm, self.ld, self.sel_idx, self.sel_count, self.fused,
+                                      self.ws_stepsel, self.ws_stepsel_bytes, pending, own, stream)
+        finally:
+            self.params.k_per_seq = None
+        return own
+
     def _new_event(self):
         e = torch.cuda.Event()
         self._events.append(e)

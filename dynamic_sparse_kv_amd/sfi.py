@@ -54,6 +54,16 @@ class sfi_select_params(ctypes.Structure):
     ]
 
 
+class sfi_deferred(ctypes.Structure):
+    """A postponed selection (filled by sfi_decode_layer_step, passed on as is)."""
+    _fields_ = [
+        ("active", _c_int), ("params", sfi_select_params), ("batch_ids", _vp), ("batch_n", _c_int),
+        ("seq_len", _vp), ("B", _c_int), ("H", _c_int), ("max_seq_len", _c_int),
+        ("evidence", _vp), ("key_norm", _vp), ("ld", _c_int), ("sel_idx", _vp), ("sel_count", _vp),
+        ("fused_out", _vp), ("ws", _vp), ("ws_bytes", _sz),
+    ]
+
+
 _lib = None
 
 
@@ -90,6 +100,12 @@ def lib():
         L.sfi_decode_step_select.argtypes = [P(sfi_kv), P(sfi_select_params), _vp, _c_int, _vp, _c_int,
                                              _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _vp, _vp, _sz, _vp]
         L.sfi_decode_step_select.restype = _c_int
+        L.sfi_decode_layer_step.argtypes = [P(sfi_kv), P(sfi_select_params), _vp, _c_int, _vp, _c_int,
+                                            _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _vp, _vp, _sz,
+                                            P(sfi_deferred), P(sfi_deferred), _vp]
+        L.sfi_decode_layer_step.restype = _c_int
+        L.sfi_run_deferred.argtypes = [P(sfi_deferred), _vp]
+        L.sfi_run_deferred.restype = _c_int
         L.sfi_verify_aggregate.argtypes = [P(sfi_kv), _vp, _c_int, _vp, _c_int, ctypes.c_uint32, _vp,
                                            _vp, _c_int, _vp, _sz, _vp]
         L.sfi_verify_aggregate.restype = _c_int
@@ -233,6 +249,24 @@ def sfi_decode_step_select(kv: sfi_kv, p: sfi_select_params, slow_ids, n_slow: i
                                         _ptr(key_norm), ld, _ptr(sel_idx), _ptr(sel_count),
                                         _ptr(fused_out), _ptr(ws), ws_bytes, _stream(stream)),
            "sfi_decode_step_select")
+
+
+def sfi_decode_layer_step(kv: sfi_kv, p: sfi_select_params, slow_ids, n_slow: int, fast_ids,
+                          n_fast: int, q, out, evidence, key_norm, ld: int, sel_idx, sel_count,
+                          fused_out, ws, ws_bytes: int, pending: Optional[sfi_deferred],
+                          defer: Optional[sfi_deferred], stream=None):
+    _check(lib().sfi_decode_layer_step(ctypes.byref(kv), ctypes.byref(p), _ptr(slow_ids), n_slow,
+                                       _ptr(fast_ids), n_fast, _ptr(q), _ptr(out), _ptr(evidence),
+                                       _ptr(key_norm), ld, _ptr(sel_idx), _ptr(sel_count),
+                                       _ptr(fused_out), _ptr(ws), ws_bytes,
+                                       None if pending is None else ctypes.byref(pending),
+                                       None if defer is None else ctypes.byref(defer),
+                                       _stream(stream)), "sfi_decode_layer_step")
+
+
+def sfi_run_deferred(d: Optional[sfi_deferred], stream=None):
+    _check(lib().sfi_run_deferred(None if d is None else ctypes.byref(d), _stream(stream)),
+           "sfi_run_deferred")
 
 
 def sfi_verify_aggregate(kv: sfi_kv, batch_ids, batch_n: int, q, T: int, row_mask: int, out, agg,

@@ -213,6 +213,56 @@ sfi_status sfi_decode_step_select(const sfi_kv *kv, const sfi_select_params *p,
                                   float *key_norm, int32_t ld, int32_t *sel_idx, int32_t *sel_count,
                                   float *fused_out, void *ws, size_t ws_bytes, void *stream);
 
+/* A selection whose slow step has run and whose key and pick passes are
+ * postponed: the cross-layer pipeline of sfi_decode_layer_step [SFI 3.C: the
+ * slow path's selector is overlapped with other work].  Host struct, filled
+ * by sfi_decode_layer_step (defer) and passed on unchanged; active = 0 means
+ * nothing is pending.  The buffers it names (its layer's evidence, key norms,
+ * index lists, fused scores, selector workspace and slow_ids list) must stay
+ * untouched until the selection has run. */
+typedef struct {
+  int32_t active;
+  sfi_select_params params;
+  const int32_t *batch_ids;
+  int32_t batch_n;
+  const int32_t *seq_len;
+  int32_t B, H, max_seq_len;
+  const float *evidence;
+  const float *key_norm;
+  int32_t ld;
+  int32_t *sel_idx;
+  int32_t *sel_count;
+  float *fused_out;
+  void *ws;
+  size_t ws_bytes;
+} sfi_deferred;
+
+/* sfi_decode_step_select for one layer of a stack, with the selections of
+ * consecutive layers overlapped [SFI 3.C]: a layer's attention does not read
+ * another layer's selection, so the key and pick passes of the previous
+ * layer's slow sequences (`pending`) run inside this call's partial and
+ * finalize grids.  With `defer` non-NULL this layer's own selection is not
+ * run but described in *defer (active = 1 when n_slow > 0), for the next
+ * layer's call or sfi_run_deferred; with `defer` NULL it runs at the end of
+ * this call.  pending NULL or inactive and defer NULL: exactly
+ * sfi_decode_step_select.  Results are those of sfi_decode_step_select per
+ * layer, bit for bit.
+ *   pending   must name other buffers than this call's (another layer's):
+ *             the same selector workspace, index lists or evidence give
+ *             SFI_ERR_RANGE; it is validated like sfi_select (FUSED only).
+ *   Other arguments and the workspace: as sfi_decode_step_select.
+ * The caller orders the layers on one stream; the pending selection's index
+ * lists are complete when this call's work on the stream is. */
+sfi_status sfi_decode_layer_step(const sfi_kv *kv, const sfi_select_params *p, const int32_t *slow_ids,
+                                 int32_t n_slow, const int32_t *fast_ids, int32_t n_fast,
+                                 const uint16_t *q, float *out, float *evidence, float *key_norm,
+                                 int32_t ld, int32_t *sel_idx, int32_t *sel_count, float *fused_out,
+                                 void *ws, size_t ws_bytes, const sfi_deferred *pending,
+                                 sfi_deferred *defer, void *stream);
+/* Runs a deferred selection on its own (the last layer's, or when the next
+ * call is not a layer step).  d NULL: SFI_ERR_NULL; inactive: nothing. */
+sfi_status sfi_run_deferred(const sfi_deferred *d, void *stream);
+
 /* Verification with aggregated logits [Vegas 2, 2.A, 2.B, 3]: T query rows
  * per sequence; row t sits at position n - T + t (n = seq_len[b], which
  * already counts the T rows) and attends keys [0, n - T + t].

@@ -165,6 +165,52 @@ def test_decode_step_validation():
     assert call(kv, n_slow=0, n_fast=0, ws_bytes=need) == sfi.SFI_OK
 
 
+def test_layer_step_validation():
+    """sfi_decode_layer_step / sfi_run_deferred: argument checks and the
+    cases with nothing to launch (no kernel runs here)."""
+    L = sfi.lib()
+    p = sfi.select_params(sfi.SFI_SCORE_FUSED, 0.3, 64, 4, 256)
+
+    def deferred(**over):
+        d = sfi.sfi_deferred()
+        d.active = 1
+        d.params = sfi.select_params(sfi.SFI_SCORE_FUSED, 0.3, 64, 4, 256)
+        d.batch_ids, d.batch_n, d.seq_len = FAKE + 64, 1, FAKE + 128
+        d.B, d.H, d.max_seq_len = 2, 2, 900
+        d.evidence, d.key_norm, d.ld = FAKE + 192, FAKE + 256, 1000
+        d.sel_idx, d.sel_count, d.fused_out = FAKE + 320, FAKE + 384, None
+        d.ws, d.ws_bytes = FAKE + 448, 1 << 40
+        for k, v in over.items():
+            setattr(d, k, v)
+        return d
+
+    def call(kv, pending=None, defer=None, n_slow=0, n_fast=0):
+        return L.sfi_decode_layer_step(ctypes.byref(kv), ctypes.byref(p), FAKE, n_slow, FAKE, n_fast, FAKE,
+                                       FAKE, FAKE, FAKE, 1000, FAKE, FAKE, None, FAKE, 1 << 40,
+                                       None if pending is None else ctypes.byref(pending),
+                                       None if defer is None else ctypes.byref(defer), None)
+
+    kv = _kv()
+    assert L.sfi_run_deferred(None, None) == sfi.SFI_ERR_NULL
+    assert L.sfi_run_deferred(ctypes.byref(deferred(active=0)), None) == sfi.SFI_OK
+    assert L.sfi_run_deferred(ctypes.byref(deferred(batch_n=0)), None) == sfi.SFI_OK
+    out = sfi.sfi_deferred()
+    out.active = 7
+    assert call(kv, deferred(batch_n=0), out) == sfi.SFI_OK                   # nothing to run
+    assert out.active == 0                                                      # no slow sequences
+    assert call(kv, deferred(sel_idx=FAKE), out) == sfi.SFI_ERR_RANGE          # aliases this call
+    assert call(kv, deferred(evidence=FAKE), out) == sfi.SFI_ERR_RANGE
+    raw = deferred()
+    raw.params.mode = sfi.SFI_SCORE_RAW
+    assert call(kv, raw, out) == sfi.SFI_ERR_RANGE                             # FUSED only
+    assert call(kv, deferred(B=0), out) == sfi.SFI_ERR_SHAPE
+    assert call(kv, deferred(ld=10), out) == sfi.SFI_ERR_RANGE
+    assert call(kv, deferred(ws_bytes=8), out) == sfi.SFI_ERR_WORKSPACE
+    assert call(kv, deferred(key_norm=None), out) == sfi.SFI_ERR_NULL
+    assert call(kv, None, out, n_slow=kv.B, n_fast=1) == sfi.SFI_ERR_RANGE    # this call's own checks
+    assert call(_kv(d=256), None, out) == sfi.SFI_ERR_UNSUPPORTED
+
+
 def test_verify_validation():
     L = sfi.lib()
 

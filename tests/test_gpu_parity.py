@@ -533,6 +533,58 @@ def test_decode_run_mixed_batch_co_launch():
     assert ties == 0
 
 
+@pytest.mark.parametrize("kdiv", [0, 16])
+def test_layer_pipeline_matches_per_layer_calls(kdiv):
+    """sfi_decode_layer_step over a 3-layer stack, each layer's selection run
+    inside the next layer's grids (and across the step boundary), against
+    sfi_decode_step_select per layer: outputs and selections bit for bit.
+    Steps: all slow, mixed, all fast, all slow, mixed; per-sequence k with
+    kdiv > 0."""
+    _say(f"layer pipeline, kdiv={kdiv}")
+    B, Hq, Hkv, d, L = 4, 32, 8, 128, 3
+    ctx = np.array([6000, 4500, 7000, 2600])
+    slow = np.array([[1, 1, 1, 1], [0, 1, 0, 1], [0, 0, 0, 0], [1, 1, 1, 1], [1, 0, 0, 0]], dtype=bool)
+    steps = slow.shape[0]
+    cap = int(ctx.max()) + steps + 1
+    plan = DecodePlan(slow, ctx, DEV, k_cap=300 if kdiv else 0, k_div=kdiv)
+    kw = dict(n_sink=4, window=256, k=300, lam=0.3)
+    layers = []
+    for layer in range(L):
+        K, V = _rand_kv(B, Hkv, cap, d, seed=90 + layer, hh=25)
+        q = _rand_q((steps, B, Hq, d), seed=95 + layer)
+        layers.append((K, V, q))
+    pipe = [SFIDecoder(K, V, Hq, cap, **kw) for K, V, _ in layers]
+    ref = [SFIDecoder(K, V, Hq, cap, **kw) for K, V, _ in layers]
+    outs_p, outs_r = [], []
+    pend = None
+    for s in range(steps):
+        for layer in range(L):
+            q = layers[layer][2]
+            pend = pipe[layer].layer_step(plan, s, q, pending=pend)
+            ks = None if plan.k_seq is None else plan.k_seq[s]
+            ref[layer].step_select(q[s], plan.seq_len[s], plan.slow_ids[s], int(plan.n_slow[s]),
+                                   plan.fast_ids[s], int(plan.n_fast[s]), k_seq=ks)
+            outs_p.append(pipe[layer].out.clone())
+            outs_r.append(ref[layer].out.clone())
+    sfi.sfi_run_deferred(pend)
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(zip(outs_p, outs_r)):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32)), f"out, step {i // L} layer {i % L}"
+    for layer in range(L):
+        assert torch.equal(pipe[layer].sel_idx, ref[layer].sel_idx), layer
+        assert torch.equal(pipe[layer].sel_count, ref[layer].sel_count), layer
+    # the last step's slow sequence against the oracle (layer 1)
+    K, V, q = layers[1]
+    s, b = steps - 1, 0
+    n = int(plan.seq_len_host[s, b])
+    kb = min(300, n // kdiv) if kdiv else 300
+    r = O.slow_select(_bits(q[s, b]), _bits(K[b]), _bits(V[b]), n, lam=0.3, k=kb, n_sink=4, window=256)
+    sel, cnt = pipe[1].sel_idx.cpu().numpy(), pipe[1].sel_count.cpu().numpy()
+    ties = sum(check_selection(sel[b, g, :kb], cnt[b, g], r["s"][g], r["lo"], r["hi"], kb) for g in range(Hkv))
+    assert row_rel_err(pipe[1].out[b].cpu().numpy(), r["o"]) <= OUT_TOL
+    _say(f"  near-tie differences: {ties}")
+
+
 @pytest.mark.parametrize("paged", [False, True])
 def test_decode_step_select_matches_separate_calls(paged):
     """sfi_decode_step_select (one call: co-launched step + the slow
