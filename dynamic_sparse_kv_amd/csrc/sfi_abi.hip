@@ -119,7 +119,7 @@ struct VerWs {
 VerWs verify_ws(const sfi_kv *kv, int T) {
   VerWs w{};
   w.chunk = verify_chunk_for(kv->B, kv->Hkv, kv->max_seq_len);
-  w.stride = (kv->max_seq_len + w.chunk - 1) / w.chunk;
+  w.stride = verify_stride_for(kv->max_seq_len, w.chunk);
   const size_t rows = (size_t)kv->B * T * kv->Hq * w.stride;
   w.o = 0;
   w.ml = align_up(rows * kv->d * sizeof(float));

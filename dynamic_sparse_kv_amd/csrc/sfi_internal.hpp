@@ -162,5 +162,7 @@ struct VerifyLaunch {
 
 hipError_t launch_verify(const VerifyLaunch &a, hipStream_t st);
 int verify_chunk_for(int batch_n, int Hkv, int max_seq_len);
+// Partial slots per (row, sequence) of the verify kernel for keys per wave `chunk`.
+int verify_stride_for(int max_seq_len, int chunk);
 
 }  // namespace sfi

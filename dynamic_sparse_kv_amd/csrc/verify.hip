@@ -79,10 +79,15 @@ __global__ __launch_bounds__(kVThreads) void verify_partial_kernel(VArgs a) {
   const int n = clamp_len(a.seq_len, b, a.max_len);
   const int T = a.T;
   const int R = G * T;
+  // The workgroup owns keys [K0, k1), kVWaves * wchunk of them, and wave w
+  // takes its 32-key tiles w, w + kVWaves, ...: the workgroup sweeps one
+  // contiguous range of K and of V (one stream per workgroup, not per wave,
+  // measured faster), while each wave keeps its own (m, Z, O) partial.
   const int widx = blockIdx.x * kVWaves + wave;
-  const int k0 = widx * a.wchunk;
-  if (k0 >= n) return;
-  const int k1 = min(n, k0 + a.wchunk);
+  const int K0 = blockIdx.x * kVWaves * a.wchunk;
+  if (K0 >= n) return;
+  const int k1 = min(n, K0 + kVWaves * a.wchunk);
+  const int k0 = K0 + 32 * wave;  // this wave's first tile
 
   // Query column of this lane: verify row jt, head jh of the group.
   const bool colv = col < R;
@@ -116,8 +121,8 @@ __global__ __launch_bounds__(kVThreads) void verify_partial_kernel(VArgs a) {
     bf16x8_t ka[KK];
     uint32_t vw[2][NP][8];
   };
-  // Every lane issues its loads unconditionally: a key past the wave's range
-  // reads row k1 - 1 instead (k1 > k0, so it exists) and is masked in
+  // Every lane issues its loads unconditionally: a key past the range reads
+  // row k1 - 1 instead (k1 > K0, so it exists) and is masked in
   // consume().  Loads behind per-lane branches would leave the number of
   // loads in flight unknown at compile time and every later wait would have
   // to drain them all, which would collapse the two-stage pipeline below.
@@ -238,14 +243,18 @@ __global__ __launch_bounds__(kVThreads) void verify_partial_kernel(VArgs a) {
   };
 
   // Two tiles in flight: the loads of one overlap the MFMA and softmax work
-  // of the other.  Tiles past k1 are fully masked (p = 0, no aggregate write).
-  Tile ta, tb;
-  load_tile(ta, k0);
-  for (int kb = k0; kb < k1; kb += 64) {
-    load_tile(tb, kb + 32);
-    consume(ta, kb);
-    load_tile(ta, kb + 64);
-    consume(tb, kb + 32);
+  // of the other.  Tiles past k1 are fully masked (p = 0, no aggregate write);
+  // a wave with no tile at all leaves Z = 0, which the combine skips.
+  constexpr int TS = 32 * kVWaves;  // key step between a wave's tiles
+  if (k0 < k1) {
+    Tile ta, tb;
+    load_tile(ta, k0);
+    for (int kb = k0; kb < k1; kb += 2 * TS) {
+      load_tile(tb, kb + TS);
+      consume(ta, kb);
+      load_tile(ta, kb + 2 * TS);
+      consume(tb, kb + TS);
+    }
   }
 
   const float zt = z + __shfl_xor(z, 32);
@@ -284,16 +293,20 @@ __global__ __launch_bounds__(D) void verify_combine_kernel(VFinal a) {
   if (b < 0) return;
   const int row = blockIdx.x;  // t*Hq + h
   const int n = clamp_len(a.seq_len, b, a.max_len);
-  const int S = (n + a.wchunk - 1) / a.wchunk;
+  // every wave of the workgroups that cover [0, n); waves without keys hold Z = 0
+  const int S = (n + kVWaves * a.wchunk - 1) / (kVWaves * a.wchunk) * kVWaves;
   const size_t base = ((size_t)b * a.T * a.Hq + row) * a.stride;
   float M = kNegBig;
   for (int s = 0; s < S; ++s) M = fmaxf(M, a.part_ml[(base + s) * 2]);
   float Z = 0.f, o = 0.f;
   const int e = threadIdx.x;
   for (int s = 0; s < S; ++s) {
-    const float w = exp2f(a.part_ml[(base + s) * 2] - M);
-    Z = fmaf(a.part_ml[(base + s) * 2 + 1], w, Z);
-    o = fmaf(a.part_o[(base + s) * D + e], w, o);
+    const float zs = a.part_ml[(base + s) * 2 + 1];
+    if (zs > 0.f) {
+      const float w = exp2f(a.part_ml[(base + s) * 2] - M);
+      Z = fmaf(zs, w, Z);
+      o = fmaf(a.part_o[(base + s) * D + e], w, o);
+    }
   }
   a.out[((size_t)b * a.T * a.Hq + row) * D + e] = (Z > 0.f) ? o / Z : 0.f;
 }
@@ -340,6 +353,12 @@ hipError_t verify_t(const VerifyLaunch &L, hipStream_t st) {
 }
 
 }  // namespace
+
+int verify_stride_for(int max_seq_len, int chunk) {
+  // partial slots per row: every wave of the workgroups covering max_seq_len
+  const int per_wg = kVWaves * chunk;
+  return (max_seq_len + per_wg - 1) / per_wg * kVWaves;
+}
 
 int verify_chunk_for(int batch_n, int Hkv, int max_seq_len) {
   // Keys per wave: long enough that a wave's (m, Z, O) partial (R x (d+2)
