@@ -7,6 +7,8 @@ sequences against the CPU oracle, which computes them one by one:
 
 * one layer of the 32-layer stack at 128K context (B=4, Hq=32/Hkv=8, d=128,
   k=4096, lambda 0.2): slow step + selection + a later fast step;
+* two layers of that stack with the cross-layer selection pipeline, against
+  the per-layer calls, bit for bit;
 * Vegas verification at 64K context (B=16, T=8): outputs of every verify
   row, the aggregate over ALL rows and Collect-2-Query, the head-shared
   top-2048 selection and a draft step;
@@ -84,6 +86,54 @@ def test_full_size_stack_layer_128k_sampled():
     o_ref = O.fast_step(qb[7], Kb, Vb, n + 7, lists, cfg.n_sink, cfg.window)
     assert row_rel_err(of[b], o_ref) <= OUT_TOL
     del dec, K, V
+    _free()
+
+
+def test_full_size_stack_pipeline_128k():
+    """Two layers of the 128K stack (B=4, k=4096, lambda 0.2) through three
+    steps (all slow, then the schedule's steps 1 and 2) with each layer's
+    selection run inside the next layer's grids, as the benchmark times it,
+    against sfi_decode_step_select per layer: outputs and index lists bit
+    for bit; one slow sequence's selection against the oracle."""
+    cfg = W.CONFIGS["c3"].replace(steps=3)
+    _say("full size: 128K layer pipeline, 2 layers")
+    ctx = W.context_lengths(cfg)
+    ml = int(ctx.max()) + cfg.steps
+    starts = W.sentence_starts(cfg)
+    slow = np.zeros((cfg.steps, cfg.B), dtype=bool)
+    slow[0] = True
+    slow[1, 1] = slow[2, 2] = True
+    plan = DecodePlan(slow, ctx, DEV)
+    kw = dict(n_sink=cfg.n_sink, window=cfg.window, k=cfg.k, lam=cfg.lam, norm_coef=cfg.norm_coef,
+              pos_tau=cfg.pos_tau)
+    layers = []
+    for layer in (3, 4):
+        K, V = W.make_kv(cfg, layer=layer, device=DEV, cap=ml)
+        q = W.make_queries(cfg, starts, layer=layer).to(DEV)
+        layers.append((K, V, q, SFIDecoder(K, V, cfg.Hq, ml, **kw), SFIDecoder(K, V, cfg.Hq, ml, **kw)))
+    pend = None
+    for s in range(cfg.steps):
+        for K, V, q, pipe, ref in layers:
+            pend = pipe.layer_step(plan, s, q, pending=pend)
+            ref.step_select(q[s], plan.seq_len[s], plan.slow_ids[s], int(plan.n_slow[s]), plan.fast_ids[s],
+                            int(plan.n_fast[s]))
+            torch.cuda.synchronize()
+            assert torch.equal(pipe.out.view(torch.int32), ref.out.view(torch.int32)), s
+    sfi.sfi_run_deferred(pend)
+    torch.cuda.synchronize()
+    for _, _, _, pipe, ref in layers:
+        assert torch.equal(pipe.sel_idx, ref.sel_idx)
+        assert torch.equal(pipe.sel_count, ref.sel_count)
+    _say("  pipelined = per layer, bit for bit")
+    K, V, q, pipe, _ = layers[1]
+    b, s = 2, 2
+    n = int(plan.seq_len_host[s, b])
+    r = O.slow_select(_bits(q[s, b]), _bits(K[b, :, :n]), _bits(V[b, :, :n]), n, lam=cfg.lam, k=cfg.k,
+                      n_sink=cfg.n_sink, window=cfg.window, norm_coef=cfg.norm_coef, pos_tau=cfg.pos_tau)
+    sel, cnt = pipe.sel_idx.cpu().numpy(), pipe.sel_count.cpu().numpy()
+    ties = sum(check_selection(sel[b, g], cnt[b, g], r["s"][g], r["lo"], r["hi"], cfg.k) for g in range(cfg.Hkv))
+    _say(f"  near-tie differences: {ties}")
+    del layers
     _free()
 
 
