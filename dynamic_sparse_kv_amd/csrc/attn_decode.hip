@@ -332,7 +332,7 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
       for (int u = 1; u < U; ++u) mx = fmaxf(mx, l[u][h]);
       if (__any(mx > m[h] + kSlack)) {
         const float mn = wave_max_groups(fmaxf(mx, m[h]));
-        const float sc = exp2f(m[h] - mn);
+        const float sc = exp2_hw(m[h] - mn);
         m[h] = mn;
         Z[h] *= sc;
 #pragma unroll
@@ -344,7 +344,7 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
       float pu[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        pu[h] = exp2f(l[u][h] - m[h]);
+        pu[h] = exp2_hw(l[u][h] - m[h]);
         Z[h] += pu[h];
       }
       // a masked row contributes p = 0; zeroing its V bits keeps a non-finite
@@ -465,7 +465,7 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
     float o = 0.f, z = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      const float sc = exp2f(s_m[w][h] - M);
+      const float sc = exp2_hw(s_m[w][h] - M);
       o = fmaf(s_acc[w][h][e], sc, o);
       z = fmaf(s_z[w][h], sc, z);
     }
@@ -548,7 +548,7 @@ struct FinalArgs {
 // reference and the sum of 2^(l - reference) over their keys.
 __device__ __forceinline__ void mz_merge(float &m, float &z, float m2, float z2) {
   const float mn = fmaxf(m, m2);
-  z = z * exp2f(m - mn) + z2 * exp2f(m2 - mn);
+  z = z * exp2_hw(m - mn) + z2 * exp2_hw(m2 - mn);
   m = mn;
 }
 
@@ -595,7 +595,7 @@ __device__ __forceinline__ void finalize_body(const FinalArgs &a, int x, int g, 
       for (int i = 0; i < 4; ++i) {
         if (s0 + i * PARTS < S && zs[i] > 0.f) {
           const float mn = fmaxf(m, ms[i]);
-          const float c = exp2f(m - mn), w = exp2f(ms[i] - mn);
+          const float c = exp2_hw(m - mn), w = exp2_hw(ms[i] - mn);
           z = z * c + zs[i] * w;
           o.x = o.x * c + v[i].x * w;
           o.y = o.y * c + v[i].y * w;
@@ -621,7 +621,7 @@ __device__ __forceinline__ void finalize_body(const FinalArgs &a, int x, int g, 
       float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
       for (int p = 0; p < PARTS; ++p) {
-        const float w = exp2f(s_pm[p] - M);
+        const float w = exp2_hw(s_pm[p] - M);
         const float4 t = s_po[p][e4];
         Z = fmaf(s_pz[p], w, Z);
         acc.x = fmaf(t.x, w, acc.x);
@@ -644,33 +644,60 @@ __device__ __forceinline__ void finalize_body(const FinalArgs &a, int x, int g, 
     const int j0 = (x - G) * kEvidChunk;
     const int j1 = min(n, j0 + kEvidChunk);
     constexpr int PER = kEvidChunk / kThreads;
-    // the chunk's logits (and key norms) do not depend on the merged
-    // maxima: load them first
+    // Every global load of the block goes out before the first use: the
+    // chunk's logits (one 16-byte load per key and 4 heads) and key norms,
+    // the partials' (max, sum) pairs and, for the selector's prior, the
+    // per-split key-norm sums.
     const bool prior = a.nsum != nullptr;
     float lg[PER][G], nv[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int j = j0 + tid + i * kThreads;
       const float *lp = a.logits + (lrow * a.lld + (size_t)min(j, j1 - 1)) * G;
+      if constexpr (G % 4 == 0) {
 #pragma unroll
-      for (int h = 0; h < G; ++h) lg[i][h] = lp[h];
+        for (int c = 0; c < G / 4; ++c) {
+          const float4 t = reinterpret_cast<const float4 *>(lp)[c];
+          lg[i][4 * c + 0] = t.x; lg[i][4 * c + 1] = t.y; lg[i][4 * c + 2] = t.z; lg[i][4 * c + 3] = t.w;
+        }
+      } else if constexpr (G == 2) {
+        const float2 t = *reinterpret_cast<const float2 *>(lp);
+        lg[i][0] = t.x; lg[i][1] = t.y;
+      } else {
+#pragma unroll
+        for (int h = 0; h < G; ++h) lg[i][h] = lp[h];
+      }
       nv[i] = prior ? a.key_norm[lrow * a.ld + min(j, j1 - 1)] : 0.f;
     }
-    // merged (max, sum) of every head of the group over the S partials
+    // merged (max, sum) of every head of the group over the S partials, and
+    // the row's key-norm sums (fixed order; every chunk block repeats them)
     float m[G], z[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       m[h] = kNegBig;
       z[h] = 0.f;
     }
+    double s1 = 0.0, s2 = 0.0;
     for (int s = tid; s < S; s += kThreads) {
+      float ml[G][2];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         const float *ml2 = a.part_ml + ((hbase + h) * a.stride + s) * 2;
-        mz_merge(m[h], z[h], ml2[0], ml2[1]);
+        ml[h][0] = ml2[0];
+        ml[h][1] = ml2[1];
       }
+      double n1 = 0.0, n2 = 0.0;
+      if (prior) {
+        n1 = a.nsum[(lrow * a.stride + s) * 2 + 0];
+        n2 = a.nsum[(lrow * a.stride + s) * 2 + 1];
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) mz_merge(m[h], z[h], ml[h][0], ml[h][1]);
+      s1 += n1;
+      s2 += n2;
     }
     __shared__ float s_m[NW][G], s_z[NW][G];
+    __shared__ double s_d[NW][2], s_w[NW];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
 #pragma unroll
@@ -681,6 +708,17 @@ __device__ __forceinline__ void finalize_body(const FinalArgs &a, int x, int g, 
       if (lane == 0) {
         s_m[wv][h] = m[h];
         s_z[wv][h] = z[h];
+      }
+    }
+    if (prior) {
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        s1 += __shfl_xor(s1, off);
+        s2 += __shfl_xor(s2, off);
+      }
+      if (lane == 0) {
+        s_d[wv][0] = s1;
+        s_d[wv][1] = s2;
       }
     }
     __syncthreads();
@@ -698,33 +736,16 @@ __device__ __forceinline__ void finalize_body(const FinalArgs &a, int x, int g, 
       const int j = j0 + tid + i * kThreads;
       float f = 0.f;
 #pragma unroll
-      for (int h = 0; h < G; ++h) f = fmaf(exp2f(lg[i][h] - M[h]), rz[h], f);
+      for (int h = 0; h < G; ++h) f = fmaf(exp2_hw(lg[i][h] - M[h]), rz[h], f);
       if (j < j1) a.evidence[lrow * a.ld + j] = f;
     }
     if (!prior) return;
     // The selector's prior for this 2048-key chunk (the selector's chunk p):
-    // mean and population std of the row's key norms from the partial
-    // kernel's per-split sums (fixed order; every chunk block repeats it),
-    // then the chunk's sum of prior weights.  Chunk 0 also stores the row
-    // constants, and the blocks clear the row's bucket histogram between
-    // them, so the selection can start at its key pass.
+    // mean and population std of the row's key norms, then the chunk's sum
+    // of prior weights.  Chunk 0 also stores the row constants, and the
+    // blocks clear the row's bucket histogram between them, so the selection
+    // can start at its key pass.
     const int pch = x - G;
-    double s1 = 0.0, s2 = 0.0;
-    for (int sp = tid; sp < S; sp += kThreads) {
-      s1 += a.nsum[(lrow * a.stride + sp) * 2 + 0];
-      s2 += a.nsum[(lrow * a.stride + sp) * 2 + 1];
-    }
-    __shared__ double s_d[NW][2];
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      s1 += __shfl_xor(s1, off);
-      s2 += __shfl_xor(s2, off);
-    }
-    if (lane == 0) {
-      s_d[wv][0] = s1;
-      s_d[wv][1] = s2;
-    }
-    __syncthreads();
     s1 = 0.0;
     s2 = 0.0;
 #pragma unroll
@@ -732,7 +753,6 @@ __device__ __forceinline__ void finalize_body(const FinalArgs &a, int x, int g, 
       s1 += s_d[w][0];
       s2 += s_d[w][1];
     }
-    __syncthreads();
     float muf, cz;
     prior_consts(s1, s2, n, a.norm_coef, &muf, &cz);
     const float ct = kLog2e / a.pos_tau;
@@ -746,12 +766,12 @@ __device__ __forceinline__ void finalize_body(const FinalArgs &a, int x, int g, 
     double W = (double)sw;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) W += __shfl_xor(W, off);
-    if (lane == 0) s_d[wv][0] = W;
+    if (lane == 0) s_w[wv] = W;
     __syncthreads();
     if (tid == 0) {
       double t = 0.0;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) t += s_d[w][0];
+      for (int w = 0; w < NW; ++w) t += s_w[w];
       a.sel_wsum[lrow * a.selP + pch] = t;
       if (pch == 0) {
         a.sel_meta[lrow].muf = muf;
@@ -768,9 +788,10 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(FinalArgs a) {
   finalize_body<D, G, MODE, EVID>(a, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
-// Slow and fast finalize blocks of one decode step in a single grid (layout
-// as in copartial_kernel: s_gx x Hkv x slow sequences, then the fast grid);
-// with PEND it ends with the pending selection's pick pass.
+// Slow and fast finalize blocks of one decode step in a single grid: the
+// slow pairs' evidence blocks, their combine blocks, then the fast combine
+// blocks (G x Hkv x fast sequences); with PEND it ends with the pending
+// selection's pick pass.
 template <int D, int G, bool PEND>
 __global__ __launch_bounds__(kThreads) void cofinal_kernel(FinalArgs s, FinalArgs f, int s_gx, int f_gx,
                                                            int Hkv, int ns, SelectLaunch pend, int np) {
@@ -784,7 +805,14 @@ __global__ __launch_bounds__(kThreads) void cofinal_kernel(FinalArgs s, FinalArg
     }
   }
   if (id < ns) {
-    finalize_body<D, G, MODE_SLOW, true>(s, id % s_gx, (id / s_gx) % Hkv, id / (s_gx * Hkv));
+    // the evidence blocks (the longest) are dispatched first
+    const int ne = s_gx - G, pairs = ns / s_gx;
+    if (id < ne * pairs) {
+      finalize_body<D, G, MODE_SLOW, true>(s, G + id % ne, (id / ne) % Hkv, id / (ne * Hkv));
+    } else {
+      id -= ne * pairs;
+      finalize_body<D, G, MODE_SLOW, true>(s, id % G, (id / G) % Hkv, id / (G * Hkv));
+    }
   } else {
     id -= ns;
     finalize_body<D, G, MODE_FAST, false>(f, id % f_gx, (id / f_gx) % Hkv, id / (f_gx * Hkv));

@@ -21,10 +21,9 @@
 //                         keys are bucket-sorted by their top 12 bits in LDS
 //                         and written (one coalesced pass) as 64-bit (key,
 //                         inverted index) composites in descending bucket
-//                         order, with the
-//                         chunk's cumulative bucket counts; the bucket counts
-//                         are merged into the row histogram with integer
-//                         atomics;
+//                         order, with the chunk's cumulative bucket counts;
+//                         the bucket counts are merged into the row histogram
+//                         with integer atomics;
 //   4. pick (per chunk)   every chunk workgroup reads the row histogram and
 //                         finds the bucket b1 holding the k-th largest key;
 //                         the bucket's keys (a contiguous run in each chunk)

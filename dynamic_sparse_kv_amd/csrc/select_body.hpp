@@ -39,16 +39,50 @@ __device__ __forceinline__ double block_sum_d(double x, double *s_red) {
   return t;
 }
 
+// Inclusive prefix sum over the wave in lane order, by DPP: row_shr 1, 2,
+// 4, 8 scan each 16-lane row (lanes with no source lane add 0), then
+// row_bcast 15 adds the last lane of rows 0 and 2 to rows 1 and 3, and
+// row_bcast 31 adds lane 31 to rows 2 and 3.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
+// Sums of two values over the workgroup (s_pair holds 2 ints per wave).
+// Like block_exscan, it ends without a barrier: the next write to s_pair
+// must follow another barrier.
+template <int NW>
+__device__ __forceinline__ void block_sum2(int a, int b, int *s_pair, int *ta, int *tb) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  a = wave_incl_scan(a);
+  b = wave_incl_scan(b);
+  if (lane == 63) {
+    s_pair[2 * wv] = a;
+    s_pair[2 * wv + 1] = b;
+  }
+  __syncthreads();
+  int x = 0, y = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    x += s_pair[2 * w];
+    y += s_pair[2 * w + 1];
+  }
+  *ta = x;
+  *tb = y;
+}
+
 // Exclusive prefix sum over the workgroup in thread order; *total = sum.
+// It ends without a barrier: the next write to s_wave must follow another
+// barrier (every caller has one before its next scan).
 template <int NW>
 __device__ __forceinline__ int block_exscan(int v, int *s_wave, int *total) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
+  const int x = wave_incl_scan(v);
   if (lane == 63) s_wave[wv] = x;
   __syncthreads();
   int base = 0, tot = 0;
@@ -58,7 +92,6 @@ __device__ __forceinline__ int block_exscan(int v, int *s_wave, int *total) {
     base += (w < wv) ? t : 0;
     tot += t;
   }
-  __syncthreads();
   *total = tot;
   return base + x - v;
 }
@@ -278,6 +311,7 @@ __device__ __forceinline__ void pick_body(const SelectLaunch &a, int p, int h, i
   __shared__ int s_tw[kSelMaxChunks];      // bucket winners per chunk
   __shared__ unsigned s_bits[kCH / 32];
   __shared__ int s_wave[kTW];
+  __shared__ int s_pair[2 * kTW];
   __shared__ int s_res[3];
   RowGeo r;
   if (!row_geo(a, h, z, r)) return;
@@ -308,13 +342,12 @@ __device__ __forceinline__ void pick_body(const SelectLaunch &a, int p, int h, i
 #pragma unroll
   for (int i = 0; i < kBPT; ++i) cnt += (int)hb[i];
   int total;
-  const int below = block_exscan<kTW>(cnt, s_wave, &total);
-  if (tid == 0) {
+  if (tid == 0) {  // default, ordered before the finder's write by the scan's barrier
     s_res[0] = 0;  // b1 = 0: every candidate wins (candidate keys never sit in bucket 0)
     s_res[1] = 0;
     s_res[2] = 0;
   }
-  __syncthreads();
+  const int below = block_exscan<kTW>(cnt, s_wave, &total);
   const int above = total - below - cnt;
   if (total > K && above < K && K <= above + cnt) {
     int acc = above;
@@ -387,7 +420,20 @@ __device__ __forceinline__ void pick_body(const SelectLaunch &a, int p, int h, i
       return srow[lo * kCH + s_above[lo] + (i - s_toff[lo])];
     };
     if (in_lds) {
-      for (int i = tid; i < mtot; i += kT) s_cand[i] = cand_at(i);
+      // four candidates per thread per round, their loads in flight together
+      for (int i0 = 0; i0 < mtot; i0 += 4 * kT) {
+        unsigned long long v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = i0 + tid + u * kT;
+          v[u] = (i < mtot) ? cand_at(i) : 0ull;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = i0 + tid + u * kT;
+          if (i < mtot) s_cand[i] = v[u];
+        }
+      }
       __syncthreads();
     }
     auto cand = [&](int i) { return in_lds ? s_cand[i] : cand_at(i); };
@@ -442,8 +488,7 @@ __device__ __forceinline__ void pick_body(const SelectLaunch &a, int p, int h, i
     }
   }
   int before, total_w;
-  block_exscan<kTW>(wb, s_wave, &before);
-  block_exscan<kTW>(wt, s_wave, &total_w);
+  block_sum2<kTW>(wb, wt, s_pair, &before, &total_w);
   const int count = min(total_w, K);
 
   // 5. This chunk's winners, ascending, through a 2048-bit bitmap.

@@ -75,6 +75,12 @@ __device__ __forceinline__ int clamp_len(const int32_t *seq_len, int b, int max_
 }
 
 // Order-preserving map float -> uint32 (larger float -> larger key).
+// 2^x by the hardware instruction (v_exp_f32).  It matches the library's
+// exp2f wherever the result is a normal number; below 2^-126 it returns 0
+// instead of a denormal.  Every use either adds the result to a sum that
+// holds a term of at least 1 or weights a term that is then negligible.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ uint32_t float_key(float x) {
   uint32_t u = __float_as_uint(x);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
@@ -85,7 +91,7 @@ __device__ __forceinline__ uint32_t float_key(float x) {
 // ct = log2(e)/tau, tq = t).  Every kernel that forms the weights or their
 // sum calls this one function, so sums and keys agree bit for bit.
 __device__ __forceinline__ float prior_w(float nu, int j, float muf, float cz, float tq, float ct) {
-  return exp2f(cz * (nu - muf)) * (1.0f + exp2f(((float)j - tq) * ct));
+  return exp2_hw(cz * (nu - muf)) * (1.0f + exp2_hw(((float)j - tq) * ct));
 }
 
 // Row constants of the prior from fp64 sums of the key norms over n keys:

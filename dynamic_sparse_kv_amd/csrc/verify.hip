@@ -203,7 +203,7 @@ __global__ __launch_bounds__(kVThreads) void verify_partial_kernel(VArgs a) {
     const bool need = mx > m + kSlack;
     if (__any(need)) {
       const float mn = need ? mx : m;
-      const float sc = exp2f(m - mn);
+      const float sc = exp2_hw(m - mn);
       m = mn;
       z *= sc;
 #pragma unroll
@@ -217,7 +217,7 @@ __global__ __launch_bounds__(kVThreads) void verify_partial_kernel(VArgs a) {
       bf16x8_t phi, plo;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float p = exp2f(sv[8 * ks + e] - m);
+        const float p = exp2_hw(sv[8 * ks + e] - m);
         z += p;
         const float ph = __uint_as_float(__float_as_uint(p) & 0xffff0000u);
         phi[e] = (__bf16)ph;
@@ -303,7 +303,7 @@ __global__ __launch_bounds__(D) void verify_combine_kernel(VFinal a) {
   for (int s = 0; s < S; ++s) {
     const float zs = a.part_ml[(base + s) * 2 + 1];
     if (zs > 0.f) {
-      const float w = exp2f(a.part_ml[(base + s) * 2] - M);
+      const float w = exp2_hw(a.part_ml[(base + s) * 2] - M);
       Z = fmaf(zs, w, Z);
       o = fmaf(a.part_o[(base + s) * D + e], w, o);
     }
