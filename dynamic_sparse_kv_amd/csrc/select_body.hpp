@@ -231,6 +231,12 @@ __device__ __forceinline__ void keys_body(const SelectLaunch &a, int p, int h, i
     c[i] = hist[kBPT * tid + i];
     tot += (int)c[i];
   }
+  // Merge the counts into the row histogram first: the atomics complete
+  // while the rest of the pass runs instead of after it.
+  uint32_t *h1 = a.ws.ghist + r.row * kBins1 + kBPT * tid;
+#pragma unroll
+  for (int i = 0; i < kBPT; ++i)
+    if (c[i]) atomicAdd(&h1[i], c[i]);
   int total;
   const int below = block_exscan<kTW>(tot, s_wave, &total);  // keys in lower buckets
   int run = total - below - tot;                              // keys in higher buckets
@@ -248,10 +254,6 @@ __device__ __forceinline__ void keys_body(const SelectLaunch &a, int p, int h, i
                      cum[6] | cum[7] << 16);
   cd[1] = make_uint4(cum[8] | cum[9] << 16, cum[10] | cum[11] << 16, cum[12] | cum[13] << 16,
                      cum[14] | cum[15] << 16);
-  uint32_t *h1 = a.ws.ghist + r.row * kBins1 + kBPT * tid;
-#pragma unroll
-  for (int i = 0; i < kBPT; ++i)
-    if (c[i]) atomicAdd(&h1[i], c[i]);
   __syncthreads();
   // bucket sort in LDS, then one coalesced write of the chunk's sorted run
 #pragma unroll
