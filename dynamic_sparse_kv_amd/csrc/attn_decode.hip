@@ -82,6 +82,8 @@ struct PartialArgs {
   int sel_heads, sel_k, n_sink, window;
   float qscale;  // log2(e) / sqrt(d)
   double *nsum;  // [B][Hkv][stride][2] per-split key-norm sums, or null
+  // fast step: compact copy of the selected rows, [B][Hkv][sel_k][D] (or null)
+  const uint16_t *ck, *cv;
 };
 
 // Maximum over the wave of a value that is equal within each aligned group
@@ -117,7 +119,7 @@ __device__ __forceinline__ FastList fast_list(const int32_t *sel_idx, const int3
 // One workgroup's share of a decode step: rows [split*chunk, ...) of the row
 // list of (sequence batch_ids[zb], kv head g).  A device function so that the
 // co-launch kernel below can run slow and fast shares in one grid.
-template <int D, int G, bool PAGED, int MODE, bool EVID, bool STREAM = false>
+template <int D, int G, bool PAGED, int MODE, bool EVID, bool STREAM = false, bool COMPACT = false>
 __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, int g, int zb) {
   // 8 lanes per row halves the cross-lane reduction and softmax work per row
   // compared with 16; wide groups (G*D >= 640) use 16 to bound accumulators
@@ -169,6 +171,35 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
   constexpr int IPT = (MODE == MODE_FAST) ? kMaxFastChunk / kThreads : 1;
   int jv[IPT];
   const int nfix_full = a.n_sink + a.window;
+  const size_t lrow = (size_t)(b * a.kv.Hkv + g);
+
+  // One pipeline stage: U rows per lane group, K and V slices of DPL dims.
+  struct Stage {
+    uint4 k[U][NV], v[U][NV];
+    int j[U];
+  };
+  // Compact rows: list position p >= nfix is entry p - nfix of the selection,
+  // row p - nfix of the compact copy; the address needs no index, so a chunk
+  // made only of selected entries issues its first stage with the query
+  // loads (taking nfix = n_sink + window, every sequence longer than that)
+  // and fills the rows' key ids in once the list is staged.
+  auto load_compact = [&](Stage &st, int base, int nfix) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = min(max(base + u * RPB - nfix, 0), a.sel_k - 1);
+      const size_t off = (lrow * a.sel_k + i) * D;
+#pragma unroll
+      for (int c = 0; c < NV; ++c) {
+        st.k[u][c] = ldg16(a.ck + off + slice(c));
+        st.v[u][c] = ldg16(a.cv + off + slice(c));
+      }
+    }
+  };
+  Stage sa, sb;
+  const bool spec_c = COMPACT && p0 >= nfix_full;  // chunk inside the selected part (if n is long)
+  if constexpr (COMPACT) {
+    if (spec_c) load_compact(sa, p0 + rg, nfix_full);
+  }
   if constexpr (MODE == MODE_FAST) {
     const int32_t *srow =
         a.sel_idx + ((size_t)b * a.sel_heads + (a.sel_heads == 1 ? 0 : g)) * a.sel_k;
@@ -236,13 +267,6 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
     for (int e = 0; e < DPL; ++e) acc[h][e] = 0.f;
   }
 
-  const size_t lrow = (size_t)(b * a.kv.Hkv + g);
-
-  // One pipeline stage: U rows per lane group, K and V slices of DPL dims.
-  struct Stage {
-    uint4 k[U][NV], v[U][NV];
-    int j[U];
-  };
   // Every lane issues its loads unconditionally: a row past the chunk or a
   // skipped list entry reads row 0 of the same (sequence, kv head), which
   // exists whenever the list is non-empty, and is masked out in consume().
@@ -372,13 +396,39 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
   // The trip count is the same for every lane of the wave (lane groups past
   // the chunk's end consume masked rows), so the wave-wide maximum updates
   // in consume() see every lane and m stays wave-uniform.
-  Stage sa, sb;
-  load_stage(sa, p0 + rg);
-  for (int base = p0; base < p1; base += 2 * STEP) {
-    load_stage(sb, base + rg + STEP);
-    consume(sa);
-    load_stage(sa, base + rg + 2 * STEP);
-    consume(sb);
+  bool compact_run = false;
+  if constexpr (COMPACT) {
+    const int nfix = fl.ns + fl.nw;
+    compact_run = p0 >= nfix;  // uniform over the workgroup
+    if (compact_run) {
+      // key ids of a compact stage, for the masks in consume()
+      auto ids = [&](Stage &st, int base) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int pp = base + u * RPB;
+          st.j[u] = (pp < p1) ? s_idx[min(pp - p0, a.chunk - 1)] : -1;
+        }
+      };
+      if (!spec_c || nfix != nfix_full) load_compact(sa, p0 + rg, nfix);
+      ids(sa, p0 + rg);
+      for (int base = p0; base < p1; base += 2 * STEP) {
+        load_compact(sb, base + rg + STEP, nfix);
+        ids(sb, base + rg + STEP);
+        consume(sa);
+        load_compact(sa, base + rg + 2 * STEP, nfix);
+        ids(sa, base + rg + 2 * STEP);
+        consume(sb);
+      }
+    }
+  }
+  if (!compact_run) {
+    load_stage(sa, p0 + rg);
+    for (int base = p0; base < p1; base += 2 * STEP) {
+      load_stage(sb, base + rg + STEP);
+      consume(sa);
+      load_stage(sa, base + rg + 2 * STEP);
+      consume(sb);
+    }
   }
 
   // Merge the lane groups of each wave as a reduce-scatter: in the round
@@ -481,6 +531,37 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
 template <int D, int G, bool PAGED, int MODE, bool EVID>
 __global__ __launch_bounds__(kThreads) void partial_kernel(PartialArgs a) {
   partial_body<D, G, PAGED, MODE, EVID>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+// Fast step reading its selected rows from the compact copy.
+template <int D, int G, bool PAGED>
+__global__ __launch_bounds__(kThreads) void fast_compact_kernel(PartialArgs a) {
+  partial_body<D, G, PAGED, MODE_FAST, false, false, true>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+// Compact copy of the selected rows: row i of (sequence, kv head) holds the
+// K and V rows of selection entry i.  D / 8 lanes move a row with 16-byte
+// loads and stores; a workgroup moves kThreads * 8 / D rows.
+template <int D, bool PAGED>
+__global__ __launch_bounds__(kThreads) void compact_kernel(PartialArgs a, uint16_t *ck, uint16_t *cv) {
+  constexpr int LPR = D / 8;
+  constexpr int RPB = kThreads / LPR;
+  const int b = batch_seq(a.batch_ids, blockIdx.z, a.B);
+  if (b < 0) return;
+  const int g = blockIdx.y;
+  const int i = blockIdx.x * RPB + (int)threadIdx.x / LPR;
+  const int sub = (int)threadIdx.x % LPR;
+  const int hs = (a.sel_heads == 1) ? 0 : g;
+  const int cnt = min(max(a.sel_count[b * a.sel_heads + hs], 0), a.sel_k);
+  if (i >= cnt) return;
+  const int n = clamp_len(a.seq_len, b, a.max_len);
+  const int j = a.sel_idx[((size_t)b * a.sel_heads + hs) * a.sel_k + i];
+  if (j < 0 || j >= n) return;
+  const size_t src = kv_row<D, PAGED>(a.kv, b, g, j) + 8 * sub;
+  const size_t dst = (((size_t)b * a.kv.Hkv + g) * a.sel_k + i) * D + 8 * sub;
+  const uint4 kk = ldg16(a.kv.k + src), vv = ldg16(a.kv.v + src);
+  *reinterpret_cast<uint4 *>(ck + dst) = kk;
+  *reinterpret_cast<uint4 *>(cv + dst) = vv;
 }
 
 // Slow (dense with evidence) and fast shares of one decode step in a single
@@ -846,6 +927,8 @@ PartialArgs partial_args(const AttnLaunch &a) {
   p.n_sink = a.n_sink; p.window = a.window;
   p.qscale = kLog2e / sqrtf((float)D);
   p.nsum = a.nsum;
+  p.ck = a.ck;
+  p.cv = a.cv;
   return p;
 }
 
@@ -919,6 +1002,34 @@ hipError_t fast_t(const AttnLaunch &a_in, hipStream_t st) {
   const FinalArgs f = final_args(a);
   dim3 g2(G, a.Hkv, a.batch_n);
   hipLaunchKernelGGL((finalize_kernel<D, G, MODE_FAST, false>), g2, dim3(kThreads), 0, st, f);
+  return hipGetLastError();
+}
+
+template <int D, int G, bool PAGED>
+hipError_t fast_compact_t(const AttnLaunch &a_in, hipStream_t st) {
+  AttnLaunch a = a_in;
+  {
+    // the index-gather kernel's plan, so both routes give the same bits
+    const int slots = resident_slots<partial_kernel<D, G, false, MODE_FAST, false>>();
+    a.plan = plan_splits(fast_rows(a), a.batch_n * a.Hkv, slots, a.plan.stride, kMaxFastChunk, false);
+  }
+  const PartialArgs p = partial_args<D>(a);
+  dim3 grid(a.plan.splits, a.Hkv, a.batch_n);
+  hipLaunchKernelGGL((fast_compact_kernel<D, G, PAGED>), grid, dim3(kThreads), 0, st, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const FinalArgs f = final_args(a);
+  dim3 g2(G, a.Hkv, a.batch_n);
+  hipLaunchKernelGGL((finalize_kernel<D, G, MODE_FAST, false>), g2, dim3(kThreads), 0, st, f);
+  return hipGetLastError();
+}
+
+template <int D, bool PAGED>
+hipError_t compact_t(const AttnLaunch &a, uint16_t *ck, uint16_t *cv, hipStream_t st) {
+  const PartialArgs p = partial_args<D>(a);
+  constexpr int RPB = kThreads / (D / 8);
+  dim3 grid((a.sel_k + RPB - 1) / RPB, a.Hkv, a.batch_n);
+  hipLaunchKernelGGL((compact_kernel<D, PAGED>), grid, dim3(kThreads), 0, st, p, ck, cv);
   return hipGetLastError();
 }
 
@@ -1109,6 +1220,17 @@ hipError_t launch_step(const AttnLaunch &sa, const AttnLaunch &fa, hipStream_t s
 
 hipError_t launch_fast(const AttnLaunch &a, hipStream_t st) {
   SFI_DISPATCH(fast_t, a, st);
+}
+
+hipError_t launch_fast_compact(const AttnLaunch &a, hipStream_t st) {
+  SFI_DISPATCH(fast_compact_t, a, st);
+}
+
+hipError_t launch_compact(const AttnLaunch &a, uint16_t *ck, uint16_t *cv, hipStream_t st) {
+  if (a.sel_k < 1 || a.batch_n < 1) return hipSuccess;
+  if (a.d == 128) return a.paged ? compact_t<128, true>(a, ck, cv, st) : compact_t<128, false>(a, ck, cv, st);
+  if (a.d == 64) return a.paged ? compact_t<64, true>(a, ck, cv, st) : compact_t<64, false>(a, ck, cv, st);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace sfi

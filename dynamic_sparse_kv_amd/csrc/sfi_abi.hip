@@ -19,6 +19,8 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool supported_group(int G) { return G == 1 || G == 2 || G == 4 || G == 5 || G == 8; }
 
 // Validates the cache description; on success fills the device view.
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
 sfi_status check_kv(const sfi_kv *kv, KVView *view, bool *paged) {
   if (!kv) return SFI_ERR_NULL;
   if (!kv->k || !kv->v || !kv->seq_len) return SFI_ERR_NULL;
@@ -548,6 +550,61 @@ sfi_status sfi_fast_step(const sfi_kv *kv, const int32_t *batch_ids, int32_t bat
   const AttnLaunch a = fast_launch(kv, view, paged, w, ws, batch_ids, batch_n, q, out, sel_idx,
                                    sel_count, sel_heads, sel_k, n_sink, window);
   return launch_fast(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SFI_OK : SFI_ERR_HIP;
+}
+
+sfi_status sfi_compact_selected(const sfi_kv *kv, const int32_t *batch_ids, int32_t batch_n,
+                                const int32_t *sel_idx, const int32_t *sel_count, int32_t sel_heads,
+                                int32_t sel_k, uint16_t *ck, uint16_t *cv, void *stream) {
+  KVView view;
+  bool paged = false;
+  sfi_status s = check_kv(kv, &view, &paged);
+  if (s != SFI_OK) return s;
+  if ((s = check_batch(kv, batch_n)) != SFI_OK) return s;
+  if ((s = check_fast(kv, sel_idx, sel_count, sel_heads, sel_k, 0, 0)) != SFI_OK) return s;
+  if (!ck || !cv) return SFI_ERR_NULL;
+  if (!aligned16(ck) || !aligned16(cv)) return SFI_ERR_RANGE;
+  if (batch_n == 0 || sel_k == 0) return SFI_OK;
+  AttnLaunch a{};
+  a.kv = view;
+  a.seq_len = kv->seq_len;
+  a.batch_ids = batch_ids;
+  a.batch_n = batch_n;
+  a.B = kv->B; a.Hq = kv->Hq; a.Hkv = kv->Hkv; a.d = kv->d; a.G = kv->Hq / kv->Hkv;
+  a.max_len = kv->max_seq_len;
+  a.paged = paged;
+  a.sel_idx = sel_idx;
+  a.sel_count = sel_count;
+  a.sel_heads = sel_heads;
+  a.sel_k = sel_k;
+  return launch_compact(a, ck, cv, static_cast<hipStream_t>(stream)) == hipSuccess ? SFI_OK : SFI_ERR_HIP;
+}
+
+sfi_status sfi_fast_step_compact(const sfi_kv *kv, const int32_t *batch_ids, int32_t batch_n,
+                                 const uint16_t *q, const int32_t *sel_idx, const int32_t *sel_count,
+                                 int32_t sel_heads, int32_t sel_k, int32_t n_sink, int32_t window,
+                                 const uint16_t *ck, const uint16_t *cv, float *out, void *ws,
+                                 size_t ws_bytes, void *stream) {
+  KVView view;
+  bool paged = false;
+  sfi_status s = check_kv(kv, &view, &paged);
+  if (s != SFI_OK) return s;
+  if ((s = check_batch(kv, batch_n)) != SFI_OK) return s;
+  if (!q || !out) return SFI_ERR_NULL;
+  if ((s = check_fast(kv, sel_idx, sel_count, sel_heads, sel_k, n_sink, window)) != SFI_OK) return s;
+  if (!ck || !cv) return SFI_ERR_NULL;
+  if (!aligned16(ck) || !aligned16(cv)) return SFI_ERR_RANGE;
+  const FastWs w = fast_ws(kv, sel_k, n_sink, window);
+  if (!ws) return SFI_ERR_NULL;
+  if (ws_bytes < w.total) return SFI_ERR_WORKSPACE;
+  if (batch_n == 0) return SFI_OK;
+  AttnLaunch a = fast_launch(kv, view, paged, w, ws, batch_ids, batch_n, q, out, sel_idx, sel_count,
+                             sel_heads, sel_k, n_sink, window);
+  a.ck = ck;
+  a.cv = cv;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  // without selected rows there is nothing to read from the copy
+  const hipError_t e = (sel_k > 0) ? launch_fast_compact(a, st) : launch_fast(a, st);
+  return e == hipSuccess ? SFI_OK : SFI_ERR_HIP;
 }
 
 size_t sfi_verify_workspace_bytes(const sfi_kv *kv, int32_t T) {

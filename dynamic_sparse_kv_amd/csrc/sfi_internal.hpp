@@ -86,10 +86,17 @@ struct AttnLaunch {
   SelRowMeta *sel_meta;  // [B*Hkv]
   uint32_t *sel_ghist;   // [B*Hkv][4096]
   int selP;
+  // fast step: compact copy of the selected rows [B][Hkv][sel_k][d] (or null)
+  const uint16_t *ck, *cv;
 };
 
 hipError_t launch_slow(const AttnLaunch &a, hipStream_t st);
 hipError_t launch_fast(const AttnLaunch &a, hipStream_t st);
+// Fast step whose selected rows come from the compact copy a.ck / a.cv.
+hipError_t launch_fast_compact(const AttnLaunch &a, hipStream_t st);
+// Copy the K/V rows of every valid selected entry (i < count, 0 <= id < n)
+// to row i of the compact copy ck / cv ([B][Hkv][sel_k][d]).
+hipError_t launch_compact(const AttnLaunch &a, uint16_t *ck, uint16_t *cv, hipStream_t st);
 struct SelectLaunch;
 // Slow step with evidence (sa) and fast step (fa) on disjoint sequences,
 // co-launched; either share may be empty.  A non-null pend is a selection

@@ -99,6 +99,7 @@ class SFIDecoder:
         self.fused = torch.zeros((B, Hkv, self.ld), **f32) if keep_fused else None
         self.sel_idx = torch.full((B, Hkv, k), -1, dtype=torch.int32, device=dev)
         self.sel_count = torch.zeros((B, Hkv), dtype=torch.int32, device=dev)
+        self.ck = self.cv = None  # compact copies of the selected rows (allocated by compact())
         # second evidence / key-norm copy for the pipelined schedule (allocated
         # here, never inside a graph capture)
         self.evidence_alt = torch.zeros((B, Hkv, self.ld), **f32)
@@ -154,6 +155,23 @@ class SFIDecoder:
         sfi.sfi_fast_step(self.kv, batch_ids, batch_n, q, self.sel_idx, self.sel_count, self.Hkv,
                           self.k, self.n_sink, self.window, self.out if out is None else out,
                           self.ws_fast, self.ws_fast_bytes, stream)
+
+    def compact(self, seq_len, batch_ids, batch_n: int, stream=None):
+        """Copy the selected K/V rows of the listed sequences into the
+        compact buffers (allocated on first use, outside any capture)."""
+        if self.ck is None:
+            self.ck = torch.zeros((self.B, self.Hkv, self.k, self.d), dtype=torch.bfloat16, device=self.dev)
+            self.cv = torch.zeros_like(self.ck)
+        self.kv.seq_len = seq_len.data_ptr() if torch.is_tensor(seq_len) else seq_len
+        sfi.sfi_compact_selected(self.kv, batch_ids, batch_n, self.sel_idx, self.sel_count, self.Hkv,
+                                 self.k, self.ck, self.cv, stream)
+
+    def fast_compact(self, q, seq_len, batch_ids, batch_n: int, stream=None, out=None):
+        """Fast step reading the selected rows from the compact buffers."""
+        self.kv.seq_len = seq_len.data_ptr() if torch.is_tensor(seq_len) else seq_len
+        sfi.sfi_fast_step_compact(self.kv, batch_ids, batch_n, q, self.sel_idx, self.sel_count, self.Hkv,
+                                  self.k, self.n_sink, self.window, self.ck, self.cv,
+                                  self.out if out is None else out, self.ws_fast, self.ws_fast_bytes, stream)
 
     def co_step(self, q, seq_len, slow_ids, n_slow: int, fast_ids, n_fast: int, stream=None,
                 out=None, select: bool = True, k_seq=None):

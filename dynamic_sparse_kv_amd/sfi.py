@@ -90,6 +90,11 @@ def lib():
         L.sfi_fast_step.argtypes = [P(sfi_kv), _vp, _c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int,
                                     _c_int, _vp, _vp, _sz, _vp]
         L.sfi_fast_step.restype = _c_int
+        L.sfi_compact_selected.argtypes = [P(sfi_kv), _vp, _c_int, _vp, _vp, _c_int, _c_int, _vp, _vp, _vp]
+        L.sfi_compact_selected.restype = _c_int
+        L.sfi_fast_step_compact.argtypes = [P(sfi_kv), _vp, _c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int,
+                                            _c_int, _vp, _vp, _vp, _vp, _sz, _vp]
+        L.sfi_fast_step_compact.restype = _c_int
         L.sfi_decode_step_workspace_bytes.argtypes = [P(sfi_kv), _c_int, _c_int, _c_int]
         L.sfi_decode_step_workspace_bytes.restype = _sz
         L.sfi_decode_step.argtypes = [P(sfi_kv), _vp, _c_int, _vp, _c_int, _vp, _vp, _vp, _vp, _c_int,
@@ -222,6 +227,21 @@ def sfi_fast_step(kv: sfi_kv, batch_ids, batch_n: int, q, sel_idx, sel_count, se
     _check(lib().sfi_fast_step(ctypes.byref(kv), _ptr(batch_ids), batch_n, _ptr(q), _ptr(sel_idx),
                                _ptr(sel_count), sel_heads, sel_k, n_sink, window, _ptr(out),
                                _ptr(ws), ws_bytes, _stream(stream)), "sfi_fast_step")
+
+
+def sfi_compact_selected(kv: sfi_kv, batch_ids, batch_n: int, sel_idx, sel_count, sel_heads: int,
+                         sel_k: int, ck, cv, stream=None):
+    _check(lib().sfi_compact_selected(ctypes.byref(kv), _ptr(batch_ids), batch_n, _ptr(sel_idx),
+                                      _ptr(sel_count), sel_heads, sel_k, _ptr(ck), _ptr(cv), _stream(stream)),
+           "sfi_compact_selected")
+
+
+def sfi_fast_step_compact(kv: sfi_kv, batch_ids, batch_n: int, q, sel_idx, sel_count, sel_heads: int,
+                          sel_k: int, n_sink: int, window: int, ck, cv, out, ws, ws_bytes: int, stream=None):
+    _check(lib().sfi_fast_step_compact(ctypes.byref(kv), _ptr(batch_ids), batch_n, _ptr(q), _ptr(sel_idx),
+                                       _ptr(sel_count), sel_heads, sel_k, n_sink, window, _ptr(ck), _ptr(cv),
+                                       _ptr(out), _ptr(ws), ws_bytes, _stream(stream)),
+           "sfi_fast_step_compact")
 
 
 def sfi_decode_step_workspace_bytes(kv: sfi_kv, sel_k: int, n_sink: int, window: int) -> int:

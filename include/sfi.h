@@ -166,6 +166,35 @@ sfi_status sfi_fast_step(const sfi_kv *kv, const int32_t *batch_ids, int32_t bat
                          int32_t sel_heads, int32_t sel_k, int32_t n_sink, int32_t window,
                          float *out, void *ws, size_t ws_bytes, void *stream);
 
+/* Compact copy of the selected rows [SFI 3.C and the Portuguese summary,
+ * section 2.C: a fast kernel that reads the sink and selected rows from one
+ * contiguous buffer instead of scattered cache rows]: for every sequence b of
+ * the batch and kv head g, row i of ck / cv becomes the K / V row of key
+ * j = sel_idx[b][hs][i], for i < min(sel_count[b][hs], sel_k) and
+ * 0 <= j < seq_len[b] (hs as in sfi_fast_step); other rows are left as they
+ * are.  Call it after a selection (the copy holds that selection's rows) and
+ * before the fast steps that use it.
+ *   ck, cv  [B][Hkv][sel_k][d] bf16 bits, 16-byte aligned (else
+ *           SFI_ERR_RANGE); caller-owned.
+ * Moves 2 x 2 d bytes per listed row (read and write of K and V). */
+sfi_status sfi_compact_selected(const sfi_kv *kv, const int32_t *batch_ids, int32_t batch_n,
+                                const int32_t *sel_idx, const int32_t *sel_count, int32_t sel_heads,
+                                int32_t sel_k, uint16_t *ck, uint16_t *cv, void *stream);
+
+/* sfi_fast_step with the selected rows read from the compact copy made by
+ * sfi_compact_selected from the same sel_idx / sel_count (sinks and window
+ * still come from the cache).  Same set, same split plan and same order of
+ * arithmetic as sfi_fast_step, so the results are equal bit for bit.  A
+ * chunk of the row list made only of selected entries issues its first row
+ * loads together with its query and index loads (the copy's addresses need
+ * no index).  Arguments as sfi_fast_step, plus ck, cv as above; workspace
+ * sfi_fast_workspace_bytes. */
+sfi_status sfi_fast_step_compact(const sfi_kv *kv, const int32_t *batch_ids, int32_t batch_n,
+                                 const uint16_t *q, const int32_t *sel_idx, const int32_t *sel_count,
+                                 int32_t sel_heads, int32_t sel_k, int32_t n_sink, int32_t window,
+                                 const uint16_t *ck, const uint16_t *cv, float *out, void *ws,
+                                 size_t ws_bytes, void *stream);
+
 /* One decode step of a batch whose sequences take different paths [SFI 3.A
  * slow and fast steps; 3.C, which overlaps the slow path with fast steps]:
  * the slow step (dense attention with evidence) of slow_ids[0..n_slow) and the

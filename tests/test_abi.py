@@ -228,3 +228,32 @@ def test_verify_validation():
     assert call(kv, ws_bytes=8) == sfi.SFI_ERR_WORKSPACE
     assert call(_kv(Hq=40, Hkv=8), T=4, mask=0xF) == sfi.SFI_ERR_UNSUPPORTED  # G = 5 has no MFMA tile
     assert call(kv, batch_n=0) == sfi.SFI_OK
+
+
+def test_compact_validation():
+    """sfi_compact_selected / sfi_fast_step_compact: argument checks and the
+    cases with nothing to launch (no kernel runs here)."""
+    L = sfi.lib()
+
+    def compact(kv, ck=FAKE, cv=FAKE, sel_heads=2, sel_k=64, batch_n=1, sel_count=FAKE):
+        return L.sfi_compact_selected(ctypes.byref(kv), None, batch_n, FAKE, sel_count, sel_heads, sel_k,
+                                      ck, cv, None)
+
+    def fast(kv, ck=FAKE, cv=FAKE, ws_bytes=1 << 40, batch_n=1, q=FAKE):
+        return L.sfi_fast_step_compact(ctypes.byref(kv), None, batch_n, q, FAKE, FAKE, 2, 64, 4, 256,
+                                       ck, cv, FAKE, FAKE, ws_bytes, None)
+
+    kv = _kv()
+    assert compact(kv, ck=None) == sfi.SFI_ERR_NULL
+    assert compact(kv, cv=FAKE + 8) == sfi.SFI_ERR_RANGE                  # copies are 16-byte aligned
+    assert compact(kv, sel_heads=3) == sfi.SFI_ERR_SHAPE
+    assert compact(kv, sel_count=None) == sfi.SFI_ERR_NULL
+    assert compact(kv, batch_n=3) == sfi.SFI_ERR_RANGE
+    assert compact(_kv(d=96)) == sfi.SFI_ERR_UNSUPPORTED
+    assert compact(kv, batch_n=0) == sfi.SFI_OK
+    assert compact(kv, sel_k=0) == sfi.SFI_OK
+    assert fast(kv, ck=None) == sfi.SFI_ERR_NULL
+    assert fast(kv, ck=FAKE + 4) == sfi.SFI_ERR_RANGE
+    assert fast(kv, q=None) == sfi.SFI_ERR_NULL
+    assert fast(kv, ws_bytes=8) == sfi.SFI_ERR_WORKSPACE
+    assert fast(kv, batch_n=0) == sfi.SFI_OK

@@ -739,6 +739,75 @@ def test_paged_cache_matches_contiguous_and_oracle():
         assert row_rel_err(out[b], o_ref) <= OUT_TOL
 
 
+@pytest.mark.parametrize("paged", [False, True])
+def test_fast_compact_matches_index_gather(paged):
+    """sfi_compact_selected + sfi_fast_step_compact: the same outputs bit for
+    bit as the index-gather fast step, and the oracle's fast step, with the
+    selection a few steps old (the keys that left the window since are
+    dropped), ragged lengths (one sequence shorter than sinks + window, one with fewer
+    candidates than k) and a batch subset in non-sorted order."""
+    _say(f"fast compact paged={paged}")
+    cfg = W.CONFIGS["c5"].replace(B=4, Hq=32, Hkv=8, d=128)
+    cap = 5008
+    K, V = _rand_kv(cfg.B, cfg.Hkv, cap, cfg.d, seed=70, hh=8)
+    lens0 = [4900, 200, 700, 3100]          # at the selection
+    adv = 37                                # fast steps later
+    lens1 = [n + adv for n in lens0]
+    assert max(lens1) <= cap
+    kwargs = {}
+    if paged:
+        table, npages = W.page_table(cfg, np.full(cfg.B, cap))
+        K = W.to_paged(K, table, npages, 16)
+        V = W.to_paged(V, table, npages, 16)
+        kwargs = dict(page_table=torch.from_numpy(table).to(DEV), page_size=16)
+    ml = max(lens1)
+    k = 512
+    dec = SFIDecoder(K, V, cfg.Hq, ml, n_sink=4, window=256, k=k, lam=0.3, **kwargs)
+    q0 = _rand_q((cfg.B, cfg.Hq, cfg.d), seed=71)
+    q1 = _rand_q((cfg.B, cfg.Hq, cfg.d), seed=72)
+    seq0 = torch.tensor(lens0, dtype=torch.int32, device=DEV)
+    seq1 = torch.tensor(lens1, dtype=torch.int32, device=DEV)
+    dec.slow(q0, seq0, None, cfg.B)
+    dec.compact(seq0, None, cfg.B)
+    ids = torch.tensor([3, 0, 1, 2], dtype=torch.int32, device=DEV)
+    out_i = torch.full_like(dec.out, float("nan"))
+    out_c = torch.full_like(dec.out, float("nan"))
+    dec.fast(q1, seq1, ids, 4, out=out_i)
+    dec.fast_compact(q1, seq1, ids, 4, out=out_c)
+    # a subset (its own split plan): other rows untouched
+    sub = torch.tensor([2, 3], dtype=torch.int32, device=DEV)
+    out_s = torch.full_like(dec.out, float("nan"))
+    out_si = torch.full_like(dec.out, float("nan"))
+    dec.fast_compact(q1, seq1, sub, 2, out=out_s)
+    dec.fast(q1, seq1, sub, 2, out=out_si)
+    torch.cuda.synchronize()
+    assert torch.equal(out_i.view(torch.int32), out_c.view(torch.int32))
+    assert torch.equal(out_s.view(torch.int32), out_si.view(torch.int32))
+    assert torch.isnan(out_s[:2]).all() and not torch.isnan(out_s[2:]).any()
+    sel = dec.sel_idx.cpu().numpy()
+    cnt = dec.sel_count.cpu().numpy()
+    assert cnt[1].max() == 0 and 0 < cnt[2].max() < k        # the degenerate lengths
+    Kd = _bits(K) if not paged else None
+    qb = _bits(q1)
+    out = out_c.cpu().numpy()
+    for b in range(cfg.B):
+        if paged:
+            Kb = W.bf16_bits(_unpage(K, table, b, cap))
+            Vb = W.bf16_bits(_unpage(V, table, b, cap))
+        else:
+            Kb, Vb = Kd[b], _bits(V[b])
+        lists = [sel[b, g, : cnt[b, g]] for g in range(cfg.Hkv)]
+        o_ref = O.fast_step(qb[b], Kb, Vb, lens1[b], lists, 4, 256)
+        assert row_rel_err(out[b], o_ref) <= OUT_TOL
+
+
+def _unpage(P, table, b, cap):
+    """Contiguous [Hkv][cap][d] rows of sequence b from a paged pool."""
+    npg = (cap + 15) // 16
+    pages = torch.as_tensor(table[b, :npg].astype(np.int64), device=P.device)
+    return P[pages].permute(1, 0, 2, 3).reshape(P.shape[1], npg * 16, P.shape[3])[:, :cap]
+
+
 # ------------------------------------------------- full size, sampled outputs
 
 def test_full_size_llama_layer_32k_sampled():
