@@ -140,6 +140,14 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
   constexpr float kSlack = 8.0f;
 
   __shared__ int s_idx[MODE == MODE_FAST ? kMaxFastChunk : 1];
+  // Paged caches: the physical page of each row the chunk reads, resolved
+  // once into LDS (fast: one per list entry; dense/slow: one per page of the
+  // chunk's contiguous rows, chunks of at most kMaxSlowChunk rows and pages
+  // of at least 16), so the main loop's row addresses need no global load:
+  // a page-table load issued behind a stage's row loads would make its wait
+  // drain them too, leaving one stage in flight.
+  constexpr int kPgSlots = (MODE == MODE_FAST) ? kMaxFastChunk : kMaxSlowChunk / 16 + 2;
+  __shared__ int s_pg[PAGED ? kPgSlots : 1];
   __shared__ float s_m[NW][G], s_z[NW][G];
   __shared__ float s_acc[NW][G][D];
 
@@ -237,21 +245,55 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
       for (int i = 0; i < IPT; ++i)
         jv[i] = (fl.cnt > 0) ? fl.sel[min(max(p0 + tid + i * kThreads - nfix, 0), fl.cnt - 1)] : -1;
     }
+    int jr[IPT];
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
       const int p = p0 + tid + i * kThreads;
-      if (p < p1) {
-        int j;
-        if (p < fl.ns) {
-          j = p;
-        } else if (p < nfix) {
-          j = fl.w0 + (p - fl.ns);
-        } else {
-          j = jv[i];
-          if (j < a.n_sink || j >= fl.w0) j = -1;  // padding, sink or now in window
-        }
-        s_idx[p - p0] = j;
+      int j = -1;
+      if (p < fl.ns) {
+        j = p;
+      } else if (p < nfix) {
+        j = fl.w0 + (p - fl.ns);
+      } else {
+        j = jv[i];
+        if (j < a.n_sink || j >= fl.w0) j = -1;  // padding, sink or now in window
       }
+      jr[i] = j;
+    }
+    if constexpr (PAGED) {
+      // every entry's page-table load in flight together (j < n <= the
+      // table's rows; a skipped entry looks up page 0)
+      int pgv[IPT];
+#pragma unroll
+      for (int i = 0; i < IPT; ++i)
+        pgv[i] = a.kv.page_table[(size_t)b * a.kv.max_pages + (max(jr[i], 0) >> a.kv.page_shift)];
+#pragma unroll
+      for (int i = 0; i < IPT; ++i) {
+        const int p = p0 + tid + i * kThreads;
+        if (p < p1) s_pg[p - p0] = pgv[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+      const int p = p0 + tid + i * kThreads;
+      if (p < p1) s_idx[p - p0] = jr[i];
+    }
+    __syncthreads();
+  } else if constexpr (PAGED) {
+    // pages of the chunk's rows [p0, p1)
+    const int pb = p0 >> a.kv.page_shift;
+    const int npg = ((p1 - 1) >> a.kv.page_shift) - pb + 1;
+    constexpr int PR = (kPgSlots + kThreads - 1) / kThreads;
+    int pgv[PR];
+#pragma unroll
+    for (int r = 0; r < PR; ++r) {
+      const int i = tid + r * kThreads;
+      pgv[r] = (i < npg) ? a.kv.page_table[(size_t)b * a.kv.max_pages + pb + i] : 0;
+    }
+#pragma unroll
+    for (int r = 0; r < PR; ++r) {
+      const int i = tid + r * kThreads;
+      if (i < npg && i < kPgSlots) s_pg[i] = pgv[r];
     }
     __syncthreads();
   }
@@ -285,7 +327,17 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
         j = (p < p1) ? p : -1;
       }
       st.j[u] = j;
-      const size_t off = kv_row<D, PAGED>(a.kv, b, g, max(j, 0));
+      size_t off;
+      if constexpr (PAGED) {
+        const int sh = a.kv.page_shift;
+        int pg;
+        if constexpr (MODE == MODE_FAST) pg = s_pg[min(p - p0, a.chunk - 1)];
+        else pg = s_pg[min((max(j, p0) >> sh) - (p0 >> sh), kPgSlots - 1)];
+        pg = min(max(pg, 0), a.kv.num_pages - 1);
+        off = ((((size_t)pg * a.kv.Hkv + g) << sh) + (size_t)(max(j, 0) & ((1 << sh) - 1))) * D;
+      } else {
+        off = kv_row<D, false>(a.kv, b, g, max(j, 0));
+      }
 #pragma unroll
       for (int c = 0; c < NV; ++c) {
         // the slow share of a co-launched step streams its rows once with a

@@ -37,6 +37,9 @@ sfi_status check_kv(const sfi_kv *kv, KVView *view, bool *paged) {
     if (ps < 16 || ps > 1024 || (ps & (ps - 1)) != 0) return SFI_ERR_RANGE;
     if (kv->max_pages < 1 || kv->num_pages < 1) return SFI_ERR_SHAPE;
     if ((long long)kv->max_seq_len > (long long)kv->max_pages * ps) return SFI_ERR_RANGE;
+    // a decode chunk's pages are staged in LDS: chunks of at most
+    // kMaxSlowChunk rows, which the split plans guarantee up to this length
+    if ((long long)kv->max_seq_len > (long long)kMaxSplits * kMaxSlowChunk) return SFI_ERR_UNSUPPORTED;
     int sh = 0;
     while ((1 << sh) < ps) ++sh;
     view->page_shift = sh;

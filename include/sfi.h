@@ -62,7 +62,8 @@ typedef enum {
  *   Contiguous (page_table == NULL): k, v are [B][Hkv][cap][d].
  *   Paged: k, v are a pool [num_pages][Hkv][page_size][d]; logical row j of
  *   sequence b lives in page page_table[b * max_pages + j / page_size] at
- *   offset j % page_size.
+ *   offset j % page_size.  max_seq_len <= 4,194,304 for a paged cache (else
+ *   SFI_ERR_UNSUPPORTED).
  * seq_len[b] (device) is the number of cached keys of sequence b, including
  * the token(s) being decoded.  max_seq_len [host] bounds seq_len over every
  * sequence a call touches; it sizes grids and workspaces.  Device values are

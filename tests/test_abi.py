@@ -257,3 +257,15 @@ def test_compact_validation():
     assert fast(kv, q=None) == sfi.SFI_ERR_NULL
     assert fast(kv, ws_bytes=8) == sfi.SFI_ERR_WORKSPACE
     assert fast(kv, batch_n=0) == sfi.SFI_OK
+
+
+def test_paged_length_limit():
+    """A paged cache longer than 4,194,304 rows is rejected (its decode chunks
+    stage their page ids in LDS)."""
+    L = sfi.lib()
+    kv = _kv(page_table=FAKE, page_size=16, max_pages=300000, num_pages=10, cap=0, max_seq_len=4194305)
+    assert L.sfi_fast_step(ctypes.byref(kv), None, 1, FAKE, FAKE, FAKE, 2, 64, 4, 256, FAKE, FAKE, 1 << 40,
+                           None) == sfi.SFI_ERR_UNSUPPORTED
+    kv.max_seq_len = 4194304
+    assert L.sfi_fast_step(ctypes.byref(kv), None, 0, FAKE, FAKE, FAKE, 2, 64, 4, 256, FAKE, FAKE, 1 << 40,
+                           None) == sfi.SFI_OK
