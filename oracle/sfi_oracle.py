@@ -113,6 +113,30 @@ def evidence(p: np.ndarray, Hkv: int) -> np.ndarray:
     return p.reshape(Hkv, G, n).mean(axis=1)
 
 
+def window_evidence(q_rows, K, V, n: int):
+    """Evidence observed over a window of w queries [SFI-it s3.B: the logits
+    observed in the slow step's window; reading: the window is the last w
+    decode queries].  Row t (0..w-1) sits at position n - w + t and attends
+    keys [0, n - w + t].  Returns (o [w][Hq][d], f [Hkv][n]) with
+    f[g, j] = (1 / (w G)) sum_t sum_{h of group g} p_t[h, j], where p_t is row
+    t's softmax over its visible keys (zero beyond them)."""
+    q_rows = _as_f64(q_rows)
+    w, Hq, d = q_rows.shape
+    Hkv = K.shape[0]
+    G = Hq // Hkv
+    o = np.empty((w, Hq, d))
+    f = np.zeros((Hkv, n))
+    for t in range(w):
+        nt = n - w + t + 1
+        l = attention_logits(q_rows[t], K, nt)
+        p = softmax_rows(l)
+        Vf = _as_f64(V[:, :nt])
+        for h in range(Hq):
+            o[t, h] = p[h] @ Vf[h // G]
+            f[h // G, :nt] += p[h]
+    return o, f / (w * G)
+
+
 # ---------------------------------------------------------------------------
 # O3: prior from cache statistics  [SFI-it s3.B prior from key norms and
 # positions; formula: the workload's choice -- parity unpinned w.r.t. pages]

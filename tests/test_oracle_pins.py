@@ -366,3 +366,59 @@ def test_slow_select_invariants():
     # context too short for any candidate
     e = O.slow_select(q, K, V, 200, lam=0.3, k=k, n_sink=ns, window=W)
     assert all(len(s) == 0 for s in e["sel"])
+
+
+# ------------------------------------------------- observation-window evidence
+
+def test_window_evidence_one_query_is_the_slow_step_evidence():
+    """w = 1 reduces to the slow step: o = dense output, f = O2's evidence."""
+    rng = np.random.default_rng(21)
+    Hq, Hkv, d, n = 8, 2, 16, 70
+    q = _rand_bits(rng, (1, Hq, d))
+    K = _rand_bits(rng, (Hkv, n, d))
+    V = _rand_bits(rng, (Hkv, n, d))
+    o, f = O.window_evidence(q, K, V, n)
+    o1, p1 = O.dense_step(q[0], K, V, n)
+    np.testing.assert_allclose(o[0], o1, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(f, O.evidence(p1, Hkv), rtol=1e-12, atol=1e-15)
+
+
+def test_window_evidence_is_the_mean_of_causal_slow_steps():
+    """f = mean over window rows of each row's own slow-step evidence at its
+    cache length n - w + t + 1, zero beyond it; rows are causal dense steps;
+    f sums to 1 per kv head."""
+    rng = np.random.default_rng(22)
+    w, Hq, Hkv, d, n = 5, 12, 3, 16, 45
+    q = _rand_bits(rng, (w, Hq, d))
+    K = _rand_bits(rng, (Hkv, n, d))
+    V = _rand_bits(rng, (Hkv, n, d))
+    o, f = O.window_evidence(q, K, V, n)
+    want = np.zeros((Hkv, n))
+    for t in range(w):
+        nt = n - w + t + 1
+        o_t, p_t = O.dense_step(q[t], K, V, nt)
+        np.testing.assert_allclose(o[t], o_t, rtol=1e-12, atol=1e-14)
+        want[:, :nt] += O.evidence(p_t, Hkv)
+    np.testing.assert_allclose(f, want / w, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(f.sum(axis=1), 1.0, rtol=1e-12)
+    # the newest keys are seen by fewer rows: key n-1 only by the last row
+    _, p_last = O.dense_step(q[w - 1], K, V, n)
+    np.testing.assert_allclose(f[:, n - 1], O.evidence(p_last, Hkv)[:, n - 1] / w, rtol=1e-12)
+
+
+def test_window_evidence_equal_keys_closed_form():
+    """All keys equal: every visible key gets probability 1/n_t in row t, so
+    f_j = (1/w) sum over rows that see j of 1/(n - w + t + 1)."""
+    rng = np.random.default_rng(23)
+    w, Hq, Hkv, d, n = 4, 4, 2, 8, 20
+    q = _rand_bits(rng, (w, Hq, d))
+    row = _rand_bits(rng, (d,))
+    K = np.broadcast_to(row, (Hkv, n, d)).copy()
+    V = _rand_bits(rng, (Hkv, n, d))
+    _, f = O.window_evidence(q, K, V, n)
+    want = np.zeros(n)
+    for t in range(w):
+        nt = n - w + t + 1
+        want[:nt] += 1.0 / nt
+    for g in range(Hkv):
+        np.testing.assert_allclose(f[g], want / w, rtol=1e-12)
