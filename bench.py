@@ -54,6 +54,9 @@ def algorithmic_bytes(kind, n, cfg, k=None):
     if kind == "fast":
         rows = min(cfg.n_sink, n) + min(cfg.window, n) + k
         return rows * Hkv * 4 * d + k * Hkv * 4 + Hq * d * 6
+    if kind.startswith("slow_window"):   # w rows: K and V, K again for the evidence
+        w = int(kind[len("slow_window"):])
+        return n * Hkv * 6 * d + w * Hq * d * 6 + n * Hkv * 8
     raise ValueError(kind)
 
 
@@ -661,7 +664,8 @@ def main():
     # busy while the host enqueues the call and its events ----------------
     _log("[bench] per-call timing pass")
     flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-    calls = {"step": [], "slow": [], "select": [], "fast": [], "step_select": []}
+    calls = {"step": [], "slow": [], "select": [], "fast": [], "step_select": [], "slow_all": [],
+             "slow_window8": []}
     bytes_by = {k_: [] for k_ in calls}
     ev = []
 
@@ -684,6 +688,26 @@ def main():
               "step_select": lambda: dec.step_select(q[s], plan.seq_len[s], plan.slow_ids[s], ns,
                                                      plan.fast_ids[s], nf, stream)}[kind]
         timed(kind, fn, nbytes)
+    # Observation-window slow step over the last 8 queries, next to the
+    # one-query slow step, for every sequence (informational; left out of
+    # the counter runs, which pair each flush-bounded segment with the
+    # calls of percall_list).
+    wq = 8
+    if plan_steps >= wq and not args.calib_copy:
+        s_w = wq - 1
+        q_win = q[s_w - wq + 1:s_w + 1].permute(1, 0, 2, 3).contiguous()
+        lens_w = ctx + s_w + 1
+        out_w = torch.empty((cfg.B, wq, cfg.Hq, cfg.d), dtype=torch.float32, device=dev)
+        ws_wb = sfi.sfi_slow_window_workspace_bytes(dec.kv, wq)
+        ws_w = torch.empty(ws_wb, dtype=torch.uint8, device=dev)
+        dec.kv.seq_len = plan.seq_len[s_w].data_ptr()
+        for _ in range(3):
+            timed("slow_all", lambda: dec.slow(q[s_w], plan.seq_len[s_w], None, cfg.B, stream, select=False),
+                  sum(algorithmic_bytes("slow", int(n), cfg) for n in lens_w))
+            timed("slow_window8", lambda: sfi.sfi_slow_step_window(dec.kv, None, cfg.B, q_win, wq, out_w,
+                                                                  dec.evidence, dec.key_norm, dec.ld, ws_w,
+                                                                  ws_wb, stream),
+                  sum(algorithmic_bytes("slow_window8", int(n), cfg) for n in lens_w))
     torch.cuda.synchronize()
     del flush
     for kind, a, b_, nbytes in ev:

@@ -121,6 +121,24 @@ struct VerWs {
   int stride, chunk;
 };
 
+// Observation-window slow step: the verify partials, then per-row stats.
+struct WinWs {
+  size_t o, ml, rstat, total;
+  int stride, chunk;
+};
+
+WinWs window_ws(const sfi_kv *kv, int w) {
+  WinWs x{};
+  x.chunk = verify_chunk_for(kv->B, kv->Hkv, kv->max_seq_len);
+  x.stride = verify_stride_for(kv->max_seq_len, x.chunk);
+  const size_t rows = (size_t)kv->B * w * kv->Hq * x.stride;
+  x.o = 0;
+  x.ml = align_up(rows * kv->d * sizeof(float));
+  x.rstat = align_up(x.ml + rows * 2 * sizeof(float));
+  x.total = align_up(x.rstat + (size_t)kv->B * w * kv->Hq * 2 * sizeof(float));
+  return x;
+}
+
 VerWs verify_ws(const sfi_kv *kv, int T) {
   VerWs w{};
   w.chunk = verify_chunk_for(kv->B, kv->Hkv, kv->max_seq_len);
@@ -658,6 +676,57 @@ sfi_status sfi_verify_aggregate(const sfi_kv *kv, const int32_t *batch_ids, int3
   a.plan.chunk = w.chunk;
   a.plan.splits = w.stride;
   a.plan.stride = w.stride;
+  return launch_verify(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SFI_OK : SFI_ERR_HIP;
+}
+
+size_t sfi_slow_window_workspace_bytes(const sfi_kv *kv, int32_t w) {
+  KVView v;
+  bool pg;
+  if (check_kv(kv, &v, &pg) != SFI_OK || w < 1 || w > 32) return 0;
+  return window_ws(kv, w).total;
+}
+
+sfi_status sfi_slow_step_window(const sfi_kv *kv, const int32_t *batch_ids, int32_t batch_n,
+                                const uint16_t *q_win, int32_t w, float *out, float *evidence,
+                                float *key_norm, int32_t ld, void *ws, size_t ws_bytes, void *stream) {
+  KVView view;
+  bool paged = false;
+  sfi_status s = check_kv(kv, &view, &paged);
+  if (s != SFI_OK) return s;
+  if ((s = check_batch(kv, batch_n)) != SFI_OK) return s;
+  if (!q_win || !out || !evidence) return SFI_ERR_NULL;
+  const int G = kv->Hq / kv->Hkv;
+  if (w < 1 || G * w > 32 || G == 5) return SFI_ERR_UNSUPPORTED;
+  if (kv->max_seq_len < w) return SFI_ERR_RANGE;
+  if (ld < kv->max_seq_len) return SFI_ERR_RANGE;
+  const WinWs x = window_ws(kv, w);
+  if (!ws) return SFI_ERR_NULL;
+  if (ws_bytes < x.total) return SFI_ERR_WORKSPACE;
+  if (batch_n == 0) return SFI_OK;
+
+  VerifyLaunch a{};
+  a.kv = view;
+  a.seq_len = kv->seq_len;
+  a.batch_ids = batch_ids;
+  a.batch_n = batch_n;
+  a.B = kv->B; a.Hq = kv->Hq; a.Hkv = kv->Hkv; a.d = kv->d; a.G = G; a.T = w;
+  a.max_seq_len = kv->max_seq_len;
+  a.paged = paged;
+  a.row_mask = 0u;
+  a.q = q_win;
+  a.out = out;
+  a.agg = nullptr;
+  a.ld = ld;
+  a.part_o = carve<float>(ws, x.o);
+  a.part_ml = carve<float>(ws, x.ml);
+  a.part_agg = nullptr;
+  a.lld = kv->max_seq_len;
+  a.plan.chunk = x.chunk;
+  a.plan.splits = x.stride;
+  a.plan.stride = x.stride;
+  a.rstat = carve<float>(ws, x.rstat);
+  a.evidence = evidence;
+  a.key_norm = key_norm;
   return launch_verify(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SFI_OK : SFI_ERR_HIP;
 }
 

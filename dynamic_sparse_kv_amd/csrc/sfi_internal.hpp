@@ -162,9 +162,14 @@ struct VerifyLaunch {
   int ld;
   float *part_o;      // [B][T*Hq][stride][d]
   float *part_ml;     // [B][T*Hq][stride][2]
-  float *part_agg;    // [B][Hkv][lld]
+  float *part_agg;    // [B][Hkv][lld], or null (observation-window slow step)
   int lld;
   SplitPlan plan;
+  // observation-window slow step: per-row (reference, sum) [B][T*Hq][2]
+  // (workspace) and the evidence / key norms [B][Hkv][ld] it writes
+  float *rstat;
+  float *evidence;
+  float *key_norm;
 };
 
 hipError_t launch_verify(const VerifyLaunch &a, hipStream_t st);

@@ -156,7 +156,7 @@ __global__ __launch_bounds__(kVThreads) void verify_partial_kernel(VArgs a) {
     for (int kk = 0; kk < KK; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t.ka[kk], qb[kk], s, 0, 0, 0);
 
     // Aggregate: masked column sum, reduce-scattered over the 32 lanes of the half.
-    {
+    if (a.part_agg) {
       float v[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) v[r] = s[r] * amask;
@@ -284,6 +284,7 @@ struct VFinal {
   int lld;
   float *agg;
   int ld;
+  float *rstat;  // [B][T*Hq][2] merged (reference, sum) per row, or null
 };
 
 // grid.x = T*Hq rows, one block of D threads each: fixed-order merge.
@@ -309,6 +310,10 @@ __global__ __launch_bounds__(D) void verify_combine_kernel(VFinal a) {
     }
   }
   a.out[((size_t)b * a.T * a.Hq + row) * D + e] = (Z > 0.f) ? o / Z : 0.f;
+  if (a.rstat && e == 0) {
+    a.rstat[((size_t)b * a.T * a.Hq + row) * 2 + 0] = M;
+    a.rstat[((size_t)b * a.T * a.Hq + row) * 2 + 1] = Z;
+  }
 }
 
 // agg[b][i] = sum over kv heads (fixed order) of the per-head partials, i < n - T.
@@ -321,6 +326,130 @@ __global__ __launch_bounds__(256) void verify_agg_kernel(VFinal a) {
     float s = 0.f;
     for (int g = 0; g < a.Hkv; ++g) s += a.part_agg[((size_t)b * a.Hkv + g) * a.lld + i];
     a.agg[(size_t)b * a.ld + i] = s;
+  }
+}
+
+// Evidence over the verify rows used as a slow step's observation window:
+// for every key j < n of kv head g,
+//   f_j = (1 / (T G)) * sum over the rows t that see j and the heads h of the
+//         group of 2^(l_thj - M_th) / Z_th,
+// with (M_th, Z_th) the row's merged softmax reference and sum (log2 domain)
+// from the combine kernel.  The keys are read again (K only) and S^T = K Q^T
+// is recomputed tile by tile on MFMA as in verify_partial_kernel; the column
+// sums use the aggregate's reduce-scatter.  Optionally writes the key norms.
+template <int D, int G, bool PAGED>
+__global__ __launch_bounds__(kVThreads) void window_evidence_kernel(VArgs a, const float *rstat,
+                                                                    float *evidence, float *key_norm,
+                                                                    int ld) {
+  constexpr int KK = D / 16;
+  const int b = batch_seq(a.batch_ids, blockIdx.z, a.B);
+  if (b < 0) return;
+  const int g = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 31, hs = lane >> 5;
+  const int n = clamp_len(a.seq_len, b, a.max_len);
+  const int T = a.T;
+  const int R = G * T;
+  const int K0 = blockIdx.x * kVWaves * a.wchunk;
+  if (K0 >= n) return;
+  const int k1 = min(n, K0 + kVWaves * a.wchunk);
+  const int k0 = K0 + 32 * wave;
+  const bool colv = col < R;
+  const int jt = colv ? col / G : 0;
+  const int jh = colv ? col % G : 0;
+  const int lim = n - T + jt;  // last key row jt sees
+  float Mc = 0.f, wc = 0.f;
+  if (colv) {
+    const size_t rrow = ((size_t)b * T + jt) * a.Hq + g * G + jh;
+    Mc = rstat[rrow * 2];
+    const float Zc = rstat[rrow * 2 + 1];
+    wc = (Zc > 0.f) ? 1.0f / (Zc * (float)R) : 0.f;
+  }
+  bf16x8_t qb[KK];
+  {
+    const uint16_t *qp = a.q + (((size_t)b * T + jt) * a.Hq + g * G + jh) * D + 8 * hs;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const uint4 t = colv ? ldg16(qp + 16 * kk) : make_uint4(0, 0, 0, 0);
+      qb[kk] = as_bf16x8(t);
+    }
+  }
+  const size_t erow = ((size_t)b * a.kv.Hkv + g) * ld;
+  struct KTile {
+    bf16x8_t ka[KK];
+  };
+  // loads issued unconditionally (a key past the range reads row k1 - 1)
+  auto load_tile = [&](KTile &t, int kb) {
+    const int key = min(kb + col, k1 - 1);
+    const uint16_t *kp = a.kv.k + kv_row<D, PAGED>(a.kv, b, g, key) + 8 * hs;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) t.ka[kk] = as_bf16x8(ldg16(kp + 16 * kk));
+  };
+  auto consume = [&](const KTile &t, int kb) {
+    f32x16_t s;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t.ka[kk], qb[kk], s, 0, 0, 0);
+    float v[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = kb + acc_key(r, hs);
+      const bool ok = key < k1 && key <= lim;
+      v[r] = ok ? exp2_hw(s[r] * a.qscale - Mc) * wc : 0.f;
+    }
+    const bool b4 = (col & 16) != 0, b3 = (col & 8) != 0, b2 = (col & 4) != 0, b1 = (col & 2) != 0;
+    float w8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float keep = b4 ? v[8 + i] : v[i];
+      const float send = b4 ? v[i] : v[8 + i];
+      w8[i] = keep + __shfl_xor(send, 16);
+    }
+    float w4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float keep = b3 ? w8[4 + i] : w8[i];
+      const float send = b3 ? w8[i] : w8[4 + i];
+      w4[i] = keep + __shfl_xor(send, 8);
+    }
+    float w2[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float keep = b2 ? w4[2 + i] : w4[i];
+      const float send = b2 ? w4[i] : w4[2 + i];
+      w2[i] = keep + __shfl_xor(send, 4);
+    }
+    float w1 = (b1 ? w2[1] : w2[0]) + __shfl_xor(b1 ? w2[0] : w2[1], 2);
+    w1 += __shfl_xor(w1, 1);
+    const int r = 8 * (int)b4 + 4 * (int)b3 + 2 * (int)b2 + (int)b1;
+    const int key = kb + acc_key(r, hs);
+    if ((col & 1) == 0 && key < k1) evidence[erow + key] = w1;
+    if (key_norm) {
+      // lane (col, hs) holds half of key kb + col's dims
+      float nn = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = (float)t.ka[kk][e];
+          nn = fmaf(x, x, nn);
+        }
+      nn += __shfl_xor(nn, 32);
+      if (hs == 0 && kb + col < k1) key_norm[erow + kb + col] = sqrtf(nn);
+    }
+  };
+  constexpr int TS = 32 * kVWaves;
+  if (k0 < k1) {
+    KTile ta, tb;
+    load_tile(ta, k0);
+    for (int kb = k0; kb < k1; kb += 2 * TS) {
+      load_tile(tb, kb + TS);
+      consume(ta, kb);
+      load_tile(ta, kb + 2 * TS);
+      consume(tb, kb + TS);
+    }
   }
 }
 
@@ -344,9 +473,15 @@ hipError_t verify_t(const VerifyLaunch &L, hipStream_t st) {
   f.seq_len = L.seq_len; f.batch_ids = L.batch_ids; f.Hq = L.Hq; f.Hkv = L.Hkv; f.T = L.T;
   f.wchunk = L.plan.chunk; f.stride = L.plan.stride; f.part_o = L.part_o; f.part_ml = L.part_ml;
   f.out = L.out; f.part_agg = L.part_agg; f.lld = L.lld; f.agg = L.agg; f.ld = L.ld;
+  f.rstat = L.rstat;
   hipLaunchKernelGGL((verify_combine_kernel<D>), dim3(L.T * L.Hq, L.batch_n), dim3(D), 0, st, f);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (L.evidence) {  // observation-window slow step: evidence instead of the aggregate
+    hipLaunchKernelGGL((window_evidence_kernel<D, G, PAGED>), dim3(wgs, L.Hkv, L.batch_n), dim3(kVThreads), 0,
+                       st, a, L.rstat, L.evidence, L.key_norm, L.ld);
+    return hipGetLastError();
+  }
   const int aggb = min(1024, (L.max_seq_len + 255) / 256);
   hipLaunchKernelGGL(verify_agg_kernel, dim3(aggb > 0 ? aggb : 1, L.batch_n), dim3(256), 0, st, f);
   return hipGetLastError();

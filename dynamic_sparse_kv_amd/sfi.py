@@ -90,6 +90,11 @@ def lib():
         L.sfi_fast_step.argtypes = [P(sfi_kv), _vp, _c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int,
                                     _c_int, _vp, _vp, _sz, _vp]
         L.sfi_fast_step.restype = _c_int
+        L.sfi_slow_window_workspace_bytes.argtypes = [P(sfi_kv), _c_int]
+        L.sfi_slow_window_workspace_bytes.restype = _sz
+        L.sfi_slow_step_window.argtypes = [P(sfi_kv), _vp, _c_int, _vp, _c_int, _vp, _vp, _vp, _c_int, _vp,
+                                           _sz, _vp]
+        L.sfi_slow_step_window.restype = _c_int
         L.sfi_compact_selected.argtypes = [P(sfi_kv), _vp, _c_int, _vp, _vp, _c_int, _c_int, _vp, _vp, _vp]
         L.sfi_compact_selected.restype = _c_int
         L.sfi_fast_step_compact.argtypes = [P(sfi_kv), _vp, _c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int,
@@ -227,6 +232,17 @@ def sfi_fast_step(kv: sfi_kv, batch_ids, batch_n: int, q, sel_idx, sel_count, se
     _check(lib().sfi_fast_step(ctypes.byref(kv), _ptr(batch_ids), batch_n, _ptr(q), _ptr(sel_idx),
                                _ptr(sel_count), sel_heads, sel_k, n_sink, window, _ptr(out),
                                _ptr(ws), ws_bytes, _stream(stream)), "sfi_fast_step")
+
+
+def sfi_slow_window_workspace_bytes(kv: sfi_kv, w: int) -> int:
+    return int(lib().sfi_slow_window_workspace_bytes(ctypes.byref(kv), w))
+
+
+def sfi_slow_step_window(kv: sfi_kv, batch_ids, batch_n: int, q_win, w: int, out, evidence, key_norm,
+                         ld: int, ws, ws_bytes: int, stream=None):
+    _check(lib().sfi_slow_step_window(ctypes.byref(kv), _ptr(batch_ids), batch_n, _ptr(q_win), w, _ptr(out),
+                                      _ptr(evidence), _ptr(key_norm), ld, _ptr(ws), ws_bytes, _stream(stream)),
+           "sfi_slow_step_window")
 
 
 def sfi_compact_selected(kv: sfi_kv, batch_ids, batch_n: int, sel_idx, sel_count, sel_heads: int,

@@ -196,6 +196,28 @@ sfi_status sfi_fast_step_compact(const sfi_kv *kv, const int32_t *batch_ids, int
                                  const uint16_t *ck, const uint16_t *cv, float *out, void *ws,
                                  size_t ws_bytes, void *stream);
 
+/* Slow step with a multi-query observation window [SFI 3.B: the evidence is
+ * the attention observed in the slow step's window; here the window is the
+ * last w decode queries of the sequence].  Row t (0..w-1) of q_win sits at
+ * position n - w + t (n = seq_len[b]) and attends keys [0, n - w + t]:
+ *   out[b][t][h]   that row's attention output (row w-1 is the decode step);
+ *   evidence[b][g][j] = (1/(w G)) sum_t sum_{h of group g} p_t[h][j], j < n,
+ *                  the rows' softmax probabilities (zero past a row's last
+ *                  key) averaged over the window and the group: with w = 1
+ *                  it is sfi_slow_step's evidence;
+ *   key_norm[b][g][j] = ||k_j|| for j < n (optional).
+ * Then sfi_select (FUSED) forms the selection as after sfi_slow_step.
+ *   q_win [B][w][Hq][d] bf16; out [B][w][Hq][d] fp32; evidence, key_norm
+ *   [B][Hkv][ld] fp32, ld >= max_seq_len; w <= max_seq_len.
+ * Needs w * (Hq/Hkv) <= 32 and Hq/Hkv != 5 (SFI_ERR_UNSUPPORTED otherwise):
+ * the w x G rows of a kv head are one 32-column MFMA tile.  The keys are read
+ * twice (K, V for the outputs and the rows' softmax sums, then K again for
+ * the evidence): 6 d bytes per key and kv head. */
+size_t sfi_slow_window_workspace_bytes(const sfi_kv *kv, int32_t w);
+sfi_status sfi_slow_step_window(const sfi_kv *kv, const int32_t *batch_ids, int32_t batch_n,
+                                const uint16_t *q_win, int32_t w, float *out, float *evidence,
+                                float *key_norm, int32_t ld, void *ws, size_t ws_bytes, void *stream);
+
 /* One decode step of a batch whose sequences take different paths [SFI 3.A
  * slow and fast steps; 3.C, which overlaps the slow path with fast steps]:
  * the slow step (dense attention with evidence) of slow_ids[0..n_slow) and the

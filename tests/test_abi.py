@@ -269,3 +269,22 @@ def test_paged_length_limit():
     kv.max_seq_len = 4194304
     assert L.sfi_fast_step(ctypes.byref(kv), None, 0, FAKE, FAKE, FAKE, 2, 64, 4, 256, FAKE, FAKE, 1 << 40,
                            None) == sfi.SFI_OK
+
+
+def test_slow_window_validation():
+    L = sfi.lib()
+
+    def call(kv, w=8, ld=1000, ws_bytes=1 << 40, ev=FAKE, batch_n=1):
+        return L.sfi_slow_step_window(ctypes.byref(kv), None, batch_n, FAKE, w, FAKE, ev, None, ld, FAKE,
+                                      ws_bytes, None)
+
+    kv = _kv(Hq=32, Hkv=8)
+    assert call(kv, w=9) == sfi.SFI_ERR_UNSUPPORTED                 # 4 x 9 rows > one 32-column tile
+    assert call(kv, w=0) == sfi.SFI_ERR_UNSUPPORTED
+    assert call(_kv(Hq=40, Hkv=8), w=4) == sfi.SFI_ERR_UNSUPPORTED  # G = 5
+    assert call(kv, ld=899) == sfi.SFI_ERR_RANGE
+    assert call(kv, ev=None) == sfi.SFI_ERR_NULL
+    assert call(kv, ws_bytes=8) == sfi.SFI_ERR_WORKSPACE
+    assert call(kv, batch_n=0) == sfi.SFI_OK
+    assert L.sfi_slow_window_workspace_bytes(ctypes.byref(kv), 8) > 0
+    assert L.sfi_slow_window_workspace_bytes(ctypes.byref(kv), 0) == 0

@@ -739,6 +739,74 @@ def test_paged_cache_matches_contiguous_and_oracle():
         assert row_rel_err(out[b], o_ref) <= OUT_TOL
 
 
+@pytest.mark.parametrize("Hq,Hkv,d,w,paged", [(32, 8, 128, 8, False), (8, 2, 64, 4, True),
+                                               (8, 8, 128, 16, False), (16, 8, 128, 1, False)])
+def test_slow_step_window_matches_oracle(Hq, Hkv, d, w, paged):
+    """sfi_slow_step_window: every window row's output, the window evidence
+    and the key norms against the oracle (ragged lengths spanning several
+    workgroups, a length not a multiple of the tile); with w = 1 the evidence
+    is sfi_slow_step's; the FUSED selection over it matches the oracle's."""
+    _say(f"slow window Hq={Hq} Hkv={Hkv} d={d} w={w} paged={paged}")
+    B, cap = 2, 3008
+    K, V = _rand_kv(B, Hkv, cap, d, seed=80 + w, hh=6)
+    lens = [2999, 1717]
+    seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    q = _rand_q((B, w, Hq, d), seed=81 + w)
+    ml = max(lens)
+    ld = ml + 5
+    Kc, Vc = K, V
+    table = None
+    if paged:
+        cfg = W.CONFIGS["c5"].replace(B=B, Hq=Hq, Hkv=Hkv, d=d)
+        table, npages = W.page_table(cfg, np.full(B, cap))
+        K = W.to_paged(K, table, npages, 16)
+        V = W.to_paged(V, table, npages, 16)
+        tab = torch.from_numpy(table).to(DEV)      # kept alive: kv holds its raw pointer
+        kv = sfi.make_kv(K, V, seq, Hq, ml, tab, 16)
+    else:
+        kv = sfi.make_kv(K, V, seq, Hq, ml)
+    wsb = sfi.sfi_slow_window_workspace_bytes(kv, w)
+    assert wsb > 0
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=DEV)
+    out = torch.full((B, w, Hq, d), float("nan"), device=DEV)
+    ev = torch.full((B, Hkv, ld), float("nan"), device=DEV)
+    nrm = torch.full((B, Hkv, ld), float("nan"), device=DEV)
+    sfi.sfi_slow_step_window(kv, None, B, q, w, out, ev, nrm, ld, ws, wsb)
+    torch.cuda.synchronize()
+    Kb, Vb, qb = _bits(Kc), _bits(Vc), _bits(q)
+    o_g, ev_g, nrm_g = out.cpu().numpy(), ev.cpu().numpy(), nrm.cpu().numpy()
+    f_refs = []
+    for b in range(B):
+        n = lens[b]
+        o_ref, f_ref = O.window_evidence(qb[b], Kb[b], Vb[b], n)
+        f_refs.append(f_ref)
+        assert row_rel_err(o_g[b], o_ref) <= OUT_TOL
+        assert row_rel_err(ev_g[b, :, :n], f_ref) <= EVID_TOL
+        np.testing.assert_allclose(ev_g[b, :, :n].sum(axis=1), 1.0, rtol=1e-4)
+        np.testing.assert_allclose(nrm_g[b, :, :n], O.key_norms(Kb[b], n), rtol=NORM_TOL)
+        assert np.isnan(ev_g[b, :, n:]).all()          # nothing past the sequence
+    if w == 1:
+        dec = SFIDecoder(Kc, Vc, Hq, ml, n_sink=4, window=256, k=256, lam=0.3)
+        dec.slow(q[:, 0].contiguous(), seq, None, B, select=False)
+        torch.cuda.synchronize()
+        for b in range(B):
+            n = lens[b]
+            assert row_rel_err(ev_g[b, :, :n], dec.evidence[b, :, :n].cpu().numpy()) <= EVID_TOL
+    # the selector over the window evidence
+    k = 300
+    sel, cnt, fo = _select_gpu(sfi.SFI_SCORE_FUSED, torch.nan_to_num(ev[:, :, :ml]).contiguous(),
+                               torch.nan_to_num(nrm[:, :, :ml]).contiguous(), lens, k, 4, 256, lam=0.3,
+                               fused=True)
+    ties = 0
+    for b in range(B):
+        n = lens[b]
+        s_ref = O.fuse(f_refs[b], O.prior(Kb[b], n), 0.3)
+        lo, hi = O.candidate_range(n, 4, 256)
+        for g in range(Hkv):
+            ties += check_selection(sel[b, g], cnt[b, g], s_ref[g], lo, hi, k)
+    _say(f"  near-tie differences: {ties}")
+
+
 @pytest.mark.parametrize("paged", [False, True])
 def test_fast_compact_matches_index_gather(paged):
     """sfi_compact_selected + sfi_fast_step_compact: the same outputs bit for
