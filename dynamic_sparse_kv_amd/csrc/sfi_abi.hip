@@ -19,11 +19,13 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool supported_group(int G) { return G == 1 || G == 2 || G == 4 || G == 5 || G == 8; }
 
 // Validates the cache description; on success fills the device view.
-bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+bool aligned16(const void *p) { return aligned(p, 16); }
 
 sfi_status check_kv(const sfi_kv *kv, KVView *view, bool *paged) {
   if (!kv) return SFI_ERR_NULL;
   if (!kv->k || !kv->v || !kv->seq_len) return SFI_ERR_NULL;
+  if (!aligned16(kv->k) || !aligned16(kv->v)) return SFI_ERR_RANGE;
   if (kv->B < 1 || kv->Hq < 1 || kv->Hkv < 1 || kv->Hq % kv->Hkv != 0) return SFI_ERR_SHAPE;
   if (kv->d != 64 && kv->d != 128) return SFI_ERR_UNSUPPORTED;
   if (!supported_group(kv->Hq / kv->Hkv)) return SFI_ERR_UNSUPPORTED;
@@ -177,6 +179,7 @@ sfi_status select_launch(const sfi_select_params *p, const int32_t *batch_ids, i
   }
   const SelWs w = select_ws(B, H, max_seq_len);
   if (!ws) return SFI_ERR_NULL;
+  if (!aligned(ws, kAlign)) return SFI_ERR_RANGE;
   if (ws_bytes < w.total) return SFI_ERR_WORKSPACE;
 
   SelectLaunch &a = *out;
@@ -312,9 +315,11 @@ sfi_status sfi_slow_step(const sfi_kv *kv, const int32_t *batch_ids, int32_t bat
   if (s != SFI_OK) return s;
   if ((s = check_batch(kv, batch_n)) != SFI_OK) return s;
   if (!q || !out) return SFI_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(out, 16)) return SFI_ERR_RANGE;
   if ((evidence || key_norm) && ld < kv->max_seq_len) return SFI_ERR_RANGE;
   const SlowWs w = slow_ws(kv);
   if (!ws) return SFI_ERR_NULL;
+  if (!aligned(ws, kAlign)) return SFI_ERR_RANGE;
   if (ws_bytes < w.total) return SFI_ERR_WORKSPACE;
   if (batch_n == 0) return SFI_OK;
   const AttnLaunch a = slow_launch(kv, view, paged, w, ws, batch_ids, batch_n, q, out, evidence,
@@ -344,6 +349,7 @@ sfi_status sfi_decode_step(const sfi_kv *kv, const int32_t *slow_ids, int32_t n_
   if ((s = check_batch(kv, n_fast)) != SFI_OK) return s;
   if (n_slow + n_fast > kv->B) return SFI_ERR_RANGE;
   if (!q || !out) return SFI_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(out, 16)) return SFI_ERR_RANGE;
   if (n_slow > 0 && !evidence) return SFI_ERR_NULL;
   if (n_slow > 0 && ld < kv->max_seq_len) return SFI_ERR_RANGE;
   if (n_fast > 0 && (s = check_fast(kv, sel_idx, sel_count, sel_heads, sel_k, n_sink, window)) != SFI_OK)
@@ -352,6 +358,7 @@ sfi_status sfi_decode_step(const sfi_kv *kv, const int32_t *slow_ids, int32_t n_
   const SlowWs sw = slow_ws(kv);
   const FastWs fw = fast_ws(kv, sel_k, n_sink, window);
   if (!ws) return SFI_ERR_NULL;
+  if (!aligned(ws, kAlign)) return SFI_ERR_RANGE;
   if (ws_bytes < sw.total + fw.total) return SFI_ERR_WORKSPACE;
   if (n_slow == 0 && n_fast == 0) return SFI_OK;
   void *ws_fast = static_cast<char *>(ws) + sw.total;
@@ -398,6 +405,7 @@ sfi_status sfi_decode_step_select(const sfi_kv *kv, const sfi_select_params *p,
   if ((s = check_batch(kv, n_fast)) != SFI_OK) return s;
   if (n_slow + n_fast > kv->B) return SFI_ERR_RANGE;
   if (!q || !out || !sel_idx || !sel_count) return SFI_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(out, 16)) return SFI_ERR_RANGE;
   if (n_slow > 0 && (!evidence || !key_norm)) return SFI_ERR_NULL;
   if (n_slow > 0 && ld < kv->max_seq_len) return SFI_ERR_RANGE;
   if (n_fast > 0 &&
@@ -408,6 +416,7 @@ sfi_status sfi_decode_step_select(const sfi_kv *kv, const sfi_select_params *p,
   const SelWs ew = select_ws(kv->B, kv->Hkv, kv->max_seq_len);
   const size_t nsum_bytes = align_up((size_t)kv->B * kv->Hkv * sw.stride * 2 * sizeof(double));
   if (!ws) return SFI_ERR_NULL;
+  if (!aligned(ws, kAlign)) return SFI_ERR_RANGE;
   if (ws_bytes < sw.total + fw.total + ew.total + nsum_bytes) return SFI_ERR_WORKSPACE;
   if (n_slow == 0 && n_fast == 0) return SFI_OK;
   char *base = static_cast<char *>(ws);
@@ -459,6 +468,7 @@ sfi_status sfi_decode_layer_step(const sfi_kv *kv, const sfi_select_params *p, c
   if ((s = check_batch(kv, n_fast)) != SFI_OK) return s;
   if (n_slow + n_fast > kv->B) return SFI_ERR_RANGE;
   if (!q || !out || !sel_idx || !sel_count) return SFI_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(out, 16)) return SFI_ERR_RANGE;
   if (n_slow > 0 && (!evidence || !key_norm)) return SFI_ERR_NULL;
   if (n_slow > 0 && ld < kv->max_seq_len) return SFI_ERR_RANGE;
   if (n_fast > 0 &&
@@ -469,6 +479,7 @@ sfi_status sfi_decode_layer_step(const sfi_kv *kv, const sfi_select_params *p, c
   const SelWs ew = select_ws(kv->B, kv->Hkv, kv->max_seq_len);
   const size_t nsum_bytes = align_up((size_t)kv->B * kv->Hkv * sw.stride * 2 * sizeof(double));
   if (!ws) return SFI_ERR_NULL;
+  if (!aligned(ws, kAlign)) return SFI_ERR_RANGE;
   if (ws_bytes < sw.total + fw.total + ew.total + nsum_bytes) return SFI_ERR_WORKSPACE;
   char *base = static_cast<char *>(ws);
   void *ws_fast = base + sw.total;
@@ -563,9 +574,11 @@ sfi_status sfi_fast_step(const sfi_kv *kv, const int32_t *batch_ids, int32_t bat
   if (s != SFI_OK) return s;
   if ((s = check_batch(kv, batch_n)) != SFI_OK) return s;
   if (!q || !out) return SFI_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(out, 16)) return SFI_ERR_RANGE;
   if ((s = check_fast(kv, sel_idx, sel_count, sel_heads, sel_k, n_sink, window)) != SFI_OK) return s;
   const FastWs w = fast_ws(kv, sel_k, n_sink, window);
   if (!ws) return SFI_ERR_NULL;
+  if (!aligned(ws, kAlign)) return SFI_ERR_RANGE;
   if (ws_bytes < w.total) return SFI_ERR_WORKSPACE;
   if (batch_n == 0) return SFI_OK;
   const AttnLaunch a = fast_launch(kv, view, paged, w, ws, batch_ids, batch_n, q, out, sel_idx,
@@ -611,11 +624,13 @@ sfi_status sfi_fast_step_compact(const sfi_kv *kv, const int32_t *batch_ids, int
   if (s != SFI_OK) return s;
   if ((s = check_batch(kv, batch_n)) != SFI_OK) return s;
   if (!q || !out) return SFI_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(out, 16)) return SFI_ERR_RANGE;
   if ((s = check_fast(kv, sel_idx, sel_count, sel_heads, sel_k, n_sink, window)) != SFI_OK) return s;
   if (!ck || !cv) return SFI_ERR_NULL;
   if (!aligned16(ck) || !aligned16(cv)) return SFI_ERR_RANGE;
   const FastWs w = fast_ws(kv, sel_k, n_sink, window);
   if (!ws) return SFI_ERR_NULL;
+  if (!aligned(ws, kAlign)) return SFI_ERR_RANGE;
   if (ws_bytes < w.total) return SFI_ERR_WORKSPACE;
   if (batch_n == 0) return SFI_OK;
   AttnLaunch a = fast_launch(kv, view, paged, w, ws, batch_ids, batch_n, q, out, sel_idx, sel_count,
@@ -644,6 +659,7 @@ sfi_status sfi_verify_aggregate(const sfi_kv *kv, const int32_t *batch_ids, int3
   if (s != SFI_OK) return s;
   if ((s = check_batch(kv, batch_n)) != SFI_OK) return s;
   if (!q || !out || !agg) return SFI_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(out, 16)) return SFI_ERR_RANGE;
   const int G = kv->Hq / kv->Hkv;
   if (T < 1 || G * T > 32) return SFI_ERR_UNSUPPORTED;
   if (G == 5) return SFI_ERR_UNSUPPORTED;
@@ -653,6 +669,7 @@ sfi_status sfi_verify_aggregate(const sfi_kv *kv, const int32_t *batch_ids, int3
   if (ld < kv->max_seq_len - T) return SFI_ERR_RANGE;
   const VerWs w = verify_ws(kv, T);
   if (!ws) return SFI_ERR_NULL;
+  if (!aligned(ws, kAlign)) return SFI_ERR_RANGE;
   if (ws_bytes < w.total) return SFI_ERR_WORKSPACE;
   if (batch_n == 0) return SFI_OK;
 
@@ -695,12 +712,14 @@ sfi_status sfi_slow_step_window(const sfi_kv *kv, const int32_t *batch_ids, int3
   if (s != SFI_OK) return s;
   if ((s = check_batch(kv, batch_n)) != SFI_OK) return s;
   if (!q_win || !out || !evidence) return SFI_ERR_NULL;
+  if (!aligned(q_win, 16) || !aligned(out, 16)) return SFI_ERR_RANGE;
   const int G = kv->Hq / kv->Hkv;
   if (w < 1 || G * w > 32 || G == 5) return SFI_ERR_UNSUPPORTED;
   if (kv->max_seq_len < w) return SFI_ERR_RANGE;
   if (ld < kv->max_seq_len) return SFI_ERR_RANGE;
   const WinWs x = window_ws(kv, w);
   if (!ws) return SFI_ERR_NULL;
+  if (!aligned(ws, kAlign)) return SFI_ERR_RANGE;
   if (ws_bytes < x.total) return SFI_ERR_WORKSPACE;
   if (batch_n == 0) return SFI_OK;
 

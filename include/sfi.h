@@ -30,6 +30,9 @@
  *     synchronisation.
  *   - K/V/Q are bf16 bit patterns (uint16_t).  Outputs are fp32.  Logits are
  *     q.k / sqrt(d); query head h reads kv head h / (Hq / Hkv).
+ *   - K, V, queries, attention outputs and compact copies are 16-byte
+ *     aligned and workspaces 256-byte aligned (SFI_ERR_RANGE otherwise);
+ *     device allocators return such addresses.
  *   - A batch is a list of sequence ids (`batch_ids`, int32, device, length
  *     `batch_n`; NULL means 0..batch_n-1).  Results are written at each
  *     sequence's own slot b, so full-batch buffers can be shared by calls

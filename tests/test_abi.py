@@ -179,7 +179,7 @@ def test_layer_step_validation():
         d.B, d.H, d.max_seq_len = 2, 2, 900
         d.evidence, d.key_norm, d.ld = FAKE + 192, FAKE + 256, 1000
         d.sel_idx, d.sel_count, d.fused_out = FAKE + 320, FAKE + 384, None
-        d.ws, d.ws_bytes = FAKE + 448, 1 << 40
+        d.ws, d.ws_bytes = FAKE + 512, 1 << 40
         for k, v in over.items():
             setattr(d, k, v)
         return d
@@ -206,6 +206,7 @@ def test_layer_step_validation():
     assert call(kv, deferred(B=0), out) == sfi.SFI_ERR_SHAPE
     assert call(kv, deferred(ld=10), out) == sfi.SFI_ERR_RANGE
     assert call(kv, deferred(ws_bytes=8), out) == sfi.SFI_ERR_WORKSPACE
+    assert call(kv, deferred(ws=FAKE + 520), out) == sfi.SFI_ERR_RANGE          # workspaces 256-byte aligned
     assert call(kv, deferred(key_norm=None), out) == sfi.SFI_ERR_NULL
     assert call(kv, None, out, n_slow=kv.B, n_fast=1) == sfi.SFI_ERR_RANGE    # this call's own checks
     assert call(_kv(d=256), None, out) == sfi.SFI_ERR_UNSUPPORTED
@@ -288,3 +289,20 @@ def test_slow_window_validation():
     assert call(kv, batch_n=0) == sfi.SFI_OK
     assert L.sfi_slow_window_workspace_bytes(ctypes.byref(kv), 8) > 0
     assert L.sfi_slow_window_workspace_bytes(ctypes.byref(kv), 0) == 0
+
+
+def test_alignment_requirements():
+    """K/V, queries and outputs are 16-byte aligned, workspaces 256-byte
+    aligned: misaligned pointers are rejected before any launch."""
+    L = sfi.lib()
+
+    def fast(kv, q=FAKE, out=FAKE, ws=FAKE):
+        return L.sfi_fast_step(ctypes.byref(kv), None, 1, q, FAKE, FAKE, 2, 64, 4, 256, out, ws, 1 << 40, None)
+
+    assert fast(_kv(k=FAKE + 8)) == sfi.SFI_ERR_RANGE
+    assert fast(_kv(v=FAKE + 2)) == sfi.SFI_ERR_RANGE
+    assert fast(_kv(), q=FAKE + 4) == sfi.SFI_ERR_RANGE
+    assert fast(_kv(), out=FAKE + 12) == sfi.SFI_ERR_RANGE
+    assert fast(_kv(), ws=FAKE + 128) == sfi.SFI_ERR_RANGE
+    assert L.sfi_slow_step(ctypes.byref(_kv()), None, 1, FAKE, FAKE, None, None, 1000, FAKE + 64, 1 << 40,
+                           None) == sfi.SFI_ERR_RANGE
