@@ -13,7 +13,10 @@ namespace sfi {
 // multiple of kSplitGranule rows, at most kMaxSplits per pair.
 constexpr int kSplitGranule = 32;
 constexpr int kMaxSplits = 512;
-constexpr int kMaxFastChunk = 1024;  // fast-step chunks stage their row ids in LDS
+#ifndef SFI_MAX_FAST_CHUNK
+#define SFI_MAX_FAST_CHUNK 1024
+#endif
+constexpr int kMaxFastChunk = SFI_MAX_FAST_CHUNK;  // fast-step chunks stage their row ids in LDS
 // Rows per workgroup of a dense or slow step at most.  Splits are planned
 // from the longest sequence of the batch (its lengths are on the device), so
 // without a cap a long sequence in a ragged batch gets a few huge chunks

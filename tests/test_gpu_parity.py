@@ -739,6 +739,89 @@ def test_paged_cache_matches_contiguous_and_oracle():
         assert row_rel_err(out[b], o_ref) <= OUT_TOL
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shapes_step_select_then_fast(seed):
+    """Seeded sweep over shapes and parameters: GQA group 1/2/4/5/8, d 64/128,
+    contiguous or paged, ragged lengths from 1 to ~6000 (several below
+    sinks + window), sinks 0/4/16, window 0/64/256, k 16..1000, lambda 0..1.
+    One sfi_decode_step_select over a random slow/fast split (fast sequences
+    use planted selections), then a fast step for every sequence a few keys
+    later with the new selections; all against the oracle."""
+    rng = np.random.default_rng(1000 + seed)
+    Hq, Hkv = [(8, 2), (32, 8), (40, 8), (8, 8), (16, 2), (16, 8)][rng.integers(6)]
+    d = int(rng.choice([64, 128]))
+    paged = bool(rng.integers(2))
+    B = int(rng.integers(1, 6))
+    n_sink = int(rng.choice([0, 4, 16]))
+    window = int(rng.choice([0, 64, 256]))
+    k = int(rng.choice([16, 200, 1000]))
+    lam = float(rng.choice([0.0, 0.3, 1.0]))
+    lens = [int(x) for x in rng.integers(1, 6000, size=B)]
+    lens[int(rng.integers(B))] = int(rng.integers(1, n_sink + window + 8))   # short one
+    adv = int(rng.integers(1, 9))
+    cap = (max(lens) + adv + 15) // 16 * 16
+    _say(f"random seed={seed}: Hq={Hq} Hkv={Hkv} d={d} paged={paged} B={B} lens={lens} "
+         f"sinks={n_sink} window={window} k={k} lam={lam}")
+    K, V = _rand_kv(B, Hkv, cap, d, seed=2000 + seed, hh=5)
+    q0 = _rand_q((B, Hq, d), seed=3000 + seed)
+    q1 = _rand_q((B, Hq, d), seed=4000 + seed)
+    ml = max(lens) + adv
+    kw = {}
+    if paged:
+        cfg = W.CONFIGS["c5"].replace(B=B, Hq=Hq, Hkv=Hkv, d=d)
+        table, npages = W.page_table(cfg, np.full(B, cap))
+        Kd, Vd = W.to_paged(K, table, npages, 16), W.to_paged(V, table, npages, 16)
+        kw = dict(page_table=torch.from_numpy(table).to(DEV), page_size=16)
+    else:
+        Kd, Vd = K, V
+    dec = SFIDecoder(Kd, Vd, Hq, ml, n_sink=n_sink, window=window, k=k, lam=lam, **kw)
+    # planted selections for the sequences that take a fast step
+    sel0 = np.full((B, Hkv, k), -1, dtype=np.int32)
+    cnt0 = np.zeros((B, Hkv), dtype=np.int32)
+    for b in range(B):
+        for g in range(Hkv):
+            c = min(k, lens[b], int(rng.integers(0, k + 1)))
+            sel0[b, g, :c] = np.sort(rng.choice(lens[b], c, replace=False))
+            cnt0[b, g] = c
+    dec.sel_idx.copy_(torch.from_numpy(sel0))
+    dec.sel_count.copy_(torch.from_numpy(cnt0))
+    order = rng.permutation(B)
+    n_slow = int(rng.integers(1, B + 1))
+    slow_b, fast_b = [int(x) for x in order[:n_slow]], [int(x) for x in order[n_slow:]]
+    seq0 = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    sids = torch.tensor(slow_b, dtype=torch.int32, device=DEV)
+    fids = torch.tensor(fast_b if fast_b else [0], dtype=torch.int32, device=DEV)
+    dec.step_select(q0, seq0, sids, len(slow_b), fids, len(fast_b))
+    torch.cuda.synchronize()
+    out = dec.out.cpu().numpy()
+    sel = dec.sel_idx.cpu().numpy()
+    cnt = dec.sel_count.cpu().numpy()
+    Kb, Vb = _bits(K), _bits(V)
+    qb0, qb1 = _bits(q0), _bits(q1)
+    ties = 0
+    for b in slow_b:
+        n = lens[b]
+        r = O.slow_select(qb0[b], Kb[b], Vb[b], n, lam=lam, k=k, n_sink=n_sink, window=window)
+        assert row_rel_err(out[b], r["o"]) <= OUT_TOL
+        for g in range(Hkv):
+            ties += check_selection(sel[b, g], cnt[b, g], r["s"][g], r["lo"], r["hi"], k)
+    for b in fast_b:
+        lists = [sel0[b, g, : cnt0[b, g]] for g in range(Hkv)]
+        o_ref = O.fast_step(qb0[b], Kb[b], Vb[b], lens[b], lists, n_sink, window)
+        assert row_rel_err(out[b], o_ref) <= OUT_TOL
+    # every sequence a few keys later, with the selections now held
+    lens1 = [n + adv for n in lens]
+    seq1 = torch.tensor(lens1, dtype=torch.int32, device=DEV)
+    dec.fast(q1, seq1, None, B)
+    torch.cuda.synchronize()
+    out1 = dec.out.cpu().numpy()
+    for b in range(B):
+        lists = [sel[b, g, : cnt[b, g]] for g in range(Hkv)]
+        o_ref = O.fast_step(qb1[b], Kb[b], Vb[b], lens1[b], lists, n_sink, window)
+        assert row_rel_err(out1[b], o_ref) <= OUT_TOL
+    _say(f"  near-tie differences: {ties}")
+
+
 @pytest.mark.parametrize("Hq,Hkv,d,w,paged", [(32, 8, 128, 8, False), (8, 2, 64, 4, True),
                                                (8, 8, 128, 16, False), (16, 8, 128, 1, False)])
 def test_slow_step_window_matches_oracle(Hq, Hkv, d, w, paged):
