@@ -75,8 +75,9 @@ struct PartialArgs {
   float *part_ml;
   float *logits;
   int lld;
-  float *key_norm;
+  float *key_norm;  // evidence mode: never null (workspace rows when the caller passes none)
   int ld;
+  int nld;          // row stride of key_norm
   const int32_t *sel_idx;
   const int32_t *sel_count;
   int sel_heads, sel_k, n_sink, window;
@@ -184,7 +185,8 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
   // One pipeline stage: U rows per lane group, K and V slices of DPL dims.
   struct Stage {
     uint4 k[U][NV], v[U][NV];
-    int j[U];
+    int j[U];   // key id, -1 for a masked row
+    int js[U];  // dense/slow: the row actually read (a masked row reads the chunk's last row)
   };
   // Compact rows: list position p >= nfix is entry p - nfix of the selection,
   // row p - nfix of the compact copy; the address needs no index, so a chunk
@@ -319,24 +321,29 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int p = base + u * RPB;
-      int j;
+      int j, jr;
       if constexpr (MODE == MODE_FAST) {
         j = s_idx[min(p - p0, a.chunk - 1)];
         j = (p < p1) ? j : -1;
+        jr = max(j, 0);
       } else {
+        // a masked lane reads the chunk's last row, so the logits and norm it
+        // stores in evidence mode are that row's own (see consume())
         j = (p < p1) ? p : -1;
+        jr = min(p, p1 - 1);
       }
       st.j[u] = j;
+      st.js[u] = jr;
       size_t off;
       if constexpr (PAGED) {
         const int sh = a.kv.page_shift;
         int pg;
         if constexpr (MODE == MODE_FAST) pg = s_pg[min(p - p0, a.chunk - 1)];
-        else pg = s_pg[min((max(j, p0) >> sh) - (p0 >> sh), kPgSlots - 1)];
+        else pg = s_pg[min((jr >> sh) - (p0 >> sh), kPgSlots - 1)];
         pg = min(max(pg, 0), a.kv.num_pages - 1);
-        off = ((((size_t)pg * a.kv.Hkv + g) << sh) + (size_t)(max(j, 0) & ((1 << sh) - 1))) * D;
+        off = ((((size_t)pg * a.kv.Hkv + g) << sh) + (size_t)(jr & ((1 << sh) - 1))) * D;
       } else {
-        off = kv_row<D, false>(a.kv, b, g, max(j, 0));
+        off = kv_row<D, false>(a.kv, b, g, jr);
       }
 #pragma unroll
       for (int c = 0; c < NV; ++c) {
@@ -355,7 +362,7 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
     }
   };
   auto consume = [&](const Stage &st) {
-    float l[U][G];
+    float l[U][G], lr[U][G];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
 #pragma unroll
@@ -369,7 +376,8 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
           sdot = dot2_bf16(qv[h][4 * c + 3], st.k[u][c].w, sdot);
         }
         sdot = group_sum<LPR>(sdot);
-        l[u][h] = (st.j[u] >= 0) ? sdot * a.qscale : -INFINITY;
+        lr[u][h] = sdot * a.qscale;
+        l[u][h] = (st.j[u] >= 0) ? lr[u][h] : -INFINITY;
       }
     }
     if constexpr (EVID) {
@@ -384,21 +392,22 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
           nn = dot2_bf16(st.k[u][c].w, st.k[u][c].w, nn);
         }
         nn = group_sum<LPR>(nn);
-        const int j = st.j[u];
-        if (j >= 0) {
-          if (sub < G) {
-            float v = l[u][0];
+        // Every lane stores, with no branch: on gfx950 stores share the
+        // vector-memory counter with loads, and a store the compiler cannot
+        // count (one behind a per-lane branch) makes the next stage's wait
+        // drain it too.  Lanes past the group's G heads repeat a head's
+        // logit, every lane of the group stores the same norm, and a masked
+        // row rewrites the chunk's last row with that row's own values.
+        const int js = st.js[u];
+        float v = lr[u][0];
 #pragma unroll
-            for (int h = 1; h < G; ++h) v = (sub == h) ? l[u][h] : v;
-            a.logits[(lrow * a.lld + j) * G + sub] = v;
-          }
-          if (sub == G % LPR) {
-            const float nv = sqrtf(nn);
-            if (a.key_norm) a.key_norm[lrow * a.ld + j] = nv;
-            ns1 += (double)nv;
-            ns2 = fma((double)nv, (double)nv, ns2);
-          }
-        }
+        for (int h = 1; h < G; ++h) v = (sub % G == h) ? lr[u][h] : v;
+        a.logits[(lrow * a.lld + js) * G + sub % G] = v;
+        const float nv = sqrtf(nn);
+        a.key_norm[lrow * a.nld + js] = nv;
+        const bool acc = st.j[u] >= 0 && sub == G % LPR;
+        ns1 += acc ? (double)nv : 0.0;
+        ns2 = acc ? fma((double)nv, (double)nv, ns2) : ns2;
       }
     }
 #pragma unroll
@@ -974,7 +983,7 @@ PartialArgs partial_args(const AttnLaunch &a) {
   p.B = a.B; p.max_len = a.max_len;
   p.kv = a.kv; p.seq_len = a.seq_len; p.batch_ids = a.batch_ids; p.q = a.q; p.Hq = a.Hq;
   p.chunk = a.plan.chunk; p.stride = a.plan.stride; p.part_o = a.part_o; p.part_ml = a.part_ml;
-  p.logits = a.logits; p.lld = a.lld; p.key_norm = a.key_norm; p.ld = a.ld;
+  p.logits = a.logits; p.lld = a.lld; p.key_norm = a.key_norm; p.ld = a.ld; p.nld = a.nld;
   p.sel_idx = a.sel_idx; p.sel_count = a.sel_count; p.sel_heads = a.sel_heads; p.sel_k = a.sel_k;
   p.n_sink = a.n_sink; p.window = a.window;
   p.qscale = kLog2e / sqrtf((float)D);

@@ -67,7 +67,7 @@ sfi_status check_batch(const sfi_kv *kv, int32_t batch_n) {
 }
 
 struct SlowWs {
-  size_t o, ml, logits, total;
+  size_t o, ml, logits, norms, total;
   int stride;
 };
 
@@ -78,7 +78,9 @@ SlowWs slow_ws(const sfi_kv *kv) {
   w.o = 0;
   w.ml = align_up(w.o + rows * kv->d * sizeof(float));
   w.logits = align_up(w.ml + rows * 2 * sizeof(float));
-  w.total = align_up(w.logits + (size_t)kv->B * kv->Hq * kv->max_seq_len * sizeof(float));
+  // key norms of an evidence-mode step whose caller passes no key_norm
+  w.norms = align_up(w.logits + (size_t)kv->B * kv->Hq * kv->max_seq_len * sizeof(float));
+  w.total = align_up(w.norms + (size_t)kv->B * kv->Hkv * kv->max_seq_len * sizeof(float));
   return w;
 }
 
@@ -245,6 +247,11 @@ AttnLaunch slow_launch(const sfi_kv *kv, const KVView &view, bool paged, const S
   a.evidence = evidence;
   a.key_norm = key_norm;
   a.ld = ld;
+  a.nld = ld;
+  if (evidence && !key_norm) {  // the evidence kernel always writes norms
+    a.key_norm = carve<float>(ws, w.norms);
+    a.nld = kv->max_seq_len;
+  }
   return a;
 }
 

@@ -73,8 +73,9 @@ struct AttnLaunch {
   float *logits;      // [B][Hkv][lld][G] (log2-scaled), workspace
   int lld;
   float *evidence;    // [B][Hkv][ld] or nullptr
-  float *key_norm;    // [B][Hkv][ld] or nullptr
+  float *key_norm;    // [B][Hkv][nld] or nullptr
   int ld;
+  int nld;            // row stride of key_norm (ld, or max_len for workspace rows)
   // fast step
   const int32_t *sel_idx;
   const int32_t *sel_count;
