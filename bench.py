@@ -33,6 +33,21 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix peak of one MI355X
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_llama3_8b_layer_32k.json")
+LEGS_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_long_context_legs.json")
+
+# --record-calls: (workload, kind, algorithmic bytes) of every timed eager
+# call in launch order, and a one-element fill kernel after each call
+# (outside its events) that closes the call's dispatch segment for the
+# counter reducer.
+CALL_LOG = None
+_MARK = None
+
+
+def _mark_call(leg, kind, nbytes):
+    if CALL_LOG is None:
+        return
+    _MARK.zero_()
+    CALL_LOG.append([leg, kind, int(nbytes)])
 METRIC = "decode attn tokens/s (slow+fast mix) at 32K/128K ctx; % HBM roofline/kernel"
 
 
@@ -97,16 +112,17 @@ def percall_list(slow, ctx, cfg, steps):
 
 def traffic_from_counters(d, steps):
     """HBM bytes per call kind from two rocprofv3 counter runs of
-    bench.py --no-graph --steps S --warmup 1 --no-cpu-baseline --calib-copy --legs none
+    bench.py --no-graph --steps S --warmup 1 --no-cpu-baseline --calib-copy
+      --record-calls d/fetch/calls.json
     (d/fetch with FETCH_SIZE, d/write with WRITE_SIZE).  The dispatch streams
     of the two runs are paired in order; FETCH_SIZE and WRITE_SIZE are scaled
-    by what they read for the plain 256 MiB copy the run starts with; after
-    the first 1 GiB flush read every segment between flush reads is one timed
-    call of the eager pass.  Writes the traffic summary json beside the
-    profiles and prints a markdown table."""
+    by what they read for the plain 256 MiB copy the run starts with.  Every
+    timed eager call is the run of dispatches between its 1 GiB flush read
+    (the last reduction before it) and the marker fill kernel after it, in
+    the order of the recorded calls.  Writes the headline's summary beside the
+    profiles (per kind), the long-context workloads' one (per workload and
+    kind), and prints markdown tables."""
     import csv
-    from dynamic_sparse_kv_amd import sfi
-    from dynamic_sparse_kv_amd import workload as W
 
     def load(which):
         rows = list(csv.DictReader(open(os.path.join(d, which, "bench_counter_collection.csv"))))
@@ -123,53 +139,69 @@ def traffic_from_counters(d, steps):
     copy_kib = (1 << 26) * 4 / 1024
     fs = copy_kib / float(F[ci]["Counter_Value"])
     ws = copy_kib / float(Wr[ci]["Counter_Value"])
-    flush = [i for i, r in enumerate(F) if "reduce_kernel" in r["Kernel_Name"]]
-    cfg = W.CONFIGS["c2"].replace(steps=steps)
-    slow = sfi.sfi_schedule(W.sentence_starts(cfg), cfg.budget).astype(bool)
-    calls = percall_list(slow, W.context_lengths(cfg), cfg, steps)
-    kinds = {"step": ("copartial_kernel", "cofinal_kernel"),
-             "slow": ("partial_kernel", "finalize_kernel"),
-             "fast": ("partial_kernel", "finalize_kernel"),
-             "select": ("norm_sums_kernel", "prior_kernel", "keys_kernel", "pick_kernel"),
-             "step_select": ("copartial_kernel", "cofinal_kernel", "partial_kernel", "finalize_kernel",
-                             "keys_kernel", "pick_kernel")}
-    nk = {"step": 2, "slow": 2, "fast": 2, "select": 4, "step_select": 4}   # kernels per call
+    with open(os.path.join(d, "fetch", "calls.json")) as fh:
+        calls = json.load(fh)
+    segs, last_flush = [], None
+    for i, r in enumerate(F):
+        nm = r["Kernel_Name"]
+        if "reduce_kernel" in nm:
+            last_flush = i
+        elif "FillFunctor" in nm and last_flush is not None:
+            # a timed call: a 1 GiB flush read, then only library kernels
+            lo = last_flush + 1
+            big = float(F[last_flush]["Counter_Value"]) * fs > 512 * 1024
+            if big and i > lo and all("sfi" in F[j]["Kernel_Name"] for j in range(lo, i)):
+                segs.append((lo, i))
+            last_flush = None
+    assert len(segs) == len(calls), (len(segs), len(calls))
+    flush_gib = sorted(set(round(float(F[lo - 1]["Counter_Value"]) * fs / 1048576, 3) for lo, _ in segs))
     tot = {}
-    for c, (kind, s, alg) in enumerate(calls):
-        lo = flush[c] + 1
-        hi = lo + nk[kind]
-        assert c + 1 >= len(flush) or flush[c + 1] == hi, (c, kind)
-        names = [F[i]["Kernel_Name"] for i in range(lo, hi)]
-        for nm in names:
-            assert any(k in nm for k in kinds[kind]), (c, kind, nm)
+    for (lo, hi), (leg, kind, alg) in zip(segs, calls):
+        assert hi > lo and all("sfi" in F[i]["Kernel_Name"] for i in range(lo, hi)), (leg, kind)
         fb = sum(float(F[i]["Counter_Value"]) for i in range(lo, hi)) * fs * 1024
         wb = sum(float(Wr[i]["Counter_Value"]) for i in range(lo, hi)) * ws * 1024
-        t = tot.setdefault(kind, [0.0, 0.0, 0, 0])
+        t = tot.setdefault(leg, {}).setdefault(kind, [0.0, 0.0, 0, 0])
         t[0] += fb; t[1] += wb; t[2] += alg; t[3] += 1
-    res = {
-        "workload": f"{cfg.name} (B={cfg.B}, Hq={cfg.Hq}, Hkv={cfg.Hkv}, d={cfg.d}, ctx {cfg.ctx}, "
-                    f"{cfg.n_sink}+{cfg.window}+{cfg.k}, lambda {cfg.lam}), eager pass over decode steps 0..{steps - 1}",
-        "commands": [f"rocprofv3 --pmc {c} --output-format csv -d gpurun_out/traffic/{w} -o bench -- python3 -u "
-                     f"bench.py --no-graph --steps {steps} --warmup 1 --no-cpu-baseline --calib-copy --legs none"
-                     for c, w in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write"))],
-        "calibration": {"copy_bytes": 1 << 28, "fetch_kib_read": float(F[ci]["Counter_Value"]),
-                        "write_kib_read": float(Wr[ci]["Counter_Value"]),
-                        "fetch_scale": round(fs, 4), "write_scale": round(ws, 4)},
-        "ratio": {k: round((v[0] + v[1]) / v[2], 4) for k, v in tot.items()},
-        "totals_bytes": {k: {"calls": v[3], "fetch": int(v[0]), "write": int(v[1]), "algorithmic": int(v[2])}
-                         for k, v in tot.items()},
-        "kernel_source_sha256": kernel_source_hash(),
-    }
+    cmds = [f"rocprofv3 --pmc {c} --output-format csv -d gpurun_out/traffic/{w} -o bench -- python3 -u "
+            f"bench.py --no-graph --steps {steps} --warmup 1 --no-cpu-baseline --calib-copy "
+            f"--record-calls gpurun_out/traffic/{w}/calls.json" for c, w in (("FETCH_SIZE", "fetch"),
+                                                                                ("WRITE_SIZE", "write"))]
+    cal = {"copy_bytes": 1 << 28, "fetch_kib_read": float(F[ci]["Counter_Value"]),
+           "write_kib_read": float(Wr[ci]["Counter_Value"]), "fetch_scale": round(fs, 4),
+           "write_scale": round(ws, 4), "flush_reads_gib": flush_gib}
+
+    def summary(per_kind):
+        return ({k: round((v[0] + v[1]) / v[2], 4) for k, v in per_kind.items() if v[2] > 0},
+                {k: {"calls": v[3], "fetch": int(v[0]), "write": int(v[1]), "algorithmic": int(v[2])}
+                 for k, v in per_kind.items()})
+    from dynamic_sparse_kv_amd import workload as W
+    cfg = W.CONFIGS["c2"].replace(steps=steps)
+    ratio, totals = summary(tot.get("headline", {}))
+    res = {"workload": f"{cfg.name} (B={cfg.B}, Hq={cfg.Hq}, Hkv={cfg.Hkv}, d={cfg.d}, ctx {cfg.ctx}, "
+                       f"{cfg.n_sink}+{cfg.window}+{cfg.k}, lambda {cfg.lam}), eager pass over decode steps "
+                       f"0..{steps - 1}",
+           "commands": cmds, "calibration": cal, "ratio": ratio, "totals_bytes": totals,
+           "kernel_source_sha256": kernel_source_hash()}
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(res, fh, indent=1)
+    legs = {}
+    for leg, per_kind in tot.items():
+        if leg == "headline":
+            continue
+        r_, t_ = summary(per_kind)
+        legs[leg] = {"ratio": r_, "totals_bytes": t_}
+    if legs:
+        with open(LEGS_TRAFFIC_FILE, "w") as fh:
+            json.dump({"commands": cmds, "calibration": cal, "legs": legs,
+                       "kernel_source_sha256": kernel_source_hash()}, fh, indent=1)
     print(f"calibration: FETCH_SIZE {F[ci]['Counter_Value']} KiB, WRITE_SIZE {Wr[ci]['Counter_Value']} KiB "
-          f"for a 256 MiB copy -> scales {fs:.4f}, {ws:.4f}; flush reads "
-          f"{sorted(set(round(float(F[i]['Counter_Value']) * fs / 1048576, 3) for i in flush))} GiB")
-    print("| call | calls | fetch MB | write MB | algorithmic MB | measured / algorithmic |")
-    print("|---|---|---|---|---|---|")
-    for k, v in tot.items():
-        print(f"| {k} | {v[3]} | {v[0] / 1e6:.2f} | {v[1] / 1e6:.2f} | {v[2] / 1e6:.2f} | "
-              f"{(v[0] + v[1]) / v[2]:.4f} |")
+          f"for a 256 MiB copy -> scales {fs:.4f}, {ws:.4f}; flush reads {flush_gib} GiB")
+    print("| workload | call | calls | fetch MB | write MB | algorithmic MB | measured / algorithmic |")
+    print("|---|---|---|---|---|---|---|")
+    for leg, per_kind in tot.items():
+        for k, v in per_kind.items():
+            ratio_s = f"{(v[0] + v[1]) / v[2]:.4f}" if v[2] > 0 else "-"
+            print(f"| {leg} | {k} | {v[3]} | {v[0] / 1e6:.2f} | {v[1] / 1e6:.2f} | {v[2] / 1e6:.2f} | {ratio_s} |")
 
 
 def kernel_source_hash():
@@ -275,11 +307,12 @@ class _CallTimer:
     """HIP events around single calls on the launch stream, each call after
     a 1 GiB read that evicts L2 and the Infinity Cache."""
 
-    def __init__(self, dev, stream):
+    def __init__(self, dev, stream, leg):
         import torch
         self.torch = torch
         self.flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         self.stream = stream
+        self.leg = leg
         self.ev = []
 
     def __call__(self, kind, fn, nbytes, flops=0.0):
@@ -289,6 +322,7 @@ class _CallTimer:
         e0.record(self.stream)
         fn()
         e1.record(self.stream)
+        _mark_call(self.leg, kind, nbytes)
         self.ev.append((kind, e0, e1, nbytes, flops))
 
     def summary(self):
@@ -370,7 +404,7 @@ def leg_stack128k(timed_steps=24, dense_steps=4):
     t_layer, g = _graph_time(run, side, stream)
     del g
 
-    timer = _CallTimer(dev, stream)
+    timer = _CallTimer(dev, stream, "stack32-128k")
     for s in range(1, steps):
         ns, nf = int(plan.n_slow[s]), int(plan.n_fast[s])
         lens = plan.seq_len_host[s]
@@ -465,7 +499,7 @@ def leg_vegas64k(iters=12):
         del g
         res[f"tokens_per_s_{name}"] = round(cfg.B * T * iters / t_total, 1)
         res[f"ms_per_iteration_{name}"] = round(t_total / iters * 1e3, 4)
-    timer = _CallTimer(dev, stream)
+    timer = _CallTimer(dev, stream, "vegas-64k")
     d, Hq, Hkv = cfg.d, cfg.Hq, cfg.Hkv
     for it in range(min(iters, 4)):
         n = ctx + T * (it + 1)
@@ -527,7 +561,7 @@ def leg_ragged_paged(timed_steps=32, dense_steps=4):
     del g
     value = cfg.B * timed_steps / t_total
     kseq = np.minimum(cfg.k, plan.seq_len_host // cfg.k_div)
-    timer = _CallTimer(dev, stream)
+    timer = _CallTimer(dev, stream, "ragged-paged")
     for s in range(1, steps):
         ns, nf = int(plan.n_slow[s]), int(plan.n_fast[s])
         lens = plan.seq_len_host[s]
@@ -590,6 +624,9 @@ def main():
     ap.add_argument("--traffic", metavar="DIR",
                     help="no GPU run: derive per-call HBM traffic from the two counter runs under DIR "
                          "(DIR/fetch, DIR/write; see traffic_from_counters) and rewrite the traffic summary")
+    ap.add_argument("--record-calls", metavar="PATH",
+                    help="write the timed eager calls (workload, kind, algorithmic bytes) to PATH as "
+                         "json, each followed by a marker kernel, for the counter reducer")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy (a known-size kernel "
                          "for scaling hardware byte counters)")
@@ -612,6 +649,10 @@ def main():
         sys.exit(2)
     sfi.lib()
     dev = "cuda"
+    global CALL_LOG, _MARK
+    if args.record_calls:
+        CALL_LOG = []
+        _MARK = torch.zeros(1, dtype=torch.float32, device=dev)
     if args.calib_copy:
         src = torch.ones(1 << 26, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -689,6 +730,7 @@ def main():
         e0.record(stream)
         fn()
         e1.record(stream)
+        _mark_call("headline", kind, nbytes)
         ev.append((kind, e0, e1, nbytes))
 
     for kind, s, nbytes in percall_list(plan.slow, ctx, cfg, K_steps):
@@ -703,11 +745,9 @@ def main():
                                                      plan.fast_ids[s], nf, stream)}[kind]
         timed(kind, fn, nbytes)
     # Observation-window slow step over the last 8 queries, next to the
-    # one-query slow step, for every sequence (informational; left out of
-    # the counter runs, which pair each flush-bounded segment with the
-    # calls of percall_list).
+    # one-query slow step, for every sequence (informational).
     wq = 8
-    if plan_steps >= wq and not args.calib_copy:
+    if plan_steps >= wq:
         s_w = wq - 1
         q_win = q[s_w - wq + 1:s_w + 1].permute(1, 0, 2, 3).contiguous()
         lens_w = ctx + s_w + 1
@@ -819,6 +859,9 @@ def main():
                   "ragged-paged": leg_ragged_paged}[leg]
             result["legs"][leg] = fn()
     print(json.dumps(result), flush=True)
+    if CALL_LOG is not None:
+        with open(args.record_calls, "w") as fh:
+            json.dump(CALL_LOG, fh)
 
 
 if __name__ == "__main__":
