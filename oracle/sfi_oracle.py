@@ -189,6 +189,54 @@ def topk_indices(score: np.ndarray, lo: int, hi: int, k: int) -> np.ndarray:
     return np.sort(j[order[:k]])
 
 
+def soft_nms(score, lo: int, hi: int, radius: int, alpha: float) -> np.ndarray:
+    """Soft-NMS inside one head row [SFI-it s3.B, SFI-pt s2.B: keeps
+    neighbouring, correlated keys from filling the budget; the pages give no
+    formula -- this reading: one pass, not greedy].  For a candidate j of
+    [lo, hi): s'_j = s_j (1 - alpha)^m_j, m_j = number of candidates i with
+    0 < |i - j| <= radius that rank above j (larger score, or an equal score
+    and a lower index).  The ranking comparisons use float32 values (the
+    precision the kernel decides them in); other keys keep s.  Parity of
+    this form with the paper: unpinned."""
+    s = np.asarray(score, dtype=np.float64)
+    out = s.copy()
+    lo = max(lo, 0)
+    if hi <= lo or radius <= 0 or alpha == 0.0:
+        return out
+    s32 = s.astype(np.float32)
+    for j in range(lo, hi):
+        m = 0
+        for i in range(max(lo, j - radius), min(hi, j + radius + 1)):
+            if i != j and (s32[i] > s32[j] or (s32[i] == s32[j] and i < j)):
+                m += 1
+        out[j] = s[j] * (1.0 - alpha) ** m
+    return out
+
+
+def exclusive_topk(rows, lo: int, hi: int, k: int, beta: float):
+    """Cross-head exclusivity over the head rows of one sequence [SFI-it
+    s3.B, SFI-pt s2.B: penalise the same key being picked by several heads;
+    no formula in the pages -- this reading].  T_g = Top-K of row g;
+    c_j = number of rows whose T_g holds j; row g's key j is scaled by
+    (1 - beta)^(c_j - [j in T_g]) (once per other head that picked it) and
+    the Top-K is taken again.  Returns (rescaled rows, final lists).  Parity
+    of this form with the paper: unpinned."""
+    rows = [np.asarray(r, dtype=np.float64) for r in rows]
+    first = [topk_indices(r, lo, hi, k) for r in rows]
+    if beta == 0.0 or len(rows) < 2:
+        return rows, first
+    n = len(rows[0])
+    c = np.zeros(n, dtype=np.int64)
+    for t in first:
+        c[t] += 1
+    out = []
+    for r, t in zip(rows, first):
+        own = np.zeros(n, dtype=np.int64)
+        own[t] = 1
+        out.append(r * (1.0 - beta) ** (c - own))
+    return out, [topk_indices(r, lo, hi, k) for r in out]
+
+
 def candidate_range(n: int, n_sink: int, window: int):
     """Selectable keys at a slow step of length n: [n_sink, n - window)."""
     return n_sink, max(n_sink, n - window)

@@ -422,3 +422,59 @@ def test_window_evidence_equal_keys_closed_form():
         want[:nt] += 1.0 / nt
     for g in range(Hkv):
         np.testing.assert_allclose(f[g], want / w, rtol=1e-12)
+
+
+# ------------------------------------------- Soft-NMS and cross-head exclusivity
+
+def test_soft_nms_hand_case_and_identities():
+    """Hand-computed: radius 1, alpha 0.5 over s = [0.5, 0.95, 0.9, 0.1, 0.6]:
+    keys 0 and 2 have one stronger neighbour (key 1), so they halve; key 3
+    has two (keys 2 and 4), so it is quartered; top-2 moves from {1, 2} to
+    {1, 4}.  alpha = 0 or radius = 0 is the identity."""
+    s = np.array([0.5, 0.95, 0.9, 0.1, 0.6])
+    out = O.soft_nms(s, 0, 5, 1, 0.5)
+    np.testing.assert_allclose(out, [0.25, 0.95, 0.45, 0.025, 0.6], rtol=1e-15)
+    assert list(O.topk_indices(s, 0, 5, 2)) == [1, 2]
+    assert list(O.topk_indices(out, 0, 5, 2)) == [1, 4]
+    np.testing.assert_array_equal(O.soft_nms(s, 0, 5, 1, 0.0), s)
+    np.testing.assert_array_equal(O.soft_nms(s, 0, 5, 0, 0.5), s)
+    # outside the candidate range nothing changes; neighbours outside it do not count
+    out = O.soft_nms(s, 1, 4, 1, 0.5)
+    np.testing.assert_allclose(out, [0.5, 0.95, 0.45, 0.05, 0.6], rtol=1e-15)
+
+
+def test_soft_nms_invariants():
+    """Scores never grow; a key with no stronger candidate within the radius
+    keeps its score; equal neighbours: the lower index counts as stronger."""
+    rng = np.random.default_rng(31)
+    s = rng.random(300)
+    out = O.soft_nms(s, 10, 290, 3, 0.4)
+    assert np.all(out <= s)
+    for j in range(10, 290):
+        nb = [i for i in range(max(10, j - 3), min(290, j + 4)) if i != j]
+        if all(s[i] < s[j] for i in nb):
+            assert out[j] == s[j]
+    eq = np.array([0.3, 0.3, 0.3])
+    np.testing.assert_allclose(O.soft_nms(eq, 0, 3, 1, 0.5), [0.3, 0.15, 0.15], rtol=1e-15)
+
+
+def test_exclusivity_hand_case_and_identities():
+    """Hand-computed: two heads, k = 1, both pick key 0 first; with beta 0.5
+    each halves key 0 once (one other head picked it), so both move to key
+    1.  beta = 0 or a single head is the plain Top-K."""
+    rows = [np.array([0.9, 0.8]), np.array([0.9, 0.85])]
+    out, lists = O.exclusive_topk(rows, 0, 2, 1, 0.5)
+    np.testing.assert_allclose(out[0], [0.45, 0.8])
+    np.testing.assert_allclose(out[1], [0.45, 0.85])
+    assert [list(t) for t in lists] == [[1], [1]]
+    _, lists0 = O.exclusive_topk(rows, 0, 2, 1, 0.0)
+    assert [list(t) for t in lists0] == [[0], [0]]
+    _, one = O.exclusive_topk(rows[:1], 0, 2, 1, 0.5)
+    assert [list(t) for t in one] == [[0]]
+    # a key is scaled once per OTHER head that picked it: head 0's pick
+    # (key 0) is kept in head 0 and halved in head 1, and vice versa
+    rows = [np.array([0.9, 0.1, 0.2]), np.array([0.1, 0.9, 0.2])]
+    out, lists = O.exclusive_topk(rows, 0, 3, 1, 0.5)
+    np.testing.assert_allclose(out[0], [0.9, 0.05, 0.2])
+    np.testing.assert_allclose(out[1], [0.05, 0.9, 0.2])
+    assert [list(t) for t in lists] == [[0], [1]]
