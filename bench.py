@@ -720,7 +720,7 @@ def main():
     _log("[bench] per-call timing pass")
     flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     calls = {"step": [], "slow": [], "select": [], "fast": [], "step_select": [], "slow_all": [],
-             "slow_window8": []}
+             "slow_window8": [], "step_select_refined": []}
     bytes_by = {k_: [] for k_ in calls}
     ev = []
 
@@ -744,6 +744,22 @@ def main():
               "step_select": lambda: dec.step_select(q[s], plan.seq_len[s], plan.slow_ids[s], ns,
                                                      plan.fast_ids[s], nf, stream)}[kind]
         timed(kind, fn, nbytes)
+    # The combined call again for the same slow steps, with Soft-NMS (radius
+    # 4, alpha 0.5) and cross-head exclusivity (beta 0.5) on: the cost of the
+    # score refinements (informational; the pages give no constants, so the
+    # headline runs without them).  Last, since it replaces the selections.
+    for kind, s, nbytes in percall_list(plan.slow, ctx, cfg, K_steps):
+        if kind != "step_select":
+            continue
+        ns, nf = int(plan.n_slow[s]), int(plan.n_fast[s])
+
+        def refined(s=s, ns=ns, nf=nf):
+            dec.params.nms_radius, dec.params.nms_alpha, dec.params.excl_beta = 4, 0.5, 0.5
+            try:
+                dec.step_select(q[s], plan.seq_len[s], plan.slow_ids[s], ns, plan.fast_ids[s], nf, stream)
+            finally:
+                dec.params.nms_radius, dec.params.nms_alpha, dec.params.excl_beta = 0, 0.0, 0.0
+        timed("step_select_refined", refined, nbytes)
     # Observation-window slow step over the last 8 queries, next to the
     # one-query slow step, for every sequence (informational).
     wq = 8

@@ -175,6 +175,8 @@ __device__ __forceinline__ void keys_body(const SelectLaunch &a, int p, int h, i
   const int tid = threadIdx.x;
 
   float s[kPT];
+  // the fused score's constants (FUSED), kept for the Soft-NMS halo keys
+  float cf = 0.f, cr = 0.f, muf = 0.f, cz = 0.f, ct = 0.f, tq = 0.f;
   if constexpr (FUSED) {
     const float *f = a.score + r.row * a.ld;
     const float *nu = a.key_norm + r.row * a.ld;
@@ -187,11 +189,12 @@ __device__ __forceinline__ void keys_body(const SelectLaunch &a, int p, int h, i
     for (int q = tid; q < Pn; q += kT) W += a.ws.wsum[r.row * a.ws.P + q];
     for (int i = tid; i < kBins1; i += kT) hist[i] = 0u;
     W = block_sum_d<kTW>(W, s_red);
-    const float cf = 1.0f - a.lambda;
-    const float cr = W > 0.0 ? (float)((double)a.lambda / W) : 0.f;
-    const float muf = a.ws.meta[r.row].muf, cz = a.ws.meta[r.row].cz;
-    const float ct = kLog2e / a.pos_tau;
-    const float tq = (float)(r.n - 1);
+    cf = 1.0f - a.lambda;
+    cr = W > 0.0 ? (float)((double)a.lambda / W) : 0.f;
+    muf = a.ws.meta[r.row].muf;
+    cz = a.ws.meta[r.row].cz;
+    ct = kLog2e / a.pos_tau;
+    tq = (float)(r.n - 1);
 #pragma unroll
     for (int i = 0; i < kPT; ++i) {
       const int j = key_pos(j0, i);
@@ -213,6 +216,69 @@ __device__ __forceinline__ void keys_body(const SelectLaunch &a, int p, int h, i
     __syncthreads();
   }
   if (p >= r.nch) return;  // no candidates in this chunk
+
+  // Soft-NMS: a candidate's score is scaled by (1 - alpha) once per
+  // candidate within the radius that ranks above it (larger score, or equal
+  // score and lower index).  The chunk's scores and a halo of kNmsMaxRadius
+  // keys on each side are staged in LDS; non-candidates never rank above.
+  if (a.nms_radius > 0) {
+    __shared__ float s_nm[kCH + 2 * kNmsMaxRadius];
+    constexpr int HALO = kNmsMaxRadius;
+#pragma unroll
+    for (int i = 0; i < kPT; ++i) {
+      const int j = key_pos(j0, i);
+      s_nm[j - j0 + HALO] = (j >= r.lo && j < r.hi) ? s[i] : -INFINITY;
+    }
+    if (tid < 2 * HALO) {
+      const int off = (tid < HALO) ? tid - HALO : kCH + tid - HALO;
+      const int j = j0 + off;
+      float v = -INFINITY;
+      if (j >= r.lo && j < r.hi) {
+        // the same expression as the chunk's own keys
+        if constexpr (FUSED) {
+          const float w = prior_w(a.key_norm[r.row * a.ld + j], j, muf, cz, tq, ct);
+          v = fmaf(cf, a.score[r.row * a.ld + j], cr * w);
+        } else {
+          v = a.score[r.row * a.ld + j];
+        }
+      }
+      s_nm[off + HALO] = v;
+    }
+    __syncthreads();
+    const float keep = 1.0f - a.nms_alpha;
+#pragma unroll
+    for (int i = 0; i < kPT; ++i) {
+      const int j = key_pos(j0, i);
+      if (j >= r.lo && j < r.hi) {
+        const float sj = s_nm[j - j0 + HALO];
+        int m = 0;
+        for (int dd = 1; dd <= a.nms_radius; ++dd) {
+          m += (s_nm[j - j0 + HALO - dd] >= sj) ? 1 : 0;  // lower index: ties rank above
+          m += (s_nm[j - j0 + HALO + dd] > sj) ? 1 : 0;
+        }
+        float f = 1.0f;
+        for (int t = 0; t < m; ++t) f *= keep;
+        s[i] *= f;
+      }
+    }
+  }
+  // Exclusivity's second pass: scaled by (1 - beta) once per other head row
+  // of the sequence whose first Top-K holds the key.
+  if (a.round == 1) {
+    const float keep = 1.0f - a.excl_beta;
+    const uint32_t *cnt = a.excl_cnt + (size_t)r.b * a.ld32 * 32;
+    const uint32_t *bits = a.excl_bits + r.row * a.ld32;
+#pragma unroll
+    for (int i = 0; i < kPT; ++i) {
+      const int j = key_pos(j0, i);
+      if (j >= r.lo && j < r.hi) {
+        const int e = (int)cnt[j] - (int)((bits[j >> 5] >> (j & 31)) & 1u);
+        float f = 1.0f;
+        for (int t = 0; t < e; ++t) f *= keep;
+        s[i] *= f;
+      }
+    }
+  }
 
   uint32_t key[kPT];
 #pragma unroll

@@ -102,8 +102,8 @@ FastWs fast_ws(const sfi_kv *kv, int sel_k, int n_sink, int window) {
 }
 
 struct SelWs {
-  int P;
-  size_t ghist, cum, sorted, nsum, wsum, meta, total;
+  int P, ld32;
+  size_t ghist, cum, sorted, nsum, wsum, meta, ecnt, ebits, total;
 };
 
 SelWs select_ws(int B, int H, int max_seq_len) {
@@ -116,7 +116,11 @@ SelWs select_ws(int B, int H, int max_seq_len) {
   w.nsum = align_up(w.sorted + rows * w.P * kSelChunk * sizeof(unsigned long long));
   w.wsum = align_up(w.nsum + rows * w.P * 2 * sizeof(double));
   w.meta = align_up(w.wsum + rows * w.P * sizeof(double));
-  w.total = align_up(w.meta + rows * sizeof(SelRowMeta));
+  // cross-head exclusivity: per-key row counts and per-row membership bits
+  w.ld32 = (max_seq_len + 31) / 32;
+  w.ecnt = align_up(w.meta + rows * sizeof(SelRowMeta));
+  w.ebits = align_up(w.ecnt + (size_t)B * w.ld32 * 32 * sizeof(uint32_t));
+  w.total = align_up(w.ebits + rows * w.ld32 * sizeof(uint32_t));
   return w;
 }
 
@@ -173,6 +177,9 @@ sfi_status select_launch(const sfi_select_params *p, const int32_t *batch_ids, i
   if (batch_n < 0 || batch_n > B) return SFI_ERR_RANGE;
   if (ld < max_seq_len) return SFI_ERR_RANGE;
   if (p->k < 1 || p->n_sink < 0 || p->window < 0) return SFI_ERR_RANGE;
+  if (p->nms_radius < 0 || p->nms_radius > kNmsMaxRadius) return SFI_ERR_RANGE;
+  if (!(p->nms_alpha >= 0.f && p->nms_alpha < 1.f) || !(p->excl_beta >= 0.f && p->excl_beta < 1.f))
+    return SFI_ERR_RANGE;
   const bool fused = p->mode == SFI_SCORE_FUSED;
   if (fused) {
     if (!key_norm) return SFI_ERR_NULL;
@@ -197,6 +204,12 @@ sfi_status select_launch(const sfi_select_params *p, const int32_t *batch_ids, i
   a.fused_out = fused ? fused_out : nullptr;
   a.fo_ld = ld;
   a.prior_done = prior_done;
+  a.nms_radius = (p->nms_alpha > 0.f) ? p->nms_radius : 0;
+  a.nms_alpha = p->nms_alpha;
+  a.excl_beta = (H > 1) ? p->excl_beta : 0.f;
+  a.excl_cnt = carve<uint32_t>(ws, w.ecnt);
+  a.excl_bits = carve<uint32_t>(ws, w.ebits);
+  a.ld32 = w.ld32;
   a.ws.P = w.P;
   a.ws.ghist = carve<uint32_t>(ws, w.ghist);
   a.ws.cum = carve<uint16_t>(ws, w.cum);
@@ -467,6 +480,9 @@ sfi_status sfi_decode_layer_step(const sfi_kv *kv, const sfi_select_params *p, c
   if (s != SFI_OK) return s;
   if (!p) return SFI_ERR_NULL;
   if (p->mode != SFI_SCORE_FUSED) return SFI_ERR_RANGE;
+  // a deferred selection runs one key and one pick pass inside the next
+  // layer's grids: exclusivity's second round does not fit there
+  if (p->excl_beta != 0.f) return SFI_ERR_UNSUPPORTED;
   if (!(p->lambda >= 0.f && p->lambda <= 1.f)) return SFI_ERR_RANGE;
   if (!(p->pos_tau > 0.f) || !(p->norm_coef == p->norm_coef)) return SFI_ERR_RANGE;
   if (p->k < 1 || p->n_sink < 0 || p->window < 0) return SFI_ERR_RANGE;
@@ -498,6 +514,7 @@ sfi_status sfi_decode_layer_step(const sfi_kv *kv, const sfi_select_params *p, c
       return SFI_ERR_RANGE;
     if ((s = deferred_launch(pending, &pend)) != SFI_OK) return s;
     if (pend.mode != SFI_SCORE_FUSED) return SFI_ERR_RANGE;
+    if (pend.excl_beta != 0.f) return SFI_ERR_UNSUPPORTED;
   }
   const bool pend_run = pend_on && pending->batch_n > 0;
   // this call's own selection (validated before anything is launched)

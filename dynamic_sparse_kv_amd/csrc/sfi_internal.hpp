@@ -110,6 +110,7 @@ hipError_t launch_step(const AttnLaunch &sa, const AttnLaunch &fa, hipStream_t s
                        const SelectLaunch *pend = nullptr);
 
 constexpr int kSelChunk = 2048;       // keys per selector chunk workgroup
+constexpr int kNmsMaxRadius = 8;      // Soft-NMS neighbourhood (halo staged in LDS)
 constexpr int kSelMaxChunks = 1024;   // chunks per row
 constexpr int kSelMaxLen = kSelChunk * kSelMaxChunks;  // longest row: 2,097,152 keys
 
@@ -147,6 +148,16 @@ struct SelectLaunch {
   int fo_ld;
   bool prior_done;    // the slow step already wrote wsum, meta and cleared ghist
   SelWork ws;
+  // Soft-NMS (radius 0: off) and cross-head exclusivity (beta 0: off)
+  int nms_radius;
+  float nms_alpha;
+  float excl_beta;
+  // exclusivity's second round: per-key count of rows whose first Top-K
+  // holds it [B][ld32 * 32] and each row's membership bits [B*H][ld32]
+  uint32_t *excl_cnt;
+  uint32_t *excl_bits;
+  int ld32;
+  int round;  // 1: exclusivity's second key pass (applies the penalty)
 };
 
 hipError_t launch_select(const SelectLaunch &a, hipStream_t st);

@@ -74,7 +74,8 @@ class SFIDecoder:
 
     def __init__(self, K, V, Hq: int, max_len: int, *, n_sink: int, window: int, k: int,
                  lam: float, norm_coef: float = 0.5, pos_tau: float = 1024.0,
-                 page_table=None, page_size: int = 0, keep_fused: bool = False):
+                 page_table=None, page_size: int = 0, keep_fused: bool = False,
+                 nms_radius: int = 0, nms_alpha: float = 0.0, excl_beta: float = 0.0):
         dev = K.device
         self.dev = dev
         self.K, self.V = K, V
@@ -90,7 +91,9 @@ class SFIDecoder:
         self.n_sink, self.window, self.k = n_sink, window, k
         self._dummy_len = torch.full((B,), self.max_len, dtype=torch.int32, device=dev)
         self.kv = sfi.make_kv(K, V, self._dummy_len, Hq, self.max_len, page_table, page_size)
-        self.params = sfi.select_params(sfi.SFI_SCORE_FUSED, lam, k, n_sink, window, norm_coef, pos_tau)
+        self.params = sfi.select_params(sfi.SFI_SCORE_FUSED, lam, k, n_sink, window, norm_coef, pos_tau,
+                                        nms_radius=nms_radius, nms_alpha=nms_alpha,
+                                        excl_beta=excl_beta)
         self.ld = self.max_len
         f32 = dict(dtype=torch.float32, device=dev)
         self.out = torch.zeros((B, Hq, d), **f32)

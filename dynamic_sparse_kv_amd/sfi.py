@@ -50,7 +50,8 @@ class sfi_select_params(ctypes.Structure):
     _fields_ = [
         ("mode", _c_int), ("lambda_", ctypes.c_float), ("norm_coef", ctypes.c_float),
         ("pos_tau", ctypes.c_float), ("n_sink", _c_int), ("window", _c_int), ("k", _c_int),
-        ("k_per_seq", _vp),
+        ("k_per_seq", _vp), ("nms_radius", _c_int), ("nms_alpha", ctypes.c_float),
+        ("excl_beta", ctypes.c_float),
     ]
 
 
@@ -187,11 +188,13 @@ def make_kv(k, v, seq_len, Hq: int, max_seq_len: int, page_table=None, page_size
 
 def select_params(mode: int, lam: float, k: int, n_sink: int, window: int,
                   norm_coef: float = 0.5, pos_tau: float = 1024.0,
-                  k_per_seq=None) -> sfi_select_params:
+                  k_per_seq=None, nms_radius: int = 0, nms_alpha: float = 0.0,
+                  excl_beta: float = 0.0) -> sfi_select_params:
     p = sfi_select_params()
     p.mode, p.lambda_, p.norm_coef, p.pos_tau = mode, lam, norm_coef, pos_tau
     p.n_sink, p.window, p.k = n_sink, window, k
     p.k_per_seq = _ptr(k_per_seq)
+    p.nms_radius, p.nms_alpha, p.excl_beta = nms_radius, nms_alpha, excl_beta
     return p
 
 

@@ -103,6 +103,27 @@ typedef struct sfi_select_params {
   const int32_t *k_per_seq; /* device [B] or NULL: sequence b keeps at most
                                min(k_per_seq[b], k) keys (negative -> 0);
                                NULL: k for every sequence */
+  /* Score refinements [SFI 3.B; the Portuguese summary, 2.B: Soft-NMS keeps
+   * neighbouring, correlated keys from filling one head's budget; cross-head
+   * exclusivity penalises the same key being picked by several heads].  The
+   * pages give no formula; the reading implemented (all 0 = off):
+   *   Soft-NMS: a candidate's score is multiplied by (1 - nms_alpha) once
+   *     per candidate within nms_radius positions that ranks above it
+   *     (larger score, or equal score and lower index); one pass.
+   *   Exclusivity: after a first Top-K of every head row of a sequence, a
+   *     row's key j is multiplied by (1 - excl_beta) once per other row whose
+   *     first Top-K holds j, and the Top-K is taken again (two selection
+   *     rounds; H >= 2 rows).
+   * Both act on log scores: for s > 0 each factor is the subtraction of
+   * m log(1/(1 - alpha)) from log s (a RAW score <= 0 is scaled the same
+   * way, which is no penalty there).  Decisions use the float32 scores.
+   * fused_out holds the score before either refinement.
+   * nms_radius in [0, 8], nms_alpha and excl_beta in [0, 1) (else
+   * SFI_ERR_RANGE).  sfi_decode_layer_step defers a selection into one key
+   * and one pick pass, so it rejects excl_beta != 0 (SFI_ERR_UNSUPPORTED). */
+  int32_t nms_radius;
+  float nms_alpha;
+  float excl_beta;
 } sfi_select_params;
 
 /* ---------------------------------------------------------------- sizes */

@@ -29,12 +29,14 @@ def row_rel_err(x, y):
     return float((num / den).max())
 
 
-def check_selection(gpu_idx, gpu_cnt, score, lo, hi, k):
+def check_selection(gpu_idx, gpu_cnt, score, lo, hi, k, ambiguous=None):
     """Compare one GPU index list with the oracle's Top-K of ``score``.
 
     Returns the number of near-tie keys that differ.  Asserts that the GPU
     list is ascending, unique, inside [lo, hi), padded with -1, of the right
-    length, and that every difference lies in the near-tie band.
+    length, and that every difference lies in the near-tie band or is marked
+    in the boolean mask ``ambiguous`` (keys whose refined score hangs on an
+    earlier near-tie decision).
     """
     gpu_idx = np.asarray(gpu_idx)
     want = O.topk_indices(score, lo, hi, k)
@@ -50,5 +52,33 @@ def check_selection(gpu_idx, gpu_cnt, score, lo, hi, k):
     kth = O.kth_score(score, lo, hi, k)
     assert kth is not None
     band = np.abs(np.asarray(score)[diff] - kth) <= TIE_BAND * abs(kth)
+    if ambiguous is not None:
+        band |= np.asarray(ambiguous)[diff]
     assert band.all(), f"selection differs outside the near-tie band: {diff[~band][:10]}"
     return int(diff.size)
+
+
+def nms_ambiguous(score, lo, hi, radius):
+    """Keys of [lo, hi) whose Soft-NMS count depends on a near-tie: some
+    candidate within ``radius`` lies within the near-tie band of it (the
+    kernel compares float32 scores formed in another rounding order)."""
+    s = np.asarray(score, dtype=np.float64)
+    amb = np.zeros(len(s), dtype=bool)
+    for dd in range(1, radius + 1):
+        if hi - dd <= lo:
+            break
+        a, b = s[lo:hi - dd], s[lo + dd:hi]
+        close = np.abs(a - b) <= TIE_BAND * np.maximum(np.abs(a), np.abs(b))
+        amb[lo:hi - dd] |= close
+        amb[lo + dd:hi] |= close
+    return amb
+
+
+def tie_band_keys(score, lo, hi, k):
+    """Keys of [lo, hi) within the near-tie band of the k-th score."""
+    s = np.asarray(score, dtype=np.float64)
+    amb = np.zeros(len(s), dtype=bool)
+    kth = O.kth_score(s, lo, hi, k)
+    if kth is not None:
+        amb[lo:hi] = np.abs(s[lo:hi] - kth) <= TIE_BAND * abs(kth)
+    return amb

@@ -122,6 +122,13 @@ def test_select_validation():
     assert _select(ok, batch_n=0) == sfi.SFI_OK
     raw = P(sfi.SFI_SCORE_RAW, 0.0, 64, 4, 256)
     assert _select(raw, key_norm=None, batch_n=0) == sfi.SFI_OK          # RAW needs no norms
+    # score refinements: radius in [0, 8], alpha and beta in [0, 1)
+    for kw in (dict(nms_radius=9), dict(nms_radius=-1), dict(nms_radius=2, nms_alpha=1.0),
+               dict(nms_radius=2, nms_alpha=-0.1), dict(excl_beta=1.0), dict(excl_beta=-0.5),
+               dict(excl_beta=float("nan"))):
+        assert _select(P(sfi.SFI_SCORE_FUSED, 0.3, 64, 4, 256, **kw)) == sfi.SFI_ERR_RANGE, kw
+    ref = P(sfi.SFI_SCORE_FUSED, 0.3, 64, 4, 256, nms_radius=8, nms_alpha=0.9, excl_beta=0.5)
+    assert _select(ref, batch_n=0) == sfi.SFI_OK
 
 
 def test_fast_step_validation():
@@ -210,6 +217,13 @@ def test_layer_step_validation():
     assert call(kv, deferred(key_norm=None), out) == sfi.SFI_ERR_NULL
     assert call(kv, None, out, n_slow=kv.B, n_fast=1) == sfi.SFI_ERR_RANGE    # this call's own checks
     assert call(_kv(d=256), None, out) == sfi.SFI_ERR_UNSUPPORTED
+    # a deferred selection has one key and one pick pass: no exclusivity
+    ex = deferred()
+    ex.params.excl_beta = 0.5
+    assert call(kv, ex, out) == sfi.SFI_ERR_UNSUPPORTED
+    p.excl_beta = 0.5
+    assert call(kv, None, out) == sfi.SFI_ERR_UNSUPPORTED
+    p.excl_beta = 0.0
 
 
 def test_verify_validation():

@@ -19,7 +19,8 @@ from dynamic_sparse_kv_amd import workload as W
 from dynamic_sparse_kv_amd.runner import DecodePlan, SFIDecoder, VegasDecoder
 from oracle import sfi_oracle as O
 
-from parity_util import EVID_TOL, NORM_TOL, OUT_TOL, check_selection, row_rel_err
+from parity_util import (EVID_TOL, NORM_TOL, OUT_TOL, check_selection, nms_ambiguous, row_rel_err,
+                         tie_band_keys)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -108,13 +109,13 @@ def test_slow_batch_subset_and_plain_dense():
 
 # ------------------------------------------------------------------- select
 
-def _select_gpu(mode, score, key_norm, lens, k, n_sink, window, lam=0.3, H=None, fused=False):
+def _select_gpu(mode, score, key_norm, lens, k, n_sink, window, lam=0.3, H=None, fused=False, **refine):
     B = score.shape[0]
     H = score.shape[1] if H is None else H
     ld = score.shape[2]
     max_len = max(lens)
     seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
-    p = sfi.select_params(mode, lam, k, n_sink, window)
+    p = sfi.select_params(mode, lam, k, n_sink, window, **refine)
     sel = torch.full((B, H, k), -7, dtype=torch.int32, device=DEV)
     cnt = torch.full((B, H), -7, dtype=torch.int32, device=DEV)
     fo = torch.zeros((B, H, ld), dtype=torch.float32, device=DEV) if fused else None
@@ -240,6 +241,141 @@ def test_select_fused_long_row_streams_blocks():
     assert row_rel_err(fo[0], s_ref) <= EVID_TOL
     ties = sum(check_selection(sel[0, g], cnt[0, g], s_ref[g], lo, hi, k) for g in range(Hkv))
     _say(f"  near-tie differences: {ties}")
+
+
+# ------------------------------------------- Soft-NMS and cross-head exclusivity
+# The pages name both refinements without a formula; the oracle's reading
+# (soft_nms, exclusive_topk) is the one the key kernel implements.  Where a
+# refined score hangs on an earlier near-tie (a neighbour comparison, a
+# first-round membership) the difference is allowed and counted.
+
+def _oracle_fused_inputs(B, Hq, Hkv, d, lens, seed, lam=0.3):
+    cap = max(lens) + 7
+    K, V = _rand_kv(B, Hkv, cap, d, seed=seed, hh=20)
+    q = _rand_q((B, Hq, d), seed=seed + 1)
+    Kb, Vb, qb = _bits(K), _bits(V), _bits(q)
+    f = np.zeros((B, Hkv, cap), dtype=np.float32)
+    nu = np.zeros((B, Hkv, cap), dtype=np.float32)
+    s_ref = []
+    for b in range(B):
+        n = lens[b]
+        _, p = O.dense_step(qb[b], Kb[b], Vb[b], n)
+        fb = O.evidence(p, Hkv)
+        f[b, :, :n] = fb
+        nu[b, :, :n] = O.key_norms(Kb[b], n)
+        s_ref.append(O.fuse(fb, O.prior(Kb[b], n), lam))
+    return torch.from_numpy(f).to(DEV), torch.from_numpy(nu).to(DEV), s_ref
+
+
+def _check_refined(sel, cnt, s_rows, lo, hi, k, radius, alpha, beta):
+    """Oracle Soft-NMS then exclusivity on one sequence's head rows; returns
+    the number of differing keys (near-tie or ambiguous)."""
+    H = len(s_rows)
+    s_n = [O.soft_nms(s_rows[g], lo, hi, radius, alpha) for g in range(H)]
+    rows, _ = O.exclusive_topk(s_n, lo, hi, k, beta)
+    amb = np.zeros(len(s_rows[0]), dtype=bool)
+    for g in range(H):
+        amb |= nms_ambiguous(s_rows[g], lo, hi, radius)
+        if beta > 0 and H > 1:
+            amb |= tie_band_keys(s_n[g], lo, hi, k)
+    return sum(check_selection(sel[g], cnt[g], rows[g], lo, hi, k, ambiguous=amb) for g in range(H))
+
+
+@pytest.mark.parametrize("radius,alpha", [(1, 0.5), (3, 0.3), (8, 0.9)])
+def test_select_soft_nms_raw(radius, alpha):
+    _say(f"select soft-nms raw radius={radius} alpha={alpha}")
+    rng = np.random.default_rng(40 + radius)
+    B, H, ld = 3, 2, 9000
+    lens = [9000, 5000, 600]                      # 600: 340 candidates for k = 300
+    # positive scores (the refinements act on log scores)
+    sc = np.exp(rng.standard_normal((B, H, ld))).astype(np.float32)
+    sc[2, 1] = rng.integers(1, 9, size=ld).astype(np.float32)     # exact ties between neighbours
+    k = 300
+    sel, cnt, _ = _select_gpu(sfi.SFI_SCORE_RAW, torch.from_numpy(sc).to(DEV), None, lens, k, 4, 256,
+                              nms_radius=radius, nms_alpha=alpha)
+    diff = 0
+    for b in range(B):
+        lo, hi = O.candidate_range(lens[b], 4, 256)
+        for h in range(H):
+            diff += check_selection(sel[b, h], cnt[b, h], O.soft_nms(sc[b, h], lo, hi, radius, alpha),
+                                    lo, hi, k)
+    _say(f"  near-tie differences: {diff}")
+
+
+@pytest.mark.parametrize("beta", [0.5, 0.95])
+def test_select_exclusivity_raw(beta):
+    _say(f"select exclusivity raw beta={beta}")
+    rng = np.random.default_rng(50)
+    B, H, ld = 3, 4, 7000
+    lens = [7000, 4000, 700]                      # 700: every candidate fits k
+    common = rng.standard_normal((B, 1, ld))
+    sc = np.exp(common + 0.6 * rng.standard_normal((B, H, ld))).astype(np.float32)   # heads overlap
+    k = 500
+    sel, cnt, _ = _select_gpu(sfi.SFI_SCORE_RAW, torch.from_numpy(sc).to(DEV), None, lens, k, 4, 256,
+                              excl_beta=beta)
+    diff = 0
+    for b in range(B):
+        lo, hi = O.candidate_range(lens[b], 4, 256)
+        rows, lists = O.exclusive_topk([sc[b, h] for h in range(H)], lo, hi, k, beta)
+        first = [O.topk_indices(sc[b, h].astype(np.float64), lo, hi, k) for h in range(H)]
+        if b == 0:   # the penalty changes the lists (the test exercises the second round)
+            assert any(len(np.setxor1d(lists[h], first[h])) > 0 for h in range(H))
+        for h in range(H):
+            diff += check_selection(sel[b, h], cnt[b, h], rows[h], lo, hi, k)
+    _say(f"  near-tie differences: {diff}")
+
+
+def test_select_refinements_fused_from_oracle_evidence():
+    """FUSED scores with Soft-NMS, exclusivity and both; fused_out keeps the
+    score before the refinements."""
+    _say("select fused + refinements")
+    B, Hq, Hkv, d = 2, 16, 4, 64
+    lens = [4100, 3000]
+    f, nu, s_ref = _oracle_fused_inputs(B, Hq, Hkv, d, lens, seed=31)
+    k = 256
+    for radius, alpha, beta in ((4, 0.5, 0.0), (0, 0.0, 0.6), (2, 0.3, 0.5)):
+        sel, cnt, fo = _select_gpu(sfi.SFI_SCORE_FUSED, f, nu, lens, k, 4, 256, lam=0.3, fused=True,
+                                   nms_radius=radius, nms_alpha=alpha, excl_beta=beta)
+        diff = 0
+        for b in range(B):
+            n = lens[b]
+            lo, hi = O.candidate_range(n, 4, 256)
+            assert row_rel_err(fo[b, :, :n], s_ref[b]) <= EVID_TOL
+            diff += _check_refined(sel[b], cnt[b], list(s_ref[b]), lo, hi, k, radius, alpha, beta)
+        _say(f"  radius={radius} alpha={alpha} beta={beta}: differing keys {diff}")
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_step_select_with_refinements(paged):
+    """The combined step + selection call with Soft-NMS and exclusivity
+    against the oracle's slow step, fused score and refinements."""
+    _say(f"step_select + refinements, paged={paged}")
+    B, Hq, Hkv, d = 3, 32, 8, 128
+    lens = [5000, 3500, 6100]
+    cap = 6200
+    K, V = _rand_kv(B, Hkv, cap, d, seed=71, hh=30)
+    q = _rand_q((B, Hq, d), seed=72)
+    seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    kw = dict(n_sink=4, window=256, k=200, lam=0.3, nms_radius=3, nms_alpha=0.4, excl_beta=0.5)
+    if paged:
+        cfg = W.CONFIGS["c5"].replace(B=B, Hq=Hq, Hkv=Hkv, d=d)
+        table, npages = W.page_table(cfg, np.full(B, cap))
+        Kp, Vp = W.to_paged(K, table, npages, 16), W.to_paged(V, table, npages, 16)
+        tab = torch.from_numpy(table).to(DEV)
+        dec = SFIDecoder(Kp, Vp, Hq, cap, page_table=tab, page_size=16, **kw)
+    else:
+        dec = SFIDecoder(K, V, Hq, cap, **kw)
+    ids = torch.tensor([2, 0], dtype=torch.int32, device=DEV)
+    dec.step_select(q, seq, ids, 2, None, 0)
+    torch.cuda.synchronize()
+    sel, cnt = dec.sel_idx.cpu().numpy(), dec.sel_count.cpu().numpy()
+    Kb, Vb, qb = _bits(K), _bits(V), _bits(q)
+    diff = 0
+    for b in (0, 2):
+        r = O.slow_select(qb[b], Kb[b], Vb[b], lens[b], lam=0.3, k=200, n_sink=4, window=256)
+        diff += _check_refined(sel[b], cnt[b], list(r["s"]), r["lo"], r["hi"], 200, 3, 0.4, 0.5)
+    assert np.all(cnt[1] == 0) and np.all(sel[1] == -1)     # sequence 1 not selected
+    _say(f"  differing keys: {diff}")
 
 
 # ----------------------------------------------------------------- fast step
