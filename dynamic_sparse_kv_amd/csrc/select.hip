@@ -125,40 +125,6 @@ __global__ __launch_bounds__(kT) void pick_kernel(SelectLaunch a) {
   pick_body(a, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
-// ------------------------------------------- cross-head exclusivity
-// Between the two rounds: clear the sequence's per-key counts, its rows'
-// membership bits and their bucket histograms (the second key pass fills
-// them again).  grid (blocks, batch entries).
-__global__ __launch_bounds__(kT) void excl_clear_kernel(SelectLaunch a) {
-  const int b = batch_seq(a.batch_ids, blockIdx.y, a.B);
-  if (b < 0) return;
-  const int stride = gridDim.x * kT;
-  const int i0 = blockIdx.x * kT + threadIdx.x;
-  uint32_t *cnt = a.excl_cnt + (size_t)b * a.ld32 * 32;
-  for (int i = i0; i < a.ld32 * 32; i += stride) cnt[i] = 0u;
-  for (int h = 0; h < a.H; ++h) {
-    const size_t row = (size_t)b * a.H + h;
-    for (int i = i0; i < a.ld32; i += stride) a.excl_bits[row * a.ld32 + i] = 0u;
-    for (int i = i0; i < kBins1; i += stride) a.ws.ghist[row * kBins1 + i] = 0u;
-  }
-}
-
-// Every listed key of the first round: count it for its sequence and mark
-// it in its row.  grid (H, batch entries).
-__global__ __launch_bounds__(kT) void excl_scatter_kernel(SelectLaunch a) {
-  const int b = batch_seq(a.batch_ids, blockIdx.y, a.B);
-  if (b < 0) return;
-  const size_t row = (size_t)b * a.H + blockIdx.x;
-  const int c = min(max(a.sel_count[row], 0), a.k);
-  const int n = clamp_len(a.seq_len, b, a.max_seq_len);
-  for (int i = threadIdx.x; i < c; i += kT) {
-    const int j = a.sel_idx[row * a.k + i];
-    if (j < 0 || j >= n) continue;
-    atomicAdd(&a.excl_cnt[(size_t)b * a.ld32 * 32 + j], 1u);
-    atomicOr(&a.excl_bits[row * a.ld32 + (j >> 5)], 1u << (j & 31));
-  }
-}
-
 }  // namespace
 
 hipError_t launch_select(const SelectLaunch &a, hipStream_t st) {
@@ -182,14 +148,12 @@ hipError_t launch_select(const SelectLaunch &a, hipStream_t st) {
   hipLaunchKernelGGL(pick_kernel, grid, dim3(kT), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.excl_beta > 0.f && a.H > 1) {
-    // exclusivity: count the first round's picks, then select again
-    const int cb = std::min(64, (a.ld32 * 32 + kT - 1) / kT);
-    hipLaunchKernelGGL(excl_clear_kernel, dim3(cb, a.batch_n), dim3(kT), 0, st, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(excl_scatter_kernel, dim3(a.H, a.batch_n), dim3(kT), 0, st, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // exclusivity: the first round's key pass cleared the counts and the
+    // second histograms, its pick pass filled the counts and bits; select
+    // again with the penalty
     SelectLaunch a2 = a;
     a2.round = 1;
+    a2.ws.ghist = a.excl_ghist;
     if (fused)
       hipLaunchKernelGGL(keys_kernel<true>, grid, dim3(kT), 0, st, a2);
     else

@@ -171,8 +171,39 @@ __device__ __forceinline__ void keys_body(const SelectLaunch &a, int p, int h, i
   RowGeo r;
   if (!row_geo(a, h, z, r)) return;
   const int j0 = p * kCH;
-  if (j0 >= r.span) return;
   const int tid = threadIdx.x;
+  const bool excl0 = a.excl_beta > 0.f && a.round == 0;
+  // exclusivity: the first round clears the second round's row histogram
+  if (excl0 && p == 0)
+    for (int i = tid; i < kBins1; i += kT) a.excl_ghist[r.row * kBins1 + i] = 0u;
+  if (j0 >= r.span) return;
+
+  // Loads issued before the chunk's own work: the Soft-NMS halo keys
+  // (kNmsMaxRadius on each side; threads past the halo re-read key j0, so
+  // no load sits behind a per-lane branch) and, in exclusivity's second
+  // round, the per-key counts and this row's first-round membership bits.
+  const bool nms = a.nms_radius > 0;
+  int hoff = 0;
+  float hs = 0.f, hn = 0.f;
+  if (nms) {
+    hoff = (tid < kNmsMaxRadius) ? tid - kNmsMaxRadius
+                                 : (tid < 2 * kNmsMaxRadius ? kCH + tid - kNmsMaxRadius : 0);
+    const int jc = min(max(j0 + hoff, 0), r.span - 1);
+    hs = a.score[r.row * a.ld + jc];
+    if constexpr (FUSED) hn = a.key_norm[r.row * a.ld + jc];
+  }
+  uint4 ecnt[kPT / 4];
+  uint32_t ebit[kPT / 4];
+  if (a.round == 1) {
+    const uint32_t *cnt = a.excl_cnt + (size_t)r.b * a.ld32 * 32;
+    const uint32_t *bits = a.excl_bits + r.row * a.ld32;
+#pragma unroll
+    for (int q = 0; q < kPT / 4; ++q) {
+      const int jq = j0 + q * kQuarter + 4 * tid;
+      ecnt[q] = *reinterpret_cast<const uint4 *>(cnt + jq);
+      ebit[q] = bits[jq >> 5];
+    }
+  }
 
   float s[kPT];
   // the fused score's constants (FUSED), kept for the Soft-NMS halo keys
@@ -216,49 +247,75 @@ __device__ __forceinline__ void keys_body(const SelectLaunch &a, int p, int h, i
     __syncthreads();
   }
   if (p >= r.nch) return;  // no candidates in this chunk
+  // exclusivity: the first round clears this chunk's per-key counts (the
+  // first-round pick adds to them)
+  if (excl0 && h == 0) {
+    uint4 *c4 = reinterpret_cast<uint4 *>(a.excl_cnt + (size_t)r.b * a.ld32 * 32 + j0);
+#pragma unroll
+    for (int q = 0; q < kCH / 4 / kT; ++q) c4[q * kT + tid] = make_uint4(0u, 0u, 0u, 0u);
+  }
 
   // Soft-NMS: a candidate's score is scaled by (1 - alpha) once per
   // candidate within the radius that ranks above it (larger score, or equal
   // score and lower index).  The chunk's scores and a halo of kNmsMaxRadius
   // keys on each side are staged in LDS; non-candidates never rank above.
-  if (a.nms_radius > 0) {
-    __shared__ float s_nm[kCH + 2 * kNmsMaxRadius];
+  if (nms) {
+    __shared__ __align__(16) float s_nm[kCH + 2 * kNmsMaxRadius];
     constexpr int HALO = kNmsMaxRadius;
+    static_assert(HALO % 4 == 0, "the halo keeps the thread's keys 16-byte aligned");
 #pragma unroll
-    for (int i = 0; i < kPT; ++i) {
-      const int j = key_pos(j0, i);
-      s_nm[j - j0 + HALO] = (j >= r.lo && j < r.hi) ? s[i] : -INFINITY;
+    for (int q = 0; q < kPT / 4; ++q) {
+      const int jb = j0 + q * kQuarter + 4 * tid;
+      float4 v;
+      v.x = (jb >= r.lo && jb < r.hi) ? s[4 * q] : -INFINITY;
+      v.y = (jb + 1 >= r.lo && jb + 1 < r.hi) ? s[4 * q + 1] : -INFINITY;
+      v.z = (jb + 2 >= r.lo && jb + 2 < r.hi) ? s[4 * q + 2] : -INFINITY;
+      v.w = (jb + 3 >= r.lo && jb + 3 < r.hi) ? s[4 * q + 3] : -INFINITY;
+      *reinterpret_cast<float4 *>(&s_nm[q * kQuarter + 4 * tid + HALO]) = v;
     }
     if (tid < 2 * HALO) {
-      const int off = (tid < HALO) ? tid - HALO : kCH + tid - HALO;
-      const int j = j0 + off;
+      const int j = j0 + hoff;
       float v = -INFINITY;
       if (j >= r.lo && j < r.hi) {
         // the same expression as the chunk's own keys
-        if constexpr (FUSED) {
-          const float w = prior_w(a.key_norm[r.row * a.ld + j], j, muf, cz, tq, ct);
-          v = fmaf(cf, a.score[r.row * a.ld + j], cr * w);
-        } else {
-          v = a.score[r.row * a.ld + j];
-        }
+        if constexpr (FUSED)
+          v = fmaf(cf, hs, cr * prior_w(hn, j, muf, cz, tq, ct));
+        else
+          v = hs;
       }
-      s_nm[off + HALO] = v;
+      s_nm[hoff + HALO] = v;
     }
     __syncthreads();
     const float keep = 1.0f - a.nms_alpha;
+    const int R = a.nms_radius;
 #pragma unroll
-    for (int i = 0; i < kPT; ++i) {
-      const int j = key_pos(j0, i);
-      if (j >= r.lo && j < r.hi) {
-        const float sj = s_nm[j - j0 + HALO];
+    for (int q = 0; q < kPT / 4; ++q) {
+      // s_nm[b0 + t] holds key j0 + q kQuarter + 4 tid - HALO + t
+      const int b0 = q * kQuarter + 4 * tid;
+      float w[4 + 2 * HALO];
+#pragma unroll
+      for (int v = 0; v < (4 + 2 * HALO) / 4; ++v) {
+        const float4 x = *reinterpret_cast<const float4 *>(&s_nm[b0 + 4 * v]);
+        w[4 * v] = x.x;
+        w[4 * v + 1] = x.y;
+        w[4 * v + 2] = x.z;
+        w[4 * v + 3] = x.w;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = j0 + b0 + e;
+        const float sj = w[HALO + e];
         int m = 0;
-        for (int dd = 1; dd <= a.nms_radius; ++dd) {
-          m += (s_nm[j - j0 + HALO - dd] >= sj) ? 1 : 0;  // lower index: ties rank above
-          m += (s_nm[j - j0 + HALO + dd] > sj) ? 1 : 0;
+#pragma unroll
+        for (int dd = 1; dd <= HALO; ++dd) {
+          // lower index: an equal score ranks above
+          const int c = (w[HALO + e - dd] >= sj ? 1 : 0) + (w[HALO + e + dd] > sj ? 1 : 0);
+          m += (dd <= R) ? c : 0;
         }
         float f = 1.0f;
-        for (int t = 0; t < m; ++t) f *= keep;
-        s[i] *= f;
+#pragma unroll
+        for (int t = 0; t < 2 * HALO; ++t) f = (t < m) ? f * keep : f;
+        if (j >= r.lo && j < r.hi) s[4 * q + e] *= f;
       }
     }
   }
@@ -266,16 +323,18 @@ __device__ __forceinline__ void keys_body(const SelectLaunch &a, int p, int h, i
   // of the sequence whose first Top-K holds the key.
   if (a.round == 1) {
     const float keep = 1.0f - a.excl_beta;
-    const uint32_t *cnt = a.excl_cnt + (size_t)r.b * a.ld32 * 32;
-    const uint32_t *bits = a.excl_bits + r.row * a.ld32;
 #pragma unroll
-    for (int i = 0; i < kPT; ++i) {
-      const int j = key_pos(j0, i);
-      if (j >= r.lo && j < r.hi) {
-        const int e = (int)cnt[j] - (int)((bits[j >> 5] >> (j & 31)) & 1u);
-        float f = 1.0f;
-        for (int t = 0; t < e; ++t) f *= keep;
-        s[i] *= f;
+    for (int q = 0; q < kPT / 4; ++q) {
+      const uint32_t c4[4] = {ecnt[q].x, ecnt[q].y, ecnt[q].z, ecnt[q].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = j0 + q * kQuarter + 4 * tid + e;
+        if (j >= r.lo && j < r.hi) {
+          const int x = (int)c4[e] - (int)((ebit[q] >> (j & 31)) & 1u);
+          float f = 1.0f;
+          for (int t = 0; t < x; ++t) f *= keep;
+          s[4 * q + e] *= f;
+        }
       }
     }
   }
@@ -579,11 +638,26 @@ __device__ __forceinline__ void pick_body(const SelectLaunch &a, int p, int h, i
     const uint32_t byte = (s_bits[tid >> 2] >> (8 * (tid & 3))) & 0xFFu;
     int tot8;
     int o = before + block_exscan<kTW>(__popc(byte), s_wave, &tot8);
+    const bool scat = a.excl_beta > 0.f && a.round == 0;
+    uint32_t unw = 0u;  // winners past the list's capacity
     for (int e = 0; e < 8; ++e) {
       if (byte & (1u << e)) {
-        if (o < K) out[o] = p * kCH + 8 * tid + e;
+        const int j = p * kCH + 8 * tid + e;
+        if (o < K) {
+          out[o] = j;
+          if (scat) atomicAdd(&a.excl_cnt[(size_t)r.b * a.ld32 * 32 + j], 1u);
+        } else {
+          unw |= 1u << e;
+        }
         ++o;
       }
+    }
+    if (scat) {
+      // this chunk's words of the row's membership bits (every thread read
+      // its byte before the scan's barrier)
+      if (unw) atomicAnd(&s_bits[tid >> 2], ~(unw << (8 * (tid & 3))));
+      __syncthreads();
+      if (tid < kCH / 32) a.excl_bits[r.row * a.ld32 + p * (kCH / 32) + tid] = s_bits[tid];
     }
   }
   // 6. The last chunk's workgroup pads the list and writes its length.

@@ -103,7 +103,7 @@ FastWs fast_ws(const sfi_kv *kv, int sel_k, int n_sink, int window) {
 
 struct SelWs {
   int P, ld32;
-  size_t ghist, cum, sorted, nsum, wsum, meta, ecnt, ebits, total;
+  size_t ghist, cum, sorted, nsum, wsum, meta, ecnt, ebits, eghist, total;
 };
 
 SelWs select_ws(int B, int H, int max_seq_len) {
@@ -117,10 +117,12 @@ SelWs select_ws(int B, int H, int max_seq_len) {
   w.wsum = align_up(w.nsum + rows * w.P * 2 * sizeof(double));
   w.meta = align_up(w.wsum + rows * w.P * sizeof(double));
   // cross-head exclusivity: per-key row counts and per-row membership bits
-  w.ld32 = (max_seq_len + 31) / 32;
+  // over whole chunks, and the second round's row histograms
+  w.ld32 = w.P * (kSelChunk / 32);
   w.ecnt = align_up(w.meta + rows * sizeof(SelRowMeta));
   w.ebits = align_up(w.ecnt + (size_t)B * w.ld32 * 32 * sizeof(uint32_t));
-  w.total = align_up(w.ebits + rows * w.ld32 * sizeof(uint32_t));
+  w.eghist = align_up(w.ebits + rows * w.ld32 * sizeof(uint32_t));
+  w.total = align_up(w.eghist + rows * 4096 * sizeof(uint32_t));
   return w;
 }
 
@@ -209,6 +211,7 @@ sfi_status select_launch(const sfi_select_params *p, const int32_t *batch_ids, i
   a.excl_beta = (H > 1) ? p->excl_beta : 0.f;
   a.excl_cnt = carve<uint32_t>(ws, w.ecnt);
   a.excl_bits = carve<uint32_t>(ws, w.ebits);
+  a.excl_ghist = carve<uint32_t>(ws, w.eghist);
   a.ld32 = w.ld32;
   a.ws.P = w.P;
   a.ws.ghist = carve<uint32_t>(ws, w.ghist);

@@ -154,8 +154,11 @@ struct SelectLaunch {
   float excl_beta;
   // exclusivity's second round: per-key count of rows whose first Top-K
   // holds it [B][ld32 * 32] and each row's membership bits [B*H][ld32]
+  // (ld32 * 32 = whole chunks), and the second round's row histograms
+  // [B*H][4096]
   uint32_t *excl_cnt;
   uint32_t *excl_bits;
+  uint32_t *excl_ghist;
   int ld32;
   int round;  // 1: exclusivity's second key pass (applies the penalty)
 };
