@@ -325,6 +325,37 @@ def test_select_exclusivity_raw(beta):
     _say(f"  near-tie differences: {diff}")
 
 
+def test_select_exclusivity_reuses_workspace():
+    """Two exclusivity calls in a row on one workspace, the second on
+    shorter rows with a per-sequence k: the first key pass of each call
+    clears the counts and histograms the previous call left."""
+    _say("select exclusivity, workspace reuse")
+    rng = np.random.default_rng(52)
+    B, H, ld, k = 3, 4, 9000, 400
+    wsb = sfi.sfi_select_workspace_bytes(B, H, ld)
+    ws = torch.full((wsb,), 0xA5, dtype=torch.uint8, device=DEV)     # not zeroed
+    diff = 0
+    for lens, kseq in (([9000, 8000, 6000], None), ([5000, 2000, 4100], [400, 150, 0])):
+        common = rng.standard_normal((B, 1, ld))
+        sc = np.exp(common + 0.7 * rng.standard_normal((B, H, ld))).astype(np.float32)
+        seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+        ks = None if kseq is None else torch.tensor(kseq, dtype=torch.int32, device=DEV)
+        p = sfi.select_params(sfi.SFI_SCORE_RAW, 0.0, k, 4, 256, k_per_seq=ks, nms_radius=2, nms_alpha=0.5,
+                              excl_beta=0.7)
+        sel = torch.full((B, H, k), -7, dtype=torch.int32, device=DEV)
+        cnt = torch.full((B, H), -7, dtype=torch.int32, device=DEV)
+        sfi.sfi_select(p, None, B, seq, B, H, ld, torch.from_numpy(sc).to(DEV), None, ld, sel, cnt, None,
+                       ws, wsb)
+        torch.cuda.synchronize()
+        sel, cnt = sel.cpu().numpy(), cnt.cpu().numpy()
+        for b in range(B):
+            kb = k if kseq is None else min(max(kseq[b], 0), k)
+            lo, hi = O.candidate_range(lens[b], 4, 256)
+            diff += _check_refined(sel[b], cnt[b], [sc[b, h] for h in range(H)], lo, hi, kb, 2, 0.5, 0.7)
+            assert np.all(sel[b, :, kb:] == -1)
+    _say(f"  differing keys: {diff}")
+
+
 def test_select_refinements_fused_from_oracle_evidence():
     """FUSED scores with Soft-NMS, exclusivity and both; fused_out keeps the
     score before the refinements."""
