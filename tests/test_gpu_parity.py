@@ -700,14 +700,14 @@ def test_decode_run_mixed_batch_co_launch():
     assert ties == 0
 
 
-@pytest.mark.parametrize("kdiv", [0, 16])
-def test_layer_pipeline_matches_per_layer_calls(kdiv):
+@pytest.mark.parametrize("kdiv,nms", [(0, False), (16, False), (0, True)])
+def test_layer_pipeline_matches_per_layer_calls(kdiv, nms):
     """sfi_decode_layer_step over a 3-layer stack, each layer's selection run
     inside the next layer's grids (and across the step boundary), against
     sfi_decode_step_select per layer: outputs and selections bit for bit.
     Steps: all slow, mixed, all fast, all slow, mixed; per-sequence k with
-    kdiv > 0."""
-    _say(f"layer pipeline, kdiv={kdiv}")
+    kdiv > 0; Soft-NMS (radius 3, alpha 0.4) with nms."""
+    _say(f"layer pipeline, kdiv={kdiv}, nms={nms}")
     B, Hq, Hkv, d, L = 4, 32, 8, 128, 3
     ctx = np.array([6000, 4500, 7000, 2600])
     slow = np.array([[1, 1, 1, 1], [0, 1, 0, 1], [0, 0, 0, 0], [1, 1, 1, 1], [1, 0, 0, 0]], dtype=bool)
@@ -715,6 +715,8 @@ def test_layer_pipeline_matches_per_layer_calls(kdiv):
     cap = int(ctx.max()) + steps + 1
     plan = DecodePlan(slow, ctx, DEV, k_cap=300 if kdiv else 0, k_div=kdiv)
     kw = dict(n_sink=4, window=256, k=300, lam=0.3)
+    if nms:
+        kw.update(nms_radius=3, nms_alpha=0.4)
     layers = []
     for layer in range(L):
         K, V = _rand_kv(B, Hkv, cap, d, seed=90 + layer, hh=25)
@@ -747,7 +749,11 @@ def test_layer_pipeline_matches_per_layer_calls(kdiv):
     kb = min(300, n // kdiv) if kdiv else 300
     r = O.slow_select(_bits(q[s, b]), _bits(K[b]), _bits(V[b]), n, lam=0.3, k=kb, n_sink=4, window=256)
     sel, cnt = pipe[1].sel_idx.cpu().numpy(), pipe[1].sel_count.cpu().numpy()
-    ties = sum(check_selection(sel[b, g, :kb], cnt[b, g], r["s"][g], r["lo"], r["hi"], kb) for g in range(Hkv))
+    if nms:
+        ties = _check_refined(sel[b, :, :kb], cnt[b], list(r["s"]), r["lo"], r["hi"], kb, 3, 0.4, 0.0)
+    else:
+        ties = sum(check_selection(sel[b, g, :kb], cnt[b, g], r["s"][g], r["lo"], r["hi"], kb)
+                   for g in range(Hkv))
     assert row_rel_err(pipe[1].out[b].cpu().numpy(), r["o"]) <= OUT_TOL
     _say(f"  near-tie differences: {ties}")
 
