@@ -162,10 +162,10 @@ def traffic_from_counters(d, steps):
         wb = sum(float(Wr[i]["Counter_Value"]) for i in range(lo, hi)) * ws * 1024
         t = tot.setdefault(leg, {}).setdefault(kind, [0.0, 0.0, 0, 0])
         t[0] += fb; t[1] += wb; t[2] += alg; t[3] += 1
-    cmds = [f"rocprofv3 --pmc {c} --output-format csv -d gpurun_out/traffic/{w} -o bench -- python3 -u "
+    dd = os.path.relpath(d) if os.path.isabs(d) else d.rstrip("/")
+    cmds = [f"rocprofv3 --pmc {c} --output-format csv -d {dd}/{w} -o bench -- python3 -u "
             f"bench.py --no-graph --steps {steps} --warmup 1 --no-cpu-baseline --calib-copy "
-            f"--record-calls gpurun_out/traffic/{w}/calls.json" for c, w in (("FETCH_SIZE", "fetch"),
-                                                                                ("WRITE_SIZE", "write"))]
+            f"--record-calls {dd}/{w}/calls.json" for c, w in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write"))]
     cal = {"copy_bytes": 1 << 28, "fetch_kib_read": float(F[ci]["Counter_Value"]),
            "write_kib_read": float(Wr[ci]["Counter_Value"]), "fetch_scale": round(fs, 4),
            "write_scale": round(ws, 4), "flush_reads_gib": flush_gib}
@@ -175,7 +175,7 @@ def traffic_from_counters(d, steps):
                 {k: {"calls": v[3], "fetch": int(v[0]), "write": int(v[1]), "algorithmic": int(v[2])}
                  for k, v in per_kind.items()})
     from dynamic_sparse_kv_amd import workload as W
-    cfg = W.CONFIGS["c2"].replace(steps=steps)
+    cfg = W.CONFIGS["llama3-8b-layer-32k"].replace(steps=steps)
     ratio, totals = summary(tot.get("headline", {}))
     res = {"workload": f"{cfg.name} (B={cfg.B}, Hq={cfg.Hq}, Hkv={cfg.Hkv}, d={cfg.d}, ctx {cfg.ctx}, "
                        f"{cfg.n_sink}+{cfg.window}+{cfg.k}, lambda {cfg.lam}), eager pass over decode steps "
@@ -363,7 +363,7 @@ def leg_stack128k(timed_steps=24, dense_steps=4):
     from dynamic_sparse_kv_amd.runner import DecodePlan, SFIDecoder
     dev = "cuda"
     steps = timed_steps + 1
-    cfg = W.CONFIGS["c3"].replace(steps=steps)
+    cfg = W.CONFIGS["stack32-128k"].replace(steps=steps)
     ctx = W.context_lengths(cfg)
     starts = W.sentence_starts(cfg)
     slow = sfi.sfi_schedule(starts, cfg.budget).astype(bool)
@@ -466,7 +466,7 @@ def leg_vegas64k(iters=12):
     from dynamic_sparse_kv_amd import workload as W
     from dynamic_sparse_kv_amd.runner import VegasDecoder
     dev = "cuda"
-    cfg = W.CONFIGS["c4"].replace(steps=iters)
+    cfg = W.CONFIGS["vegas-64k"].replace(steps=iters)
     T = cfg.vegas_T
     ctx = int(W.context_lengths(cfg).max())
     _log("[bench] vegas-64k: generating")
@@ -532,7 +532,7 @@ def leg_ragged_paged(timed_steps=32, dense_steps=4):
     from dynamic_sparse_kv_amd.runner import DecodePlan, SFIDecoder
     dev = "cuda"
     steps = timed_steps + 1
-    cfg = W.CONFIGS["c5"].replace(steps=steps)
+    cfg = W.CONFIGS["ragged-paged-8k-128k"].replace(steps=steps)
     ctx = W.context_lengths(cfg)
     caps = ctx + cfg.growth()
     table, npages = W.page_table(cfg, caps)
@@ -616,7 +616,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="c2")
+    ap.add_argument("--config", default="llama3-8b-layer-32k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--legs", default="stack32-128k,vegas-64k,ragged-paged",
                     help="extra workloads measured after the headline (comma list, or 'none')")

@@ -14,7 +14,7 @@ multi-query verification).  No dataset item is reproduced: keys, values and
 queries are Gaussian, with planted high-norm "heavy hitter" keys and
 sentence-structured queries so that attention has stable, shifting support.
 
-Random streams are keyed by ``SeedSequence([cfg_id, layer, b, kind])``.
+Random streams are keyed by ``SeedSequence([seed_key, layer, b, kind])``.
 Large tensors are drawn with a ``torch.Generator`` on the device they are
 used on; the same seed on another device gives other (equally valid) bytes, so
 every consumer that needs the values on the host copies them from the tensor
@@ -37,7 +37,7 @@ class SFIConfig:
     """One synthetic decode workload."""
 
     name: str
-    cfg_id: int
+    seed_key: int          # first key of the workload's random streams
     B: int
     Hq: int
     Hkv: int
@@ -86,27 +86,27 @@ class SFIConfig:
 
 CONFIGS = {
     # Tiny single layer: every step fits the oracle in seconds.
-    "c1": SFIConfig("tiny-4k", 1, B=1, Hq=8, Hkv=2, d=64, ctx=4096, steps=64,
+    "tiny-4k": SFIConfig("tiny-4k", 1, B=1, Hq=8, Hkv=2, d=64, ctx=4096, steps=64,
                     k=256, lam=0.3, hh_count=32),
     # Llama-3-8B-shaped layer at 32K context.
-    "c2": SFIConfig("llama3-8b-layer-32k", 2, B=8, Hq=32, Hkv=8, d=128, ctx=32768,
+    "llama3-8b-layer-32k": SFIConfig("llama3-8b-layer-32k", 2, B=8, Hq=32, Hkv=8, d=128, ctx=32768,
                     steps=256, k=2048, lam=0.3, hh_frac=0.01),
     # 32-layer stack at 128K context.
-    "c3": SFIConfig("stack32-128k", 3, B=4, Hq=32, Hkv=8, d=128, ctx=131072,
+    "stack32-128k": SFIConfig("stack32-128k", 3, B=4, Hq=32, Hkv=8, d=128, ctx=131072,
                     steps=128, k=4096, lam=0.2, mean_sentence=24.0, budget=32,
                     hh_frac=0.005, layers=32),
     # Verification-guided selection at 64K context, 8 verify rows.
-    "c4": SFIConfig("vegas-64k", 4, B=16, Hq=32, Hkv=8, d=128, ctx=65536, steps=64,
+    "vegas-64k": SFIConfig("vegas-64k", 4, B=16, Hq=32, Hkv=8, d=128, ctx=65536, steps=64,
                     k=2048, hh_frac=0.01, vegas_T=8),
     # Ragged long-reasoning batch, paged KV, Bernoulli slow steps.
-    "c5": SFIConfig("ragged-paged-8k-128k", 5, B=32, Hq=40, Hkv=8, d=128, ctx=131072,
+    "ragged-paged-8k-128k": SFIConfig("ragged-paged-8k-128k", 5, B=32, Hq=40, Hkv=8, d=128, ctx=131072,
                     steps=512, k=4096, lam=0.3, hh_frac=0.01, ragged_min=8192,
                     page_size=16, slow_prob=1.0 / 20.0, k_div=16),
 }
 
 
 def seed_for(cfg: SFIConfig, layer: int, b: int, kind: str) -> int:
-    ss = np.random.SeedSequence([cfg.cfg_id, layer, b, KIND[kind]])
+    ss = np.random.SeedSequence([cfg.seed_key, layer, b, KIND[kind]])
     return int(ss.generate_state(1, dtype=np.uint64)[0] & np.uint64(0x7FFF_FFFF_FFFF_FFFF))
 
 

@@ -50,7 +50,7 @@ def _free():
 
 
 def test_full_size_stack_layer_128k_sampled():
-    cfg = W.CONFIGS["c3"]
+    cfg = W.CONFIGS["stack32-128k"]
     layer = 5
     _say("full size: one 128K layer of the 32-layer stack")
     ctx = W.context_lengths(cfg)
@@ -95,7 +95,7 @@ def test_full_size_stack_pipeline_128k():
     selection run inside the next layer's grids, as the benchmark times it,
     against sfi_decode_step_select per layer: outputs and index lists bit
     for bit; one slow sequence's selection against the oracle."""
-    cfg = W.CONFIGS["c3"].replace(steps=3)
+    cfg = W.CONFIGS["stack32-128k"].replace(steps=3)
     _say("full size: 128K layer pipeline, 2 layers")
     ctx = W.context_lengths(cfg)
     ml = int(ctx.max()) + cfg.steps
@@ -138,7 +138,7 @@ def test_full_size_stack_pipeline_128k():
 
 
 def test_full_size_vegas_64k_sampled():
-    cfg = W.CONFIGS["c4"]
+    cfg = W.CONFIGS["vegas-64k"]
     T = cfg.vegas_T
     _say("full size: Vegas verification at 64K, B=16, T=8")
     ctx = int(W.context_lengths(cfg).max())
@@ -184,7 +184,7 @@ def test_full_size_vegas_64k_sampled():
 
 
 def test_full_size_ragged_paged_sampled():
-    cfg = W.CONFIGS["c5"].replace(steps=4)
+    cfg = W.CONFIGS["ragged-paged-8k-128k"].replace(steps=4)
     _say("full size: ragged paged batch, B=32, 8K-128K contexts")
     ctx = W.context_lengths(cfg)
     caps = ctx + cfg.growth()

@@ -389,7 +389,7 @@ def test_step_select_with_refinements(paged):
     seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
     kw = dict(n_sink=4, window=256, k=200, lam=0.3, nms_radius=3, nms_alpha=0.4, excl_beta=0.5)
     if paged:
-        cfg = W.CONFIGS["c5"].replace(B=B, Hq=Hq, Hkv=Hkv, d=d)
+        cfg = W.CONFIGS["ragged-paged-8k-128k"].replace(B=B, Hq=Hq, Hkv=Hkv, d=d)
         table, npages = W.page_table(cfg, np.full(B, cap))
         Kp, Vp = W.to_paged(K, table, npages, 16), W.to_paged(V, table, npages, 16)
         tab = torch.from_numpy(table).to(DEV)
@@ -502,7 +502,7 @@ def test_fast_without_selection_list():
 
 def test_decode_run_tiny_config_every_step():
     """Config: tiny 4K single layer, all 64 steps, slow/fast schedule."""
-    cfg = W.CONFIGS["c1"]
+    cfg = W.CONFIGS["tiny-4k"]
     _say("decode run c1")
     K, V = W.make_kv(cfg, device=DEV)
     starts = W.sentence_starts(cfg)
@@ -534,7 +534,7 @@ def test_decode_run_tiny_config_every_step():
 
 
 def test_bitwise_repeatable():
-    cfg = W.CONFIGS["c1"].replace(B=2, steps=24)
+    cfg = W.CONFIGS["tiny-4k"].replace(B=2, steps=24)
     K, V = W.make_kv(cfg, device=DEV)
     starts = W.sentence_starts(cfg)
     slow = O.schedule(starts, cfg.budget)
@@ -559,7 +559,7 @@ def test_bitwise_repeatable():
 def test_stream_pipelines_match_single_stream():
     """Two- and three-stream schedules (eager and graph-captured) give the same
     bits per step as one stream."""
-    cfg = W.CONFIGS["c1"].replace(B=3, steps=40, k=128)
+    cfg = W.CONFIGS["tiny-4k"].replace(B=3, steps=40, k=128)
     K, V = W.make_kv(cfg, device=DEV)
     starts = W.sentence_starts(cfg)
     slow = O.schedule(starts, cfg.budget)
@@ -629,7 +629,7 @@ def test_decode_step_co_launch_matches_oracle(Hq, Hkv, d, paged):
             sel[b, g, :c] = np.sort(rng.choice(lens[b], c, replace=False))
             cnt[b, g] = c
     if paged:
-        cfg = W.CONFIGS["c5"].replace(B=B, Hq=Hq, Hkv=Hkv, d=d)
+        cfg = W.CONFIGS["ragged-paged-8k-128k"].replace(B=B, Hq=Hq, Hkv=Hkv, d=d)
         table, npages = W.page_table(cfg, np.full(B, cap))
         Kd, Vd = W.to_paged(K, table, npages, 16), W.to_paged(V, table, npages, 16)
         tab = torch.from_numpy(table).to(DEV)
@@ -666,7 +666,7 @@ def test_decode_run_mixed_batch_co_launch():
     mixes slow and fast sequences is co-launched; each sequence's outputs and
     selections follow the oracle's decode run, and the separate-call path
     agrees within tolerance."""
-    cfg = W.CONFIGS["c1"].replace(B=3, steps=40)
+    cfg = W.CONFIGS["tiny-4k"].replace(B=3, steps=40)
     _say("mixed-batch decode run")
     K, V = W.make_kv(cfg, device=DEV)
     starts = W.sentence_starts(cfg)
@@ -773,7 +773,7 @@ def test_decode_step_select_matches_separate_calls(paged):
     kseq = torch.tensor([300, 120, 300, 64], dtype=torch.int32, device=DEV)
     kw = dict(n_sink=4, window=256, k=300, lam=0.3)
     if paged:
-        cfg = W.CONFIGS["c5"].replace(B=B, Hq=Hq, Hkv=Hkv, d=d)
+        cfg = W.CONFIGS["ragged-paged-8k-128k"].replace(B=B, Hq=Hq, Hkv=Hkv, d=d)
         table, npages = W.page_table(cfg, np.full(B, cap))
         Kp, Vp = W.to_paged(K, table, npages, 16), W.to_paged(V, table, npages, 16)
         tab = torch.from_numpy(table).to(DEV)
@@ -882,7 +882,7 @@ def test_vegas_draft_steps_with_shared_selection():
 
 def test_paged_cache_matches_contiguous_and_oracle():
     _say("paged")
-    cfg = W.CONFIGS["c5"].replace(B=4, Hq=40, Hkv=8, d=128, ctx=6000, ragged_min=1000, steps=2)
+    cfg = W.CONFIGS["ragged-paged-8k-128k"].replace(B=4, Hq=40, Hkv=8, d=128, ctx=6000, ragged_min=1000, steps=2)
     ctx = W.context_lengths(cfg)
     K, V = W.make_kv(cfg, device=DEV)
     cap = K.shape[2]
@@ -941,7 +941,7 @@ def test_random_shapes_step_select_then_fast(seed):
     ml = max(lens) + adv
     kw = {}
     if paged:
-        cfg = W.CONFIGS["c5"].replace(B=B, Hq=Hq, Hkv=Hkv, d=d)
+        cfg = W.CONFIGS["ragged-paged-8k-128k"].replace(B=B, Hq=Hq, Hkv=Hkv, d=d)
         table, npages = W.page_table(cfg, np.full(B, cap))
         Kd, Vd = W.to_paged(K, table, npages, 16), W.to_paged(V, table, npages, 16)
         kw = dict(page_table=torch.from_numpy(table).to(DEV), page_size=16)
@@ -1013,7 +1013,7 @@ def test_slow_step_window_matches_oracle(Hq, Hkv, d, w, paged):
     Kc, Vc = K, V
     table = None
     if paged:
-        cfg = W.CONFIGS["c5"].replace(B=B, Hq=Hq, Hkv=Hkv, d=d)
+        cfg = W.CONFIGS["ragged-paged-8k-128k"].replace(B=B, Hq=Hq, Hkv=Hkv, d=d)
         table, npages = W.page_table(cfg, np.full(B, cap))
         K = W.to_paged(K, table, npages, 16)
         V = W.to_paged(V, table, npages, 16)
@@ -1071,7 +1071,7 @@ def test_fast_compact_matches_index_gather(paged):
     dropped), ragged lengths (one sequence shorter than sinks + window, one with fewer
     candidates than k) and a batch subset in non-sorted order."""
     _say(f"fast compact paged={paged}")
-    cfg = W.CONFIGS["c5"].replace(B=4, Hq=32, Hkv=8, d=128)
+    cfg = W.CONFIGS["ragged-paged-8k-128k"].replace(B=4, Hq=32, Hkv=8, d=128)
     cap = 5008
     K, V = _rand_kv(cfg.B, cfg.Hkv, cap, cfg.d, seed=70, hh=8)
     lens0 = [4900, 200, 700, 3100]          # at the selection
@@ -1137,7 +1137,7 @@ def _unpage(P, table, b, cap):
 def test_full_size_llama_layer_32k_sampled():
     """8 sequences x 32K context, Hq=32/Hkv=8, d=128, k=2048: the benchmark's
     launch shapes; the oracle checks two sampled sequences."""
-    cfg = W.CONFIGS["c2"]
+    cfg = W.CONFIGS["llama3-8b-layer-32k"]
     _say("full size 32K")
     K, V = W.make_kv(cfg, device=DEV)
     ctx = W.context_lengths(cfg)

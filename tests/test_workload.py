@@ -6,7 +6,7 @@ from dynamic_sparse_kv_amd import workload as W
 
 
 def _tiny():
-    return W.CONFIGS["c1"].replace(ctx=300, steps=20, hh_count=5)
+    return W.CONFIGS["tiny-4k"].replace(ctx=300, steps=20, hh_count=5)
 
 
 def test_same_seed_same_bytes():
@@ -55,7 +55,7 @@ def test_queries_ar1_structure():
 
 
 def test_ragged_and_pages():
-    cfg = W.CONFIGS["c5"].replace(B=6, Hkv=2, Hq=4, d=64, ctx=4096, ragged_min=256, steps=3)
+    cfg = W.CONFIGS["ragged-paged-8k-128k"].replace(B=6, Hkv=2, Hq=4, d=64, ctx=4096, ragged_min=256, steps=3)
     ctxs = W.context_lengths(cfg)
     assert ctxs.min() >= 256 and ctxs.max() <= 4096
     table, total = W.page_table(cfg, ctxs + cfg.growth())
