@@ -115,9 +115,9 @@ __global__ __launch_bounds__(kT) void prior_kernel(SelectLaunch a) {
 }
 
 // --------------------------------------------------------------- 3. keys
-template <bool FUSED>
+template <bool FUSED, bool REFINE>
 __global__ __launch_bounds__(kT) void keys_kernel(SelectLaunch a) {
-  keys_body<FUSED>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+  keys_body<FUSED, REFINE>(a, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // ----------------------------------------------------------- 4. pick
@@ -130,6 +130,17 @@ __global__ __launch_bounds__(kT) void pick_kernel(SelectLaunch a) {
 hipError_t launch_select(const SelectLaunch &a, hipStream_t st) {
   const dim3 grid(a.ws.P, a.H, a.batch_n);
   const bool fused = a.mode == 0;
+  const bool refine = a.nms_radius > 0 || (a.excl_beta > 0.f && a.H > 1);
+  auto keys = [&](const SelectLaunch &x) {
+    if (fused && refine)
+      hipLaunchKernelGGL((keys_kernel<true, true>), grid, dim3(kT), 0, st, x);
+    else if (fused)
+      hipLaunchKernelGGL((keys_kernel<true, false>), grid, dim3(kT), 0, st, x);
+    else if (refine)
+      hipLaunchKernelGGL((keys_kernel<false, true>), grid, dim3(kT), 0, st, x);
+    else
+      hipLaunchKernelGGL((keys_kernel<false, false>), grid, dim3(kT), 0, st, x);
+  };
   hipError_t e;
   if (fused) {
     if (!a.prior_done) {  // else the slow step's finalize wrote the prior sums
@@ -138,11 +149,11 @@ hipError_t launch_select(const SelectLaunch &a, hipStream_t st) {
       hipLaunchKernelGGL(prior_kernel<true>, grid, dim3(kT), 0, st, a);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(keys_kernel<true>, grid, dim3(kT), 0, st, a);
+    keys(a);
   } else {
     hipLaunchKernelGGL(prior_kernel<false>, grid, dim3(kT), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(keys_kernel<false>, grid, dim3(kT), 0, st, a);
+    keys(a);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(pick_kernel, grid, dim3(kT), 0, st, a);
@@ -154,10 +165,7 @@ hipError_t launch_select(const SelectLaunch &a, hipStream_t st) {
     SelectLaunch a2 = a;
     a2.round = 1;
     a2.ws.ghist = a.excl_ghist;
-    if (fused)
-      hipLaunchKernelGGL(keys_kernel<true>, grid, dim3(kT), 0, st, a2);
-    else
-      hipLaunchKernelGGL(keys_kernel<false>, grid, dim3(kT), 0, st, a2);
+    keys(a2);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(pick_kernel, grid, dim3(kT), 0, st, a2);
   }

@@ -162,7 +162,9 @@ __device__ __forceinline__ int composite_index(unsigned long long c) {
 
 // --------------------------------------------------------------- 3. keys
 // Workgroup (chunk p, head row h, batch entry z) of the key pass.
-template <bool FUSED>
+// REFINE = false compiles out Soft-NMS and exclusivity (a call with both
+// off runs that variant).
+template <bool FUSED, bool REFINE = true>
 __device__ __forceinline__ void keys_body(const SelectLaunch &a, int p, int h, int z) {
   __shared__ unsigned hist[kBins1];
   __shared__ unsigned long long s_sorted[kCH];
@@ -172,7 +174,7 @@ __device__ __forceinline__ void keys_body(const SelectLaunch &a, int p, int h, i
   if (!row_geo(a, h, z, r)) return;
   const int j0 = p * kCH;
   const int tid = threadIdx.x;
-  const bool excl0 = a.excl_beta > 0.f && a.round == 0;
+  const bool excl0 = REFINE && a.excl_beta > 0.f && a.round == 0;
   // exclusivity: the first round clears the second round's row histogram
   if (excl0 && p == 0)
     for (int i = tid; i < kBins1; i += kT) a.excl_ghist[r.row * kBins1 + i] = 0u;
@@ -182,7 +184,7 @@ __device__ __forceinline__ void keys_body(const SelectLaunch &a, int p, int h, i
   // (kNmsMaxRadius on each side; threads past the halo re-read key j0, so
   // no load sits behind a per-lane branch) and, in exclusivity's second
   // round, the per-key counts and this row's first-round membership bits.
-  const bool nms = a.nms_radius > 0;
+  const bool nms = REFINE && a.nms_radius > 0;
   int hoff = 0;
   float hs = 0.f, hn = 0.f;
   if (nms) {
@@ -194,7 +196,7 @@ __device__ __forceinline__ void keys_body(const SelectLaunch &a, int p, int h, i
   }
   uint4 ecnt[kPT / 4];
   uint32_t ebit[kPT / 4];
-  if (a.round == 1) {
+  if (REFINE && a.round == 1) {
     const uint32_t *cnt = a.excl_cnt + (size_t)r.b * a.ld32 * 32;
     const uint32_t *bits = a.excl_bits + r.row * a.ld32;
 #pragma unroll
@@ -259,6 +261,7 @@ __device__ __forceinline__ void keys_body(const SelectLaunch &a, int p, int h, i
   // candidate within the radius that ranks above it (larger score, or equal
   // score and lower index).  The chunk's scores and a halo of kNmsMaxRadius
   // keys on each side are staged in LDS; non-candidates never rank above.
+  if constexpr (REFINE) {
   if (nms) {
     __shared__ __align__(16) float s_nm[kCH + 2 * kNmsMaxRadius];
     constexpr int HALO = kNmsMaxRadius;
@@ -338,6 +341,7 @@ __device__ __forceinline__ void keys_body(const SelectLaunch &a, int p, int h, i
       }
     }
   }
+  }  // REFINE
 
   uint32_t key[kPT];
 #pragma unroll
