@@ -478,3 +478,39 @@ def test_exclusivity_hand_case_and_identities():
     np.testing.assert_allclose(out[0], [0.9, 0.05, 0.2])
     np.testing.assert_allclose(out[1], [0.05, 0.9, 0.2])
     assert [list(t) for t in lists] == [[0], [1]]
+
+
+def test_soft_nms_closed_forms_on_monotone_runs():
+    """With the radius covering the whole range, a strictly decreasing run
+    has every lower index ranking above, so key j keeps s_j (1 - a)^j; an
+    increasing run gives (1 - a)^(n - 1 - j); a constant run ranks by index
+    (the decreasing case again).  Checked against these closed forms."""
+    n, a = 7, 0.3
+    dec = np.linspace(1.0, 0.4, n)
+    np.testing.assert_allclose(O.soft_nms(dec, 0, n, n, a), dec * (1 - a) ** np.arange(n), rtol=1e-14)
+    inc = dec[::-1].copy()
+    np.testing.assert_allclose(O.soft_nms(inc, 0, n, n, a), inc * (1 - a) ** (n - 1 - np.arange(n)),
+                               rtol=1e-14)
+    const = np.full(n, 0.5)
+    np.testing.assert_allclose(O.soft_nms(const, 0, n, n, a), const * (1 - a) ** np.arange(n), rtol=1e-14)
+    # radius 2 on the decreasing run: key j has min(j, 2) stronger neighbours
+    np.testing.assert_allclose(O.soft_nms(dec, 0, n, 2, a), dec * (1 - a) ** np.minimum(np.arange(n), 2),
+                               rtol=1e-14)
+
+
+def test_exclusivity_closed_form_on_identical_rows():
+    """H identical rows: every first list is the same top-k, so each picked
+    key is scaled by (1 - beta)^(H - 1) in every row and the others keep
+    their score; the second Top-K of that closed form is every row's list."""
+    rng = np.random.default_rng(8)
+    n, k, H, beta = 40, 6, 3, 0.5
+    base = rng.random(n)
+    rows = [base.copy() for _ in range(H)]
+    out, lists = O.exclusive_topk(rows, 0, n, k, beta)
+    first = O.topk_indices(base, 0, n, k)
+    want = base.copy()
+    want[first] *= (1 - beta) ** (H - 1)
+    for g in range(H):
+        np.testing.assert_allclose(out[g], want, rtol=1e-14)
+        np.testing.assert_array_equal(lists[g], O.topk_indices(want, 0, n, k))
+    assert set(lists[0]) != set(first)      # the penalty moved part of the list
