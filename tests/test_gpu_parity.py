@@ -1175,3 +1175,32 @@ def test_full_size_llama_layer_32k_sampled():
         o_ref = O.fast_step(qb, Kf, Vf, lens_f[b], r["sel"], cfg.n_sink, cfg.window)
         assert row_rel_err(of[b], o_ref) <= OUT_TOL
     _say(f"  near-tie differences: {ties}")
+
+
+def test_full_size_llama_layer_32k_refined_sampled():
+    """The 32K benchmark shapes (8 x 32K, Hq=32/Hkv=8, k=2048) through the
+    combined step + selection call with Soft-NMS (radius 4, alpha 0.5) and
+    exclusivity (beta 0.5): one sampled sequence against the oracle's slow
+    step, fused score and refinements."""
+    cfg = W.CONFIGS["llama3-8b-layer-32k"]
+    _say("full size 32K, refined selection")
+    K, V = W.make_kv(cfg, device=DEV)
+    ctx = W.context_lengths(cfg)
+    ml = int(ctx.max()) + cfg.steps
+    q = _rand_q((cfg.B, cfg.Hq, cfg.d), seed=98)
+    lens = [int(ctx[b]) + 1 + 7 * b for b in range(cfg.B)]
+    seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    dec = SFIDecoder(K, V, cfg.Hq, ml, n_sink=cfg.n_sink, window=cfg.window, k=cfg.k, lam=cfg.lam,
+                     nms_radius=4, nms_alpha=0.5, excl_beta=0.5)
+    slow_ids = torch.tensor([5, 2], dtype=torch.int32, device=DEV)
+    fast_ids = torch.tensor([0, 1, 3, 4, 6, 7], dtype=torch.int32, device=DEV)
+    dec.step_select(q, seq, slow_ids, 2, fast_ids, 6)
+    torch.cuda.synchronize()
+    sel, cnt = dec.sel_idx.cpu().numpy(), dec.sel_count.cpu().numpy()
+    b = 5
+    n = lens[b]
+    r = O.slow_select(_bits(q[b]), _bits(K[b, :, :n]), _bits(V[b, :, :n]), n, lam=cfg.lam, k=cfg.k,
+                      n_sink=cfg.n_sink, window=cfg.window)
+    assert row_rel_err(dec.out[b].cpu().numpy(), r["o"]) <= OUT_TOL
+    diff = _check_refined(sel[b], cnt[b], list(r["s"]), r["lo"], r["hi"], cfg.k, 4, 0.5, 0.5)
+    _say(f"  differing keys: {diff}")
