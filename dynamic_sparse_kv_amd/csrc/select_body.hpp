@@ -257,7 +257,7 @@ __device__ __forceinline__ void keys_body(const SelectLaunch &a, int p, int h, i
     for (int q = 0; q < kCH / 4 / kT; ++q) c4[q * kT + tid] = make_uint4(0u, 0u, 0u, 0u);
   }
 
-  // Soft-NMS: a candidate's score is scaled by (1 - alpha) once per
+  // Soft-NMS: a candidate's log score drops by log(1/(1 - alpha)) once per
   // candidate within the radius that ranks above it (larger score, or equal
   // score and lower index).  The chunk's scores and a halo of kNmsMaxRadius
   // keys on each side are staged in LDS; non-candidates never rank above.
@@ -290,6 +290,7 @@ __device__ __forceinline__ void keys_body(const SelectLaunch &a, int p, int h, i
     }
     __syncthreads();
     const float keep = 1.0f - a.nms_alpha;
+    const float lkeep = logf(keep);
     const int R = a.nms_radius;
 #pragma unroll
     for (int q = 0; q < kPT / 4; ++q) {
@@ -315,17 +316,25 @@ __device__ __forceinline__ void keys_body(const SelectLaunch &a, int p, int h, i
           const int c = (w[HALO + e - dd] >= sj ? 1 : 0) + (w[HALO + e + dd] > sj ? 1 : 0);
           m += (dd <= R) ? c : 0;
         }
-        float f = 1.0f;
+        // a penalty of m log(1/keep) on the log score: a factor keep^m on
+        // the fused score (a probability), a subtraction on a RAW score
+        // (summed logits are already log scores)
+        if constexpr (FUSED) {
+          float f = 1.0f;
 #pragma unroll
-        for (int t = 0; t < 2 * HALO; ++t) f = (t < m) ? f * keep : f;
-        if (j >= r.lo && j < r.hi) s[4 * q + e] *= f;
+          for (int t = 0; t < 2 * HALO; ++t) f = (t < m) ? f * keep : f;
+          if (j >= r.lo && j < r.hi) s[4 * q + e] *= f;
+        } else {
+          if (j >= r.lo && j < r.hi) s[4 * q + e] = fmaf((float)m, lkeep, s[4 * q + e]);
+        }
       }
     }
   }
-  // Exclusivity's second pass: scaled by (1 - beta) once per other head row
-  // of the sequence whose first Top-K holds the key.
+  // Exclusivity's second pass: the log score drops by log(1/(1 - beta))
+  // once per other head row of the sequence whose first Top-K holds the key.
   if (a.round == 1) {
     const float keep = 1.0f - a.excl_beta;
+    const float lkeep = logf(keep);
 #pragma unroll
     for (int q = 0; q < kPT / 4; ++q) {
       const uint32_t c4[4] = {ecnt[q].x, ecnt[q].y, ecnt[q].z, ecnt[q].w};
@@ -334,9 +343,13 @@ __device__ __forceinline__ void keys_body(const SelectLaunch &a, int p, int h, i
         const int j = j0 + q * kQuarter + 4 * tid + e;
         if (j >= r.lo && j < r.hi) {
           const int x = (int)c4[e] - (int)((ebit[q] >> (j & 31)) & 1u);
-          float f = 1.0f;
-          for (int t = 0; t < x; ++t) f *= keep;
-          s[4 * q + e] *= f;
+          if constexpr (FUSED) {
+            float f = 1.0f;
+            for (int t = 0; t < x; ++t) f *= keep;
+            s[4 * q + e] *= f;
+          } else {
+            s[4 * q + e] = fmaf((float)x, lkeep, s[4 * q + e]);
+          }
         }
       }
     }

@@ -224,9 +224,20 @@ class SFIDecoder:
         return own
 
     def _new_event(self):
+        # events of earlier runs that have completed are released here
+        self._events = [e for e in self._events if not e.query()]
         e = torch.cuda.Event()
         self._events.append(e)
         return e
+
+    @staticmethod
+    def _no_capture(what: str):
+        """The multi-stream schedules run eagerly only: capturing their
+        fork/join structure into a HIP graph ended the host process inside
+        the capture's end, and that is not fixed, so a capture is refused."""
+        if torch.cuda.is_current_stream_capturing():
+            raise RuntimeError(f"{what}: multi-stream schedules cannot be captured into a HIP graph; "
+                               "run them eagerly, or capture the one-stream step()")
 
     # -- one decode step of a planned run ------------------------------------
     def step(self, plan: DecodePlan, s: int, q_steps, stream=None, out=None, co: bool = True,
@@ -272,6 +283,10 @@ class SFIDecoder:
         may run different steps at the same time.  All chains join back into
         stream_a.
         """
+        self._no_capture("run_pipelined")
+        for st in (stream_a, stream_b, stream_c):
+            with torch.cuda.stream(st):
+                self._no_capture("run_pipelined")
         copies = [(self.evidence, self.key_norm), (self.evidence_alt, self.key_norm_alt)]
         ev = self._new_event
         start = ev()
@@ -338,6 +353,10 @@ class SFIDecoder:
         output; otherwise the shared output buffer is used (still race-free:
         the two chains never write the same slot concurrently).
         """
+        self._no_capture("run_two_streams")
+        for st in (stream_a, stream_b):
+            with torch.cuda.stream(st):
+                self._no_capture("run_two_streams")
         ev = self._new_event
         start = ev()
         start.record(stream_a)

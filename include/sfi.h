@@ -107,16 +107,17 @@ typedef struct sfi_select_params {
    * neighbouring, correlated keys from filling one head's budget; cross-head
    * exclusivity penalises the same key being picked by several heads].  The
    * pages give no formula; the reading implemented (all 0 = off):
-   *   Soft-NMS: a candidate's score is multiplied by (1 - nms_alpha) once
-   *     per candidate within nms_radius positions that ranks above it
+   *   Soft-NMS: a candidate's log score drops by log(1/(1 - nms_alpha))
+   *     once per candidate within nms_radius positions that ranks above it
    *     (larger score, or equal score and lower index); one pass.
    *   Exclusivity: after a first Top-K of every head row of a sequence, a
-   *     row's key j is multiplied by (1 - excl_beta) once per other row whose
-   *     first Top-K holds j, and the Top-K is taken again (two selection
-   *     rounds; H >= 2 rows).
-   * Both act on log scores: for s > 0 each factor is the subtraction of
-   * m log(1/(1 - alpha)) from log s (a RAW score <= 0 is scaled the same
-   * way, which is no penalty there).  Decisions use the float32 scores.
+   *     row's key j loses log(1/(1 - excl_beta)) of log score once per other
+   *     row whose first Top-K holds j, and the Top-K is taken again (two
+   *     selection rounds; H >= 2 rows).
+   * Both penalties act on log scores [SFI 3.B]: the FUSED score is a
+   * probability, so a penalty of m log(1/(1 - a)) is the factor (1 - a)^m;
+   * a RAW score (Vegas' summed logits) is already a log score of either
+   * sign, so the penalty is subtracted from it.  Decisions use float32.
    * fused_out holds the score before either refinement.
    * nms_radius in [0, 8], nms_alpha and excl_beta in [0, 1) (else
    * SFI_ERR_RANGE).  sfi_decode_layer_step defers a selection into one key

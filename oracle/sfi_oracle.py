@@ -161,6 +161,8 @@ def prior(K, n: int, norm_coef: float = 0.5, pos_tau: float = 1024.0) -> np.ndar
 
 
 def key_norms(K, n: int) -> np.ndarray:
+    """nu[g, j] = Euclidean norm of key j of kv head g, j < n: the norm
+    statistic the prior standardises [SFI-it s3.B, key norms]."""
     Kf = _as_f64(K[:, :n])
     return np.sqrt((Kf * Kf).sum(axis=-1))
 
@@ -189,38 +191,48 @@ def topk_indices(score: np.ndarray, lo: int, hi: int, k: int) -> np.ndarray:
     return np.sort(j[order[:k]])
 
 
-def soft_nms(score, lo: int, hi: int, radius: int, alpha: float) -> np.ndarray:
-    """Soft-NMS inside one head row [SFI-it s3.B, SFI-pt s2.B: keeps
-    neighbouring, correlated keys from filling the budget; the pages give no
-    formula -- this reading: one pass, not greedy].  For a candidate j of
-    [lo, hi): s'_j = s_j (1 - alpha)^m_j, m_j = number of candidates i with
-    0 < |i - j| <= radius that rank above j (larger score, or an equal score
-    and a lower index).  The ranking comparisons use float32 values (the
-    precision the kernel decides them in); other keys keep s.  Parity of
-    this form with the paper: unpinned."""
+def _penalise(s, m, keep: float, log_scores: bool):
+    """A penalty of m log(1/keep) in log-score space: for a probability-like
+    score (FUSED) log s' = log s + m log keep, i.e. s' = s keep^m; a score
+    that is already a log score (RAW: Vegas' summed logits) loses
+    m log(1/keep) directly."""
+    if log_scores:
+        return s + m * math.log(keep)
+    return s * keep ** m
+
+
+def soft_nms(score, lo: int, hi: int, radius: int, alpha: float, log_scores: bool = False) -> np.ndarray:
+    """Soft-NMS inside one head row [SFI-it s3.B: a refinement applied to the
+    log scores before the Top-K; SFI-pt s2.B: keeps neighbouring, correlated
+    keys from filling the budget; the pages give no formula -- this reading:
+    one pass, not greedy].  For a candidate j of [lo, hi), m_j = number of
+    candidates i with 0 < |i - j| <= radius that rank above j (larger score,
+    or an equal score and a lower index), compared in float64; the log score
+    of j drops by m_j log(1 / (1 - alpha)) (see _penalise); other keys keep
+    theirs.  Parity of this form with the paper: unpinned."""
     s = np.asarray(score, dtype=np.float64)
     out = s.copy()
     lo = max(lo, 0)
     if hi <= lo or radius <= 0 or alpha == 0.0:
         return out
-    s32 = s.astype(np.float32)
     for j in range(lo, hi):
         m = 0
         for i in range(max(lo, j - radius), min(hi, j + radius + 1)):
-            if i != j and (s32[i] > s32[j] or (s32[i] == s32[j] and i < j)):
+            if i != j and (s[i] > s[j] or (s[i] == s[j] and i < j)):
                 m += 1
-        out[j] = s[j] * (1.0 - alpha) ** m
+        out[j] = _penalise(s[j], m, 1.0 - alpha, log_scores)
     return out
 
 
-def exclusive_topk(rows, lo: int, hi: int, k: int, beta: float):
+def exclusive_topk(rows, lo: int, hi: int, k: int, beta: float, log_scores: bool = False):
     """Cross-head exclusivity over the head rows of one sequence [SFI-it
     s3.B, SFI-pt s2.B: penalise the same key being picked by several heads;
     no formula in the pages -- this reading].  T_g = Top-K of row g;
-    c_j = number of rows whose T_g holds j; row g's key j is scaled by
-    (1 - beta)^(c_j - [j in T_g]) (once per other head that picked it) and
-    the Top-K is taken again.  Returns (rescaled rows, final lists).  Parity
-    of this form with the paper: unpinned."""
+    c_j = number of rows whose T_g holds j; the log score of row g's key j
+    drops by (c_j - [j in T_g]) log(1 / (1 - beta)) (once per other head that
+    picked it; see _penalise) and the Top-K is taken again.  Returns
+    (rescaled rows, final lists).  Parity of this form with the paper:
+    unpinned."""
     rows = [np.asarray(r, dtype=np.float64) for r in rows]
     first = [topk_indices(r, lo, hi, k) for r in rows]
     if beta == 0.0 or len(rows) < 2:
@@ -233,7 +245,7 @@ def exclusive_topk(rows, lo: int, hi: int, k: int, beta: float):
     for r, t in zip(rows, first):
         own = np.zeros(n, dtype=np.int64)
         own[t] = 1
-        out.append(r * (1.0 - beta) ** (c - own))
+        out.append(_penalise(r, c - own, 1.0 - beta, log_scores))
     return out, [topk_indices(r, lo, hi, k) for r in out]
 
 
@@ -243,7 +255,10 @@ def candidate_range(n: int, n_sink: int, window: int):
 
 
 def kth_score(score: np.ndarray, lo: int, hi: int, k: int) -> Optional[float]:
-    """The k-th largest score over [lo, hi) (None when |C| <= k)."""
+    """The k-th largest score over [lo, hi), counting equal scores
+    separately (None when |C| <= k: every candidate is then selected and no
+    near-tie decision exists).  It sets the near-tie band of the selection
+    checks."""
     if hi - lo <= k:
         return None
     s = np.sort(np.asarray(score[lo:hi], dtype=np.float64))[::-1]

@@ -514,3 +514,136 @@ def test_exclusivity_closed_form_on_identical_rows():
         np.testing.assert_allclose(out[g], want, rtol=1e-14)
         np.testing.assert_array_equal(lists[g], O.topk_indices(want, 0, n, k))
     assert set(lists[0]) != set(first)      # the penalty moved part of the list
+
+
+def test_soft_nms_log_scores_hand_case():
+    """RAW scores (Vegas' summed logits) are already log scores, so the
+    penalty is subtracted: radius 1, alpha 0.5 over s = [-1, -2, -1.5, -3]:
+    key 1 has two stronger neighbours -> -2 + 2 ln 0.5, key 3 one -> -3 +
+    ln 0.5, keys 0 and 2 none.  A negative score never rises (the top-2
+    stays {0, 2}); multiplying it by 0.5 would lift key 1 to -1 and
+    promote it above key 2."""
+    s = np.array([-1.0, -2.0, -1.5, -3.0])
+    out = O.soft_nms(s, 0, 4, 1, 0.5, log_scores=True)
+    ln2 = math.log(2.0)
+    np.testing.assert_allclose(out, [-1.0, -2.0 - 2 * ln2, -1.5, -3.0 - ln2], rtol=1e-15)
+    assert list(O.topk_indices(out, 0, 4, 2)) == [0, 2]
+    assert np.all(out <= s)
+
+
+def test_refinements_in_log_space_agree_between_domains():
+    """The log-score reading, checked across its two forms: for positive
+    scores, Soft-NMS and exclusivity on log s with additive penalties equal
+    the log of the multiplicative forms on s (same ranks, same counts)."""
+    rng = np.random.default_rng(12)
+    s = rng.random(200) + 0.01
+    for radius, alpha in ((1, 0.5), (4, 0.3), (8, 0.9)):
+        mult = O.soft_nms(s, 5, 190, radius, alpha)
+        logv = O.soft_nms(np.log(s), 5, 190, radius, alpha, log_scores=True)
+        np.testing.assert_allclose(logv, np.log(mult), rtol=1e-12, atol=1e-12)
+    rows = [rng.random(60) + 0.01 for _ in range(4)]
+    out_m, lists_m = O.exclusive_topk(rows, 2, 50, 7, 0.4)
+    out_l, lists_l = O.exclusive_topk([np.log(r) for r in rows], 2, 50, 7, 0.4, log_scores=True)
+    for a, b, la, lb in zip(out_m, out_l, lists_m, lists_l):
+        np.testing.assert_allclose(b, np.log(a), rtol=1e-12, atol=1e-12)
+        np.testing.assert_array_equal(la, lb)
+
+
+def test_exclusivity_log_scores_hand_case():
+    """Two heads of negative RAW scores, k = 1, both pick key 0 first; beta
+    0.5 lowers key 0 by ln 2 in each row (one other head picked it): -1 -
+    ln 2 = -1.69 < -1.2 and < -1.5, so both move to key 1."""
+    rows = [np.array([-1.0, -1.2]), np.array([-1.0, -1.5])]
+    out, lists = O.exclusive_topk(rows, 0, 2, 1, 0.5, log_scores=True)
+    np.testing.assert_allclose(out[0], [-1.0 - math.log(2.0), -1.2], rtol=1e-15)
+    np.testing.assert_allclose(out[1], [-1.0 - math.log(2.0), -1.5], rtol=1e-15)
+    assert [list(t) for t in lists] == [[1], [1]]
+
+
+def test_soft_nms_ranks_in_float64():
+    """Two scores that are equal in float32 but not in float64 rank by their
+    float64 values: the later, larger one suppresses the earlier one."""
+    a = 0.5
+    b = 0.5 + 1e-12                      # rounds to 0.5 in float32
+    assert np.float32(a) == np.float32(b)
+    out = O.soft_nms(np.array([a, b]), 0, 2, 1, 0.5)
+    np.testing.assert_allclose(out, [a * 0.5, b], rtol=1e-15)
+
+
+# ----------------------------------------------------------- key norms, k-th score
+
+def test_key_norms_hand_values():
+    """Pythagorean rows are exact in bf16 and give exact norms: (3, 4) -> 5,
+    (5, 12) -> 13, (8, 15) -> 17, (1, 2, 2) -> 3, a sign flip changes
+    nothing and a zero row gives 0; two kv heads are kept apart, and keys
+    past n are not returned."""
+    d = 8
+    K = np.zeros((2, 6, d), dtype=np.float32)
+    K[0, 0, :2] = [3, 4]
+    K[0, 1, :2] = [5, 12]
+    K[0, 2, 3:5] = [-8, 15]
+    K[0, 3, :3] = [1, -2, 2]
+    K[1, 0, 7] = -7
+    K[1, 1, :] = 0.5                      # sqrt(8 * 0.25) = sqrt(2)
+    K[1, 2, :4] = [2, 2, 2, 2]            # 4
+    K[1, 4, :] = 1e6                      # past n: ignored
+    bits = (K.view(np.uint32) >> 16).astype(np.uint16)
+    nu = O.key_norms(bits, 4)
+    assert nu.shape == (2, 4)
+    np.testing.assert_array_equal(nu[0], [5.0, 13.0, 17.0, 3.0])
+    np.testing.assert_allclose(nu[1], [7.0, math.sqrt(2.0), 4.0, 0.0], rtol=1e-15)
+
+
+def test_key_norms_scale_and_agree_with_the_prior():
+    """A power-of-two scale of the keys scales the norms exactly, and the
+    norms are the ones the prior standardises: with two keys the population
+    z-scores are -1 and +1, so the prior's ratio is fixed by which norm is
+    larger (checked for the norms key_norms returns)."""
+    rng = np.random.default_rng(3)
+    K = rng.standard_normal((2, 5, 16)).astype(np.float32)
+    bits = (K.view(np.uint32) >> 16).astype(np.uint16)
+    bits4 = ((K * 4).view(np.uint32) >> 16).astype(np.uint16)
+    np.testing.assert_array_equal(O.key_norms(bits4, 5), 4 * O.key_norms(bits, 5))
+    nu = O.key_norms(bits, 2)
+    r = O.prior(bits, 2, norm_coef=0.5, pos_tau=1e9)   # position factor ~2 for both keys
+    for g in range(2):
+        big = int(np.argmax(nu[g]))
+        want = math.exp(-0.5) / (math.exp(-0.5) + math.exp(0.5))
+        np.testing.assert_allclose(r[g, big], want, rtol=1e-8)
+
+
+def test_kth_score_hand_cases():
+    """Hand cases: s = [5, 3, 3, 1, 4] over [0, 5) sorted is 5, 4, 3, 3, 1;
+    equal scores count separately; |C| <= k gives None (every candidate is
+    taken); |C| = k + 1 gives the k-th, not the last; a sub-range [1, 4)
+    ranks only its own keys."""
+    s = np.array([5.0, 3.0, 3.0, 1.0, 4.0])
+    assert O.kth_score(s, 0, 5, 1) == 5.0
+    assert O.kth_score(s, 0, 5, 2) == 4.0
+    assert O.kth_score(s, 0, 5, 3) == 3.0
+    assert O.kth_score(s, 0, 5, 4) == 3.0          # |C| = k + 1
+    assert O.kth_score(s, 0, 5, 5) is None         # |C| = k
+    assert O.kth_score(s, 0, 5, 6) is None
+    assert O.kth_score(s, 1, 4, 1) == 3.0
+    assert O.kth_score(s, 1, 4, 2) == 3.0
+    assert O.kth_score(s, 1, 4, 3) is None
+    assert O.kth_score(s, 2, 2, 1) is None         # empty range
+
+
+def test_kth_score_is_the_weakest_selected_score():
+    """Brute force: for |C| > k the k-th score is the minimum over the
+    Top-K, and exactly k - 1 candidates of the Top-K beat it strictly or
+    tie it at a lower rank; every unselected candidate is <= it."""
+    rng = np.random.default_rng(44)
+    for _ in range(50):
+        n = int(rng.integers(3, 40))
+        s = rng.integers(0, 6, n).astype(np.float64)       # many ties
+        lo = int(rng.integers(0, 2))
+        hi = int(rng.integers(lo + 2, n + 1))
+        k = int(rng.integers(1, hi - lo))
+        kth = O.kth_score(s, lo, hi, k)
+        sel = O.topk_indices(s, lo, hi, k)
+        assert kth == s[sel].min()
+        rest = np.setdiff1d(np.arange(lo, hi), sel)
+        assert np.all(s[rest] <= kth)
+        assert int(np.sum(s[lo:hi] > kth)) <= k - 1
