@@ -85,6 +85,7 @@ struct PartialArgs {
   double *nsum;  // [B][Hkv][stride][2] per-split key-norm sums, or null
   // fast step: compact copy of the selected rows, [B][Hkv][sel_k][D] (or null)
   const uint16_t *ck, *cv;
+  int pe;  // 1: partial buffers indexed by batch entry instead of sequence id
 };
 
 // Maximum over the wave of a value that is equal within each aligned group
@@ -229,7 +230,7 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
     // no rows here: a neutral partial (Z = 0), so the finalize can merge
     // every planned split without reading the list length
     if (tid < G) {
-      const size_t slot = ((size_t)b * a.Hq + g * G + tid) * a.stride + split;
+      const size_t slot = ((size_t)(a.pe ? zb : b) * a.Hq + g * G + tid) * a.stride + split;
       a.part_ml[slot * 2 + 0] = kNegBig;
       a.part_ml[slot * 2 + 1] = 0.f;
     }
@@ -580,7 +581,7 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
       o = fmaf(s_acc[w][h][e], sc, o);
       z = fmaf(s_z[w][h], sc, z);
     }
-    const size_t slot = ((size_t)b * a.Hq + g * G + h) * a.stride + split;
+    const size_t slot = ((size_t)(a.pe ? zb : b) * a.Hq + g * G + h) * a.stride + split;
     a.part_o[slot * D + e] = o;
     if (e == 0) {
       a.part_ml[slot * 2 + 0] = M;
@@ -684,6 +685,7 @@ struct FinalArgs {
   SelRowMeta *sel_meta;
   uint32_t *sel_ghist;
   int selP;
+  int pe;  // 1: partial buffers indexed by batch entry instead of sequence id
 };
 
 // Merge (m2, z2) into the running softmax pair (m, z): both are a log2-domain
@@ -707,6 +709,7 @@ __device__ __forceinline__ void finalize_body(const FinalArgs &a, int x, int g, 
   const bool comb = x < G;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const size_t hbase = (size_t)b * a.Hq + (size_t)g * G;
+  const size_t pbase = (size_t)(a.pe ? zb : b) * a.Hq + (size_t)g * G;  // rows of the partial buffers
 
   if (comb) {
     // every planned split: those past the row list wrote Z = 0 and are
@@ -717,10 +720,10 @@ __device__ __forceinline__ void finalize_body(const FinalArgs &a, int x, int g, 
     // into a running (m, z, o); the groups are then merged through LDS.
     constexpr int TPP = D / 4;
     constexpr int PARTS = kThreads / TPP;
-    const size_t row = hbase + x;
+    const size_t row = hbase + x, prow = pbase + x;
     const int e4 = tid % TPP, part = tid / TPP;
-    const float *pm = a.part_ml + row * a.stride * 2;
-    const float4 *po = reinterpret_cast<const float4 *>(a.part_o + row * a.stride * D) + e4;
+    const float *pm = a.part_ml + prow * a.stride * 2;
+    const float4 *po = reinterpret_cast<const float4 *>(a.part_o + prow * a.stride * D) + e4;
     float m = kNegBig, z = 0.f;
     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int s0 = part; s0 < S; s0 += 4 * PARTS) {
@@ -824,7 +827,7 @@ __device__ __forceinline__ void finalize_body(const FinalArgs &a, int x, int g, 
       float ml[G][2];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float *ml2 = a.part_ml + ((hbase + h) * a.stride + s) * 2;
+        const float *ml2 = a.part_ml + ((pbase + h) * a.stride + s) * 2;
         ml[h][0] = ml2[0];
         ml[h][1] = ml2[1];
       }
@@ -990,6 +993,7 @@ PartialArgs partial_args(const AttnLaunch &a) {
   p.nsum = a.nsum;
   p.ck = a.ck;
   p.cv = a.cv;
+  p.pe = a.part_by_entry ? 1 : 0;
   return p;
 }
 
@@ -1004,6 +1008,7 @@ FinalArgs final_args(const AttnLaunch &a) {
   f.sel_k = a.sel_k; f.n_sink = a.n_sink; f.window = a.window;
   f.nsum = a.nsum; f.key_norm = a.key_norm; f.norm_coef = a.norm_coef; f.pos_tau = a.pos_tau;
   f.sel_wsum = a.sel_wsum; f.sel_meta = a.sel_meta; f.sel_ghist = a.sel_ghist; f.selP = a.selP;
+  f.pe = a.part_by_entry ? 1 : 0;
   return f;
 }
 
@@ -1048,13 +1053,17 @@ hipError_t slow_t(const AttnLaunch &a_in, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Split plan of a fast step (chunks of the row list per (sequence, kv head)).
+template <int D, int G>
+SplitPlan fast_plan_t(const AttnLaunch &a) {
+  const int slots = resident_slots<partial_kernel<D, G, false, MODE_FAST, false>>();
+  return plan_splits(fast_rows(a), a.batch_n * a.Hkv, slots, a.plan.stride, kMaxFastChunk, false);
+}
+
 template <int D, int G, bool PAGED>
 hipError_t fast_t(const AttnLaunch &a_in, hipStream_t st) {
   AttnLaunch a = a_in;
-  {
-    const int slots = resident_slots<partial_kernel<D, G, false, MODE_FAST, false>>();
-    a.plan = plan_splits(fast_rows(a), a.batch_n * a.Hkv, slots, a.plan.stride, kMaxFastChunk, false);
-  }
+  if (!a.planned) a.plan = fast_plan_t<D, G>(a);
   const PartialArgs p = partial_args<D>(a);
   dim3 grid(a.plan.splits, a.Hkv, a.batch_n);
   hipLaunchKernelGGL((partial_kernel<D, G, PAGED, MODE_FAST, false>), grid, dim3(kThreads), 0, st, p);
@@ -1281,6 +1290,22 @@ hipError_t launch_step(const AttnLaunch &sa, const AttnLaunch &fa, hipStream_t s
 
 hipError_t launch_fast(const AttnLaunch &a, hipStream_t st) {
   SFI_DISPATCH(fast_t, a, st);
+}
+
+SplitPlan plan_fast(const AttnLaunch &a) {
+  switch (a.d * 16 + a.G) {
+    case 64 * 16 + 1: return fast_plan_t<64, 1>(a);
+    case 64 * 16 + 2: return fast_plan_t<64, 2>(a);
+    case 64 * 16 + 4: return fast_plan_t<64, 4>(a);
+    case 64 * 16 + 5: return fast_plan_t<64, 5>(a);
+    case 64 * 16 + 8: return fast_plan_t<64, 8>(a);
+    case 128 * 16 + 1: return fast_plan_t<128, 1>(a);
+    case 128 * 16 + 2: return fast_plan_t<128, 2>(a);
+    case 128 * 16 + 4: return fast_plan_t<128, 4>(a);
+    case 128 * 16 + 5: return fast_plan_t<128, 5>(a);
+    case 128 * 16 + 8: return fast_plan_t<128, 8>(a);
+    default: return SplitPlan{1, 1, 1};
+  }
 }
 
 hipError_t launch_fast_compact(const AttnLaunch &a, hipStream_t st) {

@@ -5,8 +5,17 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "sfi_internal.hpp"
+
+// Library-owned scratch of sfi_fast_step_noalloc: the split partials of one
+// call live here instead of in a caller workspace.  Each GPU the library runs
+// on holds its own copy (module globals are per device) until the process
+// ends.  Host code never passes this name to a kernel or a copy: on the host
+// it is only a stand-in for the symbol; the device address comes from
+// hipGetSymbolAddress (noalloc_scratch below).
+static __device__ __align__(256) unsigned char scratch[SFI_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -295,6 +304,26 @@ AttnLaunch fast_launch(const sfi_kv *kv, const KVView &view, bool paged, const F
   a.n_sink = n_sink;
   a.window = window;
   return a;
+}
+
+// Device address of `scratch` on the current device, resolved once per
+// device with that device current and cached.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+sfi_status noalloc_scratch(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SFI_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return SFI_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return SFI_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SFI_OK;
 }
 
 sfi_status check_fast(const sfi_kv *kv, const int32_t *sel_idx, const int32_t *sel_count,
@@ -610,6 +639,38 @@ sfi_status sfi_fast_step(const sfi_kv *kv, const int32_t *batch_ids, int32_t bat
   if (batch_n == 0) return SFI_OK;
   const AttnLaunch a = fast_launch(kv, view, paged, w, ws, batch_ids, batch_n, q, out, sel_idx,
                                    sel_count, sel_heads, sel_k, n_sink, window);
+  return launch_fast(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SFI_OK : SFI_ERR_HIP;
+}
+
+sfi_status sfi_fast_step_noalloc(const sfi_kv *kv, const int32_t *batch_ids, int32_t batch_n,
+                                 const uint16_t *q, const int32_t *sel_idx, const int32_t *sel_count,
+                                 int32_t sel_heads, int32_t sel_k, int32_t n_sink, int32_t window,
+                                 float *out, void *stream) {
+  KVView view;
+  bool paged = false;
+  sfi_status s = check_kv(kv, &view, &paged);
+  if (s != SFI_OK) return s;
+  if ((s = check_batch(kv, batch_n)) != SFI_OK) return s;
+  if (!q || !out) return SFI_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(out, 16)) return SFI_ERR_RANGE;
+  if ((s = check_fast(kv, sel_idx, sel_count, sel_heads, sel_k, n_sink, window)) != SFI_OK) return s;
+  if (batch_n == 0) return SFI_OK;
+  void *ptr = nullptr;
+  if ((s = noalloc_scratch(&ptr)) != SFI_OK) return s;
+  // The plan of sfi_fast_step (same chunks, same bits); the partials are
+  // packed by batch entry with the plan's split count as their stride.
+  const FastWs wfull = fast_ws(kv, sel_k, n_sink, window);
+  AttnLaunch a = fast_launch(kv, view, paged, wfull, ptr, batch_ids, batch_n, q, out, sel_idx, sel_count,
+                             sel_heads, sel_k, n_sink, window);
+  const SplitPlan plan = plan_fast(a);
+  const size_t rows = (size_t)batch_n * kv->Hq * plan.splits;
+  const size_t ml = align_up(rows * kv->d * sizeof(float));
+  if (ml + rows * 2 * sizeof(float) > (size_t)SFI_NOALLOC_SCRATCH_BYTES) return SFI_ERR_WORKSPACE;
+  a.part_o = carve<float>(ptr, 0);
+  a.part_ml = carve<float>(ptr, ml);
+  a.plan = SplitPlan{plan.chunk, plan.splits, plan.splits};
+  a.planned = true;
+  a.part_by_entry = true;
   return launch_fast(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SFI_OK : SFI_ERR_HIP;
 }
 

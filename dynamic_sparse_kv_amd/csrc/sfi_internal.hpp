@@ -92,10 +92,18 @@ struct AttnLaunch {
   int selP;
   // fast step: compact copy of the selected rows [B][Hkv][sel_k][d] (or null)
   const uint16_t *ck, *cv;
+  // partial buffers indexed by batch entry (rows [batch_n][Hq][stride])
+  // instead of by sequence id (rows [B][Hq][stride])
+  bool part_by_entry;
+  // plan fixed by the caller (launch_fast only): `plan` is used as given
+  bool planned;
 };
 
 hipError_t launch_slow(const AttnLaunch &a, hipStream_t st);
 hipError_t launch_fast(const AttnLaunch &a, hipStream_t st);
+// The split plan launch_fast takes for `a` (chunk and split count; the
+// stride is a.plan.stride's cap).
+SplitPlan plan_fast(const AttnLaunch &a);
 // Fast step whose selected rows come from the compact copy a.ck / a.cv.
 hipError_t launch_fast_compact(const AttnLaunch &a, hipStream_t st);
 // Copy the K/V rows of every valid selected entry (i < count, 0 <= id < n)

@@ -91,6 +91,9 @@ def lib():
         L.sfi_fast_step.argtypes = [P(sfi_kv), _vp, _c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int,
                                     _c_int, _vp, _vp, _sz, _vp]
         L.sfi_fast_step.restype = _c_int
+        L.sfi_fast_step_noalloc.argtypes = [P(sfi_kv), _vp, _c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int,
+                                            _c_int, _vp, _vp]
+        L.sfi_fast_step_noalloc.restype = _c_int
         L.sfi_slow_window_workspace_bytes.argtypes = [P(sfi_kv), _c_int]
         L.sfi_slow_window_workspace_bytes.restype = _sz
         L.sfi_slow_step_window.argtypes = [P(sfi_kv), _vp, _c_int, _vp, _c_int, _vp, _vp, _vp, _c_int, _vp,
@@ -235,6 +238,13 @@ def sfi_fast_step(kv: sfi_kv, batch_ids, batch_n: int, q, sel_idx, sel_count, se
     _check(lib().sfi_fast_step(ctypes.byref(kv), _ptr(batch_ids), batch_n, _ptr(q), _ptr(sel_idx),
                                _ptr(sel_count), sel_heads, sel_k, n_sink, window, _ptr(out),
                                _ptr(ws), ws_bytes, _stream(stream)), "sfi_fast_step")
+
+
+def sfi_fast_step_noalloc(kv: sfi_kv, batch_ids, batch_n: int, q, sel_idx, sel_count, sel_heads: int,
+                          sel_k: int, n_sink: int, window: int, out, stream=None):
+    _check(lib().sfi_fast_step_noalloc(ctypes.byref(kv), _ptr(batch_ids), batch_n, _ptr(q), _ptr(sel_idx),
+                                       _ptr(sel_count), sel_heads, sel_k, n_sink, window, _ptr(out),
+                                       _stream(stream)), "sfi_fast_step_noalloc")
 
 
 def sfi_slow_window_workspace_bytes(kv: sfi_kv, w: int) -> int:

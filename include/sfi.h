@@ -192,6 +192,29 @@ sfi_status sfi_fast_step(const sfi_kv *kv, const int32_t *batch_ids, int32_t bat
                          int32_t sel_heads, int32_t sel_k, int32_t n_sink, int32_t window,
                          float *out, void *ws, size_t ws_bytes, void *stream);
 
+/* sfi_fast_step for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, set, split plan and results (bit for bit) as
+ * sfi_fast_step, minus the workspace: the split partials live in a
+ * library-owned device array of SFI_NOALLOC_SCRATCH_BYTES per GPU, held
+ * until the process ends.  The call allocates and frees nothing.
+ *   Limit: the partials take batch_n * Hq * S * (d + 2) * 4 bytes (plus
+ *   alignment), S the call's split count per (sequence, kv head) (about
+ *   the GPU's resident workgroups / (batch_n * Hkv), at least 1); a call
+ *   that needs more than SFI_NOALLOC_SCRATCH_BYTES returns
+ *   SFI_ERR_WORKSPACE before anything is enqueued.
+ *   The first call on each device resolves the array's device address
+ *   (hipGetSymbolAddress, not a stream operation); make it outside a graph
+ *   capture.  Every call on one GPU shares that GPU's array: calls that
+ *   overlap in time on one GPU (other streams, other threads) race and give
+ *   wrong results; order them.  Nothing in the array needs clearing: every
+ *   planned partial is written before it is read. */
+#define SFI_NOALLOC_SCRATCH_BYTES (16u << 20)
+sfi_status sfi_fast_step_noalloc(const sfi_kv *kv, const int32_t *batch_ids, int32_t batch_n,
+                                 const uint16_t *q, const int32_t *sel_idx, const int32_t *sel_count,
+                                 int32_t sel_heads, int32_t sel_k, int32_t n_sink, int32_t window,
+                                 float *out, void *stream);
+
 /* Compact copy of the selected rows [SFI 3.C and the Portuguese summary,
  * section 2.C: a fast kernel that reads the sink and selected rows from one
  * contiguous buffer instead of scattered cache rows]: for every sequence b of

@@ -147,6 +147,26 @@ def test_fast_step_validation():
     assert call(_kv(), batch_n=0) == sfi.SFI_OK
 
 
+def test_fast_step_noalloc_validation():
+    """Argument errors of the no-workspace fast step are reported before the
+    library's scratch array is touched (no device call is made)."""
+    L = sfi.lib()
+
+    def call(kv, sel_heads=2, sel_k=64, sel_idx=FAKE, q=FAKE, n_sink=4, window=256, batch_n=1):
+        return L.sfi_fast_step_noalloc(ctypes.byref(kv), None, batch_n, q, sel_idx, FAKE, sel_heads, sel_k,
+                                       n_sink, window, FAKE, None)
+
+    assert call(_kv(), sel_heads=3) == sfi.SFI_ERR_SHAPE
+    assert call(_kv(), sel_k=-1) == sfi.SFI_ERR_RANGE
+    assert call(_kv(), n_sink=-1) == sfi.SFI_ERR_RANGE
+    assert call(_kv(), sel_idx=None) == sfi.SFI_ERR_NULL
+    assert call(_kv(), q=None) == sfi.SFI_ERR_NULL
+    assert call(_kv(), q=FAKE + 4) == sfi.SFI_ERR_RANGE
+    assert call(_kv(d=256)) == sfi.SFI_ERR_UNSUPPORTED
+    assert call(_kv(), batch_n=-1) == sfi.SFI_ERR_RANGE
+    assert call(_kv(), batch_n=0) == sfi.SFI_OK
+
+
 def test_decode_step_validation():
     L = sfi.lib()
 
