@@ -92,8 +92,8 @@ struct PartialArgs {
 // of 8 lanes (xor 8 stays inside a 16-lane row: a DPP rotate).
 __device__ __forceinline__ float wave_max_groups(float x) {
   x = fmaxf(x, dpp_f32<0x128>(x));  // row_ror:8 == lane ^ 8 within a row
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
+  x = xmax<16>(x);
+  x = xmax<32>(x);
   return x;
 }
 
@@ -504,18 +504,20 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
     constexpr int OFF = decltype(off_c)::value;
     constexpr int HALF = decltype(half_c)::value;
     const bool bit = (lane & OFF) != 0;
-    auto xch = [&](float x) -> float {
-      if constexpr (OFF == 8) return dpp_f32<0x128>(x);  // row_ror:8 == lane ^ 8 within a row
-      else return __shfl_xor(x, OFF);
-    };
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      Z[h] += xch(Z[h]);  // the reference m is wave-uniform: partials just add
+      if constexpr (OFF == 8) {  // row_ror:8 == lane ^ 8 within a row (DPP)
+        Z[h] += dpp_f32<0x128>(Z[h]);  // the reference m is wave-uniform: partials just add
 #pragma unroll
-      for (int i = 0; i < HALF; ++i) {
-        const float keep = bit ? acc[h][HALF + i] : acc[h][i];
-        const float send = bit ? acc[h][i] : acc[h][HALF + i];
-        acc[h][i] = keep + xch(send);
+        for (int i = 0; i < HALF; ++i) {
+          const float keep = bit ? acc[h][HALF + i] : acc[h][i];
+          const float send = bit ? acc[h][i] : acc[h][HALF + i];
+          acc[h][i] = keep + dpp_f32<0x128>(send);
+        }
+      } else {  // lane halves: permlane swaps (same sums, same order of operands)
+        Z[h] = xsum<OFF>(Z[h]);
+#pragma unroll
+        for (int i = 0; i < HALF; ++i) acc[h][i] = xsum_scatter<OFF>(acc[h][i], acc[h][HALF + i]);
       }
     }
     dim_off += bit ? HALF : 0;
@@ -624,6 +626,29 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(PartialArgs a, uint16
   const uint4 kk = ldg16(a.kv.k + src), vv = ldg16(a.kv.v + src);
   *reinterpret_cast<uint4 *>(ck + dst) = kk;
   *reinterpret_cast<uint4 *>(cv + dst) = vv;
+}
+
+// Cache append: rows t < T of the new tokens of sequence batch_ids[z] go to
+// cache rows seq_len[b] - T + t (rows below 0 are skipped).  One thread per
+// 16-byte slice of a K and a V row; grid (slices / kThreads, batch entries).
+template <int D, bool PAGED>
+__global__ __launch_bounds__(kThreads) void append_kernel(KVView kv, const int32_t *seq_len,
+                                                          const int32_t *batch_ids, int B, int max_len,
+                                                          const uint16_t *k_new, const uint16_t *v_new,
+                                                          int T) {
+  constexpr int SPR = D / 8;  // 16-byte slices per row
+  const int b = batch_seq(batch_ids, blockIdx.y, B);
+  if (b < 0) return;
+  const int i = blockIdx.x * kThreads + (int)threadIdx.x;
+  if (i >= T * kv.Hkv * SPR) return;
+  const int c = i % SPR, g = (i / SPR) % kv.Hkv, t = i / (SPR * kv.Hkv);
+  const int j = clamp_len(seq_len, b, max_len) - T + t;
+  if (j < 0) return;
+  const size_t src = (((size_t)b * T + t) * kv.Hkv + g) * D + 8 * c;
+  const size_t dst = kv_row<D, PAGED>(kv, b, g, j) + 8 * c;
+  const uint4 kk = ldg16(k_new + src), vv = ldg16(v_new + src);
+  *reinterpret_cast<uint4 *>(const_cast<uint16_t *>(kv.k) + dst) = kk;
+  *reinterpret_cast<uint4 *>(const_cast<uint16_t *>(kv.v) + dst) = vv;
 }
 
 // Slow (dense with evidence) and fast shares of one decode step in a single
@@ -1310,6 +1335,21 @@ SplitPlan plan_fast(const AttnLaunch &a) {
 
 hipError_t launch_fast_compact(const AttnLaunch &a, hipStream_t st) {
   SFI_DISPATCH(fast_compact_t, a, st);
+}
+
+hipError_t launch_append(const AttnLaunch &a, const uint16_t *k_new, const uint16_t *v_new, int T,
+                         hipStream_t st) {
+  if (a.batch_n < 1 || T < 1) return hipSuccess;
+  const int slices = T * a.Hkv * (a.d / 8);
+  dim3 grid((slices + kThreads - 1) / kThreads, a.batch_n);
+#define SFI_APPEND(D_, P_) \
+  hipLaunchKernelGGL((append_kernel<D_, P_>), grid, dim3(kThreads), 0, st, a.kv, a.seq_len, a.batch_ids, a.B, \
+                     a.max_len, k_new, v_new, T)
+  if (a.d == 128) { if (a.paged) SFI_APPEND(128, true); else SFI_APPEND(128, false); }
+  else if (a.d == 64) { if (a.paged) SFI_APPEND(64, true); else SFI_APPEND(64, false); }
+  else return hipErrorInvalidValue;
+#undef SFI_APPEND
+  return hipGetLastError();
 }
 
 hipError_t launch_compact(const AttnLaunch &a, uint16_t *ck, uint16_t *cv, hipStream_t st) {

@@ -674,6 +674,29 @@ sfi_status sfi_fast_step_noalloc(const sfi_kv *kv, const int32_t *batch_ids, int
   return launch_fast(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SFI_OK : SFI_ERR_HIP;
 }
 
+sfi_status sfi_append_kv(const sfi_kv *kv, const int32_t *batch_ids, int32_t batch_n,
+                         const uint16_t *k_new, const uint16_t *v_new, int32_t T, void *stream) {
+  KVView view;
+  bool paged = false;
+  sfi_status s = check_kv(kv, &view, &paged);
+  if (s != SFI_OK) return s;
+  if ((s = check_batch(kv, batch_n)) != SFI_OK) return s;
+  if (T < 1 || T > kv->max_seq_len) return SFI_ERR_RANGE;
+  if (!k_new || !v_new) return SFI_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new)) return SFI_ERR_RANGE;
+  if (batch_n == 0) return SFI_OK;
+  AttnLaunch a{};
+  a.kv = view;
+  a.seq_len = kv->seq_len;
+  a.batch_ids = batch_ids;
+  a.batch_n = batch_n;
+  a.B = kv->B; a.Hq = kv->Hq; a.Hkv = kv->Hkv; a.d = kv->d; a.G = kv->Hq / kv->Hkv;
+  a.max_len = kv->max_seq_len;
+  a.paged = paged;
+  return launch_append(a, k_new, v_new, T, static_cast<hipStream_t>(stream)) == hipSuccess ? SFI_OK
+                                                                                            : SFI_ERR_HIP;
+}
+
 sfi_status sfi_compact_selected(const sfi_kv *kv, const int32_t *batch_ids, int32_t batch_n,
                                 const int32_t *sel_idx, const int32_t *sel_count, int32_t sel_heads,
                                 int32_t sel_k, uint16_t *ck, uint16_t *cv, void *stream) {

@@ -39,6 +39,49 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Lane exchange across lane ^ OFF (OFF = 16 or 32) by the gfx950 permlane
+// swaps, which move data between lane halves in the VALU instead of through
+// the LDS crossbar.  permlaneOFF_swap(a, b) swaps a of the upper lanes with b
+// of the lower lanes, so afterwards a lower lane holds (own a, partner's a)
+// and an upper lane (partner's b, own b): the sum of the two results is, in
+// every lane, that lane's kept value (a below, b above) plus the partner's
+// copy of it -- one step of a reduce-scatter, with no per-lane select.
+template <int OFF>
+__device__ __forceinline__ float xsum_scatter(float a, float b) {
+  static_assert(OFF == 16 || OFF == 32, "lane halves of a row pair or of the wave");
+  uint32_t r0, r1;
+  if constexpr (OFF == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    r0 = r[0];
+    r1 = r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    r0 = r[0];
+    r1 = r[1];
+  }
+  return __uint_as_float(r0) + __uint_as_float(r1);
+}
+
+// x[lane] + x[lane ^ OFF] and max(x[lane], x[lane ^ OFF]) in every lane.
+template <int OFF>
+__device__ __forceinline__ float xsum(float x) { return xsum_scatter<OFF>(x, x); }
+
+template <int OFF>
+__device__ __forceinline__ float xmax(float x) {
+  static_assert(OFF == 16 || OFF == 32, "lane halves of a row pair or of the wave");
+  uint32_t r0, r1;
+  if constexpr (OFF == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    r0 = r[0];
+    r1 = r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    r0 = r[0];
+    r1 = r[1];
+  }
+  return fmaxf(__uint_as_float(r0), __uint_as_float(r1));
+}
+
 // Location of one cached K/V row.
 struct KVView {
   const uint16_t *k;

@@ -109,6 +109,9 @@ hipError_t launch_fast_compact(const AttnLaunch &a, hipStream_t st);
 // Copy the K/V rows of every valid selected entry (i < count, 0 <= id < n)
 // to row i of the compact copy ck / cv ([B][Hkv][sel_k][d]).
 hipError_t launch_compact(const AttnLaunch &a, uint16_t *ck, uint16_t *cv, hipStream_t st);
+// Write T new K/V rows per listed sequence at cache rows seq_len - T + t.
+hipError_t launch_append(const AttnLaunch &a, const uint16_t *k_new, const uint16_t *v_new, int T,
+                         hipStream_t st);
 struct SelectLaunch;
 // Slow step with evidence (sa) and fast step (fa) on disjoint sequences,
 // co-launched; either share may be empty.  A non-null pend is a selection

@@ -68,6 +68,16 @@ class DecodePlan:
         self.fast_old_ids = _dev_i32(old_ids, device)
         self.fast_new_ids = _dev_i32(new_ids, device)
 
+    def slow_list(self, s: int):
+        """Step s's slow-sequence list, or None when it is every sequence in
+        order (a NULL list: the kernels then need no id load before their
+        first dependent loads)."""
+        return None if self.n_slow[s] == self.B else self.slow_ids[s]
+
+    def fast_list(self, s: int):
+        """Step s's fast-sequence list, or None when it is every sequence."""
+        return None if self.n_fast[s] == self.B else self.fast_ids[s]
+
 
 class SFIDecoder:
     """Slow/fast decode of one attention layer over a resident KV cache."""
@@ -147,6 +157,12 @@ class SFIDecoder:
         finally:
             self.params.k_per_seq = None
 
+    def append(self, k_new, v_new, seq_len, batch_ids, batch_n: int, stream=None):
+        """Write the step's new K/V rows (k_new, v_new [B][T][Hkv][d]) at cache
+        rows seq_len - T .. seq_len - 1 of the listed sequences."""
+        self.kv.seq_len = seq_len.data_ptr() if torch.is_tensor(seq_len) else seq_len
+        sfi.sfi_append_kv(self.kv, batch_ids, batch_n, k_new, v_new, int(k_new.shape[1]), stream)
+
     def dense(self, q, seq_len, batch_ids, batch_n: int, stream=None):
         """Plain dense attention (no evidence): the full-KV comparator."""
         self.kv.seq_len = seq_len.data_ptr() if torch.is_tensor(seq_len) else seq_len
@@ -203,7 +219,8 @@ class SFIDecoder:
         finally:
             self.params.k_per_seq = None
 
-    def layer_step(self, plan: "DecodePlan", s: int, q_steps, pending=None, stream=None, out=None):
+    def layer_step(self, plan: "DecodePlan", s: int, q_steps, pending=None, stream=None, out=None,
+                   new_kv=None):
         """Decode step s of this layer in a stack (sfi_decode_layer_step): the
         previous layer's deferred selection (pending, an sfi_deferred or None)
         runs inside this call's grids and this layer's own selection is
@@ -211,11 +228,13 @@ class SFIDecoder:
         to the next layer's call, or to sfi_run_deferred after the last."""
         ks = None if plan.k_seq is None else plan.k_seq[s]
         ns, nf = int(plan.n_slow[s]), int(plan.n_fast[s])
+        if new_kv is not None:
+            self.append(new_kv[0][s], new_kv[1][s], plan.seq_len[s], None, self.B, stream)
         self.kv.seq_len = plan.seq_len[s].data_ptr()
         self.params.k_per_seq = None if ks is None else ks.data_ptr()
         own = sfi.sfi_deferred()
         try:
-            sfi.sfi_decode_layer_step(self.kv, self.params, plan.slow_ids[s], ns, plan.fast_ids[s], nf,
+            sfi.sfi_decode_layer_step(self.kv, self.params, plan.slow_list(s), ns, plan.fast_list(s), nf,
                                       q_steps[s], self.out if out is None else out, self.evidence,
                                       self.key_norm, self.ld, self.sel_idx, self.sel_count, self.fused,
                                       self.ws_stepsel, self.ws_stepsel_bytes, pending, own, stream)
@@ -241,8 +260,11 @@ class SFIDecoder:
 
     # -- one decode step of a planned run ------------------------------------
     def step(self, plan: DecodePlan, s: int, q_steps, stream=None, out=None, co: bool = True,
-             fused_select: bool = True):
+             fused_select: bool = True, new_kv=None):
         """Decode step s: q_steps is the device tensor [steps][B][Hq][d].
+
+        new_kv = (K_new, V_new), each [steps][B][1][Hkv][d]: the step first
+        appends every sequence's new row (sfi_append_kv) at row seq_len - 1.
 
         With co=True a step that has slow sequences runs as one call that
         co-launches its slow and fast shares and refreshes the slow
@@ -253,16 +275,19 @@ class SFIDecoder:
         sl = plan.seq_len[s]
         ks = None if plan.k_seq is None else plan.k_seq[s]
         ns, nf = int(plan.n_slow[s]), int(plan.n_fast[s])
+        sids, fids = plan.slow_list(s), plan.fast_list(s)
+        if new_kv is not None:
+            self.append(new_kv[0][s], new_kv[1][s], sl, None, self.B, stream)
         if co and ns and fused_select:
-            self.step_select(q, sl, plan.slow_ids[s], ns, plan.fast_ids[s], nf, stream, out=out, k_seq=ks)
+            self.step_select(q, sl, sids, ns, fids, nf, stream, out=out, k_seq=ks)
             return
         if co and ns and nf:
-            self.co_step(q, sl, plan.slow_ids[s], ns, plan.fast_ids[s], nf, stream, out=out, k_seq=ks)
+            self.co_step(q, sl, sids, ns, fids, nf, stream, out=out, k_seq=ks)
             return
         if ns:
-            self.slow(q, sl, plan.slow_ids[s], ns, stream, out=out, k_seq=ks)
+            self.slow(q, sl, sids, ns, stream, out=out, k_seq=ks)
         if nf:
-            self.fast(q, sl, plan.fast_ids[s], nf, stream, out=out)
+            self.fast(q, sl, fids, nf, stream, out=out)
 
     def run_pipelined(self, plan: DecodePlan, q_steps, s_begin: int, s_end: int, stream_a,
                       stream_b, stream_c, out_steps):

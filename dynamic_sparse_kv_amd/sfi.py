@@ -91,6 +91,8 @@ def lib():
         L.sfi_fast_step.argtypes = [P(sfi_kv), _vp, _c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int,
                                     _c_int, _vp, _vp, _sz, _vp]
         L.sfi_fast_step.restype = _c_int
+        L.sfi_append_kv.argtypes = [P(sfi_kv), _vp, _c_int, _vp, _vp, _c_int, _vp]
+        L.sfi_append_kv.restype = _c_int
         L.sfi_fast_step_noalloc.argtypes = [P(sfi_kv), _vp, _c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int,
                                             _c_int, _vp, _vp]
         L.sfi_fast_step_noalloc.restype = _c_int
@@ -238,6 +240,11 @@ def sfi_fast_step(kv: sfi_kv, batch_ids, batch_n: int, q, sel_idx, sel_count, se
     _check(lib().sfi_fast_step(ctypes.byref(kv), _ptr(batch_ids), batch_n, _ptr(q), _ptr(sel_idx),
                                _ptr(sel_count), sel_heads, sel_k, n_sink, window, _ptr(out),
                                _ptr(ws), ws_bytes, _stream(stream)), "sfi_fast_step")
+
+
+def sfi_append_kv(kv: sfi_kv, batch_ids, batch_n: int, k_new, v_new, T: int, stream=None):
+    _check(lib().sfi_append_kv(ctypes.byref(kv), _ptr(batch_ids), batch_n, _ptr(k_new), _ptr(v_new), T,
+                               _stream(stream)), "sfi_append_kv")
 
 
 def sfi_fast_step_noalloc(kv: sfi_kv, batch_ids, batch_n: int, q, sel_idx, sel_count, sel_heads: int,

@@ -292,6 +292,43 @@ def gather_paged(pool: torch.Tensor, table: np.ndarray, b: int, n: int) -> torch
     return rows[:, :n].contiguous()
 
 
+def take_decode_rows(K: torch.Tensor, V: torch.Tensor, ctx: np.ndarray, steps: int, rows_per_step: int = 1,
+                     table: Optional[np.ndarray] = None):
+    """Move the rows a decode run appends out of the cache.
+
+    Row t of step s of sequence b is cache row ctx[b] + s * rows_per_step + t.
+    Returns (K_new, V_new), each [steps][B][rows_per_step][Hkv][d] (copies of
+    those rows), and zeroes the rows in K and V, so that a run which appends
+    them before each step (sfi_append_kv) sees the same bytes as the cache
+    drawn up front.  Contiguous caches are [B][Hkv][cap][d]; with ``table``
+    they are paged pools [P][Hkv][page][d].  Layout only: nothing computed.
+    """
+    T = rows_per_step
+    B = len(ctx)
+    if table is None:
+        Hkv, d = K.shape[1], K.shape[3]
+    else:
+        Hkv, d = K.shape[1], K.shape[3]
+        ps = K.shape[2]
+    Kn = torch.empty((steps, B, T, Hkv, d), dtype=K.dtype, device=K.device)
+    Vn = torch.empty_like(Kn)
+    for b in range(B):
+        pos = int(ctx[b]) + torch.arange(steps * T, device=K.device)
+        if table is None:
+            for src, dst in ((K, Kn), (V, Vn)):
+                rows = src[b][:, pos]                                   # [Hkv][steps*T][d]
+                dst[:, b] = rows.permute(1, 0, 2).reshape(steps, T, Hkv, d)
+                src[b][:, pos] = 0
+        else:
+            tab = torch.as_tensor(table[b].astype(np.int64), device=K.device)
+            pg, off = tab[pos // ps], pos % ps
+            for src, dst in ((K, Kn), (V, Vn)):
+                rows = src[pg, :, off]                                  # [steps*T][Hkv][d]
+                dst[:, b] = rows.reshape(steps, T, Hkv, d)
+                src[pg, :, off] = 0
+    return Kn, Vn
+
+
 def bf16_bits(x: torch.Tensor) -> np.ndarray:
     """Raw bf16 bit patterns of a tensor as a host uint16 array."""
     return x.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)

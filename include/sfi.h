@@ -178,6 +178,19 @@ sfi_status sfi_select(const sfi_select_params *p, const int32_t *batch_ids, int3
                       int32_t *sel_idx, int32_t *sel_count, float *fused_out,
                       void *ws, size_t ws_bytes, void *stream);
 
+/* Cache append [SFI technical summary, section 1: every decode step attends
+ * the whole cached history, which grows by the step's own key and value]:
+ * for each listed sequence b, the T new rows k_new[b][t], v_new[b][t]
+ * (t < T) are written to cache row j = seq_len[b] - T + t of every kv head
+ * (seq_len already counts them; rows with j < 0 are skipped).  Paged caches
+ * write through the page table.  k/v of *kv must be writable device memory.
+ *   k_new, v_new  [B][T][Hkv][d] bf16 bits, 16-byte aligned.
+ *   1 <= T <= max_seq_len (else SFI_ERR_RANGE).
+ * Call it before the step that reads the rows, on the same stream.  Moves
+ * 2 x 2 d bytes per row and kv head (read and write of K and V). */
+sfi_status sfi_append_kv(const sfi_kv *kv, const int32_t *batch_ids, int32_t batch_n,
+                         const uint16_t *k_new, const uint16_t *v_new, int32_t T, void *stream);
+
 /* Fast step [SFI 3.A fast steps; Vegas 2 drafting]: attention of one decode
  * query per sequence over the fast set of its kv head g, with n = seq_len[b]:
  *   [0, min(n_sink, n))  U  [max(n_sink, n - window), n)  U

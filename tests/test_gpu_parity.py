@@ -612,6 +612,82 @@ def test_stream_pipelines_match_single_stream():
             assert row_rel_err(got[s], r["o"]) <= OUT_TOL, s
 
 
+# ------------------------------------------------------------ cache append
+
+@pytest.mark.parametrize("paged,T", [(False, 1), (True, 1), (False, 8), (True, 8)])
+def test_append_kv_writes_the_new_rows(paged, T):
+    """sfi_append_kv writes row t of each listed sequence at cache row
+    seq_len - T + t (rows below 0 skipped) of every kv head, bit for bit,
+    and leaves everything else untouched."""
+    _say(f"append paged={paged} T={T}")
+    B, Hq, Hkv, d, ps = 4, 8, 2, 128, 16
+    lens = [37, 5, 300, 129]          # sequence 1 has fewer than T = 8 rows
+    cap = 320
+    g = torch.Generator(device=DEV).manual_seed(90 + T)
+    Kc = torch.randn((B, Hkv, cap, d), generator=g, device=DEV).to(torch.bfloat16)
+    Vc = torch.randn((B, Hkv, cap, d), generator=g, device=DEV).to(torch.bfloat16)
+    kn = torch.randn((B, T, Hkv, d), generator=g, device=DEV).to(torch.bfloat16)
+    vn = torch.randn((B, T, Hkv, d), generator=g, device=DEV).to(torch.bfloat16)
+    seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    ids = torch.tensor([3, 1, 0], dtype=torch.int32, device=DEV)      # sequence 2 not listed
+    want_k, want_v = Kc.clone(), Vc.clone()
+    for b in (3, 1, 0):
+        for t in range(T):
+            j = lens[b] - T + t
+            if j >= 0:
+                want_k[b, :, j] = kn[b, t]
+                want_v[b, :, j] = vn[b, t]
+    if not paged:
+        K, V = Kc.clone(), Vc.clone()
+        kv = sfi.make_kv(K, V, seq, Hq, cap)
+    else:
+        npg = cap // ps
+        table = np.random.default_rng(5).permutation(B * npg).astype(np.int32).reshape(B, npg)
+        K = W.to_paged(Kc, table, B * npg, ps)
+        V = W.to_paged(Vc, table, B * npg, ps)
+        tab = torch.from_numpy(table).to(DEV)
+        kv = sfi.make_kv(K, V, seq, Hq, cap, tab, ps)
+    sfi.sfi_append_kv(kv, ids, 3, kn, vn, T)
+    torch.cuda.synchronize()
+    if paged:
+        got_k = torch.stack([W.gather_paged(K, table, b, cap) for b in range(B)])
+        got_v = torch.stack([W.gather_paged(V, table, b, cap) for b in range(B)])
+    else:
+        got_k, got_v = K, V
+    assert torch.equal(got_k.view(torch.int16), want_k.view(torch.int16))
+    assert torch.equal(got_v.view(torch.int16), want_v.view(torch.int16))
+
+
+def test_decode_run_with_append_equals_predrawn_cache():
+    """A decode run whose steps append their own K/V row (the cache holds
+    only the prefill at the start) gives the same bits, outputs and
+    selections, as the run over the cache drawn up front."""
+    _say("decode run with per-step append")
+    cfg = W.CONFIGS["tiny-4k"].replace(B=3, steps=30, k=128)
+    starts = W.sentence_starts(cfg)
+    slow = O.schedule(starts, cfg.budget)
+    q = W.make_queries(cfg, starts).to(DEV)
+    ctx = W.context_lengths(cfg)
+    plan = DecodePlan(slow, ctx, DEV)
+    res = []
+    for with_append in (False, True):
+        K, V = W.make_kv(cfg, device=DEV)
+        new_kv = W.take_decode_rows(K, V, ctx, cfg.steps) if with_append else None
+        if with_append:
+            assert torch.all(K[:, :, int(ctx[0]):] == 0)
+        dec = SFIDecoder(K, V, cfg.Hq, cfg.ctx + cfg.steps, n_sink=4, window=256, k=cfg.k, lam=cfg.lam)
+        outs = torch.zeros((cfg.steps, cfg.B, cfg.Hq, cfg.d), device=DEV)
+        for s in range(cfg.steps):
+            dec.step(plan, s, q, out=outs[s], new_kv=new_kv)
+        torch.cuda.synchronize()
+        res.append((outs.clone(), dec.sel_idx.clone(), K.clone(), V.clone()))
+    assert torch.equal(res[0][0].view(torch.int32), res[1][0].view(torch.int32))
+    assert torch.equal(res[0][1], res[1][1])
+    n_end = int(ctx[0]) + cfg.steps
+    assert torch.equal(res[0][2][:, :, :n_end].view(torch.int16), res[1][2][:, :, :n_end].view(torch.int16))
+    assert torch.equal(res[0][3][:, :, :n_end].view(torch.int16), res[1][3][:, :, :n_end].view(torch.int16))
+
+
 # ------------------------------------------------- co-launched decode step
 
 @pytest.mark.parametrize("Hq,Hkv,d,paged", [(8, 2, 64, False), (40, 8, 128, True)])

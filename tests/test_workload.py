@@ -66,3 +66,36 @@ def test_ragged_and_pages():
     b, pos = 3, int(ctxs[3]) - 1
     pg = table[b, pos // 16]
     assert torch.equal(pool[pg, :, pos % 16], K[b, :, pos])
+
+
+def test_take_decode_rows_contiguous_and_paged():
+    """The rows a run appends are moved out of the cache bit for bit: the
+    returned [steps][B][T][Hkv][d] rows equal the cache rows ctx + s*T + t,
+    which are then zero; the prefill is untouched (contiguous and paged)."""
+    cfg = W.CONFIGS["tiny-4k"].replace(B=2, steps=5, ctx=300)
+    K, V = W.make_kv(cfg)
+    K0, V0 = K.clone(), V.clone()
+    ctx = W.context_lengths(cfg)
+    Kn, Vn = W.take_decode_rows(K, V, ctx, 2, rows_per_step=2)
+    assert Kn.shape == (2, 2, 2, cfg.Hkv, cfg.d)
+    for s in range(2):
+        for b in range(2):
+            for t in range(2):
+                j = int(ctx[b]) + 2 * s + t
+                assert torch.equal(Kn[s, b, t], K0[b, :, j]) and torch.equal(Vn[s, b, t], V0[b, :, j])
+                assert torch.all(K[b, :, j] == 0) and torch.all(V[b, :, j] == 0)
+    assert torch.equal(K[:, :, :300], K0[:, :, :300])
+    cfgp = W.CONFIGS["ragged-paged-8k-128k"].replace(B=3, steps=4, ctx=9000, ragged_min=1000, Hq=8, Hkv=2)
+    ctx = W.context_lengths(cfgp)
+    caps = ctx + cfgp.growth()
+    table, npg = W.page_table(cfgp, caps)
+    Kp, Vp = W.make_paged_kv(cfgp, table, npg, caps)
+    Kp0 = Kp.clone()
+    Kn, Vn = W.take_decode_rows(Kp, Vp, ctx, 4, table=table)
+    for b in range(3):
+        full = W.gather_paged(Kp0, table, b, int(ctx[b]) + 4)
+        after = W.gather_paged(Kp, table, b, int(ctx[b]) + 4)
+        for s in range(4):
+            assert torch.equal(Kn[s, b, 0], full[:, int(ctx[b]) + s])
+        assert torch.all(after[:, int(ctx[b]):] == 0)
+        assert torch.equal(after[:, :int(ctx[b])], full[:, :int(ctx[b])])
