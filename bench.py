@@ -1,21 +1,28 @@
 """Decode-attention throughput of the slow/fast mix on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--replicas R] [--no-cpu-baseline]
 
 Workload: one Llama-3-8B-shaped attention layer (B=8, Hq=32, Hkv=8, d=128)
 at 32K context, bf16 KV resident in HBM, 4 sinks + 256-token window + 2048
 selected keys per kv head, lambda 0.3, sentence-driven schedule (mean
 sentence 20 tokens, reuse budget 16).  A step is one decode step of the whole
-batch: every sequence takes either a slow step (dense attention with
-evidence, then the selector) or a fast step (sparse attention), as the
-schedule says.  The K timed steps are replayed from one HIP graph; inputs are
-on the device before the clock starts.
+batch: every sequence appends its new K/V row, then takes either a slow step
+(dense attention with evidence, then the selector) or a fast step (sparse
+attention), as the schedule says.
 
-Printed: one JSON line with the throughput, a roofline record for the
-dominant call (algorithmic bytes / duration from HIP events on the launch
-stream in a second, eager pass over the same steps, each call preceded by a
-1 GiB read that evicts L2 and the Infinity Cache), and the CPU oracle's
-throughput on a bounded sample of the same workload.
+Headline (cold): R independent copies of the layer (own seeded K/V and
+queries, same schedule) run each step in turn, so between two steps of one
+copy the other copies stream more than the 256 MB Infinity Cache holds; the
+K x R layer-steps are replayed from one HIP graph, value = B K R / time
+(tokens/s of one layer), median of 3 replays.  The same K steps of one copy
+alone (warm: its fast rows stay cached) are reported beside it.
+
+Per call: each call kind is timed with HIP events on the launch stream over
+a region of R back-to-back launches on the R copies (cold), after a 1 GiB
+read that evicts L2 and the Infinity Cache; the roofline record is the
+dominant call's algorithmic bytes per launch / its average launch duration.
+The CPU oracle's throughput on a bounded sample of the same workload is
+reported as the baseline.
 """
 from __future__ import annotations
 
@@ -69,6 +76,8 @@ def algorithmic_bytes(kind, n, cfg, k=None):
     if kind == "fast":
         rows = min(cfg.n_sink, n) + min(cfg.window, n) + k
         return rows * Hkv * 4 * d + k * Hkv * 4 + Hq * d * 6
+    if kind == "append":                 # the step's new K and V rows: read, then written to the cache
+        return Hkv * 2 * d * 2 * 2
     if kind.startswith("slow_window"):   # w rows: K and V, K again for the evidence
         w = int(kind[len("slow_window"):])
         return n * Hkv * 6 * d + w * Hq * d * 6 + n * Hkv * 8
@@ -232,11 +241,23 @@ def measured_traffic(kind, alg_bytes_per_launch):
     return int(round(t["ratio"][kind] * alg_bytes_per_launch))
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or the platform's."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(cfg, K, V, q_host, slow, ctx, budget_s=15.0):
     """The oracle, untuned, on a bounded sample: the slow and fast steps of
     sequences 0, 1, ... in step order until about budget_s of CPU work; the
     per-kind mean time x the run's slow fraction -> tokens/s."""
-    import torch
     from oracle import sfi_oracle as O
     from dynamic_sparse_kv_amd.workload import bf16_bits
 
@@ -276,8 +297,10 @@ def cpu_baseline(cfg, K, V, q_host, slow, ctx, budget_s=15.0):
         "value": round(1.0 / per_tok, 3),
         "unit": "tokens/s",
         "cores": int(cores),
+        "cpu_model": cpu_model(),
+        "host_cpus": os.cpu_count(),
         "kind": "oracle",
-        "sample": (f"sequences 0..{seqs - 1} of the same workload in step order: {len(t_slow)} slow + "
+        "sample": (f"sequences 0..{seqs - 1} of copy 0 of the same workload in step order: {len(t_slow)} slow + "
                    f"{len(t_fast)} fast steps (NumPy fp64), mean per kind weighted by the run's slow "
                    f"fraction {frac:.4f}; {time.perf_counter() - t_start:.1f} s of CPU work"),
         "slow_step_s": round(float(np.mean(t_slow)), 4),
@@ -285,9 +308,9 @@ def cpu_baseline(cfg, K, V, q_host, slow, ctx, budget_s=15.0):
     }
 
 
-def _graph_time(fn, side, stream):
-    """Capture fn(side) into one HIP graph, replay once untimed, then time one
-    replay (seconds)."""
+def _graph_time(fn, side, stream, reps=3):
+    """Capture fn(side) into one HIP graph, replay once untimed, then time
+    `reps` replays; returns (median seconds, list of seconds, graph)."""
     import torch
     g = torch.cuda.CUDAGraph()
     side.wait_stream(stream)
@@ -297,15 +320,21 @@ def _graph_time(fn, side, stream):
     torch.cuda.synchronize()
     g.replay()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    g.replay()
-    torch.cuda.synchronize()
-    return time.perf_counter() - t0, g
+    ts = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        ts.append(time.perf_counter() - t0)
+    return float(np.median(ts)), ts, g
 
 
-class _CallTimer:
-    """HIP events around single calls on the launch stream, each call after
-    a 1 GiB read that evicts L2 and the Infinity Cache."""
+class RegionTimer:
+    """HIP events on the launch stream around a region of back-to-back
+    launches of one call kind on different data (the R copies of a layer,
+    the layers of a stack), after a 1 GiB read that evicts L2 and the
+    Infinity Cache and keeps the stream busy while the host enqueues the
+    region.  A launch's duration is the region's time / its launches."""
 
     def __init__(self, dev, stream, leg):
         import torch
@@ -315,33 +344,37 @@ class _CallTimer:
         self.leg = leg
         self.ev = []
 
-    def __call__(self, kind, fn, nbytes, flops=0.0):
+    def __call__(self, kind, fns, nbytes, flops=0.0):
+        """fns: the region's launches; nbytes / flops: per launch (mean)."""
         t = self.torch
         self.flush.sum()
         e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
         e0.record(self.stream)
-        fn()
+        for fn in fns:
+            fn()
         e1.record(self.stream)
-        _mark_call(self.leg, kind, nbytes)
-        self.ev.append((kind, e0, e1, nbytes, flops))
+        _mark_call(self.leg, kind, nbytes * len(fns))
+        self.ev.append((kind, e0, e1, len(fns), nbytes, flops))
 
     def summary(self):
         self.torch.cuda.synchronize()
         agg = {}
-        for kind, a, b, nbytes, flops in self.ev:
-            d = agg.setdefault(kind, [[], [], []])
-            d[0].append(a.elapsed_time(b) * 1e-3)
+        for kind, a, b, nl, nbytes, flops in self.ev:
+            d = agg.setdefault(kind, [[], [], [], 0])
+            d[0].append(a.elapsed_time(b) * 1e-3 / nl)
             d[1].append(nbytes)
             d[2].append(flops)
+            d[3] += nl
         out = {}
-        for kind, (ts, bs, fs) in agg.items():
+        for kind, (ts, bs, fs, nl) in agg.items():
             keep = host_stall_mask(ts)
             ts = np.asarray(ts)[keep]
             bs = np.asarray(bs)[keep]
             fs = np.asarray(fs)[keep]
             t = float(np.mean(ts))
             by = float(np.mean(bs))
-            rec = {"launches": len(ts), "host_stalls_dropped": int((~keep).sum()), "avg_us": round(t * 1e6, 2),
+            rec = {"launches": int(nl), "regions": int(len(keep)), "host_stalls_dropped": int((~keep).sum()),
+                   "avg_us": round(t * 1e6, 2), "total_ms": round(float(np.sum(ts)) * 1e3, 3),
                    "alg_bytes_per_launch": int(by), "alg_GBps": round(by / t / 1e9, 1),
                    "frac_of_hbm_peak": round(by / t / 1e9 / HBM_PEAK_GBS, 4)}
             if any(fs):
@@ -353,10 +386,22 @@ class _CallTimer:
         return out
 
 
+def _step_bytes(plan, s, cfg, kseq=None):
+    """Algorithmic bytes of step s: (slow share, fast share, selections, appends)."""
+    lens = plan.seq_len_host[s]
+    sl_b, fa_b = np.nonzero(plan.slow[s])[0], np.nonzero(~plan.slow[s])[0]
+    k = (lambda b: None) if kseq is None else (lambda b: int(kseq[s, b]))
+    sb = sum(algorithmic_bytes("slow", int(lens[b]), cfg) for b in sl_b)
+    fb = sum(algorithmic_bytes("fast", int(lens[b]), cfg, k=k(b)) for b in fa_b)
+    selb = sum(algorithmic_bytes("select", int(lens[b]), cfg, k=k(b)) for b in sl_b)
+    return sb, fb, selb, cfg.B * algorithmic_bytes("append", 0, cfg)
+
+
 def leg_stack128k(timed_steps=24, dense_steps=4):
     """32 attention layers of the Llama-3-8B shape at 128K context, B=4,
     4+256+4096, lambda 0.2, sentence schedule shared by the layers; one token
-    passes all 32 layers (independent seeded KV and queries per layer)."""
+    passes all 32 layers (independent seeded KV and queries per layer), each
+    layer appending its new K/V row first."""
     import torch
     from dynamic_sparse_kv_amd import sfi
     from dynamic_sparse_kv_amd import workload as W
@@ -369,23 +414,24 @@ def leg_stack128k(timed_steps=24, dense_steps=4):
     slow = sfi.sfi_schedule(starts, cfg.budget).astype(bool)
     plan = DecodePlan(slow, ctx, dev)
     max_len = int(ctx.max()) + steps
-    decs, qs = [], []
+    decs, qs, nks = [], [], []
     _log(f"[bench] stack32-128k: generating {cfg.layers} layers")
     for layer in range(cfg.layers):
         K, V = W.make_kv(cfg, layer=layer, device=dev, cap=max_len)
+        nks.append(W.take_decode_rows(K, V, ctx, steps))
         qs.append(W.make_queries(cfg, starts, layer=layer).to(dev))
         decs.append(SFIDecoder(K, V, cfg.Hq, max_len, n_sink=cfg.n_sink, window=cfg.window,
                                k=cfg.k, lam=cfg.lam, norm_coef=cfg.norm_coef, pos_tau=cfg.pos_tau))
     stream = torch.cuda.current_stream()
     side = torch.cuda.Stream()
     for layer in range(cfg.layers):      # step 0: every sequence slow (first selection)
-        decs[layer].step(plan, 0, qs[layer], stream)
+        decs[layer].step(plan, 0, qs[layer], stream, new_kv=nks[layer])
     torch.cuda.synchronize()
 
     def run(st):
         for s in range(1, steps):
             for layer in range(cfg.layers):
-                decs[layer].step(plan, s, qs[layer], st)
+                decs[layer].step(plan, s, qs[layer], st, new_kv=nks[layer])
 
     def run_pipe(st):
         # each layer's selection runs inside the next layer's grids (the last
@@ -393,87 +439,93 @@ def leg_stack128k(timed_steps=24, dense_steps=4):
         pend = None
         for s in range(1, steps):
             for layer in range(cfg.layers):
-                pend = decs[layer].layer_step(plan, s, qs[layer], pending=pend, stream=st)
+                pend = decs[layer].layer_step(plan, s, qs[layer], pending=pend, stream=st, new_kv=nks[layer])
         sfi.sfi_run_deferred(pend, st)
 
     _log("[bench] stack32-128k: timing graph replay (selections pipelined across layers)")
-    t_total, g = _graph_time(run_pipe, side, stream)
+    t_total, ts_pipe, g = _graph_time(run_pipe, side, stream)
     del g
     value = cfg.B * timed_steps / t_total
     _log("[bench] stack32-128k: timing graph replay (selection after each layer)")
-    t_layer, g = _graph_time(run, side, stream)
+    t_layer, _, g = _graph_time(run, side, stream)
     del g
 
-    timer = _CallTimer(dev, stream, "stack32-128k")
+    timer = RegionTimer(dev, stream, "stack32-128k")
+    L = range(cfg.layers)
     for s in range(1, steps):
         ns, nf = int(plan.n_slow[s]), int(plan.n_fast[s])
-        lens = plan.seq_len_host[s]
-        sb = sum(algorithmic_bytes("slow", int(lens[b]), cfg) for b in np.nonzero(plan.slow[s])[0])
-        fb = sum(algorithmic_bytes("fast", int(lens[b]), cfg) for b in np.nonzero(~plan.slow[s])[0])
-        selb = sum(algorithmic_bytes("select", int(lens[b]), cfg) for b in np.nonzero(plan.slow[s])[0])
-        for layer in (0, cfg.layers // 2):
-            d, q = decs[layer], qs[layer][s]
-            if ns and nf:
-                timer("step", lambda: d.co_step(q, plan.seq_len[s], plan.slow_ids[s], ns, plan.fast_ids[s],
-                                                nf, stream, select=False), sb + fb)
-            elif ns:
-                timer("slow", lambda: d.slow(q, plan.seq_len[s], plan.slow_ids[s], ns, stream,
-                                             select=False), sb)
-            elif nf:
-                timer("fast", lambda: d.fast(q, plan.seq_len[s], plan.fast_ids[s], nf, stream), fb)
-            if ns:
-                timer("select", lambda: d.slow_select_only(plan.seq_len[s], plan.slow_ids[s], ns, stream),
-                      selb)
-    all_ids = torch.arange(cfg.B, dtype=torch.int32, device=dev)
+        sids, fids = plan.slow_list(s), plan.fast_list(s)
+        sb, fb, selb, ab = _step_bytes(plan, s, cfg)
+        sl = plan.seq_len[s]
+        timer("append", [lambda d=decs[l], nk=nks[l]: d.append(nk[0][s], nk[1][s], sl, None, cfg.B, stream)
+                         for l in L], ab)
+        if ns and nf:
+            timer("step", [lambda d=decs[l], q=qs[l][s]: d.co_step(q, sl, sids, ns, fids, nf, stream, select=False)
+                           for l in L], sb + fb)
+        elif ns:
+            timer("slow", [lambda d=decs[l], q=qs[l][s]: d.slow(q, sl, sids, ns, stream, select=False)
+                           for l in L], sb)
+        elif nf:
+            timer("fast", [lambda d=decs[l], q=qs[l][s]: d.fast(q, sl, fids, nf, stream) for l in L], fb)
+        if ns:
+            timer("select", [lambda d=decs[l]: d.slow_select_only(sl, sids, ns, stream) for l in L], selb)
     for s in range(1, 1 + dense_steps):
-        lens = plan.seq_len_host[s]
-        db = sum(algorithmic_bytes("dense", int(lens[b]), cfg) for b in range(cfg.B))
-        timer("dense", lambda: decs[0].dense(qs[0][s], plan.seq_len[s], all_ids, cfg.B, stream), db)
+        sb, fb, selb, ab = _step_bytes(plan, s, cfg)
+        db = sum(algorithmic_bytes("dense", int(n), cfg) for n in plan.seq_len_host[s])
+        timer("dense", [lambda d=decs[l], q=qs[l][s]: d.dense(q, plan.seq_len[s], None, cfg.B, stream)
+                        for l in L], db)
     per_call = timer.summary()
 
     def run_dense(st):
         for s in range(1, 1 + dense_steps):
             for layer in range(cfg.layers):
-                decs[layer].dense(qs[layer][s], plan.seq_len[s], all_ids, cfg.B, st)
+                decs[layer].dense(qs[layer][s], plan.seq_len[s], None, cfg.B, st)
 
     _log("[bench] stack32-128k: dense comparator")
-    t_dense, g = _graph_time(run_dense, side, stream)
+    t_dense, _, g = _graph_time(run_dense, side, stream)
     del g
     dense_tps = cfg.B * dense_steps / t_dense
     res = {"workload": f"{cfg.name}: {cfg.layers} layers, B={cfg.B} Hq={cfg.Hq} Hkv={cfg.Hkv} d={cfg.d}, "
                        f"ctx {cfg.ctx}, fast state {cfg.n_sink}+{cfg.window}+{cfg.k}, lambda {cfg.lam}, "
-                       f"{timed_steps} decode steps after a first all-slow step",
+                       f"{timed_steps} decode steps after a first all-slow step, each layer appending its row",
            "tokens_per_s": round(value, 1), "ms_per_step": round(t_total / timed_steps * 1e3, 4),
+           "replays_s": [round(x, 6) for x in ts_pipe],
            "tokens_per_s_selection_per_layer": round(cfg.B * timed_steps / t_layer, 1),
            "slow_fraction": round(float(plan.slow[1:].mean()), 4),
-           "timing": "hip graph replay, one stream; tokens_per_s with each layer's selection run inside "
-                     "the next layer's grids (sfi_decode_layer_step), tokens_per_s_selection_per_layer "
-                     "with it after each layer (sfi_decode_step_select); per_call: eager, cold, layers 0 "
-                     "and 16",
+           "timing": "hip graph replay, one stream, median of 3; tokens_per_s with each layer's selection run "
+                     "inside the next layer's grids (sfi_decode_layer_step), tokens_per_s_selection_per_layer "
+                     "with it after each layer (sfi_decode_step_select); per_call: regions of the 32 layers' "
+                     "launches (cold), hip events",
            "per_call": per_call, "dense_tokens_per_s": round(dense_tps, 2),
            "speedup_vs_dense": round(value / dense_tps, 2)}
-    del decs, qs
+    del decs, qs, nks
     torch.cuda.empty_cache()
     return res
 
 
 def leg_vegas64k(iters=12):
     """Verification-guided selection at 64K context, B=16, T=8 verify rows:
-    per iteration verify (all T rows, logits aggregated in-kernel), top-2048
-    of the aggregate per sequence, 7 sparse draft steps; ALL rows and
-    Collect-2-Query (first and last row) aggregates."""
+    per iteration the T verified rows are appended, verify (all T rows,
+    logits aggregated in-kernel), top-2048 of the aggregate per sequence, 7
+    sparse draft steps (each appending its row); ALL rows and Collect-2-Query
+    (first and last row) aggregates, and the raw-logit emission mode."""
     import torch
     from dynamic_sparse_kv_amd import workload as W
     from dynamic_sparse_kv_amd.runner import VegasDecoder
     dev = "cuda"
     cfg = W.CONFIGS["vegas-64k"].replace(steps=iters)
     T = cfg.vegas_T
-    ctx = int(W.context_lengths(cfg).max())
+    ctx_a = W.context_lengths(cfg)
+    ctx = int(ctx_a.max())
     _log("[bench] vegas-64k: generating")
     K, V = W.make_kv(cfg, device=dev)
     cap = K.shape[2]
+    kn, vn = W.take_decode_rows(K, V, ctx_a, iters + 1, rows_per_step=T)   # [iters+1][B][T][Hkv][d]
+    # a draft's own row: row j - 1 of the next iteration's verified rows
+    dk = [[kn[it + 1][:, j - 1:j].contiguous() for j in range(1, T)] for it in range(iters)]
+    dv = [[vn[it + 1][:, j - 1:j].contiguous() for j in range(1, T)] for it in range(iters)]
     qpos = W.make_vegas_queries(cfg).to(dev)           # [positions][B][Hq][d]
-    vd = VegasDecoder(K, V, cfg.Hq, cap, T, n_sink=cfg.n_sink, window=cfg.window, k=cfg.k)
+    vd = VegasDecoder(K, V, cfg.Hq, cap, T, n_sink=cfg.n_sink, window=cfg.window, k=cfg.k, keep_raw=True)
     q_rows = [qpos[it * T: it * T + T].permute(1, 0, 2, 3).contiguous() for it in range(iters)]
     seq_v = [torch.full((cfg.B,), ctx + T * (it + 1), dtype=torch.int32, device=dev) for it in range(iters)]
     seq_d = [[torch.full((cfg.B,), ctx + T * (it + 1) + j, dtype=torch.int32, device=dev)
@@ -482,37 +534,41 @@ def leg_vegas64k(iters=12):
     side = torch.cuda.Stream()
     masks = {"all": (1 << T) - 1, "collect2": 1 | (1 << (T - 1))}
 
-    def iteration(it, mask, st):
-        vd.verify(q_rows[it], seq_v[it], mask, stream=st)
+    def iteration(it, mask, st, raw=False):
+        vd.append(kn[it], vn[it], seq_v[it], stream=st)
+        vd.verify(q_rows[it], seq_v[it], mask, stream=st, raw=raw)
         vd.select(seq_v[it], stream=st)
         for j in range(1, T):
+            vd.append(dk[it][j - 1], dv[it][j - 1], seq_d[it][j - 1], stream=st)
             vd.draft(qpos[it * T + T + j - 1], seq_d[it][j - 1], stream=st)
 
     res = {"workload": f"{cfg.name}: B={cfg.B} Hq={cfg.Hq} Hkv={cfg.Hkv} d={cfg.d}, ctx {ctx}, "
                        f"T={T} verify rows, top-{cfg.k} of the aggregated logits + {cfg.n_sink} sinks + "
-                       f"{cfg.window} window, {T - 1} drafts per iteration, {iters} iterations",
+                       f"{cfg.window} window, {T - 1} drafts per iteration, {iters} iterations; rows appended",
            "tokens_per_iteration": f"{T} per sequence (all drafts accepted)"}
     for name, mask in masks.items():
         iteration(0, mask, stream)
         torch.cuda.synchronize()
-        t_total, g = _graph_time(lambda st: [iteration(it, mask, st) for it in range(iters)], side, stream)
+        t_total, _, g = _graph_time(lambda st: [iteration(it, mask, st) for it in range(iters)], side, stream)
         del g
         res[f"tokens_per_s_{name}"] = round(cfg.B * T * iters / t_total, 1)
         res[f"ms_per_iteration_{name}"] = round(t_total / iters * 1e3, 4)
-    timer = _CallTimer(dev, stream, "vegas-64k")
+    timer = RegionTimer(dev, stream, "vegas-64k")
     d, Hq, Hkv = cfg.d, cfg.Hq, cfg.Hkv
     for it in range(min(iters, 4)):
         n = ctx + T * (it + 1)
         vbytes = cfg.B * (n * Hkv * 4 * d + (n - T) * 4 + T * Hq * d * 6)
         vflops = cfg.B * 4.0 * d * T * Hq * n
         for name, mask in masks.items():
-            timer(f"verify_{name}", lambda: vd.verify(q_rows[it], seq_v[it], mask, stream=stream),
-                  vbytes, vflops)
-        timer("select", lambda: vd.select(seq_v[it], stream=stream), cfg.B * ((n - T) * 4 + cfg.k * 4))
+            timer(f"verify_{name}", [lambda: vd.verify(q_rows[it], seq_v[it], mask, stream=stream)], vbytes, vflops)
+            # raw-logit emission: the collected rows' pre-softmax logits written out
+            nrow = bin(mask).count("1")
+            timer(f"verify_raw_{name}", [lambda: vd.verify(q_rows[it], seq_v[it], mask, stream=stream, raw=True)],
+                  vbytes + cfg.B * nrow * Hq * (n - T) * 4, vflops)
+        timer("select", [lambda: vd.select(seq_v[it], stream=stream)], cfg.B * ((n - T) * 4 + cfg.k * 4))
         for j in (1, T - 1):
-            nd = n + j
             rows = cfg.n_sink + cfg.window + cfg.k
-            timer("draft", lambda: vd.draft(qpos[it * T + T + j - 1], seq_d[it][j - 1], stream=stream),
+            timer("draft", [lambda: vd.draft(qpos[it * T + T + j - 1], seq_d[it][j - 1], stream=stream)],
                   cfg.B * (rows * Hkv * 4 * d + cfg.k * 4 + Hq * d * 6))
     res["per_call"] = timer.summary()
     del vd, K, V, qpos, q_rows
@@ -524,8 +580,10 @@ def leg_ragged_paged(timed_steps=32, dense_steps=4):
     """Ragged long-reasoning batch: B=32 sequences, contexts log-uniform in
     [8K, 128K], paged bf16 KV in 16-token pages (shuffled pool), Hq=40
     Hkv=8 d=128, 4+256+min(4096, n/16) keys, lambda 0.3, each sequence
-    slow with probability 1/20 per step (step 0 slow).  Slow and fast shares
-    of a step run in one co-launched grid."""
+    slow with probability 1/20 per step (step 0 slow), each step appending
+    its rows.  Graph: slow and fast shares of a step co-launched in one grid
+    on one stream.  Two streams: slow steps and selector on one stream, fast
+    steps on another, co-running (eager, hip events around the run)."""
     import torch
     from dynamic_sparse_kv_amd import sfi
     from dynamic_sparse_kv_amd import workload as W
@@ -538,6 +596,7 @@ def leg_ragged_paged(timed_steps=32, dense_steps=4):
     table, npages = W.page_table(cfg, caps)
     _log(f"[bench] ragged-paged: generating {npages} pages")
     Kp, Vp = W.make_paged_kv(cfg, table, npages, caps, device=dev)
+    nk = W.take_decode_rows(Kp, Vp, ctx, steps, table=table)
     tab = torch.from_numpy(table).to(dev)
     starts = W.sentence_starts(cfg)
     slow = sfi.sfi_schedule(starts, -1).astype(bool)
@@ -549,64 +608,82 @@ def leg_ragged_paged(timed_steps=32, dense_steps=4):
                      page_size=cfg.page_size)
     stream = torch.cuda.current_stream()
     side = torch.cuda.Stream()
-    dec.step(plan, 0, q, stream)
+    dec.step(plan, 0, q, stream, new_kv=nk)
     torch.cuda.synchronize()
 
     def run(st):
         for s in range(1, steps):
-            dec.step(plan, s, q, st)
+            dec.step(plan, s, q, st, new_kv=nk)
 
     _log("[bench] ragged-paged: timing graph replay")
-    t_total, g = _graph_time(run, side, stream)
+    t_total, _, g = _graph_time(run, side, stream)
     del g
     value = cfg.B * timed_steps / t_total
+
+    # eager runs timed with hip events: two streams (slow + selector on one,
+    # fast on the other) and, for comparison, the one-stream co-launched step
+    _log("[bench] ragged-paged: two-stream eager run")
+    sb_stream = torch.cuda.Stream()
+    outs = torch.zeros((steps, cfg.B, cfg.Hq, cfg.d), dtype=torch.float32, device=dev)
+
+    def eager(fn):
+        ts = []
+        for _ in range(4):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return float(np.median(ts[1:]))          # the first run is untimed
+    t_two = eager(lambda: dec.run_two_streams(plan, q, 1, steps, stream, sb_stream, out_steps=outs, new_kv=nk))
+    t_one = eager(lambda: [dec.step(plan, s, q, stream, new_kv=nk) for s in range(1, steps)])
+
     kseq = np.minimum(cfg.k, plan.seq_len_host // cfg.k_div)
-    timer = _CallTimer(dev, stream, "ragged-paged")
+    timer = RegionTimer(dev, stream, "ragged-paged")
     for s in range(1, steps):
         ns, nf = int(plan.n_slow[s]), int(plan.n_fast[s])
-        lens = plan.seq_len_host[s]
-        sl_b, fa_b = np.nonzero(plan.slow[s])[0], np.nonzero(~plan.slow[s])[0]
-        sb = sum(algorithmic_bytes("slow", int(lens[b]), cfg) for b in sl_b)
-        fb = sum(algorithmic_bytes("fast", int(lens[b]), cfg, k=int(kseq[s, b])) for b in fa_b)
-        selb = sum(algorithmic_bytes("select", int(lens[b]), cfg, k=int(kseq[s, b])) for b in sl_b)
+        sids, fids = plan.slow_list(s), plan.fast_list(s)
+        sb, fb, selb, ab = _step_bytes(plan, s, cfg, kseq)
         ks = plan.k_seq[s]
+        sl = plan.seq_len[s]
         if ns and nf:
-            timer("step", lambda: dec.co_step(q[s], plan.seq_len[s], plan.slow_ids[s], ns, plan.fast_ids[s],
-                                              nf, stream, select=False), sb + fb)
+            timer("step", [lambda: dec.co_step(q[s], sl, sids, ns, fids, nf, stream, select=False)], sb + fb)
         elif ns:
-            timer("slow", lambda: dec.slow(q[s], plan.seq_len[s], plan.slow_ids[s], ns, stream,
-                                           select=False), sb)
+            timer("slow", [lambda: dec.slow(q[s], sl, sids, ns, stream, select=False)], sb)
         elif nf:
-            timer("fast", lambda: dec.fast(q[s], plan.seq_len[s], plan.fast_ids[s], nf, stream), fb)
+            timer("fast", [lambda: dec.fast(q[s], sl, fids, nf, stream)], fb)
         if ns:
-            timer("select", lambda: dec.slow_select_only(plan.seq_len[s], plan.slow_ids[s], ns, stream,
-                                                         k_seq=ks), selb)
-    all_ids = torch.arange(cfg.B, dtype=torch.int32, device=dev)
+            timer("select", [lambda: dec.slow_select_only(sl, sids, ns, stream, k_seq=ks)], selb)
     for s in range(1, 1 + dense_steps):
-        lens = plan.seq_len_host[s]
-        db = sum(algorithmic_bytes("dense", int(lens[b]), cfg) for b in range(cfg.B))
-        timer("dense", lambda: dec.dense(q[s], plan.seq_len[s], all_ids, cfg.B, stream), db)
+        db = sum(algorithmic_bytes("dense", int(n), cfg) for n in plan.seq_len_host[s])
+        timer("dense", [lambda: dec.dense(q[s], plan.seq_len[s], None, cfg.B, stream)], db)
     per_call = timer.summary()
 
     def run_dense(st):
         for s in range(1, 1 + dense_steps):
-            dec.dense(q[s], plan.seq_len[s], all_ids, cfg.B, st)
+            dec.dense(q[s], plan.seq_len[s], None, cfg.B, st)
 
-    t_dense, g = _graph_time(run_dense, side, stream)
+    t_dense, _, g = _graph_time(run_dense, side, stream)
     del g
     dense_tps = cfg.B * dense_steps / t_dense
     res = {"workload": f"{cfg.name}: B={cfg.B} Hq={cfg.Hq} Hkv={cfg.Hkv} d={cfg.d}, ctx log-uniform in "
                        f"[{cfg.ragged_min}, {cfg.ctx}] (mean {int(ctx.mean())}), paged {cfg.page_size}-token "
                        f"pages ({npages} in a shuffled pool), fast state {cfg.n_sink}+{cfg.window}+"
                        f"min({cfg.k}, n/{cfg.k_div}), lambda {cfg.lam}, slow probability {cfg.slow_prob:.3f}, "
-                       f"{timed_steps} steps after a first all-slow step",
+                       f"{timed_steps} steps after a first all-slow step, rows appended",
            "tokens_per_s": round(value, 1), "ms_per_step": round(t_total / timed_steps * 1e3, 4),
+           "tokens_per_s_two_streams": round(cfg.B * timed_steps / t_two, 1),
+           "tokens_per_s_one_stream_eager": round(cfg.B * timed_steps / t_one, 1),
            "slow_fraction": round(float(plan.slow[1:].mean()), 4),
-           "timing": "hip graph replay, one stream (slow and fast shares co-launched in one grid); "
-                     "per_call: eager, cold",
+           "timing": "tokens_per_s: hip graph replay, one stream (slow and fast shares co-launched in one grid), "
+                     "median of 3; tokens_per_s_two_streams: eager, slow steps + selector on one stream and "
+                     "fast steps on another, hip events around the run, median of 3; "
+                     "tokens_per_s_one_stream_eager: the graph's calls issued eagerly; per_call: eager, cold",
            "per_call": per_call, "dense_tokens_per_s": round(dense_tps, 1),
            "speedup_vs_dense": round(value / dense_tps, 2)}
-    del dec, Kp, Vp, q
+    del dec, Kp, Vp, q, nk
     torch.cuda.empty_cache()
     return res
 
@@ -614,8 +691,10 @@ def leg_ragged_paged(timed_steps=32, dense_steps=4):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--replicas", type=int, default=8,
+                    help="independent copies of the layer stepped in turn (cold headline)")
     ap.add_argument("--config", default="llama3-8b-layer-32k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--legs", default="stack32-128k,vegas-64k,ragged-paged",
@@ -661,89 +740,76 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     cfg = W.CONFIGS[args.config]
-    K_steps, W_steps = args.steps, args.warmup
+    K_steps, W_steps, R = args.steps, args.warmup, max(1, args.replicas)
     plan_steps = max(K_steps, W_steps, 1)
     cfg = cfg.replace(steps=plan_steps)
 
-    _log(f"[bench] generating {cfg.name} inputs")
-    K, V = W.make_kv(cfg, device=dev)
+    _log(f"[bench] generating {cfg.name} inputs, {R} copies of the layer")
     ctx = W.context_lengths(cfg)
     starts = W.sentence_starts(cfg)
     slow = sfi.sfi_schedule(starts, cfg.budget).astype(bool)
-    q_host = W.make_queries(cfg, starts)
-    q = q_host.to(dev)
     plan = DecodePlan(slow, ctx, dev)
     max_len = int(ctx.max()) + plan_steps
-    dec = SFIDecoder(K, V, cfg.Hq, max_len, n_sink=cfg.n_sink, window=cfg.window, k=cfg.k,
-                     lam=cfg.lam, norm_coef=cfg.norm_coef, pos_tau=cfg.pos_tau)
+    reps = []
+    for r in range(R):
+        K, V = W.make_kv(cfg, layer=r, device=dev)
+        nk = W.take_decode_rows(K, V, ctx, plan_steps)
+        q_host = W.make_queries(cfg, starts, layer=r)
+        dec = SFIDecoder(K, V, cfg.Hq, max_len, n_sink=cfg.n_sink, window=cfg.window, k=cfg.k,
+                         lam=cfg.lam, norm_coef=cfg.norm_coef, pos_tau=cfg.pos_tau)
+        reps.append({"K": K, "V": V, "nk": nk, "q_host": q_host, "q": q_host.to(dev), "dec": dec})
     stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
     torch.cuda.synchronize()
 
-    def run_steps(n_steps):
-        for s in range(n_steps):
-            dec.step(plan, s, q, stream)
+    def run_steps(st, s0, s1, copies):
+        for s in range(s0, s1):
+            for rp in copies:
+                rp["dec"].step(plan, s, rp["q"], st, new_kv=rp["nk"])
 
     _log(f"[bench] warmup {W_steps} steps")
-    run_steps(W_steps)
+    run_steps(stream, 0, W_steps, reps)
     torch.cuda.synchronize()
 
-    # ---- headline: K steps replayed from one HIP graph -------------------
+    # ---- headline: K steps x R copies replayed from one HIP graph (cold) ----
     use_graph = not args.no_graph
-    side = torch.cuda.Stream()
+    warm_tps = None
     if use_graph:
-        g = torch.cuda.CUDAGraph()
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            with torch.cuda.graph(g, stream=side):
-                for s in range(K_steps):
-                    dec.step(plan, s, q, side)
-        torch.cuda.synchronize()
-        g.replay()                      # untimed replay (first launch of the graph)
-        torch.cuda.synchronize()
-        _log("[bench] timing graph replay")
-        t0 = time.perf_counter()
-        g.replay()
-        torch.cuda.synchronize()
-        t_total = time.perf_counter() - t0
+        _log("[bench] timing graph replays (cold: copies in turn)")
+        t_total, ts_cold, g = _graph_time(lambda st: run_steps(st, 0, K_steps, reps), side, stream)
+        del g
+        _log("[bench] timing graph replays (warm: one copy)")
+        t_warm, ts_warm, g = _graph_time(lambda st: run_steps(st, 0, K_steps, reps[:1]), side, stream)
+        del g
+        warm_tps = cfg.B * K_steps / t_warm
     else:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        run_steps(K_steps)
+        run_steps(stream, 0, K_steps, reps)
         torch.cuda.synchronize()
         t_total = time.perf_counter() - t0
-    tokens = cfg.B * K_steps
-    value = tokens / t_total
+        ts_cold = [t_total]
+    value = cfg.B * K_steps * R / t_total
 
-    # ---- eager pass: HIP events around every call, each call preceded by a
-    # 1 GiB read that evicts L2 and the Infinity Cache and keeps the stream
-    # busy while the host enqueues the call and its events ----------------
+    # ---- per call: regions of R launches on the R copies (cold) -------------
     _log("[bench] per-call timing pass")
-    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-    calls = {"step": [], "slow": [], "select": [], "fast": [], "step_select": [], "slow_all": [],
-             "slow_window8": [], "step_select_refined": []}
-    bytes_by = {k_: [] for k_ in calls}
-    ev = []
-
-    def timed(kind, fn, nbytes):
-        flush.sum()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        fn()
-        e1.record(stream)
-        _mark_call("headline", kind, nbytes)
-        ev.append((kind, e0, e1, nbytes))
-
+    timer = RegionTimer(dev, stream, "headline")
+    decs = [rp["dec"] for rp in reps]
     for kind, s, nbytes in percall_list(plan.slow, ctx, cfg, K_steps):
         ns, nf = int(plan.n_slow[s]), int(plan.n_fast[s])
-        fn = {"step": lambda: dec.co_step(q[s], plan.seq_len[s], plan.slow_ids[s], ns, plan.fast_ids[s], nf,
-                                          stream, select=False),
-              "slow": lambda: dec.slow(q[s], plan.seq_len[s], plan.slow_ids[s], ns, stream, select=False),
-              "fast": lambda: dec.fast(q[s], plan.seq_len[s], plan.fast_ids[s], nf, stream),
-              "select": lambda: dec.slow_select_only(plan.seq_len[s], plan.slow_ids[s], ns, stream),
+        sl = plan.seq_len[s]
+        sids, fids = plan.slow_list(s), plan.fast_list(s)
+        mk = {"step": lambda d, q: d.co_step(q, sl, sids, ns, fids, nf, stream, select=False),
+              "slow": lambda d, q: d.slow(q, sl, sids, ns, stream, select=False),
+              "fast": lambda d, q: d.fast(q, sl, fids, nf, stream),
+              "select": lambda d, q: d.slow_select_only(sl, sids, ns, stream),
               # informational: not a roofline candidate (its selector part is latency-bound)
-              "step_select": lambda: dec.step_select(q[s], plan.seq_len[s], plan.slow_ids[s], ns,
-                                                     plan.fast_ids[s], nf, stream)}[kind]
-        timed(kind, fn, nbytes)
+              "step_select": lambda d, q: d.step_select(q, sl, sids, ns, fids, nf, stream)}[kind]
+        timer(kind, [lambda d=rp["dec"], q=rp["q"][s]: mk(d, q) for rp in reps], nbytes)
+        if kind in ("step", "slow", "fast"):
+            timer("append", [lambda rp=rp: rp["dec"].append(rp["nk"][0][s], rp["nk"][1][s], sl, None, cfg.B,
+                                                            stream) for rp in reps],
+                  cfg.B * algorithmic_bytes("append", 0, cfg))
     # The combined call again for the same slow steps, with Soft-NMS (radius
     # 4, alpha 0.5) and cross-head exclusivity (beta 0.5) on: the cost of the
     # score refinements (informational; the pages give no constants, so the
@@ -752,90 +818,72 @@ def main():
         if kind != "step_select":
             continue
         ns, nf = int(plan.n_slow[s]), int(plan.n_fast[s])
+        sl = plan.seq_len[s]
+        sids, fids = plan.slow_list(s), plan.fast_list(s)
 
-        def refined(s=s, ns=ns, nf=nf):
-            dec.params.nms_radius, dec.params.nms_alpha, dec.params.excl_beta = 4, 0.5, 0.5
+        def refined(d, q):
+            d.params.nms_radius, d.params.nms_alpha, d.params.excl_beta = 4, 0.5, 0.5
             try:
-                dec.step_select(q[s], plan.seq_len[s], plan.slow_ids[s], ns, plan.fast_ids[s], nf, stream)
+                d.step_select(q, sl, sids, ns, fids, nf, stream)
             finally:
-                dec.params.nms_radius, dec.params.nms_alpha, dec.params.excl_beta = 0, 0.0, 0.0
-        timed("step_select_refined", refined, nbytes)
-    # Observation-window slow step over the last 8 queries, next to the
-    # one-query slow step, for every sequence (informational).
+                d.params.nms_radius, d.params.nms_alpha, d.params.excl_beta = 0, 0.0, 0.0
+        timer("step_select_refined", [lambda d=rp["dec"], q=rp["q"][s]: refined(d, q) for rp in reps], nbytes)
+    # Every sequence slow at once (the full slow step and the dense
+    # comparator's call), and the observation-window slow step over the last
+    # 8 queries, for every sequence (informational).
     wq = 8
+    s_w = min(plan_steps, wq) - 1
+    sl_w = plan.seq_len[s_w]
+    lens_w = plan.seq_len_host[s_w]
+    timer("slow_all", [lambda d=rp["dec"], q=rp["q"][s_w]: d.slow(q, sl_w, None, cfg.B, stream, select=False)
+                       for rp in reps], sum(algorithmic_bytes("slow", int(n), cfg) for n in lens_w))
+    timer("dense", [lambda d=rp["dec"], q=rp["q"][s_w]: d.dense(q, sl_w, None, cfg.B, stream) for rp in reps],
+          sum(algorithmic_bytes("dense", int(n), cfg) for n in lens_w))
     if plan_steps >= wq:
-        s_w = wq - 1
-        q_win = q[s_w - wq + 1:s_w + 1].permute(1, 0, 2, 3).contiguous()
-        lens_w = ctx + s_w + 1
+        q_wins = [rp["q"][s_w - wq + 1:s_w + 1].permute(1, 0, 2, 3).contiguous() for rp in reps]
         out_w = torch.empty((cfg.B, wq, cfg.Hq, cfg.d), dtype=torch.float32, device=dev)
-        ws_wb = sfi.sfi_slow_window_workspace_bytes(dec.kv, wq)
+        ws_wb = sfi.sfi_slow_window_workspace_bytes(decs[0].kv, wq)
         ws_w = torch.empty(ws_wb, dtype=torch.uint8, device=dev)
-        dec.kv.seq_len = plan.seq_len[s_w].data_ptr()
-        sfi.sfi_slow_step_window(dec.kv, None, cfg.B, q_win, wq, out_w, dec.evidence, dec.key_norm, dec.ld,
-                                 ws_w, ws_wb, stream)    # untimed first launch of the window kernels
-        for _ in range(3):
-            timed("slow_all", lambda: dec.slow(q[s_w], plan.seq_len[s_w], None, cfg.B, stream, select=False),
-                  sum(algorithmic_bytes("slow", int(n), cfg) for n in lens_w))
-            timed("slow_window8", lambda: sfi.sfi_slow_step_window(dec.kv, None, cfg.B, q_win, wq, out_w,
-                                                                  dec.evidence, dec.key_norm, dec.ld, ws_w,
-                                                                  ws_wb, stream),
+
+        def window(d, qw):
+            d.kv.seq_len = sl_w.data_ptr()
+            sfi.sfi_slow_step_window(d.kv, None, cfg.B, qw, wq, out_w, d.evidence, d.key_norm, d.ld, ws_w, ws_wb,
+                                     stream)
+        window(decs[0], q_wins[0])    # untimed first launch of the window kernels
+        for _ in range(2):
+            timer("slow_window8", [lambda d=d, qw=qw: window(d, qw) for d, qw in zip(decs, q_wins)],
                   sum(algorithmic_bytes("slow_window8", int(n), cfg) for n in lens_w))
-    torch.cuda.synchronize()
-    del flush
-    for kind, a, b_, nbytes in ev:
-        calls[kind].append(a.elapsed_time(b_) * 1e-3)
-        bytes_by[kind].append(nbytes)
-    per_call = {}
-    for kind in calls:
-        if calls[kind]:
-            keep = host_stall_mask(calls[kind])
-            dropped = int((~keep).sum())
-            calls[kind] = list(np.asarray(calls[kind])[keep])
-            bytes_by[kind] = list(np.asarray(bytes_by[kind])[keep])
-            t = float(np.mean(calls[kind]))
-            by = float(np.mean(bytes_by[kind]))
-            per_call[kind] = {"launches": len(calls[kind]), "host_stalls_dropped": dropped,
-                              "avg_us": round(t * 1e6, 2),
-                              "total_ms": round(sum(calls[kind]) * 1e3, 3),
-                              "alg_bytes_per_launch": int(by),
-                              "alg_GBps": round(by / t / 1e9, 1)}
-    # the roofline record is for the HBM-streaming attention calls; the
-    # selector (a few MB per call, latency-bound) and the combined call are
-    # reported in per_call only
+    per_call = timer.summary()
+    # the roofline record is for the HBM-streaming attention calls of the
+    # schedule; the selector (a few MB per call, latency-bound) and the
+    # combined call are reported in per_call only
     dom = max((k_ for k_ in per_call if k_ in ("step", "slow", "fast")), key=lambda k_: per_call[k_]["total_ms"])
     dc = per_call[dom]
     achieved = dc["alg_GBps"]
     roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(dom, dc["alg_bytes_per_launch"]),
-                "kernel": {"step": "sfi_decode_step: co-launched slow + fast partial and finalize kernels",
+                "call": dom, "avg_launch_us": dc["avg_us"], "alg_bytes_per_launch": dc["alg_bytes_per_launch"],
+                "kernel": {"step": "sfi_decode_step: co-launched slow + fast partial kernel and finalize kernel",
                            "slow": "sfi_slow_step: split-K partial + finalize kernels",
                            "fast": "sfi_fast_step: gather partial + finalize kernels"}[dom]}
 
-    # ---- all-dense comparator: every sequence dense every step -----------
+    # ---- all-dense comparator: every sequence dense every step (cold) -------
     _log("[bench] dense comparator")
-    all_ids = torch.arange(cfg.B, dtype=torch.int32, device=dev)
-    n_dense = min(K_steps, 64)
+    n_dense = min(K_steps, 8)
     if use_graph:
-        gd = torch.cuda.CUDAGraph()
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            with torch.cuda.graph(gd, stream=side):
-                for s in range(n_dense):
-                    dec.dense(q[s], plan.seq_len[s], all_ids, cfg.B, side)
-        torch.cuda.synchronize()
-        gd.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        gd.replay()
-        torch.cuda.synchronize()
+        t_d, _, g = _graph_time(lambda st: [rp["dec"].dense(rp["q"][s], plan.seq_len[s], None, cfg.B, st)
+                                            for s in range(n_dense) for rp in reps], side, stream)
+        del g
     else:
+        torch.cuda.synchronize()
         t0 = time.perf_counter()
         for s in range(n_dense):
-            dec.dense(q[s], plan.seq_len[s], all_ids, cfg.B, stream)
+            for rp in reps:
+                rp["dec"].dense(rp["q"][s], plan.seq_len[s], None, cfg.B, stream)
         torch.cuda.synchronize()
-    t_dense = (time.perf_counter() - t0) / n_dense
-    dense_tps = cfg.B / t_dense
+        t_d = time.perf_counter() - t0
+    dense_tps = cfg.B * n_dense * R / t_d
 
     result = {
         "metric": METRIC,
@@ -844,7 +892,7 @@ def main():
         "n_gpus": 1,
         "steps": K_steps,
         "warmup": W_steps,
-        "ms_per_step": round(t_total / K_steps * 1e3, 4),
+        "ms_per_step": round(t_total / (K_steps * R) * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -852,22 +900,28 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: one attention layer, B={cfg.B} Hq={cfg.Hq} Hkv={cfg.Hkv} "
                                f"d={cfg.d}, ctx {cfg.ctx}, fast state {cfg.n_sink}+{cfg.window}+{cfg.k}, "
-                               f"lambda {cfg.lam}, {K_steps} decode steps",
+                               f"lambda {cfg.lam}, {K_steps} decode steps (each appends its K/V row)",
                    "global_batch": cfg.B, "seq_len": cfg.ctx, "parallelism": "none (1 GPU)",
                    "slow_fraction": round(float(plan.slow[:K_steps].mean()), 4),
-                   "timing": ("hip graph replay, one stream" if use_graph else "eager, one stream") +
+                   "copies": R,
+                   "timing": ("hip graph replay, one stream, median of 3 replays; cold: the step's "
+                              f"layer-steps of {R} independent copies of the layer run in turn, value = "
+                              "tokens/s of one layer" if use_graph else "eager, one stream") +
                              "; a step with slow sequences is one sfi_decode_step_select call"},
         "roofline": roofline,
+        "warm_tokens_per_s": None if warm_tps is None else round(warm_tps, 1),
+        "replays_s": [round(x, 6) for x in ts_cold],
         "per_call": per_call,
         "dense_tokens_per_s": round(dense_tps, 1),
         "fast_vs_dense_speedup": round(value / dense_tps, 2),
     }
     if not args.no_cpu_baseline:
         _log("[bench] cpu baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline(cfg, K, V, q_host, slow[:K_steps], ctx)
+        rp = reps[0]
+        result["cpu_baseline"] = cpu_baseline(cfg, rp["K"], rp["V"], rp["q_host"], slow[:K_steps], ctx)
     legs = [x for x in args.legs.split(",") if x and x != "none"]
     if legs:
-        del dec, K, V, q
+        del reps, decs
         torch.cuda.empty_cache()
         result["legs"] = {}
         for leg in legs:

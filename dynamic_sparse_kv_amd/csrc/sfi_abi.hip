@@ -761,9 +761,12 @@ size_t sfi_verify_workspace_bytes(const sfi_kv *kv, int32_t T) {
   return verify_ws(kv, T).total;
 }
 
-sfi_status sfi_verify_aggregate(const sfi_kv *kv, const int32_t *batch_ids, int32_t batch_n,
-                                const uint16_t *q, int32_t T, uint32_t row_mask, float *out,
-                                float *agg, int32_t ld, void *ws, size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+sfi_status verify_impl(const sfi_kv *kv, const int32_t *batch_ids, int32_t batch_n, const uint16_t *q,
+                       int32_t T, uint32_t row_mask, float *out, float *agg, int32_t ld, float *raw,
+                       int32_t raw_ld, void *ws, size_t ws_bytes, void *stream) {
   KVView view;
   bool paged = false;
   sfi_status s = check_kv(kv, &view, &paged);
@@ -778,6 +781,7 @@ sfi_status sfi_verify_aggregate(const sfi_kv *kv, const int32_t *batch_ids, int3
   if (row_mask == 0u || (row_mask & ~all) != 0u) return SFI_ERR_RANGE;
   if (kv->max_seq_len < T) return SFI_ERR_RANGE;
   if (ld < kv->max_seq_len - T) return SFI_ERR_RANGE;
+  if (raw && (raw_ld < kv->max_seq_len - T || !aligned16(raw))) return SFI_ERR_RANGE;
   const VerWs w = verify_ws(kv, T);
   if (!ws) return SFI_ERR_NULL;
   if (!aligned(ws, kAlign)) return SFI_ERR_RANGE;
@@ -804,7 +808,27 @@ sfi_status sfi_verify_aggregate(const sfi_kv *kv, const int32_t *batch_ids, int3
   a.plan.chunk = w.chunk;
   a.plan.splits = w.stride;
   a.plan.stride = w.stride;
+  a.raw = raw;
+  a.raw_ld = raw_ld;
   return launch_verify(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SFI_OK : SFI_ERR_HIP;
+}
+}  // namespace
+
+extern "C" {
+
+sfi_status sfi_verify_aggregate(const sfi_kv *kv, const int32_t *batch_ids, int32_t batch_n,
+                                const uint16_t *q, int32_t T, uint32_t row_mask, float *out,
+                                float *agg, int32_t ld, void *ws, size_t ws_bytes, void *stream) {
+  return verify_impl(kv, batch_ids, batch_n, q, T, row_mask, out, agg, ld, nullptr, 0, ws, ws_bytes, stream);
+}
+
+sfi_status sfi_verify_raw_logits(const sfi_kv *kv, const int32_t *batch_ids, int32_t batch_n,
+                                 const uint16_t *q, int32_t T, uint32_t row_mask, float *out, float *agg,
+                                 int32_t ld, float *logits, int32_t logits_ld, void *ws, size_t ws_bytes,
+                                 void *stream) {
+  if (!logits) return SFI_ERR_NULL;
+  return verify_impl(kv, batch_ids, batch_n, q, T, row_mask, out, agg, ld, logits, logits_ld, ws, ws_bytes,
+                     stream);
 }
 
 size_t sfi_slow_window_workspace_bytes(const sfi_kv *kv, int32_t w) {

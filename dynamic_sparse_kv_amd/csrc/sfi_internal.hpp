@@ -199,6 +199,9 @@ struct VerifyLaunch {
   float *rstat;
   float *evidence;
   float *key_norm;
+  // raw-logit emission (or null): [B][popcount(row_mask)][Hq][raw_ld]
+  float *raw;
+  int raw_ld;
 };
 
 hipError_t launch_verify(const VerifyLaunch &a, hipStream_t st);

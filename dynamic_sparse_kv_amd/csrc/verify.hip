@@ -54,6 +54,10 @@ struct VArgs {
   int lld;
   float qscale;       // log2(e)/sqrt(d)
   float lscale;       // 1/sqrt(d)
+  // raw-logit emission: pre-softmax logits of the collected rows,
+  // [B][nraw][Hq][raw_ld] (row index = rank of the row among row_mask's bits)
+  float *raw;
+  int raw_ld, nraw;
 };
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) {
@@ -64,7 +68,7 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) {
 // Key (within a 32-key tile) held by accumulator element r of a lane in half hs.
 __device__ __forceinline__ int acc_key(int r, int hs) { return 8 * (r >> 2) + 4 * hs + (r & 3); }
 
-template <int D, int G, bool PAGED>
+template <int D, int G, bool PAGED, bool RAW = false>
 __global__ __launch_bounds__(kVThreads) void verify_partial_kernel(VArgs a) {
   constexpr int KK = D / 16;  // k-steps of Q K^T
   constexpr int MT = D / 32;  // m-tiles of O^T
@@ -96,6 +100,15 @@ __global__ __launch_bounds__(kVThreads) void verify_partial_kernel(VArgs a) {
   const int lim = n - T + jt;  // last visible key of row jt
   const float amask = (colv && ((a.row_mask >> jt) & 1u)) ? 1.f : 0.f;
   const int prefix = n - T;    // aggregate covers keys < prefix
+  // raw-logit emission: this lane's column writes its logits when its row is
+  // collected, at row rank(jt) of the collected rows
+  float *rawp = nullptr;
+  if constexpr (RAW) {
+    if (amask != 0.f) {
+      const int rr = __popc(a.row_mask & ((1u << jt) - 1u));
+      rawp = a.raw + (((size_t)b * a.nraw + rr) * a.Hq + g * G + jh) * a.raw_ld;
+    }
+  }
 
   bf16x8_t qb[KK];
   {
@@ -155,8 +168,28 @@ __global__ __launch_bounds__(kVThreads) void verify_partial_kernel(VArgs a) {
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t.ka[kk], qb[kk], s, 0, 0, 0);
 
+    // Raw-logit emission: the lane's 16 logits of its column, 4 runs of 4
+    // consecutive keys (keys of the prefix only).
+    if constexpr (RAW) {
+      if (rawp) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int key = kb + acc_key(4 * r4, hs);
+          const float4 v = make_float4(s[4 * r4] * a.lscale, s[4 * r4 + 1] * a.lscale, s[4 * r4 + 2] * a.lscale,
+                                       s[4 * r4 + 3] * a.lscale);
+          if (key + 3 < prefix && key + 3 < k1 && (a.raw_ld & 3) == 0) {
+            *reinterpret_cast<float4 *>(rawp + key) = v;
+          } else {
+            if (key < prefix && key < k1) rawp[key] = v.x;
+            if (key + 1 < prefix && key + 1 < k1) rawp[key + 1] = v.y;
+            if (key + 2 < prefix && key + 2 < k1) rawp[key + 2] = v.z;
+            if (key + 3 < prefix && key + 3 < k1) rawp[key + 3] = v.w;
+          }
+        }
+      }
+    }
     // Aggregate: masked column sum, reduce-scattered over the 32 lanes of the half.
-    if (a.part_agg) {
+    if (!RAW && a.part_agg) {
       float v[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) v[r] = s[r] * amask;
@@ -316,6 +349,20 @@ __global__ __launch_bounds__(D) void verify_combine_kernel(VFinal a) {
   }
 }
 
+// Raw-logit mode: agg[b][i] = sum over the collected rows and all query heads
+// (fixed order) of the emitted logits, i < n - T.
+__global__ __launch_bounds__(256) void verify_raw_agg_kernel(VFinal a, const float *raw, int raw_ld, int nraw) {
+  const int b = batch_seq(a.batch_ids, blockIdx.y, a.B);
+  if (b < 0) return;
+  const int n = clamp_len(a.seq_len, b, a.max_len);
+  const int P = n - a.T;
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < P; i += gridDim.x * 256) {
+    float s = 0.f;
+    for (int r = 0; r < nraw * a.Hq; ++r) s += raw[((size_t)b * nraw * a.Hq + r) * raw_ld + i];
+    a.agg[(size_t)b * a.ld + i] = s;
+  }
+}
+
 // agg[b][i] = sum over kv heads (fixed order) of the per-head partials, i < n - T.
 __global__ __launch_bounds__(256) void verify_agg_kernel(VFinal a) {
   const int b = batch_seq(a.batch_ids, blockIdx.y, a.B);
@@ -463,9 +510,14 @@ hipError_t verify_t(const VerifyLaunch &L, hipStream_t st) {
   a.part_o = L.part_o; a.part_ml = L.part_ml; a.part_agg = L.part_agg; a.lld = L.lld;
   a.qscale = kLog2e / sqrtf((float)D);
   a.lscale = 1.0f / sqrtf((float)D);
+  a.raw = L.raw; a.raw_ld = L.raw_ld; a.nraw = __builtin_popcount(L.row_mask);
   const int wgs = (L.plan.splits + kVWaves - 1) / kVWaves;
-  hipLaunchKernelGGL((verify_partial_kernel<D, G, PAGED>), dim3(wgs, L.Hkv, L.batch_n),
-                     dim3(kVThreads), 0, st, a);
+  if (L.raw)
+    hipLaunchKernelGGL((verify_partial_kernel<D, G, PAGED, true>), dim3(wgs, L.Hkv, L.batch_n),
+                       dim3(kVThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((verify_partial_kernel<D, G, PAGED>), dim3(wgs, L.Hkv, L.batch_n),
+                       dim3(kVThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   VFinal f{};
@@ -483,7 +535,11 @@ hipError_t verify_t(const VerifyLaunch &L, hipStream_t st) {
     return hipGetLastError();
   }
   const int aggb = min(1024, (L.max_seq_len + 255) / 256);
-  hipLaunchKernelGGL(verify_agg_kernel, dim3(aggb > 0 ? aggb : 1, L.batch_n), dim3(256), 0, st, f);
+  if (L.raw)
+    hipLaunchKernelGGL(verify_raw_agg_kernel, dim3(aggb > 0 ? aggb : 1, L.batch_n), dim3(256), 0, st, f, L.raw,
+                       L.raw_ld, a.nraw);
+  else
+    hipLaunchKernelGGL(verify_agg_kernel, dim3(aggb > 0 ? aggb : 1, L.batch_n), dim3(256), 0, st, f);
   return hipGetLastError();
 }
 

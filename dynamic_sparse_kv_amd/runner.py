@@ -364,19 +364,20 @@ class SFIDecoder:
         stream_a.wait_event(end_c)
 
     def run_two_streams(self, plan: DecodePlan, q_steps, s_begin: int, s_end: int, stream_a,
-                        stream_b, out_steps=None):
+                        stream_b, out_steps=None, new_kv=None):
         """Steps [s_begin, s_end) as two overlapping chains.
 
         Stream A carries each step's slow steps and selector, stream B its fast
-        steps, so the selector of step s runs while the fast steps of step s
-        stream their rows (the asynchronous pipeline of the Slow-Fast Inference
-        pages, technical summary section 3.C).  Ordering: B(s) waits for A(s-1)
-        (a sequence refreshed at s-1 reads its new index list at s), and A(s)
-        waits for B(s-1) (the selector may only overwrite a list once the fast
-        steps that read it are done).  Both chains join back into stream_a.
-        out_steps, if given, is [steps][B][Hq][d] and receives each step's
-        output; otherwise the shared output buffer is used (still race-free:
-        the two chains never write the same slot concurrently).
+        steps, so slow and fast kernels co-run and the selector of step s runs
+        while fast steps stream their rows (the asynchronous pipeline of the
+        Slow-Fast Inference pages, technical summary section 3.C).  Ordering:
+        B(s) waits for A(s-1) (a sequence refreshed at s-1 reads its new index
+        list at s); A(s)'s selector waits for B(s-1) (it may only overwrite a
+        list once the fast steps that read it are done), and with a shared
+        output buffer (out_steps None) so does A(s)'s slow step (a sequence
+        fast at s-1 and slow at s writes the same output slot).  With new_kv
+        each chain first appends its own sequences' rows of the step.  Both
+        chains join back into stream_a.  Eager only (see _no_capture).
         """
         self._no_capture("run_two_streams")
         for st in (stream_a, stream_b):
@@ -392,16 +393,26 @@ class SFIDecoder:
             sl = plan.seq_len[s]
             out = None if out_steps is None else out_steps[s]
             ns, nf = int(plan.n_slow[s]), int(plan.n_fast[s])
-            if prev_b is not None:
-                stream_a.wait_event(prev_b)
             if ns:
-                self.slow(q, sl, plan.slow_ids[s], ns, stream_a, out=out)
+                sids = plan.slow_list(s)
+                if new_kv is not None:
+                    self.append(new_kv[0][s], new_kv[1][s], sl, sids, ns, stream_a)
+                if out_steps is None and prev_b is not None:
+                    stream_a.wait_event(prev_b)
+                self.slow(q, sl, sids, ns, stream_a, out=out, select=False)
+                if prev_b is not None:
+                    stream_a.wait_event(prev_b)
+                self.slow_select_only(sl, sids, ns, stream_a,
+                                      k_seq=None if plan.k_seq is None else plan.k_seq[s])
             ev_a = ev()
             ev_a.record(stream_a)
             if prev_a is not None:
                 stream_b.wait_event(prev_a)
             if nf:
-                self.fast(q, sl, plan.fast_ids[s], nf, stream_b, out=out)
+                fids = plan.fast_list(s)
+                if new_kv is not None:
+                    self.append(new_kv[0][s], new_kv[1][s], sl, fids, nf, stream_b)
+                self.fast(q, sl, fids, nf, stream_b, out=out)
             ev_b = ev()
             ev_b.record(stream_b)
             prev_a, prev_b = ev_a, ev_b
@@ -413,7 +424,7 @@ class VegasDecoder:
     """Verify -> select -> draft iterations over a resident KV cache."""
 
     def __init__(self, K, V, Hq: int, max_len: int, T: int, *, n_sink: int, window: int, k: int,
-                 page_table=None, page_size: int = 0):
+                 page_table=None, page_size: int = 0, keep_raw: bool = False):
         dev = K.device
         self.dev = dev
         self.Hq, self.T = Hq, T
@@ -433,6 +444,9 @@ class VegasDecoder:
         self.vout = torch.zeros((B, T, Hq, d), **f32)
         self.out = torch.zeros((B, Hq, d), **f32)
         self.agg = torch.zeros((B, self.ld), **f32)
+        # raw-logit emission: room for every row's logits; a call with R
+        # collected rows fills it as [B][R][Hq][ld] (raw_view(R))
+        self.raw_logits = torch.zeros((B, T, Hq, self.ld), **f32) if keep_raw else None
         self.sel_idx = torch.full((B, 1, k), -1, dtype=torch.int32, device=dev)
         self.sel_count = torch.zeros((B, 1), dtype=torch.int32, device=dev)
         u8 = dict(dtype=torch.uint8, device=dev)
@@ -443,12 +457,32 @@ class VegasDecoder:
         self.ws_sel = torch.zeros(self.ws_sel_bytes, **u8)
         self.ws_fast = torch.zeros(self.ws_fast_bytes, **u8)
 
-    def verify(self, q_rows, seq_len, row_mask: int, batch_ids=None, batch_n=None, stream=None):
-        """q_rows [B][T][Hq][d] bf16; seq_len counts the T verified rows."""
+    def verify(self, q_rows, seq_len, row_mask: int, batch_ids=None, batch_n=None, stream=None,
+               raw: bool = False):
+        """q_rows [B][T][Hq][d] bf16; seq_len counts the T verified rows.
+        raw: emit the collected rows' logits to self.raw_logits and sum them
+        in a second pass (sfi_verify_raw_logits) instead of aggregating in
+        the kernel."""
         self.kv.seq_len = seq_len.data_ptr() if torch.is_tensor(seq_len) else seq_len
         bn = self.B if batch_n is None else batch_n
+        if raw:
+            sfi.sfi_verify_raw_logits(self.kv, batch_ids, bn, q_rows, self.T, row_mask, self.vout, self.agg,
+                                      self.ld, self.raw_logits, self.ld, self.ws_ver, self.ws_ver_bytes, stream)
+            return
         sfi.sfi_verify_aggregate(self.kv, batch_ids, bn, q_rows, self.T, row_mask, self.vout,
                                  self.agg, self.ld, self.ws_ver, self.ws_ver_bytes, stream)
+
+    def raw_view(self, R: int):
+        """The emitted logits of a call that collected R rows, [B][R][Hq][ld]."""
+        n = self.B * R * self.Hq * self.ld
+        return self.raw_logits.view(-1)[:n].view(self.B, R, self.Hq, self.ld)
+
+    def append(self, k_new, v_new, seq_len, batch_ids=None, batch_n=None, stream=None):
+        """Write new K/V rows (k_new, v_new [B][T'][Hkv][d]) at cache rows
+        seq_len - T' .. seq_len - 1 (sfi_append_kv)."""
+        self.kv.seq_len = seq_len.data_ptr() if torch.is_tensor(seq_len) else seq_len
+        bn = self.B if batch_n is None else batch_n
+        sfi.sfi_append_kv(self.kv, batch_ids, bn, k_new, v_new, int(k_new.shape[1]), stream)
 
     def select(self, seq_len, batch_ids=None, batch_n=None, stream=None):
         ptr = seq_len.data_ptr() if torch.is_tensor(seq_len) else seq_len

@@ -91,6 +91,9 @@ def lib():
         L.sfi_fast_step.argtypes = [P(sfi_kv), _vp, _c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int,
                                     _c_int, _vp, _vp, _sz, _vp]
         L.sfi_fast_step.restype = _c_int
+        L.sfi_verify_raw_logits.argtypes = [P(sfi_kv), _vp, _c_int, _vp, _c_int, ctypes.c_uint32, _vp, _vp,
+                                            _c_int, _vp, _c_int, _vp, _sz, _vp]
+        L.sfi_verify_raw_logits.restype = _c_int
         L.sfi_append_kv.argtypes = [P(sfi_kv), _vp, _c_int, _vp, _vp, _c_int, _vp]
         L.sfi_append_kv.restype = _c_int
         L.sfi_fast_step_noalloc.argtypes = [P(sfi_kv), _vp, _c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int,
@@ -240,6 +243,13 @@ def sfi_fast_step(kv: sfi_kv, batch_ids, batch_n: int, q, sel_idx, sel_count, se
     _check(lib().sfi_fast_step(ctypes.byref(kv), _ptr(batch_ids), batch_n, _ptr(q), _ptr(sel_idx),
                                _ptr(sel_count), sel_heads, sel_k, n_sink, window, _ptr(out),
                                _ptr(ws), ws_bytes, _stream(stream)), "sfi_fast_step")
+
+
+def sfi_verify_raw_logits(kv: sfi_kv, batch_ids, batch_n: int, q, T: int, row_mask: int, out, agg, ld: int,
+                          logits, logits_ld: int, ws, ws_bytes: int, stream=None):
+    _check(lib().sfi_verify_raw_logits(ctypes.byref(kv), _ptr(batch_ids), batch_n, _ptr(q), T, row_mask,
+                                       _ptr(out), _ptr(agg), ld, _ptr(logits), logits_ld, _ptr(ws), ws_bytes,
+                                       _stream(stream)), "sfi_verify_raw_logits")
 
 
 def sfi_append_kv(kv: sfi_kv, batch_ids, batch_n: int, k_new, v_new, T: int, stream=None):

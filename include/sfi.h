@@ -390,6 +390,24 @@ sfi_status sfi_verify_aggregate(const sfi_kv *kv, const int32_t *batch_ids, int3
                                 const uint16_t *q, int32_t T, uint32_t row_mask, float *out,
                                 float *agg, int32_t ld, void *ws, size_t ws_bytes, void *stream);
 
+/* sfi_verify_aggregate with raw-logit emission, the collection that the
+ * Vegas page sets its design against [Vegas 2.B and 3: writing the
+ * pre-softmax logits of the verified queries out to memory costs bandwidth,
+ * which Collect-2-Query limits to two rows]: the verify kernel writes the
+ * collected rows' logits to HBM and a second pass sums them into agg.
+ *   logits  [B][R][Hq][logits_ld] fp32, R = popcount(row_mask): entry
+ *           (b, r, h, i) = q_{t,h} . k_i / sqrt(d) for the r-th collected row t
+ *           (ascending) and prefix keys i < n - T; entries past the prefix
+ *           are not written.  16-byte aligned; logits_ld >= max_seq_len - T.
+ *   agg     as sfi_verify_aggregate (summed over rows, then heads, in a fixed
+ *           order: equal to the in-kernel aggregate up to rounding).
+ * Other arguments, workspace and errors as sfi_verify_aggregate.  Moves
+ * R * Hq * (n - T) * 4 bytes more than it, written and read back. */
+sfi_status sfi_verify_raw_logits(const sfi_kv *kv, const int32_t *batch_ids, int32_t batch_n,
+                                 const uint16_t *q, int32_t T, uint32_t row_mask, float *out, float *agg,
+                                 int32_t ld, float *logits, int32_t logits_ld, void *ws, size_t ws_bytes,
+                                 void *stream);
+
 /* Slow/fast schedule [SFI 3.A: slow at a semantic boundary or when the reuse
  * budget is spent] -- host only.  events [steps][B] [host] marks boundaries
  * (or any other slow trigger); slow [steps][B] [host] receives 1 where the

@@ -934,6 +934,59 @@ def test_verify_matches_oracle(Hq, Hkv, d, T):
             check_selection(sel[b, 0], cnt[b, 0], a_ref, lo, hi, 256)
 
 
+@pytest.mark.parametrize("Hq,Hkv,d,T,paged", [(32, 8, 128, 8, False), (8, 2, 64, 8, True), (16, 8, 128, 4, False)])
+def test_verify_raw_logits_match_oracle(Hq, Hkv, d, T, paged):
+    """Raw-logit emission: the collected rows' pre-softmax logits against the
+    oracle's, element by element per row; their sum (a second pass) against
+    the oracle's aggregate and the in-kernel aggregate; outputs equal to the
+    aggregating call's bit for bit; nothing written past the prefix."""
+    _say(f"verify raw logits Hq={Hq} Hkv={Hkv} d={d} T={T} paged={paged}")
+    B = 2
+    lens = [2600, 905]
+    cap = 2624
+    K, V = _rand_kv(B, Hkv, cap, d, seed=Hq * 3 + T + 1)
+    q = _rand_q((B, T, Hq, d), seed=T + 200)
+    seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    if paged:
+        ps = 16
+        npg = cap // ps
+        table = np.random.default_rng(3).permutation(B * npg).astype(np.int32).reshape(B, npg)
+        tab = torch.from_numpy(table).to(DEV)
+        vd = VegasDecoder(W.to_paged(K, table, B * npg, ps), W.to_paged(V, table, B * npg, ps), Hq, cap, T,
+                          n_sink=4, window=256, k=256, page_table=tab, page_size=ps, keep_raw=True)
+    else:
+        vd = VegasDecoder(K, V, Hq, cap, T, n_sink=4, window=256, k=256, keep_raw=True)
+    Kb, Vb, qb = _bits(K), _bits(V), _bits(q)
+    for mode in ("all", "c2q"):
+        rows = O.collect_rows(T, mode)
+        mask = sum(1 << t for t in rows)
+        vd.verify(q, seq, mask)
+        torch.cuda.synchronize()
+        out_agg, agg_in = vd.vout.clone(), vd.agg.clone()
+        vd.raw_logits.fill_(7.0)
+        vd.agg.fill_(123.0)
+        vd.verify(q, seq, mask, raw=True)
+        torch.cuda.synchronize()
+        assert torch.equal(vd.vout.view(torch.int32), out_agg.view(torch.int32))
+        raw = vd.raw_view(len(rows)).cpu().numpy()
+        # nothing written past the [B][R][Hq][ld] block of this call
+        assert torch.all(vd.raw_logits.view(-1)[raw.size:] == 7.0)
+        agg = vd.agg.cpu().numpy()
+        for b in range(B):
+            n = lens[b]
+            P = n - T
+            _, a_ref = O.verify(qb[b], Kb[b], Vb[b], n, rows)
+            for r, t in enumerate(rows):
+                l_ref = O.attention_logits(qb[b, t], Kb[b], n - T + t + 1)[:, :P]
+                assert row_rel_err(raw[b, r, :, :P], l_ref) <= 1e-5, (mode, b, t)
+                assert np.all(raw[b, r, :, P:] == 7.0)                # nothing past the prefix
+            err = np.abs(agg[b, :P] - a_ref).max() / np.abs(a_ref).max()
+            assert err <= 1e-5, (mode, b, err)
+            err_in = np.abs(agg[b, :P] - agg_in.cpu().numpy()[b, :P]).max() / np.abs(a_ref).max()
+            assert err_in <= 1e-6, (mode, b, err_in)
+            assert np.all(agg[b, P:n] == 123.0)
+
+
 def test_vegas_draft_steps_with_shared_selection():
     B, Hq, Hkv, d, T = 2, 32, 8, 128, 8
     n0 = 2600
