@@ -148,7 +148,7 @@ struct WinWs {
 
 WinWs window_ws(const sfi_kv *kv, int w) {
   WinWs x{};
-  x.chunk = verify_chunk_for(kv->B, kv->Hkv, kv->max_seq_len);
+  x.chunk = verify_chunk_for(kv->B, kv->Hkv, kv->max_seq_len, kv->d, kv->Hq / kv->Hkv);
   x.stride = verify_stride_for(kv->max_seq_len, x.chunk);
   const size_t rows = (size_t)kv->B * w * kv->Hq * x.stride;
   x.o = 0;
@@ -160,7 +160,7 @@ WinWs window_ws(const sfi_kv *kv, int w) {
 
 VerWs verify_ws(const sfi_kv *kv, int T) {
   VerWs w{};
-  w.chunk = verify_chunk_for(kv->B, kv->Hkv, kv->max_seq_len);
+  w.chunk = verify_chunk_for(kv->B, kv->Hkv, kv->max_seq_len, kv->d, kv->Hq / kv->Hkv);
   w.stride = verify_stride_for(kv->max_seq_len, w.chunk);
   const size_t rows = (size_t)kv->B * T * kv->Hq * w.stride;
   w.o = 0;

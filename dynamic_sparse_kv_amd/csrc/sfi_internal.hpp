@@ -205,7 +205,9 @@ struct VerifyLaunch {
 };
 
 hipError_t launch_verify(const VerifyLaunch &a, hipStream_t st);
-int verify_chunk_for(int batch_n, int Hkv, int max_seq_len);
+// Keys per wave of the verify kernel: the workgroups of B x Hkv pairs fill
+// the device's resident slots in whole rounds.
+int verify_chunk_for(int B, int Hkv, int max_seq_len, int d, int G);
 // Partial slots per (row, sequence) of the verify kernel for keys per wave `chunk`.
 int verify_stride_for(int max_seq_len, int chunk);
 

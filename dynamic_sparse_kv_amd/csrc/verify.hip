@@ -26,6 +26,8 @@
 // Each wave owns a contiguous key range and writes its own (m, Z, O) partial;
 // a finalize kernel merges them in a fixed order and sums the per-kv-head
 // aggregates over kv heads.
+#include <algorithm>
+
 #include "sfi_internal.hpp"
 
 namespace sfi {
@@ -551,14 +553,60 @@ int verify_stride_for(int max_seq_len, int chunk) {
   return (max_seq_len + per_wg - 1) / per_wg * kVWaves;
 }
 
-int verify_chunk_for(int batch_n, int Hkv, int max_seq_len) {
-  // Keys per wave: long enough that a wave's (m, Z, O) partial (R x (d+2)
-  // floats) stays a few percent of the K/V bytes it streams.
-  (void)batch_n;
-  (void)Hkv;
-  if (max_seq_len >= 32768) return 2048;
-  if (max_seq_len >= 8192) return 1024;
-  return 256;
+namespace {
+
+// Resident workgroups of the verify kernel on this device (cached per
+// device and shape; the contiguous-cache kernel's, so paged caches get the
+// same plan and bits).
+template <int D, int G>
+int verify_slots_t() {
+  static int slots[16] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) dev = 0;
+  if (slots[dev] == 0) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, verify_partial_kernel<D, G, false>, kVThreads, 0) !=
+            hipSuccess || nb < 1)
+      nb = 1;
+    slots[dev] = nb * device_cu_count();
+  }
+  return slots[dev];
+}
+
+int verify_slots(int d, int G) {
+  switch (d * 16 + G) {
+    case 64 * 16 + 1: return verify_slots_t<64, 1>();
+    case 64 * 16 + 2: return verify_slots_t<64, 2>();
+    case 64 * 16 + 4: return verify_slots_t<64, 4>();
+    case 64 * 16 + 8: return verify_slots_t<64, 8>();
+    case 128 * 16 + 1: return verify_slots_t<128, 1>();
+    case 128 * 16 + 2: return verify_slots_t<128, 2>();
+    case 128 * 16 + 4: return verify_slots_t<128, 4>();
+    case 128 * 16 + 8: return verify_slots_t<128, 8>();
+    default: return 256;
+  }
+}
+
+}  // namespace
+
+int verify_chunk_for(int B, int Hkv, int max_seq_len, int d, int G) {
+  // Keys per wave.  The workgroups of all (sequence, kv head) pairs should
+  // fill the resident slots in whole rounds: a plan that leaves a short last
+  // round (say 2.25 rounds) runs its tail on a fraction of the chip.  So a
+  // pair gets slots / pairs workgroups (at least one), and the chunk spreads
+  // max_seq_len over them -- but a wave streams at least kMinChunk keys, so
+  // its (m, Z, O) partial (R x (d+2) floats) stays a few percent of the K/V
+  // bytes it reads.
+  constexpr int kMinChunk = 512;
+  const long long pairs = std::max(1LL, (long long)B * Hkv);
+  const long long slots = verify_slots(d, G);
+  const long long per_pair = std::max(1LL, slots / pairs);
+  const long long keys_per_wg = (max_seq_len + per_pair - 1) / per_pair;
+  long long chunk = (keys_per_wg + kVWaves - 1) / kVWaves;
+  chunk = (chunk + 31) / 32 * 32;
+  const long long small = ((long long)max_seq_len + kVWaves * 32 - 1) / (kVWaves * 32) * 32;  // one workgroup
+  chunk = std::max(chunk, std::min<long long>(kMinChunk, small));
+  return (int)std::max(32LL, chunk);
 }
 
 hipError_t launch_verify(const VerifyLaunch &L, hipStream_t st) {
