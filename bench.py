@@ -84,16 +84,6 @@ def algorithmic_bytes(kind, n, cfg, k=None):
     raise ValueError(kind)
 
 
-def host_stall_mask(ts):
-    """Samples to keep: a call whose event interval exceeds 4x the median of
-    its kind waited for the host (the flush read ran out before the call was
-    enqueued, e.g. a profiler buffer flush or a garbage-collection pause), so
-    the GPU sat idle inside the interval.  Such samples are dropped from the
-    per-call averages and counted."""
-    ts = np.asarray(ts, dtype=np.float64)
-    return ts <= 4.0 * float(np.median(ts))
-
-
 def percall_list(slow, ctx, cfg, steps):
     """The eager per-call pass of the headline workload, in launch order:
     (kind, step, algorithmic bytes).  A step with both slow and fast
@@ -113,8 +103,9 @@ def percall_list(slow, ctx, cfg, steps):
             out.append(("fast", s, fb))
         if len(sl):
             # the same step as one sfi_decode_step_select call (what the
-            # graph replays), then the selector alone
-            out.append(("step_select", s, sb + fb + selb))
+            # graph replays; a step with every sequence slow is its own
+            # kind), then the selector alone
+            out.append(("step_select" if len(fa) else "slow_select", s, sb + fb + selb))
             out.append(("select", s, selb))
     return out
 
@@ -329,12 +320,24 @@ def _graph_time(fn, side, stream, reps=3):
     return float(np.median(ts)), ts, g
 
 
+def host_stall_mask(ts):
+    """Samples to keep: a region whose time exceeds 4x the median of its kind
+    (every region of a kind has the same composition) waited for the host
+    (the flush read ran out before the region was enqueued, e.g. a
+    garbage-collection pause), so the GPU sat idle inside it.  Such samples
+    are dropped from the per-call averages and counted."""
+    ts = np.asarray(ts, dtype=np.float64)
+    return ts <= 4.0 * float(np.median(ts))
+
+
 class RegionTimer:
     """HIP events on the launch stream around a region of back-to-back
     launches of one call kind on different data (the R copies of a layer,
     the layers of a stack), after a 1 GiB read that evicts L2 and the
     Infinity Cache and keeps the stream busy while the host enqueues the
-    region.  A launch's duration is the region's time / its launches."""
+    region.  A launch's duration is the region's time / its launches.  (A
+    region replayed from a HIP graph instead measured a few microseconds
+    more per replay: the graph launch's own start-up.)"""
 
     def __init__(self, dev, stream, leg):
         import torch
@@ -345,13 +348,14 @@ class RegionTimer:
         self.ev = []
 
     def __call__(self, kind, fns, nbytes, flops=0.0):
-        """fns: the region's launches; nbytes / flops: per launch (mean)."""
+        """fns: the region's launches, each called with the stream to issue
+        on; nbytes / flops: per launch (mean)."""
         t = self.torch
         self.flush.sum()
         e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
         e0.record(self.stream)
         for fn in fns:
-            fn()
+            fn(self.stream)
         e1.record(self.stream)
         _mark_call(self.leg, kind, nbytes * len(fns))
         self.ev.append((kind, e0, e1, len(fns), nbytes, flops))
@@ -360,21 +364,22 @@ class RegionTimer:
         self.torch.cuda.synchronize()
         agg = {}
         for kind, a, b, nl, nbytes, flops in self.ev:
-            d = agg.setdefault(kind, [[], [], [], 0])
+            d = agg.setdefault(kind, [[], [], [], []])
             d[0].append(a.elapsed_time(b) * 1e-3 / nl)
             d[1].append(nbytes)
             d[2].append(flops)
-            d[3] += nl
+            d[3].append(nl)
         out = {}
-        for kind, (ts, bs, fs, nl) in agg.items():
+        for kind, (ts, bs, fs, nls) in agg.items():
             keep = host_stall_mask(ts)
             ts = np.asarray(ts)[keep]
             bs = np.asarray(bs)[keep]
             fs = np.asarray(fs)[keep]
             t = float(np.mean(ts))
             by = float(np.mean(bs))
-            rec = {"launches": int(nl), "regions": int(len(keep)), "host_stalls_dropped": int((~keep).sum()),
-                   "avg_us": round(t * 1e6, 2), "total_ms": round(float(np.sum(ts)) * 1e3, 3),
+            rec = {"launches": int(np.asarray(nls)[keep].sum()), "regions": int(keep.sum()),
+                   "host_stalls_dropped": int((~keep).sum()), "avg_us": round(t * 1e6, 2),
+                   "total_ms": round(float(np.sum(ts * np.asarray(nls)[keep])) * 1e3, 3),
                    "alg_bytes_per_launch": int(by), "alg_GBps": round(by / t / 1e9, 1),
                    "frac_of_hbm_peak": round(by / t / 1e9 / HBM_PEAK_GBS, 4)}
             if any(fs):
@@ -457,22 +462,22 @@ def leg_stack128k(timed_steps=24, dense_steps=4):
         sids, fids = plan.slow_list(s), plan.fast_list(s)
         sb, fb, selb, ab = _step_bytes(plan, s, cfg)
         sl = plan.seq_len[s]
-        timer("append", [lambda d=decs[l], nk=nks[l]: d.append(nk[0][s], nk[1][s], sl, None, cfg.B, stream)
+        timer("append", [lambda st, d=decs[l], nk=nks[l]: d.append(nk[0][s], nk[1][s], sl, None, cfg.B, st)
                          for l in L], ab)
         if ns and nf:
-            timer("step", [lambda d=decs[l], q=qs[l][s]: d.co_step(q, sl, sids, ns, fids, nf, stream, select=False)
+            timer("step", [lambda st, d=decs[l], q=qs[l][s]: d.co_step(q, sl, sids, ns, fids, nf, st, select=False)
                            for l in L], sb + fb)
         elif ns:
-            timer("slow", [lambda d=decs[l], q=qs[l][s]: d.slow(q, sl, sids, ns, stream, select=False)
+            timer("slow", [lambda st, d=decs[l], q=qs[l][s]: d.slow(q, sl, sids, ns, st, select=False)
                            for l in L], sb)
         elif nf:
-            timer("fast", [lambda d=decs[l], q=qs[l][s]: d.fast(q, sl, fids, nf, stream) for l in L], fb)
+            timer("fast", [lambda st, d=decs[l], q=qs[l][s]: d.fast(q, sl, fids, nf, st) for l in L], fb)
         if ns:
-            timer("select", [lambda d=decs[l]: d.slow_select_only(sl, sids, ns, stream) for l in L], selb)
+            timer("select", [lambda st, d=decs[l]: d.slow_select_only(sl, sids, ns, st) for l in L], selb)
     for s in range(1, 1 + dense_steps):
         sb, fb, selb, ab = _step_bytes(plan, s, cfg)
         db = sum(algorithmic_bytes("dense", int(n), cfg) for n in plan.seq_len_host[s])
-        timer("dense", [lambda d=decs[l], q=qs[l][s]: d.dense(q, plan.seq_len[s], None, cfg.B, stream)
+        timer("dense", [lambda st, d=decs[l], q=qs[l][s]: d.dense(q, plan.seq_len[s], None, cfg.B, st)
                         for l in L], db)
     per_call = timer.summary()
 
@@ -560,15 +565,16 @@ def leg_vegas64k(iters=12):
         vbytes = cfg.B * (n * Hkv * 4 * d + (n - T) * 4 + T * Hq * d * 6)
         vflops = cfg.B * 4.0 * d * T * Hq * n
         for name, mask in masks.items():
-            timer(f"verify_{name}", [lambda: vd.verify(q_rows[it], seq_v[it], mask, stream=stream)], vbytes, vflops)
-            # raw-logit emission: the collected rows' pre-softmax logits written out
+            timer(f"verify_{name}", [lambda st: vd.verify(q_rows[it], seq_v[it], mask, stream=st)], vbytes, vflops)
+            # raw-logit emission: the collected rows' pre-softmax logits written
+            # out and read back by the aggregation pass
             nrow = bin(mask).count("1")
-            timer(f"verify_raw_{name}", [lambda: vd.verify(q_rows[it], seq_v[it], mask, stream=stream, raw=True)],
-                  vbytes + cfg.B * nrow * Hq * (n - T) * 4, vflops)
-        timer("select", [lambda: vd.select(seq_v[it], stream=stream)], cfg.B * ((n - T) * 4 + cfg.k * 4))
+            timer(f"verify_raw_{name}", [lambda st: vd.verify(q_rows[it], seq_v[it], mask, stream=st, raw=True)],
+                  vbytes + 2 * cfg.B * nrow * Hq * (n - T) * 4, vflops)
+        timer("select", [lambda st: vd.select(seq_v[it], stream=st)], cfg.B * ((n - T) * 4 + cfg.k * 4))
         for j in (1, T - 1):
             rows = cfg.n_sink + cfg.window + cfg.k
-            timer("draft", [lambda: vd.draft(qpos[it * T + T + j - 1], seq_d[it][j - 1], stream=stream)],
+            timer("draft", [lambda st: vd.draft(qpos[it * T + T + j - 1], seq_d[it][j - 1], stream=st)],
                   cfg.B * (rows * Hkv * 4 * d + cfg.k * 4 + Hq * d * 6))
     res["per_call"] = timer.summary()
     del vd, K, V, qpos, q_rows
@@ -649,16 +655,16 @@ def leg_ragged_paged(timed_steps=32, dense_steps=4):
         ks = plan.k_seq[s]
         sl = plan.seq_len[s]
         if ns and nf:
-            timer("step", [lambda: dec.co_step(q[s], sl, sids, ns, fids, nf, stream, select=False)], sb + fb)
+            timer("step", [lambda st: dec.co_step(q[s], sl, sids, ns, fids, nf, st, select=False)], sb + fb)
         elif ns:
-            timer("slow", [lambda: dec.slow(q[s], sl, sids, ns, stream, select=False)], sb)
+            timer("slow", [lambda st: dec.slow(q[s], sl, sids, ns, st, select=False)], sb)
         elif nf:
-            timer("fast", [lambda: dec.fast(q[s], sl, fids, nf, stream)], fb)
+            timer("fast", [lambda st: dec.fast(q[s], sl, fids, nf, st)], fb)
         if ns:
-            timer("select", [lambda: dec.slow_select_only(sl, sids, ns, stream, k_seq=ks)], selb)
+            timer("select", [lambda st: dec.slow_select_only(sl, sids, ns, st, k_seq=ks)], selb)
     for s in range(1, 1 + dense_steps):
         db = sum(algorithmic_bytes("dense", int(n), cfg) for n in plan.seq_len_host[s])
-        timer("dense", [lambda: dec.dense(q[s], plan.seq_len[s], None, cfg.B, stream)], db)
+        timer("dense", [lambda st: dec.dense(q[s], plan.seq_len[s], None, cfg.B, st)], db)
     per_call = timer.summary()
 
     def run_dense(st):
@@ -799,35 +805,36 @@ def main():
         ns, nf = int(plan.n_slow[s]), int(plan.n_fast[s])
         sl = plan.seq_len[s]
         sids, fids = plan.slow_list(s), plan.fast_list(s)
-        mk = {"step": lambda d, q: d.co_step(q, sl, sids, ns, fids, nf, stream, select=False),
-              "slow": lambda d, q: d.slow(q, sl, sids, ns, stream, select=False),
-              "fast": lambda d, q: d.fast(q, sl, fids, nf, stream),
-              "select": lambda d, q: d.slow_select_only(sl, sids, ns, stream),
+        mk = {"step": lambda d, q, st: d.co_step(q, sl, sids, ns, fids, nf, st, select=False),
+              "slow": lambda d, q, st: d.slow(q, sl, sids, ns, st, select=False),
+              "fast": lambda d, q, st: d.fast(q, sl, fids, nf, st),
+              "select": lambda d, q, st: d.slow_select_only(sl, sids, ns, st),
               # informational: not a roofline candidate (its selector part is latency-bound)
-              "step_select": lambda d, q: d.step_select(q, sl, sids, ns, fids, nf, stream)}[kind]
-        timer(kind, [lambda d=rp["dec"], q=rp["q"][s]: mk(d, q) for rp in reps], nbytes)
+              "step_select": lambda d, q, st: d.step_select(q, sl, sids, ns, fids, nf, st),
+              "slow_select": lambda d, q, st: d.step_select(q, sl, sids, ns, fids, nf, st)}[kind]
+        timer(kind, [lambda st, d=rp["dec"], q=rp["q"][s]: mk(d, q, st) for rp in reps], nbytes)
         if kind in ("step", "slow", "fast"):
-            timer("append", [lambda rp=rp: rp["dec"].append(rp["nk"][0][s], rp["nk"][1][s], sl, None, cfg.B,
-                                                            stream) for rp in reps],
+            timer("append", [lambda st, rp=rp: rp["dec"].append(rp["nk"][0][s], rp["nk"][1][s], sl, None, cfg.B,
+                                                                st) for rp in reps],
                   cfg.B * algorithmic_bytes("append", 0, cfg))
     # The combined call again for the same slow steps, with Soft-NMS (radius
     # 4, alpha 0.5) and cross-head exclusivity (beta 0.5) on: the cost of the
     # score refinements (informational; the pages give no constants, so the
     # headline runs without them).  Last, since it replaces the selections.
     for kind, s, nbytes in percall_list(plan.slow, ctx, cfg, K_steps):
-        if kind != "step_select":
+        if kind != "step_select":     # the mixed steps (every sequence slow is timed above)
             continue
         ns, nf = int(plan.n_slow[s]), int(plan.n_fast[s])
         sl = plan.seq_len[s]
         sids, fids = plan.slow_list(s), plan.fast_list(s)
 
-        def refined(d, q):
+        def refined(d, q, st):
             d.params.nms_radius, d.params.nms_alpha, d.params.excl_beta = 4, 0.5, 0.5
             try:
-                d.step_select(q, sl, sids, ns, fids, nf, stream)
+                d.step_select(q, sl, sids, ns, fids, nf, st)
             finally:
                 d.params.nms_radius, d.params.nms_alpha, d.params.excl_beta = 0, 0.0, 0.0
-        timer("step_select_refined", [lambda d=rp["dec"], q=rp["q"][s]: refined(d, q) for rp in reps], nbytes)
+        timer("step_select_refined", [lambda st, d=rp["dec"], q=rp["q"][s]: refined(d, q, st) for rp in reps], nbytes)
     # Every sequence slow at once (the full slow step and the dense
     # comparator's call), and the observation-window slow step over the last
     # 8 queries, for every sequence (informational).
@@ -835,9 +842,9 @@ def main():
     s_w = min(plan_steps, wq) - 1
     sl_w = plan.seq_len[s_w]
     lens_w = plan.seq_len_host[s_w]
-    timer("slow_all", [lambda d=rp["dec"], q=rp["q"][s_w]: d.slow(q, sl_w, None, cfg.B, stream, select=False)
+    timer("slow_all", [lambda st, d=rp["dec"], q=rp["q"][s_w]: d.slow(q, sl_w, None, cfg.B, st, select=False)
                        for rp in reps], sum(algorithmic_bytes("slow", int(n), cfg) for n in lens_w))
-    timer("dense", [lambda d=rp["dec"], q=rp["q"][s_w]: d.dense(q, sl_w, None, cfg.B, stream) for rp in reps],
+    timer("dense", [lambda st, d=rp["dec"], q=rp["q"][s_w]: d.dense(q, sl_w, None, cfg.B, st) for rp in reps],
           sum(algorithmic_bytes("dense", int(n), cfg) for n in lens_w))
     if plan_steps >= wq:
         q_wins = [rp["q"][s_w - wq + 1:s_w + 1].permute(1, 0, 2, 3).contiguous() for rp in reps]
@@ -845,13 +852,13 @@ def main():
         ws_wb = sfi.sfi_slow_window_workspace_bytes(decs[0].kv, wq)
         ws_w = torch.empty(ws_wb, dtype=torch.uint8, device=dev)
 
-        def window(d, qw):
+        def window(d, qw, st):
             d.kv.seq_len = sl_w.data_ptr()
             sfi.sfi_slow_step_window(d.kv, None, cfg.B, qw, wq, out_w, d.evidence, d.key_norm, d.ld, ws_w, ws_wb,
-                                     stream)
-        window(decs[0], q_wins[0])    # untimed first launch of the window kernels
+                                     st)
+        window(decs[0], q_wins[0], stream)    # untimed first launch of the window kernels
         for _ in range(2):
-            timer("slow_window8", [lambda d=d, qw=qw: window(d, qw) for d, qw in zip(decs, q_wins)],
+            timer("slow_window8", [lambda st, d=d, qw=qw: window(d, qw, st) for d, qw in zip(decs, q_wins)],
                   sum(algorithmic_bytes("slow_window8", int(n), cfg) for n in lens_w))
     per_call = timer.summary()
     # the roofline record is for the HBM-streaming attention calls of the

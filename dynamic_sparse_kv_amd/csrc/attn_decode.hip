@@ -58,6 +58,13 @@ namespace {
 #ifndef SFI_WAVES_OF_WG
 #define SFI_WAVES_OF_WG 1
 #endif
+// Evidence mode: stage the per-key logits and norms in LDS and write them
+// out in bulk every kEvBlock keys (1), or store them row by row from the
+// main loop (0).
+#ifndef SFI_EVID_LDS
+#define SFI_EVID_LDS 1
+#endif
+
 
 enum { MODE_SLOW = 0, MODE_FAST = 1 };
 constexpr int kThreads = 256;
@@ -121,7 +128,7 @@ __device__ __forceinline__ FastList fast_list(const int32_t *sel_idx, const int3
 // One workgroup's share of a decode step: rows [split*chunk, ...) of the row
 // list of (sequence batch_ids[zb], kv head g).  A device function so that the
 // co-launch kernel below can run slow and fast shares in one grid.
-template <int D, int G, bool PAGED, int MODE, bool EVID, bool STREAM = false, bool COMPACT = false>
+template <int D, int G, bool PAGED, int MODE, bool EVID, bool COMPACT = false>
 __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, int g, int zb) {
   // 8 lanes per row halves the cross-lane reduction and softmax work per row
   // compared with 16; wide groups (G*D >= 640) use 16 to bound accumulators
@@ -152,6 +159,12 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
   __shared__ int s_pg[PAGED ? kPgSlots : 1];
   __shared__ float s_m[NW][G], s_z[NW][G];
   __shared__ float s_acc[NW][G][D];
+  // Evidence staging: the logits (G per key) and norms of one block of
+  // kEvBlock consecutive rows, written out when the block is complete.
+  constexpr bool EV_LDS = EVID && SFI_EVID_LDS;
+  constexpr int kEvBlock = 512;
+  __shared__ float s_evl[EV_LDS ? kEvBlock * G : 1];
+  __shared__ float s_evn[EV_LDS ? kEvBlock : 1];
 
   const int b = batch_seq(a.batch_ids, zb, a.B);
   if (b < 0) return;
@@ -201,8 +214,8 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
       const size_t off = (lrow * a.sel_k + i) * D;
 #pragma unroll
       for (int c = 0; c < NV; ++c) {
-        st.k[u][c] = ldg16(a.ck + off + slice(c));
-        st.v[u][c] = ldg16(a.cv + off + slice(c));
+        st.k[u][c] = ldg16_stream(a.ck + off + slice(c));
+        st.v[u][c] = ldg16_stream(a.cv + off + slice(c));
       }
     }
   };
@@ -348,17 +361,13 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
       }
 #pragma unroll
       for (int c = 0; c < NV; ++c) {
-        // the slow share of a co-launched step streams its rows once with a
-        // non-temporal hint, so it does not evict the rows that the fast
-        // share (and the next fast steps) read again; alone, a dense stream
-        // measured faster with ordinary loads
-        if constexpr (STREAM) {
-          st.k[u][c] = ldg16_stream(a.kv.k + off + slice(c));
-          st.v[u][c] = ldg16_stream(a.kv.v + off + slice(c));
-        } else {
-          st.k[u][c] = ldg16(a.kv.k + off + slice(c));
-          st.v[u][c] = ldg16(a.kv.v + off + slice(c));
-        }
+        // Rows are loaded with the non-temporal hint.  Cold, back to back,
+        // it measured faster in every mode: 8 sequences at 32K, dense 188 ->
+        // 170 us, dense with evidence 236 -> 216 us (the logits it writes
+        // and the finalize reads back are no longer pushed out by the row
+        // stream), fast 23.8 -> 22.5 us (warm too: 21.2 -> 20.8 us).
+        st.k[u][c] = ldg16_stream(a.kv.k + off + slice(c));
+        st.v[u][c] = ldg16_stream(a.kv.v + off + slice(c));
       }
     }
   };
@@ -403,12 +412,24 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
         float v = lr[u][0];
 #pragma unroll
         for (int h = 1; h < G; ++h) v = (sub % G == h) ? lr[u][h] : v;
-        a.logits[(lrow * a.lld + js) * G + sub % G] = v;
-        const float nv = sqrtf(nn);
-        a.key_norm[lrow * a.nld + js] = nv;
-        const bool acc = st.j[u] >= 0 && sub == G % LPR;
-        ns1 += acc ? (double)nv : 0.0;
-        ns2 = acc ? fma((double)nv, (double)nv, ns2) : ns2;
+        // the hardware square root (within 1 ulp; the library's sqrtf adds
+        // a ~15-instruction correctly rounded refinement per key)
+        const float nv = __builtin_amdgcn_sqrtf(nn);
+        if constexpr (EV_LDS) {
+          // row js sits in the current block (a masked row repeats the
+          // chunk's last row, which is in the chunk's last block)
+          const int r = (js - p0) & (kEvBlock - 1);
+          s_evl[r * G + sub % G] = v;
+          s_evn[r] = nv;
+        } else {
+          a.logits[(lrow * a.lld + js) * G + sub % G] = v;
+          a.key_norm[lrow * a.nld + js] = nv;
+        }
+        if (a.nsum) {  // wave-uniform: only a step that forms the prior needs the sums
+          const bool acc = st.j[u] >= 0 && sub == G % LPR;
+          ns1 += acc ? (double)nv : 0.0;
+          ns2 = acc ? fma((double)nv, (double)nv, ns2) : ns2;
+        }
       }
     }
 #pragma unroll
@@ -483,6 +504,19 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
       }
     }
   }
+  // Evidence staging: write the block of rows [blk, blk + nr) out of LDS
+  // (every thread of the workgroup takes part; barriers on both sides).
+  auto ev_flush = [&](int blk, int nr) {
+    if constexpr (EV_LDS) {
+      __syncthreads();
+      float *lg = a.logits + (lrow * a.lld + blk) * G;
+      for (int i = tid; i < nr * G; i += kThreads) lg[i] = s_evl[i];
+      float *nm = a.key_norm + lrow * a.nld + blk;
+      for (int i = tid; i < nr; i += kThreads) nm[i] = s_evn[i];
+      __syncthreads();
+    }
+  };
+  static_assert(!EV_LDS || kEvBlock % (2 * STEP) == 0, "a staging block is whole loop trips");
   if (!compact_run) {
     load_stage(sa, p0 + rg);
     for (int base = p0; base < p1; base += 2 * STEP) {
@@ -490,6 +524,14 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
       consume(sa);
       load_stage(sa, base + rg + 2 * STEP);
       consume(sb);
+      if constexpr (EV_LDS) {
+        // a block is complete, or the chunk ends inside this one
+        const int next = base + 2 * STEP;
+        if (((next - p0) & (kEvBlock - 1)) == 0 || next >= p1) {
+          const int blk = p0 + ((base - p0) & ~(kEvBlock - 1));
+          ev_flush(blk, min(next, p1) - blk);
+        }
+      }
     }
   }
 
@@ -600,7 +642,7 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(PartialArgs a) {
 // Fast step reading its selected rows from the compact copy.
 template <int D, int G, bool PAGED>
 __global__ __launch_bounds__(kThreads) void fast_compact_kernel(PartialArgs a) {
-  partial_body<D, G, PAGED, MODE_FAST, false, false, true>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+  partial_body<D, G, PAGED, MODE_FAST, false, true>(a, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // Compact copy of the selected rows: row i of (sequence, kv head) holds the
@@ -676,7 +718,7 @@ __global__ __launch_bounds__(kThreads) void copartial_kernel(PartialArgs s, Part
     }
   }
   if (id < ns) {
-    partial_body<D, G, PAGED, MODE_SLOW, true, true>(s, id % s_splits, (id / s_splits) % Hkv,
+    partial_body<D, G, PAGED, MODE_SLOW, true>(s, id % s_splits, (id / s_splits) % Hkv,
                                                      id / (s_splits * Hkv));
   } else {
     id -= ns;
