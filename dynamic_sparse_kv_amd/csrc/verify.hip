@@ -133,31 +133,40 @@ __global__ __launch_bounds__(kVThreads) void verify_partial_kernel(VArgs a) {
 
   // One 32-key tile: the K rows as the A operand of S^T = K Q^T, and the
   // (even, odd)-dim dwords of the V rows this lane needs for O^T's A operand.
+  // K and V arrive as whole 128-byte lines (8 lanes per line, 16 bytes
+  // each, the lines of 8 keys per instruction: D/16 instructions per tile
+  // and operand) and are rearranged through the wave's LDS slice: K into
+  // the MFMA layout of S^T (lane: one key, 8 consecutive dims per k-step),
+  // V into the (even, odd)-dim dwords O^T's A operand needs.  With every
+  // load covering whole lines they are loaded non-temporally, and a tile
+  // takes 16 load instructions instead of 40 (V read straight from HBM as
+  // dwords took 32).  16 sequences x 64K: 852 -> ~760 us with K through LDS;
+  // a K load straight in the MFMA layout reads 32 bytes of 32 lines per
+  // instruction, and the non-temporal hint made that 30 % slower.
+  constexpr int CPR = D / 8;  // 16-byte chunks per row
   struct Tile {
-    bf16x8_t ka[KK];
-    uint32_t vw[2][NP][8];
+    uint4 kraw[KK];
+    uint4 vraw[KK];
   };
+  __shared__ uint4 s_kt[kVWaves][32 * CPR];
+  __shared__ uint4 s_vt[kVWaves][32 * CPR];
+  uint4 *kt = s_kt[wave];
+  uint4 *vt = s_vt[wave];
+  const uint32_t *vt32 = reinterpret_cast<const uint32_t *>(vt);
   // Every lane issues its loads unconditionally: a key past the range reads
   // row k1 - 1 instead (k1 > K0, so it exists) and is masked in
   // consume().  Loads behind per-lane branches would leave the number of
   // loads in flight unknown at compile time and every later wait would have
   // to drain them all, which would collapse the two-stage pipeline below.
   auto load_tile = [&](Tile &t, int kb) {
-    {
-      const int key = min(kb + col, k1 - 1);
-      const uint16_t *kp = a.kv.k + kv_row<D, PAGED>(a.kv, b, g, key) + 8 * hs;
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) t.ka[kk] = as_bf16x8(ldg16(kp + 16 * kk));
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int key = min(kb + 16 * ks + acc_key(e, hs), k1 - 1);
-        const uint16_t *vp = a.kv.v + kv_row<D, PAGED>(a.kv, b, g, key) + 2 * col;
-#pragma unroll
-        for (int p = 0; p < NP; ++p) t.vw[ks][p][e] = *reinterpret_cast<const uint32_t *>(vp + 64 * p);
-      }
+    for (int i = 0; i < KK; ++i) {
+      const int L = i * 8 + (lane >> 3);  // line of the tile: key L % 32, line L / 32 of its row
+      const int key = min(kb + (L & 31), k1 - 1);
+      const int ch = (L >> 5) * 8 + (lane & 7);
+      const size_t row = kv_row<D, PAGED>(a.kv, b, g, key) + 8 * ch;
+      t.kraw[i] = ldg16_stream(a.kv.k + row);
+      t.vraw[i] = ldg16_stream(a.kv.v + row);
     }
   };
   // Lazy rescaling: the running reference m only moves when a logit exceeds
@@ -165,11 +174,30 @@ __global__ __launch_bounds__(kVThreads) void verify_partial_kernel(VArgs a) {
   // and the accumulators are rescaled on few tiles.
   constexpr float kSlack = 8.0f;
   auto consume = [&](const Tile &t, int kb) {
+    // K tile through LDS: row-major [32 keys][CPR chunks], chunk index
+    // XOR-swizzled by the key (spreads a k-step's 32 rows over the banks);
+    // only this wave touches its slice, and LDS operations of a wave run in
+    // order, so the wave barriers (compiler ordering only) suffice.
+    bf16x8_t ka[KK];
+#pragma unroll
+    for (int i = 0; i < KK; ++i) {
+      const int L = i * 8 + (lane >> 3);
+      const int key = L & 31, ch = (L >> 5) * 8 + (lane & 7);
+      kt[key * CPR + (ch ^ (key & (CPR - 1)))] = t.kraw[i];
+      vt[key * CPR + (ch ^ (key & (CPR - 1)))] = t.vraw[i];
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const int ch = 2 * kk + hs;
+      ka[kk] = as_bf16x8(kt[col * CPR + (ch ^ (col & (CPR - 1)))]);
+    }
+    __builtin_amdgcn_wave_barrier();
     f32x16_t s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t.ka[kk], qb[kk], s, 0, 0, 0);
+    for (int kk = 0; kk < KK; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], qb[kk], s, 0, 0, 0);
 
     // Raw-logit emission: the lane's 16 logits of its column, 4 runs of 4
     // consecutive keys (keys of the prefix only).
@@ -261,10 +289,19 @@ __global__ __launch_bounds__(kVThreads) void verify_partial_kernel(VArgs a) {
       }
 #pragma unroll
       for (int pp = 0; pp < NP; ++pp) {
+        // the (even, odd)-dim dword of dims 2 col, 2 col + 1 (+ 64 pp) of
+        // the 8 keys of k-step ks held by this lane's half, from the V tile
+        uint32_t vw[8];
+        const int dw = col + 32 * pp, chv = dw >> 2;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int key = 16 * ks + acc_key(e, hs);
+          vw[e] = vt32[(key * CPR + (chv ^ (key & (CPR - 1)))) * 4 + (dw & 3)];
+        }
         u32x4_t ev, od;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const uint32_t w0 = t.vw[ks][pp][2 * i], w1 = t.vw[ks][pp][2 * i + 1];
+          const uint32_t w0 = vw[2 * i], w1 = vw[2 * i + 1];
           ev[i] = (w0 & 0xffffu) | (w1 << 16);
           od[i] = (w0 >> 16) | (w1 & 0xffff0000u);
         }
