@@ -78,6 +78,8 @@ def algorithmic_bytes(kind, n, cfg, k=None):
         return rows * Hkv * 4 * d + k * Hkv * 4 + Hq * d * 6
     if kind == "append":                 # the step's new K and V rows: read, then written to the cache
         return Hkv * 2 * d * 2 * 2
+    if kind == "append_fused":           # the same rows written by the step call that reads them
+        return Hkv * 2 * d * 2
     if kind.startswith("slow_window"):   # w rows: K and V, K again for the evidence
         w = int(kind[len("slow_window"):])
         return n * Hkv * 6 * d + w * Hq * d * 6 + n * Hkv * 8
@@ -89,11 +91,12 @@ def percall_list(slow, ctx, cfg, steps):
     (kind, step, algorithmic bytes).  A step with both slow and fast
     sequences runs them co-launched ("step"), then the selector."""
     out = []
+    ab = algorithmic_bytes("append_fused", 0, cfg)    # each call appends its sequences' rows
     for s in range(steps):
         lens = ctx + s + 1
         sl, fa = np.nonzero(slow[s])[0], np.nonzero(~slow[s])[0]
-        sb = sum(algorithmic_bytes("slow", int(lens[b]), cfg) for b in sl)
-        fb = sum(algorithmic_bytes("fast", int(lens[b]), cfg) for b in fa)
+        sb = sum(algorithmic_bytes("slow", int(lens[b]), cfg) + ab for b in sl)
+        fb = sum(algorithmic_bytes("fast", int(lens[b]), cfg) + ab for b in fa)
         selb = sum(algorithmic_bytes("select", int(lens[b]), cfg) for b in sl)
         if len(sl) and len(fa):
             out.append(("step", s, sb + fb))
@@ -392,14 +395,16 @@ class RegionTimer:
 
 
 def _step_bytes(plan, s, cfg, kseq=None):
-    """Algorithmic bytes of step s: (slow share, fast share, selections, appends)."""
+    """Algorithmic bytes of step s: (slow share, fast share, selections); the
+    shares include the fused append of their sequences' rows."""
     lens = plan.seq_len_host[s]
     sl_b, fa_b = np.nonzero(plan.slow[s])[0], np.nonzero(~plan.slow[s])[0]
     k = (lambda b: None) if kseq is None else (lambda b: int(kseq[s, b]))
-    sb = sum(algorithmic_bytes("slow", int(lens[b]), cfg) for b in sl_b)
-    fb = sum(algorithmic_bytes("fast", int(lens[b]), cfg, k=k(b)) for b in fa_b)
+    ab = algorithmic_bytes("append_fused", 0, cfg)
+    sb = sum(algorithmic_bytes("slow", int(lens[b]), cfg) + ab for b in sl_b)
+    fb = sum(algorithmic_bytes("fast", int(lens[b]), cfg, k=k(b)) + ab for b in fa_b)
     selb = sum(algorithmic_bytes("select", int(lens[b]), cfg, k=k(b)) for b in sl_b)
-    return sb, fb, selb, cfg.B * algorithmic_bytes("append", 0, cfg)
+    return sb, fb, selb
 
 
 def leg_stack128k(timed_steps=24, dense_steps=4):
@@ -460,22 +465,23 @@ def leg_stack128k(timed_steps=24, dense_steps=4):
     for s in range(1, steps):
         ns, nf = int(plan.n_slow[s]), int(plan.n_fast[s])
         sids, fids = plan.slow_list(s), plan.fast_list(s)
-        sb, fb, selb, ab = _step_bytes(plan, s, cfg)
+        sb, fb, selb = _step_bytes(plan, s, cfg)
         sl = plan.seq_len[s]
-        timer("append", [lambda st, d=decs[l], nk=nks[l]: d.append(nk[0][s], nk[1][s], sl, None, cfg.B, st)
-                         for l in L], ab)
+        nr = [(nks[l][0][s], nks[l][1][s]) for l in L]
         if ns and nf:
-            timer("step", [lambda st, d=decs[l], q=qs[l][s]: d.co_step(q, sl, sids, ns, fids, nf, st, select=False)
+            timer("step", [lambda st, d=decs[l], q=qs[l][s], r=nr[l]: d.co_step(q, sl, sids, ns, fids, nf, st,
+                                                                                select=False, new_rows=r)
                            for l in L], sb + fb)
         elif ns:
-            timer("slow", [lambda st, d=decs[l], q=qs[l][s]: d.slow(q, sl, sids, ns, st, select=False)
+            timer("slow", [lambda st, d=decs[l], q=qs[l][s], r=nr[l]: d.slow(q, sl, sids, ns, st, select=False,
+                                                                             new_rows=r)
                            for l in L], sb)
         elif nf:
-            timer("fast", [lambda st, d=decs[l], q=qs[l][s]: d.fast(q, sl, fids, nf, st) for l in L], fb)
+            timer("fast", [lambda st, d=decs[l], q=qs[l][s], r=nr[l]: d.fast(q, sl, fids, nf, st, new_rows=r)
+                           for l in L], fb)
         if ns:
             timer("select", [lambda st, d=decs[l]: d.slow_select_only(sl, sids, ns, st) for l in L], selb)
     for s in range(1, 1 + dense_steps):
-        sb, fb, selb, ab = _step_bytes(plan, s, cfg)
         db = sum(algorithmic_bytes("dense", int(n), cfg) for n in plan.seq_len_host[s])
         timer("dense", [lambda st, d=decs[l], q=qs[l][s]: d.dense(q, plan.seq_len[s], None, cfg.B, st)
                         for l in L], db)
@@ -544,8 +550,7 @@ def leg_vegas64k(iters=12):
         vd.verify(q_rows[it], seq_v[it], mask, stream=st, raw=raw)
         vd.select(seq_v[it], stream=st)
         for j in range(1, T):
-            vd.append(dk[it][j - 1], dv[it][j - 1], seq_d[it][j - 1], stream=st)
-            vd.draft(qpos[it * T + T + j - 1], seq_d[it][j - 1], stream=st)
+            vd.draft(qpos[it * T + T + j - 1], seq_d[it][j - 1], stream=st, new_rows=(dk[it][j - 1], dv[it][j - 1]))
 
     res = {"workload": f"{cfg.name}: B={cfg.B} Hq={cfg.Hq} Hkv={cfg.Hkv} d={cfg.d}, ctx {ctx}, "
                        f"T={T} verify rows, top-{cfg.k} of the aggregated logits + {cfg.n_sink} sinks + "
@@ -574,8 +579,9 @@ def leg_vegas64k(iters=12):
         timer("select", [lambda st: vd.select(seq_v[it], stream=st)], cfg.B * ((n - T) * 4 + cfg.k * 4))
         for j in (1, T - 1):
             rows = cfg.n_sink + cfg.window + cfg.k
-            timer("draft", [lambda st: vd.draft(qpos[it * T + T + j - 1], seq_d[it][j - 1], stream=st)],
-                  cfg.B * (rows * Hkv * 4 * d + cfg.k * 4 + Hq * d * 6))
+            timer("draft", [lambda st: vd.draft(qpos[it * T + T + j - 1], seq_d[it][j - 1], stream=st,
+                                                new_rows=(dk[it][j - 1], dv[it][j - 1]))],
+                  cfg.B * (rows * Hkv * 4 * d + cfg.k * 4 + Hq * d * 6 + algorithmic_bytes("append_fused", 0, cfg)))
     res["per_call"] = timer.summary()
     del vd, K, V, qpos, q_rows
     torch.cuda.empty_cache()
@@ -651,15 +657,17 @@ def leg_ragged_paged(timed_steps=32, dense_steps=4):
     for s in range(1, steps):
         ns, nf = int(plan.n_slow[s]), int(plan.n_fast[s])
         sids, fids = plan.slow_list(s), plan.fast_list(s)
-        sb, fb, selb, ab = _step_bytes(plan, s, cfg, kseq)
+        sb, fb, selb = _step_bytes(plan, s, cfg, kseq)
         ks = plan.k_seq[s]
         sl = plan.seq_len[s]
+        nr = (nk[0][s], nk[1][s])
         if ns and nf:
-            timer("step", [lambda st: dec.co_step(q[s], sl, sids, ns, fids, nf, st, select=False)], sb + fb)
+            timer("step", [lambda st: dec.co_step(q[s], sl, sids, ns, fids, nf, st, select=False, new_rows=nr)],
+                  sb + fb)
         elif ns:
-            timer("slow", [lambda st: dec.slow(q[s], sl, sids, ns, st, select=False)], sb)
+            timer("slow", [lambda st: dec.slow(q[s], sl, sids, ns, st, select=False, new_rows=nr)], sb)
         elif nf:
-            timer("fast", [lambda st: dec.fast(q[s], sl, fids, nf, st)], fb)
+            timer("fast", [lambda st: dec.fast(q[s], sl, fids, nf, st, new_rows=nr)], fb)
         if ns:
             timer("select", [lambda st: dec.slow_select_only(sl, sids, ns, st, k_seq=ks)], selb)
     for s in range(1, 1 + dense_steps):
@@ -805,18 +813,16 @@ def main():
         ns, nf = int(plan.n_slow[s]), int(plan.n_fast[s])
         sl = plan.seq_len[s]
         sids, fids = plan.slow_list(s), plan.fast_list(s)
-        mk = {"step": lambda d, q, st: d.co_step(q, sl, sids, ns, fids, nf, st, select=False),
-              "slow": lambda d, q, st: d.slow(q, sl, sids, ns, st, select=False),
-              "fast": lambda d, q, st: d.fast(q, sl, fids, nf, st),
-              "select": lambda d, q, st: d.slow_select_only(sl, sids, ns, st),
+        # every step call appends its sequences' rows (fused append), as in the run
+        mk = {"step": lambda d, q, st, r: d.co_step(q, sl, sids, ns, fids, nf, st, select=False, new_rows=r),
+              "slow": lambda d, q, st, r: d.slow(q, sl, sids, ns, st, select=False, new_rows=r),
+              "fast": lambda d, q, st, r: d.fast(q, sl, fids, nf, st, new_rows=r),
+              "select": lambda d, q, st, r: d.slow_select_only(sl, sids, ns, st),
               # informational: not a roofline candidate (its selector part is latency-bound)
-              "step_select": lambda d, q, st: d.step_select(q, sl, sids, ns, fids, nf, st),
-              "slow_select": lambda d, q, st: d.step_select(q, sl, sids, ns, fids, nf, st)}[kind]
-        timer(kind, [lambda st, d=rp["dec"], q=rp["q"][s]: mk(d, q, st) for rp in reps], nbytes)
-        if kind in ("step", "slow", "fast"):
-            timer("append", [lambda st, rp=rp: rp["dec"].append(rp["nk"][0][s], rp["nk"][1][s], sl, None, cfg.B,
-                                                                st) for rp in reps],
-                  cfg.B * algorithmic_bytes("append", 0, cfg))
+              "step_select": lambda d, q, st, r: d.step_select(q, sl, sids, ns, fids, nf, st, new_rows=r),
+              "slow_select": lambda d, q, st, r: d.step_select(q, sl, sids, ns, fids, nf, st, new_rows=r)}[kind]
+        timer(kind, [lambda st, d=rp["dec"], q=rp["q"][s], r=(rp["nk"][0][s], rp["nk"][1][s]): mk(d, q, st, r)
+                     for rp in reps], nbytes)
     # The combined call again for the same slow steps, with Soft-NMS (radius
     # 4, alpha 0.5) and cross-head exclusivity (beta 0.5) on: the cost of the
     # score refinements (informational; the pages give no constants, so the

@@ -239,7 +239,32 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
     fl = fast_list(a.sel_idx, a.sel_count, a.sel_heads, a.sel_k, a.n_sink, a.window, b, g, n);
     L = fl.length();
   }
+  // Fused append: row n - 1 is this step's own key and value, at list
+  // position app_p (-1 when the list does not hold it: a fast list without
+  // a window).  The one workgroup whose chunk holds that position (the
+  // first split when none does) reads the row from kv.k_new / kv.v_new in
+  // the one stage that covers it, so no workgroup of this launch reads that
+  // cache row, and stores it into the cache as it ends.
+  constexpr int kAppSlices = D / 8;  // 16-byte slices per row
+  const size_t new_row = lrow * D;
+  int app_p = -1;
+  bool app_wg = false;  // uniform over the workgroup
+  if (a.kv.k_new != nullptr && n > 0) {
+    app_p = n - 1;
+    if constexpr (MODE == MODE_FAST) app_p = (fl.nw > 0) ? fl.ns + fl.nw - 1 : (n - 1 < fl.ns ? n - 1 : -1);
+    app_wg = (app_p >= 0) ? (app_p >= p0 && app_p < p0 + a.chunk) : (split == 0);
+  }
+  auto append_store = [&]() {
+    if (app_wg && tid < 2 * kAppSlices) {
+      const bool isv = tid >= kAppSlices;
+      const int c = tid % kAppSlices;
+      const uint4 x = ldg16((isv ? a.kv.v_new : a.kv.k_new) + new_row + 8 * c);
+      uint16_t *dst = const_cast<uint16_t *>(isv ? a.kv.v : a.kv.k);
+      *reinterpret_cast<uint4 *>(dst + kv_row<D, PAGED>(a.kv, b, g, n - 1) + 8 * c) = x;
+    }
+  };
   if (p0 >= L) {
+    append_store();
     // no rows here: a neutral partial (Z = 0), so the finalize can merge
     // every planned split without reading the list length
     if (tid < G) {
@@ -332,6 +357,12 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
   // in flight unknown at compile time, and every later wait would have to
   // drain all of them, collapsing the two-stage pipeline.
   auto load_stage = [&](Stage &st, int base) {
+    // Can a lane of this stage read the step's own row (fused append)?
+    // Uniform: the stage holding its list position and every later one (a
+    // masked dense row re-reads the chunk's last row, which is that row in
+    // the last chunk, and its evidence values must be the row's own).
+    const int sbase = __builtin_amdgcn_readfirstlane(base - rg);
+    const bool st_fresh = app_wg && app_p >= 0 && app_p < sbase + RPB * U;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int p = base + u * RPB;
@@ -359,6 +390,12 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
       } else {
         off = kv_row<D, false>(a.kv, b, g, jr);
       }
+      const uint16_t *kp = a.kv.k + off, *vp = a.kv.v + off;
+      if (st_fresh) {  // the step's own row comes from the new-row buffers
+        const bool f = jr == n - 1;
+        kp = f ? a.kv.k_new + new_row : kp;
+        vp = f ? a.kv.v_new + new_row : vp;
+      }
 #pragma unroll
       for (int c = 0; c < NV; ++c) {
         // Rows are loaded with the non-temporal hint.  Cold, back to back,
@@ -366,8 +403,8 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
         // 170 us, dense with evidence 236 -> 216 us (the logits it writes
         // and the finalize reads back are no longer pushed out by the row
         // stream), fast 23.8 -> 22.5 us (warm too: 21.2 -> 20.8 us).
-        st.k[u][c] = ldg16_stream(a.kv.k + off + slice(c));
-        st.v[u][c] = ldg16_stream(a.kv.v + off + slice(c));
+        st.k[u][c] = ldg16_stream(kp + slice(c));
+        st.v[u][c] = ldg16_stream(vp + slice(c));
       }
     }
   };
@@ -632,6 +669,7 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
       a.part_ml[slot * 2 + 1] = z;
     }
   }
+  append_store();
 }
 
 template <int D, int G, bool PAGED, int MODE, bool EVID>

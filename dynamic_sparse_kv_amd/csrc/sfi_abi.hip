@@ -39,8 +39,12 @@ sfi_status check_kv(const sfi_kv *kv, KVView *view, bool *paged) {
   if (kv->d != 64 && kv->d != 128) return SFI_ERR_UNSUPPORTED;
   if (!supported_group(kv->Hq / kv->Hkv)) return SFI_ERR_UNSUPPORTED;
   if (kv->max_seq_len < 1) return SFI_ERR_RANGE;
+  if ((kv->k_new == nullptr) != (kv->v_new == nullptr)) return SFI_ERR_NULL;
+  if (kv->k_new && (!aligned16(kv->k_new) || !aligned16(kv->v_new))) return SFI_ERR_RANGE;
   view->k = kv->k;
   view->v = kv->v;
+  view->k_new = kv->k_new;
+  view->v_new = kv->v_new;
   view->Hkv = kv->Hkv;
   view->page_table = kv->page_table;
   if (kv->page_table) {
@@ -682,6 +686,7 @@ sfi_status sfi_append_kv(const sfi_kv *kv, const int32_t *batch_ids, int32_t bat
   if (s != SFI_OK) return s;
   if ((s = check_batch(kv, batch_n)) != SFI_OK) return s;
   if (T < 1 || T > kv->max_seq_len) return SFI_ERR_RANGE;
+  if (view.k_new) return SFI_ERR_RANGE;  // the rows come in k_new / v_new here
   if (!k_new || !v_new) return SFI_ERR_NULL;
   if (!aligned16(k_new) || !aligned16(v_new)) return SFI_ERR_RANGE;
   if (batch_n == 0) return SFI_OK;
@@ -774,6 +779,7 @@ sfi_status verify_impl(const sfi_kv *kv, const int32_t *batch_ids, int32_t batch
   if ((s = check_batch(kv, batch_n)) != SFI_OK) return s;
   if (!q || !out || !agg) return SFI_ERR_NULL;
   if (!aligned(q, 16) || !aligned(out, 16)) return SFI_ERR_RANGE;
+  if (view.k_new) return SFI_ERR_RANGE;  // T new rows: append them with sfi_append_kv
   const int G = kv->Hq / kv->Hkv;
   if (T < 1 || G * T > 32) return SFI_ERR_UNSUPPORTED;
   if (G == 5) return SFI_ERR_UNSUPPORTED;
@@ -848,6 +854,7 @@ sfi_status sfi_slow_step_window(const sfi_kv *kv, const int32_t *batch_ids, int3
   if ((s = check_batch(kv, batch_n)) != SFI_OK) return s;
   if (!q_win || !out || !evidence) return SFI_ERR_NULL;
   if (!aligned(q_win, 16) || !aligned(out, 16)) return SFI_ERR_RANGE;
+  if (view.k_new) return SFI_ERR_RANGE;  // no fused append here
   const int G = kv->Hq / kv->Hkv;
   if (w < 1 || G * w > 32 || G == 5) return SFI_ERR_UNSUPPORTED;
   if (kv->max_seq_len < w) return SFI_ERR_RANGE;

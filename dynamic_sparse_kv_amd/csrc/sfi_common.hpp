@@ -92,6 +92,11 @@ struct KVView {
   int32_t num_pages;
   int32_t Hkv;
   int32_t cap;
+  // The step's own new row per (sequence, kv head), [B][Hkv][D], or null.
+  // Set, a decode kernel takes row seq_len - 1 from here and the workgroup
+  // that owns that row's list position stores it into the cache.
+  const uint16_t *k_new;
+  const uint16_t *v_new;
 };
 
 template <int D, bool PAGED>

@@ -135,11 +135,17 @@ class SFIDecoder:
         self.ws_stepsel = torch.zeros(self.ws_stepsel_bytes, **u8)
 
     # -- single calls -------------------------------------------------------
+    # new_rows = (k_new, v_new), each [B][Hkv][d] bf16 (or [B][1][Hkv][d]):
+    # the call also appends each listed sequence's row at cache row
+    # seq_len - 1 (the fused append of the sfi_kv description).
+    def _kvx(self, new_rows):
+        return self.kv if new_rows is None else sfi.with_new_rows(self.kv, new_rows[0], new_rows[1])
+
     def slow(self, q, seq_len, batch_ids, batch_n: int, stream=None, select: bool = True, out=None,
-             k_seq=None):
+             k_seq=None, new_rows=None):
         """Dense step + evidence for the listed sequences, then the selector."""
         self.kv.seq_len = seq_len.data_ptr() if torch.is_tensor(seq_len) else seq_len
-        sfi.sfi_slow_step(self.kv, batch_ids, batch_n, q, self.out if out is None else out,
+        sfi.sfi_slow_step(self._kvx(new_rows), batch_ids, batch_n, q, self.out if out is None else out,
                           self.evidence, self.key_norm, self.ld, self.ws_slow, self.ws_slow_bytes,
                           stream)
         if select:
@@ -163,15 +169,15 @@ class SFIDecoder:
         self.kv.seq_len = seq_len.data_ptr() if torch.is_tensor(seq_len) else seq_len
         sfi.sfi_append_kv(self.kv, batch_ids, batch_n, k_new, v_new, int(k_new.shape[1]), stream)
 
-    def dense(self, q, seq_len, batch_ids, batch_n: int, stream=None):
+    def dense(self, q, seq_len, batch_ids, batch_n: int, stream=None, new_rows=None):
         """Plain dense attention (no evidence): the full-KV comparator."""
         self.kv.seq_len = seq_len.data_ptr() if torch.is_tensor(seq_len) else seq_len
-        sfi.sfi_slow_step(self.kv, batch_ids, batch_n, q, self.out, None, None, self.ld,
+        sfi.sfi_slow_step(self._kvx(new_rows), batch_ids, batch_n, q, self.out, None, None, self.ld,
                           self.ws_slow, self.ws_slow_bytes, stream)
 
-    def fast(self, q, seq_len, batch_ids, batch_n: int, stream=None, out=None):
+    def fast(self, q, seq_len, batch_ids, batch_n: int, stream=None, out=None, new_rows=None):
         self.kv.seq_len = seq_len.data_ptr() if torch.is_tensor(seq_len) else seq_len
-        sfi.sfi_fast_step(self.kv, batch_ids, batch_n, q, self.sel_idx, self.sel_count, self.Hkv,
+        sfi.sfi_fast_step(self._kvx(new_rows), batch_ids, batch_n, q, self.sel_idx, self.sel_count, self.Hkv,
                           self.k, self.n_sink, self.window, self.out if out is None else out,
                           self.ws_fast, self.ws_fast_bytes, stream)
 
@@ -185,19 +191,19 @@ class SFIDecoder:
         sfi.sfi_compact_selected(self.kv, batch_ids, batch_n, self.sel_idx, self.sel_count, self.Hkv,
                                  self.k, self.ck, self.cv, stream)
 
-    def fast_compact(self, q, seq_len, batch_ids, batch_n: int, stream=None, out=None):
+    def fast_compact(self, q, seq_len, batch_ids, batch_n: int, stream=None, out=None, new_rows=None):
         """Fast step reading the selected rows from the compact buffers."""
         self.kv.seq_len = seq_len.data_ptr() if torch.is_tensor(seq_len) else seq_len
-        sfi.sfi_fast_step_compact(self.kv, batch_ids, batch_n, q, self.sel_idx, self.sel_count, self.Hkv,
+        sfi.sfi_fast_step_compact(self._kvx(new_rows), batch_ids, batch_n, q, self.sel_idx, self.sel_count, self.Hkv,
                                   self.k, self.n_sink, self.window, self.ck, self.cv,
                                   self.out if out is None else out, self.ws_fast, self.ws_fast_bytes, stream)
 
     def co_step(self, q, seq_len, slow_ids, n_slow: int, fast_ids, n_fast: int, stream=None,
-                out=None, select: bool = True, k_seq=None):
+                out=None, select: bool = True, k_seq=None, new_rows=None):
         """Slow steps of slow_ids and fast steps of fast_ids in one co-launched
         pass, then the selector of the slow sequences."""
         self.kv.seq_len = seq_len.data_ptr() if torch.is_tensor(seq_len) else seq_len
-        sfi.sfi_decode_step(self.kv, slow_ids, n_slow, fast_ids, n_fast, q,
+        sfi.sfi_decode_step(self._kvx(new_rows), slow_ids, n_slow, fast_ids, n_fast, q,
                             self.out if out is None else out, self.evidence, self.key_norm, self.ld,
                             self.sel_idx, self.sel_count, self.Hkv, self.k, self.n_sink, self.window,
                             self.ws_step, self.ws_step_bytes, stream)
@@ -205,14 +211,14 @@ class SFIDecoder:
             self.slow_select_only(self.kv.seq_len, slow_ids, n_slow, stream, k_seq=k_seq)
 
     def step_select(self, q, seq_len, slow_ids, n_slow: int, fast_ids, n_fast: int, stream=None,
-                    out=None, k_seq=None):
+                    out=None, k_seq=None, new_rows=None):
         """One call for the step and the slow sequences' new selections
         (sfi_decode_step_select): the slow step forms the selector's prior
         statistics, so the selection runs only its key and pick passes."""
         self.kv.seq_len = seq_len.data_ptr() if torch.is_tensor(seq_len) else seq_len
         self.params.k_per_seq = None if k_seq is None else k_seq.data_ptr()
         try:
-            sfi.sfi_decode_step_select(self.kv, self.params, slow_ids, n_slow, fast_ids, n_fast, q,
+            sfi.sfi_decode_step_select(self._kvx(new_rows), self.params, slow_ids, n_slow, fast_ids, n_fast, q,
                                        self.out if out is None else out, self.evidence, self.key_norm,
                                        self.ld, self.sel_idx, self.sel_count, self.fused, self.ws_stepsel,
                                        self.ws_stepsel_bytes, stream)
@@ -225,16 +231,16 @@ class SFIDecoder:
         previous layer's deferred selection (pending, an sfi_deferred or None)
         runs inside this call's grids and this layer's own selection is
         deferred.  Returns it (active when step s has slow sequences); pass it
-        to the next layer's call, or to sfi_run_deferred after the last."""
+        to the next layer's call, or to sfi_run_deferred after the last.
+        new_kv as in step(): the call appends the rows itself."""
         ks = None if plan.k_seq is None else plan.k_seq[s]
         ns, nf = int(plan.n_slow[s]), int(plan.n_fast[s])
-        if new_kv is not None:
-            self.append(new_kv[0][s], new_kv[1][s], plan.seq_len[s], None, self.B, stream)
         self.kv.seq_len = plan.seq_len[s].data_ptr()
+        kvx = self._kvx(None if new_kv is None else (new_kv[0][s], new_kv[1][s]))
         self.params.k_per_seq = None if ks is None else ks.data_ptr()
         own = sfi.sfi_deferred()
         try:
-            sfi.sfi_decode_layer_step(self.kv, self.params, plan.slow_list(s), ns, plan.fast_list(s), nf,
+            sfi.sfi_decode_layer_step(kvx, self.params, plan.slow_list(s), ns, plan.fast_list(s), nf,
                                       q_steps[s], self.out if out is None else out, self.evidence,
                                       self.key_norm, self.ld, self.sel_idx, self.sel_count, self.fused,
                                       self.ws_stepsel, self.ws_stepsel_bytes, pending, own, stream)
@@ -260,11 +266,12 @@ class SFIDecoder:
 
     # -- one decode step of a planned run ------------------------------------
     def step(self, plan: DecodePlan, s: int, q_steps, stream=None, out=None, co: bool = True,
-             fused_select: bool = True, new_kv=None):
+             fused_select: bool = True, new_kv=None, fused_append: bool = True):
         """Decode step s: q_steps is the device tensor [steps][B][Hq][d].
 
-        new_kv = (K_new, V_new), each [steps][B][1][Hkv][d]: the step first
-        appends every sequence's new row (sfi_append_kv) at row seq_len - 1.
+        new_kv = (K_new, V_new), each [steps][B][1][Hkv][d]: the step appends
+        every sequence's new row at row seq_len - 1, inside its own calls
+        (fused_append) or by a separate sfi_append_kv call first.
 
         With co=True a step that has slow sequences runs as one call that
         co-launches its slow and fast shares and refreshes the slow
@@ -276,18 +283,22 @@ class SFIDecoder:
         ks = None if plan.k_seq is None else plan.k_seq[s]
         ns, nf = int(plan.n_slow[s]), int(plan.n_fast[s])
         sids, fids = plan.slow_list(s), plan.fast_list(s)
+        nr = None
         if new_kv is not None:
-            self.append(new_kv[0][s], new_kv[1][s], sl, None, self.B, stream)
+            if fused_append:
+                nr = (new_kv[0][s], new_kv[1][s])
+            else:
+                self.append(new_kv[0][s], new_kv[1][s], sl, None, self.B, stream)
         if co and ns and fused_select:
-            self.step_select(q, sl, sids, ns, fids, nf, stream, out=out, k_seq=ks)
+            self.step_select(q, sl, sids, ns, fids, nf, stream, out=out, k_seq=ks, new_rows=nr)
             return
         if co and ns and nf:
-            self.co_step(q, sl, sids, ns, fids, nf, stream, out=out, k_seq=ks)
+            self.co_step(q, sl, sids, ns, fids, nf, stream, out=out, k_seq=ks, new_rows=nr)
             return
         if ns:
-            self.slow(q, sl, sids, ns, stream, out=out, k_seq=ks)
+            self.slow(q, sl, sids, ns, stream, out=out, k_seq=ks, new_rows=nr)
         if nf:
-            self.fast(q, sl, fids, nf, stream, out=out)
+            self.fast(q, sl, fids, nf, stream, out=out, new_rows=nr)
 
     def run_pipelined(self, plan: DecodePlan, q_steps, s_begin: int, s_end: int, stream_a,
                       stream_b, stream_c, out_steps):
@@ -376,8 +387,9 @@ class SFIDecoder:
         list once the fast steps that read it are done), and with a shared
         output buffer (out_steps None) so does A(s)'s slow step (a sequence
         fast at s-1 and slow at s writes the same output slot).  With new_kv
-        each chain first appends its own sequences' rows of the step.  Both
-        chains join back into stream_a.  Eager only (see _no_capture).
+        each chain's step call appends its own sequences' rows (fused
+        append).  Both chains join back into stream_a.  Eager only (see
+        _no_capture).
         """
         self._no_capture("run_two_streams")
         for st in (stream_a, stream_b):
@@ -395,11 +407,10 @@ class SFIDecoder:
             ns, nf = int(plan.n_slow[s]), int(plan.n_fast[s])
             if ns:
                 sids = plan.slow_list(s)
-                if new_kv is not None:
-                    self.append(new_kv[0][s], new_kv[1][s], sl, sids, ns, stream_a)
+                nr = None if new_kv is None else (new_kv[0][s], new_kv[1][s])
                 if out_steps is None and prev_b is not None:
                     stream_a.wait_event(prev_b)
-                self.slow(q, sl, sids, ns, stream_a, out=out, select=False)
+                self.slow(q, sl, sids, ns, stream_a, out=out, select=False, new_rows=nr)
                 if prev_b is not None:
                     stream_a.wait_event(prev_b)
                 self.slow_select_only(sl, sids, ns, stream_a,
@@ -410,9 +421,8 @@ class SFIDecoder:
                 stream_b.wait_event(prev_a)
             if nf:
                 fids = plan.fast_list(s)
-                if new_kv is not None:
-                    self.append(new_kv[0][s], new_kv[1][s], sl, fids, nf, stream_b)
-                self.fast(q, sl, fids, nf, stream_b, out=out)
+                nr = None if new_kv is None else (new_kv[0][s], new_kv[1][s])
+                self.fast(q, sl, fids, nf, stream_b, out=out, new_rows=nr)
             ev_b = ev()
             ev_b.record(stream_b)
             prev_a, prev_b = ev_a, ev_b
@@ -491,9 +501,12 @@ class VegasDecoder:
                        self.ld, self.sel_idx, self.sel_count, None, self.ws_sel, self.ws_sel_bytes,
                        stream)
 
-    def draft(self, q, seq_len, batch_ids=None, batch_n=None, stream=None):
+    def draft(self, q, seq_len, batch_ids=None, batch_n=None, stream=None, new_rows=None):
+        """Draft step (sparse attention on the selection); new_rows =
+        (k_new, v_new) [B][Hkv][d] appends the step's row in the same call."""
         self.kv.seq_len = seq_len.data_ptr() if torch.is_tensor(seq_len) else seq_len
         bn = self.B if batch_n is None else batch_n
-        sfi.sfi_fast_step(self.kv, batch_ids, bn, q, self.sel_idx, self.sel_count, 1, self.k,
+        kv = self.kv if new_rows is None else sfi.with_new_rows(self.kv, new_rows[0], new_rows[1])
+        sfi.sfi_fast_step(kv, batch_ids, bn, q, self.sel_idx, self.sel_count, 1, self.k,
                           self.n_sink, self.window, self.out, self.ws_fast, self.ws_fast_bytes,
                           stream)

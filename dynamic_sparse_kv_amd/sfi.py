@@ -43,6 +43,7 @@ class sfi_kv(ctypes.Structure):
         ("seq_len", _vp),
         ("B", _c_int), ("Hq", _c_int), ("Hkv", _c_int), ("d", _c_int),
         ("cap", _c_int), ("max_seq_len", _c_int),
+        ("k_new", _vp), ("v_new", _vp),
     ]
 
 
@@ -192,6 +193,15 @@ def make_kv(k, v, seq_len, Hq: int, max_seq_len: int, page_table=None, page_size
         kv.num_pages = int(k.shape[0])
         kv.cap = 0
     return kv
+
+
+def with_new_rows(kv: sfi_kv, k_new, v_new) -> sfi_kv:
+    """A copy of kv whose step calls also append each listed sequence's new
+    row (k_new, v_new: [B][Hkv][d] bf16) at cache row seq_len - 1."""
+    x = sfi_kv()
+    ctypes.pointer(x)[0] = kv
+    x.k_new, x.v_new = _ptr(k_new), _ptr(v_new)
+    return x
 
 
 def select_params(mode: int, lam: float, k: int, n_sink: int, window: int,

@@ -72,7 +72,19 @@ typedef enum {
  * sequence a call touches; it sizes grids and workspaces.  Device values are
  * trusted only within bounds: seq_len is clamped to [0, max_seq_len], page ids
  * to [0, num_pages), and listed sequence ids outside [0, B) are skipped, so a
- * corrupt argument yields wrong numbers, never an out-of-bounds access. */
+ * corrupt argument yields wrong numbers, never an out-of-bounds access.
+ *
+ * Fused append [SFI technical summary, section 1: the cache grows by each
+ * decode step's own key and value]: k_new, v_new ([B][Hkv][d] bf16 bits,
+ * 16-byte aligned; both NULL or both set) hold that row of every sequence.
+ * Set, the step calls (sfi_slow_step, sfi_fast_step, sfi_fast_step_noalloc,
+ * sfi_fast_step_compact, sfi_decode_step, sfi_decode_step_select,
+ * sfi_decode_layer_step) take cache row seq_len[b] - 1 of each listed
+ * sequence from them and store it into the cache (k, v must then be
+ * writable): the same results as sfi_append_kv with T = 1 followed by the
+ * step, without the extra launch.  Sequences a call does not list are not
+ * appended.  sfi_append_kv, sfi_verify_* and sfi_slow_step_window return
+ * SFI_ERR_RANGE when they are set; sfi_compact_selected ignores them. */
 typedef struct sfi_kv {
   const uint16_t *k;
   const uint16_t *v;
@@ -84,6 +96,8 @@ typedef struct sfi_kv {
   int32_t B, Hq, Hkv, d;      /* d in {64, 128}; Hq % Hkv == 0; Hq/Hkv in {1,2,4,5,8} */
   int32_t cap;                /* contiguous only: rows per (b, kv head) */
   int32_t max_seq_len;        /* [host] */
+  const uint16_t *k_new;      /* NULL, or the step's new rows [B][Hkv][d] (fused append) */
+  const uint16_t *v_new;
 } sfi_kv;
 
 enum { SFI_SCORE_FUSED = 0, SFI_SCORE_RAW = 1 };

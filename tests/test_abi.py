@@ -96,6 +96,24 @@ def test_slow_step_validation():
     assert _slow(_kv(page_table=FAKE, page_size=24, max_pages=100, num_pages=200)) == sfi.SFI_ERR_RANGE
     assert _slow(_kv(page_table=FAKE, page_size=16, max_pages=10, num_pages=200)) == sfi.SFI_ERR_RANGE
     assert _slow(_kv(page_table=FAKE, page_size=16, max_pages=100, num_pages=0)) == sfi.SFI_ERR_SHAPE
+    # fused-append rows: both or neither, 16-byte aligned
+    assert _slow(_kv(k_new=FAKE)) == sfi.SFI_ERR_NULL
+    assert _slow(_kv(k_new=FAKE, v_new=FAKE + 4)) == sfi.SFI_ERR_RANGE
+    assert _slow(_kv(k_new=FAKE, v_new=FAKE), batch_n=0) == sfi.SFI_OK
+
+
+def test_fused_rows_refused_where_unsupported():
+    """sfi_append_kv (its rows come as arguments) and the verify and window
+    calls reject a cache description that carries fused-append rows."""
+    L = sfi.lib()
+    kv = _kv(k_new=FAKE, v_new=FAKE)
+    assert L.sfi_append_kv(ctypes.byref(kv), None, 1, FAKE, FAKE, 1, None) == sfi.SFI_ERR_RANGE
+    assert L.sfi_verify_aggregate(ctypes.byref(kv), None, 1, FAKE, 8, 0xFF, FAKE, FAKE, 1000, FAKE,
+                                  1 << 40, None) == sfi.SFI_ERR_RANGE
+    assert L.sfi_slow_step_window(ctypes.byref(kv), None, 1, FAKE, 4, FAKE, FAKE, None, 1000, FAKE,
+                                  1 << 40, None) == sfi.SFI_ERR_RANGE
+    kv2 = sfi.with_new_rows(_kv(), FAKE, FAKE)
+    assert (kv2.k_new, kv2.v_new, kv2.B, kv2.max_seq_len) == (FAKE, FAKE, 2, 900)
 
 
 def _select(p, B=2, H=2, max_len=900, ld=900, ws_bytes=1 << 40, **kw):

@@ -688,6 +688,116 @@ def test_decode_run_with_append_equals_predrawn_cache():
     assert torch.equal(res[0][3][:, :, :n_end].view(torch.int16), res[1][3][:, :, :n_end].view(torch.int16))
 
 
+@pytest.mark.parametrize("mode,paged", [("select", False), ("select", True), ("co", False),
+                                        ("split", True), ("two", False), ("layer", False),
+                                        ("compact", False)])
+def test_fused_append_equals_predrawn_cache(mode, paged):
+    """Step calls given the step's new rows in the cache description (fused
+    append) give the same bits -- outputs, selections and cache contents --
+    as the same calls over the cache drawn up front, in every call path."""
+    _say(f"fused append, mode={mode} paged={paged}")
+    cfg = W.CONFIGS["tiny-4k"].replace(B=3, steps=28, k=128)
+    starts = W.sentence_starts(cfg)
+    slow = O.schedule(starts, cfg.budget)
+    slow[1] = [True, False, True]     # a step with slow and fast sequences
+    q = W.make_queries(cfg, starts).to(DEV)
+    ctx = W.context_lengths(cfg)
+    plan = DecodePlan(slow, ctx, DEV)
+    cap = cfg.ctx + cfg.steps
+    ps = 16
+    table = None
+    if paged:
+        npg = (cap + ps - 1) // ps
+        table = np.random.default_rng(7).permutation(cfg.B * npg).astype(np.int32).reshape(cfg.B, npg)
+    res = []
+    for fused in (False, True):
+        Kc, Vc = W.make_kv(cfg, device=DEV, cap=cap)
+        if paged:
+            K = W.to_paged(Kc, table, table.size, ps)
+            V = W.to_paged(Vc, table, table.size, ps)
+            kw = dict(page_table=torch.from_numpy(table).to(DEV), page_size=ps)
+        else:
+            K, V, kw = Kc, Vc, {}
+        new_kv = W.take_decode_rows(K, V, ctx, cfg.steps, table=table) if fused else None
+        dec = SFIDecoder(K, V, cfg.Hq, cap, n_sink=4, window=256, k=cfg.k, lam=cfg.lam, **kw)
+        outs = torch.zeros((cfg.steps, cfg.B, cfg.Hq, cfg.d), device=DEV)
+        sa = torch.cuda.current_stream()
+        if mode == "two":
+            dec.run_two_streams(plan, q, 0, cfg.steps, sa, torch.cuda.Stream(), out_steps=outs, new_kv=new_kv)
+        for s in range(cfg.steps if mode != "two" else 0):
+            nr = None if new_kv is None else (new_kv[0][s], new_kv[1][s])
+            if mode == "select":
+                dec.step(plan, s, q, out=outs[s], new_kv=new_kv)
+            elif mode == "co":
+                dec.step(plan, s, q, out=outs[s], new_kv=new_kv, fused_select=False)
+            elif mode == "split":
+                dec.step(plan, s, q, out=outs[s], new_kv=new_kv, co=False)
+            elif mode == "layer":
+                own = dec.layer_step(plan, s, q, out=outs[s], new_kv=new_kv)
+                sfi.sfi_run_deferred(own)
+            else:  # compact: slow steps refresh the compact copy, fast steps read it
+                sl, ns, nf = plan.seq_len[s], int(plan.n_slow[s]), int(plan.n_fast[s])
+                if ns:
+                    dec.slow(q[s], sl, plan.slow_list(s), ns, out=outs[s], new_rows=nr)
+                    dec.compact(sl, plan.slow_list(s), ns)
+                if nf:
+                    dec.fast_compact(q[s], sl, plan.fast_list(s), nf, out=outs[s], new_rows=nr)
+        torch.cuda.synchronize()
+        if paged:
+            n = cap
+            Kg = torch.stack([W.gather_paged(K, table, b, n) for b in range(cfg.B)])
+            Vg = torch.stack([W.gather_paged(V, table, b, n) for b in range(cfg.B)])
+        else:
+            Kg, Vg = K, V
+        res.append((outs.clone(), dec.sel_idx.clone(), dec.sel_count.clone(), Kg.clone(), Vg.clone()))
+    a, b = res
+    assert torch.equal(a[0].view(torch.int32), b[0].view(torch.int32))
+    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+    n_end = int(ctx[0]) + cfg.steps
+    for x, y in ((a[3], b[3]), (a[4], b[4])):
+        assert torch.equal(x[:, :, :n_end].view(torch.int16), y[:, :, :n_end].view(torch.int16))
+
+
+def test_fused_append_short_lists_and_rejections():
+    """Fused append where the row sits in the sinks (seq_len <= n_sink) or in
+    no list position (window 0: the first split stores it), and the calls
+    that take no fused rows refuse them."""
+    _say("fused append edge cases")
+    B, Hq, Hkv, d, cap = 3, 8, 2, 64, 600
+    g = torch.Generator(device=DEV).manual_seed(11)
+    Kc = torch.randn((B, Hkv, cap, d), generator=g, device=DEV).to(torch.bfloat16)
+    Vc = torch.randn((B, Hkv, cap, d), generator=g, device=DEV).to(torch.bfloat16)
+    kn = torch.randn((B, Hkv, d), generator=g, device=DEV).to(torch.bfloat16)
+    vn = torch.randn((B, Hkv, d), generator=g, device=DEV).to(torch.bfloat16)
+    q = torch.randn((B, Hq, d), generator=g, device=DEV).to(torch.bfloat16)
+    seq = torch.tensor([3, 1, 500], dtype=torch.int32, device=DEV)
+    sel = torch.full((B, Hkv, 16), -1, dtype=torch.int32, device=DEV)
+    sel[2, :, :3] = torch.tensor([10, 200, 498], dtype=torch.int32, device=DEV)
+    cnt = torch.tensor([[0, 0], [0, 0], [3, 3]], dtype=torch.int32, device=DEV)
+    outs = []
+    for fused in (False, True):
+        K, V = Kc.clone(), Vc.clone()
+        kv = sfi.make_kv(K, V, seq, Hq, cap)
+        if fused:
+            kvx = sfi.with_new_rows(kv, kn, vn)
+        else:
+            for b in range(B):
+                n = int(seq[b])
+                K[b, :, n - 1], V[b, :, n - 1] = kn[b], vn[b]
+            kvx = kv
+        out = torch.zeros((B, Hq, d), device=DEV)
+        ws = torch.zeros(sfi.sfi_fast_workspace_bytes(kv, 16, 4, 0), dtype=torch.uint8, device=DEV)
+        sfi.sfi_fast_step(kvx, None, B, q, sel, cnt, Hkv, 16, 4, 0, out, ws, ws.numel())
+        torch.cuda.synchronize()
+        outs.append((out.clone(), K.clone(), V.clone()))
+    for x, y in zip(outs[0], outs[1]):
+        assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x.view(torch.int32),
+                           y.view(torch.int16) if y.dtype == torch.bfloat16 else y.view(torch.int32))
+    kv = sfi.with_new_rows(sfi.make_kv(Kc, Vc, seq, Hq, cap), kn, vn)
+    with pytest.raises(sfi.SfiError):
+        sfi.sfi_append_kv(kv, None, B, kn, vn, 1)
+
+
 # ------------------------------------------------- co-launched decode step
 
 @pytest.mark.parametrize("Hq,Hkv,d,paged", [(8, 2, 64, False), (40, 8, 128, True)])
