@@ -207,6 +207,81 @@ def traffic_from_counters(d, steps):
             print(f"| {leg} | {k} | {v[3]} | {v[0] / 1e6:.2f} | {v[1] / 1e6:.2f} | {v[2] / 1e6:.2f} | {ratio_s} |")
 
 
+def _short_kernel(name):
+    import re
+    n = name.replace("(anonymous namespace)::", "").replace("sfi::", "").replace("void ", "")
+    return re.sub(r"\(.*", "", n)
+
+
+def kernel_stats(d):
+    """Markdown summary of a rocprofv3 --kernel-trace run (d/bench_kernel_trace.csv):
+    per kernel, every launch, then the graph replays: runs of at least 300
+    back-to-back launches (under 30 us apart) and their per-kernel share."""
+    import csv
+    rows = list(csv.DictReader(open(os.path.join(d, "bench_kernel_trace.csv"))))
+    ks = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), _short_kernel(r["Kernel_Name"]))
+                for r in rows)
+
+    def table(items, title):
+        per = {}
+        for s0, e0, n in items:
+            per.setdefault(n, []).append((e0 - s0) / 1000.0)
+        tot = sum(sum(v) for v in per.values())
+        print(f"{title}\n")
+        print("| kernel | launches | avg us | median us | min us | max us | total ms | % of kernel time |")
+        print("|---|---|---|---|---|---|---|---|")
+        for n, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+            if sum(v) < 0.001 * tot:
+                continue
+            print(f"| `{n[:80]}` | {len(v)} | {np.mean(v):.2f} | {np.median(v):.2f} | {min(v):.2f} | "
+                  f"{max(v):.2f} | {sum(v) / 1e3:.3f} | {100 * sum(v) / tot:.2f} |")
+        print()
+    table(ks, "All launches")
+    bursts, cur = [], [ks[0]]
+    for k in ks[1:]:
+        if k[0] - cur[-1][1] < 30000:
+            cur.append(k)
+        else:
+            bursts.append(cur)
+            cur = [k]
+    bursts.append(cur)
+    for i, b in enumerate(x for x in bursts if len(x) >= 300 and all("at::" not in k[2] for k in x)):
+        span = (b[-1][1] - b[0][0]) / 1000.0
+        busy = sum(e0 - s0 for s0, e0, _ in b) / 1000.0
+        table(b, f"Graph replay {i}: {len(b)} launches back to back, {span:.1f} us from the first start "
+                 f"to the last end, {busy:.1f} us inside kernels")
+
+
+def mfma_stats(d):
+    """MFMA use per kernel from one rocprofv3 --pmc run of
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE
+    (d/bench_counter_collection.csv): bf16 MFMA flops per launch (MOPS x
+    512), the MFMA busy share of the SIMDs over the dispatch's active cycles
+    (busy / (active / 8 XCDs x 1024 SIMDs)), and the flop rate over those
+    cycles at 2.4 GHz."""
+    import csv
+    per = {}
+    for r in csv.DictReader(open(os.path.join(d, "bench_counter_collection.csv"))):
+        key = (int(r["Dispatch_Id"]), _short_kernel(r["Kernel_Name"]))
+        per.setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    agg = {}
+    for (_, n), c in per.items():
+        a = agg.setdefault(n, [0, 0.0, 0.0, 0.0])
+        a[0] += 1
+        a[1] += c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512
+        a[2] += c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+        a[3] += c.get("GRBM_GUI_ACTIVE", 0.0) / 8
+    print("| kernel | launches | bf16 MFMA GFLOP per launch | active cycles per launch | MFMA busy (of SIMD cycles) "
+          "| TFLOP/s over active cycles |")
+    print("|---|---|---|---|---|---|")
+    for n, (cnt, fl, busy, act) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
+        if fl <= 0:
+            continue
+        util = busy / (act * 1024) if act > 0 else float("nan")
+        tf = fl / (act / 2.4e9) / 1e12 if act > 0 else float("nan")
+        print(f"| `{n[:70]}` | {cnt} | {fl / cnt / 1e9:.2f} | {act / cnt:.0f} | {util:.4f} | {tf:.1f} |")
+
+
 def kernel_source_hash():
     """sha256 over every HIP source of the library: counter-derived traffic
     is reported only while the kernels are the ones it was measured on."""
@@ -427,7 +502,7 @@ def leg_stack128k(timed_steps=24, dense_steps=4):
     decs, qs, nks = [], [], []
     _log(f"[bench] stack32-128k: generating {cfg.layers} layers")
     for layer in range(cfg.layers):
-        K, V = W.make_kv(cfg, layer=layer, device=dev, cap=max_len)
+        K, V = W.make_kv(cfg, layer=layer, device=dev)
         nks.append(W.take_decode_rows(K, V, ctx, steps))
         qs.append(W.make_queries(cfg, starts, layer=layer).to(dev))
         decs.append(SFIDecoder(K, V, cfg.Hq, max_len, n_sink=cfg.n_sink, window=cfg.window,
@@ -705,7 +780,7 @@ def leg_ragged_paged(timed_steps=32, dense_steps=4):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--replicas", type=int, default=8,
                     help="independent copies of the layer stepped in turn (cold headline)")
@@ -720,12 +795,22 @@ def main():
     ap.add_argument("--record-calls", metavar="PATH",
                     help="write the timed eager calls (workload, kind, algorithmic bytes) to PATH as "
                          "json, each followed by a marker kernel, for the counter reducer")
+    ap.add_argument("--kernel-stats", metavar="DIR",
+                    help="no GPU run: markdown per-kernel summary of a rocprofv3 --kernel-trace csv run in DIR")
+    ap.add_argument("--mfma-stats", metavar="DIR",
+                    help="no GPU run: markdown MFMA summary of a rocprofv3 --pmc csv run in DIR (see mfma_stats)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy (a known-size kernel "
                          "for scaling hardware byte counters)")
     args = ap.parse_args()
     if args.traffic:
         traffic_from_counters(args.traffic, args.steps)
+        return
+    if args.kernel_stats:
+        kernel_stats(args.kernel_stats)
+        return
+    if args.mfma_stats:
+        mfma_stats(args.mfma_stats)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); the path has no multi-GPU mode",

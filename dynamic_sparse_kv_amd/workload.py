@@ -129,32 +129,44 @@ def heavy_hitter_positions(cfg: SFIConfig, layer: int, b: int, ctx: int) -> np.n
     return out
 
 
+def padded_capacity(rows: int) -> int:
+    """Row capacity of a contiguous cache that holds ``rows`` rows: rounded up
+    to 64 rows, plus 32.  A (sequence, kv head) stride that is an exact
+    multiple of a large power of two can alias in the HBM channel mapping:
+    on one MI355X a stride of 2^23 + 2^16 bytes (33024 rows of 256 B) made
+    the cold fast step 2x and the dense step 15 % slower than the padded
+    neighbours (layout only; nothing computed)."""
+    return -(-int(rows) // 64) * 64 + 32
+
+
 def make_kv(cfg: SFIConfig, layer: int = 0, device="cpu", cap: Optional[int] = None):
     """Contiguous K, V caches, bf16 [B][Hkv][cap][d].
 
     Entries are N(0,1); heavy-hitter key rows are scaled by ``hh_scale``
     before the single round-to-nearest-even conversion to bf16.  Rows past the
     prefill are the tokens a decode run appends; they are drawn up front so
-    the cache only has to grow its length.
+    the cache only has to grow its length.  Without ``cap`` the run's rows
+    are drawn and the capacity is padded (padded_capacity; the padding rows
+    are zero); with ``cap``, all cap rows are drawn.
     """
     ctxs = context_lengths(cfg)
-    if cap is None:
-        cap = int(ctxs.max()) + cfg.growth()
-    K = torch.empty((cfg.B, cfg.Hkv, cap, cfg.d), dtype=torch.bfloat16, device=device)
-    V = torch.empty_like(K)
+    rows = int(ctxs.max()) + cfg.growth() if cap is None else cap
+    cap = padded_capacity(rows) if cap is None else cap
+    K = torch.zeros((cfg.B, cfg.Hkv, cap, cfg.d), dtype=torch.bfloat16, device=device)
+    V = torch.zeros_like(K)
     for b in range(cfg.B):
         gk = torch.Generator(device=device).manual_seed(seed_for(cfg, layer, b, "K"))
-        x = torch.randn((cfg.Hkv, cap, cfg.d), generator=gk, device=device, dtype=torch.float32)
+        x = torch.randn((cfg.Hkv, rows, cfg.d), generator=gk, device=device, dtype=torch.float32)
         hh = heavy_hitter_positions(cfg, layer, b, int(ctxs[b]))
         if hh.size:
             for h in range(cfg.Hkv):
                 idx = torch.as_tensor(hh[h], device=device)
                 x[h, idx] *= cfg.hh_scale
-        K[b] = x.to(torch.bfloat16)
+        K[b, :, :rows] = x.to(torch.bfloat16)
         del x
         gv = torch.Generator(device=device).manual_seed(seed_for(cfg, layer, b, "V"))
-        V[b] = torch.randn((cfg.Hkv, cap, cfg.d), generator=gv, device=device,
-                           dtype=torch.float32).to(torch.bfloat16)
+        V[b, :, :rows] = torch.randn((cfg.Hkv, rows, cfg.d), generator=gv, device=device,
+                                     dtype=torch.float32).to(torch.bfloat16)
     return K, V
 
 

@@ -32,8 +32,16 @@ def test_layers_and_configs_differ():
 def test_shapes_and_heavy_hitters():
     cfg = _tiny()
     K, V = W.make_kv(cfg)
-    cap = cfg.ctx + cfg.steps
+    rows = cfg.ctx + cfg.steps
+    cap = W.padded_capacity(rows)
+    assert cap >= rows and cap % 64 == 32
     assert K.shape == (1, 2, cap, 64) and K.dtype == torch.bfloat16
+    # the padding rows are zero; the drawn rows do not depend on the padding
+    assert not K[:, :, rows:].any() and not V[:, :, rows:].any()
+    K2, _ = W.make_kv(cfg, cap=rows)
+    assert torch.equal(K[:, :, :rows].view(torch.int16), K2.view(torch.int16))
+    K = K[:, :, :rows]
+    cap = rows
     hh = W.heavy_hitter_positions(cfg, 0, 0, cfg.ctx)
     assert hh.shape == (2, 5) and hh.max() < cfg.ctx
     norms = K.float().norm(dim=-1)[0]
