@@ -215,8 +215,8 @@ def _short_kernel(name):
 
 def kernel_stats(d):
     """Markdown summary of a rocprofv3 --kernel-trace run (d/bench_kernel_trace.csv):
-    per kernel, every launch, then the graph replays: runs of at least 300
-    back-to-back launches (under 30 us apart) and their per-kernel share."""
+    per kernel, every launch, then the launches of the graph replays (runs
+    of at least 300 library launches under 30 us apart)."""
     import csv
     rows = list(csv.DictReader(open(os.path.join(d, "bench_kernel_trace.csv"))))
     ks = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), _short_kernel(r["Kernel_Name"]))
@@ -245,11 +245,13 @@ def kernel_stats(d):
             bursts.append(cur)
             cur = [k]
     bursts.append(cur)
-    for i, b in enumerate(x for x in bursts if len(x) >= 300 and all("at::" not in k[2] for k in x)):
-        span = (b[-1][1] - b[0][0]) / 1000.0
-        busy = sum(e0 - s0 for s0, e0, _ in b) / 1000.0
-        table(b, f"Graph replay {i}: {len(b)} launches back to back, {span:.1f} us from the first start "
-                 f"to the last end, {busy:.1f} us inside kernels")
+    runs = [x for x in bursts if len(x) >= 300 and all("at::" not in k[2] for k in x)]
+    if runs:
+        span = sum((b[-1][1] - b[0][0]) for b in runs) / 1000.0
+        busy = sum(e0 - s0 for b in runs for s0, e0, _ in b) / 1000.0
+        table([k for b in runs for k in b],
+              f"Graph replays: {sum(len(b) for b in runs)} launches in {len(runs)} back-to-back runs, "
+              f"{span:.1f} us from first start to last end, {busy:.1f} us inside kernels")
 
 
 def mfma_stats(d):
