@@ -822,7 +822,7 @@ def main():
     import torch
     from dynamic_sparse_kv_amd import sfi
     from dynamic_sparse_kv_amd import workload as W
-    from dynamic_sparse_kv_amd.runner import DecodePlan, SFIDecoder
+    from dynamic_sparse_kv_amd.runner import DecodePlan, SFIDecoder, stats_prior_steps
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -896,6 +896,10 @@ def main():
     _log("[bench] per-call timing pass")
     timer = RegionTimer(dev, stream, "headline")
     decs = [rp["dec"] for rp in reps]
+    # the combined calls form their prior from the key-norm statistics where
+    # the run does (the statistics' values at this point are the run's end
+    # state: the work is the same, the selections are not the run's)
+    use_st = stats_prior_steps(plan)
     for kind, s, nbytes in percall_list(plan.slow, ctx, cfg, K_steps):
         ns, nf = int(plan.n_slow[s]), int(plan.n_fast[s])
         sl = plan.seq_len[s]
@@ -906,8 +910,10 @@ def main():
               "fast": lambda d, q, st, r: d.fast(q, sl, fids, nf, st, new_rows=r),
               "select": lambda d, q, st, r: d.slow_select_only(sl, sids, ns, st),
               # informational: not a roofline candidate (its selector part is latency-bound)
-              "step_select": lambda d, q, st, r: d.step_select(q, sl, sids, ns, fids, nf, st, new_rows=r),
-              "slow_select": lambda d, q, st, r: d.step_select(q, sl, sids, ns, fids, nf, st, new_rows=r)}[kind]
+              "step_select": lambda d, q, st, r: d.step_select(q, sl, sids, ns, fids, nf, st, new_rows=r,
+                                                               use_stats=bool(use_st[s])),
+              "slow_select": lambda d, q, st, r: d.step_select(q, sl, sids, ns, fids, nf, st, new_rows=r,
+                                                               use_stats=bool(use_st[s]))}[kind]
         timer(kind, [lambda st, d=rp["dec"], q=rp["q"][s], r=(rp["nk"][0][s], rp["nk"][1][s]): mk(d, q, st, r)
                      for rp in reps], nbytes)
     # The combined call again for the same slow steps, with Soft-NMS (radius

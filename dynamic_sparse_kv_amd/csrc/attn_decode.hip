@@ -58,12 +58,6 @@ namespace {
 #ifndef SFI_WAVES_OF_WG
 #define SFI_WAVES_OF_WG 1
 #endif
-// Evidence mode: stage the per-key logits and norms in LDS and write them
-// out in bulk every kEvBlock keys (1), or store them row by row from the
-// main loop (0).
-#ifndef SFI_EVID_LDS
-#define SFI_EVID_LDS 1
-#endif
 
 
 enum { MODE_SLOW = 0, MODE_FAST = 1 };
@@ -93,6 +87,20 @@ struct PartialArgs {
   // fast step: compact copy of the selected rows, [B][Hkv][sel_k][D] (or null)
   const uint16_t *ck, *cv;
   int pe;  // 1: partial buffers indexed by batch entry instead of sequence id
+  // Evidence mode with the prior formed from the key-norm statistics
+  // (the STATS kernels; nsum null): mean and std of the row's key norms from
+  // kv.nstat (plus the step's own row when it is appended here), each
+  // split's sum of the prior weights into wpart [B*Hkv][stride] (fp64), the
+  // row constants into sel_meta and the updated statistics into nnext
+  // [B*Hkv][2] (split 0; the finalize stores them), and the splits clear
+  // the row's bucket histogram sel_ghist between them for the key pass in
+  // the finalize.
+  double *wpart;
+  double *nnext;
+  SelRowMeta *sel_meta;
+  uint32_t *sel_ghist;
+  int nsp;  // planned splits per (sequence, kv head)
+  float norm_coef, pos_tau;
 };
 
 // Maximum over the wave of a value that is equal within each aligned group
@@ -128,8 +136,9 @@ __device__ __forceinline__ FastList fast_list(const int32_t *sel_idx, const int3
 // One workgroup's share of a decode step: rows [split*chunk, ...) of the row
 // list of (sequence batch_ids[zb], kv head g).  A device function so that the
 // co-launch kernel below can run slow and fast shares in one grid.
-template <int D, int G, bool PAGED, int MODE, bool EVID, bool COMPACT = false>
+template <int D, int G, bool PAGED, int MODE, bool EVID, bool COMPACT = false, bool STATS = false>
 __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, int g, int zb) {
+  static_assert(!STATS || EVID, "the statistics prior is an evidence-mode variant");
   // 8 lanes per row halves the cross-lane reduction and softmax work per row
   // compared with 16; wide groups (G*D >= 640) use 16 to bound accumulators
   // (at G = 5, d = 128 eight lanes would need all 256 VGPRs).
@@ -161,7 +170,7 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
   __shared__ float s_acc[NW][G][D];
   // Evidence staging: the logits (G per key) and norms of one block of
   // kEvBlock consecutive rows, written out when the block is complete.
-  constexpr bool EV_LDS = EVID && SFI_EVID_LDS;
+  constexpr bool EV_LDS = EVID;
   constexpr int kEvBlock = 512;
   __shared__ float s_evl[EV_LDS ? kEvBlock * G : 1];
   __shared__ float s_evn[EV_LDS ? kEvBlock : 1];
@@ -195,6 +204,18 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
   int jv[IPT];
   const int nfix_full = a.n_sink + a.window;
   const size_t lrow = (size_t)(b * a.kv.Hkv + g);
+  // Prior from the key-norm statistics: the row's sums and (fused append)
+  // the slices of the step's own K row go out with the query loads and
+  // have arrived once the sequence length has.
+  double st1 = 0.0, st2 = 0.0;
+  uint4 knx = make_uint4(0u, 0u, 0u, 0u);
+  if constexpr (STATS) {
+    {
+      st1 = a.kv.nstat[lrow * 2 + 0];
+      st2 = a.kv.nstat[lrow * 2 + 1];
+      if (a.kv.k_new != nullptr) knx = ldg16(a.kv.k_new + lrow * D + 8 * ((tid & 63) % (D / 8)));
+    }
+  }
 
   // One pipeline stage: U rows per lane group, K and V slices of DPL dims.
   struct Stage {
@@ -233,6 +254,29 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
   }
 
   const int n = clamp_len(a.seq_len, b, a.max_len);
+  // the prior's row constants (mean and std of the key norms, the step's
+  // own row included), uniform over the workgroup and so held in scalar
+  // registers through the main loop
+  float st_muf = 0.f, st_cz = 0.f, st_ct = 0.f;
+  if constexpr (STATS) {
+    {
+      if (a.kv.k_new != nullptr) {
+        const float nu = wave_row_norm<D>(knx);
+        st1 += (double)nu;
+        st2 = fma((double)nu, (double)nu, st2);
+      }
+      prior_consts(st1, st2, n, a.norm_coef, &st_muf, &st_cz);
+      st_muf = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(st_muf)));
+      st_cz = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(st_cz)));
+      st_ct = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(kLog2e / a.pos_tau)));
+      if (tid == 0 && split == 0) {
+        a.sel_meta[lrow].muf = st_muf;
+        a.sel_meta[lrow].cz = st_cz;
+        a.nnext[lrow * 2 + 0] = st1;
+        a.nnext[lrow * 2 + 1] = st2;
+      }
+    }
+  }
   int L = n;
   FastList fl;
   if constexpr (MODE == MODE_FAST) {
@@ -254,16 +298,36 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
     if constexpr (MODE == MODE_FAST) app_p = (fl.nw > 0) ? fl.ns + fl.nw - 1 : (n - 1 < fl.ns ? n - 1 : -1);
     app_wg = (app_p >= 0) ? (app_p >= p0 && app_p < p0 + a.chunk) : (split == 0);
   }
+  // With key-norm statistics and no prior formed here (whose finalize
+  // stores them), the row's norm is added to them.
   auto append_store = [&]() {
-    if (app_wg && tid < 2 * kAppSlices) {
-      const bool isv = tid >= kAppSlices;
-      const int c = tid % kAppSlices;
-      const uint4 x = ldg16((isv ? a.kv.v_new : a.kv.k_new) + new_row + 8 * c);
-      uint16_t *dst = const_cast<uint16_t *>(isv ? a.kv.v : a.kv.k);
-      *reinterpret_cast<uint4 *>(dst + kv_row<D, PAGED>(a.kv, b, g, n - 1) + 8 * c) = x;
+    if (app_wg) {
+      uint4 x = make_uint4(0u, 0u, 0u, 0u);
+      if (tid < 2 * kAppSlices) {
+        const bool isv = tid >= kAppSlices;
+        const int c = tid % kAppSlices;
+        x = ldg16((isv ? a.kv.v_new : a.kv.k_new) + new_row + 8 * c);
+        uint16_t *dst = const_cast<uint16_t *>(isv ? a.kv.v : a.kv.k);
+        *reinterpret_cast<uint4 *>(dst + kv_row<D, PAGED>(a.kv, b, g, n - 1) + 8 * c) = x;
+      }
+      if (!STATS && a.kv.nstat != nullptr && a.nsum == nullptr && tid < 64) {  // wave 0: lanes 0 .. D/8 - 1 hold K
+        const float nu = wave_row_norm<D>(x);
+        if (tid == 0) {
+          a.kv.nstat[lrow * 2 + 0] += (double)nu;
+          a.kv.nstat[lrow * 2 + 1] = fma((double)nu, (double)nu, a.kv.nstat[lrow * 2 + 1]);
+        }
+      }
     }
   };
+  if constexpr (STATS) {
+    {  // this split's stripe of the row histogram
+      for (int i = split * kThreads + tid; i < 4096; i += a.nsp * kThreads) a.sel_ghist[lrow * 4096 + i] = 0u;
+    }
+  }
   if (p0 >= L) {
+    if constexpr (STATS) {
+      if (tid == 0) a.wpart[lrow * a.stride + split] = 0.0;
+    }
     append_store();
     // no rows here: a neutral partial (Z = 0), so the finalize can merge
     // every planned split without reading the list length
@@ -452,20 +516,21 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
         // the hardware square root (within 1 ulp; the library's sqrtf adds
         // a ~15-instruction correctly rounded refinement per key)
         const float nv = __builtin_amdgcn_sqrtf(nn);
-        if constexpr (EV_LDS) {
-          // row js sits in the current block (a masked row repeats the
-          // chunk's last row, which is in the chunk's last block)
-          const int r = (js - p0) & (kEvBlock - 1);
-          s_evl[r * G + sub % G] = v;
-          s_evn[r] = nv;
-        } else {
-          a.logits[(lrow * a.lld + js) * G + sub % G] = v;
-          a.key_norm[lrow * a.nld + js] = nv;
-        }
-        if (a.nsum) {  // wave-uniform: only a step that forms the prior needs the sums
+        // row js sits in the current block (a masked row repeats the
+        // chunk's last row, which is in the chunk's last block)
+        const int r = (js - p0) & (kEvBlock - 1);
+        s_evl[r * G + sub % G] = v;
+        s_evn[r] = nv;
+        if constexpr (!STATS) {
+          if (a.nsum) {  // wave-uniform: only a step that forms the prior needs the sums
+            const bool acc = st.j[u] >= 0 && sub == G % LPR;
+            ns1 += acc ? (double)nv : 0.0;
+            ns2 = acc ? fma((double)nv, (double)nv, ns2) : ns2;
+          }
+        } else {  // the prior weights' sum instead
           const bool acc = st.j[u] >= 0 && sub == G % LPR;
-          ns1 += acc ? (double)nv : 0.0;
-          ns2 = acc ? fma((double)nv, (double)nv, ns2) : ns2;
+          const float w = prior_w(nv, st.j[u], st_muf, st_cz, (float)(n - 1), st_ct);
+          ns1 += acc ? (double)w : 0.0;
         }
       }
     }
@@ -543,6 +608,9 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
   }
   // Evidence staging: write the block of rows [blk, blk + nr) out of LDS
   // (every thread of the workgroup takes part; barriers on both sides).
+  // Prior from the statistics: each flushed block's prior weights into this
+  // thread's fp64 sum.
+
   auto ev_flush = [&](int blk, int nr) {
     if constexpr (EV_LDS) {
       __syncthreads();
@@ -554,6 +622,7 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
     }
   };
   static_assert(!EV_LDS || kEvBlock % (2 * STEP) == 0, "a staging block is whole loop trips");
+  static_assert(!EV_LDS || !COMPACT, "evidence mode streams the cache rows");
   if (!compact_run) {
     load_stage(sa, p0 + rg);
     for (int base = p0; base < p1; base += 2 * STEP) {
@@ -624,7 +693,7 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
   }
   __shared__ double s_ns[NW][2];
   if constexpr (EVID) {
-    if (a.nsum) {
+    if (STATS || a.nsum) {
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) {
         ns1 += __shfl_xor(ns1, off);
@@ -647,6 +716,12 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
       }
       a.nsum[(lrow * a.stride + split) * 2 + 0] = t1;
       a.nsum[(lrow * a.stride + split) * 2 + 1] = t2;
+    }
+    if (STATS && tid == 0) {
+      double t = 0.0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) t += s_ns[w][0];
+      a.wpart[lrow * a.stride + split] = t;
     }
   }
 
@@ -672,9 +747,9 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
   append_store();
 }
 
-template <int D, int G, bool PAGED, int MODE, bool EVID>
+template <int D, int G, bool PAGED, int MODE, bool EVID, bool STATS = false>
 __global__ __launch_bounds__(kThreads) void partial_kernel(PartialArgs a) {
-  partial_body<D, G, PAGED, MODE, EVID>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+  partial_body<D, G, PAGED, MODE, EVID, false, STATS>(a, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // Fast step reading its selected rows from the compact copy.
@@ -731,6 +806,31 @@ __global__ __launch_bounds__(kThreads) void append_kernel(KVView kv, const int32
   *reinterpret_cast<uint4 *>(const_cast<uint16_t *>(kv.v) + dst) = vv;
 }
 
+// Key-norm statistics of appended rows: one wave per (kv head, listed
+// sequence) adds the norms of its T new K rows (rows j < 0 are skipped) in
+// row order.
+template <int D>
+__global__ __launch_bounds__(64) void norm_add_kernel(double *nstat, const int32_t *seq_len,
+                                                      const int32_t *batch_ids, int B, int Hkv, int max_len,
+                                                      const uint16_t *k_new, int T) {
+  const int b = batch_seq(batch_ids, blockIdx.y, B);
+  if (b < 0) return;
+  const int g = blockIdx.x, lane = threadIdx.x;
+  const int n = clamp_len(seq_len, b, max_len);
+  double s1 = 0.0, s2 = 0.0;
+  for (int t = max(0, T - n); t < T; ++t) {
+    const uint4 x = (lane < D / 8) ? ldg16(k_new + (((size_t)b * T + t) * Hkv + g) * D + 8 * lane)
+                                   : make_uint4(0u, 0u, 0u, 0u);
+    const float nu = wave_row_norm<D>(x);
+    s1 += (double)nu;
+    s2 = fma((double)nu, (double)nu, s2);
+  }
+  if (lane == 0) {
+    nstat[((size_t)b * Hkv + g) * 2 + 0] += s1;
+    nstat[((size_t)b * Hkv + g) * 2 + 1] += s2;
+  }
+}
+
 // Slow (dense with evidence) and fast shares of one decode step in a single
 // grid: linear blocks [0, ns) are the slow grid (s_splits x Hkv x slow
 // sequences), the rest the fast grid.  The two sets of sequences are
@@ -742,7 +842,7 @@ __global__ __launch_bounds__(kThreads) void append_kernel(KVView kv, const int32
 // workgroups finish and fill the wave's tail (placed first, they took the
 // attention's slots and serialised: workgroups of one kernel all get the
 // attention's register allocation).
-template <int D, int G, bool PAGED, bool PEND>
+template <int D, int G, bool PAGED, bool PEND, bool STATS = false>
 __global__ __launch_bounds__(kThreads) void copartial_kernel(PartialArgs s, PartialArgs f, int s_splits,
                                                              int f_splits, int Hkv, int ns,
                                                              SelectLaunch pend, int np) {
@@ -756,8 +856,8 @@ __global__ __launch_bounds__(kThreads) void copartial_kernel(PartialArgs s, Part
     }
   }
   if (id < ns) {
-    partial_body<D, G, PAGED, MODE_SLOW, true>(s, id % s_splits, (id / s_splits) % Hkv,
-                                                     id / (s_splits * Hkv));
+    partial_body<D, G, PAGED, MODE_SLOW, true, false, STATS>(s, id % s_splits, (id / s_splits) % Hkv,
+                                                            id / (s_splits * Hkv));
   } else {
     id -= ns;
     partial_body<D, G, PAGED, MODE_FAST, false>(f, id % f_splits, (id / f_splits) % Hkv,
@@ -791,6 +891,18 @@ struct FinalArgs {
   uint32_t *sel_ghist;
   int selP;
   int pe;  // 1: partial buffers indexed by batch entry instead of sequence id
+  // Key-norm statistics [B*Hkv][2], stored by the evidence blocks of a step
+  // that forms the prior (null: none kept): the sums of this pass, or with
+  // keys the partial kernel's updated statistics nnext
+  double *nstat;
+  // Prior formed from the statistics by the partial kernel (keys = 1, nsum
+  // null): the evidence blocks also run the selection's key pass (sel) on
+  // the fused scores, from the splits' prior-weight sums wpart and the row
+  // constants the partial kernel wrote to sel_meta.
+  int keys;
+  const double *wpart;
+  const double *nnext;
+  SelectLaunch sel;
 };
 
 // Merge (m2, z2) into the running softmax pair (m, z): both are a log2-domain
@@ -804,8 +916,9 @@ __device__ __forceinline__ void mz_merge(float &m, float &z, float m2, float z2)
 // grid.x = G combine blocks (one per query head of the group) followed, for
 // slow steps with evidence, by one block per kEvidChunk keys.  Every block
 // issues all of its global loads before it needs the merged maxima, so a
-// block costs one memory round trip.
-template <int D, int G, int MODE, bool EVID>
+// block costs one memory round trip.  KEYS: the evidence blocks also run
+// the selection's key pass (FinalArgs::keys).
+template <int D, int G, int MODE, bool EVID, bool KEYS = false>
 __device__ __forceinline__ void finalize_body(const FinalArgs &a, int x, int g, int zb) {
   constexpr int NW = kThreads / 64;
 
@@ -898,7 +1011,7 @@ __device__ __forceinline__ void finalize_body(const FinalArgs &a, int x, int g, 
     // chunk's logits (one 16-byte load per key and 4 heads) and key norms,
     // the partials' (max, sum) pairs and, for the selector's prior, the
     // per-split key-norm sums.
-    const bool prior = a.nsum != nullptr;
+    const bool prior = KEYS || a.nsum != nullptr;
     float lg[PER][G], nv[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -927,7 +1040,13 @@ __device__ __forceinline__ void finalize_body(const FinalArgs &a, int x, int g, 
       m[h] = kNegBig;
       z[h] = 0.f;
     }
-    double s1 = 0.0, s2 = 0.0;
+    double s1 = 0.0, s2 = 0.0, sw = 0.0;
+    float rm_muf = 0.f, rm_cz = 0.f;
+    if constexpr (KEYS) {
+      const SelRowMeta rm = a.sel_meta[lrow];
+      rm_muf = rm.muf;
+      rm_cz = rm.cz;
+    }
     for (int s = tid; s < S; s += kThreads) {
       float ml[G][2];
 #pragma unroll
@@ -936,8 +1055,10 @@ __device__ __forceinline__ void finalize_body(const FinalArgs &a, int x, int g, 
         ml[h][0] = ml2[0];
         ml[h][1] = ml2[1];
       }
-      double n1 = 0.0, n2 = 0.0;
-      if (prior) {
+      double n1 = 0.0, n2 = 0.0, w1 = 0.0;
+      if constexpr (KEYS) {
+        w1 = a.wpart[lrow * a.stride + s];
+      } else if (prior) {
         n1 = a.nsum[(lrow * a.stride + s) * 2 + 0];
         n2 = a.nsum[(lrow * a.stride + s) * 2 + 1];
       }
@@ -945,9 +1066,10 @@ __device__ __forceinline__ void finalize_body(const FinalArgs &a, int x, int g, 
       for (int h = 0; h < G; ++h) mz_merge(m[h], z[h], ml[h][0], ml[h][1]);
       s1 += n1;
       s2 += n2;
+      sw += w1;
     }
     __shared__ float s_m[NW][G], s_z[NW][G];
-    __shared__ double s_d[NW][2], s_w[NW];
+    __shared__ double s_d[NW][3], s_w[NW];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
 #pragma unroll
@@ -965,10 +1087,12 @@ __device__ __forceinline__ void finalize_body(const FinalArgs &a, int x, int g, 
       for (int off = 32; off >= 1; off >>= 1) {
         s1 += __shfl_xor(s1, off);
         s2 += __shfl_xor(s2, off);
+        sw += __shfl_xor(sw, off);
       }
       if (lane == 0) {
         s_d[wv][0] = s1;
         s_d[wv][1] = s2;
+        s_d[wv][2] = sw;
       }
     }
     __syncthreads();
@@ -981,12 +1105,14 @@ __device__ __forceinline__ void finalize_body(const FinalArgs &a, int x, int g, 
       M[h] = mm;
       rz[h] = 1.0f / ((float)G * zz);
     }
+    float fv[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int j = j0 + tid + i * kThreads;
       float f = 0.f;
 #pragma unroll
       for (int h = 0; h < G; ++h) f = fmaf(exp2_hw(lg[i][h] - M[h]), rz[h], f);
+      fv[i] = f;
       if (j < j1) a.evidence[lrow * a.ld + j] = f;
     }
     if (!prior) return;
@@ -998,22 +1124,60 @@ __device__ __forceinline__ void finalize_body(const FinalArgs &a, int x, int g, 
     const int pch = x - G;
     s1 = 0.0;
     s2 = 0.0;
+    sw = 0.0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       s1 += s_d[w][0];
       s2 += s_d[w][1];
+      sw += s_d[w][2];
+    }
+    // the row's key-norm statistics: exact from this pass, or those the
+    // partial kernel formed the prior from
+    if (a.nstat != nullptr && pch == 0 && tid == 0) {
+      a.nstat[lrow * 2 + 0] = KEYS ? a.nnext[lrow * 2 + 0] : s1;
+      a.nstat[lrow * 2 + 1] = KEYS ? a.nnext[lrow * 2 + 1] : s2;
+    }
+    if constexpr (KEYS) {
+      // the selection's key pass on this chunk (the selector's chunk pch):
+      // s = (1 - lambda) f + lambda w / W with the partial kernel's row
+      // constants and weight sums, so w is the weight it summed, bit for bit
+      static_assert(kEvidChunk == kSelChunk && PER == kPT, "evidence blocks are selector chunks");
+      RowGeo r;
+      row_geo(a.sel, g, zb, r);
+      const float cf = 1.0f - a.sel.lambda;
+      const float cr = sw > 0.0 ? (float)((double)a.sel.lambda / sw) : 0.f;
+      const float ct = kLog2e / a.pos_tau;
+      const float tq = (float)(n - 1);
+      float sc[PER];
+      int jj[PER];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int j = j0 + tid + i * kThreads;
+        const float w = (j < j1) ? prior_w(nv[i], j, rm_muf, rm_cz, tq, ct) : 0.f;
+        sc[i] = fmaf(cf, fv[i], cr * w);
+        jj[i] = j;
+      }
+      if (a.sel.fused_out) {
+        float *fo = a.sel.fused_out + r.row * a.sel.fo_ld;
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+          if (jj[i] < j1) fo[jj[i]] = sc[i];
+      }
+      if (pch >= r.nch) return;  // no candidates in this chunk
+      keys_core(a.sel, r, pch, sc, jj);
+      return;
     }
     float muf, cz;
     prior_consts(s1, s2, n, a.norm_coef, &muf, &cz);
     const float ct = kLog2e / a.pos_tau;
     const float tq = (float)(n - 1);
-    float sw = 0.f;
+    float wc = 0.f;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int j = j0 + tid + i * kThreads;
-      sw += (j < j1) ? prior_w(nv[i], j, muf, cz, tq, ct) : 0.f;
+      wc += (j < j1) ? prior_w(nv[i], j, muf, cz, tq, ct) : 0.f;
     }
-    double W = (double)sw;
+    double W = (double)wc;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) W += __shfl_xor(W, off);
     if (lane == 0) s_w[wv] = W;
@@ -1033,16 +1197,17 @@ __device__ __forceinline__ void finalize_body(const FinalArgs &a, int x, int g, 
   }
 }
 
-template <int D, int G, int MODE, bool EVID>
+template <int D, int G, int MODE, bool EVID, bool KEYS = false>
 __global__ __launch_bounds__(kThreads) void finalize_kernel(FinalArgs a) {
-  finalize_body<D, G, MODE, EVID>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+  finalize_body<D, G, MODE, EVID, KEYS>(a, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // Slow and fast finalize blocks of one decode step in a single grid: the
 // slow pairs' evidence blocks, their combine blocks, then the fast combine
 // blocks (G x Hkv x fast sequences); with PEND it ends with the pending
-// selection's pick pass.
-template <int D, int G, bool PEND>
+// selection's pick pass; with KEYS the slow share's evidence blocks run its
+// own selection's key pass.
+template <int D, int G, bool PEND, bool KEYS = false>
 __global__ __launch_bounds__(kThreads) void cofinal_kernel(FinalArgs s, FinalArgs f, int s_gx, int f_gx,
                                                            int Hkv, int ns, SelectLaunch pend, int np) {
   int id = blockIdx.x;
@@ -1058,10 +1223,10 @@ __global__ __launch_bounds__(kThreads) void cofinal_kernel(FinalArgs s, FinalArg
     // the evidence blocks (the longest) are dispatched first
     const int ne = s_gx - G, pairs = ns / s_gx;
     if (id < ne * pairs) {
-      finalize_body<D, G, MODE_SLOW, true>(s, G + id % ne, (id / ne) % Hkv, id / (ne * Hkv));
+      finalize_body<D, G, MODE_SLOW, true, KEYS>(s, G + id % ne, (id / ne) % Hkv, id / (ne * Hkv));
     } else {
       id -= ne * pairs;
-      finalize_body<D, G, MODE_SLOW, true>(s, id % G, (id / G) % Hkv, id / (G * Hkv));
+      finalize_body<D, G, MODE_SLOW, true, KEYS>(s, id % G, (id / G) % Hkv, id / (G * Hkv));
     }
   } else {
     id -= ns;
@@ -1096,6 +1261,13 @@ PartialArgs partial_args(const AttnLaunch &a) {
   p.n_sink = a.n_sink; p.window = a.window;
   p.qscale = kLog2e / sqrtf((float)D);
   p.nsum = a.nsum;
+  p.wpart = a.wpart;
+  p.nnext = a.nnext;
+  p.sel_meta = a.sel_meta;
+  p.sel_ghist = a.sel_ghist;
+  p.nsp = a.plan.splits;
+  p.norm_coef = a.norm_coef;
+  p.pos_tau = a.pos_tau;
   p.ck = a.ck;
   p.cv = a.cv;
   p.pe = a.part_by_entry ? 1 : 0;
@@ -1114,6 +1286,13 @@ FinalArgs final_args(const AttnLaunch &a) {
   f.nsum = a.nsum; f.key_norm = a.key_norm; f.norm_coef = a.norm_coef; f.pos_tau = a.pos_tau;
   f.sel_wsum = a.sel_wsum; f.sel_meta = a.sel_meta; f.sel_ghist = a.sel_ghist; f.selP = a.selP;
   f.pe = a.part_by_entry ? 1 : 0;
+  f.nstat = (a.nsum != nullptr || a.stats) ? a.kv.nstat : nullptr;
+  if (a.stats && a.keysel != nullptr) {
+    f.keys = 1;
+    f.wpart = a.wpart;
+    f.nnext = a.nnext;
+    f.sel = *a.keysel;
+  }
   return f;
 }
 
@@ -1142,7 +1321,10 @@ hipError_t slow_t(const AttnLaunch &a_in, hipStream_t st) {
   }
   const PartialArgs p = partial_args<D>(a);
   dim3 grid(a.plan.splits, a.Hkv, a.batch_n);
-  if (side)
+  if (a.stats && (!a.evidence || !a.keysel || a.nsum)) return hipErrorInvalidValue;
+  if (a.stats)
+    hipLaunchKernelGGL((partial_kernel<D, G, PAGED, MODE_SLOW, true, true>), grid, dim3(kThreads), 0, st, p);
+  else if (side)
     hipLaunchKernelGGL((partial_kernel<D, G, PAGED, MODE_SLOW, true>), grid, dim3(kThreads), 0, st, p);
   else
     hipLaunchKernelGGL((partial_kernel<D, G, PAGED, MODE_SLOW, false>), grid, dim3(kThreads), 0, st, p);
@@ -1151,7 +1333,9 @@ hipError_t slow_t(const AttnLaunch &a_in, hipStream_t st) {
 
   const FinalArgs f = final_args(a);
   dim3 g2(slow_final_blocks(a, G), a.Hkv, a.batch_n);
-  if (a.evidence)
+  if (a.evidence && f.keys)
+    hipLaunchKernelGGL((finalize_kernel<D, G, MODE_SLOW, true, true>), g2, dim3(kThreads), 0, st, f);
+  else if (a.evidence)
     hipLaunchKernelGGL((finalize_kernel<D, G, MODE_SLOW, true>), g2, dim3(kThreads), 0, st, f);
   else
     hipLaunchKernelGGL((finalize_kernel<D, G, MODE_SLOW, false>), g2, dim3(kThreads), 0, st, f);
@@ -1273,6 +1457,8 @@ hipError_t step_t(const AttnLaunch &sa_in, const AttnLaunch &fa_in, hipStream_t 
   const PartialArgs ps = partial_args<D>(sa), pf = partial_args<D>(fa);
   const FinalArgs fs = final_args(sa), ff = final_args(fa);
   hipError_t e;
+  if (pend && sa.stats) return hipErrorInvalidValue;  // one selection's key pass per grid
+  if (sa.stats && (!sa.evidence || !sa.keysel || sa.nsum)) return hipErrorInvalidValue;
   if (pend) {
     const int np = pend->ws.P * pend->H * pend->batch_n;
     hipLaunchKernelGGL((copartial_kernel<D, G, PAGED, true>), dim3(np + ns + nf), dim3(kThreads), 0, st, ps,
@@ -1283,11 +1469,19 @@ hipError_t step_t(const AttnLaunch &sa_in, const AttnLaunch &fa_in, hipStream_t 
     return hipGetLastError();
   }
   if (ns + nf > 0) {
-    hipLaunchKernelGGL((copartial_kernel<D, G, PAGED, false>), dim3(ns + nf), dim3(kThreads), 0, st, ps, pf,
-                       sa.plan.splits, fa.plan.splits, sa.Hkv, ns, SelectLaunch{}, 0);
+    if (sa.stats)
+      hipLaunchKernelGGL((copartial_kernel<D, G, PAGED, false, true>), dim3(ns + nf), dim3(kThreads), 0, st, ps,
+                         pf, sa.plan.splits, fa.plan.splits, sa.Hkv, ns, SelectLaunch{}, 0);
+    else
+      hipLaunchKernelGGL((copartial_kernel<D, G, PAGED, false>), dim3(ns + nf), dim3(kThreads), 0, st, ps, pf,
+                         sa.plan.splits, fa.plan.splits, sa.Hkv, ns, SelectLaunch{}, 0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((cofinal_kernel<D, G, false>), dim3(ms + mf), dim3(kThreads), 0, st, fs, ff, sgx, G,
-                       sa.Hkv, ms, SelectLaunch{}, 0);
+    if (fs.keys)
+      hipLaunchKernelGGL((cofinal_kernel<D, G, false, true>), dim3(ms + mf), dim3(kThreads), 0, st, fs, ff, sgx,
+                         G, sa.Hkv, ms, SelectLaunch{}, 0);
+    else
+      hipLaunchKernelGGL((cofinal_kernel<D, G, false>), dim3(ms + mf), dim3(kThreads), 0, st, fs, ff, sgx, G,
+                         sa.Hkv, ms, SelectLaunch{}, 0);
   }
   return hipGetLastError();
 }
@@ -1429,6 +1623,15 @@ hipError_t launch_append(const AttnLaunch &a, const uint16_t *k_new, const uint1
   else if (a.d == 64) { if (a.paged) SFI_APPEND(64, true); else SFI_APPEND(64, false); }
   else return hipErrorInvalidValue;
 #undef SFI_APPEND
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.kv.nstat == nullptr) return e;
+  const dim3 g2(a.Hkv, a.batch_n);
+  if (a.d == 128)
+    hipLaunchKernelGGL(norm_add_kernel<128>, g2, dim3(64), 0, st, a.kv.nstat, a.seq_len, a.batch_ids, a.B, a.Hkv,
+                       a.max_len, k_new, T);
+  else
+    hipLaunchKernelGGL(norm_add_kernel<64>, g2, dim3(64), 0, st, a.kv.nstat, a.seq_len, a.batch_ids, a.B, a.Hkv,
+                       a.max_len, k_new, T);
   return hipGetLastError();
 }
 

@@ -172,4 +172,9 @@ hipError_t launch_select(const SelectLaunch &a, hipStream_t st) {
   return hipGetLastError();
 }
 
+hipError_t launch_pick(const SelectLaunch &a, hipStream_t st) {
+  hipLaunchKernelGGL(pick_kernel, dim3(a.ws.P, a.H, a.batch_n), dim3(kT), 0, st, a);
+  return hipGetLastError();
+}
+
 }  // namespace sfi

@@ -160,16 +160,81 @@ __device__ __forceinline__ int composite_index(unsigned long long c) {
   return (int)(0xFFFFFFFFu - (uint32_t)(c & 0xFFFFFFFFull));
 }
 
+// The key pass of chunk p of a row once its scores are known: s[i] is the
+// score of key jj[i] (any assignment of the chunk's keys to threads; the
+// candidates are the keys in [r.lo, r.hi)).  Order-preserving 32-bit keys,
+// their bucket histogram in LDS merged into the row histogram, the chunk's
+// cumulative bucket counts and its bucket-sorted run of (key, inverted
+// index) composites.  Every thread of the workgroup calls it.
+__device__ __forceinline__ void keys_core(const SelectLaunch &a, const RowGeo &r, int p, const float (&s)[kPT],
+                                          const int (&jj)[kPT]) {
+  __shared__ unsigned hist[kBins1];
+  __shared__ unsigned long long s_sorted[kCH];
+  __shared__ int s_wave[kTW];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kBins1; i += kT) hist[i] = 0u;
+  __syncthreads();
+  uint32_t key[kPT];
+#pragma unroll
+  for (int i = 0; i < kPT; ++i) {
+    key[i] = (jj[i] >= r.lo && jj[i] < r.hi) ? float_key(s[i]) : 0u;
+    if (key[i]) atomicAdd(&hist[key[i] >> (32 - kD1)], 1u);
+  }
+  __syncthreads();
+  // Cumulative counts in descending bucket order: cum[b] = keys in buckets
+  // >= b.  Thread t owns buckets 16 t .. 16 t + 15.
+  uint32_t c[kBPT];
+  int tot = 0;
+#pragma unroll
+  for (int i = 0; i < kBPT; ++i) {
+    c[i] = hist[kBPT * tid + i];
+    tot += (int)c[i];
+  }
+  // Merge the counts into the row histogram first: the atomics complete
+  // while the rest of the pass runs instead of after it.
+  uint32_t *h1 = a.ws.ghist + r.row * kBins1 + kBPT * tid;
+#pragma unroll
+  for (int i = 0; i < kBPT; ++i)
+    if (c[i]) atomicAdd(&h1[i], c[i]);
+  int total;
+  const int below = block_exscan<kTW>(tot, s_wave, &total);  // keys in lower buckets
+  int run = total - below - tot;                              // keys in higher buckets
+  uint32_t cum[kBPT];
+#pragma unroll
+  for (int i = kBPT - 1; i >= 0; --i) {
+    run += (int)c[i];
+    cum[i] = (uint32_t)run;
+  }
+  // bucket b's first slot in the descending layout is cum[b] - count[b]
+#pragma unroll
+  for (int i = 0; i < kBPT; ++i) hist[kBPT * tid + i] = cum[i] - c[i];
+  uint4 *cd = reinterpret_cast<uint4 *>(a.ws.cum + (r.row * a.ws.P + p) * kBins1 + kBPT * tid);
+  cd[0] = make_uint4(cum[0] | cum[1] << 16, cum[2] | cum[3] << 16, cum[4] | cum[5] << 16,
+                     cum[6] | cum[7] << 16);
+  cd[1] = make_uint4(cum[8] | cum[9] << 16, cum[10] | cum[11] << 16, cum[12] | cum[13] << 16,
+                     cum[14] | cum[15] << 16);
+  __syncthreads();
+  // bucket sort in LDS, then one coalesced write of the chunk's sorted run
+#pragma unroll
+  for (int i = 0; i < kPT; ++i) {
+    if (key[i]) {
+      const unsigned slot = atomicAdd(&hist[key[i] >> (32 - kD1)], 1u);
+      s_sorted[slot] = composite(key[i], jj[i]);
+    }
+  }
+  __syncthreads();
+  unsigned long long *so = a.ws.sorted + (r.row * a.ws.P + p) * kCH;
+  for (int i = tid; i < total; i += kT) so[i] = s_sorted[i];
+}
+
+
 // --------------------------------------------------------------- 3. keys
 // Workgroup (chunk p, head row h, batch entry z) of the key pass.
 // REFINE = false compiles out Soft-NMS and exclusivity (a call with both
 // off runs that variant).
 template <bool FUSED, bool REFINE = true>
 __device__ __forceinline__ void keys_body(const SelectLaunch &a, int p, int h, int z) {
-  __shared__ unsigned hist[kBins1];
-  __shared__ unsigned long long s_sorted[kCH];
   __shared__ double s_red[kTW];
-  __shared__ int s_wave[kTW];
   RowGeo r;
   if (!row_geo(a, h, z, r)) return;
   const int j0 = p * kCH;
@@ -220,7 +285,6 @@ __device__ __forceinline__ void keys_body(const SelectLaunch &a, int p, int h, i
     const int Pn = (r.n + kCH - 1) / kCH;
     double W = 0.0;
     for (int q = tid; q < Pn; q += kT) W += a.ws.wsum[r.row * a.ws.P + q];
-    for (int i = tid; i < kBins1; i += kT) hist[i] = 0u;
     W = block_sum_d<kTW>(W, s_red);
     cf = 1.0f - a.lambda;
     cr = W > 0.0 ? (float)((double)a.lambda / W) : 0.f;
@@ -245,8 +309,6 @@ __device__ __forceinline__ void keys_body(const SelectLaunch &a, int p, int h, i
   } else {
     const float *sc = a.score + r.row * a.ld;
     load_chunk(sc, j0, r.span, aligned16(sc) && (a.ld & 3) == 0, s);
-    for (int i = tid; i < kBins1; i += kT) hist[i] = 0u;
-    __syncthreads();
   }
   if (p >= r.nch) return;  // no candidates in this chunk
   // exclusivity: the first round clears this chunk's per-key counts (the
@@ -356,58 +418,10 @@ __device__ __forceinline__ void keys_body(const SelectLaunch &a, int p, int h, i
   }
   }  // REFINE
 
-  uint32_t key[kPT];
+  int jj[kPT];
 #pragma unroll
-  for (int i = 0; i < kPT; ++i) {
-    const int j = key_pos(j0, i);
-    key[i] = (j >= r.lo && j < r.hi) ? float_key(s[i]) : 0u;
-    if (key[i]) atomicAdd(&hist[key[i] >> (32 - kD1)], 1u);
-  }
-  __syncthreads();
-  // Cumulative counts in descending bucket order: cum[b] = keys in buckets
-  // >= b.  Thread t owns buckets 16 t .. 16 t + 15.
-  uint32_t c[kBPT];
-  int tot = 0;
-#pragma unroll
-  for (int i = 0; i < kBPT; ++i) {
-    c[i] = hist[kBPT * tid + i];
-    tot += (int)c[i];
-  }
-  // Merge the counts into the row histogram first: the atomics complete
-  // while the rest of the pass runs instead of after it.
-  uint32_t *h1 = a.ws.ghist + r.row * kBins1 + kBPT * tid;
-#pragma unroll
-  for (int i = 0; i < kBPT; ++i)
-    if (c[i]) atomicAdd(&h1[i], c[i]);
-  int total;
-  const int below = block_exscan<kTW>(tot, s_wave, &total);  // keys in lower buckets
-  int run = total - below - tot;                              // keys in higher buckets
-  uint32_t cum[kBPT];
-#pragma unroll
-  for (int i = kBPT - 1; i >= 0; --i) {
-    run += (int)c[i];
-    cum[i] = (uint32_t)run;
-  }
-  // bucket b's first slot in the descending layout is cum[b] - count[b]
-#pragma unroll
-  for (int i = 0; i < kBPT; ++i) hist[kBPT * tid + i] = cum[i] - c[i];
-  uint4 *cd = reinterpret_cast<uint4 *>(a.ws.cum + (r.row * a.ws.P + p) * kBins1 + kBPT * tid);
-  cd[0] = make_uint4(cum[0] | cum[1] << 16, cum[2] | cum[3] << 16, cum[4] | cum[5] << 16,
-                     cum[6] | cum[7] << 16);
-  cd[1] = make_uint4(cum[8] | cum[9] << 16, cum[10] | cum[11] << 16, cum[12] | cum[13] << 16,
-                     cum[14] | cum[15] << 16);
-  __syncthreads();
-  // bucket sort in LDS, then one coalesced write of the chunk's sorted run
-#pragma unroll
-  for (int i = 0; i < kPT; ++i) {
-    if (key[i]) {
-      const unsigned slot = atomicAdd(&hist[key[i] >> (32 - kD1)], 1u);
-      s_sorted[slot] = composite(key[i], key_pos(j0, i));
-    }
-  }
-  __syncthreads();
-  unsigned long long *so = a.ws.sorted + (r.row * a.ws.P + p) * kCH;
-  for (int i = tid; i < total; i += kT) so[i] = s_sorted[i];
+  for (int i = 0; i < kPT; ++i) jj[i] = key_pos(j0, i);
+  keys_core(a, r, p, s, jj);
 }
 
 // Bin of an nb-bin histogram (nb <= kBins2, highest bin = largest values)

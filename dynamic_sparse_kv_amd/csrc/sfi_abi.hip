@@ -43,8 +43,10 @@ sfi_status check_kv(const sfi_kv *kv, KVView *view, bool *paged) {
   if (kv->k_new && (!aligned16(kv->k_new) || !aligned16(kv->v_new))) return SFI_ERR_RANGE;
   view->k = kv->k;
   view->v = kv->v;
+  if (kv->norm_stats && !aligned(kv->norm_stats, 8)) return SFI_ERR_RANGE;
   view->k_new = kv->k_new;
   view->v_new = kv->v_new;
+  view->nstat = kv->norm_stats;
   view->Hkv = kv->Hkv;
   view->page_table = kv->page_table;
   if (kv->page_table) {
@@ -118,6 +120,13 @@ struct SelWs {
   int P, ld32;
   size_t ghist, cum, sorted, nsum, wsum, meta, ecnt, ebits, eghist, total;
 };
+
+// Prior workspace of the calls that form the selector's prior (fp64): the
+// per-split key-norm sums [B*Hkv][stride][2], the per-split prior-weight
+// sums [B*Hkv][stride] and the updated key-norm statistics [B*Hkv][2].
+size_t prior_ws_bytes(const sfi_kv *kv, int stride) {
+  return align_up((size_t)kv->B * kv->Hkv * (stride * 3 + 2) * sizeof(double));
+}
 
 SelWs select_ws(int B, int H, int max_seq_len) {
   SelWs w{};
@@ -438,8 +447,7 @@ size_t sfi_decode_step_select_workspace_bytes(const sfi_kv *kv, int32_t sel_k, i
   if (kv->max_seq_len > kSelMaxLen) return 0;
   const SlowWs sw = slow_ws(kv);
   return sw.total + fast_ws(kv, sel_k, n_sink, window).total +
-         select_ws(kv->B, kv->Hkv, kv->max_seq_len).total +
-         align_up((size_t)kv->B * kv->Hkv * sw.stride * 2 * sizeof(double));
+         select_ws(kv->B, kv->Hkv, kv->max_seq_len).total + prior_ws_bytes(kv, sw.stride);
 }
 
 sfi_status sfi_decode_step_select(const sfi_kv *kv, const sfi_select_params *p,
@@ -470,7 +478,7 @@ sfi_status sfi_decode_step_select(const sfi_kv *kv, const sfi_select_params *p,
   const SlowWs sw = slow_ws(kv);
   const FastWs fw = fast_ws(kv, p->k, p->n_sink, p->window);
   const SelWs ew = select_ws(kv->B, kv->Hkv, kv->max_seq_len);
-  const size_t nsum_bytes = align_up((size_t)kv->B * kv->Hkv * sw.stride * 2 * sizeof(double));
+  const size_t nsum_bytes = prior_ws_bytes(kv, sw.stride);
   if (!ws) return SFI_ERR_NULL;
   if (!aligned(ws, kAlign)) return SFI_ERR_RANGE;
   if (ws_bytes < sw.total + fw.total + ew.total + nsum_bytes) return SFI_ERR_WORKSPACE;
@@ -487,6 +495,24 @@ sfi_status sfi_decode_step_select(const sfi_kv *kv, const sfi_select_params *p,
   sa.sel_meta = carve<SelRowMeta>(ws_sel, ew.meta);
   sa.sel_ghist = carve<uint32_t>(ws_sel, ew.ghist);
   sa.selP = ew.P;
+  // the prior from the key-norm statistics: the key pass moves into the
+  // step's finalize and the selection ends with its pick pass
+  SelectLaunch keysel{};
+  bool stats = false;
+  if (n_slow > 0 && view.nstat != nullptr && kv->norm_stats_valid == 1) {
+    if ((s = select_launch(p, slow_ids, n_slow, kv->seq_len, kv->B, kv->Hkv, kv->max_seq_len, evidence,
+                           key_norm, ld, sel_idx, sel_count, fused_out, ws_sel, ew.total, true, &keysel)) !=
+        SFI_OK)
+      return s;
+    stats = keysel.nms_radius == 0 && keysel.excl_beta == 0.f;  // the plain key pass only
+  }
+  if (stats) {
+    sa.stats = true;
+    sa.nsum = nullptr;
+    sa.wpart = nsum + (size_t)kv->B * kv->Hkv * sw.stride * 2;
+    sa.nnext = sa.wpart + (size_t)kv->B * kv->Hkv * sw.stride;
+    sa.keysel = &keysel;
+  }
   const AttnLaunch fa = fast_launch(kv, view, paged, fw, ws_fast, fast_ids, n_fast, q, out, sel_idx,
                                     sel_count, kv->Hkv, p->k, p->n_sink, p->window);
   const hipStream_t st = static_cast<hipStream_t>(stream);
@@ -496,6 +522,7 @@ sfi_status sfi_decode_step_select(const sfi_kv *kv, const sfi_select_params *p,
   else e = launch_step(sa, fa, st);
   if (e != hipSuccess) return SFI_ERR_HIP;
   if (n_slow == 0) return SFI_OK;
+  if (stats) return launch_pick(keysel, st) == hipSuccess ? SFI_OK : SFI_ERR_HIP;
   return select_impl(p, slow_ids, n_slow, kv->seq_len, kv->B, kv->Hkv, kv->max_seq_len, evidence,
                      key_norm, ld, sel_idx, sel_count, fused_out, ws_sel, ew.total, stream, true);
 }
@@ -536,7 +563,7 @@ sfi_status sfi_decode_layer_step(const sfi_kv *kv, const sfi_select_params *p, c
   const SlowWs sw = slow_ws(kv);
   const FastWs fw = fast_ws(kv, p->k, p->n_sink, p->window);
   const SelWs ew = select_ws(kv->B, kv->Hkv, kv->max_seq_len);
-  const size_t nsum_bytes = align_up((size_t)kv->B * kv->Hkv * sw.stride * 2 * sizeof(double));
+  const size_t nsum_bytes = prior_ws_bytes(kv, sw.stride);
   if (!ws) return SFI_ERR_NULL;
   if (!aligned(ws, kAlign)) return SFI_ERR_RANGE;
   if (ws_bytes < sw.total + fw.total + ew.total + nsum_bytes) return SFI_ERR_WORKSPACE;

@@ -97,6 +97,9 @@ struct KVView {
   // that owns that row's list position stores it into the cache.
   const uint16_t *k_new;
   const uint16_t *v_new;
+  // Key-norm statistics [B][Hkv][2] (sum and sum of squares of the norms of
+  // the cached rows, fp64), or null.
+  double *nstat;
 };
 
 template <int D, bool PAGED>
@@ -156,6 +159,26 @@ __device__ __forceinline__ void prior_consts(double s1, double s2, int n, float 
 
 __device__ __forceinline__ uint4 ldg16(const uint16_t *p) {
   return *reinterpret_cast<const uint4 *>(p);
+}
+
+// Sum of squares of 8 bf16 values (one 16-byte slice of a row).
+__device__ __forceinline__ float slice_sumsq(uint4 t) {
+  float ss = dot2_bf16(t.x, t.x, 0.f);
+  ss = dot2_bf16(t.y, t.y, ss);
+  ss = dot2_bf16(t.z, t.z, ss);
+  return dot2_bf16(t.w, t.w, ss);
+}
+
+// Euclidean norm of a row of D bf16 values from its 16-byte slices held by
+// lanes 0 .. D/8 - 1 of the wave (t; other lanes pass anything): a sum over
+// the wave, so every lane returns it.  The one formula the key-norm
+// statistics use for a row they add.
+template <int D>
+__device__ __forceinline__ float wave_row_norm(uint4 t) {
+  float ss = ((threadIdx.x & 63) < D / 8) ? slice_sumsq(t) : 0.f;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+  return __builtin_amdgcn_sqrtf(ss);
 }
 
 // 16-byte load marked non-temporal: for rows streamed once per call (dense

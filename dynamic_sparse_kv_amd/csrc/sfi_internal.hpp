@@ -54,6 +54,7 @@ SplitPlan plan_rows(long long L, int stride, long long R, int max_chunk);
 int device_cu_count();
 
 struct SelRowMeta;
+struct SelectLaunch;
 
 struct AttnLaunch {
   KVView kv;
@@ -90,6 +91,15 @@ struct AttnLaunch {
   SelRowMeta *sel_meta;  // [B*Hkv]
   uint32_t *sel_ghist;   // [B*Hkv][4096]
   int selP;
+  // Prior from the key-norm statistics kv.nstat instead of the per-split
+  // sums (stats, nsum null): the partial kernel forms the row constants,
+  // the splits' prior-weight sums wpart [B*Hkv][stride] and the updated
+  // statistics nnext [B*Hkv][2], and the finalize stores those and runs the
+  // key pass of keysel (non-null with stats) on the fused scores.
+  bool stats;
+  double *wpart;
+  double *nnext;
+  const SelectLaunch *keysel;
   // fast step: compact copy of the selected rows [B][Hkv][sel_k][d] (or null)
   const uint16_t *ck, *cv;
   // partial buffers indexed by batch entry (rows [batch_n][Hq][stride])
@@ -175,6 +185,8 @@ struct SelectLaunch {
 };
 
 hipError_t launch_select(const SelectLaunch &a, hipStream_t st);
+// The pick pass alone, for a selection whose key pass already ran.
+hipError_t launch_pick(const SelectLaunch &a, hipStream_t st);
 
 struct VerifyLaunch {
   KVView kv;

@@ -79,13 +79,31 @@ class DecodePlan:
         return None if self.n_fast[s] == self.B else self.fast_ids[s]
 
 
+def stats_prior_steps(plan: DecodePlan) -> np.ndarray:
+    """Steps of a run whose every row comes through the library's appends
+    (from a cache that holds the prefill only) at which the key-norm
+    statistics are current for every slow sequence, so the combined
+    step-and-select call may form its prior from them: those after each of
+    their slow sequences' first slow step.  The order of SFIDecoder.step's
+    own bookkeeping, for callers that issue the calls themselves."""
+    covered = np.full(plan.B, -1, dtype=np.int64)
+    use = np.zeros(plan.steps, dtype=bool)
+    for s in range(plan.steps):
+        lens = plan.seq_len_host[s].astype(np.int64)
+        b = plan.slow[s]
+        use[s] = plan.n_slow[s] > 0 and bool(np.all(covered[b] == lens[b] - 1))
+        covered = np.where((covered == lens - 1) | b, lens, -1)
+    return use
+
+
 class SFIDecoder:
     """Slow/fast decode of one attention layer over a resident KV cache."""
 
     def __init__(self, K, V, Hq: int, max_len: int, *, n_sink: int, window: int, k: int,
                  lam: float, norm_coef: float = 0.5, pos_tau: float = 1024.0,
                  page_table=None, page_size: int = 0, keep_fused: bool = False,
-                 nms_radius: int = 0, nms_alpha: float = 0.0, excl_beta: float = 0.0):
+                 nms_radius: int = 0, nms_alpha: float = 0.0, excl_beta: float = 0.0,
+                 norm_stats: bool = True):
         dev = K.device
         self.dev = dev
         self.K, self.V = K, V
@@ -101,6 +119,16 @@ class SFIDecoder:
         self.n_sink, self.window, self.k = n_sink, window, k
         self._dummy_len = torch.full((B,), self.max_len, dtype=torch.int32, device=dev)
         self.kv = sfi.make_kv(K, V, self._dummy_len, Hq, self.max_len, page_table, page_size)
+        # Key-norm statistics of the cache rows, kept current by every call
+        # that appends rows; _stats_len[b] is the row count they cover for
+        # sequence b as far as the host can tell (-1: unknown), so a planned
+        # step knows when a combined step-and-select call may form the prior
+        # from them.
+        self.nstat = None
+        self._stats_len = np.full(B, -1, dtype=np.int64)
+        if norm_stats:
+            self.nstat = torch.zeros((B, Hkv, 2), dtype=torch.float64, device=dev)
+            self.kv.norm_stats = self.nstat.data_ptr()
         self.params = sfi.select_params(sfi.SFI_SCORE_FUSED, lam, k, n_sink, window, norm_coef, pos_tau,
                                         nms_radius=nms_radius, nms_alpha=nms_alpha,
                                         excl_beta=excl_beta)
@@ -138,8 +166,13 @@ class SFIDecoder:
     # new_rows = (k_new, v_new), each [B][Hkv][d] bf16 (or [B][1][Hkv][d]):
     # the call also appends each listed sequence's row at cache row
     # seq_len - 1 (the fused append of the sfi_kv description).
-    def _kvx(self, new_rows):
-        return self.kv if new_rows is None else sfi.with_new_rows(self.kv, new_rows[0], new_rows[1])
+    def _kvx(self, new_rows, stats_valid: bool = False):
+        kv = self.kv if new_rows is None else sfi.with_new_rows(self.kv, new_rows[0], new_rows[1])
+        if stats_valid:
+            if self.nstat is None:
+                raise ValueError("this decoder keeps no key-norm statistics")
+            kv = sfi.with_norm_stats(kv, self.nstat, True)
+        return kv
 
     def slow(self, q, seq_len, batch_ids, batch_n: int, stream=None, select: bool = True, out=None,
              k_seq=None, new_rows=None):
@@ -211,14 +244,17 @@ class SFIDecoder:
             self.slow_select_only(self.kv.seq_len, slow_ids, n_slow, stream, k_seq=k_seq)
 
     def step_select(self, q, seq_len, slow_ids, n_slow: int, fast_ids, n_fast: int, stream=None,
-                    out=None, k_seq=None, new_rows=None):
+                    out=None, k_seq=None, new_rows=None, use_stats: bool = False):
         """One call for the step and the slow sequences' new selections
         (sfi_decode_step_select): the slow step forms the selector's prior
-        statistics, so the selection runs only its key and pick passes."""
+        statistics, so the selection runs only its key and pick passes.
+        use_stats vouches that the key-norm statistics are current for the
+        slow sequences (rows before this call's own): the prior then comes
+        from them and the key pass runs inside the step's finalize."""
         self.kv.seq_len = seq_len.data_ptr() if torch.is_tensor(seq_len) else seq_len
         self.params.k_per_seq = None if k_seq is None else k_seq.data_ptr()
         try:
-            sfi.sfi_decode_step_select(self._kvx(new_rows), self.params, slow_ids, n_slow, fast_ids, n_fast, q,
+            sfi.sfi_decode_step_select(self._kvx(new_rows, use_stats), self.params, slow_ids, n_slow, fast_ids, n_fast, q,
                                        self.out if out is None else out, self.evidence, self.key_norm,
                                        self.ld, self.sel_idx, self.sel_count, self.fused, self.ws_stepsel,
                                        self.ws_stepsel_bytes, stream)
@@ -233,6 +269,7 @@ class SFIDecoder:
         deferred.  Returns it (active when step s has slow sequences); pass it
         to the next layer's call, or to sfi_run_deferred after the last.
         new_kv as in step(): the call appends the rows itself."""
+        self._note_stats(plan, s, new_kv is not None, ns_refresh=int(plan.n_slow[s]) > 0)
         ks = None if plan.k_seq is None else plan.k_seq[s]
         ns, nf = int(plan.n_slow[s]), int(plan.n_fast[s])
         self.kv.seq_len = plan.seq_len[s].data_ptr()
@@ -247,6 +284,28 @@ class SFIDecoder:
         finally:
             self.params.k_per_seq = None
         return own
+
+    def _stats_current(self, plan: DecodePlan, s: int) -> bool:
+        """Whether the statistics cover exactly the rows before step s for
+        every slow sequence of step s."""
+        if self.nstat is None or plan.n_slow[s] == 0:
+            return False
+        b = plan.slow[s]
+        return bool(np.all(self._stats_len[b] == plan.seq_len_host[s][b].astype(np.int64) - 1))
+
+    def _note_stats(self, plan: DecodePlan, s: int, appended: bool, ns_refresh: bool):
+        """Host record of the statistics after step s: sequences whose rows
+        the step appended through the library keep (or, for the slow
+        sequences of a prior-forming call, get) exact statistics; rows that
+        appear any other way leave them unknown."""
+        lens = plan.seq_len_host[s].astype(np.int64)
+        if not appended:
+            self._stats_len[:] = -1
+            return
+        ok = self._stats_len == lens - 1
+        if ns_refresh:
+            ok |= plan.slow[s]
+        self._stats_len = np.where(ok, lens, -1)
 
     def _new_event(self):
         # events of earlier runs that have completed are released here
@@ -289,8 +348,12 @@ class SFIDecoder:
                 nr = (new_kv[0][s], new_kv[1][s])
             else:
                 self.append(new_kv[0][s], new_kv[1][s], sl, None, self.B, stream)
-        if co and ns and fused_select:
-            self.step_select(q, sl, sids, ns, fids, nf, stream, out=out, k_seq=ks, new_rows=nr)
+        combined = bool(co and ns and fused_select)
+        use_stats = combined and new_kv is not None and self._stats_current(plan, s)
+        self._note_stats(plan, s, new_kv is not None, ns_refresh=combined)
+        if combined:
+            self.step_select(q, sl, sids, ns, fids, nf, stream, out=out, k_seq=ks, new_rows=nr,
+                             use_stats=use_stats)
             return
         if co and ns and nf:
             self.co_step(q, sl, sids, ns, fids, nf, stream, out=out, k_seq=ks, new_rows=nr)

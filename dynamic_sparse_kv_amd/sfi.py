@@ -44,6 +44,7 @@ class sfi_kv(ctypes.Structure):
         ("B", _c_int), ("Hq", _c_int), ("Hkv", _c_int), ("d", _c_int),
         ("cap", _c_int), ("max_seq_len", _c_int),
         ("k_new", _vp), ("v_new", _vp),
+        ("norm_stats", _vp), ("norm_stats_valid", _c_int),
     ]
 
 
@@ -201,6 +202,18 @@ def with_new_rows(kv: sfi_kv, k_new, v_new) -> sfi_kv:
     x = sfi_kv()
     ctypes.pointer(x)[0] = kv
     x.k_new, x.v_new = _ptr(k_new), _ptr(v_new)
+    return x
+
+
+def with_norm_stats(kv: sfi_kv, norm_stats, valid: bool) -> sfi_kv:
+    """A copy of kv that keeps the key-norm statistics norm_stats ([B][Hkv][2]
+    float64: sum and sum of squares of the cached rows' key norms) current;
+    valid = True vouches that they are current for the call's slow sequences,
+    so a combined step-and-select call forms the prior from them."""
+    x = sfi_kv()
+    ctypes.pointer(x)[0] = kv
+    x.norm_stats = _ptr(norm_stats)
+    x.norm_stats_valid = 1 if valid else 0
     return x
 
 

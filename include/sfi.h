@@ -88,7 +88,26 @@ typedef enum {
  * writable): the same results as sfi_append_kv with T = 1 followed by the
  * step, without the extra launch.  Sequences a call does not list are not
  * appended.  sfi_append_kv, sfi_verify_* and sfi_slow_step_window return
- * SFI_ERR_RANGE when they are set; sfi_compact_selected ignores them. */
+ * SFI_ERR_RANGE when they are set; sfi_compact_selected ignores them.
+ *
+ * Key-norm statistics [SFI technical summary, section 3.B: the prior
+ * standardises each key's norm by the mean and spread of the row's key
+ * norms]: norm_stats ([B][Hkv][2] fp64, 8-byte aligned, device) holds for
+ * every (sequence b, kv head g) the sum and the sum of squares of the
+ * L2 norms of the cache rows written so far (rows j < seq_len[b], less a
+ * row that a fused append is about to write).  Set, the calls keep it
+ * current: step calls add the norm of each fused-append row, sfi_append_kv
+ * adds its rows' norms, and the calls that form the selector's prior
+ * (sfi_decode_step_select, sfi_decode_layer_step) overwrite the sums of
+ * their slow sequences with the exact sums of their pass (their fused rows
+ * included).  Rows written by other means leave it stale.  With
+ * norm_stats_valid = 1 as well, the caller vouches that the sums are
+ * current for every slow sequence of the call, and sfi_decode_step_select
+ * then forms the prior from them: its attention pass computes the prior
+ * weights and its finalize runs the selection's key pass, one launch fewer
+ * (Soft-NMS and exclusivity keep the separate passes).  The norms are fp32
+ * roundings summed in fp64, so the prior matches the one formed from the
+ * pass up to rounding (near-tie keys may select differently). */
 typedef struct sfi_kv {
   const uint16_t *k;
   const uint16_t *v;
@@ -102,6 +121,8 @@ typedef struct sfi_kv {
   int32_t max_seq_len;        /* [host] */
   const uint16_t *k_new;      /* NULL, or the step's new rows [B][Hkv][d] (fused append) */
   const uint16_t *v_new;
+  double *norm_stats;         /* NULL, or [B][Hkv][2] key-norm statistics (above) */
+  int32_t norm_stats_valid;   /* [host] 1: norm_stats is current for the slow sequences */
 } sfi_kv;
 
 enum { SFI_SCORE_FUSED = 0, SFI_SCORE_RAW = 1 };
@@ -205,7 +226,8 @@ sfi_status sfi_select(const sfi_select_params *p, const int32_t *batch_ids, int3
  *   k_new, v_new  [B][T][Hkv][d] bf16 bits, 16-byte aligned.
  *   1 <= T <= max_seq_len (else SFI_ERR_RANGE).
  * Call it before the step that reads the rows, on the same stream.  Moves
- * 2 x 2 d bytes per row and kv head (read and write of K and V). */
+ * 2 x 2 d bytes per row and kv head (read and write of K and V).  With
+ * kv->norm_stats set, a second launch adds the rows' key norms to it. */
 sfi_status sfi_append_kv(const sfi_kv *kv, const int32_t *batch_ids, int32_t batch_n,
                          const uint16_t *k_new, const uint16_t *v_new, int32_t T, void *stream);
 

@@ -100,6 +100,9 @@ def test_slow_step_validation():
     assert _slow(_kv(k_new=FAKE)) == sfi.SFI_ERR_NULL
     assert _slow(_kv(k_new=FAKE, v_new=FAKE + 4)) == sfi.SFI_ERR_RANGE
     assert _slow(_kv(k_new=FAKE, v_new=FAKE), batch_n=0) == sfi.SFI_OK
+    # key-norm statistics: 8-byte aligned
+    assert _slow(_kv(norm_stats=FAKE + 4)) == sfi.SFI_ERR_RANGE
+    assert _slow(_kv(norm_stats=FAKE, norm_stats_valid=1), batch_n=0) == sfi.SFI_OK
 
 
 def test_fused_rows_refused_where_unsupported():
@@ -114,6 +117,9 @@ def test_fused_rows_refused_where_unsupported():
                                   1 << 40, None) == sfi.SFI_ERR_RANGE
     kv2 = sfi.with_new_rows(_kv(), FAKE, FAKE)
     assert (kv2.k_new, kv2.v_new, kv2.B, kv2.max_seq_len) == (FAKE, FAKE, 2, 900)
+    kv3 = sfi.with_norm_stats(kv2, FAKE, True)
+    assert (kv3.norm_stats, kv3.norm_stats_valid, kv3.k_new, kv3.B) == (FAKE, 1, FAKE, 2)
+    assert kv2.norm_stats is None and kv2.norm_stats_valid == 0
 
 
 def _select(p, B=2, H=2, max_len=900, ld=900, ws_bytes=1 << 40, **kw):

@@ -950,6 +950,145 @@ def test_layer_pipeline_matches_per_layer_calls(kdiv, nms):
     _say(f"  near-tie differences: {ties}")
 
 
+def _norm_sums(Kf, n):
+    """fp64 sum and sum of squares of the L2 norms of rows [0, n) of each
+    kv head (Kf: [Hkv][rows][d], the bf16 values as float)."""
+    nu = np.sqrt((Kf[:, :n].astype(np.float64) ** 2).sum(-1))
+    return np.stack([nu.sum(-1), (nu * nu).sum(-1)], axis=-1)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_norm_stats_prior_matches_the_pass(paged):
+    """Key-norm statistics: a prior-forming step stores the exact sums of
+    its pass, sfi_append_kv and fused appends add the new rows' norms, and a
+    step whose prior comes from the statistics (key pass in its finalize)
+    gives the same attention bits as the step that forms the prior from its
+    pass, fused scores within the evidence tolerance and selections that
+    match the oracle's Top-K."""
+    _say(f"norm statistics prior, paged={paged}")
+    B, Hq, Hkv, d = 4, 32, 8, 128
+    lens = [6100, 4500, 7000, 2600]
+    cap = 7200
+    K, V = _rand_kv(B, Hkv, cap, d, seed=71, hh=30)
+    q = _rand_q((B, Hq, d), seed=72)
+    kw = dict(n_sink=4, window=256, k=300, lam=0.3, keep_fused=True)
+    if paged:
+        cfg = W.CONFIGS["ragged-paged-8k-128k"].replace(B=B, Hq=Hq, Hkv=Hkv, d=d)
+        table, npages = W.page_table(cfg, np.full(B, cap))
+        Kp, Vp = W.to_paged(K, table, npages, 16), W.to_paged(V, table, npages, 16)
+        tab = torch.from_numpy(table).to(DEV)
+        mk = lambda: SFIDecoder(Kp, Vp, Hq, cap, page_table=tab, page_size=16, **kw)
+    else:
+        mk = lambda: SFIDecoder(K, V, Hq, cap, **kw)
+    st, ex = mk(), mk()      # the statistics-prior decoder and the exact one
+    all_ids = torch.arange(B, dtype=torch.int32, device=DEV)
+    seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    # step A: every sequence slow, prior from the pass: the exact sums
+    for dec in (st, ex):
+        dec.step_select(q, seq, all_ids, B, None, 0)
+    torch.cuda.synchronize()
+    kn = st.key_norm.double().cpu().numpy()
+    got = st.nstat.cpu().numpy()
+    for b in range(B):
+        want = np.stack([kn[b, :, : lens[b]].sum(-1), (kn[b, :, : lens[b]] ** 2).sum(-1)], -1)
+        np.testing.assert_allclose(got[b], want, rtol=1e-12)
+    np.testing.assert_array_equal(got, ex.nstat.cpu().numpy())
+    # three rows appended by sfi_append_kv, one by each step's fused append
+    g = torch.Generator(device=DEV).manual_seed(73)
+    rows = torch.randn((B, 4, Hkv, d), generator=g, device=DEV).to(torch.bfloat16)
+    vrows = torch.randn((B, 4, Hkv, d), generator=g, device=DEV).to(torch.bfloat16)
+    seq3 = seq + 3
+    before = st.nstat.clone()
+    for dec in (st, ex):
+        dec.append(rows[:, :3].contiguous(), vrows[:, :3].contiguous(), seq3, None, B)
+    torch.cuda.synchronize()
+    rb = rows.double().cpu().numpy()                          # [B][4][Hkv][d]
+    nu = np.sqrt((rb ** 2).sum(-1))                           # [B][4][Hkv]
+    add = np.stack([nu[:, :3].sum(1), (nu[:, :3] ** 2).sum(1)], -1)
+    np.testing.assert_allclose((st.nstat - before).cpu().numpy(), add, rtol=1e-5)
+    # step B: 1 and 3 slow, 0 and 2 fast, with the step's own row fused
+    seq4 = seq + 4
+    nr = (rows[:, 3].contiguous(), vrows[:, 3].contiguous())
+    slow_ids = torch.tensor([1, 3], dtype=torch.int32, device=DEV)
+    fast_ids = torch.tensor([0, 2], dtype=torch.int32, device=DEV)
+    st.step_select(q, seq4, slow_ids, 2, fast_ids, 2, new_rows=nr, use_stats=True)
+    ex.step_select(q, seq4, slow_ids, 2, fast_ids, 2, new_rows=nr)
+    torch.cuda.synchronize()
+    for t in ("out", "evidence", "key_norm"):
+        assert torch.equal(getattr(st, t).view(torch.int32), getattr(ex, t).view(torch.int32)), t
+    a, e = st.nstat.cpu().numpy(), ex.nstat.cpu().numpy()
+    np.testing.assert_allclose(a, e, rtol=1e-9)
+    for b in (0, 2):      # fast sequences: the fused row's norm added
+        np.testing.assert_allclose(a[b] - before.cpu().numpy()[b],
+                                   add[b] + np.stack([nu[b, 3], nu[b, 3] ** 2], -1), rtol=1e-5)
+    # slow sequences: selections and fused scores against the oracle, over
+    # the cache as it now stands
+    if paged:
+        Kg = torch.stack([W.gather_paged(Kp, table, b, cap) for b in range(B)])
+        Vg = torch.stack([W.gather_paged(Vp, table, b, cap) for b in range(B)])
+    else:
+        Kg, Vg = K, V
+    Kb, Vb, qb = _bits(Kg), _bits(Vg), _bits(q)
+    Kf = Kg.float().cpu().numpy()
+    sel, cnt = st.sel_idx.cpu().numpy(), st.sel_count.cpu().numpy()
+    sel_e, cnt_e = ex.sel_idx.cpu().numpy(), ex.sel_count.cpu().numpy()
+    ties = 0
+    for b in (1, 3):
+        n = lens[b] + 4
+        r = O.slow_select(qb[b], Kb[b], Vb[b], n, lam=0.3, k=300, n_sink=4, window=256)
+        np.testing.assert_allclose(a[b], _norm_sums(Kf[b], n), rtol=1e-5)
+        assert row_rel_err(st.fused[b, :, :n].cpu().numpy(), r["s"]) <= EVID_TOL
+        for g in range(Hkv):
+            ties += check_selection(sel[b, g], cnt[b, g], r["s"][g], r["lo"], r["hi"], 300)
+            ties += check_selection(sel_e[b, g], cnt_e[b, g], r["s"][g], r["lo"], r["hi"], 300)
+    _say(f"  near-tie differences: {ties}")
+
+
+def test_decode_run_with_stats_prior_vs_oracle():
+    """A decode run whose steps append their own rows: after a sequence's
+    first slow step, its later slow steps form the prior from the key-norm
+    statistics.  Every step's output, and every slow step's fused scores and
+    selection, against the oracle's decode run; the statistics at the end
+    against the sums of the cache rows' norms."""
+    _say("decode run, statistics prior")
+    cfg = W.CONFIGS["tiny-4k"].replace(B=2, steps=48)
+    K, V = W.make_kv(cfg, device=DEV)
+    starts = W.sentence_starts(cfg)
+    slow = O.schedule(starts, cfg.budget)
+    qh = W.make_queries(cfg, starts)
+    q = qh.to(DEV)
+    ctx = W.context_lengths(cfg)
+    Kb, Vb, qb = _bits(K), _bits(V), _bits(qh)
+    Kf = K.float().cpu().numpy()
+    new_kv = W.take_decode_rows(K, V, ctx, cfg.steps)
+    plan = DecodePlan(slow, ctx, DEV)
+    dec = SFIDecoder(K, V, cfg.Hq, int(ctx.max()) + cfg.steps, n_sink=cfg.n_sink, window=cfg.window,
+                     k=cfg.k, lam=cfg.lam, keep_fused=True)
+    refs = [O.decode_run(qb[:, b], Kb[b], Vb[b], int(ctx[b]), slow[:, b], lam=cfg.lam, k=cfg.k,
+                         n_sink=cfg.n_sink, window=cfg.window) for b in range(cfg.B)]
+    used, ties = 0, 0
+    for s in range(cfg.steps):
+        used += int(dec._stats_current(plan, s))
+        dec.step(plan, s, q, new_kv=new_kv)
+        torch.cuda.synchronize()
+        out = dec.out.cpu().numpy()
+        for b in range(cfg.B):
+            r = refs[b][s]
+            assert row_rel_err(out[b], r["o"]) <= OUT_TOL, (s, b)
+            if r["kind"] == "slow":
+                sel = dec.sel_idx[b].cpu().numpy()
+                cnt = dec.sel_count[b].cpu().numpy()
+                for g in range(cfg.Hkv):
+                    ties += check_selection(sel[g], cnt[g], r["s"][g], r["lo"], r["hi"], cfg.k)
+                assert row_rel_err(dec.fused[b, :, : r["n"]].cpu().numpy(), r["s"]) <= EVID_TOL
+    assert used > 0, "no step formed its prior from the statistics"
+    got = dec.nstat.cpu().numpy()
+    for b in range(cfg.B):
+        np.testing.assert_allclose(got[b], _norm_sums(Kf[b], int(ctx[b]) + cfg.steps), rtol=1e-5)
+    _say(f"  steps with the statistics prior: {used}; near-tie differences: {ties}")
+    assert ties == 0
+
+
 @pytest.mark.parametrize("paged", [False, True])
 def test_decode_step_select_matches_separate_calls(paged):
     """sfi_decode_step_select (one call: co-launched step + the slow
