@@ -405,7 +405,7 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
 
 
   float m[G], Z[G], acc[G][DPL];
-  double ns1 = 0.0, ns2 = 0.0;  // key-norm sums of this lane's rows (evidence mode)
+  double ns1 = 0.0, ns2 = 0.0;  // key-norm sums of this lane's rows (evidence mode; STATS: prior-weight sum)
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     m[h] = kNegBig;
@@ -527,10 +527,6 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
             ns1 += acc ? (double)nv : 0.0;
             ns2 = acc ? fma((double)nv, (double)nv, ns2) : ns2;
           }
-        } else {  // the prior weights' sum instead
-          const bool acc = st.j[u] >= 0 && sub == G % LPR;
-          const float w = prior_w(nv, st.j[u], st_muf, st_cz, (float)(n - 1), st_ct);
-          ns1 += acc ? (double)w : 0.0;
         }
       }
     }
@@ -618,6 +614,11 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
       for (int i = tid; i < nr * G; i += kThreads) lg[i] = s_evl[i];
       float *nm = a.key_norm + lrow * a.nld + blk;
       for (int i = tid; i < nr; i += kThreads) nm[i] = s_evn[i];
+      if constexpr (STATS) {  // the block's prior weights, a few per thread
+        float w = 0.f;
+        for (int i = tid; i < nr; i += kThreads) w += prior_w(s_evn[i], blk + i, st_muf, st_cz, (float)(n - 1), st_ct);
+        ns1 += (double)w;
+      }
       __syncthreads();
     }
   };
