@@ -14,8 +14,13 @@ constexpr int kTW = kT / 64;
 constexpr int kCH = kSelChunk;          // keys per chunk
 constexpr int kQuarter = kCH / 2;       // keys per half chunk (4 per thread)
 constexpr int kPT = kCH / kT;           // keys per thread
-constexpr int kD1 = 12;                 // bucket: key bits 31..20
+constexpr int kD1 = 12;                 // first-level buckets: 4096
 constexpr int kBins1 = 1 << kD1;
+// Fine buckets (fused scores): key bits 30..17 (the float's exponent and
+// its top 6 mantissa bits) less kFineBase, 64 buckets per octave from
+// 2^-63 (bucket 1) to 2^0 (bucket 4033).
+constexpr int kFineShift = 17;
+constexpr int kFineBase = (64 << 6) - 1;
 constexpr int kBPT = kBins1 / kT;       // buckets per thread
 constexpr int kD2 = 11;                 // digit width inside the bucket
 constexpr int kBins2 = 1 << kD2;
@@ -160,6 +165,21 @@ __device__ __forceinline__ int composite_index(unsigned long long c) {
   return (int)(0xFFFFFFFFu - (uint32_t)(c & 0xFFFFFFFFull));
 }
 
+// First-level bucket of a candidate's key: non-decreasing in the key and
+// never 0 (the pick reserves bucket 0).  Coarse (any score): the key's top
+// 12 bits, so a bucket's keys share them.  Fine (fused scores, non-negative
+// probability mixtures whose values spread over a few dozen octaves): 64
+// buckets per octave, so the k-th largest score's bucket holds about an
+// eighth of the keys the coarse one does.  Inside a fine bucket other than
+// the two end buckets the keys share bits 31..17; the end buckets also
+// take the values below 2^-63 (and negative ones) and those above 2^0.
+__device__ __forceinline__ int key_bucket(uint32_t key, bool fine) {
+  if (!fine) return (int)(key >> (32 - kD1));
+  if (!(key & 0x80000000u)) return 1;
+  const int v = (int)((key & 0x7FFFFFFFu) >> kFineShift);
+  return min(max(v - kFineBase, 1), kBins1 - 1);
+}
+
 // The key pass of chunk p of a row once its scores are known: s[i] is the
 // score of key jj[i] (any assignment of the chunk's keys to threads; the
 // candidates are the keys in [r.lo, r.hi)).  Order-preserving 32-bit keys,
@@ -172,15 +192,31 @@ __device__ __forceinline__ void keys_core(const SelectLaunch &a, const RowGeo &r
   __shared__ unsigned long long s_sorted[kCH];
   __shared__ int s_wave[kTW];
   const int tid = threadIdx.x;
+  const bool fine = a.mode == 0;
   for (int i = tid; i < kBins1; i += kT) hist[i] = 0u;
   __syncthreads();
   uint32_t key[kPT];
+  int bk[kPT];
 #pragma unroll
   for (int i = 0; i < kPT; ++i) {
     key[i] = (jj[i] >= r.lo && jj[i] < r.hi) ? float_key(s[i]) : 0u;
-    if (key[i]) atomicAdd(&hist[key[i] >> (32 - kD1)], 1u);
+    bk[i] = key_bucket(key[i], fine);
+    if (key[i]) atomicAdd(&hist[bk[i]], 1u);
   }
   __syncthreads();
+  // Merge the counts into the row histogram first, so the atomics complete
+  // while the rest of the pass runs: one 64-bit add per pair of buckets
+  // (a count stays far below 2^32, so the low word never carries into the
+  // high one), lane t taking pairs t, t + 256, ..., so that one wave's
+  // atomics fall on a few adjacent cache lines.
+  unsigned long long *h1 = reinterpret_cast<unsigned long long *>(a.ws.ghist + r.row * kBins1);
+#pragma unroll
+  for (int i = 0; i < kBPT / 2; ++i) {
+    const int pr = i * kT + tid;
+    const unsigned long long cc =
+        (unsigned long long)hist[2 * pr] | ((unsigned long long)hist[2 * pr + 1] << 32);
+    if (cc) atomicAdd(&h1[pr], cc);
+  }
   // Cumulative counts in descending bucket order: cum[b] = keys in buckets
   // >= b.  Thread t owns buckets 16 t .. 16 t + 15.
   uint32_t c[kBPT];
@@ -190,12 +226,6 @@ __device__ __forceinline__ void keys_core(const SelectLaunch &a, const RowGeo &r
     c[i] = hist[kBPT * tid + i];
     tot += (int)c[i];
   }
-  // Merge the counts into the row histogram first: the atomics complete
-  // while the rest of the pass runs instead of after it.
-  uint32_t *h1 = a.ws.ghist + r.row * kBins1 + kBPT * tid;
-#pragma unroll
-  for (int i = 0; i < kBPT; ++i)
-    if (c[i]) atomicAdd(&h1[i], c[i]);
   int total;
   const int below = block_exscan<kTW>(tot, s_wave, &total);  // keys in lower buckets
   int run = total - below - tot;                              // keys in higher buckets
@@ -218,7 +248,7 @@ __device__ __forceinline__ void keys_core(const SelectLaunch &a, const RowGeo &r
 #pragma unroll
   for (int i = 0; i < kPT; ++i) {
     if (key[i]) {
-      const unsigned slot = atomicAdd(&hist[key[i] >> (32 - kD1)], 1u);
+      const unsigned slot = atomicAdd(&hist[bk[i]], 1u);
       s_sorted[slot] = composite(key[i], jj[i]);
     }
   }
@@ -562,8 +592,9 @@ __device__ __forceinline__ void pick_body(const SelectLaunch &a, int p, int h, i
   __syncthreads();
 
   // 3. Radix select of the want1-th largest composite among the m bucket-b1
-  //    keys; their top 12 bits all equal b1 and 11-bit digits cover bits
-  //    51..0.  Bucket keys win iff their composite >= T.
+  //    keys, 11-bit digits below the bits the bucket's keys share (bits
+  //    63..52 for a coarse bucket, 63..49 for a fine one; none for a fine
+  //    end bucket).  Bucket keys win iff their composite >= T.
   unsigned long long T = 0ull;
   if (split) {
     const bool in_lds = mtot <= kCandLds;
@@ -595,8 +626,16 @@ __device__ __forceinline__ void pick_body(const SelectLaunch &a, int p, int h, i
       __syncthreads();
     }
     auto cand = [&](int i) { return in_lds ? s_cand[i] : cand_at(i); };
-    unsigned long long prefix = (unsigned long long)b1;
-    int top = 51, want = want1;
+    const bool fine = a.mode == 0;
+    unsigned long long prefix = 0ull;
+    int top = 63, want = want1;
+    if (!fine) {
+      prefix = (unsigned long long)b1;
+      top = 63 - kD1;
+    } else if (b1 > 1 && b1 < kBins1 - 1) {
+      prefix = 0x4000ull | (unsigned long long)(b1 + kFineBase);  // key bits 31..17
+      top = 31 + kFineShift;
+    }
     for (;;) {
       const int lo_bit = max(top - kD2 + 1, 0);
       const int width = top - lo_bit + 1;
@@ -610,7 +649,7 @@ __device__ __forceinline__ void pick_body(const SelectLaunch &a, int p, int h, i
       __syncthreads();
       for (int i = tid; i < mtot; i += kT) {
         const unsigned long long c = cand(i);
-        if ((c >> (top + 1)) == prefix) atomicAdd(&h2[(c >> lo_bit) & dmask], 1u);
+        if (top == 63 || (c >> (top + 1)) == prefix) atomicAdd(&h2[(c >> lo_bit) & dmask], 1u);
       }
       __syncthreads();
       find_bin_desc(h2, 1 << width, want, s_wave, s_res);
