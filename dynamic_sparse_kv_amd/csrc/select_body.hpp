@@ -626,6 +626,35 @@ __device__ __forceinline__ void pick_body(const SelectLaunch &a, int p, int h, i
       __syncthreads();
     }
     auto cand = [&](int i) { return in_lds ? s_cand[i] : cand_at(i); };
+    if (mtot <= kT) {
+      // A candidate's rank among the candidates (the composites are
+      // distinct) decides it, and the one of rank want1 - 1 is the
+      // threshold.  Up to 64 candidates, 4 adjacent lanes rank one, each
+      // over a quarter of the list (2 lanes up to 128); the comparisons go
+      // four at a time so the LDS reads overlap.
+      __shared__ unsigned long long s_thr;
+      const int lg = mtot <= 64 ? 2 : (mtot <= 128 ? 1 : 0);
+      const int i = tid >> lg, part = tid & ((1 << lg) - 1);
+      const int len = (mtot + (1 << lg) - 1) >> lg;
+      const int j0 = part * len, j1 = min(mtot, j0 + len);
+      const unsigned long long c = (i < mtot) ? s_cand[i] : 0ull;
+      int r0 = 0, r1 = 0, r2 = 0, r3 = 0;
+      int j = j0;
+      for (; j + 4 <= j1; j += 4) {
+        r0 += (s_cand[j] > c) ? 1 : 0;
+        r1 += (s_cand[j + 1] > c) ? 1 : 0;
+        r2 += (s_cand[j + 2] > c) ? 1 : 0;
+        r3 += (s_cand[j + 3] > c) ? 1 : 0;
+      }
+      for (; j < j1; ++j) r0 += (s_cand[j] > c) ? 1 : 0;
+      int rank = (r0 + r1) + (r2 + r3);
+      if (lg >= 1) rank += __shfl_xor(rank, 1);
+      if (lg >= 2) rank += __shfl_xor(rank, 2);
+      if (i < mtot && part == 0 && rank < want1) atomicAdd(&s_tw[min(composite_index(c) / kCH, r.nch - 1)], 1);
+      if (i < mtot && part == 0 && rank == want1 - 1) s_thr = c;
+      __syncthreads();
+      T = s_thr;
+    } else {
     const bool fine = a.mode == 0;
     unsigned long long prefix = 0ull;
     int top = 63, want = want1;
@@ -670,6 +699,7 @@ __device__ __forceinline__ void pick_body(const SelectLaunch &a, int p, int h, i
       if (c >= T) atomicAdd(&s_tw[min(composite_index(c) / kCH, r.nch - 1)], 1);
     }
     __syncthreads();
+    }  // radix select
   }
 
   // 4. Output offset of this chunk (winners of the chunks before it) and
