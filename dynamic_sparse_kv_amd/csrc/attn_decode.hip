@@ -1033,6 +1033,10 @@ __device__ __forceinline__ void finalize_body(const FinalArgs &a, int x, int g, 
       }
       nv[i] = prior ? a.key_norm[lrow * a.ld + min(j, j1 - 1)] : 0.f;
     }
+    // the key pass's histogram is cleared while the loads are in flight
+    // (the merge's barrier below orders it before the pass)
+    __shared__ std::conditional_t<KEYS, KeysLds, int> s_keys;
+    if constexpr (KEYS) keys_clear(s_keys);
     // merged (max, sum) of every head of the group over the S partials, and
     // the row's key-norm sums (fixed order; every chunk block repeats them)
     float m[G], z[G];
@@ -1144,7 +1148,7 @@ __device__ __forceinline__ void finalize_body(const FinalArgs &a, int x, int g, 
       // constants and weight sums, so w is the weight it summed, bit for bit
       static_assert(kEvidChunk == kSelChunk && PER == kPT, "evidence blocks are selector chunks");
       RowGeo r;
-      row_geo(a.sel, g, zb, r);
+      row_geo_n(a.sel, b, g, n, r);
       const float cf = 1.0f - a.sel.lambda;
       const float cr = sw > 0.0 ? (float)((double)a.sel.lambda / sw) : 0.f;
       const float ct = kLog2e / a.pos_tau;
@@ -1165,7 +1169,7 @@ __device__ __forceinline__ void finalize_body(const FinalArgs &a, int x, int g, 
           if (jj[i] < j1) fo[jj[i]] = sc[i];
       }
       if (pch >= r.nch) return;  // no candidates in this chunk
-      keys_core(a.sel, r, pch, sc, jj);
+      keys_core(a.sel, r, pch, sc, jj, s_keys);
       return;
     }
     float muf, cz;

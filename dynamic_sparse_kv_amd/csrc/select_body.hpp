@@ -108,16 +108,22 @@ struct RowGeo {
   size_t row;
 };
 
-__device__ __forceinline__ bool row_geo(const SelectLaunch &a, int h, int z, RowGeo &r) {
-  r.b = batch_seq(a.batch_ids, z, a.B);
-  if (r.b < 0) return false;
+// The geometry of row (b, h) whose clamped length n is known.
+__device__ __forceinline__ void row_geo_n(const SelectLaunch &a, int b, int h, int n, RowGeo &r) {
+  r.b = b;
   r.h = h;
-  r.n = clamp_len(a.seq_len, r.b, a.max_seq_len);
+  r.n = n;
   r.lo = a.n_sink;
   r.hi = max(a.n_sink, r.n - a.window);
   r.span = (a.mode == 0) ? r.n : r.hi;  // keys [0, span) are visited
   r.nch = (r.hi > r.lo) ? (r.hi + kCH - 1) / kCH : 0;
   r.row = (size_t)r.b * a.H + r.h;
+}
+
+__device__ __forceinline__ bool row_geo(const SelectLaunch &a, int h, int z, RowGeo &r) {
+  r.b = batch_seq(a.batch_ids, z, a.B);
+  if (r.b < 0) return false;
+  row_geo_n(a, r.b, h, clamp_len(a.seq_len, r.b, a.max_seq_len), r);
   return true;
 }
 
@@ -180,6 +186,19 @@ __device__ __forceinline__ int key_bucket(uint32_t key, bool fine) {
   return min(max(v - kFineBase, 1), kBins1 - 1);
 }
 
+// LDS of the key pass; its histogram is cleared by keys_clear, which a
+// caller can issue early (before its own loads are back), with a barrier
+// between the clearing and keys_core.
+struct KeysLds {
+  unsigned hist[kBins1];
+  unsigned long long sorted[kCH];
+  int wave[kTW];
+};
+
+__device__ __forceinline__ void keys_clear(KeysLds &l) {
+  for (int i = threadIdx.x; i < kBins1; i += kT) l.hist[i] = 0u;
+}
+
 // The key pass of chunk p of a row once its scores are known: s[i] is the
 // score of key jj[i] (any assignment of the chunk's keys to threads; the
 // candidates are the keys in [r.lo, r.hi)).  Order-preserving 32-bit keys,
@@ -187,14 +206,12 @@ __device__ __forceinline__ int key_bucket(uint32_t key, bool fine) {
 // cumulative bucket counts and its bucket-sorted run of (key, inverted
 // index) composites.  Every thread of the workgroup calls it.
 __device__ __forceinline__ void keys_core(const SelectLaunch &a, const RowGeo &r, int p, const float (&s)[kPT],
-                                          const int (&jj)[kPT]) {
-  __shared__ unsigned hist[kBins1];
-  __shared__ unsigned long long s_sorted[kCH];
-  __shared__ int s_wave[kTW];
+                                          const int (&jj)[kPT], KeysLds &l) {
+  unsigned *hist = l.hist;
+  unsigned long long *s_sorted = l.sorted;
+  int *s_wave = l.wave;
   const int tid = threadIdx.x;
   const bool fine = a.mode == 0;
-  for (int i = tid; i < kBins1; i += kT) hist[i] = 0u;
-  __syncthreads();
   uint32_t key[kPT];
   int bk[kPT];
 #pragma unroll
@@ -451,7 +468,10 @@ __device__ __forceinline__ void keys_body(const SelectLaunch &a, int p, int h, i
   int jj[kPT];
 #pragma unroll
   for (int i = 0; i < kPT; ++i) jj[i] = key_pos(j0, i);
-  keys_core(a, r, p, s, jj);
+  __shared__ KeysLds s_keys;
+  keys_clear(s_keys);
+  __syncthreads();
+  keys_core(a, r, p, s, jj, s_keys);
 }
 
 // Bin of an nb-bin histogram (nb <= kBins2, highest bin = largest values)
@@ -714,14 +734,14 @@ __device__ __forceinline__ void pick_body(const SelectLaunch &a, int p, int h, i
       wb += (q < p) ? w : 0;
     }
   }
+  // (the bitmap of step 5 is cleared here, ordered by the sum's barrier)
+  if (tid < kCH / 32) s_bits[tid] = 0u;
   int before, total_w;
   block_sum2<kTW>(wb, wt, s_pair, &before, &total_w);
   const int count = min(total_w, K);
 
   // 5. This chunk's winners, ascending, through a 2048-bit bitmap.
   if (p < r.nch) {
-    if (tid < kCH / 32) s_bits[tid] = 0u;
-    __syncthreads();
     const int na_p = s_above[p];
     const int ne_p = split ? s_toff[p + 1] - s_toff[p] : 0;
 #pragma unroll
