@@ -222,8 +222,9 @@ def test_select_fused_from_oracle_evidence():
     _say(f"  near-tie differences: {ties}")
 
 
-def test_select_fused_long_row_streams_blocks():
-    """Rows longer than one register block (40960 keys) take the streaming path."""
+def test_select_fused_long_row_many_chunks():
+    """A 50,001-key row: 25 selector chunks of 2048 keys (the last one
+    ragged), the fused scores and the Top-3000 against the oracle."""
     _say("select fused long row")
     B, Hq, Hkv, d = 1, 4, 2, 64
     n = 50001
