@@ -750,13 +750,15 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
 
 template <int D, int G, bool PAGED, int MODE, bool EVID, bool STATS = false>
 __global__ __launch_bounds__(kThreads) void partial_kernel(PartialArgs a) {
-  partial_body<D, G, PAGED, MODE, EVID, false, STATS>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+  const PairBlock pb = pair_block(linear_block(), gridDim.x, gridDim.y, gridDim.z);
+  partial_body<D, G, PAGED, MODE, EVID, false, STATS>(a, pb.blk, pb.h, pb.z);
 }
 
 // Fast step reading its selected rows from the compact copy.
 template <int D, int G, bool PAGED>
 __global__ __launch_bounds__(kThreads) void fast_compact_kernel(PartialArgs a) {
-  partial_body<D, G, PAGED, MODE_FAST, false, true>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+  const PairBlock pb = pair_block(linear_block(), gridDim.x, gridDim.y, gridDim.z);
+  partial_body<D, G, PAGED, MODE_FAST, false, true>(a, pb.blk, pb.h, pb.z);
 }
 
 // Compact copy of the selected rows: row i of (sequence, kv head) holds the
@@ -848,21 +850,22 @@ __global__ __launch_bounds__(kThreads) void copartial_kernel(PartialArgs s, Part
                                                              int f_splits, int Hkv, int ns,
                                                              SelectLaunch pend, int np) {
   int id = blockIdx.x;
+  const int nt = gridDim.x - np;
   if constexpr (PEND) {
-    const int nt = gridDim.x - np;
     if (id >= nt) {
       id -= nt;
-      keys_body<true>(pend, id % pend.ws.P, (id / pend.ws.P) % pend.H, id / (pend.ws.P * pend.H));
+      const PairBlock pb = pair_block(id, pend.ws.P, pend.H, pend.batch_n);
+      keys_body<true>(pend, pb.blk, pb.h, pb.z);
       return;
     }
   }
   if (id < ns) {
-    partial_body<D, G, PAGED, MODE_SLOW, true, false, STATS>(s, id % s_splits, (id / s_splits) % Hkv,
-                                                            id / (s_splits * Hkv));
+    const PairBlock pb = pair_block(id, s_splits, Hkv, ns / (s_splits * Hkv));
+    partial_body<D, G, PAGED, MODE_SLOW, true, false, STATS>(s, pb.blk, pb.h, pb.z);
   } else {
     id -= ns;
-    partial_body<D, G, PAGED, MODE_FAST, false>(f, id % f_splits, (id / f_splits) % Hkv,
-                                                id / (f_splits * Hkv));
+    const PairBlock pb = pair_block(id, f_splits, Hkv, (nt - ns) / (f_splits * Hkv));
+    partial_body<D, G, PAGED, MODE_FAST, false>(f, pb.blk, pb.h, pb.z);
   }
 }
 
@@ -1204,7 +1207,8 @@ __device__ __forceinline__ void finalize_body(const FinalArgs &a, int x, int g, 
 
 template <int D, int G, int MODE, bool EVID, bool KEYS = false>
 __global__ __launch_bounds__(kThreads) void finalize_kernel(FinalArgs a) {
-  finalize_body<D, G, MODE, EVID, KEYS>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+  const PairBlock pb = pair_block(linear_block(), gridDim.x, gridDim.y, gridDim.z);
+  finalize_body<D, G, MODE, EVID, KEYS>(a, pb.blk, pb.h, pb.z);
 }
 
 // Slow and fast finalize blocks of one decode step in a single grid: the
@@ -1216,11 +1220,12 @@ template <int D, int G, bool PEND, bool KEYS = false>
 __global__ __launch_bounds__(kThreads) void cofinal_kernel(FinalArgs s, FinalArgs f, int s_gx, int f_gx,
                                                            int Hkv, int ns, SelectLaunch pend, int np) {
   int id = blockIdx.x;
+  const int nt = gridDim.x - np;
   if constexpr (PEND) {
-    const int nt = gridDim.x - np;
     if (id >= nt) {
       id -= nt;
-      pick_body(pend, id % pend.ws.P, (id / pend.ws.P) % pend.H, id / (pend.ws.P * pend.H));
+      const PairBlock pb = pair_block(id, pend.ws.P, pend.H, pend.batch_n);
+      pick_body(pend, pb.blk, pb.h, pb.z);
       return;
     }
   }
@@ -1228,14 +1233,17 @@ __global__ __launch_bounds__(kThreads) void cofinal_kernel(FinalArgs s, FinalArg
     // the evidence blocks (the longest) are dispatched first
     const int ne = s_gx - G, pairs = ns / s_gx;
     if (id < ne * pairs) {
-      finalize_body<D, G, MODE_SLOW, true, KEYS>(s, G + id % ne, (id / ne) % Hkv, id / (ne * Hkv));
+      const PairBlock pb = pair_block(id, ne, Hkv, pairs / Hkv);
+      finalize_body<D, G, MODE_SLOW, true, KEYS>(s, G + pb.blk, pb.h, pb.z);
     } else {
       id -= ne * pairs;
-      finalize_body<D, G, MODE_SLOW, true, KEYS>(s, id % G, (id / G) % Hkv, id / (G * Hkv));
+      const PairBlock pb = pair_block(id, G, Hkv, pairs / Hkv);
+      finalize_body<D, G, MODE_SLOW, true, KEYS>(s, pb.blk, pb.h, pb.z);
     }
   } else {
     id -= ns;
-    finalize_body<D, G, MODE_FAST, false>(f, id % f_gx, (id / f_gx) % Hkv, id / (f_gx * Hkv));
+    const PairBlock pb = pair_block(id, f_gx, Hkv, (nt - ns) / (f_gx * Hkv));
+    finalize_body<D, G, MODE_FAST, false>(f, pb.blk, pb.h, pb.z);
   }
 }
 

@@ -50,9 +50,10 @@ namespace {
 // ---------------------------------------------------------------- 1. sums
 __global__ __launch_bounds__(kT) void norm_sums_kernel(SelectLaunch a) {
   __shared__ double s_red[kTW];
+  const PairBlock pb = pair_block(linear_block(), gridDim.x, gridDim.y, gridDim.z);
   RowGeo r;
-  if (!row_geo(a, blockIdx.y, blockIdx.z, r)) return;
-  const int p = blockIdx.x, j0 = p * kCH;
+  if (!row_geo(a, pb.h, pb.z, r)) return;
+  const int p = pb.blk, j0 = p * kCH;
   if (j0 >= r.n) return;
   const float *nu = a.key_norm + r.row * a.ld;
   float x[kPT];
@@ -75,9 +76,10 @@ __global__ __launch_bounds__(kT) void norm_sums_kernel(SelectLaunch a) {
 template <bool FUSED>
 __global__ __launch_bounds__(kT) void prior_kernel(SelectLaunch a) {
   __shared__ double s_red[kTW];
+  const PairBlock pb = pair_block(linear_block(), gridDim.x, gridDim.y, gridDim.z);
   RowGeo r;
-  if (!row_geo(a, blockIdx.y, blockIdx.z, r)) return;
-  const int p = blockIdx.x, j0 = p * kCH;
+  if (!row_geo(a, pb.h, pb.z, r)) return;
+  const int p = pb.blk, j0 = p * kCH;
   const int tid = threadIdx.x;
   // clear the row histogram (striped over all chunk workgroups) for step 3
   uint32_t *h1 = a.ws.ghist + r.row * kBins1;
@@ -119,12 +121,14 @@ __global__ __launch_bounds__(kT) void prior_kernel(SelectLaunch a) {
 // --------------------------------------------------------------- 3. keys
 template <bool FUSED, bool REFINE>
 __global__ __launch_bounds__(kT) void keys_kernel(SelectLaunch a) {
-  keys_body<FUSED, REFINE>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+  const PairBlock pb = pair_block(linear_block(), gridDim.x, gridDim.y, gridDim.z);
+  keys_body<FUSED, REFINE>(a, pb.blk, pb.h, pb.z);
 }
 
 // ----------------------------------------------------------- 4. pick
 __global__ __launch_bounds__(kT) void pick_kernel(SelectLaunch a) {
-  pick_body(a, blockIdx.x, blockIdx.y, blockIdx.z);
+  const PairBlock pb = pair_block(linear_block(), gridDim.x, gridDim.y, gridDim.z);
+  pick_body(a, pb.blk, pb.h, pb.z);
 }
 
 }  // namespace

@@ -120,6 +120,40 @@ __device__ __forceinline__ int batch_seq(const int32_t *ids, int i, int B) {
   return (b >= 0 && b < B) ? b : -1;
 }
 
+// Blocks of a grid share over (head, batch entry) pairs: P = H x Z pairs,
+// S blocks per pair, w the block's index in the share.  Workgroups go to
+// the 8 XCDs round-robin by linear id, so when the share starts at a
+// linear id that is a multiple of 8 and P is a multiple of 8, block w takes
+// pair (w % 8) + 8 ((w / 8) / S) and block (w / 8) % S: every block of a
+// pair runs on XCD pair % 8, where a later kernel's blocks of the same pair
+// also run and find what this one wrote in that XCD's L2.  Otherwise pair
+// w / S, block w % S.
+#ifndef SFI_XCD_MAP
+#define SFI_XCD_MAP 1
+#endif
+struct PairBlock {
+  int blk, h, z;
+};
+__device__ __forceinline__ PairBlock pair_block(int w, int S, int H, int Z) {
+  int pair;
+  int blk;
+  if (SFI_XCD_MAP && ((H * Z) & 7) == 0) {
+    const int k = w >> 3;
+    const int q = k / S;
+    pair = (w & 7) + 8 * q;
+    blk = k - q * S;
+  } else {
+    pair = w / S;
+    blk = w - pair * S;
+  }
+  return {blk, pair % H, pair / H};
+}
+
+// Linear id of the block in its grid (x fastest, the dispatch order).
+__device__ __forceinline__ int linear_block() {
+  return (int)(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
+}
+
 // Cached length of sequence b clamped to [0, max_len].
 __device__ __forceinline__ int clamp_len(const int32_t *seq_len, int b, int max_len) {
   return min(max(seq_len[b], 0), max_len);
