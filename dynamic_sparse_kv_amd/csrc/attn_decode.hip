@@ -750,7 +750,7 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
 
 template <int D, int G, bool PAGED, int MODE, bool EVID, bool STATS = false>
 __global__ __launch_bounds__(kThreads) void partial_kernel(PartialArgs a) {
-  const PairBlock pb = pair_block(linear_block(), gridDim.x, gridDim.y, gridDim.z);
+  const PairBlock pb = pair_block(linear_block(), gridDim.x, gridDim.y, gridDim.z, MODE == MODE_FAST);
   partial_body<D, G, PAGED, MODE, EVID, false, STATS>(a, pb.blk, pb.h, pb.z);
 }
 
@@ -860,7 +860,7 @@ __global__ __launch_bounds__(kThreads) void copartial_kernel(PartialArgs s, Part
     }
   }
   if (id < ns) {
-    const PairBlock pb = pair_block(id, s_splits, Hkv, ns / (s_splits * Hkv));
+    const PairBlock pb = pair_block(id, s_splits, Hkv, ns / (s_splits * Hkv), false);
     partial_body<D, G, PAGED, MODE_SLOW, true, false, STATS>(s, pb.blk, pb.h, pb.z);
   } else {
     id -= ns;

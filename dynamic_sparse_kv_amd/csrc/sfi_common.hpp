@@ -122,22 +122,25 @@ __device__ __forceinline__ int batch_seq(const int32_t *ids, int i, int B) {
 
 // Blocks of a grid share over (head, batch entry) pairs: P = H x Z pairs,
 // S blocks per pair, w the block's index in the share.  Workgroups go to
-// the 8 XCDs round-robin by linear id, so when the share starts at a
-// linear id that is a multiple of 8 and P is a multiple of 8, block w takes
+// the 8 XCDs round-robin by linear id, so with xcd set, a share starting at
+// a linear id that is a multiple of 8 and P a multiple of 8, block w takes
 // pair (w % 8) + 8 ((w / 8) / S) and block (w / 8) % S: every block of a
 // pair runs on XCD pair % 8, where a later kernel's blocks of the same pair
 // also run and find what this one wrote in that XCD's L2.  Otherwise pair
-// w / S, block w % S.
+// w / S, block w % S.  The fast steps' gathers, the finalize blocks and the
+// selector gain from it; the long contiguous streams of dense and slow
+// steps measured slower with it (a 128K dense step 331 -> 346 us), so their
+// partial blocks keep the plain order.
 #ifndef SFI_XCD_MAP
 #define SFI_XCD_MAP 1
 #endif
 struct PairBlock {
   int blk, h, z;
 };
-__device__ __forceinline__ PairBlock pair_block(int w, int S, int H, int Z) {
+__device__ __forceinline__ PairBlock pair_block(int w, int S, int H, int Z, bool xcd = true) {
   int pair;
   int blk;
-  if (SFI_XCD_MAP && ((H * Z) & 7) == 0) {
+  if (SFI_XCD_MAP && xcd && ((H * Z) & 7) == 0) {
     const int k = w >> 3;
     const int q = k / S;
     pair = (w & 7) + 8 * q;
