@@ -1012,8 +1012,9 @@ def test_norm_stats_prior_matches_the_pass(paged):
     nr = (rows[:, 3].contiguous(), vrows[:, 3].contiguous())
     slow_ids = torch.tensor([1, 3], dtype=torch.int32, device=DEV)
     fast_ids = torch.tensor([0, 2], dtype=torch.int32, device=DEV)
-    st.step_select(q, seq4, slow_ids, 2, fast_ids, 2, new_rows=nr, use_stats=True)
-    ex.step_select(q, seq4, slow_ids, 2, fast_ids, 2, new_rows=nr)
+    kseq = torch.tensor([300, 300, 300, 97], dtype=torch.int32, device=DEV)   # sequence 3 keeps 97
+    st.step_select(q, seq4, slow_ids, 2, fast_ids, 2, new_rows=nr, use_stats=True, k_seq=kseq)
+    ex.step_select(q, seq4, slow_ids, 2, fast_ids, 2, new_rows=nr, k_seq=kseq)
     torch.cuda.synchronize()
     for t in ("out", "evidence", "key_norm"):
         assert torch.equal(getattr(st, t).view(torch.int32), getattr(ex, t).view(torch.int32)), t
@@ -1036,13 +1037,43 @@ def test_norm_stats_prior_matches_the_pass(paged):
     ties = 0
     for b in (1, 3):
         n = lens[b] + 4
-        r = O.slow_select(qb[b], Kb[b], Vb[b], n, lam=0.3, k=300, n_sink=4, window=256)
+        kb = 300 if b == 1 else 97
+        r = O.slow_select(qb[b], Kb[b], Vb[b], n, lam=0.3, k=kb, n_sink=4, window=256)
         np.testing.assert_allclose(a[b], _norm_sums(Kf[b], n), rtol=1e-5)
         assert row_rel_err(st.fused[b, :, :n].cpu().numpy(), r["s"]) <= EVID_TOL
         for g in range(Hkv):
-            ties += check_selection(sel[b, g], cnt[b, g], r["s"][g], r["lo"], r["hi"], 300)
-            ties += check_selection(sel_e[b, g], cnt_e[b, g], r["s"][g], r["lo"], r["hi"], 300)
+            ties += check_selection(sel[b, g, :kb], cnt[b, g], r["s"][g], r["lo"], r["hi"], kb)
+            ties += check_selection(sel_e[b, g, :kb], cnt_e[b, g], r["s"][g], r["lo"], r["hi"], kb)
+            assert np.all(sel[b, g, kb:] == -1)
     _say(f"  near-tie differences: {ties}")
+
+
+def test_norm_stats_append_short_and_unlisted():
+    """sfi_append_kv with key-norm statistics: T rows appended to a sequence
+    holding fewer than T rows add only the rows that land (j >= 0), and a
+    sequence the call does not list keeps its sums."""
+    _say("norm statistics: short appends")
+    B, Hq, Hkv, d, T = 3, 8, 2, 128, 8
+    lens = [5, 40, 300]
+    cap = 320
+    K, V = _rand_kv(B, Hkv, cap, d, seed=81)
+    seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    nstat = torch.zeros((B, Hkv, 2), dtype=torch.float64, device=DEV)
+    nstat[:, :, 0] = 1.0      # arbitrary earlier sums
+    nstat[:, :, 1] = 2.0
+    kv = sfi.with_norm_stats(sfi.make_kv(K, V, seq, Hq, cap), nstat, False)
+    g = torch.Generator(device=DEV).manual_seed(82)
+    kn = torch.randn((B, T, Hkv, d), generator=g, device=DEV).to(torch.bfloat16)
+    vn = torch.randn((B, T, Hkv, d), generator=g, device=DEV).to(torch.bfloat16)
+    ids = torch.tensor([0, 1], dtype=torch.int32, device=DEV)     # sequence 2 not listed
+    sfi.sfi_append_kv(kv, ids, 2, kn, vn, T)
+    torch.cuda.synchronize()
+    nu = np.sqrt((kn.double().cpu().numpy() ** 2).sum(-1))      # [B][T][Hkv]
+    got = nstat.cpu().numpy()
+    for b in range(B):
+        t0 = max(0, T - lens[b]) if b < 2 else T                  # rows j = n - T + t >= 0
+        want = np.stack([1.0 + nu[b, t0:].sum(0), 2.0 + (nu[b, t0:] ** 2).sum(0)], -1)
+        np.testing.assert_allclose(got[b], want, rtol=1e-6)
 
 
 def test_decode_run_with_stats_prior_vs_oracle():
