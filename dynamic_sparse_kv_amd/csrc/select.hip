@@ -18,9 +18,8 @@
 //                         also clears the row's histogram;
 //   3. keys               s_j = (1 - lambda) f_j + lambda w_j / sum(w) as an
 //                         order-preserving 32-bit key; the chunk's candidate
-//                         keys are bucket-sorted in LDS (4096 buckets: a raw
-//                         score's top 12 bits, or 64 per octave of a fused
-//                         score, which is never negative) and written (one
+//                         keys are bucket-sorted in LDS (4096 buckets, 64 per
+//                         octave over the range the scores take) and written (one
 //                         coalesced pass) as 64-bit (key, inverted index)
 //                         composites in descending bucket order, with the
 //                         chunk's cumulative bucket counts; the bucket counts

@@ -16,11 +16,13 @@ constexpr int kQuarter = kCH / 2;       // keys per half chunk (4 per thread)
 constexpr int kPT = kCH / kT;           // keys per thread
 constexpr int kD1 = 12;                 // first-level buckets: 4096
 constexpr int kBins1 = 1 << kD1;
-// Fine buckets (fused scores): key bits 30..17 (the float's exponent and
-// its top 6 mantissa bits) less kFineBase, 64 buckets per octave from
-// 2^-63 (bucket 1) to 2^0 (bucket 4033).
+// Buckets: key bits 30..17 of a positive score (the float's exponent and
+// its top 6 mantissa bits) less a base, 64 buckets per octave: from 2^-63
+// (bucket 1) to 2^0 (bucket 4033) for fused scores, from 2^-31 to 2^33 for
+// raw ones (Vegas' aggregated logits).
 constexpr int kFineShift = 17;
 constexpr int kFineBase = (64 << 6) - 1;
+constexpr int kRawBase = (96 << 6) - 1;
 constexpr int kBPT = kBins1 / kT;       // buckets per thread
 constexpr int kD2 = 11;                 // digit width inside the bucket
 constexpr int kBins2 = 1 << kD2;
@@ -172,18 +174,20 @@ __device__ __forceinline__ int composite_index(unsigned long long c) {
 }
 
 // First-level bucket of a candidate's key: non-decreasing in the key and
-// never 0 (the pick reserves bucket 0).  Coarse (any score): the key's top
-// 12 bits, so a bucket's keys share them.  Fine (fused scores, non-negative
-// probability mixtures whose values spread over a few dozen octaves): 64
-// buckets per octave, so the k-th largest score's bucket holds about an
-// eighth of the keys the coarse one does.  Inside a fine bucket other than
-// the two end buckets the keys share bits 31..17; the end buckets also
-// take the values below 2^-63 (and negative ones) and those above 2^0.
-__device__ __forceinline__ int key_bucket(uint32_t key, bool fine) {
-  if (!fine) return (int)(key >> (32 - kD1));
+// never 0 (the pick reserves bucket 0).  64 buckets per octave over the
+// range the scores take (fused: non-negative probability mixtures spread
+// over a few dozen octaves; raw: sums of logits, whose top-k sit among the
+// positive values), so the k-th largest score's bucket holds about an
+// eighth of the keys that a bucket of the key's top 12 bits (sign, exponent
+// and 3 mantissa bits) would.  Inside a bucket other than the two end
+// buckets the keys share bits 31..17; the end buckets also take what lies
+// beyond the range (bucket 1 every negative score).
+__device__ __forceinline__ int bucket_base(int mode) { return mode == 0 ? kFineBase : kRawBase; }
+
+__device__ __forceinline__ int key_bucket(uint32_t key, int base) {
   if (!(key & 0x80000000u)) return 1;
   const int v = (int)((key & 0x7FFFFFFFu) >> kFineShift);
-  return min(max(v - kFineBase, 1), kBins1 - 1);
+  return min(max(v - base, 1), kBins1 - 1);
 }
 
 // LDS of the key pass; its histogram is cleared by keys_clear, which a
@@ -211,13 +215,13 @@ __device__ __forceinline__ void keys_core(const SelectLaunch &a, const RowGeo &r
   unsigned long long *s_sorted = l.sorted;
   int *s_wave = l.wave;
   const int tid = threadIdx.x;
-  const bool fine = a.mode == 0;
+  const int base = bucket_base(a.mode);
   uint32_t key[kPT];
   int bk[kPT];
 #pragma unroll
   for (int i = 0; i < kPT; ++i) {
     key[i] = (jj[i] >= r.lo && jj[i] < r.hi) ? float_key(s[i]) : 0u;
-    bk[i] = key_bucket(key[i], fine);
+    bk[i] = key_bucket(key[i], base);
     if (key[i]) atomicAdd(&hist[bk[i]], 1u);
   }
   __syncthreads();
@@ -611,10 +615,11 @@ __device__ __forceinline__ void pick_body(const SelectLaunch &a, int p, int h, i
   if (tid == 0) s_toff[r.nch] = mtot;
   __syncthreads();
 
-  // 3. Radix select of the want1-th largest composite among the m bucket-b1
-  //    keys, 11-bit digits below the bits the bucket's keys share (bits
-  //    63..52 for a coarse bucket, 63..49 for a fine one; none for a fine
-  //    end bucket).  Bucket keys win iff their composite >= T.
+  // 3. Selection of the want1-th largest composite among the m bucket-b1
+  //    keys: their ranks when they fit one per thread, else a radix select
+  //    with 11-bit digits below the bits the bucket's keys share (bits
+  //    63..49; none for an end bucket).  Bucket keys win iff their
+  //    composite >= T.
   unsigned long long T = 0ull;
   if (split) {
     const bool in_lds = mtot <= kCandLds;
@@ -675,14 +680,10 @@ __device__ __forceinline__ void pick_body(const SelectLaunch &a, int p, int h, i
       __syncthreads();
       T = s_thr;
     } else {
-    const bool fine = a.mode == 0;
     unsigned long long prefix = 0ull;
     int top = 63, want = want1;
-    if (!fine) {
-      prefix = (unsigned long long)b1;
-      top = 63 - kD1;
-    } else if (b1 > 1 && b1 < kBins1 - 1) {
-      prefix = 0x4000ull | (unsigned long long)(b1 + kFineBase);  // key bits 31..17
+    if (b1 > 1 && b1 < kBins1 - 1) {
+      prefix = 0x4000ull | (unsigned long long)(b1 + bucket_base(a.mode));  // key bits 31..17
       top = 31 + kFineShift;
     }
     for (;;) {
