@@ -194,7 +194,7 @@ __device__ __forceinline__ int key_bucket(uint32_t key, int base) {
 // caller can issue early (before its own loads are back), with a barrier
 // between the clearing and keys_core.
 struct KeysLds {
-  unsigned hist[kBins1];
+  alignas(16) unsigned hist[kBins1];
   unsigned long long sorted[kCH];
   int wave[kTW];
 };
@@ -231,22 +231,25 @@ __device__ __forceinline__ void keys_core(const SelectLaunch &a, const RowGeo &r
   // high one), lane t taking pairs t, t + 256, ..., so that one wave's
   // atomics fall on a few adjacent cache lines.
   unsigned long long *h1 = reinterpret_cast<unsigned long long *>(a.ws.ghist + r.row * kBins1);
+  const unsigned long long *h64 = reinterpret_cast<const unsigned long long *>(hist);
 #pragma unroll
   for (int i = 0; i < kBPT / 2; ++i) {
     const int pr = i * kT + tid;
-    const unsigned long long cc =
-        (unsigned long long)hist[2 * pr] | ((unsigned long long)hist[2 * pr + 1] << 32);
+    const unsigned long long cc = h64[pr];  // buckets 2 pr (low word) and 2 pr + 1
     if (cc) atomicAdd(&h1[pr], cc);
   }
   // Cumulative counts in descending bucket order: cum[b] = keys in buckets
   // >= b.  Thread t owns buckets 16 t .. 16 t + 15.
   uint32_t c[kBPT];
   int tot = 0;
+  const uint4 *h4 = reinterpret_cast<const uint4 *>(hist) + (kBPT / 4) * tid;
 #pragma unroll
-  for (int i = 0; i < kBPT; ++i) {
-    c[i] = hist[kBPT * tid + i];
-    tot += (int)c[i];
+  for (int i = 0; i < kBPT / 4; ++i) {
+    const uint4 t = h4[i];
+    c[4 * i] = t.x; c[4 * i + 1] = t.y; c[4 * i + 2] = t.z; c[4 * i + 3] = t.w;
   }
+#pragma unroll
+  for (int i = 0; i < kBPT; ++i) tot += (int)c[i];
   int total;
   const int below = block_exscan<kTW>(tot, s_wave, &total);  // keys in lower buckets
   int run = total - below - tot;                              // keys in higher buckets
@@ -257,8 +260,11 @@ __device__ __forceinline__ void keys_core(const SelectLaunch &a, const RowGeo &r
     cum[i] = (uint32_t)run;
   }
   // bucket b's first slot in the descending layout is cum[b] - count[b]
+  uint4 *hw = reinterpret_cast<uint4 *>(hist) + (kBPT / 4) * tid;
 #pragma unroll
-  for (int i = 0; i < kBPT; ++i) hist[kBPT * tid + i] = cum[i] - c[i];
+  for (int i = 0; i < kBPT / 4; ++i)
+    hw[i] = make_uint4(cum[4 * i] - c[4 * i], cum[4 * i + 1] - c[4 * i + 1], cum[4 * i + 2] - c[4 * i + 2],
+                       cum[4 * i + 3] - c[4 * i + 3]);
   uint4 *cd = reinterpret_cast<uint4 *>(a.ws.cum + (r.row * a.ws.P + p) * kBins1 + kBPT * tid);
   cd[0] = make_uint4(cum[0] | cum[1] << 16, cum[2] | cum[3] << 16, cum[4] | cum[5] << 16,
                      cum[6] | cum[7] << 16);
