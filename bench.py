@@ -672,7 +672,9 @@ def leg_ragged_paged(timed_steps=32, dense_steps=4):
     slow with probability 1/20 per step (step 0 slow), each step appending
     its rows.  Graph: slow and fast shares of a step co-launched in one grid
     on one stream.  Two streams: slow steps and selector on one stream, fast
-    steps on another, co-running (eager, hip events around the run)."""
+    steps on another, co-running (eager, hip events around the run).  Every
+    call carries the host row-count hints, so each sequence gets the
+    workgroups of its own length."""
     import torch
     from dynamic_sparse_kv_amd import sfi
     from dynamic_sparse_kv_amd import workload as W
@@ -738,23 +740,26 @@ def leg_ragged_paged(timed_steps=32, dense_steps=4):
         ks = plan.k_seq[s]
         sl = plan.seq_len[s]
         nr = (nk[0][s], nk[1][s])
+        lh = dec.hints(plan, s)
         if ns and nf:
-            timer("step", [lambda st: dec.co_step(q[s], sl, sids, ns, fids, nf, st, select=False, new_rows=nr)],
-                  sb + fb)
+            timer("step", [lambda st: dec.co_step(q[s], sl, sids, ns, fids, nf, st, select=False, new_rows=nr,
+                                                  len_hints=lh)], sb + fb)
         elif ns:
-            timer("slow", [lambda st: dec.slow(q[s], sl, sids, ns, st, select=False, new_rows=nr)], sb)
+            timer("slow", [lambda st: dec.slow(q[s], sl, sids, ns, st, select=False, new_rows=nr,
+                                               len_hints=lh)], sb)
         elif nf:
-            timer("fast", [lambda st: dec.fast(q[s], sl, fids, nf, st, new_rows=nr)], fb)
+            timer("fast", [lambda st: dec.fast(q[s], sl, fids, nf, st, new_rows=nr, len_hints=lh)], fb)
         if ns:
             timer("select", [lambda st: dec.slow_select_only(sl, sids, ns, st, k_seq=ks)], selb)
     for s in range(1, 1 + dense_steps):
         db = sum(algorithmic_bytes("dense", int(n), cfg) for n in plan.seq_len_host[s])
-        timer("dense", [lambda st: dec.dense(q[s], plan.seq_len[s], None, cfg.B, st)], db)
+        timer("dense", [lambda st: dec.dense(q[s], plan.seq_len[s], None, cfg.B, st,
+                                             len_hints=plan.seq_len_host[s])], db)
     per_call = timer.summary()
 
     def run_dense(st):
         for s in range(1, 1 + dense_steps):
-            dec.dense(q[s], plan.seq_len[s], None, cfg.B, st)
+            dec.dense(q[s], plan.seq_len[s], None, cfg.B, st, len_hints=plan.seq_len_host[s])
 
     t_dense, _, g = _graph_time(run_dense, side, stream)
     del g

@@ -100,6 +100,7 @@ struct PartialArgs {
   SelRowMeta *sel_meta;
   uint32_t *sel_ghist;
   int nsp;  // planned splits per (sequence, kv head)
+  WorkTable wt;  // per-entry split counts (wt.n = 0: nsp for every entry)
   float norm_coef, pos_tau;
 };
 
@@ -321,7 +322,8 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
   };
   if constexpr (STATS) {
     {  // this split's stripe of the row histogram
-      for (int i = split * kThreads + tid; i < 4096; i += a.nsp * kThreads) a.sel_ghist[lrow * 4096 + i] = 0u;
+      const int nsp = entry_splits(a.wt, zb, a.nsp);
+      for (int i = split * kThreads + tid; i < 4096; i += nsp * kThreads) a.sel_ghist[lrow * 4096 + i] = 0u;
     }
   }
   if (p0 >= L) {
@@ -750,7 +752,8 @@ __device__ __forceinline__ void partial_body(const PartialArgs &a, int split, in
 
 template <int D, int G, bool PAGED, int MODE, bool EVID, bool STATS = false>
 __global__ __launch_bounds__(kThreads) void partial_kernel(PartialArgs a) {
-  const PairBlock pb = pair_block(linear_block(), gridDim.x, gridDim.y, gridDim.z, MODE == MODE_FAST);
+  const PairBlock pb = a.wt.n > 0 ? table_block(a.wt, linear_block(), a.kv.Hkv)
+                                  : pair_block(linear_block(), gridDim.x, gridDim.y, gridDim.z, MODE == MODE_FAST);
   partial_body<D, G, PAGED, MODE, EVID, false, STATS>(a, pb.blk, pb.h, pb.z);
 }
 
@@ -860,11 +863,13 @@ __global__ __launch_bounds__(kThreads) void copartial_kernel(PartialArgs s, Part
     }
   }
   if (id < ns) {
-    const PairBlock pb = pair_block(id, s_splits, Hkv, ns / (s_splits * Hkv), false);
+    const PairBlock pb = s.wt.n > 0 ? table_block(s.wt, id, Hkv)
+                                    : pair_block(id, s_splits, Hkv, ns / (s_splits * Hkv), false);
     partial_body<D, G, PAGED, MODE_SLOW, true, false, STATS>(s, pb.blk, pb.h, pb.z);
   } else {
     id -= ns;
-    const PairBlock pb = pair_block(id, f_splits, Hkv, (nt - ns) / (f_splits * Hkv));
+    const PairBlock pb = f.wt.n > 0 ? table_block(f.wt, id, Hkv)
+                                    : pair_block(id, f_splits, Hkv, (nt - ns) / (f_splits * Hkv));
     partial_body<D, G, PAGED, MODE_FAST, false>(f, pb.blk, pb.h, pb.z);
   }
 }
@@ -907,6 +912,7 @@ struct FinalArgs {
   const double *wpart;
   const double *nnext;
   SelectLaunch sel;
+  WorkTable wt;  // per-entry split counts of the partial grid (wt.n = 0: splits)
 };
 
 // Merge (m2, z2) into the running softmax pair (m, z): both are a log2-domain
@@ -934,9 +940,9 @@ __device__ __forceinline__ void finalize_body(const FinalArgs &a, int x, int g, 
   const size_t pbase = (size_t)(a.pe ? zb : b) * a.Hq + (size_t)g * G;  // rows of the partial buffers
 
   if (comb) {
-    // every planned split: those past the row list wrote Z = 0 and are
-    // skipped, so no length is read before the partials
-    const int S = a.splits;
+    // every planned split of the entry: those past the row list wrote Z = 0
+    // and are skipped, so no length is read before the partials
+    const int S = entry_splits(a.wt, zb, a.splits);
     // PARTS groups of D/4 threads; group `part` merges partials part,
     // part + PARTS, ... (four at a time, their loads in flight together)
     // into a running (m, z, o); the groups are then merged through LDS.
@@ -1279,6 +1285,7 @@ PartialArgs partial_args(const AttnLaunch &a) {
   p.sel_meta = a.sel_meta;
   p.sel_ghist = a.sel_ghist;
   p.nsp = a.plan.splits;
+  p.wt = a.wt;
   p.norm_coef = a.norm_coef;
   p.pos_tau = a.pos_tau;
   p.ck = a.ck;
@@ -1299,6 +1306,7 @@ FinalArgs final_args(const AttnLaunch &a) {
   f.nsum = a.nsum; f.key_norm = a.key_norm; f.norm_coef = a.norm_coef; f.pos_tau = a.pos_tau;
   f.sel_wsum = a.sel_wsum; f.sel_meta = a.sel_meta; f.sel_ghist = a.sel_ghist; f.selP = a.selP;
   f.pe = a.part_by_entry ? 1 : 0;
+  f.wt = a.wt;
   f.nstat = (a.nsum != nullptr || a.stats) ? a.kv.nstat : nullptr;
   if (a.stats && a.keysel != nullptr) {
     f.keys = 1;
@@ -1312,6 +1320,75 @@ FinalArgs final_args(const AttnLaunch &a) {
 // Longest row list of a fast step.
 long long fast_rows(const AttnLaunch &a) {
   return (long long)std::min(a.n_sink, a.max_len) + std::min(a.window, a.max_len) + a.sel_k;
+}
+
+// Planning from host-known per-entry row counts (AttnLaunch::len_host).
+bool tabled(const AttnLaunch &a) {
+  return a.len_host != nullptr && a.batch_n > 0 && a.batch_n <= kMaxListed;
+}
+
+long long host_max(const AttnLaunch &a) {
+  long long m = 1;
+  for (int z = 0; z < a.batch_n; ++z) m = std::max<long long>(m, a.len_host[z]);
+  return m;
+}
+
+// Chunk for about R rows per block: a multiple of the granule, at most
+// max_chunk, and at least what keeps every entry within the stride.
+long long table_chunk(const AttnLaunch &a, long long R, int max_chunk) {
+  const long long lmax = host_max(a);
+  long long c = std::max(R, (lmax + a.plan.stride - 1) / a.plan.stride);
+  c = (c + kSplitGranule - 1) / kSplitGranule * kSplitGranule;
+  return std::max<long long>(kSplitGranule, std::min<long long>(c, max_chunk));
+}
+
+// Splits of every entry at this chunk (at least one, so that an entry with
+// no rows still writes its neutral partials and takes its fused append);
+// the table in a.wt, the total number of entry-splits returned (-1 when it
+// does not fit the 16-bit table).
+long long fill_table(AttnLaunch &a, long long chunk) {
+  long long acc = 0;
+  a.wt.n = a.batch_n;
+  a.wt.cum[0] = 0;
+  int smax = 1;
+  for (int z = 0; z < a.batch_n; ++z) {
+    const long long L = std::max<long long>(a.len_host[z], 0);
+    const long long c = std::max<long long>(1, (L + chunk - 1) / chunk);
+    if (c > a.plan.stride) return -1;  // more splits than the partials hold
+    smax = std::max<int>(smax, (int)c);
+    acc += c;
+    if (acc > 65535) return -1;
+    a.wt.cum[z + 1] = (uint16_t)acc;
+  }
+  a.plan.chunk = (int)chunk;
+  a.plan.splits = smax;
+  return acc;
+}
+
+// Entry-splits of the table at this chunk, without filling it.
+long long table_total(const AttnLaunch &a, long long chunk) {
+  long long acc = 0;
+  for (int z = 0; z < a.batch_n; ++z)
+    acc += std::max<long long>(1, (std::max<long long>(a.len_host[z], 0) + chunk - 1) / chunk);
+  return acc;
+}
+
+// One share alone: the smallest chunk of at least min_chunk rows whose
+// blocks fit one wave of resident blocks, at most max_chunk rows per block
+// (more waves past that).
+bool plan_table(AttnLaunch &a, int slots, int min_chunk, int max_chunk) {
+  long long lo = (std::max(min_chunk, kSplitGranule) + kSplitGranule - 1) / kSplitGranule;
+  long long hi = std::max<long long>(lo, max_chunk / kSplitGranule);  // in granules; hi is taken if none fits
+  while (lo < hi) {
+    const long long mid = (lo + hi) / 2;
+    if (table_total(a, table_chunk(a, mid * kSplitGranule, max_chunk)) * a.Hkv <= slots) hi = mid;
+    else lo = mid + 1;
+  }
+  if (fill_table(a, table_chunk(a, lo * kSplitGranule, max_chunk)) < 0) {
+    a.wt.n = 0;
+    return false;
+  }
+  return true;
 }
 
 // Finalize blocks per (sequence, kv head) of a slow step: G combine blocks,
@@ -1330,10 +1407,12 @@ hipError_t slow_t(const AttnLaunch &a_in, hipStream_t st) {
     // gets the same split plan and therefore the same bits
     const int slots = side ? resident_slots<partial_kernel<D, G, false, MODE_SLOW, true>>()
                            : resident_slots<partial_kernel<D, G, false, MODE_SLOW, false>>();
-    a.plan = plan_splits(a.max_len, a.batch_n * a.Hkv, slots, a.plan.stride, kMaxSlowChunk, true);
+    a.wt.n = 0;
+    if (!(tabled(a) && plan_table(a, slots, kSplitGranule, kMaxSlowChunk)))
+      a.plan = plan_splits(a.max_len, a.batch_n * a.Hkv, slots, a.plan.stride, kMaxSlowChunk, true);
   }
   const PartialArgs p = partial_args<D>(a);
-  dim3 grid(a.plan.splits, a.Hkv, a.batch_n);
+  const dim3 grid = a.wt.n > 0 ? dim3((unsigned)a.wt.cum[a.wt.n] * a.Hkv) : dim3(a.plan.splits, a.Hkv, a.batch_n);
   if (a.stats && (!a.evidence || !a.keysel || a.nsum)) return hipErrorInvalidValue;
   if (a.stats)
     hipLaunchKernelGGL((partial_kernel<D, G, PAGED, MODE_SLOW, true, true>), grid, dim3(kThreads), 0, st, p);
@@ -1365,9 +1444,13 @@ SplitPlan fast_plan_t(const AttnLaunch &a) {
 template <int D, int G, bool PAGED>
 hipError_t fast_t(const AttnLaunch &a_in, hipStream_t st) {
   AttnLaunch a = a_in;
-  if (!a.planned) a.plan = fast_plan_t<D, G>(a);
+  a.wt.n = 0;
+  if (!a.planned) {
+    const int slots = resident_slots<partial_kernel<D, G, false, MODE_FAST, false>>();
+    if (!(tabled(a) && plan_table(a, slots, kMinFastTableChunk, kMaxFastChunk))) a.plan = fast_plan_t<D, G>(a);
+  }
   const PartialArgs p = partial_args<D>(a);
-  dim3 grid(a.plan.splits, a.Hkv, a.batch_n);
+  const dim3 grid = a.wt.n > 0 ? dim3((unsigned)a.wt.cum[a.wt.n] * a.Hkv) : dim3(a.plan.splits, a.Hkv, a.batch_n);
   hipLaunchKernelGGL((partial_kernel<D, G, PAGED, MODE_FAST, false>), grid, dim3(kThreads), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1410,12 +1493,78 @@ hipError_t compact_t(const AttnLaunch &a, uint16_t *ck, uint16_t *cv, hipStream_
 // are planned with the same number of rows per workgroup, so the workgroups
 // of the combined grid carry about equal bytes and the grid fills the
 // resident slots about once.
+// The co-launched kernels take both shares' arguments (and a pending
+// selection's) by value: within the 4 KB kernel-argument segment.
+static_assert(2 * sizeof(PartialArgs) + sizeof(SelectLaunch) + 64 <= 4096, "copartial arguments");
+static_assert(2 * sizeof(FinalArgs) + sizeof(SelectLaunch) + 64 <= 4096, "cofinal arguments");
+
+// Both shares of a co-launched step planned from their entries' row counts:
+// the k-wave search of the max_len plan below with the exact block count of
+// each R (a table entry per listed entry, none past its rows).  False when
+// a table does not fit.
+bool plan_step_tables(AttnLaunch &sa, AttnLaunch &fa, int slots) {
+  sa.wt.cum[0] = fa.wt.cum[0] = 0;
+  // one share: the plan of its own launcher (the same chunks, the same bits)
+  if (fa.batch_n == 0) {
+    fa.plan = SplitPlan{1, 0, fa.plan.stride};
+    return plan_table(sa, slots, kSplitGranule, kMaxSlowChunk);
+  }
+  if (sa.batch_n == 0) {
+    sa.plan = SplitPlan{1, 0, sa.plan.stride};
+    return plan_table(fa, slots, kMinFastTableChunk, kMaxFastChunk);
+  }
+  const long long Ls = host_max(sa), Lf = host_max(fa);
+  auto chunk_s = [&](long long R) { return table_chunk(sa, R, kMaxSlowChunk); };
+  auto chunk_f = [&](long long R) { return table_chunk(fa, std::max<long long>(R, kMinFastTableChunk), kMaxFastChunk); };
+  auto blocks_at = [&](long long R) {
+    return table_total(sa, chunk_s(R)) * sa.Hkv + table_total(fa, chunk_f(R)) * fa.Hkv;
+  };
+  auto rows_per_wg = [&](long long R) { return std::max(std::min(chunk_s(R), Ls), std::min(chunk_f(R), Lf)); };
+  const long long Rmax = (std::max(Ls, Lf) + kSplitGranule - 1) / kSplitGranule;  // in granules
+  long long best_cost = -1, best_R = Rmax;
+  for (int k = 1; k <= 16; ++k) {
+    const long long cap = (long long)k * slots;
+    if (blocks_at(Rmax * kSplitGranule) > cap) continue;
+    long long lo = 1, hi = Rmax;  // hi fits
+    while (lo < hi) {
+      const long long mid = (lo + hi) / 2;
+      if (blocks_at(mid * kSplitGranule) <= cap) hi = mid;
+      else lo = mid + 1;
+    }
+    const long long cost = k * rows_per_wg(hi * kSplitGranule);
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best_R = hi;
+    }
+  }
+  const long long R = best_cost < 0 ? kMaxFastChunk : best_R * kSplitGranule;
+  if (fill_table(sa, chunk_s(R)) < 0) {
+    sa.wt.n = 0;
+    return false;
+  }
+  if (fill_table(fa, chunk_f(R)) < 0) {
+    sa.wt.n = fa.wt.n = 0;
+    return false;
+  }
+  if ((long long)sa.wt.cum[sa.wt.n] * sa.Hkv + (long long)fa.wt.cum[fa.wt.n] * fa.Hkv > 0x7fffffffLL) {
+    sa.wt.n = fa.wt.n = 0;
+    return false;
+  }
+  return true;
+}
+
 template <int D, int G, bool PAGED>
 hipError_t step_t(const AttnLaunch &sa_in, const AttnLaunch &fa_in, hipStream_t st,
                   const SelectLaunch *pend) {
   AttnLaunch sa = sa_in, fa = fa_in;
   const int slots = resident_slots<copartial_kernel<D, G, false, false>>();
-  if (sa.batch_n == 0) {  // fast share only (a step that carries a pending selection)
+  sa.wt.n = 0;
+  fa.wt.n = 0;
+  const bool tab = (sa.batch_n == 0 || tabled(sa)) && (fa.batch_n == 0 || tabled(fa)) &&
+                   sa.batch_n + fa.batch_n > 0;
+  if (tab && plan_step_tables(sa, fa, slots)) {
+    // planned from the entries' own row counts
+  } else if (sa.batch_n == 0) {  // fast share only (a step that carries a pending selection)
     fa.plan = plan_splits(fast_rows(fa), fa.batch_n * fa.Hkv, slots, fa.plan.stride, kMaxFastChunk, false);
     sa.plan = SplitPlan{1, 0, sa.plan.stride};
   } else if (fa.batch_n == 0) {  // slow share only
@@ -1462,8 +1611,8 @@ hipError_t step_t(const AttnLaunch &sa_in, const AttnLaunch &fa_in, hipStream_t 
     // no plan within 16 waves: equal rows per workgroup at the fast cap
     plan_at(best_cost < 0 ? kMaxFastChunk : best_R * kSplitGranule);
   }
-  const int ns = sa.plan.splits * sa.Hkv * sa.batch_n;
-  const int nf = fa.plan.splits * fa.Hkv * fa.batch_n;
+  const int ns = sa.wt.n > 0 ? sa.wt.cum[sa.wt.n] * sa.Hkv : sa.plan.splits * sa.Hkv * sa.batch_n;
+  const int nf = fa.wt.n > 0 ? fa.wt.cum[fa.wt.n] * fa.Hkv : fa.plan.splits * fa.Hkv * fa.batch_n;
   const int sgx = slow_final_blocks(sa, G);
   const int ms = sgx * sa.Hkv * sa.batch_n;
   const int mf = G * fa.Hkv * fa.batch_n;

@@ -280,6 +280,7 @@ AttnLaunch slow_launch(const sfi_kv *kv, const KVView &view, bool paged, const S
   a.part_o = carve<float>(ws, w.o);
   a.part_ml = carve<float>(ws, w.ml);
   a.plan.stride = w.stride;  // chunking is planned by the launcher
+  a.len_host = kv->slow_len_host;
   a.logits = carve<float>(ws, w.logits);
   a.lld = kv->max_seq_len;
   a.evidence = evidence;
@@ -310,6 +311,7 @@ AttnLaunch fast_launch(const sfi_kv *kv, const KVView &view, bool paged, const F
   a.part_o = carve<float>(ws, w.o);
   a.part_ml = carve<float>(ws, w.ml);
   a.plan.stride = w.stride;  // chunking is planned by the launcher
+  a.len_host = kv->fast_len_host;
   a.sel_idx = sel_idx;
   a.sel_count = sel_count;
   a.sel_heads = sel_heads;
@@ -348,6 +350,18 @@ sfi_status check_fast(const sfi_kv *kv, const int32_t *sel_idx, const int32_t *s
   return SFI_OK;
 }
 
+// The host row-count hints of a call's lists (sfi_kv::slow_len_host and
+// fast_len_host), read for the entries the call lists.
+sfi_status check_hints(const sfi_kv *kv, int32_t n_slow, int32_t n_fast, long long fast_max) {
+  if (kv->slow_len_host)
+    for (int32_t z = 0; z < n_slow; ++z)
+      if (kv->slow_len_host[z] < 0 || kv->slow_len_host[z] > kv->max_seq_len) return SFI_ERR_RANGE;
+  if (kv->fast_len_host)
+    for (int32_t z = 0; z < n_fast; ++z)
+      if (kv->fast_len_host[z] < 0 || kv->fast_len_host[z] > fast_max) return SFI_ERR_RANGE;
+  return SFI_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -382,6 +396,7 @@ sfi_status sfi_slow_step(const sfi_kv *kv, const int32_t *batch_ids, int32_t bat
   if (!q || !out) return SFI_ERR_NULL;
   if (!aligned(q, 16) || !aligned(out, 16)) return SFI_ERR_RANGE;
   if ((evidence || key_norm) && ld < kv->max_seq_len) return SFI_ERR_RANGE;
+  if ((s = check_hints(kv, batch_n, 0, 0)) != SFI_OK) return s;
   const SlowWs w = slow_ws(kv);
   if (!ws) return SFI_ERR_NULL;
   if (!aligned(ws, kAlign)) return SFI_ERR_RANGE;
@@ -420,6 +435,7 @@ sfi_status sfi_decode_step(const sfi_kv *kv, const int32_t *slow_ids, int32_t n_
   if (n_fast > 0 && (s = check_fast(kv, sel_idx, sel_count, sel_heads, sel_k, n_sink, window)) != SFI_OK)
     return s;
   if (sel_k < 0 || n_sink < 0 || window < 0) return SFI_ERR_RANGE;
+  if ((s = check_hints(kv, n_slow, n_fast, (long long)n_sink + window + sel_k)) != SFI_OK) return s;
   const SlowWs sw = slow_ws(kv);
   const FastWs fw = fast_ws(kv, sel_k, n_sink, window);
   if (!ws) return SFI_ERR_NULL;
@@ -475,6 +491,7 @@ sfi_status sfi_decode_step_select(const sfi_kv *kv, const sfi_select_params *p,
   if (n_fast > 0 &&
       (s = check_fast(kv, sel_idx, sel_count, kv->Hkv, p->k, p->n_sink, p->window)) != SFI_OK)
     return s;
+  if ((s = check_hints(kv, n_slow, n_fast, (long long)p->n_sink + p->window + p->k)) != SFI_OK) return s;
   const SlowWs sw = slow_ws(kv);
   const FastWs fw = fast_ws(kv, p->k, p->n_sink, p->window);
   const SelWs ew = select_ws(kv->B, kv->Hkv, kv->max_seq_len);
@@ -560,6 +577,7 @@ sfi_status sfi_decode_layer_step(const sfi_kv *kv, const sfi_select_params *p, c
   if (n_fast > 0 &&
       (s = check_fast(kv, sel_idx, sel_count, kv->Hkv, p->k, p->n_sink, p->window)) != SFI_OK)
     return s;
+  if ((s = check_hints(kv, n_slow, n_fast, (long long)p->n_sink + p->window + p->k)) != SFI_OK) return s;
   const SlowWs sw = slow_ws(kv);
   const FastWs fw = fast_ws(kv, p->k, p->n_sink, p->window);
   const SelWs ew = select_ws(kv->B, kv->Hkv, kv->max_seq_len);
@@ -663,6 +681,7 @@ sfi_status sfi_fast_step(const sfi_kv *kv, const int32_t *batch_ids, int32_t bat
   if (!q || !out) return SFI_ERR_NULL;
   if (!aligned(q, 16) || !aligned(out, 16)) return SFI_ERR_RANGE;
   if ((s = check_fast(kv, sel_idx, sel_count, sel_heads, sel_k, n_sink, window)) != SFI_OK) return s;
+  if ((s = check_hints(kv, 0, batch_n, (long long)n_sink + window + sel_k)) != SFI_OK) return s;
   const FastWs w = fast_ws(kv, sel_k, n_sink, window);
   if (!ws) return SFI_ERR_NULL;
   if (!aligned(ws, kAlign)) return SFI_ERR_RANGE;
@@ -693,6 +712,7 @@ sfi_status sfi_fast_step_noalloc(const sfi_kv *kv, const int32_t *batch_ids, int
   const FastWs wfull = fast_ws(kv, sel_k, n_sink, window);
   AttnLaunch a = fast_launch(kv, view, paged, wfull, ptr, batch_ids, batch_n, q, out, sel_idx, sel_count,
                              sel_heads, sel_k, n_sink, window);
+  a.len_host = nullptr;  // planned from the bound alone, whatever the hints say
   const SplitPlan plan = plan_fast(a);
   const size_t rows = (size_t)batch_n * kv->Hq * plan.splits;
   const size_t ml = align_up(rows * kv->d * sizeof(float));
@@ -778,6 +798,7 @@ sfi_status sfi_fast_step_compact(const sfi_kv *kv, const int32_t *batch_ids, int
   if (batch_n == 0) return SFI_OK;
   AttnLaunch a = fast_launch(kv, view, paged, w, ws, batch_ids, batch_n, q, out, sel_idx, sel_count,
                              sel_heads, sel_k, n_sink, window);
+  a.len_host = nullptr;  // the index-gather kernel's plan
   a.ck = ck;
   a.cv = cv;
   const hipStream_t st = static_cast<hipStream_t>(stream);

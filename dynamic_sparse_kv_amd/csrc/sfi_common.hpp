@@ -152,6 +152,35 @@ __device__ __forceinline__ PairBlock pair_block(int w, int S, int H, int Z, bool
   return {blk, pair % H, pair / H};
 }
 
+// Split counts of a grid share planned from the lengths of its listed
+// entries (host-known): entry z of the batch list takes splits [0, c_z) of
+// every kv head, cum[z] = c_0 + ... + c_{z-1}.  The share's blocks are
+// numbered w = (cum[z] + s) * Hkv + g (heads fastest), so no block lands
+// past an entry's rows.  n = 0: no table (every entry takes the planned
+// number of splits and the blocks past its rows exit at once).
+constexpr int kMaxListed = 256;
+struct WorkTable {
+  int n;
+  uint16_t cum[kMaxListed + 1];
+};
+
+// Entry, head and split of block w of a tabled share.
+__device__ __forceinline__ PairBlock table_block(const WorkTable &t, int w, int Hkv) {
+  const int e = w / Hkv;
+  int lo = 0, hi = t.n - 1;  // the last entry z with cum[z] <= e
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((int)t.cum[mid] <= e) lo = mid;
+    else hi = mid - 1;
+  }
+  return {e - (int)t.cum[lo], w - e * Hkv, lo};
+}
+
+// Splits of entry z: its table count, or the planned number.
+__device__ __forceinline__ int entry_splits(const WorkTable &t, int z, int planned) {
+  return t.n > 0 ? (int)t.cum[z + 1] - (int)t.cum[z] : planned;
+}
+
 // Linear id of the block in its grid (x fastest, the dispatch order).
 __device__ __forceinline__ int linear_block() {
   return (int)(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));

@@ -17,6 +17,13 @@ constexpr int kMaxSplits = 512;
 #define SFI_MAX_FAST_CHUNK 1024
 #endif
 constexpr int kMaxFastChunk = SFI_MAX_FAST_CHUNK;  // fast-step chunks stage their row ids in LDS
+// Fewest rows per fast-step block when the plan comes from per-entry row
+// counts: each block pays an index -> page -> row prologue before its
+// gathers stream.
+#ifndef SFI_MIN_FAST_TABLE_CHUNK
+#define SFI_MIN_FAST_TABLE_CHUNK 512
+#endif
+constexpr int kMinFastTableChunk = SFI_MIN_FAST_TABLE_CHUNK;
 // Rows per workgroup of a dense or slow step at most.  Splits are planned
 // from the longest sequence of the batch (its lengths are on the device), so
 // without a cap a long sequence in a ragged batch gets a few huge chunks
@@ -107,6 +114,12 @@ struct AttnLaunch {
   bool part_by_entry;
   // plan fixed by the caller (launch_fast only): `plan` is used as given
   bool planned;
+  // [host] the listed entries' row counts (slow and dense: the sequence
+  // length; fast: a bound on the row list's length), in list order, or
+  // null.  Set, the launchers plan the grid from them (a work table: no
+  // block past an entry's rows) instead of from max_len.
+  const int32_t *len_host;
+  WorkTable wt;  // filled by the launcher
 };
 
 hipError_t launch_slow(const AttnLaunch &a, hipStream_t st);

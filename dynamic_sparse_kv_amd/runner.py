@@ -16,6 +16,17 @@ import torch
 from . import sfi
 
 
+class LenHints(tuple):
+    """Host row-count hints of one step's lists (int32 arrays in list
+    order): [0] the slow list, [1] the fast list, and .fast_old / .fast_new
+    the two halves of the fast list that the pipelined schedule issues."""
+
+    def __new__(cls, slow, fast, fast_old, fast_new):
+        t = super().__new__(cls, (slow, fast))
+        t.fast_old, t.fast_new = fast_old, fast_new
+        return t
+
+
 def _dev_i32(x, device):
     return torch.as_tensor(np.ascontiguousarray(x, dtype=np.int32), device=device)
 
@@ -37,8 +48,12 @@ class DecodePlan:
         self.seq_len_host = lens.astype(np.int32)
         self.seq_len = _dev_i32(lens, device)               # [steps][B]
         self.k_seq = None
+        self.k_div = k_div
+        self.k_seq_host = None
         if k_div > 0:
-            self.k_seq = _dev_i32(np.minimum(k_cap, lens // k_div), device)
+            self.k_seq_host = np.minimum(k_cap, lens // k_div).astype(np.int32)
+            self.k_seq = _dev_i32(self.k_seq_host, device)
+        self._hints = {}
         slow_ids = np.zeros((steps, B), dtype=np.int32)
         fast_ids = np.zeros((steps, B), dtype=np.int32)
         self.n_slow = np.zeros(steps, dtype=np.int64)
@@ -67,6 +82,7 @@ class DecodePlan:
             self.n_fast_new[s] = len(ni)
         self.fast_old_ids = _dev_i32(old_ids, device)
         self.fast_new_ids = _dev_i32(new_ids, device)
+        self.fast_old_ids_host, self.fast_new_ids_host = old_ids, new_ids
 
     def slow_list(self, s: int):
         """Step s's slow-sequence list, or None when it is every sequence in
@@ -77,6 +93,29 @@ class DecodePlan:
     def fast_list(self, s: int):
         """Step s's fast-sequence list, or None when it is every sequence."""
         return None if self.n_fast[s] == self.B else self.fast_ids[s]
+
+    def len_hints(self, s: int, n_sink: int, window: int, k: int):
+        """Host row-count hints of step s's lists (sfi.with_len_hints): the
+        slow sequences' lengths, and for each fast sequence its sinks and
+        window within its length plus its selection's size bound (k, or
+        min(k, seq_len // k_div) when the plan caps lists by length: a list
+        chosen at an earlier, shorter step is no longer).  Cached, so the
+        arrays outlive the calls that read them."""
+        key = (s, n_sink, window, k)
+        h = self._hints.get(key)
+        if h is None:
+            lens = self.seq_len_host[s].astype(np.int64)
+            kk = np.full(self.B, k, dtype=np.int64)
+            if self.k_seq_host is not None:
+                kk = np.minimum(kk, self.k_seq_host[s])
+            fb = np.minimum(lens, n_sink + window) + np.minimum(kk, np.maximum(lens - n_sink - window, 0))
+            slow = self.slow[s]
+            old = self.fast_old_ids_host[s, : self.n_fast_old[s]]
+            new = self.fast_new_ids_host[s, : self.n_fast_new[s]]
+            i32 = lambda a: np.ascontiguousarray(a, dtype=np.int32)
+            h = LenHints(i32(lens[slow]), i32(fb[~slow]), i32(fb[old]), i32(fb[new]))
+            self._hints[key] = h
+        return h
 
 
 def stats_prior_steps(plan: DecodePlan) -> np.ndarray:
@@ -166,19 +205,27 @@ class SFIDecoder:
     # new_rows = (k_new, v_new), each [B][Hkv][d] bf16 (or [B][1][Hkv][d]):
     # the call also appends each listed sequence's row at cache row
     # seq_len - 1 (the fused append of the sfi_kv description).
-    def _kvx(self, new_rows, stats_valid: bool = False):
+    def _kvx(self, new_rows, stats_valid: bool = False, len_hints=None):
         kv = self.kv if new_rows is None else sfi.with_new_rows(self.kv, new_rows[0], new_rows[1])
         if stats_valid:
             if self.nstat is None:
                 raise ValueError("this decoder keeps no key-norm statistics")
             kv = sfi.with_norm_stats(kv, self.nstat, True)
+        if len_hints is not None:
+            kv = sfi.with_len_hints(kv, len_hints[0], len_hints[1])
         return kv
 
+    def hints(self, plan: "DecodePlan", s: int):
+        """Row-count hints of step s's lists for this decoder's fast state."""
+        return plan.len_hints(s, self.n_sink, self.window, self.k)
+
     def slow(self, q, seq_len, batch_ids, batch_n: int, stream=None, select: bool = True, out=None,
-             k_seq=None, new_rows=None):
-        """Dense step + evidence for the listed sequences, then the selector."""
+             k_seq=None, new_rows=None, len_hints=None):
+        """Dense step + evidence for the listed sequences, then the selector.
+        len_hints = (slow lengths, unused) as DecodePlan.len_hints gives."""
         self.kv.seq_len = seq_len.data_ptr() if torch.is_tensor(seq_len) else seq_len
-        sfi.sfi_slow_step(self._kvx(new_rows), batch_ids, batch_n, q, self.out if out is None else out,
+        sl = None if len_hints is None else (len_hints[0], None)
+        sfi.sfi_slow_step(self._kvx(new_rows, len_hints=sl), batch_ids, batch_n, q, self.out if out is None else out,
                           self.evidence, self.key_norm, self.ld, self.ws_slow, self.ws_slow_bytes,
                           stream)
         if select:
@@ -202,15 +249,19 @@ class SFIDecoder:
         self.kv.seq_len = seq_len.data_ptr() if torch.is_tensor(seq_len) else seq_len
         sfi.sfi_append_kv(self.kv, batch_ids, batch_n, k_new, v_new, int(k_new.shape[1]), stream)
 
-    def dense(self, q, seq_len, batch_ids, batch_n: int, stream=None, new_rows=None):
-        """Plain dense attention (no evidence): the full-KV comparator."""
+    def dense(self, q, seq_len, batch_ids, batch_n: int, stream=None, new_rows=None, len_hints=None):
+        """Plain dense attention (no evidence): the full-KV comparator;
+        len_hints = the listed sequences' lengths (host int32), or None."""
         self.kv.seq_len = seq_len.data_ptr() if torch.is_tensor(seq_len) else seq_len
-        sfi.sfi_slow_step(self._kvx(new_rows), batch_ids, batch_n, q, self.out, None, None, self.ld,
+        sl = None if len_hints is None else (len_hints, None)
+        sfi.sfi_slow_step(self._kvx(new_rows, len_hints=sl), batch_ids, batch_n, q, self.out, None, None, self.ld,
                           self.ws_slow, self.ws_slow_bytes, stream)
 
-    def fast(self, q, seq_len, batch_ids, batch_n: int, stream=None, out=None, new_rows=None):
+    def fast(self, q, seq_len, batch_ids, batch_n: int, stream=None, out=None, new_rows=None,
+             len_hints=None):
         self.kv.seq_len = seq_len.data_ptr() if torch.is_tensor(seq_len) else seq_len
-        sfi.sfi_fast_step(self._kvx(new_rows), batch_ids, batch_n, q, self.sel_idx, self.sel_count, self.Hkv,
+        fl = None if len_hints is None else (None, len_hints[1])
+        sfi.sfi_fast_step(self._kvx(new_rows, len_hints=fl), batch_ids, batch_n, q, self.sel_idx, self.sel_count, self.Hkv,
                           self.k, self.n_sink, self.window, self.out if out is None else out,
                           self.ws_fast, self.ws_fast_bytes, stream)
 
@@ -232,11 +283,11 @@ class SFIDecoder:
                                   self.out if out is None else out, self.ws_fast, self.ws_fast_bytes, stream)
 
     def co_step(self, q, seq_len, slow_ids, n_slow: int, fast_ids, n_fast: int, stream=None,
-                out=None, select: bool = True, k_seq=None, new_rows=None):
+                out=None, select: bool = True, k_seq=None, new_rows=None, len_hints=None):
         """Slow steps of slow_ids and fast steps of fast_ids in one co-launched
         pass, then the selector of the slow sequences."""
         self.kv.seq_len = seq_len.data_ptr() if torch.is_tensor(seq_len) else seq_len
-        sfi.sfi_decode_step(self._kvx(new_rows), slow_ids, n_slow, fast_ids, n_fast, q,
+        sfi.sfi_decode_step(self._kvx(new_rows, len_hints=len_hints), slow_ids, n_slow, fast_ids, n_fast, q,
                             self.out if out is None else out, self.evidence, self.key_norm, self.ld,
                             self.sel_idx, self.sel_count, self.Hkv, self.k, self.n_sink, self.window,
                             self.ws_step, self.ws_step_bytes, stream)
@@ -244,7 +295,7 @@ class SFIDecoder:
             self.slow_select_only(self.kv.seq_len, slow_ids, n_slow, stream, k_seq=k_seq)
 
     def step_select(self, q, seq_len, slow_ids, n_slow: int, fast_ids, n_fast: int, stream=None,
-                    out=None, k_seq=None, new_rows=None, use_stats: bool = False):
+                    out=None, k_seq=None, new_rows=None, use_stats: bool = False, len_hints=None):
         """One call for the step and the slow sequences' new selections
         (sfi_decode_step_select): the slow step forms the selector's prior
         statistics, so the selection runs only its key and pick passes.
@@ -254,7 +305,7 @@ class SFIDecoder:
         self.kv.seq_len = seq_len.data_ptr() if torch.is_tensor(seq_len) else seq_len
         self.params.k_per_seq = None if k_seq is None else k_seq.data_ptr()
         try:
-            sfi.sfi_decode_step_select(self._kvx(new_rows, use_stats), self.params, slow_ids, n_slow, fast_ids, n_fast, q,
+            sfi.sfi_decode_step_select(self._kvx(new_rows, use_stats, len_hints), self.params, slow_ids, n_slow, fast_ids, n_fast, q,
                                        self.out if out is None else out, self.evidence, self.key_norm,
                                        self.ld, self.sel_idx, self.sel_count, self.fused, self.ws_stepsel,
                                        self.ws_stepsel_bytes, stream)
@@ -262,7 +313,7 @@ class SFIDecoder:
             self.params.k_per_seq = None
 
     def layer_step(self, plan: "DecodePlan", s: int, q_steps, pending=None, stream=None, out=None,
-                   new_kv=None):
+                   new_kv=None, hints: bool = True):
         """Decode step s of this layer in a stack (sfi_decode_layer_step): the
         previous layer's deferred selection (pending, an sfi_deferred or None)
         runs inside this call's grids and this layer's own selection is
@@ -273,7 +324,8 @@ class SFIDecoder:
         ks = None if plan.k_seq is None else plan.k_seq[s]
         ns, nf = int(plan.n_slow[s]), int(plan.n_fast[s])
         self.kv.seq_len = plan.seq_len[s].data_ptr()
-        kvx = self._kvx(None if new_kv is None else (new_kv[0][s], new_kv[1][s]))
+        kvx = self._kvx(None if new_kv is None else (new_kv[0][s], new_kv[1][s]),
+                        len_hints=self.hints(plan, s) if hints else None)
         self.params.k_per_seq = None if ks is None else ks.data_ptr()
         own = sfi.sfi_deferred()
         try:
@@ -325,7 +377,7 @@ class SFIDecoder:
 
     # -- one decode step of a planned run ------------------------------------
     def step(self, plan: DecodePlan, s: int, q_steps, stream=None, out=None, co: bool = True,
-             fused_select: bool = True, new_kv=None, fused_append: bool = True):
+             fused_select: bool = True, new_kv=None, fused_append: bool = True, hints: bool = True):
         """Decode step s: q_steps is the device tensor [steps][B][Hq][d].
 
         new_kv = (K_new, V_new), each [steps][B][1][Hkv][d]: the step appends
@@ -336,8 +388,11 @@ class SFIDecoder:
         co-launches its slow and fast shares and refreshes the slow
         sequences' selections (sfi_decode_step_select; with
         fused_select=False: sfi_decode_step, then sfi_select); with co=False
-        the slow step, the selector and the fast step are separate calls."""
+        the slow step, the selector and the fast step are separate calls.
+        hints: pass the step's host row-count hints (DecodePlan.len_hints),
+        so the launches plan each sequence's workgroups from its own length."""
         q = q_steps[s]
+        lh = self.hints(plan, s) if hints else None
         sl = plan.seq_len[s]
         ks = None if plan.k_seq is None else plan.k_seq[s]
         ns, nf = int(plan.n_slow[s]), int(plan.n_fast[s])
@@ -353,18 +408,18 @@ class SFIDecoder:
         self._note_stats(plan, s, new_kv is not None, ns_refresh=combined)
         if combined:
             self.step_select(q, sl, sids, ns, fids, nf, stream, out=out, k_seq=ks, new_rows=nr,
-                             use_stats=use_stats)
+                             use_stats=use_stats, len_hints=lh)
             return
         if co and ns and nf:
-            self.co_step(q, sl, sids, ns, fids, nf, stream, out=out, k_seq=ks, new_rows=nr)
+            self.co_step(q, sl, sids, ns, fids, nf, stream, out=out, k_seq=ks, new_rows=nr, len_hints=lh)
             return
         if ns:
-            self.slow(q, sl, sids, ns, stream, out=out, k_seq=ks, new_rows=nr)
+            self.slow(q, sl, sids, ns, stream, out=out, k_seq=ks, new_rows=nr, len_hints=lh)
         if nf:
-            self.fast(q, sl, fids, nf, stream, out=out, new_rows=nr)
+            self.fast(q, sl, fids, nf, stream, out=out, new_rows=nr, len_hints=lh)
 
     def run_pipelined(self, plan: DecodePlan, q_steps, s_begin: int, s_end: int, stream_a,
-                      stream_b, stream_c, out_steps):
+                      stream_b, stream_c, out_steps, hints: bool = True):
         """Steps [s_begin, s_end) as three overlapping chains.
 
         A: slow steps (dense attention + evidence), C: the selector, B: fast
@@ -400,13 +455,15 @@ class SFIDecoder:
             sl = plan.seq_len[s]
             out = out_steps[s]
             ns = int(plan.n_slow[s])
+            lh = self.hints(plan, s) if hints else None
             c_ev = None
             if ns:
                 ev_buf, kn_buf = copies[s % 2]
                 if last_c_parity[s % 2] is not None:
                     stream_a.wait_event(last_c_parity[s % 2])
                 self.kv.seq_len = sl.data_ptr()
-                sfi.sfi_slow_step(self.kv, plan.slow_ids[s], ns, q, out, ev_buf, kn_buf, self.ld,
+                kvs = self.kv if lh is None else self._kvx(None, len_hints=(lh[0], None))
+                sfi.sfi_slow_step(kvs, plan.slow_ids[s], ns, q, out, ev_buf, kn_buf, self.ld,
                                   self.ws_slow, self.ws_slow_bytes, stream_a)
                 a_ev = ev()
                 a_ev.record(stream_a)
@@ -421,11 +478,13 @@ class SFIDecoder:
                 last_c_parity[s % 2] = c_ev
             no, nn = int(plan.n_fast_old[s]), int(plan.n_fast_new[s])
             if no:
-                self.fast(q, sl, plan.fast_old_ids[s], no, stream_b, out=out)
+                self.fast(q, sl, plan.fast_old_ids[s], no, stream_b, out=out,
+                          len_hints=None if lh is None else (None, lh.fast_old))
             if nn:
                 if prev_c is not None:
                     stream_b.wait_event(prev_c)
-                self.fast(q, sl, plan.fast_new_ids[s], nn, stream_b, out=out)
+                self.fast(q, sl, plan.fast_new_ids[s], nn, stream_b, out=out,
+                          len_hints=None if lh is None else (None, lh.fast_new))
             b_ev = ev()
             b_ev.record(stream_b)
             prev_b = b_ev
@@ -438,7 +497,7 @@ class SFIDecoder:
         stream_a.wait_event(end_c)
 
     def run_two_streams(self, plan: DecodePlan, q_steps, s_begin: int, s_end: int, stream_a,
-                        stream_b, out_steps=None, new_kv=None):
+                        stream_b, out_steps=None, new_kv=None, hints: bool = True):
         """Steps [s_begin, s_end) as two overlapping chains.
 
         Stream A carries each step's slow steps and selector, stream B its fast
@@ -468,12 +527,13 @@ class SFIDecoder:
             sl = plan.seq_len[s]
             out = None if out_steps is None else out_steps[s]
             ns, nf = int(plan.n_slow[s]), int(plan.n_fast[s])
+            lh = self.hints(plan, s) if hints else None
             if ns:
                 sids = plan.slow_list(s)
                 nr = None if new_kv is None else (new_kv[0][s], new_kv[1][s])
                 if out_steps is None and prev_b is not None:
                     stream_a.wait_event(prev_b)
-                self.slow(q, sl, sids, ns, stream_a, out=out, select=False, new_rows=nr)
+                self.slow(q, sl, sids, ns, stream_a, out=out, select=False, new_rows=nr, len_hints=lh)
                 if prev_b is not None:
                     stream_a.wait_event(prev_b)
                 self.slow_select_only(sl, sids, ns, stream_a,
@@ -485,7 +545,7 @@ class SFIDecoder:
             if nf:
                 fids = plan.fast_list(s)
                 nr = None if new_kv is None else (new_kv[0][s], new_kv[1][s])
-                self.fast(q, sl, fids, nf, stream_b, out=out, new_rows=nr)
+                self.fast(q, sl, fids, nf, stream_b, out=out, new_rows=nr, len_hints=lh)
             ev_b = ev()
             ev_b.record(stream_b)
             prev_a, prev_b = ev_a, ev_b

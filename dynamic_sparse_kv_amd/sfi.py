@@ -11,6 +11,7 @@ from __future__ import annotations
 import ctypes
 import os
 from typing import Optional
+import numpy as np
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsfi.so")
 
@@ -45,6 +46,7 @@ class sfi_kv(ctypes.Structure):
         ("cap", _c_int), ("max_seq_len", _c_int),
         ("k_new", _vp), ("v_new", _vp),
         ("norm_stats", _vp), ("norm_stats_valid", _c_int),
+        ("slow_len_host", _vp), ("fast_len_host", _vp),
     ]
 
 
@@ -214,6 +216,28 @@ def with_norm_stats(kv: sfi_kv, norm_stats, valid: bool) -> sfi_kv:
     ctypes.pointer(x)[0] = kv
     x.norm_stats = _ptr(norm_stats)
     x.norm_stats_valid = 1 if valid else 0
+    return x
+
+
+def _host_i32(a) -> Optional[int]:
+    if a is None:
+        return None
+    if not (isinstance(a, np.ndarray) and a.dtype == np.int32 and a.flags.c_contiguous and a.ndim == 1):
+        raise TypeError("row-count hints are 1-D C-contiguous int32 numpy arrays")
+    return a.ctypes.data
+
+
+def with_len_hints(kv: sfi_kv, slow_lens=None, fast_lens=None) -> sfi_kv:
+    """A copy of kv carrying host row-count hints for the call's lists, in
+    list order: slow_lens the slow entries' seq_len, fast_lens bounds on the
+    fast entries' row lists (min(seq_len, n_sink + window) plus the entry's
+    selection count).  The launchers then plan each entry's workgroups from
+    its own rows.  The copy keeps the arrays referenced."""
+    x = sfi_kv()
+    ctypes.pointer(x)[0] = kv
+    x.slow_len_host = _host_i32(slow_lens)
+    x.fast_len_host = _host_i32(fast_lens)
+    x._hold = (slow_lens, fast_lens)
     return x
 
 

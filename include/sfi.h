@@ -107,7 +107,24 @@ typedef enum {
  * weights and its finalize runs the selection's key pass, one launch fewer
  * (Soft-NMS and exclusivity keep the separate passes).  The norms are fp32
  * roundings summed in fp64, so the prior matches the one formed from the
- * pass up to rounding (near-tie keys may select differently). */
+ * pass up to rounding (near-tie keys may select differently).
+ *
+ * Row-count hints (launch planning only; they change no step of the
+ * method, and serve batches whose sequences differ much in length):
+ * slow_len_host and fast_len_host are
+ * host arrays in the order of the call's slow list and fast list (the one
+ * list of sfi_slow_step and sfi_fast_step), read during the call only.
+ * slow_len_host[z] is the seq_len of the z-th slow entry (0..max_seq_len);
+ * fast_len_host[z] bounds the rows of the z-th fast entry's row list, at
+ * least min(seq_len, n_sink + window) plus the entry's largest sel_count
+ * (0..n_sink + window + sel_k).  Set, the split plan gives each listed entry
+ * only the workgroups its own rows need (a work table of at most 256
+ * entries; longer lists plan from max_seq_len) instead of max_seq_len's
+ * worth each.  A hint outside its range is SFI_ERR_RANGE; one below the true
+ * count leaves the rows past it out of the result (wrong numbers, never an
+ * out-of-bounds access).  Different chunking changes the fp32 summation
+ * order, so results with and without hints agree up to rounding.
+ * sfi_fast_step_noalloc and sfi_fast_step_compact ignore them. */
 typedef struct sfi_kv {
   const uint16_t *k;
   const uint16_t *v;
@@ -123,6 +140,8 @@ typedef struct sfi_kv {
   const uint16_t *v_new;
   double *norm_stats;         /* NULL, or [B][Hkv][2] key-norm statistics (above) */
   int32_t norm_stats_valid;   /* [host] 1: norm_stats is current for the slow sequences */
+  const int32_t *slow_len_host; /* [host] NULL, or the slow entries' seq_len (above) */
+  const int32_t *fast_len_host; /* [host] NULL, or bounds on the fast entries' row lists */
 } sfi_kv;
 
 enum { SFI_SCORE_FUSED = 0, SFI_SCORE_RAW = 1 };

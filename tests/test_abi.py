@@ -216,6 +216,48 @@ def test_decode_step_validation():
     assert call(kv, n_slow=0, n_fast=0, ws_bytes=need) == sfi.SFI_OK
 
 
+def test_len_hints_validation():
+    """Host row-count hints: each listed entry's hint is checked against its
+    range (slow: 0..max_seq_len; fast: 0..n_sink + window + sel_k) before
+    anything is enqueued; entries past the list are not read."""
+    L = sfi.lib()
+    ok_s = np.array([900, 0, -5], dtype=np.int32)      # third entry never listed below
+    bad_s = np.array([901], dtype=np.int32)
+    neg = np.array([-1], dtype=np.int32)
+    fmax = np.array([4 + 256 + 64], dtype=np.int32)
+    fbad = np.array([4 + 256 + 65], dtype=np.int32)
+
+    def slow(kv, batch_n=1):
+        return L.sfi_slow_step(ctypes.byref(kv), None, batch_n, FAKE, FAKE, None, None, 900, FAKE, 1 << 40, None)
+
+    def fast(kv, batch_n=1):
+        return L.sfi_fast_step(ctypes.byref(kv), None, batch_n, FAKE, FAKE, FAKE, 2, 64, 4, 256, FAKE, FAKE,
+                               1 << 40, None)
+
+    def step(kv, n_slow=1, n_fast=1):
+        return L.sfi_decode_step(ctypes.byref(kv), FAKE, n_slow, FAKE, n_fast, FAKE, FAKE, FAKE, None, 1000,
+                                 FAKE, FAKE, 2, 64, 4, 256, FAKE, 1 << 40, None)
+
+    H = sfi.with_len_hints
+    assert slow(H(_kv(max_seq_len=900), bad_s)) == sfi.SFI_ERR_RANGE
+    assert slow(H(_kv(max_seq_len=900), neg)) == sfi.SFI_ERR_RANGE
+    assert slow(H(_kv(max_seq_len=900), ok_s), batch_n=0) == sfi.SFI_OK
+    assert fast(H(_kv(), None, fbad)) == sfi.SFI_ERR_RANGE
+    assert fast(H(_kv(), None, neg)) == sfi.SFI_ERR_RANGE
+    assert fast(H(_kv(), None, fmax), batch_n=0) == sfi.SFI_OK
+    assert fast(H(_kv(), bad_s, None), batch_n=0) == sfi.SFI_OK       # a fast step reads no slow hint
+    assert step(H(_kv(), None, fbad)) == sfi.SFI_ERR_RANGE
+    assert step(H(_kv(max_seq_len=900), bad_s, fmax)) == sfi.SFI_ERR_RANGE
+    assert step(H(_kv(max_seq_len=900), ok_s[:2], fmax), n_slow=0, n_fast=0) == sfi.SFI_OK
+    kv = H(_kv(), ok_s, fmax)
+    assert kv.slow_len_host == ok_s.ctypes.data and kv.fast_len_host == fmax.ctypes.data
+    assert kv.B == 2 and _kv().slow_len_host is None
+    with pytest.raises(TypeError):
+        H(_kv(), np.array([1, 2], dtype=np.int64))
+    with pytest.raises(TypeError):
+        H(_kv(), None, [5])
+
+
 def test_layer_step_validation():
     """sfi_decode_layer_step / sfi_run_deferred: argument checks and the
     cases with nothing to launch (no kernel runs here)."""

@@ -116,7 +116,7 @@ def test_full_size_stack_pipeline_128k():
         for K, V, q, pipe, ref in layers:
             pend = pipe.layer_step(plan, s, q, pending=pend)
             ref.step_select(q[s], plan.seq_len[s], plan.slow_ids[s], int(plan.n_slow[s]), plan.fast_ids[s],
-                            int(plan.n_fast[s]))
+                            int(plan.n_fast[s]), len_hints=ref.hints(plan, s))
             torch.cuda.synchronize()
             assert torch.equal(pipe.out.view(torch.int32), ref.out.view(torch.int32)), s
     sfi.sfi_run_deferred(pend)

@@ -893,6 +893,87 @@ def test_decode_run_mixed_batch_co_launch():
     assert ties == 0
 
 
+@pytest.mark.parametrize("paged", [False, True])
+def test_ragged_run_with_len_hints(paged):
+    """A ragged batch (six sequences of 60 to 9000 keys, each with its own
+    slow/fast schedule, rows appended by the steps): with the host row-count
+    hints every launch plans each sequence's workgroups from its own length
+    (a work table).  Outputs, fused scores and selections follow the
+    oracle's decode run of every sequence; a run without hints agrees within
+    tolerance and selects the same keys; a step given over-stated hints
+    agrees with the exact ones within tolerance."""
+    _say(f"ragged run with length hints, paged={paged}")
+    B, Hq, Hkv, d, k = 6, 32, 8, 128, 200
+    ctx = np.array([9000, 60, 2500, 300, 6000, 1200])
+    steps = 10
+    rng = np.random.default_rng(11)
+    slow = rng.random((steps, B)) < 0.35
+    slow[0] = True
+    assert any(slow[s].any() and (~slow[s]).any() for s in range(steps))
+    cap = int(ctx.max()) + steps + 8
+    K, V = _rand_kv(B, Hkv, cap, d, seed=710, hh=9)
+    q = _rand_q((steps, B, Hq, d), seed=711)
+    Kb, Vb, qb = _bits(K), _bits(V), _bits(q)
+    refs = [O.decode_run(qb[:, b], Kb[b], Vb[b], int(ctx[b]), slow[:, b], lam=0.3, k=k, n_sink=4,
+                         window=256) for b in range(B)]
+    plan = DecodePlan(slow, ctx, DEV)
+    max_len = int(ctx.max()) + steps
+    kw = dict(n_sink=4, window=256, k=k, lam=0.3, keep_fused=True)
+    decs, news = [], []
+    for _ in range(2):
+        if paged:
+            cfg = W.CONFIGS["ragged-paged-8k-128k"].replace(B=B, Hq=Hq, Hkv=Hkv, d=d)
+            table, npages = W.page_table(cfg, np.full(B, cap))
+            Kd, Vd = W.to_paged(K, table, npages, 16), W.to_paged(V, table, npages, 16)
+            news.append(W.take_decode_rows(Kd, Vd, ctx, steps, table=table))
+            decs.append(SFIDecoder(Kd, Vd, Hq, max_len, page_table=torch.from_numpy(table).to(DEV),
+                                   page_size=16, **kw))
+        else:
+            Kd, Vd = K.clone(), V.clone()
+            news.append(W.take_decode_rows(Kd, Vd, ctx, steps))
+            decs.append(SFIDecoder(Kd, Vd, Hq, max_len, **kw))
+    ties = 0
+    for s in range(steps):
+        decs[0].step(plan, s, q, new_kv=news[0])
+        decs[1].step(plan, s, q, new_kv=news[1], hints=False)
+        torch.cuda.synchronize()
+        o_h, o_n = decs[0].out.cpu().numpy(), decs[1].out.cpu().numpy()
+        for b in range(B):
+            r = refs[b][s]
+            assert row_rel_err(o_h[b], r["o"]) <= OUT_TOL, (s, b)
+            assert row_rel_err(o_n[b], o_h[b]) <= OUT_TOL, (s, b)
+            if r["kind"] == "slow":
+                sel = decs[0].sel_idx[b].cpu().numpy()
+                cnt = decs[0].sel_count[b].cpu().numpy()
+                for g in range(Hkv):
+                    ties += check_selection(sel[g], cnt[g], r["s"][g], r["lo"], r["hi"], k)
+                assert row_rel_err(decs[0].fused[b, :, : r["n"]].cpu().numpy(), r["s"]) <= EVID_TOL
+        assert torch.equal(decs[0].sel_idx, decs[1].sel_idx), s
+        assert torch.equal(decs[0].sel_count, decs[1].sel_count), s
+    _say(f"  near-tie differences over the run: {ties}")
+    assert ties == 0
+    # one co-launched step over the final cache: exact against over-stated hints
+    dec = decs[0]
+    lens = plan.seq_len_host[steps - 1].astype(np.int64)
+    sb, fb = [0, 3], [1, 2, 4, 5]
+    bound = np.minimum(lens, 260) + np.minimum(k, np.maximum(lens - 260, 0))
+    exact = (lens[sb].astype(np.int32), bound[fb].astype(np.int32))
+    over = (np.full(len(sb), max_len, dtype=np.int32), np.full(len(fb), 4 + 256 + k, dtype=np.int32))
+    sids = torch.tensor(sb, dtype=torch.int32, device=DEV)
+    fids = torch.tensor(fb, dtype=torch.int32, device=DEV)
+    res = []
+    for h in (exact, over):
+        dec.co_step(q[steps - 1], plan.seq_len[steps - 1], sids, len(sb), fids, len(fb), select=False,
+                    len_hints=h)
+        torch.cuda.synchronize()
+        res.append((dec.out.cpu().numpy(), dec.evidence.cpu().numpy()))
+    for b in sb + fb:
+        assert row_rel_err(res[1][0][b], res[0][0][b]) <= OUT_TOL, b
+    for b in sb:
+        n = int(lens[b])
+        assert row_rel_err(res[1][1][b, :, :n], res[0][1][b, :, :n]) <= EVID_TOL, b
+
+
 @pytest.mark.parametrize("kdiv,nms", [(0, False), (16, False), (0, True)])
 def test_layer_pipeline_matches_per_layer_calls(kdiv, nms):
     """sfi_decode_layer_step over a 3-layer stack, each layer's selection run
@@ -925,7 +1006,8 @@ def test_layer_pipeline_matches_per_layer_calls(kdiv, nms):
             pend = pipe[layer].layer_step(plan, s, q, pending=pend)
             ks = None if plan.k_seq is None else plan.k_seq[s]
             ref[layer].step_select(q[s], plan.seq_len[s], plan.slow_ids[s], int(plan.n_slow[s]),
-                                   plan.fast_ids[s], int(plan.n_fast[s]), k_seq=ks)
+                                   plan.fast_ids[s], int(plan.n_fast[s]), k_seq=ks,
+                                   len_hints=ref[layer].hints(plan, s))
             outs_p.append(pipe[layer].out.clone())
             outs_r.append(ref[layer].out.clone())
     sfi.sfi_run_deferred(pend)
