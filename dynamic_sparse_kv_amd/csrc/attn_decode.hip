@@ -1323,14 +1323,29 @@ long long fast_rows(const AttnLaunch &a) {
 }
 
 // Planning from host-known per-entry row counts (AttnLaunch::len_host).
-bool tabled(const AttnLaunch &a) {
-  return a.len_host != nullptr && a.batch_n > 0 && a.batch_n <= kMaxListed;
-}
+bool hinted(const AttnLaunch &a) { return a.len_host != nullptr && a.batch_n > 0; }
 
 long long host_max(const AttnLaunch &a) {
   long long m = 1;
   for (int z = 0; z < a.batch_n; ++z) m = std::max<long long>(m, a.len_host[z]);
   return m;
+}
+
+// A table pays where the entries' row counts differ: at least a tenth of a
+// max-length plan's blocks would find no rows.  Entries of (nearly) one
+// length keep the grid of the plain plan, sized from the longest hint; a
+// table costs each block a search of the prefix sums (dependent scalar
+// loads of the kernel arguments, ~0.5-0.9 us on a 23 us fast step).
+bool tabled(const AttnLaunch &a) {
+  if (!hinted(a) || a.batch_n > kMaxListed) return false;
+  long long sum = 0;
+  for (int z = 0; z < a.batch_n; ++z) sum += std::max(a.len_host[z], 0);
+  return sum * 10 < 9LL * a.batch_n * host_max(a);
+}
+
+// Rows that size the plain plan: the longest hint, else the host bound.
+long long plan_rows_of(const AttnLaunch &a, long long bound) {
+  return hinted(a) ? std::min(bound, host_max(a)) : bound;
 }
 
 // Chunk for about R rows per block: a multiple of the granule, at most
@@ -1409,7 +1424,7 @@ hipError_t slow_t(const AttnLaunch &a_in, hipStream_t st) {
                            : resident_slots<partial_kernel<D, G, false, MODE_SLOW, false>>();
     a.wt.n = 0;
     if (!(tabled(a) && plan_table(a, slots, kSplitGranule, kMaxSlowChunk)))
-      a.plan = plan_splits(a.max_len, a.batch_n * a.Hkv, slots, a.plan.stride, kMaxSlowChunk, true);
+      a.plan = plan_splits(plan_rows_of(a, a.max_len), a.batch_n * a.Hkv, slots, a.plan.stride, kMaxSlowChunk, true);
   }
   const PartialArgs p = partial_args<D>(a);
   const dim3 grid = a.wt.n > 0 ? dim3((unsigned)a.wt.cum[a.wt.n] * a.Hkv) : dim3(a.plan.splits, a.Hkv, a.batch_n);
@@ -1438,7 +1453,7 @@ hipError_t slow_t(const AttnLaunch &a_in, hipStream_t st) {
 template <int D, int G>
 SplitPlan fast_plan_t(const AttnLaunch &a) {
   const int slots = resident_slots<partial_kernel<D, G, false, MODE_FAST, false>>();
-  return plan_splits(fast_rows(a), a.batch_n * a.Hkv, slots, a.plan.stride, kMaxFastChunk, false);
+  return plan_splits(plan_rows_of(a, fast_rows(a)), a.batch_n * a.Hkv, slots, a.plan.stride, kMaxFastChunk, false);
 }
 
 template <int D, int G, bool PAGED>
@@ -1447,7 +1462,7 @@ hipError_t fast_t(const AttnLaunch &a_in, hipStream_t st) {
   a.wt.n = 0;
   if (!a.planned) {
     const int slots = resident_slots<partial_kernel<D, G, false, MODE_FAST, false>>();
-    if (!(tabled(a) && plan_table(a, slots, kMinFastTableChunk, kMaxFastChunk))) a.plan = fast_plan_t<D, G>(a);
+    if (!(tabled(a) && plan_table(a, slots, kSplitGranule, kMaxFastChunk))) a.plan = fast_plan_t<D, G>(a);
   }
   const PartialArgs p = partial_args<D>(a);
   const dim3 grid = a.wt.n > 0 ? dim3((unsigned)a.wt.cum[a.wt.n] * a.Hkv) : dim3(a.plan.splits, a.Hkv, a.batch_n);
@@ -1511,10 +1526,11 @@ bool plan_step_tables(AttnLaunch &sa, AttnLaunch &fa, int slots) {
   }
   if (sa.batch_n == 0) {
     sa.plan = SplitPlan{1, 0, sa.plan.stride};
-    return plan_table(fa, slots, kMinFastTableChunk, kMaxFastChunk);
+    return plan_table(fa, slots, kSplitGranule, kMaxFastChunk);
   }
   const long long Ls = host_max(sa), Lf = host_max(fa);
-  auto chunk_s = [&](long long R) { return table_chunk(sa, R, kMaxSlowChunk); };
+  long long smin = kSplitGranule;  // fewest rows per slow block
+  auto chunk_s = [&](long long R) { return table_chunk(sa, std::max(R, smin), kMaxSlowChunk); };
   auto chunk_f = [&](long long R) { return table_chunk(fa, std::max<long long>(R, kMinFastTableChunk), kMaxFastChunk); };
   auto blocks_at = [&](long long R) {
     return table_total(sa, chunk_s(R)) * sa.Hkv + table_total(fa, chunk_f(R)) * fa.Hkv;
@@ -1522,20 +1538,37 @@ bool plan_step_tables(AttnLaunch &sa, AttnLaunch &fa, int slots) {
   auto rows_per_wg = [&](long long R) { return std::max(std::min(chunk_s(R), Ls), std::min(chunk_f(R), Lf)); };
   const long long Rmax = (std::max(Ls, Lf) + kSplitGranule - 1) / kSplitGranule;  // in granules
   long long best_cost = -1, best_R = Rmax;
-  for (int k = 1; k <= 16; ++k) {
-    const long long cap = (long long)k * slots;
-    if (blocks_at(Rmax * kSplitGranule) > cap) continue;
-    long long lo = 1, hi = Rmax;  // hi fits
-    while (lo < hi) {
-      const long long mid = (lo + hi) / 2;
-      if (blocks_at(mid * kSplitGranule) <= cap) hi = mid;
-      else lo = mid + 1;
+  int best_k = 0;
+  auto search = [&]() {
+    best_cost = -1;
+    best_R = Rmax;
+    best_k = 0;
+    for (int k = 1; k <= 16; ++k) {
+      const long long cap = (long long)k * slots;
+      if (blocks_at(Rmax * kSplitGranule) > cap) continue;
+      long long lo = 1, hi = Rmax;  // hi fits
+      while (lo < hi) {
+        const long long mid = (lo + hi) / 2;
+        if (blocks_at(mid * kSplitGranule) <= cap) hi = mid;
+        else lo = mid + 1;
+      }
+      const long long cost = k * rows_per_wg(hi * kSplitGranule);
+      if (best_cost < 0 || cost < best_cost) {
+        best_cost = cost;
+        best_R = hi;
+        best_k = k;
+      }
     }
-    const long long cost = k * rows_per_wg(hi * kSplitGranule);
-    if (best_cost < 0 || cost < best_cost) {
-      best_cost = cost;
-      best_R = hi;
-    }
+  };
+  search();
+  // Several waves: the dispatcher refills freed slots, so slow blocks may be
+  // longer than the fast ones; fewer slow blocks pay fewer prologues and
+  // evidence flushes (at the ragged batch 2048-row slow blocks took the
+  // co-launched step from 164-166 to 158-159 us; in a one-wave plan they
+  // would leave the slow share too few blocks).
+  if (best_k > 1) {
+    smin = kMultiWaveSlowChunk;
+    search();
   }
   const long long R = best_cost < 0 ? kMaxFastChunk : best_R * kSplitGranule;
   if (fill_table(sa, chunk_s(R)) < 0) {
@@ -1560,18 +1593,21 @@ hipError_t step_t(const AttnLaunch &sa_in, const AttnLaunch &fa_in, hipStream_t 
   const int slots = resident_slots<copartial_kernel<D, G, false, false>>();
   sa.wt.n = 0;
   fa.wt.n = 0;
-  const bool tab = (sa.batch_n == 0 || tabled(sa)) && (fa.batch_n == 0 || tabled(fa)) &&
-                   sa.batch_n + fa.batch_n > 0;
+  // tables for both shares when both carry hints and either is ragged
+  const bool tab = (sa.batch_n == 0 || (hinted(sa) && sa.batch_n <= kMaxListed)) &&
+                   (fa.batch_n == 0 || (hinted(fa) && fa.batch_n <= kMaxListed)) && (tabled(sa) || tabled(fa));
   if (tab && plan_step_tables(sa, fa, slots)) {
     // planned from the entries' own row counts
   } else if (sa.batch_n == 0) {  // fast share only (a step that carries a pending selection)
-    fa.plan = plan_splits(fast_rows(fa), fa.batch_n * fa.Hkv, slots, fa.plan.stride, kMaxFastChunk, false);
+    fa.plan = plan_splits(plan_rows_of(fa, fast_rows(fa)), fa.batch_n * fa.Hkv, slots, fa.plan.stride,
+                          kMaxFastChunk, false);
     sa.plan = SplitPlan{1, 0, sa.plan.stride};
   } else if (fa.batch_n == 0) {  // slow share only
-    sa.plan = plan_splits(sa.max_len, sa.batch_n * sa.Hkv, slots, sa.plan.stride, kMaxSlowChunk, true);
+    sa.plan = plan_splits(plan_rows_of(sa, sa.max_len), sa.batch_n * sa.Hkv, slots, sa.plan.stride,
+                          kMaxSlowChunk, true);
     fa.plan = SplitPlan{1, 0, fa.plan.stride};
   } else {
-    const long long Ls = sa.max_len, Lf = fast_rows(fa);
+    const long long Ls = plan_rows_of(sa, sa.max_len), Lf = plan_rows_of(fa, fast_rows(fa));
     const long long ps = (long long)sa.batch_n * sa.Hkv, pf = (long long)fa.batch_n * fa.Hkv;
     const int s_stride = sa.plan.stride, f_stride = fa.plan.stride;
     // workgroups of the combined grid at R rows per workgroup (non-increasing in R)

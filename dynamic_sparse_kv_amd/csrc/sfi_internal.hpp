@@ -17,13 +17,19 @@ constexpr int kMaxSplits = 512;
 #define SFI_MAX_FAST_CHUNK 1024
 #endif
 constexpr int kMaxFastChunk = SFI_MAX_FAST_CHUNK;  // fast-step chunks stage their row ids in LDS
-// Fewest rows per fast-step block when the plan comes from per-entry row
-// counts: each block pays an index -> page -> row prologue before its
+// Fewest rows per fast block of a co-launched step planned from per-entry
+// row counts: each block pays an index -> page -> row prologue before its
 // gathers stream.
 #ifndef SFI_MIN_FAST_TABLE_CHUNK
 #define SFI_MIN_FAST_TABLE_CHUNK 512
 #endif
 constexpr int kMinFastTableChunk = SFI_MIN_FAST_TABLE_CHUNK;
+// Fewest rows per slow block of such a step when its plan takes several
+// waves of resident blocks.
+#ifndef SFI_MULTIWAVE_SLOW_CHUNK
+#define SFI_MULTIWAVE_SLOW_CHUNK 2048
+#endif
+constexpr int kMultiWaveSlowChunk = SFI_MULTIWAVE_SLOW_CHUNK;
 // Rows per workgroup of a dense or slow step at most.  Splits are planned
 // from the longest sequence of the batch (its lengths are on the device), so
 // without a cap a long sequence in a ragged batch gets a few huge chunks

@@ -117,10 +117,11 @@ typedef enum {
  * slow_len_host[z] is the seq_len of the z-th slow entry (0..max_seq_len);
  * fast_len_host[z] bounds the rows of the z-th fast entry's row list, at
  * least min(seq_len, n_sink + window) plus the entry's largest sel_count
- * (0..n_sink + window + sel_k).  Set, the split plan gives each listed entry
- * only the workgroups its own rows need (a work table of at most 256
- * entries; longer lists plan from max_seq_len) instead of max_seq_len's
- * worth each.  A hint outside its range is SFI_ERR_RANGE; one below the true
+ * (0..n_sink + window + sel_k).  Set, the split plan is sized from the
+ * longest hint instead of max_seq_len, and where the entries' counts differ
+ * (a tenth or more of such a plan's workgroups would find no rows) it gives
+ * each listed entry only the workgroups its own rows need (a work table of
+ * at most 256 entries; longer lists keep the plain plan).  A hint outside its range is SFI_ERR_RANGE; one below the true
  * count leaves the rows past it out of the result (wrong numbers, never an
  * out-of-bounds access).  Different chunking changes the fp32 summation
  * order, so results with and without hints agree up to rounding.
