@@ -893,8 +893,9 @@ def test_decode_run_mixed_batch_co_launch():
     assert ties == 0
 
 
-@pytest.mark.parametrize("paged", [False, True])
-def test_ragged_run_with_len_hints(paged):
+@pytest.mark.parametrize("Hq,Hkv,d,paged", [(32, 8, 128, False), (32, 8, 128, True), (8, 2, 64, True)],
+                         ids=["hkv8-d128", "hkv8-d128-paged", "hkv2-d64-paged"])
+def test_ragged_run_with_len_hints(Hq, Hkv, d, paged):
     """A ragged batch (six sequences of 60 to 9000 keys, each with its own
     slow/fast schedule, rows appended by the steps): with the host row-count
     hints every launch plans each sequence's workgroups from its own length
@@ -902,8 +903,8 @@ def test_ragged_run_with_len_hints(paged):
     oracle's decode run of every sequence; a run without hints agrees within
     tolerance and selects the same keys; a step given over-stated hints
     agrees with the exact ones within tolerance."""
-    _say(f"ragged run with length hints, paged={paged}")
-    B, Hq, Hkv, d, k = 6, 32, 8, 128, 200
+    _say(f"ragged run with length hints, Hq={Hq} Hkv={Hkv} d={d} paged={paged}")
+    B, k = 6, 200
     ctx = np.array([9000, 60, 2500, 300, 6000, 1200])
     steps = 10
     rng = np.random.default_rng(11)
@@ -972,6 +973,59 @@ def test_ragged_run_with_len_hints(paged):
     for b in sb:
         n = int(lens[b])
         assert row_rel_err(res[1][1][b, :, :n], res[0][1][b, :, :n]) <= EVID_TOL, b
+
+
+def test_len_hints_long_list_keeps_plain_plan():
+    """More listed entries than a work table holds (300 > 256): with hints
+    the co-launched step keeps the plain grid, sized from the longest hint.
+    Outputs against the call without hints and, for sampled sequences,
+    against the oracle; evidence of the slow ones likewise."""
+    _say("length hints, 300 listed entries")
+    B, Hq, Hkv, d, k = 300, 8, 2, 64, 16
+    rng = np.random.default_rng(21)
+    lens = rng.integers(1, 400, size=B)
+    lens[7] = 1
+    cap = 416
+    K, V = _rand_kv(B, Hkv, cap, d, seed=730, hh=3)
+    q = _rand_q((B, Hq, d), seed=731)
+    seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    sel = np.full((B, Hkv, k), -1, dtype=np.int32)
+    cnt = np.zeros((B, Hkv), dtype=np.int32)
+    for b in range(B):
+        mid = np.arange(4, max(4, lens[b] - 32))
+        for g in range(Hkv):
+            c = min(k, len(mid))
+            if c:
+                sel[b, g, :c] = np.sort(rng.choice(mid, c, replace=False))
+            cnt[b, g] = c
+    slow_b = list(range(0, B, 7))
+    fast_b = [b for b in range(B) if b % 7]
+    sids = torch.tensor(slow_b, dtype=torch.int32, device=DEV)
+    fids = torch.tensor(fast_b, dtype=torch.int32, device=DEV)
+    lens64 = lens.astype(np.int64)
+    bound = np.minimum(lens64, 36) + cnt.max(axis=1)
+    hints = (lens[slow_b].astype(np.int32), bound[fast_b].astype(np.int32))
+    res = []
+    for h in (None, hints):
+        dec = SFIDecoder(K, V, Hq, cap, n_sink=4, window=32, k=k, lam=0.3)
+        dec.sel_idx.copy_(torch.from_numpy(sel))
+        dec.sel_count.copy_(torch.from_numpy(cnt))
+        dec.co_step(q, seq, sids, len(slow_b), fids, len(fast_b), select=False, len_hints=h)
+        torch.cuda.synchronize()
+        res.append((dec.out.cpu().numpy(), dec.evidence.cpu().numpy()))
+    for b in range(B):
+        assert row_rel_err(res[1][0][b], res[0][0][b]) <= OUT_TOL, b
+    for b in slow_b:
+        n = int(lens[b])
+        assert row_rel_err(res[1][1][b, :, :n], res[0][1][b, :, :n]) <= EVID_TOL, b
+    Kb, Vb, qb = _bits(K), _bits(V), _bits(q)
+    for b in slow_b[:5]:
+        o_ref, _ = O.dense_step(qb[b], Kb[b], Vb[b], int(lens[b]))
+        assert row_rel_err(res[1][0][b], o_ref) <= OUT_TOL, b
+    for b in fast_b[:8] + [7]:
+        lists = [sel[b, g, : cnt[b, g]] for g in range(Hkv)]
+        o_ref = O.fast_step(qb[b], Kb[b], Vb[b], int(lens[b]), lists, 4, 32)
+        assert row_rel_err(res[1][0][b], o_ref) <= OUT_TOL, b
 
 
 @pytest.mark.parametrize("kdiv,nms", [(0, False), (16, False), (0, True)])
