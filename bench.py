@@ -14,8 +14,12 @@ Headline (cold): R independent copies of the layer (own seeded K/V and
 queries, same schedule) run each step in turn, so between two steps of one
 copy the other copies stream more than the 256 MB Infinity Cache holds; the
 K x R layer-steps are replayed from one HIP graph, value = B K R / time
-(tokens/s of one layer), median of 3 replays.  The same K steps of one copy
-alone (warm: its fast rows stay cached) are reported beside it.
+(tokens/s of one layer), median of 3 replays.  The copies are scheduled as
+the layers of a model would be: a copy's selection runs inside the next
+copy's grids (sfi_decode_layer_step), so it completes before that copy's
+next step; the same replay with every selection inside its own step call
+(sfi_decode_step_select) is reported beside it, and so are the same K steps
+of one copy alone (warm: its fast rows stay cached).
 
 Per call: each call kind is timed with HIP events on the launch stream over
 a region of R back-to-back launches on the R copies (cold), after a 1 GiB
@@ -868,7 +872,20 @@ def main():
     side = torch.cuda.Stream()
     torch.cuda.synchronize()
 
-    def run_steps(st, s0, s1, copies):
+    def run_steps(st, s0, s1, copies, pipelined=True):
+        # The copies stand in for the layers of a model.  Pipelined (several
+        # copies): each copy's selection runs inside the next copy's grids
+        # (sfi_decode_layer_step), the last copy's inside the next step's
+        # first copy, one flush at the end; every selection still completes
+        # before its own copy's next step.  Otherwise each step call runs its
+        # selection itself (sfi_decode_step_select).
+        if pipelined and len(copies) > 1:
+            pend = None
+            for s in range(s0, s1):
+                for rp in copies:
+                    pend = rp["dec"].layer_step(plan, s, rp["q"], pending=pend, stream=st, new_kv=rp["nk"])
+            sfi.sfi_run_deferred(pend, st)
+            return
         for s in range(s0, s1):
             for rp in copies:
                 rp["dec"].step(plan, s, rp["q"], st, new_kv=rp["nk"])
@@ -879,11 +896,15 @@ def main():
 
     # ---- headline: K steps x R copies replayed from one HIP graph (cold) ----
     use_graph = not args.no_graph
-    warm_tps = None
+    warm_tps = inline_tps = None
     if use_graph:
         _log("[bench] timing graph replays (cold: copies in turn)")
         t_total, ts_cold, g = _graph_time(lambda st: run_steps(st, 0, K_steps, reps), side, stream)
         del g
+        _log("[bench] timing graph replays (cold, each copy's selection in its own step call)")
+        t_inline, _, g = _graph_time(lambda st: run_steps(st, 0, K_steps, reps, pipelined=False), side, stream)
+        del g
+        inline_tps = cfg.B * K_steps * R / t_inline
         _log("[bench] timing graph replays (warm: one copy)")
         t_warm, ts_warm, g = _graph_time(lambda st: run_steps(st, 0, K_steps, reps[:1]), side, stream)
         del g
@@ -1018,9 +1039,13 @@ def main():
                    "timing": ("hip graph replay, one stream, median of 3 replays; cold: the step's "
                               f"layer-steps of {R} independent copies of the layer run in turn, value = "
                               "tokens/s of one layer" if use_graph else "eager, one stream") +
-                             "; a step with slow sequences is one sfi_decode_step_select call"},
+                             "; the copies are scheduled as the layers of a model: each copy's selection "
+                             "runs inside the next copy's grids (sfi_decode_layer_step); "
+                             "tokens_per_s_selection_per_copy: each step with slow sequences is one "
+                             "sfi_decode_step_select call that runs its own selection"},
         "roofline": roofline,
         "warm_tokens_per_s": None if warm_tps is None else round(warm_tps, 1),
+        "tokens_per_s_selection_per_copy": None if inline_tps is None else round(inline_tps, 1),
         "replays_s": [round(x, 6) for x in ts_cold],
         "per_call": per_call,
         "dense_tokens_per_s": round(dense_tps, 1),
