@@ -1539,20 +1539,30 @@ bool plan_step_tables(AttnLaunch &sa, AttnLaunch &fa, int slots) {
   const long long Rmax = (std::max(Ls, Lf) + kSplitGranule - 1) / kSplitGranule;  // in granules
   long long best_cost = -1, best_R = Rmax;
   int best_k = 0;
+  // a fast block never holds fewer rows than this, so no plan of k waves
+  // costs less than k x (floor + block cost): the search stops there
+  const long long floor_rows = std::min<long long>(kMinFastTableChunk, Lf);
   auto search = [&]() {
     best_cost = -1;
     best_R = Rmax;
     best_k = 0;
+    bool fits = false;
+    long long hi0 = Rmax;  // fits every k from the first that fits on
     for (int k = 1; k <= 16; ++k) {
+      if (best_cost >= 0 && k * (floor_rows + kPlanBlockCost) >= best_cost) break;
       const long long cap = (long long)k * slots;
-      if (blocks_at(Rmax * kSplitGranule) > cap) continue;
-      long long lo = 1, hi = Rmax;  // hi fits
+      if (!fits) {
+        if (blocks_at(Rmax * kSplitGranule) > cap) continue;
+        fits = true;
+      }
+      long long lo = 1, hi = hi0;  // hi fits
       while (lo < hi) {
         const long long mid = (lo + hi) / 2;
         if (blocks_at(mid * kSplitGranule) <= cap) hi = mid;
         else lo = mid + 1;
       }
-      const long long cost = k * rows_per_wg(hi * kSplitGranule);
+      hi0 = hi;
+      const long long cost = k * (rows_per_wg(hi * kSplitGranule) + kPlanBlockCost);
       if (best_cost < 0 || cost < best_cost) {
         best_cost = cost;
         best_R = hi;
@@ -1638,7 +1648,7 @@ hipError_t step_t(const AttnLaunch &sa_in, const AttnLaunch &fa_in, hipStream_t 
         else lo = mid + 1;
       }
       plan_at(hi * kSplitGranule);
-      const long long cost = k * rows_per_wg();
+      const long long cost = k * (rows_per_wg() + kPlanBlockCost);
       if (best_cost < 0 || cost < best_cost) {
         best_cost = cost;
         best_R = hi;

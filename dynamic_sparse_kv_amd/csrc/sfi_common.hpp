@@ -164,16 +164,33 @@ struct WorkTable {
   uint16_t cum[kMaxListed + 1];
 };
 
-// Entry, head and split of block w of a tabled share.
+// Entry, head and split of block w of a tabled share.  The entry is the
+// number of z in [1, n) with cum[z] <= e: each lane tests up to 4 entries
+// and ballots count them, so the table's loads are in flight together and
+// the entry's own prefix sum comes from a lane (a binary search made each
+// block wait on ~log2(n) dependent loads of the kernel arguments).
 __device__ __forceinline__ PairBlock table_block(const WorkTable &t, int w, int Hkv) {
   const int e = w / Hkv;
-  int lo = 0, hi = t.n - 1;  // the last entry z with cum[z] <= e
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if ((int)t.cum[mid] <= e) lo = mid;
-    else hi = mid - 1;
+  const int lane = (int)(threadIdx.x & 63);
+  int c[kMaxListed / 64];
+#pragma unroll
+  for (int i = 0; i < kMaxListed / 64; ++i) {
+    const int zi = 1 + lane + 64 * i;
+    c[i] = (zi < t.n) ? (int)t.cum[zi] : 0x7fffffff;
   }
-  return {e - (int)t.cum[lo], w - e * Hkv, lo};
+  int z = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxListed / 64; ++i) z += __popcll(__ballot(c[i] <= e));
+  // cum[z] is entry z's value among the lanes' (z >= 1), cum[0] = 0
+  int base = 0;
+  if (z > 0) {
+    const int zi = z - 1;
+    int v = c[0];
+#pragma unroll
+    for (int i = 1; i < kMaxListed / 64; ++i) v = ((zi >> 6) == i) ? c[i] : v;
+    base = __builtin_amdgcn_readlane(v, zi & 63);
+  }
+  return {e - base, w - e * Hkv, z};
 }
 
 // Splits of entry z: its table count, or the planned number.

@@ -17,6 +17,14 @@ constexpr int kMaxSplits = 512;
 #define SFI_MAX_FAST_CHUNK 1024
 #endif
 constexpr int kMaxFastChunk = SFI_MAX_FAST_CHUNK;  // fast-step chunks stage their row ids in LDS
+// A workgroup's fixed cost in the co-launch plans' makespan estimate, in
+// rows: k waves cost k x (rows per workgroup + this).  Without it the
+// estimate could prefer 14 waves of 32-row workgroups to 3 waves of 160
+// rows (a 3.4K + 31 x 772-row step: 52 against 25 us).
+#ifndef SFI_PLAN_BLOCK_COST
+#define SFI_PLAN_BLOCK_COST 128
+#endif
+constexpr int kPlanBlockCost = SFI_PLAN_BLOCK_COST;
 // Fewest rows per fast block of a co-launched step planned from per-entry
 // row counts: each block pays an index -> page -> row prologue before its
 // gathers stream.
