@@ -1012,7 +1012,9 @@ __device__ __forceinline__ void finalize_body(const FinalArgs &a, int x, int g, 
   if constexpr (EVID) {
     const int n = clamp_len(a.seq_len, b, a.max_len);
     if ((x - G) * kEvidChunk >= n) return;
-    const int S = (n + a.chunk - 1) / a.chunk;
+    // the splits holding the row's keys, never past the entry's planned
+    // splits (a host row-count hint below n leaves keys unplanned)
+    const int S = min((n + a.chunk - 1) / a.chunk, entry_splits(a.wt, zb, a.splits));
     const size_t lrow = (size_t)b * a.Hkv + g;
     const int j0 = (x - G) * kEvidChunk;
     const int j1 = min(n, j0 + kEvidChunk);
