@@ -26,7 +26,15 @@ constexpr int kRawBase = (96 << 6) - 1;
 constexpr int kBPT = kBins1 / kT;       // buckets per thread
 constexpr int kD2 = 11;                 // digit width inside the bucket
 constexpr int kBins2 = 1 << kD2;
-constexpr int kCandLds = 4096;          // bucket candidates gathered into LDS
+// Bucket candidates staged in LDS by the pick (more are read in place from
+// the sorted runs; a 32K row's bucket holds ~100).  1024 rather than 4096
+// keeps the pick's LDS at 21 KB, so a finalize grid that carries another
+// layer's pick keeps 4 waves per SIMD instead of 2 (pipelined 32K headline
+// 176.0 -> 178.3-180.7 K tokens/s, 128K stack 2.30 -> 2.36 K).
+#ifndef SFI_CAND_LDS
+#define SFI_CAND_LDS 1024
+#endif
+constexpr int kCandLds = SFI_CAND_LDS;  // bucket candidates gathered into LDS (more: read in place)
 constexpr int kCPT = kSelMaxChunks / kT;  // chunks per thread in the pick scans
 static_assert(kQuarter == 4 * kT, "a half chunk is four keys per thread");
 static_assert(kBPT == 16, "sixteen buckets per thread");
