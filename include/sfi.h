@@ -111,20 +111,22 @@ typedef enum {
  *
  * Row-count hints (launch planning only; they change no step of the
  * method, and serve batches whose sequences differ much in length):
- * slow_len_host and fast_len_host are
- * host arrays in the order of the call's slow list and fast list (the one
- * list of sfi_slow_step and sfi_fast_step), read during the call only.
- * slow_len_host[z] is the seq_len of the z-th slow entry (0..max_seq_len);
- * fast_len_host[z] bounds the rows of the z-th fast entry's row list, at
- * least min(seq_len, n_sink + window) plus the entry's largest sel_count
+ * slow_len_host and fast_len_host are host arrays in the order of the
+ * call's slow list and fast list (the one list of sfi_slow_step and
+ * sfi_fast_step), read during the call only.  slow_len_host[z] is the
+ * seq_len of the z-th slow entry (0..max_seq_len); fast_len_host[z] bounds
+ * the rows of the z-th fast entry's row list, at least
+ * min(seq_len, n_sink + window) plus the entry's largest sel_count
  * (0..n_sink + window + sel_k).  Set, the split plan is sized from the
- * longest hint instead of max_seq_len, and where the entries' counts differ
- * (a tenth or more of such a plan's workgroups would find no rows) it gives
- * each listed entry only the workgroups its own rows need (a work table of
- * at most 256 entries; longer lists keep the plain plan).  A hint outside its range is SFI_ERR_RANGE; one below the true
- * count leaves the rows past it out of the result (wrong numbers, never an
- * out-of-bounds access).  Different chunking changes the fp32 summation
- * order, so results with and without hints agree up to rounding.
+ * longest hint instead of max_seq_len, and where the entries' counts
+ * differ (a tenth or more of such a plan's workgroups would find no rows)
+ * it gives each listed entry only the workgroups its own rows need (a work
+ * table of at most 256 entries; longer lists keep the plain plan).  A hint
+ * outside its range is SFI_ERR_RANGE; one below the true count leaves the
+ * rows past it out of the result, and the fused append of a row past it
+ * out of the cache (wrong numbers, never an out-of-bounds access).
+ * Different chunking changes the fp32 summation order, so results with and
+ * without hints agree up to rounding.
  * sfi_fast_step_noalloc and sfi_fast_step_compact ignore them. */
 typedef struct sfi_kv {
   const uint16_t *k;
