@@ -1335,9 +1335,9 @@ long long host_max(const AttnLaunch &a) {
 
 // A table pays where the entries' row counts differ: at least a tenth of a
 // max-length plan's blocks would find no rows.  Entries of (nearly) one
-// length keep the grid of the plain plan, sized from the longest hint; a
-// table costs each block a search of the prefix sums (dependent scalar
-// loads of the kernel arguments, ~0.5-0.9 us on a 23 us fast step).
+// length keep the grid of the plain plan, sized from the longest hint,
+// since a table costs each block a round trip for the prefix sums before
+// its first row load.
 bool tabled(const AttnLaunch &a) {
   if (!hinted(a) || a.batch_n > kMaxListed) return false;
   long long sum = 0;
