@@ -968,6 +968,6 @@ const char *sfi_status_string(sfi_status s) {
   return "unknown status";
 }
 
-const char *sfi_version(void) { return "libsfi 0.1 gfx950"; }
+const char *sfi_version(void) { return "libsfi 0.2 gfx950"; }
 
 }  // extern "C"

@@ -481,7 +481,8 @@ sfi_status sfi_schedule(const uint8_t *events, int32_t steps, int32_t B, int32_t
 /* Human-readable name of a status [host]. */
 const char *sfi_status_string(sfi_status s);
 
-/* Library version string [host]. */
+/* Library version string [host].  0.2: sfi_kv carries the key-norm
+ * statistics and the host row-count hints (its layout differs from 0.1's). */
 const char *sfi_version(void);
 
 #ifdef __cplusplus
